@@ -1,0 +1,300 @@
+"""CPU oracle of the DAC-style waveform decoder -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, ``__graft_entry__.smoke()`` and bench.py's CPU-baseline leg may
+import this module.  The product path (the HIP library and its binding)
+never imports or calls it, and this module imports nothing from the product.
+
+The arithmetic lives in ``oracle.c`` (direct loops; fp64 build = the oracle,
+fp32 build = the precision floor).  This file only orders the steps of the
+decoder the way the pages state them and holds the readings of points the
+pages leave open.
+
+Decoder (minimaxmusic.cpp ARCHITECTURE, "Flow VAE" listing; DAV decoder):
+    h = conv_in(latent)                                  Conv1d k7, pad 3, bias
+    for each block b (stride s):
+        h = conv_t1(Snake_b(h))                          ConvTranspose1d k=2s, stride s
+        for d in (1, 3, 9):                              residual units
+            h = h + conv2(Snake2(conv1_d(Snake1(h))))    conv1 k7 dilation d, conv2 k1
+    pcm = tanh(conv_out(Snake_out(h)))                   Conv1d k7 -> 1 channel, bias
+
+Readings of points the pages leave open (each listed in the design notes):
+  * conv padding is zero "same" padding (K-1)/2*d, so the residual add lines up;
+  * ConvTranspose1d keeps full[n + ceil(s/2)] for n in [0, T*s): for even s
+    this is the pages' "pad s/2"; for odd s it is PyTorch padding=ceil(s/2),
+    output_padding=1;
+  * the convT weight norm is taken along axis 0 of the stored [in, out, k]
+    tensor (per input channel), as the pages' "axis 0" says literally;
+  * Snake denominators are alpha + 1e-9 (Snake) and beta + 1e-9 (SnakeBeta);
+  * every conv has a bias; N(0, 0.01) biases use std 0.01;
+  * bf16 configurations: the folded weights are rounded fp64 -> fp32 (the F32
+    inference checkpoint) -> bf16 (round to nearest even), the latent is
+    rounded to bf16, and everything else stays exact.  Optionally
+    (``round_operands=True``) every convolution input after its Snake is also
+    rounded to bf16, mirroring an implementation whose matrix-core operands
+    are bf16 while accumulation and the residual stream stay wide.
+
+Pins (tests/test_oracle_pins.py) hold every function here to closed forms,
+brute force, textbook/library routines and invariants the pages fix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIBS = {"f64": os.path.join(_HERE, "liboracle_f64.so"),
+         "f32": os.path.join(_HERE, "liboracle_f32.so")}
+_DEFS = {"f64": ["-DREAL=double"], "f32": ["-DREAL=float", "-DORACLE_FLOAT"]}
+_NP = {"f64": np.float64, "f32": np.float32}
+_loaded = {}
+
+
+def build_library() -> None:
+    """Compile both builds of oracle.c with gcc (OpenMP, no fast-math)."""
+    for prec, out in _LIBS.items():
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-fno-fast-math", "-ffp-contract=off", *_DEFS[prec], _SRC, "-o",
+               out + ".tmp", "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(out + ".tmp", out)
+
+
+def _lib(prec: str):
+    if prec not in _loaded:
+        path = _LIBS[prec]
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build_library()
+        lib = ctypes.CDLL(path)
+        P, I = ctypes.c_void_p, ctypes.c_int64
+        lib.orc_real_size.restype = ctypes.c_int
+        lib.orc_snake.argtypes = [P, P, I, I, I, P, P]
+        lib.orc_weight_norm.argtypes = [P, P, P, I, I, P]
+        lib.orc_conv1d.argtypes = [P, P, I, I, I, P, P, I, I, I]
+        lib.orc_conv_transpose1d.argtypes = [P, P, I, I, I, P, P, I, I, I, I, I]
+        lib.orc_tanh.argtypes = [P, P, I]
+        lib.orc_add.argtypes = [P, P, P, I]
+        assert lib.orc_real_size() == np.dtype(_NP[prec]).itemsize
+        _loaded[prec] = lib
+    return _loaded[prec]
+
+
+def _c(a, prec):
+    return np.ascontiguousarray(a, dtype=_NP[prec])
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+# --------------------------------------------------------------------------
+# Primitive operations (each a direct loop in oracle.c).
+# --------------------------------------------------------------------------
+
+def snake(x, alpha, beta=None, prec="f64"):
+    """Snake(x) = x + sin^2(alpha x)/(alpha+1e-9); SnakeBeta uses beta+1e-9. x: [R, C, T]."""
+    x = _c(x, prec)
+    r, c, t = x.shape
+    a = _c(np.reshape(alpha, -1), prec)
+    b = None if beta is None else _c(np.reshape(beta, -1), prec)
+    assert a.size == c and (b is None or b.size == c)
+    y = np.empty_like(x)
+    _lib(prec).orc_snake(_p(x), _p(y), r, c, t, _p(a), _p(b))
+    return y
+
+
+def weight_norm(v, g, prec="f64"):
+    """Fold w = g * v / ||v|| along axis 0 of v.  Returns (w, norms)."""
+    v = _c(v, prec)
+    g = _c(np.reshape(g, -1), prec)
+    d0 = v.shape[0]
+    assert g.size == d0
+    w = np.empty_like(v)
+    n = np.empty(d0, dtype=_NP[prec])
+    _lib(prec).orc_weight_norm(_p(v), _p(g), _p(w), d0, v.size // d0, _p(n))
+    return w, n
+
+
+def conv1d(x, w, bias=None, dilation=1, prec="f64"):
+    """Zero 'same'-padded Conv1d.  x: [R, Cin, T], w: [Cout, Cin, K] (K odd)."""
+    x = _c(x, prec)
+    w = _c(w, prec)
+    r, cin, t = x.shape
+    cout, cin2, k = w.shape
+    assert cin == cin2 and k % 2 == 1
+    b = None if bias is None else _c(np.reshape(bias, -1), prec)
+    y = np.empty((r, cout, t), dtype=_NP[prec])
+    _lib(prec).orc_conv1d(_p(x), _p(y), r, cin, t, _p(w), _p(b), cout, k, dilation)
+    return y
+
+
+def convt_crop(stride: int) -> int:
+    """Left crop of the transposed conv: ceil(s/2) (s/2 for even s)."""
+    return (stride + 1) // 2
+
+
+def conv_transpose1d(x, w, bias, stride, pad_left=None, out_len=None, prec="f64"):
+    """ConvTranspose1d.  x: [R, Cin, T], w: [Cin, Cout, K]; keeps full[n+pad_left], n < out_len."""
+    x = _c(x, prec)
+    w = _c(w, prec)
+    r, cin, t = x.shape
+    cin2, cout, k = w.shape
+    assert cin == cin2
+    p = convt_crop(stride) if pad_left is None else pad_left
+    tout = t * stride if out_len is None else out_len
+    b = None if bias is None else _c(np.reshape(bias, -1), prec)
+    y = np.empty((r, cout, tout), dtype=_NP[prec])
+    _lib(prec).orc_conv_transpose1d(_p(x), _p(y), r, cin, t, _p(w), _p(b), cout, k,
+                                    stride, p, tout)
+    return y
+
+
+def tanh(x, prec="f64"):
+    x = _c(x, prec)
+    y = np.empty_like(x)
+    _lib(prec).orc_tanh(_p(x), _p(y), x.size)
+    return y
+
+
+def add(a, b, prec="f64"):
+    a = _c(a, prec)
+    b = _c(b, prec)
+    assert a.shape == b.shape
+    y = np.empty_like(a)
+    _lib(prec).orc_add(_p(a), _p(b), _p(y), a.size)
+    return y
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even) via float32; returns float64.
+
+    bf16 keeps the top 16 bits of an IEEE float32: add 0x7FFF plus the lowest
+    kept bit, then truncate.
+    """
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# The decoder.
+# --------------------------------------------------------------------------
+
+class Model:
+    """Folded weights of one decoder, held at the oracle's precision."""
+
+    def __init__(self, cfg: dict, tensors: dict, prec: str = "f64",
+                 bf16: bool | None = None, round_operands: bool = False):
+        self.cfg = cfg
+        self.prec = prec
+        self.bf16 = (cfg["dtype"] == "bf16") if bf16 is None else bf16
+        self.round_operands = round_operands and self.bf16
+        self.beta = cfg["act"] == "snakebeta"
+        self.norms = {}
+        t = tensors
+
+        def fold(prefix):
+            # The fold is always fp64 (it is done once at conversion).
+            w, n = weight_norm(t[prefix + ".weight_v"], t[prefix + ".weight_g"], "f64")
+            self.norms[prefix] = n
+            if self.bf16:
+                w = round_bf16(w.astype(np.float32))
+            return _c(w, prec)
+
+        def vec(name):
+            return _c(np.reshape(t[name], -1), prec)
+
+        def act(prefix):
+            return (vec(prefix + ".alpha"), vec(prefix + ".beta") if self.beta else None)
+
+        self.conv_in = (fold("conv_in"), vec("conv_in.bias"))
+        self.blocks = []
+        for b, s in enumerate(cfg["strides"]):
+            p = f"blocks.{b}"
+            units = []
+            for r, d in enumerate(cfg["dilations"]):
+                q = f"{p}.res_units.{r}"
+                units.append(dict(d=d, act1=act(q + ".snake1"),
+                                  w1=fold(q + ".conv1"), b1=vec(q + ".conv1.bias"),
+                                  act2=act(q + ".snake2"),
+                                  w2=fold(q + ".conv2"), b2=vec(q + ".conv2.bias")))
+            self.blocks.append(dict(s=s, act=act(p + ".snake1"),
+                                    wt=fold(p + ".conv_t1"), bt=vec(p + ".conv_t1.bias"),
+                                    units=units))
+        self.head = (act("snake_out"), fold("conv_out"), vec("conv_out.bias"))
+
+    # ---- stages -----------------------------------------------------------
+    def _snake(self, x, a):
+        y = snake(x, a[0], a[1], self.prec)
+        if self.round_operands:
+            y = _c(round_bf16(y), self.prec)
+        return y
+
+    def _latent(self, latent):
+        x = np.asarray(latent, dtype=np.float32)
+        return _c(round_bf16(x) if self.bf16 else x, self.prec)
+
+    def stage_conv_in(self, latent):
+        w, b = self.conv_in
+        return conv1d(self._latent(latent), w, b, 1, self.prec)
+
+    def stage_upsample(self, b, h):
+        blk = self.blocks[b]
+        return conv_transpose1d(self._snake(h, blk["act"]), blk["wt"], blk["bt"],
+                                blk["s"], prec=self.prec)
+
+    def stage_res_unit(self, b, r, h):
+        u = self.blocks[b]["units"][r]
+        v = conv1d(self._snake(h, u["act1"]), u["w1"], u["b1"], u["d"], self.prec)
+        return add(h, conv1d(self._snake(v, u["act2"]), u["w2"], u["b2"], 1, self.prec),
+                   self.prec)
+
+    def stage_head_pre(self, h):
+        a, w, b = self.head
+        return conv1d(self._snake(h, a), w, b, 1, self.prec)
+
+    def stage_head(self, h):
+        return tanh(self.stage_head_pre(h), self.prec)
+
+    # Stage numbering shared with the debug stage runner of the library:
+    # 0 = conv_in; then per block b: 1 + b*(1+n_res) = Snake + ConvTranspose1d,
+    # the next n_res indices = residual units; last = head.
+    def n_stages(self):
+        return 2 + len(self.blocks) * (1 + len(self.cfg["dilations"]))
+
+    def run_stage(self, k, x):
+        nr = len(self.cfg["dilations"])
+        if k == 0:
+            return self.stage_conv_in(x)
+        if k == self.n_stages() - 1:
+            return self.stage_head(x)
+        b, j = divmod(k - 1, 1 + nr)
+        return self.stage_upsample(b, x) if j == 0 else self.stage_res_unit(b, j - 1, x)
+
+    def decode(self, latent, pre_tanh=False):
+        """latent [B, C_latent, T] -> pcm [B, 1, T*hop] (or the pre-tanh value)."""
+        h = self.stage_conv_in(latent)
+        for b in range(len(self.blocks)):
+            h = self.stage_upsample(b, h)
+            for r in range(len(self.cfg["dilations"])):
+                h = self.stage_res_unit(b, r, h)
+        return self.stage_head_pre(h) if pre_tanh else self.stage_head(h)
+
+    def decode_tiled(self, latent, tile, halo):
+        """Decode latent frames [t0, t1) of each tile from the window
+        [t0 - halo, t1 + halo) clamped to the clip, keeping the tile's own
+        samples.  Equals decode() when halo covers the receptive field."""
+        latent = np.asarray(latent)
+        bsz, _, t = latent.shape
+        hop = self.cfg["hop"]
+        out = np.empty((bsz, 1, t * hop), dtype=_NP[self.prec])
+        for t0 in range(0, t, tile):
+            t1 = min(t, t0 + tile)
+            a, e = max(0, t0 - halo), min(t, t1 + halo)
+            y = self.decode(latent[:, :, a:e])
+            out[:, :, t0 * hop:t1 * hop] = y[:, :, (t0 - a) * hop:(t1 - a) * hop]
+        return out
