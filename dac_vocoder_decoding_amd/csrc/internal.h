@@ -1,0 +1,130 @@
+// internal.h -- device-side data layouts and kernel launch interfaces of
+// libvocoder (not part of the public ABI).
+//
+// Activation layouts in HBM ("channel-chunked channels-last"):
+//   operand tensors (matrix-core inputs, fp32 or bf16):
+//       [row][C / CH][T][CH] with CH = 64 bytes / element size
+//       (16 fp32 or 32 bf16 channels per chunk)
+//   residual stream h (always fp32): [row][C / 16][T][16]
+// One 64-byte chunk row holds CH consecutive channels of one time frame, so a
+// GEMM tile of a channel chunk over consecutive frames is one contiguous span.
+//
+// Packed conv weights (matrix-core dtype): [Cin / CH][tap][M][CH]
+//   Conv1d  (Cout, Cin, K):  tap = k,           M = Cout, m = o
+//   ConvT   (Cin, Cout, 2s): tap t in {0,1},    M = s*Cout, m = r*Cout + o,
+//                            value w[i][o][t*s + r]   (polyphase split)
+// Head weights: fp32 [k][C] (bf16-rounded values for BF16 configs).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace voc {
+
+constexpr int kChunkBytes = 64;
+constexpr int kHChunk = 16;  // fp32 residual stream channels per chunk
+
+enum OpType { OP_F32 = 0, OP_BF16 = 1 };
+
+inline int op_chunk(int op) { return op == OP_F32 ? 16 : 32; }
+inline int op_size(int op) { return op == OP_F32 ? 4 : 2; }
+
+// Per-row metadata of one decode (device arrays, length = rows).
+struct RowInfo {
+  const int* len;       // valid latent frames of the row
+  const int* src_b;     // source batch row of the latent
+  const int* start;     // first latent frame of the row in the source
+  const int* keep_lo;   // first output sample kept (row-local)
+  const int* keep_hi;   // one past the last output sample kept
+  const int64_t* dst;   // pcm element offset of the first kept sample
+};
+
+// One implicit-GEMM convolution launch:
+//   acc[n][m] = sum_tap sum_i W[tap][m][i] * X[row][n + off0 + tap*offstep][i]
+// X frames outside [0, len*rate_in) read as zero.  Output frame
+// tau = n*ups + m / Cout - crop, channel o = m % Cout, kept if
+// 0 <= tau < min(len*rate_out, T_out).
+// Epilogue: v = acc + bias[o] (+ res); h_out <- v (fp32);
+//           s_out <- Snake(v; s_alpha, s_invden) in the operand dtype.
+struct ConvArgs {
+  const void* x;
+  int T_in;       // allocated frames per row of x
+  int Cin;
+  const int* row_len;
+  int rate_in, rate_out;
+  const void* w;
+  int M, Cout;
+  int off0, offstep, min_off, halo;
+  int N;          // GEMM positions per row
+  int n_tiles, m_tiles, rows;
+  const float* bias;
+  float* h_out;
+  const float* res;
+  void* s_out;
+  const float* s_alpha;
+  const float* s_invden;
+  int T_out, ups, crop;
+};
+
+// Tile shape families of the conv GEMM kernel.
+enum ConvVariant { CV_64x256 = 0, CV_64x128 = 1, CV_128x128 = 2, CV_COUNT = 3 };
+int conv_variant_bm(int v);
+int conv_variant_bn(int v);
+bool conv_variant_ok(int v, int taps);
+
+hipError_t launch_conv(int op, int taps, int variant, const ConvArgs& a, hipStream_t s);
+
+// Weight-norm fold + cast + repack, one workgroup per axis-0 slice.
+enum PackKind { PACK_CONV = 0, PACK_CONVT = 1, PACK_HEAD = 2 };
+struct FoldArgs {
+  const float* v;
+  const float* g;
+  int64_t d0, rest;
+  int kind;
+  int op;           // operand dtype of the packed output (head: always fp32 storage)
+  int round_bf16;   // head of a BF16 config: round to bf16, store as fp32
+  int cin, cout, k, stride;  // original tensor geometry
+  void* out;
+  double* norms;    // [d0]
+};
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
+
+// Latent / stage import: x fp32 [src_b][C][T_src] -> per output row r:
+//   frames [0, T) from source frames start[r] + t (t < len[r], else zero);
+//   s_out (operand dtype, chunked, optional Snake), h_out (fp32 chunked).
+struct ImportArgs {
+  const float* x;
+  int64_t T_src;
+  int C;
+  RowInfo rows;
+  int nrows;
+  int T;            // allocated frames per output row
+  int op;
+  void* s_out;      // may be null
+  const float* s_alpha;  // null -> identity
+  const float* s_invden;
+  float* h_out;     // may be null
+};
+hipError_t launch_import(const ImportArgs& a, hipStream_t s);
+
+// h fp32 chunked [rows][C/16][T][16] -> y fp32 [rows][C][T].
+hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipStream_t s);
+
+// Head: pcm[dst[r] + tau - keep_lo[r]] = tanh(bias + sum_j sum_i w[j][i] *
+//   Snake(h[r][tau + j - 3][i])) for tau in [keep_lo[r], keep_hi[r]).
+struct HeadArgs {
+  const float* h;   // fp32 chunked
+  int C, T;         // channels, allocated frames per row
+  RowInfo rows;
+  int nrows;
+  int rate;         // frames per latent frame
+  const float* alpha;
+  const float* invden;
+  const float* w;   // [7][C]
+  float bias;
+  float* pcm;
+};
+hipError_t launch_head(const HeadArgs& a, hipStream_t s);
+
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+
+}  // namespace voc

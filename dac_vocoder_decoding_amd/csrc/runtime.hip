@@ -1,0 +1,1051 @@
+// runtime.hip -- host side of libvocoder: the C ABI declared in vocoder.h.
+//
+// Validation, the exact tiling halo, weight ingestion (device-side fold and
+// repack), workspace management, the launch sequence of one decode, per-launch
+// profiling and the debug stage runner.  No exception crosses the ABI.
+#include "../../include/vocoder.h"
+#include "internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#define VOC_API extern "C" __attribute__((visibility("default")))
+
+using namespace voc;
+
+namespace {
+
+std::string g_create_error;
+
+struct SnakeDev {
+  float* alpha = nullptr;
+  float* invden = nullptr;
+};
+struct ConvDev {
+  void* w = nullptr;
+  float* bias = nullptr;
+  int cin = 0, cout = 0, taps = 0, dil = 1, ups = 1, crop = 0, M = 0;
+};
+struct UnitDev {
+  SnakeDev a1, a2;
+  ConvDev c1, c2;
+};
+struct BlockDev {
+  SnakeDev act;
+  ConvDev ct;
+  std::vector<UnitDev> units;
+};
+struct Weights {
+  ConvDev conv_in;
+  std::vector<BlockDev> blocks;
+  SnakeDev head_act;
+  float* head_w = nullptr;
+  float head_bias = 0.f;
+  std::vector<void*> allocs;
+};
+
+struct ProfRec {
+  int kind;
+  double flops, bytes;
+  hipEvent_t e0, e1;
+};
+
+}  // namespace
+
+struct voc_ctx {
+  voc_config cfg{};
+  int device = 0;
+  int op = OP_F32;
+  int64_t hop = 1;
+  int halo = 0;
+  std::string err;
+  bool loaded = false;
+  Weights W;
+  // workspace
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  size_t ws_cap = 0;
+  // profiling
+  bool prof = false;
+  std::vector<ProfRec> pending;
+  std::vector<hipEvent_t> free_events;
+  voc_profile_stat stats[VOC_K_COUNT]{};
+  // cached row metadata of the last decode
+  int64_t rows_B = -1, rows_T = -1;
+  int rows_n = 0;
+  std::vector<int64_t> meta_dst;  // host copies kept alive for async uploads
+  std::vector<int> meta_int;
+};
+
+namespace {
+
+voc_status fail(voc_ctx* c, voc_status st, const std::string& msg) {
+  if (c) c->err = msg; else g_create_error = msg;
+  return st;
+}
+
+voc_status hip_fail(voc_ctx* c, hipError_t e, const char* what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  return fail(c, e == hipErrorOutOfMemory ? VOC_OOM : VOC_DEVICE_ERROR, m);
+}
+
+int total_stride(const voc_config& c) {
+  int64_t h = 1;
+  for (int b = 0; b < c.n_blocks; ++b) h *= c.stride[b];
+  return static_cast<int>(h);
+}
+
+voc_status validate(const voc_config* c, std::string* why) {
+  auto bad = [&](const char* m) { if (why) *why = m; return VOC_INVALID_PARAMS; };
+  if (!c) return bad("config is NULL");
+  if (c->abi_version != VOC_ABI_VERSION) return bad("abi_version mismatch");
+  if (c->n_blocks < 1 || c->n_blocks > VOC_MAX_BLOCKS) return bad("n_blocks out of range");
+  if (c->n_res < 1 || c->n_res > VOC_MAX_RES) return bad("n_res out of range");
+  if (c->in_kernel != 7 || c->res_kernel != 7 || c->out_kernel != 7)
+    return bad("only kernel size 7 is supported for conv_in, conv1 and conv_out");
+  if (c->act != VOC_SNAKE && c->act != VOC_SNAKE_BETA) return bad("unknown act");
+  if (c->dtype != VOC_F32 && c->dtype != VOC_BF16) return bad("unknown dtype");
+  if (c->snake_log_params != 0 && c->snake_log_params != 1) return bad("snake_log_params must be 0 or 1");
+  if (c->convt_crop != 0) return bad("convt_crop must be 0");
+  if (c->tile_frames < 0) return bad("tile_frames must be >= 0");
+  const int q = c->dtype == VOC_F32 ? 16 : 32;
+  if (c->latent_channels <= 0 || c->latent_channels % q) return bad("latent_channels must be a positive multiple of 16 (F32) / 32 (BF16)");
+  for (int b = 0; b <= c->n_blocks; ++b)
+    if (c->width[b] <= 0 || c->width[b] % q || c->width[b] > 8192)
+      return bad("widths must be positive multiples of 16 (F32) / 32 (BF16), at most 8192");
+  if (c->width[c->n_blocks] > 512) return bad("the last width must be at most 512");
+  int64_t hop = 1;
+  for (int b = 0; b < c->n_blocks; ++b) {
+    if (c->stride[b] < 1 || c->stride[b] > 64) return bad("strides must be in [1, 64]");
+    hop *= c->stride[b];
+    if (hop > (1 << 20)) return bad("hop too large");
+  }
+  for (int r = 0; r < c->n_res; ++r)
+    if (c->dilation[r] < 1 || c->dilation[r] > 9) return bad("dilations must be in [1, 9]");
+  return VOC_OK;
+}
+
+int64_t floordiv(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// Smallest H such that, for every output sample of latent frame F, the
+// dependency interval at the input of every layer lies inside the frames the
+// tile [F - H, F + 1 + H) holds at that layer's rate.  Intervals are
+// propagated backwards: k=7 conv at dilation d widens by 3d each side;
+// ConvTranspose1d (stride s, k = 2s, crop p) maps outputs [lo, hi] to inputs
+// [ceil((lo + p - 2s + 1)/s), floor((hi + p)/s)].
+int compute_halo(const voc_config& c) {
+  const int64_t hop = total_stride(c);
+  const int64_t F = 4096;
+  std::vector<int64_t> rate(c.n_blocks + 1);
+  rate[0] = 1;
+  for (int b = 0; b < c.n_blocks; ++b) rate[b + 1] = rate[b] * c.stride[b];
+  for (int H = 0; H < 4096; ++H) {
+    bool ok = true;
+    for (int64_t ph = 0; ph < hop && ok; ++ph) {
+      int64_t lo = F * hop + ph, hi = lo;
+      auto inside = [&](int64_t R) { return lo >= (F - H) * R && hi < (F + 1 + H) * R; };
+      lo -= 3, hi += 3;  // head conv k=7
+      ok = ok && inside(rate[c.n_blocks]);
+      for (int b = c.n_blocks - 1; b >= 0 && ok; --b) {
+        for (int r = c.n_res - 1; r >= 0 && ok; --r) {
+          lo -= 3 * c.dilation[r], hi += 3 * c.dilation[r];
+          ok = inside(rate[b + 1]);
+        }
+        const int64_t s = c.stride[b], p = (s + 1) / 2;
+        lo = -floordiv(-(lo + p - 2 * s + 1), s);
+        hi = floordiv(hi + p, s);
+        ok = ok && inside(rate[b]);
+      }
+      lo -= 3, hi += 3;  // conv_in
+      ok = ok && inside(1);
+    }
+    if (ok) return H;
+  }
+  return -1;
+}
+
+// ------------------------------------------------------------- profiling
+hipEvent_t take_event(voc_ctx* c) {
+  if (!c->free_events.empty()) {
+    hipEvent_t e = c->free_events.back();
+    c->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+voc_status finalize_profile(voc_ctx* c) {
+  for (auto& r : c->pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.e0, r.e1);
+    if (e != hipSuccess) return hip_fail(c, e, "profile event");
+    auto& st = c->stats[r.kind];
+    st.launches += 1;
+    st.ms += ms;
+    st.flops += r.flops;
+    st.bytes += r.bytes;
+    c->free_events.push_back(r.e0);
+    c->free_events.push_back(r.e1);
+  }
+  c->pending.clear();
+  return VOC_OK;
+}
+
+// Launch wrapper: records events around the launch when profiling is on.
+template <class F>
+voc_status launch(voc_ctx* c, hipStream_t s, int kind, double flops, double bytes, const char* what,
+                  F&& fn) {
+  ProfRec rec{kind, flops, bytes, nullptr, nullptr};
+  if (c->prof) {
+    rec.e0 = take_event(c);
+    rec.e1 = take_event(c);
+    if (!rec.e0 || !rec.e1) return fail(c, VOC_DEVICE_ERROR, "hipEventCreate failed");
+    (void)hipEventRecord(rec.e0, s);
+  }
+  hipError_t e = fn();
+  if (e != hipSuccess) return hip_fail(c, e, what);
+  if (c->prof) {
+    (void)hipEventRecord(rec.e1, s);
+    c->pending.push_back(rec);
+  }
+  return VOC_OK;
+}
+
+// ------------------------------------------------------------- workspace
+struct Plan {
+  int rows, T;            // rows and allocated latent frames per row
+  size_t off_xlat, off_h, off_s0, off_s1, off_u, off_meta, bytes;
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+Plan make_plan(const voc_ctx* c, int rows, int T) {
+  const voc_config& g = c->cfg;
+  const size_t es = op_size(c->op);
+  size_t max_act = 0;
+  int64_t t = T;
+  max_act = std::max<size_t>(max_act, static_cast<size_t>(g.width[0]) * t);
+  for (int b = 0; b < g.n_blocks; ++b) {
+    t *= g.stride[b];
+    max_act = std::max<size_t>(max_act, static_cast<size_t>(g.width[b + 1]) * t);
+  }
+  Plan p{};
+  p.rows = rows;
+  p.T = T;
+  size_t o = 0;
+  p.off_xlat = o; o = align_up(o + es * rows * static_cast<size_t>(g.latent_channels) * T);
+  p.off_h = o;    o = align_up(o + 4 * rows * max_act);
+  p.off_s0 = o;   o = align_up(o + es * rows * max_act);
+  p.off_s1 = o;   o = align_up(o + es * rows * max_act);
+  p.off_u = o;    o = align_up(o + es * rows * max_act);
+  p.off_meta = o; o = align_up(o + static_cast<size_t>(rows) * (5 * sizeof(int) + sizeof(int64_t)) + 64);
+  p.bytes = o;
+  return p;
+}
+
+voc_status ensure_ws(voc_ctx* c, size_t bytes) {
+  if (bytes <= c->ws_bytes) return VOC_OK;
+  if (c->ws_cap && bytes > c->ws_cap)
+    return fail(c, VOC_OOM, "workspace of " + std::to_string(bytes) +
+                                " bytes exceeds VOC_MAX_WORKSPACE_BYTES");
+  if (c->ws) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(c->ws);
+    c->ws = nullptr;
+    c->ws_bytes = 0;
+  }
+  c->rows_B = -1;  // row metadata lived in the old workspace
+  hipError_t e = hipMalloc(&c->ws, bytes);
+  if (e != hipSuccess) {
+    c->ws = nullptr;
+    return hip_fail(c, e, "workspace hipMalloc");
+  }
+  c->ws_bytes = bytes;
+  return VOC_OK;
+}
+
+struct Bufs {
+  void* xlat;
+  float* h;
+  void* s[2];
+  void* u;
+  RowInfo rows;
+};
+
+Bufs bufs(voc_ctx* c, const Plan& p) {
+  char* b = static_cast<char*>(c->ws);
+  Bufs r{};
+  r.xlat = b + p.off_xlat;
+  r.h = reinterpret_cast<float*>(b + p.off_h);
+  r.s[0] = b + p.off_s0;
+  r.s[1] = b + p.off_s1;
+  r.u = b + p.off_u;
+  char* m = b + p.off_meta;
+  r.rows.dst = reinterpret_cast<const int64_t*>(m);
+  const int* ib = reinterpret_cast<const int*>(m + sizeof(int64_t) * p.rows);
+  r.rows.len = ib;
+  r.rows.src_b = ib + p.rows;
+  r.rows.start = ib + 2 * p.rows;
+  r.rows.keep_lo = ib + 3 * p.rows;
+  r.rows.keep_hi = ib + 4 * p.rows;
+  return r;
+}
+
+// Upload row metadata: rows = B * tiles; per row its window of the latent.
+// The host vectors are kept in the context until the next upload, so the
+// asynchronous copy never reads freed memory.
+voc_status upload_rows(voc_ctx* c, const Plan& p, std::vector<int64_t>&& dst_in,
+                       std::vector<int>&& ints_in, hipStream_t s) {
+  c->meta_dst = std::move(dst_in);
+  c->meta_int = std::move(ints_in);
+  const std::vector<int64_t>& dst = c->meta_dst;
+  const std::vector<int>& ints = c->meta_int;
+  char* m = static_cast<char*>(c->ws) + p.off_meta;
+  hipError_t e = hipMemcpyAsync(m, dst.data(), dst.size() * sizeof(int64_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(m + sizeof(int64_t) * p.rows, ints.data(), ints.size() * sizeof(int),
+                       hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(c, e, "row metadata upload");
+  return VOC_OK;
+}
+
+// ------------------------------------------------------------ conv launch
+int pick_variant(int taps, int M, int N, int rows) {
+  // Prefer the larger tiles while they still give about two workgroups per CU.
+  const int cands[3] = {CV_64x256, CV_128x128, CV_64x128};
+  for (int v : cands) {
+    if (!conv_variant_ok(v, taps)) continue;
+    const int64_t tiles = static_cast<int64_t>((M + conv_variant_bm(v) - 1) / conv_variant_bm(v)) *
+                          ((N + conv_variant_bn(v) - 1) / conv_variant_bn(v)) * rows;
+    if (tiles >= 512) return v;
+  }
+  return CV_64x128;
+}
+
+struct ConvIO {
+  const void* x;
+  int T_in;     // allocated frames per row of x
+  int rate_in;  // frames per latent frame of x
+  float* h_out;
+  const float* res;
+  void* s_out;
+  const SnakeDev* snake_next;  // Snake applied for s_out
+};
+
+voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, const int* row_len,
+                    int kind, hipStream_t s) {
+  ConvArgs a{};
+  a.x = io.x;
+  a.T_in = io.T_in;
+  a.Cin = L.cin;
+  a.row_len = row_len;
+  a.rate_in = io.rate_in;
+  a.rate_out = io.rate_in * L.ups;
+  a.w = L.w;
+  a.M = L.M;
+  a.Cout = L.cout;
+  if (L.taps == 2) {  // polyphase ConvTranspose1d: taps at x[q], x[q-1]
+    a.off0 = 0;
+    a.offstep = -1;
+    a.min_off = -1;
+    a.halo = 1;
+    a.N = io.T_in + 1;
+  } else {
+    const int P = (L.taps - 1) / 2 * L.dil;
+    a.off0 = -P;
+    a.offstep = L.dil;
+    a.min_off = -P;
+    a.halo = 2 * P;
+    a.N = io.T_in;
+  }
+  a.T_out = io.T_in * L.ups;
+  a.ups = L.ups;
+  a.crop = L.crop;
+  a.bias = L.bias;
+  a.h_out = io.h_out;
+  a.res = io.res;
+  a.s_out = io.s_out;
+  a.s_alpha = io.snake_next ? io.snake_next->alpha : nullptr;
+  a.s_invden = io.snake_next ? io.snake_next->invden : nullptr;
+  a.rows = rows;
+  const int v = pick_variant(L.taps, L.M, a.N, rows);
+  a.n_tiles = (a.N + conv_variant_bn(v) - 1) / conv_variant_bn(v);
+  a.m_tiles = (a.M + conv_variant_bm(v) - 1) / conv_variant_bm(v);
+  // Algorithmic work: every input frame meets every tap (direct convolution).
+  const double frames_in = static_cast<double>(rows) * io.T_in;
+  const double flops = 2.0 * frames_in * L.cin * L.cout * (L.taps == 2 ? 2 * L.ups : L.taps);
+  const double es = op_size(c->op);
+  const double frames_out = frames_in * L.ups;
+  double bytes = frames_in * L.cin * es + static_cast<double>(L.taps) * L.M * L.cin * es;
+  if (io.h_out) bytes += frames_out * L.cout * 4;
+  if (io.res) bytes += frames_out * L.cout * 4;
+  if (io.s_out) bytes += frames_out * L.cout * es;
+  const int op = c->op;
+  return launch(c, s, kind, flops, bytes, "conv launch",
+                [&] { return launch_conv(op, L.taps, v, a, s); });
+}
+
+voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const RowInfo& rows,
+                      int nrows, int T, void* s_out, const SnakeDev* sn, float* h_out,
+                      hipStream_t s) {
+  ImportArgs a{};
+  a.x = x;
+  a.T_src = T_src;
+  a.C = C;
+  a.rows = rows;
+  a.nrows = nrows;
+  a.T = T;
+  a.op = c->op;
+  a.s_out = s_out;
+  a.s_alpha = sn ? sn->alpha : nullptr;
+  a.s_invden = sn ? sn->invden : nullptr;
+  a.h_out = h_out;
+  const double el = static_cast<double>(nrows) * T * C;
+  const double bytes = el * 4 + (s_out ? el * op_size(c->op) : 0) + (h_out ? el * 4 : 0);
+  return launch(c, s, VOC_K_IMPORT, 0.0, bytes, "import launch", [&] { return launch_import(a, s); });
+}
+
+voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int nrows, int rate,
+                    float* pcm, hipStream_t s) {
+  HeadArgs a{};
+  const voc_config& g = c->cfg;
+  a.h = h;
+  a.C = g.width[g.n_blocks];
+  a.T = T;
+  a.rows = rows;
+  a.nrows = nrows;
+  a.rate = rate;
+  a.alpha = c->W.head_act.alpha;
+  a.invden = c->W.head_act.invden;
+  a.w = c->W.head_w;
+  a.bias = c->W.head_bias;
+  a.pcm = pcm;
+  const double frames = static_cast<double>(nrows) * T;
+  const double flops = 2.0 * frames * a.C * 7;
+  const double bytes = frames * a.C * 4 + frames * 4;
+  return launch(c, s, VOC_K_HEAD, flops, bytes, "head launch", [&] { return launch_head(a, s); });
+}
+
+const SnakeDev* next_snake(const Weights& W, int b, int r, int nb, int nr) {
+  if (r + 1 < nr) return &W.blocks[b].units[r + 1].a1;
+  if (b + 1 < nb) return &W.blocks[b + 1].act;
+  return nullptr;
+}
+
+// The whole decoder over `rows` rows of T latent frames (already imported
+// into xlat).  Leaves the last residual stream in B.h.
+voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s) {
+  const voc_config& g = c->cfg;
+  const Weights& W = c->W;
+  const int nb = g.n_blocks, nr = g.n_res;
+  int cur = 0;
+  ConvIO io{};
+  io.x = B.xlat;
+  io.T_in = T;
+  io.rate_in = 1;
+  io.h_out = B.h;
+  io.s_out = B.s[cur];
+  io.snake_next = &W.blocks[0].act;
+  voc_status st = run_conv(c, W.conv_in, io, rows, B.rows.len, VOC_K_CONV_IN, s);
+  if (st) return st;
+  int t = T, rate = 1;
+  for (int b = 0; b < nb; ++b) {
+    const BlockDev& blk = W.blocks[b];
+    io = ConvIO{};
+    io.x = B.s[cur];
+    io.T_in = t;
+    io.rate_in = rate;
+    io.h_out = B.h;
+    io.s_out = B.s[cur ^ 1];
+    io.snake_next = &blk.units[0].a1;
+    st = run_conv(c, blk.ct, io, rows, B.rows.len, VOC_K_CONVT, s);
+    if (st) return st;
+    cur ^= 1;
+    t *= g.stride[b];
+    rate *= g.stride[b];
+    for (int r = 0; r < nr; ++r) {
+      const UnitDev& u = blk.units[r];
+      io = ConvIO{};
+      io.x = B.s[cur];
+      io.T_in = t;
+      io.rate_in = rate;
+      io.s_out = B.u;
+      io.snake_next = &u.a2;
+      st = run_conv(c, u.c1, io, rows, B.rows.len, VOC_K_RES_K7, s);
+      if (st) return st;
+      io = ConvIO{};
+      io.x = B.u;
+      io.T_in = t;
+      io.rate_in = rate;
+      io.h_out = B.h;
+      io.res = B.h;
+      io.snake_next = next_snake(W, b, r, nb, nr);
+      io.s_out = io.snake_next ? B.s[cur] : nullptr;
+      st = run_conv(c, u.c2, io, rows, B.rows.len, VOC_K_RES_K1, s);
+      if (st) return st;
+    }
+  }
+  return VOC_OK;
+}
+
+// ----------------------------------------------------------- weight names
+struct Expect {
+  std::vector<int64_t> shape;  // squeezed (size-1 dims removed)
+};
+
+std::vector<int64_t> squeeze(const int64_t* shape, int nd) {
+  std::vector<int64_t> v;
+  for (int i = 0; i < nd; ++i)
+    if (shape[i] != 1) v.push_back(shape[i]);
+  return v;
+}
+
+std::map<std::string, Expect> expected_tensors(const voc_config& g) {
+  std::map<std::string, Expect> m;
+  auto sq = [](std::vector<int64_t> v) {
+    std::vector<int64_t> r;
+    for (auto x : v)
+      if (x != 1) r.push_back(x);
+    return r;
+  };
+  auto conv = [&](const std::string& p, int64_t d0, int64_t d1, int64_t k, int64_t nbias) {
+    m[p + ".weight_v"] = {sq({d0, d1, k})};
+    m[p + ".weight_g"] = {sq({d0})};
+    m[p + ".bias"] = {sq({nbias})};
+  };
+  auto snake = [&](const std::string& p, int64_t ch) {
+    m[p + ".alpha"] = {sq({ch})};
+    if (g.act == VOC_SNAKE_BETA) m[p + ".beta"] = {sq({ch})};
+  };
+  conv("conv_in", g.width[0], g.latent_channels, 7, g.width[0]);
+  for (int b = 0; b < g.n_blocks; ++b) {
+    const std::string p = "blocks." + std::to_string(b);
+    const int cin = g.width[b], cout = g.width[b + 1];
+    snake(p + ".snake1", cin);
+    conv(p + ".conv_t1", cin, cout, 2 * g.stride[b], cout);
+    for (int r = 0; r < g.n_res; ++r) {
+      const std::string q = p + ".res_units." + std::to_string(r);
+      snake(q + ".snake1", cout);
+      conv(q + ".conv1", cout, cout, 7, cout);
+      snake(q + ".snake2", cout);
+      conv(q + ".conv2", cout, cout, 1, cout);
+    }
+  }
+  snake("snake_out", g.width[g.n_blocks]);
+  conv("conv_out", 1, g.width[g.n_blocks], 7, 1);
+  return m;
+}
+
+bool all_finite(const float* p, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (!std::isfinite(p[i])) return false;
+  return true;
+}
+
+int64_t numel(const voc_tensor& t) {
+  int64_t n = 1;
+  for (int i = 0; i < t.ndim; ++i) n *= t.shape[i];
+  return n;
+}
+
+void free_weights(Weights& W) {
+  for (void* p : W.allocs) (void)hipFree(p);
+  W = Weights{};
+}
+
+}  // namespace
+
+// =================================================================== ABI
+
+VOC_API void voc_config_default(voc_config* cfg) {
+  if (!cfg) return;
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->abi_version = VOC_ABI_VERSION;
+  cfg->latent_channels = 64;
+  cfg->n_blocks = 4;
+  const int w[5] = {1024, 512, 256, 128, 64};
+  const int st[4] = {8, 8, 4, 2};
+  for (int i = 0; i < 5; ++i) cfg->width[i] = w[i];
+  for (int i = 0; i < 4; ++i) cfg->stride[i] = st[i];
+  cfg->in_kernel = cfg->res_kernel = cfg->out_kernel = 7;
+  cfg->n_res = 3;
+  cfg->dilation[0] = 1;
+  cfg->dilation[1] = 3;
+  cfg->dilation[2] = 9;
+  cfg->act = VOC_SNAKE;
+  cfg->dtype = VOC_F32;
+}
+
+VOC_API voc_status voc_config_validate(const voc_config* cfg) { return validate(cfg, nullptr); }
+
+VOC_API int64_t voc_config_hop(const voc_config* cfg) {
+  if (validate(cfg, nullptr) != VOC_OK) return VOC_INVALID_PARAMS;
+  return total_stride(*cfg);
+}
+
+VOC_API int voc_config_halo(const voc_config* cfg) {
+  if (validate(cfg, nullptr) != VOC_OK) return VOC_INVALID_PARAMS;
+  return compute_halo(*cfg);
+}
+
+VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx** out) {
+  if (!out) return fail(nullptr, VOC_INVALID_PARAMS, "out is NULL");
+  *out = nullptr;
+  std::string why;
+  if (validate(cfg, &why) != VOC_OK) return fail(nullptr, VOC_INVALID_PARAMS, why);
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev <= 0) return fail(nullptr, VOC_DEVICE_ERROR, "no HIP device");
+  if (hip_device < 0 || hip_device >= ndev) return fail(nullptr, VOC_INVALID_PARAMS, "bad device index");
+  e = hipSetDevice(hip_device);
+  if (e != hipSuccess) return fail(nullptr, VOC_DEVICE_ERROR, "hipSetDevice failed");
+  voc_ctx* c = new (std::nothrow) voc_ctx();
+  if (!c) return fail(nullptr, VOC_OOM, "host allocation failed");
+  c->cfg = *cfg;
+  c->device = hip_device;
+  c->op = cfg->dtype == VOC_F32 ? OP_F32 : OP_BF16;
+  c->hop = total_stride(*cfg);
+  c->halo = compute_halo(*cfg);
+  if (const char* cap = std::getenv("VOC_MAX_WORKSPACE_BYTES")) c->ws_cap = std::strtoull(cap, nullptr, 10);
+  *out = c;
+  return VOC_OK;
+}
+
+VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) {
+  if (!c) return VOC_INVALID_PARAMS;
+  if (!t || n <= 0) return fail(c, VOC_INVALID_PARAMS, "no tensors");
+  const voc_config& g = c->cfg;
+  auto exp = expected_tensors(g);
+  std::map<std::string, const voc_tensor*> got;
+  for (int i = 0; i < n; ++i) {
+    if (!t[i].name || !t[i].data) return fail(c, VOC_INVALID_PARAMS, "tensor with NULL name or data");
+    if (t[i].ndim < 0 || t[i].ndim > 4) return fail(c, VOC_BAD_WEIGHTS, std::string("bad ndim: ") + t[i].name);
+    auto it = exp.find(t[i].name);
+    if (it == exp.end()) return fail(c, VOC_BAD_WEIGHTS, std::string("unknown tensor: ") + t[i].name);
+    if (got.count(t[i].name)) return fail(c, VOC_BAD_WEIGHTS, std::string("duplicate tensor: ") + t[i].name);
+    if (squeeze(t[i].shape, t[i].ndim) != it->second.shape)
+      return fail(c, VOC_BAD_WEIGHTS, std::string("shape mismatch: ") + t[i].name);
+    got[t[i].name] = &t[i];
+  }
+  for (auto& kv : exp)
+    if (!got.count(kv.first)) return fail(c, VOC_BAD_WEIGHTS, "missing tensor: " + kv.first);
+  // Small tensors are checked on the host; weight_v through its norm.
+  for (auto& kv : got) {
+    const std::string& nm = kv.first;
+    if (nm.size() > 9 && nm.compare(nm.size() - 9, 9, ".weight_v") == 0) continue;
+    if (!all_finite(kv.second->data, numel(*kv.second)))
+      return fail(c, VOC_BAD_WEIGHTS, "non-finite value in " + nm);
+  }
+
+  Weights W;
+  std::vector<void*> staging;  // v, g and norm buffers, freed after the fold
+  const int op = c->op;
+  std::vector<double*> norm_bufs;
+  std::vector<std::pair<std::string, int64_t>> norm_names;
+  auto dalloc = [&](size_t bytes, void** p) -> voc_status {
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+      *p = nullptr;
+      return hip_fail(c, e, "weight hipMalloc");
+    }
+    W.allocs.push_back(*p);
+    return VOC_OK;
+  };
+  auto upload = [&](const float* h, size_t count, float** d, bool stage = false) -> voc_status {
+    voc_status st = dalloc(count * 4, reinterpret_cast<void**>(d));
+    if (st) return st;
+    if (stage) {
+      W.allocs.pop_back();
+      staging.push_back(*d);
+    }
+    hipError_t e = hipMemcpy(*d, h, count * 4, hipMemcpyHostToDevice);
+    return e == hipSuccess ? VOC_OK : hip_fail(c, e, "weight upload");
+  };
+  auto snake = [&](const std::string& p, int ch, SnakeDev* sd) -> voc_status {
+    const float* a = got[p + ".alpha"]->data;
+    const float* b = g.act == VOC_SNAKE_BETA ? got[p + ".beta"]->data : nullptr;
+    std::vector<float> al(ch), iv(ch);
+    for (int i = 0; i < ch; ++i) {
+      double av = a[i], dv = b ? b[i] : a[i];
+      if (g.snake_log_params) av = std::exp(av), dv = std::exp(dv);
+      const double inv = 1.0 / (dv + 1e-9);
+      al[i] = static_cast<float>(av);
+      iv[i] = static_cast<float>(inv);
+      if (!std::isfinite(al[i]) || !std::isfinite(iv[i]))
+        return fail(c, VOC_BAD_WEIGHTS, "Snake parameter gives a non-finite value in " + p);
+    }
+    voc_status st = upload(al.data(), ch, &sd->alpha);
+    if (st) return st;
+    return upload(iv.data(), ch, &sd->invden);
+  };
+  // Fold one conv: v is uploaded to a staging buffer, folded into the packed layout.
+  auto fold = [&](const std::string& p, int kind, int cin, int cout, int k, int stride,
+                  void** out_w, float** out_bias) -> voc_status {
+    const voc_tensor* tv = got[p + ".weight_v"];
+    const voc_tensor* tg = got[p + ".weight_g"];
+    const int64_t cnt = numel(*tv);
+    const int64_t d0 = kind == PACK_CONVT ? cin : cout;
+    float *dv = nullptr, *dg = nullptr;
+    voc_status st = upload(tv->data, cnt, &dv, true);
+    if (st) return st;
+    st = upload(tg->data, d0, &dg, true);
+    if (st) return st;
+    double* dn = nullptr;
+    st = dalloc(d0 * sizeof(double), reinterpret_cast<void**>(&dn));
+    if (st) return st;
+    W.allocs.pop_back();
+    staging.push_back(dn);
+    const size_t es = kind == PACK_HEAD ? 4 : op_size(op);
+    st = dalloc(cnt * es, out_w);
+    if (st) return st;
+    FoldArgs fa{};
+    fa.v = dv;
+    fa.g = dg;
+    fa.d0 = d0;
+    fa.rest = cnt / d0;
+    fa.kind = kind;
+    fa.op = kind == PACK_HEAD ? OP_F32 : op;
+    fa.round_bf16 = kind == PACK_HEAD && op == OP_BF16;
+    fa.cin = cin;
+    fa.cout = cout;
+    fa.k = k;
+    fa.stride = stride;
+    fa.out = *out_w;
+    fa.norms = dn;
+    hipError_t e = launch_fold(fa, nullptr);
+    if (e != hipSuccess) return hip_fail(c, e, "fold launch");
+    norm_bufs.push_back(dn);
+    norm_names.push_back({p, d0});
+    if (out_bias) return upload(got[p + ".bias"]->data, cout, out_bias);
+    return VOC_OK;
+  };
+
+  auto build = [&]() -> voc_status {
+    voc_status st;
+    ConvDev& ci = W.conv_in;
+    ci.cin = g.latent_channels;
+    ci.cout = ci.M = g.width[0];
+    ci.taps = 7;
+    st = fold("conv_in", PACK_CONV, ci.cin, ci.cout, 7, 1, &ci.w, &ci.bias);
+    if (st) return st;
+    W.blocks.resize(g.n_blocks);
+    for (int b = 0; b < g.n_blocks; ++b) {
+      const std::string p = "blocks." + std::to_string(b);
+      BlockDev& blk = W.blocks[b];
+      const int cin = g.width[b], cout = g.width[b + 1], s = g.stride[b];
+      st = snake(p + ".snake1", cin, &blk.act);
+      if (st) return st;
+      blk.ct.cin = cin;
+      blk.ct.cout = cout;
+      blk.ct.taps = 2;
+      blk.ct.ups = s;
+      blk.ct.crop = (s + 1) / 2;
+      blk.ct.M = s * cout;
+      st = fold(p + ".conv_t1", PACK_CONVT, cin, cout, 2 * s, s, &blk.ct.w, &blk.ct.bias);
+      if (st) return st;
+      blk.units.resize(g.n_res);
+      for (int r = 0; r < g.n_res; ++r) {
+        const std::string q = p + ".res_units." + std::to_string(r);
+        UnitDev& u = blk.units[r];
+        st = snake(q + ".snake1", cout, &u.a1);
+        if (st) return st;
+        st = snake(q + ".snake2", cout, &u.a2);
+        if (st) return st;
+        u.c1.cin = u.c1.cout = u.c1.M = cout;
+        u.c1.taps = 7;
+        u.c1.dil = g.dilation[r];
+        st = fold(q + ".conv1", PACK_CONV, cout, cout, 7, 1, &u.c1.w, &u.c1.bias);
+        if (st) return st;
+        u.c2.cin = u.c2.cout = u.c2.M = cout;
+        u.c2.taps = 1;
+        st = fold(q + ".conv2", PACK_CONV, cout, cout, 1, 1, &u.c2.w, &u.c2.bias);
+        if (st) return st;
+      }
+    }
+    st = snake("snake_out", g.width[g.n_blocks], &W.head_act);
+    if (st) return st;
+    void* hw = nullptr;
+    st = fold("conv_out", PACK_HEAD, g.width[g.n_blocks], 1, 7, 1, &hw, nullptr);
+    if (st) return st;
+    W.head_w = static_cast<float*>(hw);
+    W.head_bias = got["conv_out.bias"]->data[0];
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(c, e, "fold");
+    for (size_t i = 0; i < norm_bufs.size(); ++i) {
+      std::vector<double> nv(norm_names[i].second);
+      e = hipMemcpy(nv.data(), norm_bufs[i], nv.size() * sizeof(double), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(c, e, "norm readback");
+      for (double x : nv)
+        if (!(x > 0.0) || !std::isfinite(x))
+          return fail(c, VOC_BAD_WEIGHTS, "zero or non-finite ||v|| in " + norm_names[i].first);
+    }
+    return VOC_OK;
+  };
+  voc_status st = build();
+  (void)hipDeviceSynchronize();
+  for (void* q : staging) (void)hipFree(q);
+  if (st != VOC_OK) {
+    free_weights(W);
+    return st;
+  }
+  free_weights(c->W);
+  c->W = W;
+  c->loaded = true;
+  c->err.clear();
+  return VOC_OK;
+}
+
+VOC_API int64_t vocoder_output_length(const voc_ctx* c, int64_t T) {
+  if (!c || T < 0) return -1;
+  return T * c->hop;
+}
+
+VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, int64_t T, float* pcm,
+                                  void* stream) {
+  if (!c) return VOC_INVALID_PARAMS;
+  if (!latent || !pcm) return fail(c, VOC_INVALID_PARAMS, "NULL latent or pcm");
+  if ((reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(pcm)) & 15)
+    return fail(c, VOC_INVALID_PARAMS, "latent and pcm must be 16-byte aligned");
+  if (B <= 0 || T <= 0) return fail(c, VOC_INVALID_PARAMS, "B and T must be positive");
+  if (T * c->hop > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "T*hop exceeds 2^31-1");
+  if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const voc_config& g = c->cfg;
+  // Rows: whole rows, or tiles of tile_frames latent frames with halos.
+  const int64_t F = g.tile_frames > 0 ? g.tile_frames : T;
+  const int64_t ntile = (T + F - 1) / F;
+  const int64_t rows = B * ntile;
+  if (rows > 65535) return fail(c, VOC_INVALID_PARAMS, "too many rows (B * tiles > 65535)");
+  const int H = g.tile_frames > 0 ? c->halo : 0;
+  int T_alloc = static_cast<int>(std::min<int64_t>(T, F + 2 * H));
+  int64_t work_rows_frames = 0;
+  std::vector<int64_t> dst(rows);
+  std::vector<int> ints(5 * rows);
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t k = 0; k < ntile; ++k) {
+      const int64_t r = b * ntile + k;
+      const int64_t t0 = k * F, t1 = std::min(T, t0 + F);
+      const int64_t a = std::max<int64_t>(0, t0 - H), e = std::min(T, t1 + H);
+      ints[r] = static_cast<int>(e - a);                          // len
+      ints[rows + r] = static_cast<int>(b);                       // src_b
+      ints[2 * rows + r] = static_cast<int>(a);                   // start
+      ints[3 * rows + r] = static_cast<int>((t0 - a) * c->hop);   // keep_lo
+      ints[4 * rows + r] = static_cast<int>((t1 - a) * c->hop);   // keep_hi
+      dst[r] = b * T * c->hop + t0 * c->hop;
+      work_rows_frames += e - a;
+    }
+  (void)work_rows_frames;
+  const Plan p = make_plan(c, static_cast<int>(rows), T_alloc);
+  voc_status st = ensure_ws(c, p.bytes);
+  if (st) return st;
+  if (c->rows_B != B || c->rows_T != T || c->rows_n != rows) {
+    st = upload_rows(c, p, std::move(dst), std::move(ints), s);
+    if (st) return st;
+    c->rows_B = B;
+    c->rows_T = T;
+    c->rows_n = static_cast<int>(rows);
+  }
+  const Bufs Bf = bufs(c, p);
+  st = run_import(c, latent, T, g.latent_channels, Bf.rows, static_cast<int>(rows), T_alloc, Bf.xlat,
+                  nullptr, nullptr, s);
+  if (st) return st;
+  st = run_stack(c, Bf, static_cast<int>(rows), T_alloc, s);
+  if (st) return st;
+  return run_head(c, Bf.h, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
+                  static_cast<int>(c->hop), pcm, s);
+}
+
+VOC_API const char* vocoder_last_error(const voc_ctx* c) {
+  return c ? c->err.c_str() : g_create_error.c_str();
+}
+
+VOC_API void vocoder_destroy(voc_ctx* c) {
+  if (!c) return;
+  (void)hipSetDevice(c->device);
+  (void)hipDeviceSynchronize();
+  free_weights(c->W);
+  if (c->ws) (void)hipFree(c->ws);
+  for (auto& r : c->pending) {
+    (void)hipEventDestroy(r.e0);
+    (void)hipEventDestroy(r.e1);
+  }
+  for (auto e : c->free_events) (void)hipEventDestroy(e);
+  delete c;
+}
+
+VOC_API voc_status vocoder_profile_enable(voc_ctx* c, int enable) {
+  if (!c) return VOC_INVALID_PARAMS;
+  c->prof = enable != 0;
+  return VOC_OK;
+}
+
+VOC_API voc_status vocoder_profile_reset(voc_ctx* c) {
+  if (!c) return VOC_INVALID_PARAMS;
+  voc_status st = finalize_profile(c);
+  for (auto& s : c->stats) s = voc_profile_stat{};
+  return st;
+}
+
+VOC_API voc_status vocoder_profile_read(voc_ctx* c, int kind, voc_profile_stat* out) {
+  if (!c || !out || kind < 0 || kind >= VOC_K_COUNT) return VOC_INVALID_PARAMS;
+  voc_status st = finalize_profile(c);
+  if (st) return st;
+  *out = c->stats[kind];
+  return VOC_OK;
+}
+
+// ------------------------------------------------------------------ debug
+
+namespace {
+struct StageInfo {
+  int kind;  // 0 conv_in, 1 convT, 2 res unit, 3 head
+  int b, r;
+  int c_in, c_out, ups;
+};
+bool stage_info(const voc_ctx* c, int k, StageInfo* si) {
+  const voc_config& g = c->cfg;
+  const int n = 2 + g.n_blocks * (1 + g.n_res);
+  if (k < 0 || k >= n) return false;
+  if (k == 0) {
+    *si = {0, 0, 0, g.latent_channels, g.width[0], 1};
+    return true;
+  }
+  if (k == n - 1) {
+    *si = {3, 0, 0, g.width[g.n_blocks], 1, 1};
+    return true;
+  }
+  const int b = (k - 1) / (1 + g.n_res), j = (k - 1) % (1 + g.n_res);
+  if (j == 0)
+    *si = {1, b, 0, g.width[b], g.width[b + 1], g.stride[b]};
+  else
+    *si = {2, b, j - 1, g.width[b + 1], g.width[b + 1], 1};
+  return true;
+}
+}  // namespace
+
+VOC_API int voc_dbg_stage_count(const voc_ctx* c) {
+  return c ? 2 + c->cfg.n_blocks * (1 + c->cfg.n_res) : VOC_INVALID_PARAMS;
+}
+
+VOC_API voc_status voc_dbg_stage_shape(const voc_ctx* c, int stage, int64_t T_in, int64_t* c_in,
+                                       int64_t* c_out, int64_t* t_out) {
+  StageInfo si;
+  if (!c || !c_in || !c_out || !t_out || !stage_info(c, stage, &si)) return VOC_INVALID_PARAMS;
+  *c_in = si.c_in;
+  *c_out = si.c_out;
+  *t_out = T_in * si.ups;
+  return VOC_OK;
+}
+
+VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int64_t B, int64_t T_in,
+                                     float* out, void* stream) {
+  if (!c) return VOC_INVALID_PARAMS;
+  StageInfo si;
+  if (!stage_info(c, stage, &si)) return fail(c, VOC_INVALID_PARAMS, "bad stage index");
+  if (!in || !out || B <= 0 || T_in <= 0 || B > 65535) return fail(c, VOC_INVALID_PARAMS, "bad stage arguments");
+  if ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(c, VOC_INVALID_PARAMS, "buffers must be 16-byte aligned");
+  if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  const int64_t t_out = T_in * si.ups;
+  if (t_out > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "T too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rows = static_cast<int>(B);
+  // Workspace: enough for the stage's input and output at these frames; the
+  // row metadata treats each row as a whole clip of T_in frames at rate 1.
+  const int64_t cmax = std::max(si.c_in, si.c_out);
+  const size_t es = op_size(c->op);
+  const size_t act_in = static_cast<size_t>(rows) * si.c_in * T_in;
+  const size_t act_out = static_cast<size_t>(rows) * cmax * t_out;
+  size_t o = 0;
+  const size_t off_h = o; o = align_up(o + 4 * std::max(act_in, act_out));
+  const size_t off_s0 = o; o = align_up(o + es * act_in);
+  const size_t off_s1 = o; o = align_up(o + es * act_out);
+  const size_t off_u = o; o = align_up(o + es * act_out);
+  const size_t off_meta = o; o = align_up(o + rows * (5 * sizeof(int) + sizeof(int64_t)) + 64);
+  voc_status st = ensure_ws(c, o);
+  if (st) return st;
+  char* base = static_cast<char*>(c->ws);
+  float* h = reinterpret_cast<float*>(base + off_h);
+  void* s0 = base + off_s0;
+  void* s1 = base + off_s1;
+  void* u = base + off_u;
+  Plan p{};
+  p.rows = rows;
+  p.off_meta = off_meta;
+  std::vector<int64_t> dst(rows);
+  std::vector<int> ints(5 * rows);
+  for (int r = 0; r < rows; ++r) {
+    ints[r] = static_cast<int>(T_in);
+    ints[rows + r] = r;
+    ints[2 * rows + r] = 0;
+    ints[3 * rows + r] = 0;
+    ints[4 * rows + r] = static_cast<int>(T_in);
+    dst[r] = static_cast<int64_t>(r) * T_in;
+  }
+  st = upload_rows(c, p, std::move(dst), std::move(ints), s);
+  if (st) return st;
+  c->rows_B = -1;  // the decode's cached metadata is gone
+  char* m = base + off_meta;
+  RowInfo ri{};
+  ri.dst = reinterpret_cast<const int64_t*>(m);
+  const int* ib = reinterpret_cast<const int*>(m + sizeof(int64_t) * rows);
+  ri.len = ib;
+  ri.src_b = ib + rows;
+  ri.start = ib + 2 * rows;
+  ri.keep_lo = ib + 3 * rows;
+  ri.keep_hi = ib + 4 * rows;
+  const Weights& W = c->W;
+  const int T = static_cast<int>(T_in);
+  ConvIO io{};
+  switch (si.kind) {
+    case 0:
+      st = run_import(c, in, T_in, si.c_in, ri, rows, T, s0, nullptr, nullptr, s);
+      if (st) return st;
+      io.x = s0; io.T_in = T; io.rate_in = 1; io.h_out = h;
+      st = run_conv(c, W.conv_in, io, rows, ri.len, VOC_K_CONV_IN, s);
+      break;
+    case 1:
+      st = run_import(c, in, T_in, si.c_in, ri, rows, T, s0, &W.blocks[si.b].act, nullptr, s);
+      if (st) return st;
+      io.x = s0; io.T_in = T; io.rate_in = 1; io.h_out = h;
+      st = run_conv(c, W.blocks[si.b].ct, io, rows, ri.len, VOC_K_CONVT, s);
+      break;
+    case 2: {
+      const UnitDev& un = W.blocks[si.b].units[si.r];
+      st = run_import(c, in, T_in, si.c_in, ri, rows, T, s0, &un.a1, h, s);
+      if (st) return st;
+      io.x = s0; io.T_in = T; io.rate_in = 1; io.s_out = u; io.snake_next = &un.a2;
+      st = run_conv(c, un.c1, io, rows, ri.len, VOC_K_RES_K7, s);
+      if (st) return st;
+      io = ConvIO{};
+      io.x = u; io.T_in = T; io.rate_in = 1; io.h_out = h; io.res = h;
+      st = run_conv(c, un.c2, io, rows, ri.len, VOC_K_RES_K1, s);
+      break;
+    }
+    default:
+      st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s);
+      if (st) return st;
+      return run_head(c, h, T, ri, rows, 1, out, s);
+  }
+  (void)s1;
+  if (st) return st;
+  return launch(c, s, VOC_K_EXPORT, 0.0, 8.0 * rows * si.c_out * t_out, "export launch",
+                [&] { return launch_export(h, out, rows, si.c_out, static_cast<int>(t_out), s); });
+}
+
+VOC_API voc_status voc_dbg_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (!dst || !src || bytes <= 0 || (bytes & 15) ||
+      ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15))
+    return VOC_INVALID_PARAMS;
+  hipError_t e = launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? VOC_OK : VOC_DEVICE_ERROR;
+}

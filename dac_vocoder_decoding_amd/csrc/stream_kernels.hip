@@ -1,0 +1,264 @@
+// stream_kernels.hip -- the bandwidth-bound kernels of libvocoder:
+//   fold_kernel    weight-norm fold (fp64 norms), cast and repack (load time)
+//   import_kernel  [row][C][T] fp32 -> chunked operand / residual layouts,
+//                  with the tile gather of time-tiled decoding
+//   export_kernel  chunked fp32 -> [row][C][T] (debug stage runner)
+//   head_kernel    Snake -> Conv1d k=7 to one channel -> bias -> tanh, with
+//                  the tile crop folded into the store
+//   copy_kernel    plain 16-byte vector copy (byte-counter calibration)
+#include "internal.h"
+#include "device_math.h"
+
+namespace voc {
+
+// ---------------------------------------------------------------- fold
+// Weight norm (minimaxmusic.cpp ARCHITECTURE, "Models"): w = g v / ||v||,
+// the norm over each slice along axis 0 of the stored tensor.  One workgroup
+// per slice; the sum of squares is accumulated in fp64.  The folded value is
+// rounded fp64 -> fp32 (the F32 inference weights), then for bf16 operands
+// to bf16 (round to nearest even), and written at its packed position.
+__global__ __launch_bounds__(256) void fold_kernel(const FoldArgs a) {
+  __shared__ double red[256];
+  const int64_t i = blockIdx.x;
+  const float* v = a.v + i * a.rest;
+  double ss = 0.0;
+  for (int64_t e = threadIdx.x; e < a.rest; e += 256) {
+    const double x = v[e];
+    ss += x * x;
+  }
+  red[threadIdx.x] = ss;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const double n = sqrt(red[0]);
+  if (threadIdx.x == 0) a.norms[i] = n;
+  const double g = a.g[i];
+  const int ch = a.op == OP_F32 ? 16 : 32;
+  for (int64_t e = threadIdx.x; e < a.rest; e += 256) {
+    const float wf = static_cast<float>(g * static_cast<double>(v[e]) / n);
+    int64_t idx;
+    if (a.kind == PACK_CONV) {  // (Cout, Cin, K), slice = o
+      const int ci = static_cast<int>(e / a.k), kk = static_cast<int>(e % a.k);
+      idx = ((static_cast<int64_t>(ci / ch) * a.k + kk) * a.cout + i) * ch + ci % ch;
+    } else if (a.kind == PACK_CONVT) {  // (Cin, Cout, 2s), slice = ci
+      const int o = static_cast<int>(e / (2 * a.stride));
+      const int kk = static_cast<int>(e % (2 * a.stride));
+      const int t = kk / a.stride, r = kk % a.stride;
+      const int64_t M = static_cast<int64_t>(a.stride) * a.cout;
+      idx = ((static_cast<int64_t>(i / ch) * 2 + t) * M + static_cast<int64_t>(r) * a.cout + o) * ch +
+            i % ch;
+    } else {  // PACK_HEAD (1, C, K) -> fp32 [K][C]
+      const int ci = static_cast<int>(e / a.k), kk = static_cast<int>(e % a.k);
+      static_cast<float*>(a.out)[static_cast<int64_t>(kk) * a.cin + ci] =
+          a.round_bf16 ? bf16_round(wf) : wf;
+      continue;
+    }
+    if (a.op == OP_F32)
+      static_cast<float*>(a.out)[idx] = wf;
+    else
+      static_cast<uint16_t*>(a.out)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(wf));
+  }
+}
+
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(fold_kernel, dim3(static_cast<unsigned>(a.d0)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- import
+// Tile of 64 frames x 16 channels: coalesced reads along time, then writes
+// of 4 consecutive channels per thread into the chunked layouts.
+template <int OP>
+__global__ __launch_bounds__(256) void import_kernel(const ImportArgs a) {
+  constexpr int CH = OP == OP_F32 ? 16 : 32;
+  __shared__ float tile[16][65];
+  const int r = blockIdx.y;
+  const int cblocks = a.C / 16;
+  const int c0 = (blockIdx.x % cblocks) * 16;
+  const int t0 = (blockIdx.x / cblocks) * 64;
+  const int len = min(a.rows.len[r], a.T);
+  const int sb = a.rows.src_b[r];
+  const int64_t st = a.rows.start[r];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = i * 4 + (tid >> 6), t = tid & 63;
+    const int tt = t0 + t;
+    float v = 0.f;
+    if (tt < len) v = a.x[(static_cast<int64_t>(sb) * a.C + c0 + c) * a.T_src + st + tt];
+    tile[c][t] = v;
+  }
+  __syncthreads();
+  const int t = tid >> 2, c = (tid & 3) * 4;
+  const int tt = t0 + t;
+  if (tt >= a.T) return;
+  f4 v;
+  v[0] = tile[c][t];
+  v[1] = tile[c + 1][t];
+  v[2] = tile[c + 2][t];
+  v[3] = tile[c + 3][t];
+  const int cc = c0 + c;
+  if (a.h_out) {
+    const int64_t hidx = (static_cast<int64_t>(r) * a.C + (cc & ~15)) * a.T +
+                         static_cast<int64_t>(tt) * kHChunk + (cc & 15);
+    *reinterpret_cast<f4*>(a.h_out + hidx) = v;
+  }
+  if (a.s_out) {
+    if (a.s_alpha) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = snake_f32(v[e], a.s_alpha[cc + e], a.s_invden[cc + e]);
+    }
+    const int64_t sidx = (static_cast<int64_t>(r) * a.C + (cc / CH) * CH) * a.T +
+                         static_cast<int64_t>(tt) * CH + cc % CH;
+    store_op4<OP>(a.s_out, sidx, v);
+  }
+}
+
+hipError_t launch_import(const ImportArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.C / 16) * ((a.T + 63) / 64)),
+                  static_cast<unsigned>(a.nrows));
+  if (a.op == OP_F32)
+    hipLaunchKernelGGL(import_kernel<OP_F32>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(import_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- export
+__global__ __launch_bounds__(256) void export_kernel(const float* h, float* y, int C, int T) {
+  __shared__ float tile[16][65];
+  const int r = blockIdx.y;
+  const int cblocks = C / 16;
+  const int c0 = (blockIdx.x % cblocks) * 16;
+  const int t0 = (blockIdx.x / cblocks) * 64;
+  const int tid = threadIdx.x;
+  {
+    const int t = tid >> 2, c = (tid & 3) * 4;
+    const int tt = t0 + t;
+    f4 v = f4{0.f, 0.f, 0.f, 0.f};
+    if (tt < T)
+      v = *reinterpret_cast<const f4*>(h + (static_cast<int64_t>(r) * C + c0) * T +
+                                       static_cast<int64_t>(tt) * kHChunk + c);
+    tile[c][t] = v[0];
+    tile[c + 1][t] = v[1];
+    tile[c + 2][t] = v[2];
+    tile[c + 3][t] = v[3];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = i * 4 + (tid >> 6), t = tid & 63;
+    const int tt = t0 + t;
+    if (tt < T) y[(static_cast<int64_t>(r) * C + c0 + c) * T + tt] = tile[c][t];
+  }
+}
+
+hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((C / 16) * ((T + 63) / 64)), static_cast<unsigned>(rows));
+  hipLaunchKernelGGL(export_kernel, grid, dim3(256), 0, s, h, y, C, T);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- head
+// Output head (minimaxmusic.cpp ARCHITECTURE, "Flow VAE": snake_out, conv_out
+// k=7 with bias, tanh).  A workgroup takes TT output frames: it stages
+// Snake(h) for frames [t0-3, t0+TT+3) in LDS, computes the seven per-tap
+// projections z_j[f] = sum_i w[j][i] S[f][i] once per staged frame, then
+// y[t] = tanh(bias + sum_j z_j[t + j - 3]).  Frames outside the row's valid
+// range read as zero (Snake(0) = 0, the conv's zero padding).
+__global__ __launch_bounds__(256) void head_kernel(const HeadArgs a, int TT) {
+  extern __shared__ float sm[];
+  const int C = a.C;
+  const int SR = C + 4;  // padded LDS row
+  const int F = TT + 6;
+  float* S = sm;
+  float* Z = sm + F * SR;
+  const int r = blockIdx.y;
+  const int lo = a.rows.keep_lo[r], hi = a.rows.keep_hi[r];
+  const int t0 = lo + blockIdx.x * TT;
+  if (t0 >= hi) return;
+  const int Lr = min(a.rows.len[r] * a.rate, a.T);
+  const int tid = threadIdx.x;
+  const int per_chunk = F * 4;
+  const int units = per_chunk * (C / 16);
+  for (int u = tid; u < units; u += 256) {
+    const int k = u / per_chunk, rem = u - k * per_chunk;
+    const int f = rem >> 2, q = rem & 3;
+    const int c = k * 16 + q * 4;
+    const int tt = t0 - 3 + f;
+    f4 v = f4{0.f, 0.f, 0.f, 0.f};
+    if (tt >= 0 && tt < Lr) {
+      v = *reinterpret_cast<const f4*>(a.h + (static_cast<int64_t>(r) * C + k * 16) * a.T +
+                                       static_cast<int64_t>(tt) * kHChunk + q * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = snake_f32(v[e], a.alpha[c + e], a.invden[c + e]);
+    }
+    *reinterpret_cast<f4*>(S + f * SR + c) = v;
+  }
+  __syncthreads();
+  for (int f = tid; f < F; f += 256) {
+    float z[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float* srow = S + f * SR;
+    for (int c = 0; c < C; c += 4) {
+      const f4 x = *reinterpret_cast<const f4*>(srow + c);
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        const f4 w = *reinterpret_cast<const f4*>(a.w + j * C + c);
+        z[j] = fmaf(w[0], x[0], z[j]);
+        z[j] = fmaf(w[1], x[1], z[j]);
+        z[j] = fmaf(w[2], x[2], z[j]);
+        z[j] = fmaf(w[3], x[3], z[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 7; ++j) Z[j * F + f] = z[j];
+  }
+  __syncthreads();
+  const int64_t dst = a.rows.dst[r] - lo;
+  for (int t = tid; t < TT; t += 256) {
+    const int tt = t0 + t;
+    if (tt >= hi) break;
+    float y = a.bias;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) y += Z[j * F + t + j];
+    a.pcm[dst + tt] = tanhf(y);
+  }
+}
+
+static int head_tile(int C) {
+  // Largest TT (<= 128) whose LDS footprint fits 60 KB.
+  int tt = 128;
+  while (tt > 8 && ((tt + 6) * (C + 4) + 7 * (tt + 6)) * 4 > 60 * 1024) tt >>= 1;
+  return tt;
+}
+
+hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
+  const int TT = head_tile(a.C);
+  int max_keep = 0;
+  // keep ranges are host-known via T; the grid covers the allocated frames.
+  max_keep = a.T;
+  const dim3 grid(static_cast<unsigned>((max_keep + TT - 1) / TT), static_cast<unsigned>(a.nrows));
+  const size_t lds = static_cast<size_t>((TT + 6) * (a.C + 4) + 7 * (TT + 6)) * 4;
+  hipLaunchKernelGGL(head_kernel, grid, dim3(256), lds, s, a, TT);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- copy
+__global__ __launch_bounds__(256) void copy_kernel(uint4* dst, const uint4* src, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s) {
+  const int64_t n = bytes / 16;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n);
+  return hipGetLastError();
+}
+
+}  // namespace voc

@@ -1,0 +1,293 @@
+"""Thin ctypes binding of libvocoder.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls (include/vocoder.h)
+and returns the C status code (0 = VOC_OK, negative = error) unless noted.
+Device buffers are passed as torch CUDA tensors (their data_ptr()), streams
+as torch streams or raw hipStream_t integers.  All computation happens in
+the HIP library; this module fails loudly if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvocoder.so")
+
+VOC_ABI_VERSION = 1
+VOC_MAX_BLOCKS = 8
+VOC_MAX_RES = 4
+
+VOC_OK = 0
+VOC_INVALID_PARAMS = -1
+VOC_BAD_WEIGHTS = -2
+VOC_OOM = -3
+VOC_DEVICE_ERROR = -4
+VOC_NOT_LOADED = -5
+
+VOC_F32, VOC_BF16 = 0, 1
+VOC_SNAKE, VOC_SNAKE_BETA = 0, 1
+
+KERNEL_KINDS = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export"]
+
+
+class voc_config(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int),
+        ("latent_channels", ctypes.c_int),
+        ("n_blocks", ctypes.c_int),
+        ("width", ctypes.c_int * (VOC_MAX_BLOCKS + 1)),
+        ("stride", ctypes.c_int * VOC_MAX_BLOCKS),
+        ("in_kernel", ctypes.c_int),
+        ("res_kernel", ctypes.c_int),
+        ("out_kernel", ctypes.c_int),
+        ("n_res", ctypes.c_int),
+        ("dilation", ctypes.c_int * VOC_MAX_RES),
+        ("act", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("snake_log_params", ctypes.c_int),
+        ("convt_crop", ctypes.c_int),
+        ("tile_frames", ctypes.c_int),
+    ]
+
+
+class voc_tensor(ctypes.Structure):
+    _fields_ = [
+        ("name", ctypes.c_char_p),
+        ("data", ctypes.POINTER(ctypes.c_float)),
+        ("ndim", ctypes.c_int),
+        ("shape", ctypes.c_int64 * 4),
+    ]
+
+
+class voc_profile_stat(ctypes.Structure):
+    _fields_ = [
+        ("launches", ctypes.c_int64),
+        ("ms", ctypes.c_double),
+        ("flops", ctypes.c_double),
+        ("bytes", ctypes.c_double),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libvocoder.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m dac_vocoder_decoding_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        CFG = ctypes.POINTER(voc_config)
+        sig = {
+            "voc_config_default": (None, [CFG]),
+            "voc_config_validate": (I, [CFG]),
+            "voc_config_hop": (I64, [CFG]),
+            "voc_config_halo": (I, [CFG]),
+            "vocoder_create": (I, [CFG, I, ctypes.POINTER(P)]),
+            "vocoder_load_weights": (I, [P, ctypes.POINTER(voc_tensor), I]),
+            "vocoder_output_length": (I64, [P, I64]),
+            "vocoder_decode": (I, [P, P, I64, I64, P, P]),
+            "vocoder_last_error": (ctypes.c_char_p, [P]),
+            "vocoder_destroy": (None, [P]),
+            "vocoder_profile_enable": (I, [P, I]),
+            "vocoder_profile_reset": (I, [P]),
+            "vocoder_profile_read": (I, [P, I, ctypes.POINTER(voc_profile_stat)]),
+            "voc_dbg_stage_count": (I, [P]),
+            "voc_dbg_stage_shape": (I, [P, I, I64, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                        ctypes.POINTER(I64)]),
+            "voc_dbg_run_stage": (I, [P, I, P, I64, I64, P, P]),
+            "voc_dbg_copy": (I, [P, P, I64, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class VocError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+# ------------------------------------------------------------------ config
+def config_from_dict(d: dict) -> voc_config:
+    """voc_config for an architecture dict (keys as in inputs.CONFIGS)."""
+    c = voc_config()
+    lib().voc_config_default(ctypes.byref(c))
+    c.latent_channels = d["latent_channels"]
+    c.n_blocks = len(d["strides"])
+    for i, w in enumerate(d["widths"]):
+        c.width[i] = w
+    for i, s in enumerate(d["strides"]):
+        c.stride[i] = s
+    c.in_kernel = c.res_kernel = c.out_kernel = d.get("kernel", 7)
+    c.n_res = len(d["dilations"])
+    for i, dl in enumerate(d["dilations"]):
+        c.dilation[i] = dl
+    c.act = VOC_SNAKE_BETA if d["act"] == "snakebeta" else VOC_SNAKE
+    c.dtype = VOC_BF16 if d["dtype"] == "bf16" else VOC_F32
+    c.snake_log_params = d.get("snake_log_params", 0)
+    c.tile_frames = d.get("tile_frames", 0)
+    return c
+
+
+def voc_config_default() -> voc_config:
+    c = voc_config()
+    lib().voc_config_default(ctypes.byref(c))
+    return c
+
+
+def voc_config_validate(cfg: voc_config) -> int:
+    return lib().voc_config_validate(ctypes.byref(cfg))
+
+
+def voc_config_hop(cfg: voc_config) -> int:
+    return lib().voc_config_hop(ctypes.byref(cfg))
+
+
+def voc_config_halo(cfg: voc_config) -> int:
+    return lib().voc_config_halo(ctypes.byref(cfg))
+
+
+# ----------------------------------------------------------------- context
+def vocoder_create(cfg: voc_config, device: int = 0):
+    """Returns (status, ctx)."""
+    ctx = ctypes.c_void_p()
+    st = lib().vocoder_create(ctypes.byref(cfg), device, ctypes.byref(ctx))
+    return st, ctx
+
+
+def vocoder_load_weights(ctx, tensors: dict) -> int:
+    """tensors: name -> float32 numpy array (host)."""
+    arrs = {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in tensors.items()}
+    items = (voc_tensor * len(arrs))()
+    keep = []
+    for i, (k, v) in enumerate(arrs.items()):
+        name = k.encode()
+        keep.append(name)
+        items[i].name = name
+        items[i].data = v.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+        items[i].ndim = v.ndim
+        for j, s in enumerate(v.shape):
+            items[i].shape[j] = s
+    st = lib().vocoder_load_weights(ctx, items, len(arrs))
+    del keep
+    return st
+
+
+def vocoder_output_length(ctx, T: int) -> int:
+    return lib().vocoder_output_length(ctx, T)
+
+
+def vocoder_decode(ctx, latent, B: int, T: int, pcm, stream=None) -> int:
+    return lib().vocoder_decode(ctx, _ptr(latent), B, T, _ptr(pcm), _stream(stream))
+
+
+def vocoder_last_error(ctx) -> str:
+    r = lib().vocoder_last_error(ctx)
+    return r.decode() if r else ""
+
+
+def vocoder_destroy(ctx) -> None:
+    lib().vocoder_destroy(ctx)
+
+
+def vocoder_profile_enable(ctx, enable: bool) -> int:
+    return lib().vocoder_profile_enable(ctx, int(bool(enable)))
+
+
+def vocoder_profile_reset(ctx) -> int:
+    return lib().vocoder_profile_reset(ctx)
+
+
+def vocoder_profile_read(ctx, kind: int):
+    """Returns (status, dict(launches, ms, flops, bytes))."""
+    s = voc_profile_stat()
+    st = lib().vocoder_profile_read(ctx, kind, ctypes.byref(s))
+    return st, dict(launches=s.launches, ms=s.ms, flops=s.flops, bytes=s.bytes)
+
+
+def voc_dbg_stage_count(ctx) -> int:
+    return lib().voc_dbg_stage_count(ctx)
+
+
+def voc_dbg_stage_shape(ctx, stage: int, T_in: int):
+    """Returns (status, c_in, c_out, t_out)."""
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = lib().voc_dbg_stage_shape(ctx, stage, T_in, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return st, a.value, b.value, c.value
+
+
+def voc_dbg_run_stage(ctx, stage: int, x, B: int, T_in: int, out, stream=None) -> int:
+    return lib().voc_dbg_run_stage(ctx, stage, _ptr(x), B, T_in, _ptr(out), _stream(stream))
+
+
+def voc_dbg_copy(dst, src, nbytes: int, stream=None) -> int:
+    return lib().voc_dbg_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream))
+
+
+def check(st: int, ctx=None) -> None:
+    """Raise VocError for a non-zero status, with the context's last error."""
+    if st != VOC_OK:
+        raise VocError(st, vocoder_last_error(ctx))
+
+
+# ---------------------------------------------------- marshalling helpers
+def open_context(cfg_dict: dict, tensors: dict, device: int = 0, **overrides):
+    """vocoder_create + vocoder_load_weights; raises VocError on failure."""
+    cfg = config_from_dict({**cfg_dict, **overrides})
+    st, ctx = vocoder_create(cfg, device)
+    check(st)
+    st = vocoder_load_weights(ctx, tensors)
+    if st != VOC_OK:
+        msg = vocoder_last_error(ctx)
+        vocoder_destroy(ctx)
+        raise VocError(st, msg)
+    return ctx
+
+
+def decode(ctx, latent, stream=None):
+    """pcm [B, 1, T*hop] (new CUDA tensor) for a CUDA fp32 latent [B, C, T]."""
+    import torch
+    assert latent.is_cuda and latent.dtype == torch.float32 and latent.is_contiguous()
+    b, _, t = latent.shape
+    pcm = torch.empty(b, 1, vocoder_output_length(ctx, t), device=latent.device)
+    check(vocoder_decode(ctx, latent, b, t, pcm, stream), ctx)
+    return pcm
+
+
+def run_stage(ctx, stage: int, x, stream=None):
+    """Output of debug stage `stage` for a CUDA fp32 input [B, C_in, T]."""
+    import torch
+    assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous()
+    b, _, t = x.shape
+    st, _, c_out, t_out = voc_dbg_stage_shape(ctx, stage, t)
+    check(st, ctx)
+    out = torch.empty(b, c_out, t_out, device=x.device)
+    check(voc_dbg_run_stage(ctx, stage, x, b, t, out, stream), ctx)
+    return out

@@ -1,0 +1,224 @@
+/*
+ * vocoder.h -- C ABI of the MI355X DAC-style waveform decoder (libvocoder.so).
+ *
+ * Plain C99, no C++ or PyTorch types.  Every entry point returns a voc_status
+ * (0 = success, negative = error) unless stated otherwise, never throws, and
+ * records a human-readable message retrievable with vocoder_last_error().
+ *
+ * The decoder (minimaxmusic.cpp ARCHITECTURE page, section "Flow VAE"; the
+ * DAC stack of the qwentts.cpp ARCHITECTURE page, "Audio tokenizer decoder"):
+ *
+ *   h   = conv_in(latent)                       Conv1d k=7, zero "same" padding, bias
+ *   per block b with stride s:
+ *     h = conv_t1(Snake(h))                     ConvTranspose1d k=2s, stride s, crop ceil(s/2)
+ *     per residual unit with dilation d (1, 3, 9):
+ *       h = h + conv2(Snake2(conv1_d(Snake1(h))))   conv1 k=7 dilation d, conv2 k=1
+ *   pcm = tanh(conv_out(Snake(h)))              Conv1d k=7 to one channel, bias
+ *
+ *   Snake(x)     = x + sin^2(alpha x) / (alpha + 1e-9)   alpha read verbatim
+ *   SnakeBeta(x) = x + sin^2(alpha x) / (beta  + 1e-9)
+ *
+ * Weight norm is folded once at load: w = g * v / ||v||, the norm taken over
+ * each slice along axis 0 of the stored tensor (minimaxmusic.cpp ARCHITECTURE,
+ * "Models").
+ *
+ * Stereo: the 128 latent channels of a stereo track are two independent
+ * 64-channel tracks, channels 0..63 left (minimaxmusic.cpp ARCHITECTURE,
+ * "Flow VAE").  A caller holding [b, 128, t] passes the view [2b, 64, t]
+ * (rows 2i = left, 2i+1 = right) and reads the [2b, 1, N] output as [b, 2, N].
+ *
+ * Conventions follow the qwentts.cpp public ABI (ARCHITECTURE page, "Public
+ * API" and "ABI guarantee"): an opaque context, a parameter struct carrying
+ * abi_version, a status enum, a last-error string, extern "C" with only these
+ * symbols exported.
+ *
+ * Threading: one context per host thread / stream.  A context is not safe for
+ * concurrent calls.
+ */
+#ifndef VOCODER_H
+#define VOCODER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VOC_ABI_VERSION 1
+#define VOC_MAX_BLOCKS 8
+#define VOC_MAX_RES 4
+
+typedef struct voc_ctx voc_ctx;
+
+typedef enum voc_status {
+  VOC_OK = 0,
+  VOC_INVALID_PARAMS = -1, /* bad config, shape, pointer or size            */
+  VOC_BAD_WEIGHTS = -2,    /* missing/unknown/mis-shaped tensor, ||v|| = 0,  */
+                           /* or a non-finite value                          */
+  VOC_OOM = -3,            /* device allocation failed or exceeds the cap    */
+  VOC_DEVICE_ERROR = -4,   /* a HIP call or kernel launch failed             */
+  VOC_NOT_LOADED = -5      /* decode before a successful load_weights        */
+} voc_status;
+
+typedef enum voc_dtype {
+  VOC_F32 = 0,  /* fp32 weights and matrix-core operands, fp32 accumulate   */
+  VOC_BF16 = 1  /* bf16 weights (cast after the fold) and bf16 operands,    */
+                /* fp32 accumulate, fp32 residual stream and epilogues       */
+} voc_dtype;
+
+typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
+
+/*
+ * Architecture description.  Constraints (checked by voc_config_validate):
+ * abi_version == VOC_ABI_VERSION; 1 <= n_blocks <= VOC_MAX_BLOCKS;
+ * 1 <= n_res <= VOC_MAX_RES; 1 <= dilation[r] <= 9; stride[b] >= 1;
+ * in_kernel == res_kernel == out_kernel == 7; widths and latent_channels
+ * positive multiples of 16 (F32) or 32 (BF16), width[n_blocks] <= 512;
+ * convt_crop == 0; tile_frames >= 0.
+ */
+typedef struct voc_config {
+  int abi_version;
+  int latent_channels;             /* C of the latent                          */
+  int n_blocks;                    /* upsampling blocks                         */
+  int width[VOC_MAX_BLOCKS + 1];   /* width[0] = conv_in output, width[b+1] =   */
+                                   /* block b output                            */
+  int stride[VOC_MAX_BLOCKS];      /* block strides; ConvTranspose1d k = 2*s    */
+  int in_kernel, res_kernel, out_kernel;
+  int n_res;                       /* residual units per block                  */
+  int dilation[VOC_MAX_RES];       /* their conv1 dilations                     */
+  int act;                         /* voc_act                                   */
+  int dtype;                       /* voc_dtype                                 */
+  int snake_log_params;            /* 0: alpha/beta used as given; 1: the       */
+                                   /* stored values are logs, exp() at load     */
+  int convt_crop;                  /* 0: keep full[n + ceil(s/2)], n < T*s      */
+                                   /* (other values reserved)                   */
+  int tile_frames;                 /* 0: decode whole rows; F > 0: decode time  */
+                                   /* tiles of F latent frames with exact halos */
+} voc_config;
+
+/* Fill *cfg with the full-width stereo window decoder: latent 64, widths
+ * 1024/512/256/128/64, strides 8,8,4,2, dilations 1,3,9, Snake, F32, untiled. */
+void voc_config_default(voc_config *cfg);
+
+/* Host-only checks of *cfg (no device is touched). */
+voc_status voc_config_validate(const voc_config *cfg);
+
+/* Samples per latent frame (product of the strides), or a negative status. */
+int64_t voc_config_hop(const voc_config *cfg);
+
+/* Exact receptive-field halo H in latent frames (host-only): decoding latent
+ * frames [t0-H, t1+H) (clamped to the clip) reproduces the untiled output on
+ * samples [t0*hop, t1*hop).  Negative status if *cfg is invalid. */
+int voc_config_halo(const voc_config *cfg);
+
+/* Create a context on HIP device hip_device.  Validates *cfg first (no device
+ * call happens if it is invalid).  *out receives the context or NULL. */
+voc_status vocoder_create(const voc_config *cfg, int hip_device, voc_ctx **out);
+
+/*
+ * One named host tensor, fp32, contiguous, caller-owned.  Names and shapes
+ * (PyTorch conventions; size-1 dims may be dropped, e.g. g as [d0] or
+ * [d0,1,1], alpha as [C] or [1,C,1]):
+ *   conv_in.{weight_v [W0,Clat,7], weight_g [W0,1,1], bias [W0]}
+ *   blocks.{b}.snake1.alpha [1,Wb,1]          (+ .beta for SnakeBeta)
+ *   blocks.{b}.conv_t1.{weight_v [Wb,Wb+1,2s], weight_g [Wb,1,1], bias [Wb+1]}
+ *   blocks.{b}.res_units.{r}.snake1.alpha, .conv1.{weight_v [W,W,7], weight_g, bias},
+ *                           .snake2.alpha, .conv2.{weight_v [W,W,1], weight_g, bias}
+ *   snake_out.alpha [1,Wn,1];  conv_out.{weight_v [1,Wn,7], weight_g [1,1,1], bias [1]}
+ */
+typedef struct voc_tensor {
+  const char *name;
+  const float *data;
+  int ndim;
+  int64_t shape[4];
+} voc_tensor;
+
+/*
+ * Copy the n tensors to the device, fold weight norm there (fp64 norms),
+ * cast (BF16 configs: fp64 -> fp32 -> bf16, round to nearest even), precompute
+ * 1/(alpha+1e-9) or 1/(beta+1e-9), and repack into the kernels' layouts.
+ * All-or-nothing: on any error the previously loaded weights (if any) stay
+ * in place.  Synchronizes the device.  Errors: VOC_BAD_WEIGHTS (missing,
+ * duplicate, unknown or mis-shaped tensor; ||v|| = 0; non-finite value),
+ * VOC_INVALID_PARAMS (NULL pointers), VOC_OOM, VOC_DEVICE_ERROR.
+ */
+voc_status vocoder_load_weights(voc_ctx *ctx, const voc_tensor *tensors, int n);
+
+/* Output samples per row for T latent frames (T * hop), or -1 on bad input. */
+int64_t vocoder_output_length(const voc_ctx *ctx, int64_t T);
+
+/*
+ * Decode latent (device, fp32, [B, latent_channels, T] contiguous) into pcm
+ * (device, fp32, [B, 1, T*hop] contiguous) on hip_stream (a hipStream_t;
+ * NULL = the null stream).  Asynchronous: enqueues kernels and returns; no
+ * host synchronization except when the library-owned workspace has to grow
+ * (hipMalloc), the first time a larger B*T is seen.  Both buffers stay owned
+ * by the caller and must be 16-byte aligned.  BF16 configs round the latent
+ * to bf16 as a matrix-core operand.  With tile_frames > 0 the rows are cut
+ * into tiles of tile_frames latent frames plus the exact halo on each side
+ * and all tiles are decoded as one batch.
+ * Errors: VOC_INVALID_PARAMS (NULL/misaligned pointers, B or T <= 0, sizes
+ * beyond 2^31 elements per row), VOC_NOT_LOADED, VOC_OOM, VOC_DEVICE_ERROR.
+ */
+voc_status vocoder_decode(voc_ctx *ctx, const float *latent, int64_t B, int64_t T,
+                          float *pcm, void *hip_stream);
+
+/* Message of the last error on ctx ("" if none); valid until the next call on
+ * ctx.  With ctx == NULL, the message of the last failed vocoder_create. */
+const char *vocoder_last_error(const voc_ctx *ctx);
+
+/* Release the context, its device weights and workspace.  NULL-safe.  The
+ * caller must have synchronized the streams it decoded on. */
+void vocoder_destroy(voc_ctx *ctx);
+
+/* ------------------------------------------------------------ profiling
+ * When enabled, every kernel launch of vocoder_decode and voc_dbg_run_stage
+ * is bracketed by two hipEvents recorded on the launch stream, and the
+ * algorithmic work of the launch (direct-convolution flops, minimum HBM
+ * bytes) is recorded beside them.  vocoder_profile_read synchronizes on the
+ * recorded events and returns totals per kernel kind since the last reset. */
+typedef enum voc_kernel_kind {
+  VOC_K_CONV_IN = 0,  /* conv_in implicit GEMM                          */
+  VOC_K_CONVT = 1,    /* polyphase ConvTranspose1d GEMM                 */
+  VOC_K_RES_K7 = 2,   /* residual unit conv1 (k=7, dilated) GEMM        */
+  VOC_K_RES_K1 = 3,   /* residual unit conv2 (k=1) GEMM + residual add  */
+  VOC_K_HEAD = 4,     /* Snake + Conv1d to one channel + tanh           */
+  VOC_K_IMPORT = 5,   /* latent transpose / tile gather                 */
+  VOC_K_EXPORT = 6,   /* debug-stage output transpose                   */
+  VOC_K_COUNT = 7
+} voc_kernel_kind;
+
+typedef struct voc_profile_stat {
+  int64_t launches;
+  double ms;          /* summed event time of the launches               */
+  double flops;       /* summed algorithmic flops                        */
+  double bytes;       /* summed minimum HBM bytes (inputs+outputs+weights) */
+} voc_profile_stat;
+
+voc_status vocoder_profile_enable(voc_ctx *ctx, int enable);
+voc_status vocoder_profile_reset(voc_ctx *ctx);
+voc_status vocoder_profile_read(voc_ctx *ctx, int kind, voc_profile_stat *out);
+
+/* ---------------------------------------------------- debug (not ABI-stable)
+ * Stage k of the decoder on caller buffers, for teacher-forced checks:
+ *   0 = conv_in; for block b: 1 + b*(1+n_res) = Snake + ConvTranspose1d,
+ *   the next n_res indices = its residual units; count-1 = the head.
+ * in: device fp32 [B, C_in(k), T_in] (stage 0: the latent); out: device fp32
+ * [B, C_out(k), T_out] (head: [B, 1, T_in]).  Uses the same kernels as
+ * vocoder_decode, untiled.  Asynchronous on hip_stream. */
+int voc_dbg_stage_count(const voc_ctx *ctx);
+voc_status voc_dbg_stage_shape(const voc_ctx *ctx, int stage, int64_t T_in,
+                               int64_t *c_in, int64_t *c_out, int64_t *t_out);
+voc_status voc_dbg_run_stage(voc_ctx *ctx, int stage, const float *in, int64_t B,
+                             int64_t T_in, float *out, void *hip_stream);
+
+/* A plain device-to-device copy of `bytes` bytes (16-byte vector loads and
+ * stores), used to calibrate HBM byte counters.  bytes must be a multiple
+ * of 16 and both pointers 16-byte aligned. */
+voc_status voc_dbg_copy(void *dst, const void *src, int64_t bytes, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VOCODER_H */

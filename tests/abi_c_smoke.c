@@ -1,0 +1,48 @@
+/* Plain C99 consumer of include/vocoder.h: compiled with -std=c99 -Wall
+ * -Werror -pedantic and run without a GPU.  Calls every entry point through
+ * an early-return (validation) path; never touches a device. */
+#include <stdio.h>
+#include <string.h>
+#include "vocoder.h"
+
+#define EXPECT(cond)                                              \
+  do {                                                            \
+    if (!(cond)) {                                                \
+      fprintf(stderr, "FAIL line %d: %s\n", __LINE__, #cond);     \
+      return 1;                                                   \
+    }                                                             \
+  } while (0)
+
+int main(void) {
+  voc_config cfg;
+  voc_ctx *ctx = (voc_ctx *)0;
+  voc_profile_stat st;
+  int64_t a, b, c;
+  float dummy[4];
+  voc_config_default(&cfg);
+  EXPECT(cfg.abi_version == VOC_ABI_VERSION);
+  EXPECT(voc_config_validate(&cfg) == VOC_OK);
+  EXPECT(voc_config_hop(&cfg) == 512);
+  EXPECT(voc_config_halo(&cfg) == 10);
+  EXPECT(voc_config_validate(NULL) == VOC_INVALID_PARAMS);
+  cfg.abi_version = VOC_ABI_VERSION + 1;
+  EXPECT(voc_config_validate(&cfg) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_create(&cfg, 0, &ctx) == VOC_INVALID_PARAMS);
+  EXPECT(ctx == (voc_ctx *)0);
+  EXPECT(strlen(vocoder_last_error(NULL)) > 0);
+  EXPECT(vocoder_create(NULL, 0, &ctx) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_create(&cfg, 0, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_load_weights(NULL, NULL, 0) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_output_length(NULL, 5) == -1);
+  EXPECT(vocoder_decode(NULL, dummy, 1, 1, dummy, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_profile_enable(NULL, 1) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_profile_reset(NULL) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_profile_read(NULL, 0, &st) == VOC_INVALID_PARAMS);
+  EXPECT(voc_dbg_stage_count(NULL) == VOC_INVALID_PARAMS);
+  EXPECT(voc_dbg_stage_shape(NULL, 0, 1, &a, &b, &c) == VOC_INVALID_PARAMS);
+  EXPECT(voc_dbg_run_stage(NULL, 0, dummy, 1, 1, dummy, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(voc_dbg_copy(NULL, dummy, 16, NULL) == VOC_INVALID_PARAMS);
+  vocoder_destroy(NULL);
+  puts("abi ok");
+  return 0;
+}
