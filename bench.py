@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Throughput of the DAC-style waveform decoder on one MI355X.
+
+One step = one full decode (conv_in, 4 upsampling blocks with 3 residual
+units each, head) of one batch of synthetic latents, with the latent, the
+weights and the output buffer already resident in HBM.
+
+Prints ONE JSON line: audio-seconds decoded per second (value), whole-decode
+TFLOP/s, the roofline of the dominant kernel measured live with HIP events
+recorded on the decode stream by the library's per-launch profiler over the
+timed steps, and the CPU oracle timed on a bounded sample of the same
+workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "audio-seconds decoded/sec (44.1 kHz stereo) + TFLOP/s as % of MFMA peak"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+KIND_NAMES = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export"]
+KERNEL_SOURCES = ["dac_vocoder_decoding_amd/csrc/conv_gemm.hip",
+                  "dac_vocoder_decoding_amd/csrc/device_math.h",
+                  "dac_vocoder_decoding_amd/csrc/internal.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_name(cfg: dict) -> str:
+    lat = f"[{cfg['batch']},{cfg['latent_channels']},{cfg['frames']}]"
+    w = "/".join(str(x) for x in cfg["widths"])
+    s = ",".join(str(x) for x in cfg["strides"])
+    tile = f", time tiles of {cfg['tile_frames']} frames" if cfg["tile_frames"] else ""
+    return (f"{cfg['name']}: latent {lat} {cfg['dtype']}, widths {w}, strides {s}, "
+            f"{cfg['act']}{tile}")
+
+
+def traffic_for(workload_key: str, kind: str):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    --pmc FETCH_SIZE / WRITE_SIZE runs, scaled by a copy-kernel calibration;
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload_key, {}).get(kind)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg: dict, tensors: dict, latent, target_s: float = 15.0) -> dict:
+    """The oracle (fp64 direct loops, OpenMP) on a bounded time slice of the
+    same workload: one stereo pair (or one mono row) of the first frames."""
+    from dac_vocoder_decoding_amd import inputs as I
+    from oracle import oracle as O
+    rows = 2 if cfg["stereo"] else 1
+    model = O.Model(cfg, tensors)
+    t0 = time.perf_counter()
+    model.decode(latent[:rows, :, :4])
+    t4 = time.perf_counter() - t0
+    frames = int(max(4, min(cfg["frames"], round(4 * target_s / max(t4, 1e-3)))))
+    t0 = time.perf_counter()
+    model.decode(latent[:rows, :, :frames])
+    wall = time.perf_counter() - t0
+    secs = I.audio_seconds(cfg, rows, frames)
+    return {"value": secs / wall, "unit": "audio-s/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} row(s) x {frames} latent frames of the same latent "
+                      f"({secs:.3f} audio-s) decoded by the fp64 oracle in {wall:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1,
+                    help="synthetic workload index (default 1: full-width stereo window)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="skip the per-launch event profiler (roofline becomes null)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this decoder shards rows and time tiles "
+              "across GPUs with no exchange, and only the single-GPU path is built; "
+              "run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from dac_vocoder_decoding_amd import inputs as I
+    from dac_vocoder_decoding_amd import vocoder as V
+
+    cfg = I.config(args.config)
+    tensors = I.make_weights(cfg)
+    latent_np = I.make_latent(cfg)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ctx = V.open_context(cfg, tensors, device=0)
+    latent = torch.from_numpy(latent_np).to(dev)
+    B, _, T = latent.shape
+    pcm = torch.empty(B, 1, V.vocoder_output_length(ctx, T), device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        V.check(V.vocoder_decode(ctx, latent, B, T, pcm, stream), ctx)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    profile = not args.no_profile
+    if profile:
+        V.check(V.vocoder_profile_reset(ctx), ctx)
+        V.check(V.vocoder_profile_enable(ctx, True), ctx)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    kernels = {}
+    if profile:
+        V.check(V.vocoder_profile_enable(ctx, False), ctx)
+        for k, name in enumerate(KIND_NAMES):
+            st, s = V.vocoder_profile_read(ctx, k)
+            V.check(st, ctx)
+            if s["launches"]:
+                kernels[name] = s
+
+    secs = I.audio_seconds(cfg, B, T)
+    flops = I.algorithmic_flops(cfg, B, T)
+    value = secs / (ms_per_step / 1e3)
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+    peak = PEAK_TFLOPS[cfg["dtype"]]
+    ok = bool(torch.isfinite(pcm).all().item()) and float(pcm.abs().max()) <= 1.0
+
+    roofline = None
+    per_kernel = {}
+    if kernels:
+        for name, s in kernels.items():
+            avg_ms = s["ms"] / s["launches"]
+            per_kernel[name] = {
+                "launches_per_step": s["launches"] / args.steps,
+                "avg_us": round(1e3 * avg_ms, 3),
+                "share": round(s["ms"] / sum(x["ms"] for x in kernels.values()), 4),
+                "tflops": round(s["flops"] / (s["ms"] / 1e3) / 1e12, 3),
+                "alg_gbs": round(s["bytes"] / (s["ms"] / 1e3) / 1e9, 1),
+            }
+        dom = max((n for n in kernels if n not in ("import", "export")),
+                  key=lambda n: kernels[n]["ms"])
+        s = kernels[dom]
+        if dom == "head":
+            achieved = s["bytes"] / (s["ms"] / 1e3) / 1e9
+            roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+        else:
+            achieved = s["flops"] / (s["ms"] / 1e3) / 1e12
+            roofline = {"bound": "mfma", "achieved": achieved, "peak": peak,
+                        "unit": "TFLOP/s", "frac": achieved / peak}
+        roofline.update({
+            "kernel": dom,
+            "avg_launch_us": 1e3 * s["ms"] / s["launches"],
+            "alg_flops_per_launch": s["flops"] / s["launches"],
+            "alg_bytes_per_launch": s["bytes"] / s["launches"],
+            "traffic": traffic_for(cfg["name"], dom),
+        })
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, tensors, latent_np)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "audio-s/s" if cfg["stereo"] else "audio-s/s (mono 24 kHz)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic (seeded latents and random-init weights of the stated shapes)",
+        "config": {"workload": workload_name(cfg), "batch": B, "latent_frames": T,
+                   "audio_seconds_per_step": secs, "parallelism": "single GPU"},
+        "tflops": tflops,
+        "mfma_peak_frac": tflops / peak,
+        "output_ok": ok,
+        "host_wall_s": wall,
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    V.vocoder_destroy(ctx)
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -76,7 +76,9 @@ template <> struct HaloMax<2> { static constexpr int v = 1; };
 
 constexpr int kLdsRow = 80;  // 64-byte chunk row + 16 bytes: conflict-free ds_read_b128
 
-template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N>
+// TAG only separates kernel names per layer kind (conv_in vs residual k7)
+// so that profilers report them apart; it does not change the code.
+template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   constexpr int CH = OpT<OP>::CH;
   constexpr int ES = OpT<OP>::ES;
@@ -233,20 +235,20 @@ bool conv_variant_ok(int v, int taps) {
   return !(taps == 7 && v == CV_128x128);
 }
 
-template <int OP, int TAPS>
+template <int OP, int TAPS, int TAG>
 static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
   const int total = a.n_tiles * a.m_tiles * a.rows;
   const dim3 grid(total), block(256);
   switch (variant) {
     case CV_64x256:
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 4, 1, 4>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 4, 1, 4, TAG>), grid, block, 0, s, a);
       break;
     case CV_64x128:
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 2, 1, 4>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 2, 1, 4, TAG>), grid, block, 0, s, a);
       break;
     case CV_128x128:
       if constexpr (TAPS != 7) {
-        hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 4, 2, 2>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 4, 2, 2, TAG>), grid, block, 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -257,18 +259,20 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 }
 
 template <int OP>
-static hipError_t launch_op(int taps, int variant, const ConvArgs& a, hipStream_t s) {
+static hipError_t launch_op(int taps, int variant, bool conv_in, const ConvArgs& a, hipStream_t s) {
   switch (taps) {
-    case 7: return launch_taps<OP, 7>(variant, a, s);
-    case 2: return launch_taps<OP, 2>(variant, a, s);
-    case 1: return launch_taps<OP, 1>(variant, a, s);
+    case 7:
+      return conv_in ? launch_taps<OP, 7, 1>(variant, a, s) : launch_taps<OP, 7, 0>(variant, a, s);
+    case 2: return launch_taps<OP, 2, 0>(variant, a, s);
+    case 1: return launch_taps<OP, 1, 0>(variant, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_conv(int op, int taps, int variant, const ConvArgs& a, hipStream_t s) {
-  return op == OP_F32 ? launch_op<OP_F32>(taps, variant, a, s)
-                      : launch_op<OP_BF16>(taps, variant, a, s);
+hipError_t launch_conv(int op, int taps, int variant, bool conv_in, const ConvArgs& a,
+                       hipStream_t s) {
+  return op == OP_F32 ? launch_op<OP_F32>(taps, variant, conv_in, a, s)
+                      : launch_op<OP_BF16>(taps, variant, conv_in, a, s);
 }
 
 }  // namespace voc

@@ -71,7 +71,8 @@ int conv_variant_bm(int v);
 int conv_variant_bn(int v);
 bool conv_variant_ok(int v, int taps);
 
-hipError_t launch_conv(int op, int taps, int variant, const ConvArgs& a, hipStream_t s);
+hipError_t launch_conv(int op, int taps, int variant, bool conv_in, const ConvArgs& a,
+                       hipStream_t s);
 
 // Weight-norm fold + cast + repack, one workgroup per axis-0 slice.
 enum PackKind { PACK_CONV = 0, PACK_CONVT = 1, PACK_HEAD = 2 };

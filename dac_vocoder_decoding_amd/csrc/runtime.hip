@@ -391,7 +391,7 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   if (io.s_out) bytes += frames_out * L.cout * es;
   const int op = c->op;
   return launch(c, s, kind, flops, bytes, "conv launch",
-                [&] { return launch_conv(op, L.taps, v, a, s); });
+                [&] { return launch_conv(op, L.taps, v, kind == VOC_K_CONV_IN, a, s); });
 }
 
 voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const RowInfo& rows,

@@ -159,3 +159,11 @@ EXPORT void orc_add(const REAL *a, const REAL *b, REAL *y, int64_t n) {
 #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < n; ++k) y[k] = a[k] + b[k];
 }
+
+/* Threads the parallel loops above use (OpenMP's maximum). */
+#ifdef _OPENMP
+#include <omp.h>
+EXPORT int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+EXPORT int orc_num_threads(void) { return 1; }
+#endif

@@ -29,9 +29,11 @@ Readings of points the pages leave open (each listed in the design notes):
   * bf16 configurations: the folded weights are rounded fp64 -> fp32 (the F32
     inference checkpoint) -> bf16 (round to nearest even), the latent is
     rounded to bf16, and everything else stays exact.  Optionally
-    (``round_operands=True``) every convolution input after its Snake is also
-    rounded to bf16, mirroring an implementation whose matrix-core operands
-    are bf16 while accumulation and the residual stream stay wide.
+    (``round_operands=True``) the input of every matrix-core convolution
+    (conv_in, ConvTranspose1d, residual conv1 and conv2) after its Snake is
+    also rounded to bf16, mirroring an implementation whose matrix-core
+    operands are bf16 while accumulation and the residual stream stay wide;
+    the output head (a contraction to one channel) keeps its input wide.
 
 Pins (tests/test_oracle_pins.py) hold every function here to closed forms,
 brute force, textbook/library routines and invariants the pages fix.
@@ -71,6 +73,7 @@ def _lib(prec: str):
         lib = ctypes.CDLL(path)
         P, I = ctypes.c_void_p, ctypes.c_int64
         lib.orc_real_size.restype = ctypes.c_int
+        lib.orc_num_threads.restype = ctypes.c_int
         lib.orc_snake.argtypes = [P, P, I, I, I, P, P]
         lib.orc_weight_norm.argtypes = [P, P, P, I, I, P]
         lib.orc_conv1d.argtypes = [P, P, I, I, I, P, P, I, I, I]
@@ -228,9 +231,10 @@ class Model:
         self.head = (act("snake_out"), fold("conv_out"), vec("conv_out.bias"))
 
     # ---- stages -----------------------------------------------------------
-    def _snake(self, x, a):
+    def _snake(self, x, a, operand=True):
+        """Snake; in round_operands mode a matrix-core operand is rounded to bf16."""
         y = snake(x, a[0], a[1], self.prec)
-        if self.round_operands:
+        if self.round_operands and operand:
             y = _c(round_bf16(y), self.prec)
         return y
 
@@ -254,8 +258,10 @@ class Model:
                    self.prec)
 
     def stage_head_pre(self, h):
+        # The head contracts to one output channel: no matrix-core operand,
+        # so its Snake output is not rounded even in round_operands mode.
         a, w, b = self.head
-        return conv1d(self._snake(h, a), w, b, 1, self.prec)
+        return conv1d(self._snake(h, a, operand=False), w, b, 1, self.prec)
 
     def stage_head(self, h):
         return tanh(self.stage_head_pre(h), self.prec)
@@ -298,3 +304,8 @@ class Model:
             y = self.decode(latent[:, :, a:e])
             out[:, :, t0 * hop:t1 * hop] = y[:, :, (t0 - a) * hop:(t1 - a) * hop]
         return out
+
+
+def num_threads(prec: str = "f64") -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return _lib(prec).orc_num_threads()

@@ -1,0 +1,62 @@
+"""Helpers shared by the GPU parity tests: error metrics, teacher-forced stage
+windows, and tolerance constants.
+
+Tolerances (stated by the workload definitions): fp32 max-abs error <= 1e-4
+of the output RMS, bf16 <= 2e-2.  Both are applied per stage on the GPU's own
+stage input (teacher forcing) and end to end on the conditioned twins; the
+literal end-to-end errors are compared with the precision floor of an fp32
+(or bf16-operand) evaluation of the same loops.
+"""
+import numpy as np
+import torch
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def rel_maxabs(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(got - ref).max() / max(np.sqrt((ref ** 2).mean()), 1e-30))
+
+
+def rel_rms(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.sqrt(((got - ref) ** 2).mean()) / max(np.sqrt((ref ** 2).mean()), 1e-30))
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def stage_halo(cfg, k):
+    """(ups, input frames needed each side) of debug stage k."""
+    nr = len(cfg["dilations"])
+    n = 2 + len(cfg["strides"]) * (1 + nr)
+    if k == 0 or k == n - 1:
+        return 1, 3
+    b, j = divmod(k - 1, 1 + nr)
+    if j == 0:
+        return cfg["strides"][b], 2
+    return 1, 3 * cfg["dilations"][j - 1]
+
+
+def oracle_stage_window(model, k, x_gpu, rows, a, e):
+    """Oracle output of stage k for input frames [a, e) of the given rows,
+    computed from the GPU's own stage input on [a - h, e + h) (clamped), so
+    the kept outputs are exact.  Returns (oracle [R, C, (e-a)*ups], slice)."""
+    ups, h = stage_halo(model.cfg, k)
+    t_in = x_gpu.shape[-1]
+    i0, i1 = max(0, a - h), min(t_in, e + h)
+    xin = x_gpu[rows, :, i0:i1].cpu().numpy()
+    y = model.run_stage(k, xin)
+    lo = (a - i0) * ups
+    return y[:, :, lo:lo + (e - a) * ups], slice(a * ups, e * ups)
+
+
+def windows(t, w):
+    """Start, middle and (ragged) end windows of width w over [0, t)."""
+    w = min(w, t)
+    mid = max(0, (t // 2) - w // 2 + 3)
+    out = [(0, w), (mid, min(t, mid + w)), (t - w, t)]
+    return sorted(set(out))
