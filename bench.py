@@ -95,6 +95,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip the per-launch event profiler (roofline becomes null)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before the decode, run the library's plain copy kernel 3 times "
+                         "over MIB MiB (a known byte count for HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this decoder shards rows and time tiles "
@@ -119,6 +122,15 @@ def main() -> int:
 
     def step():
         V.check(V.vocoder_decode(ctx, latent, B, T, pcm, stream), ctx)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.ones(n // 4, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            V.check(V.voc_dbg_copy(dst, src, n, stream))
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
