@@ -26,8 +26,10 @@ sys.path.insert(0, ROOT)
 METRIC = "audio-seconds decoded/sec (44.1 kHz stereo) + TFLOP/s as % of MFMA peak"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
-KIND_NAMES = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export"]
+KIND_NAMES = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused"]
 KERNEL_SOURCES = ["dac_vocoder_decoding_amd/csrc/conv_gemm.hip",
+                  "dac_vocoder_decoding_amd/csrc/fused_ru.hip",
+                  "dac_vocoder_decoding_amd/csrc/gemm_common.h",
                   "dac_vocoder_decoding_amd/csrc/device_math.h",
                   "dac_vocoder_decoding_amd/csrc/internal.h"]
 

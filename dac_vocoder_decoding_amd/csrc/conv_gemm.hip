@@ -32,49 +32,9 @@
 // both operands).  Accumulator register v of lane l holds D[4*(l/16)+v][l%16].
 #include "internal.h"
 #include "device_math.h"
+#include "gemm_common.h"
 
 namespace voc {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-template <int OP> struct OpT;
-template <> struct OpT<OP_F32> { static constexpr int CH = 16, ES = 4; };
-template <> struct OpT<OP_BF16> { static constexpr int CH = 32, ES = 2; };
-
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup id % 8).
-// Give each XCD a contiguous range of logical tiles so that tiles sharing a
-// weight slice (same m-tile) and neighbouring activation rows stay in one
-// XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  const int q = total >> 3, r = total & 7;
-  const int xcd = bid & 7, local = bid >> 3;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-}
-
-template <int OP>
-__device__ __forceinline__ void mfma_frag(const uint4& a, const uint4& b, f4& acc);
-
-template <>
-__device__ __forceinline__ void mfma_frag<OP_F32>(const uint4& a, const uint4& b, f4& acc) {
-  const f4 av = __builtin_bit_cast(f4, a);
-  const f4 bv = __builtin_bit_cast(f4, b);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bv[3], acc, 0, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ void mfma_frag<OP_BF16>(const uint4& a, const uint4& b, f4& acc) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-}
-
-template <int TAPS> struct HaloMax { static constexpr int v = 0; };
-template <> struct HaloMax<7> { static constexpr int v = 54; };  // 6 * dilation 9
-template <> struct HaloMax<2> { static constexpr int v = 1; };
-
-constexpr int kLdsRow = 80;  // 64-byte chunk row + 16 bytes: conflict-free ds_read_b128
 
 // TAG only separates kernel names per layer kind (conv_in vs residual k7)
 // so that profilers report them apart; it does not change the code.
@@ -84,10 +44,11 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   constexpr int ES = OpT<OP>::ES;
   constexpr int BM = WAVES_M * WMB * 16;
   constexpr int BN = WAVES_N * WNB * 16;
-  constexpr int XROWS = BN + HaloMax<TAPS>::v;
+  constexpr int XROWS = (BN + HaloMax<TAPS>::v + 15) / 16 * 16;
   constexpr int WROWS = TAPS * BM;
   constexpr int XU = (XROWS * 4 + 255) / 256;
   constexpr int WU = (WROWS * 4 + 255) / 256;
+  static_assert(WROWS % 16 == 0, "weight rows come in groups of 16");
   static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
   __shared__ __attribute__((aligned(16))) unsigned char Xs[XROWS * kLdsRow];
   __shared__ __attribute__((aligned(16))) unsigned char Ws[WROWS * kLdsRow];
@@ -122,10 +83,10 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
       const int idx = tid + u * 256;
-      const int r = idx >> 2, col = idx & 3;
+      const int r = unit_row(idx), col = unit_col(idx);
       const int t = tfirst + r;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < xrows * 4 && t >= 0 && t < Lin)
+      if (r < xrows && t >= 0 && t < Lin)
         v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
       xr[u] = v;
     }
@@ -133,10 +94,10 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
       const int idx = tid + u * 256;
-      const int r = idx >> 2, col = idx & 3;
+      const int r = unit_row(idx), col = unit_col(idx);
       const int j = r / BM, mm = r - j * BM;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < WROWS * 4 && m0 + mm < a.M)
+      if (r < WROWS && m0 + mm < a.M)
         v = *reinterpret_cast<const uint4*>(
             wc + (static_cast<int64_t>(j) * a.M + m0 + mm) * kChunkBytes + col * 16);
       wr[u] = v;
@@ -146,14 +107,14 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
       const int idx = tid + u * 256;
-      if (idx < xrows * 4)
-        *reinterpret_cast<uint4*>(Xs + (idx >> 2) * kLdsRow + (idx & 3) * 16) = xr[u];
+      const int r = unit_row(idx);
+      if (r < xrows) *reinterpret_cast<uint4*>(Xs + r * kLdsRow + unit_col(idx) * 16) = xr[u];
     }
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
       const int idx = tid + u * 256;
-      if (idx < WROWS * 4)
-        *reinterpret_cast<uint4*>(Ws + (idx >> 2) * kLdsRow + (idx & 3) * 16) = wr[u];
+      const int r = unit_row(idx);
+      if (r < WROWS) *reinterpret_cast<uint4*>(Ws + r * kLdsRow + unit_col(idx) * 16) = wr[u];
     }
   };
 
@@ -228,11 +189,24 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   }
 }
 
-int conv_variant_bm(int v) { return v == CV_128x128 ? 128 : 64; }
-int conv_variant_bn(int v) { return v == CV_64x256 ? 256 : 128; }
+// Block-tile families: {m-blocks per wave, n-blocks per wave, waves along M, waves along N}.
+struct VariantShape { int wmb, wnb, wav_m, wav_n; };
+static constexpr VariantShape kVariants[CV_COUNT] = {
+    {4, 8, 2, 2},  // CV_128x256
+    {4, 4, 1, 4},  // CV_64x256
+    {6, 4, 1, 4},  // CV_96x256
+    {4, 4, 2, 2},  // CV_128x128
+    {4, 2, 1, 4},  // CV_64x128
+    {6, 4, 2, 2},  // CV_192x128
+};
+
+int conv_variant_bm(int v) { return kVariants[v].wav_m * kVariants[v].wmb * 16; }
+int conv_variant_bn(int v) { return kVariants[v].wav_n * kVariants[v].wnb * 16; }
 bool conv_variant_ok(int v, int taps) {
-  // A 7-tap weight tile of 128 rows would not fit 64 KB of LDS.
-  return !(taps == 7 && v == CV_128x128);
+  if (v < 0 || v >= CV_COUNT) return false;
+  // All taps' weight rows of a chunk live in LDS: keep two workgroups per CU.
+  if (taps == 7) return v == CV_64x256 || v == CV_96x256 || v == CV_64x128;
+  return true;
 }
 
 template <int OP, int TAPS, int TAG>
@@ -240,18 +214,25 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
   const int total = a.n_tiles * a.m_tiles * a.rows;
   const dim3 grid(total), block(256);
   switch (variant) {
-    case CV_64x256:
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 4, 1, 4, TAG>), grid, block, 0, s, a);
-      break;
-    case CV_64x128:
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 2, 1, 4, TAG>), grid, block, 0, s, a);
-      break;
-    case CV_128x128:
-      if constexpr (TAPS != 7) {
-        hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, 4, 4, 2, 2, TAG>), grid, block, 0, s, a);
-        break;
-      }
-      return hipErrorInvalidValue;
+#define VOC_CASE(V, A, B, C, D)                                                            \
+  case V:                                                                                  \
+    hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG>), grid, block, 0, s, a); \
+    break;
+    VOC_CASE(CV_64x256, 4, 4, 1, 4)
+    VOC_CASE(CV_96x256, 6, 4, 1, 4)
+    VOC_CASE(CV_64x128, 4, 2, 1, 4)
+#undef VOC_CASE
+#define VOC_CASE(V, A, B, C, D)                                                              \
+  case V:                                                                                    \
+    if constexpr (TAPS != 7) {                                                               \
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG>), grid, block, 0, s, a); \
+      break;                                                                                 \
+    }                                                                                        \
+    return hipErrorInvalidValue;
+    VOC_CASE(CV_128x256, 4, 8, 2, 2)
+    VOC_CASE(CV_128x128, 4, 4, 2, 2)
+    VOC_CASE(CV_192x128, 6, 4, 2, 2)
+#undef VOC_CASE
     default:
       return hipErrorInvalidValue;
   }

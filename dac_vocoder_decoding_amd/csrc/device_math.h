@@ -8,32 +8,22 @@ namespace voc {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-// Snake / SnakeBeta: x + sin^2(alpha x) * invden, with invden = 1/(alpha+1e-9)
-// (Snake, minimaxmusic.cpp ARCHITECTURE "Flow VAE") or 1/(beta+1e-9)
-// (SnakeBeta, qwentts.cpp ARCHITECTURE glossary), precomputed at load.
+// Snake / SnakeBeta: x + sin^2(alpha x) / den with den = alpha + 1e-9
+// (Snake, minimaxmusic.cpp ARCHITECTURE "Flow VAE") or beta + 1e-9
+// (SnakeBeta, qwentts.cpp ARCHITECTURE glossary).
 //
-// sin^2 has period pi, so z = alpha x is reduced to r = z - k pi with
-// k = rint(z / pi) and |r| <= pi/2.  pi is split into PI_HI = float(pi) and
-// PI_LO = pi - PI_HI (Cody & Waite, "Software Manual for the Elementary
-// Functions", 1980); the k*PI_HI step is a fused multiply-add, so it is exact
-// up to one rounding for every |k| this network reaches.  sin(r) is the
-// Taylor series through r^13, whose truncation error on |r| <= pi/2 is below
-// (pi/2)^15 / 15! < 7e-10.
-__device__ __forceinline__ float snake_f32(float x, float alpha, float invden) {
-  const float z = alpha * x;
-  const float k = rintf(z * 0.318309886183790672f);
-  float r = fmaf(-k, 3.14159274101257324f, z);
-  r = fmaf(-k, -8.74227800037248e-08f, r);
-  const float r2 = r * r;
-  float p = 1.60590438368216146e-10f;            //  1/13!
-  p = fmaf(p, r2, -2.50521083854417188e-08f);    // -1/11!
-  p = fmaf(p, r2, 2.75573192239858907e-06f);     //  1/9!
-  p = fmaf(p, r2, -1.98412698412698413e-04f);    // -1/7!
-  p = fmaf(p, r2, 8.33333333333333333e-03f);     //  1/5!
-  p = fmaf(p, r2, -1.66666666666666667e-01f);    // -1/3!
-  p = fmaf(p, r2, 1.0f);
-  const float s = r * p;
-  return fmaf(s * s, invden, x);
+// With sin^2(t) = (1 - cos 2t) / 2 and the hardware cosine, whose argument is
+// in revolutions (v_cos_f32 computes cos(2 pi r)):
+//   cos(2 alpha x) = cos(2 pi r),  r = frac(x alpha / pi)   (v_fract_f32),
+//   Snake(x) = x + h (1 - cos(2 pi r)),  h = 1 / (2 den).
+// The per-channel parameters scale = alpha / pi and h are computed in fp64 at
+// load.  Reducing r to [0, 1) keeps the hardware cosine in its accurate
+// range; the phase error is that of the product x * scale, the same order as
+// the rounding of alpha * x itself.
+__device__ __forceinline__ float snake_f32(float x, float scale, float h) {
+  const float r = __builtin_amdgcn_fractf(x * scale);
+  const float c = __builtin_amdgcn_cosf(r);
+  return fmaf(-h, c, x + h);
 }
 
 // Round-to-nearest-even float -> bfloat16 bits (finite inputs): add 0x7FFF
@@ -57,11 +47,19 @@ __device__ __forceinline__ void store_op4<0>(void* base, int64_t idx, f4 v) {
   *reinterpret_cast<f4*>(static_cast<float*>(base) + idx) = v;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t p = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 template <>
 __device__ __forceinline__ void store_op4<1>(void* base, int64_t idx, f4 v) {
   uint2 p;
-  p.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-  p.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+  p.x = pack_bf16x2(v[0], v[1]);
+  p.y = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = p;
 }
 

@@ -1,0 +1,297 @@
+// fused_ru.hip -- one residual unit in one kernel:
+//   h <- h + conv2(Snake2(conv1_d(S) + b1)) + b2,   S = Snake1(h) (operand dtype)
+// (residual unit of the DAV decoder, minimaxmusic.cpp ARCHITECTURE "Flow VAE":
+// snake1 -> conv1 k=7 at dilation d -> snake2 -> conv2 k=1 -> add the skip).
+//
+// A workgroup owns BN frames of one row and all C channels, so the
+// intermediate U = Snake2(conv1 + b1) never leaves the CU:
+//   stage 1  conv1 as an implicit GEMM (M = C, K = 7 C) from the X tile
+//            [n0 - 3d, n0 + BN + 3d) and the weight rows of a group of taps,
+//            both staged in LDS per 64-byte channel chunk;
+//   epilogue bias + Snake2, U written into LDS over the stage-1 staging area
+//            (the same 64-byte chunk rows the GEMM reads);
+//   stage 2  conv2 as a GEMM (M = C, K = C) from U in LDS and conv2 weight
+//            chunks streamed into LDS;
+//   epilogue bias, residual add in place, the next layer's Snake operand.
+// Compared with separate conv1 and conv2 launches this removes the U round
+// trip through HBM (2 x C x T operands per unit) and the second launch.
+#include "internal.h"
+#include "device_math.h"
+#include "gemm_common.h"
+
+namespace voc {
+
+template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG>
+__global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
+  constexpr int CH = OpT<OP>::CH;
+  constexpr int ES = OpT<OP>::ES;
+  constexpr int C = WAVES_M * WMB * 16;
+  constexpr int BN = WAVES_N * WNB * 16;
+  constexpr int XROWS = (BN + 54 + 15) / 16 * 16;
+  constexpr int NG = (7 + TG - 1) / TG;        // tap groups per channel chunk
+  constexpr int WROWS = TG * C;
+  constexpr int NCH = C / CH;                  // channel chunks
+  constexpr int S1 = (XROWS + WROWS) * kLdsRow;
+  constexpr int UB = NCH * BN * kLdsRow;       // U tile: [NCH][BN] rows
+  constexpr int S2 = UB + C * kLdsRow;
+  constexpr int LDS = S1 > S2 ? S1 : S2;
+  constexpr int XU = (XROWS * 4 + 255) / 256;
+  constexpr int WU = (WROWS * 4 + 255) / 256;
+  constexpr int W2U = (C * 4 + 255) / 256;
+  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  static_assert(C % CH == 0 && C % 16 == 0, "whole channel chunks");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
+  unsigned char* Xs = smem;
+  unsigned char* Ws = smem + XROWS * kLdsRow;
+  unsigned char* Us = smem;          // stage 2 (after stage 1 is done)
+  unsigned char* W2s = smem + UB;
+
+  const int tid = threadIdx.x;
+  const int L = xcd_remap(blockIdx.x, a.n_tiles * a.rows);
+  const int n_tile = L % a.n_tiles;
+  const int row = L / a.n_tiles;
+  const int n0 = n_tile * BN;
+  const int len = a.row_len[row];
+  const int Lv = min(len * a.rate, a.T);
+  if (n0 >= Lv) return;
+
+  const int d = a.dil;
+  const int xrows = BN + 6 * d;
+  const int tfirst = n0 - 3 * d;
+  const unsigned char* xrow = static_cast<const unsigned char*>(a.x) +
+                              static_cast<int64_t>(row) * C * a.T * ES;
+  const int64_t xplane = static_cast<int64_t>(a.T) * kChunkBytes;
+  const unsigned char* w1 = static_cast<const unsigned char*>(a.w1);
+  const unsigned char* w2 = static_cast<const unsigned char*>(a.w2);
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  f4 acc[WMB][WNB];
+#pragma unroll
+  for (int i = 0; i < WMB; ++i)
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // ------------------------------------------------------------ stage 1
+  uint4 xr[XU], wr[WU];
+  auto load_x = [&](int c) {
+    const unsigned char* xc = xrow + c * xplane;
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int idx = tid + u * 256;
+      const int r = unit_row(idx), col = unit_col(idx);
+      const int t = tfirst + r;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < xrows && t >= 0 && t < Lv)
+        v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
+      xr[u] = v;
+    }
+  };
+  auto load_w = [&](int c, int g) {
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const int idx = tid + u * 256;
+      const int r = unit_row(idx), col = unit_col(idx);
+      const int jj = r / C, m = r - jj * C;
+      const int j = g * TG + jj;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < WROWS && j < 7)
+        v = *reinterpret_cast<const uint4*>(
+            w1 + ((static_cast<int64_t>(c) * 7 + j) * C + m) * kChunkBytes + col * 16);
+      wr[u] = v;
+    }
+  };
+  auto store_x = [&]() {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int idx = tid + u * 256;
+      const int r = unit_row(idx);
+      if (r < xrows) *reinterpret_cast<uint4*>(Xs + r * kLdsRow + unit_col(idx) * 16) = xr[u];
+    }
+  };
+  auto store_w = [&]() {
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const int idx = tid + u * 256;
+      const int r = unit_row(idx);
+      if (r < WROWS) *reinterpret_cast<uint4*>(Ws + r * kLdsRow + unit_col(idx) * 16) = wr[u];
+    }
+  };
+
+  load_x(0);
+  load_w(0, 0);
+  for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g == 0) store_x();
+      store_w();
+      __syncthreads();
+      if (g + 1 < NG) {
+        load_w(c, g + 1);
+      } else if (c + 1 < NCH) {
+        load_x(c + 1);
+        load_w(c + 1, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < TG; ++jj) {
+        const int j = g * TG + jj;
+        if (j >= 7) break;
+        const int xoff = j * d + wn * WNB * 16 + lr;
+        uint4 A[WMB], B[WNB];
+#pragma unroll
+        for (int mb = 0; mb < WMB; ++mb)
+          A[mb] = *reinterpret_cast<const uint4*>(
+              Ws + (jj * C + wm * WMB * 16 + mb * 16 + lr) * kLdsRow + lg * 16);
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb)
+          B[nb] = *reinterpret_cast<const uint4*>(Xs + (xoff + nb * 16) * kLdsRow + lg * 16);
+#pragma unroll
+        for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < WNB; ++nb) mfma_frag<OP>(A[mb], B[nb], acc[mb][nb]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // Fetch the first conv2 weight chunk while the U epilogue runs.
+  uint4 w2r[W2U];
+  auto load_w2 = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < W2U; ++u) {
+      const int idx = tid + u * 256;
+      const int r = unit_row(idx), col = unit_col(idx);
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < C)
+        v = *reinterpret_cast<const uint4*>(
+            w2 + (static_cast<int64_t>(c) * C + r) * kChunkBytes + col * 16);
+      w2r[u] = v;
+    }
+  };
+  load_w2(0);
+
+  // ------------------------------------------- epilogue 1: U into LDS
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb) {
+    const int m = wm * WMB * 16 + mb * 16 + lg * 4;
+    const f4 b1 = *reinterpret_cast<const f4*>(a.b1 + m);
+    const f4 sc = *reinterpret_cast<const f4*>(a.a2_scale + m);
+    const f4 hh = *reinterpret_cast<const f4*>(a.a2_h + m);
+    unsigned char* ubase = Us + (m / CH) * BN * kLdsRow + (m % CH) * ES;
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) {
+      const int nl = wn * WNB * 16 + nb * 16 + lr;
+      f4 v = acc[mb][nb] + b1;
+      v[0] = snake_f32(v[0], sc[0], hh[0]);
+      v[1] = snake_f32(v[1], sc[1], hh[1]);
+      v[2] = snake_f32(v[2], sc[2], hh[2]);
+      v[3] = snake_f32(v[3], sc[3], hh[3]);
+      store_op4<OP>(ubase + nl * kLdsRow, 0, v);
+      acc[mb][nb] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // ------------------------------------------------------------ stage 2
+  for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+    for (int u = 0; u < W2U; ++u) {
+      const int idx = tid + u * 256;
+      const int r = unit_row(idx);
+      if (r < C) *reinterpret_cast<uint4*>(W2s + r * kLdsRow + unit_col(idx) * 16) = w2r[u];
+    }
+    __syncthreads();
+    if (c + 1 < NCH) load_w2(c + 1);
+    uint4 A[WMB], B[WNB];
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
+      A[mb] = *reinterpret_cast<const uint4*>(W2s + (wm * WMB * 16 + mb * 16 + lr) * kLdsRow + lg * 16);
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb)
+      B[nb] = *reinterpret_cast<const uint4*>(
+          Us + (c * BN + wn * WNB * 16 + nb * 16 + lr) * kLdsRow + lg * 16);
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) mfma_frag<OP>(A[mb], B[nb], acc[mb][nb]);
+    __syncthreads();
+  }
+
+  // ----------------------------------- epilogue 2: bias, skip, next Snake
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb) {
+    const int m = wm * WMB * 16 + mb * 16 + lg * 4;
+    const f4 b2 = *reinterpret_cast<const f4*>(a.b2 + m);
+    f4 sc = f4{0.f, 0.f, 0.f, 0.f}, hh = f4{0.f, 0.f, 0.f, 0.f};
+    if (a.s_out) {
+      sc = *reinterpret_cast<const f4*>(a.s_scale + m);
+      hh = *reinterpret_cast<const f4*>(a.s_h + m);
+    }
+    const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
+    const int64_t sbase = (static_cast<int64_t>(row) * C + (m / CH) * CH) * a.T + (m % CH);
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) {
+      const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
+      if (n >= Lv) continue;
+      const int64_t hidx = hbase + static_cast<int64_t>(n) * kHChunk;
+      f4 v = acc[mb][nb] + b2 + *reinterpret_cast<const f4*>(a.h + hidx);
+      *reinterpret_cast<f4*>(a.h + hidx) = v;
+      if (a.s_out) {
+        v[0] = snake_f32(v[0], sc[0], hh[0]);
+        v[1] = snake_f32(v[1], sc[1], hh[1]);
+        v[2] = snake_f32(v[2], sc[2], hh[2]);
+        v[3] = snake_f32(v[3], sc[3], hh[3]);
+        store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(n) * CH, v);
+      }
+    }
+  }
+}
+
+// Instances: channel width C -> {m-blocks per wave, n-blocks, waves M, waves N, taps per group}.
+// Only widths where one fused launch beats the conv1 + conv2 pair on MI355X
+// (per-layer kernel traces): at C >= 256 the whole-C tile leaves too few
+// frames per workgroup (LDS holds U for all C), and the pair is faster.
+template <int OP>
+static hipError_t launch_ru(const ResUnitArgs& a, hipStream_t s, int* bn) {
+  const dim3 block(256);
+#define VOC_RU(CW, A, B, WM, WN, TGV)                                                       \
+  if (a.C == CW) {                                                                          \
+    *bn = WN * B * 16;                                                                      \
+    if (a.n_tiles <= 0) return hipSuccess;                                                  \
+    hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV>), dim3(a.n_tiles * a.rows), \
+                       block, 0, s, a);                                                     \
+    return hipGetLastError();                                                               \
+  }
+  if constexpr (OP == OP_BF16) {
+    VOC_RU(64, 4, 2, 1, 4, 7)
+    VOC_RU(96, 6, 2, 1, 4, 7)
+    VOC_RU(128, 4, 4, 2, 2, 4)
+    VOC_RU(192, 6, 4, 2, 2, 1)
+  } else {
+    VOC_RU(16, 1, 4, 1, 4, 7)
+    VOC_RU(32, 2, 2, 1, 4, 7)
+    VOC_RU(64, 4, 2, 1, 4, 7)
+    VOC_RU(96, 6, 2, 1, 4, 7)
+    VOC_RU(128, 4, 2, 2, 2, 4)
+  }
+#undef VOC_RU
+  return hipErrorInvalidValue;
+}
+
+int res_unit_tile(int op, int C) {
+  int bn = 0;
+  ResUnitArgs probe{};
+  probe.C = C;
+  probe.n_tiles = 0;
+  const hipError_t e = op == OP_F32 ? launch_ru<OP_F32>(probe, nullptr, &bn)
+                                    : launch_ru<OP_BF16>(probe, nullptr, &bn);
+  return e == hipSuccess ? bn : 0;
+}
+
+hipError_t launch_res_unit(int op, const ResUnitArgs& a, hipStream_t s) {
+  int bn = 0;
+  return op == OP_F32 ? launch_ru<OP_F32>(a, s, &bn) : launch_ru<OP_BF16>(a, s, &bn);
+}
+
+}  // namespace voc

@@ -66,13 +66,46 @@ struct ConvArgs {
 };
 
 // Tile shape families of the conv GEMM kernel.
-enum ConvVariant { CV_64x256 = 0, CV_64x128 = 1, CV_128x128 = 2, CV_COUNT = 3 };
+enum ConvVariant {
+  CV_128x256 = 0,
+  CV_64x256 = 1,
+  CV_96x256 = 2,
+  CV_128x128 = 3,
+  CV_64x128 = 4,
+  CV_192x128 = 5,
+  CV_COUNT = 6
+};
 int conv_variant_bm(int v);
 int conv_variant_bn(int v);
 bool conv_variant_ok(int v, int taps);
 
 hipError_t launch_conv(int op, int taps, int variant, bool conv_in, const ConvArgs& a,
                        hipStream_t s);
+
+// One fused residual unit over all C channels of BN-frame tiles:
+//   h <- h + conv2(Snake2(conv1_dil(x) + b1)) + b2;  s_out <- Snake_next(h).
+// x is Snake1(h) in the operand dtype.  Same layouts as ConvArgs.
+struct ResUnitArgs {
+  const void* x;
+  int T, C;
+  const int* row_len;
+  int rate, dil;
+  const void* w1;        // packed [C/CH][7][C][CH]
+  const float* b1;
+  const float* a2_scale;  // Snake2: alpha/pi, 1/(2 den)
+  const float* a2_h;
+  const void* w2;        // packed [C/CH][1][C][CH]
+  const float* b2;
+  float* h;              // residual stream, in place
+  void* s_out;           // may be null
+  const float* s_scale;
+  const float* s_h;
+  int n_tiles, rows;
+};
+// Frames per workgroup of the fused kernel for width C, or 0 if there is no
+// fused instance for (op, C).
+int res_unit_tile(int op, int C);
+hipError_t launch_res_unit(int op, const ResUnitArgs& a, hipStream_t s);
 
 // Weight-norm fold + cast + repack, one workgroup per axis-0 slice.
 enum PackKind { PACK_CONV = 0, PACK_CONVT = 1, PACK_HEAD = 2 };

@@ -24,8 +24,8 @@ namespace {
 std::string g_create_error;
 
 struct SnakeDev {
-  float* alpha = nullptr;
-  float* invden = nullptr;
+  float* alpha = nullptr;   // alpha / pi per channel
+  float* invden = nullptr;  // 1 / (2 (den + 1e-9)) per channel
 };
 struct ConvDev {
   void* w = nullptr;
@@ -79,6 +79,8 @@ struct voc_ctx {
   // cached row metadata of the last decode
   int64_t rows_B = -1, rows_T = -1;
   int rows_n = 0;
+  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
+  bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   std::vector<int64_t> meta_dst;  // host copies kept alive for async uploads
   std::vector<int> meta_int;
 };
@@ -319,16 +321,35 @@ voc_status upload_rows(voc_ctx* c, const Plan& p, std::vector<int64_t>&& dst_in,
 }
 
 // ------------------------------------------------------------ conv launch
-int pick_variant(int taps, int M, int N, int rows) {
-  // Prefer the larger tiles while they still give about two workgroups per CU.
-  const int cands[3] = {CV_64x256, CV_128x128, CV_64x128};
-  for (int v : cands) {
+// Tile choice: padding efficiency of M and N x wave quantization over two
+// workgroups per CU x a relative speed of the tile family for the operand
+// dtype and tap count, measured on MI355X (a sweep forcing each family on
+// the full-window fp32 and batched-window bf16 decodes).
+int pick_variant(int op, int taps, int M, int N, int rows) {
+  //                                  128x256 64x256 96x256 128x128 64x128 192x128
+  static const double f32[CV_COUNT]   = {0.60, 0.90, 0.85, 0.90, 1.00, 0.70};
+  static const double bf_t2[CV_COUNT] = {0.90, 0.80, 0.85, 1.00, 0.75, 0.92};
+  static const double bf_t7[CV_COUNT] = {0.00, 1.00, 1.00, 0.00, 0.88, 0.00};
+  static const double bf_t1[CV_COUNT] = {0.46, 0.94, 0.80, 0.95, 1.00, 0.68};
+  const double* speed = op == OP_F32 ? f32 : taps == 2 ? bf_t2 : taps == 7 ? bf_t7 : bf_t1;
+  int best = CV_64x128;
+  double best_score = -1.0;
+  for (int v = 0; v < CV_COUNT; ++v) {
     if (!conv_variant_ok(v, taps)) continue;
-    const int64_t tiles = static_cast<int64_t>((M + conv_variant_bm(v) - 1) / conv_variant_bm(v)) *
-                          ((N + conv_variant_bn(v) - 1) / conv_variant_bn(v)) * rows;
-    if (tiles >= 512) return v;
+    const int bm = conv_variant_bm(v), bn = conv_variant_bn(v);
+    const int64_t mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn;
+    const int64_t tiles = mt * nt * rows;
+    const double pad = static_cast<double>(M) * N / (static_cast<double>(mt) * bm * nt * bn);
+    const int64_t slots = 256 * 2;
+    const int64_t waves = (tiles + slots - 1) / slots;
+    const double quant = static_cast<double>(tiles) / static_cast<double>(waves * slots);
+    const double score = pad * quant * speed[v];
+    if (score > best_score) {
+      best_score = score;
+      best = v;
+    }
   }
-  return CV_64x128;
+  return best;
 }
 
 struct ConvIO {
@@ -377,7 +398,9 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.s_alpha = io.snake_next ? io.snake_next->alpha : nullptr;
   a.s_invden = io.snake_next ? io.snake_next->invden : nullptr;
   a.rows = rows;
-  const int v = pick_variant(L.taps, L.M, a.N, rows);
+  int v = pick_variant(c->op, L.taps, L.M, a.N, rows);
+  if (c->force_variant[kind] >= 0 && conv_variant_ok(c->force_variant[kind], L.taps))
+    v = c->force_variant[kind];
   a.n_tiles = (a.N + conv_variant_bn(v) - 1) / conv_variant_bn(v);
   a.m_tiles = (a.M + conv_variant_bm(v) - 1) / conv_variant_bm(v);
   // Algorithmic work: every input frame meets every tap (direct convolution).
@@ -435,6 +458,70 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
   return launch(c, s, VOC_K_HEAD, flops, bytes, "head launch", [&] { return launch_head(a, s); });
 }
 
+// One residual unit: fused into one kernel when an instance exists for its
+// width, else conv1 (epilogue: bias + Snake2 -> ubuf) and conv2 (epilogue:
+// bias + residual + next Snake).  s_in holds Snake1(h) in the operand dtype.
+// When `next` is given, the next layer's Snake operand is written to
+// *s_next: s_spare for the fused kernel (its tiles read neighbouring frames
+// of s_in while others write, so it must not write in place), s_in for the
+// two-kernel path (conv1 has finished reading s_in before conv2 runs).
+voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_spare, void* ubuf,
+                        float* h, const SnakeDev* next, void** s_next, int T, int rate, int rows,
+                        const int* row_len, hipStream_t s) {
+  const int C = u.c1.cout;
+  const int bn = c->no_fuse ? 0 : res_unit_tile(c->op, C);
+  if (s_next) *s_next = nullptr;
+  if (bn > 0) {
+    void* s_out = next ? s_spare : nullptr;
+    if (s_next) *s_next = s_out;
+    ResUnitArgs a{};
+    a.x = s_in;
+    a.T = T;
+    a.C = C;
+    a.row_len = row_len;
+    a.rate = rate;
+    a.dil = u.c1.dil;
+    a.w1 = u.c1.w;
+    a.b1 = u.c1.bias;
+    a.a2_scale = u.a2.alpha;
+    a.a2_h = u.a2.invden;
+    a.w2 = u.c2.w;
+    a.b2 = u.c2.bias;
+    a.h = h;
+    a.s_out = s_out;
+    a.s_scale = next ? next->alpha : nullptr;
+    a.s_h = next ? next->invden : nullptr;
+    a.n_tiles = (T + bn - 1) / bn;
+    a.rows = rows;
+    const double el = static_cast<double>(rows) * T * C;
+    const double es = op_size(c->op);
+    const double flops = 2.0 * el * C * 8;
+    const double bytes = el * (es + 8 + (s_out ? es : 0)) + 8.0 * C * C * es;
+    const int op = c->op;
+    return launch(c, s, VOC_K_RES_FUSED, flops, bytes, "residual unit launch",
+                  [&] { return launch_res_unit(op, a, s); });
+  }
+  void* s_out = next ? const_cast<void*>(s_in) : nullptr;
+  if (s_next) *s_next = s_out;
+  ConvIO io{};
+  io.x = s_in;
+  io.T_in = T;
+  io.rate_in = rate;
+  io.s_out = ubuf;
+  io.snake_next = &u.a2;
+  voc_status st = run_conv(c, u.c1, io, rows, row_len, VOC_K_RES_K7, s);
+  if (st) return st;
+  io = ConvIO{};
+  io.x = ubuf;
+  io.T_in = T;
+  io.rate_in = rate;
+  io.h_out = h;
+  io.res = h;
+  io.snake_next = next;
+  io.s_out = s_out;
+  return run_conv(c, u.c2, io, rows, row_len, VOC_K_RES_K1, s);
+}
+
 const SnakeDev* next_snake(const Weights& W, int b, int r, int nb, int nr) {
   if (r + 1 < nr) return &W.blocks[b].units[r + 1].a1;
   if (b + 1 < nb) return &W.blocks[b + 1].act;
@@ -473,25 +560,11 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s) 
     t *= g.stride[b];
     rate *= g.stride[b];
     for (int r = 0; r < nr; ++r) {
-      const UnitDev& u = blk.units[r];
-      io = ConvIO{};
-      io.x = B.s[cur];
-      io.T_in = t;
-      io.rate_in = rate;
-      io.s_out = B.u;
-      io.snake_next = &u.a2;
-      st = run_conv(c, u.c1, io, rows, B.rows.len, VOC_K_RES_K7, s);
+      void* s_next = nullptr;
+      st = run_res_unit(c, blk.units[r], B.s[cur], B.s[cur ^ 1], B.u, B.h,
+                        next_snake(W, b, r, nb, nr), &s_next, t, rate, rows, B.rows.len, s);
       if (st) return st;
-      io = ConvIO{};
-      io.x = B.u;
-      io.T_in = t;
-      io.rate_in = rate;
-      io.h_out = B.h;
-      io.res = B.h;
-      io.snake_next = next_snake(W, b, r, nb, nr);
-      io.s_out = io.snake_next ? B.s[cur] : nullptr;
-      st = run_conv(c, u.c2, io, rows, B.rows.len, VOC_K_RES_K1, s);
-      if (st) return st;
+      if (s_next == B.s[cur ^ 1]) cur ^= 1;
     }
   }
   return VOC_OK;
@@ -616,6 +689,12 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   c->hop = total_stride(*cfg);
   c->halo = compute_halo(*cfg);
   if (const char* cap = std::getenv("VOC_MAX_WORKSPACE_BYTES")) c->ws_cap = std::strtoull(cap, nullptr, 10);
+  // Ablation only: VOC_VARIANT_{CONV_IN,CONVT,RES_K7,RES_K1}=<tile family index>.
+  const char* names[4] = {"VOC_VARIANT_CONV_IN", "VOC_VARIANT_CONVT", "VOC_VARIANT_RES_K7",
+                          "VOC_VARIANT_RES_K1"};
+  for (int k = 0; k < 4; ++k)
+    if (const char* v = std::getenv(names[k])) c->force_variant[k] = std::atoi(v);
+  if (const char* v = std::getenv("VOC_NO_FUSED_RES")) c->no_fuse = std::atoi(v) != 0;
   *out = c;
   return VOC_OK;
 }
@@ -670,22 +749,23 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     hipError_t e = hipMemcpy(*d, h, count * 4, hipMemcpyHostToDevice);
     return e == hipSuccess ? VOC_OK : hip_fail(c, e, "weight upload");
   };
+  // Snake parameters as the kernels use them: scale = alpha / pi and
+  // h = 1 / (2 (den + 1e-9)), den = alpha (Snake) or beta (SnakeBeta).
   auto snake = [&](const std::string& p, int ch, SnakeDev* sd) -> voc_status {
     const float* a = got[p + ".alpha"]->data;
     const float* b = g.act == VOC_SNAKE_BETA ? got[p + ".beta"]->data : nullptr;
-    std::vector<float> al(ch), iv(ch);
+    std::vector<float> sc(ch), hh(ch);
     for (int i = 0; i < ch; ++i) {
       double av = a[i], dv = b ? b[i] : a[i];
       if (g.snake_log_params) av = std::exp(av), dv = std::exp(dv);
-      const double inv = 1.0 / (dv + 1e-9);
-      al[i] = static_cast<float>(av);
-      iv[i] = static_cast<float>(inv);
-      if (!std::isfinite(al[i]) || !std::isfinite(iv[i]))
+      sc[i] = static_cast<float>(av / M_PI);
+      hh[i] = static_cast<float>(0.5 / (dv + 1e-9));
+      if (!std::isfinite(sc[i]) || !std::isfinite(hh[i]))
         return fail(c, VOC_BAD_WEIGHTS, "Snake parameter gives a non-finite value in " + p);
     }
-    voc_status st = upload(al.data(), ch, &sd->alpha);
+    voc_status st = upload(sc.data(), ch, &sd->alpha);
     if (st) return st;
-    return upload(iv.data(), ch, &sd->invden);
+    return upload(hh.data(), ch, &sd->invden);
   };
   // Fold one conv: v is uploaded to a staging buffer, folded into the packed layout.
   auto fold = [&](const std::string& p, int kind, int cin, int cout, int k, int stride,
@@ -1023,12 +1103,7 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
       const UnitDev& un = W.blocks[si.b].units[si.r];
       st = run_import(c, in, T_in, si.c_in, ri, rows, T, s0, &un.a1, h, s);
       if (st) return st;
-      io.x = s0; io.T_in = T; io.rate_in = 1; io.s_out = u; io.snake_next = &un.a2;
-      st = run_conv(c, un.c1, io, rows, ri.len, VOC_K_RES_K7, s);
-      if (st) return st;
-      io = ConvIO{};
-      io.x = u; io.T_in = T; io.rate_in = 1; io.h_out = h; io.res = h;
-      st = run_conv(c, un.c2, io, rows, ri.len, VOC_K_RES_K1, s);
+      st = run_res_unit(c, un, s0, s1, u, h, nullptr, nullptr, T, 1, rows, ri.len, s);
       break;
     }
     default:
@@ -1036,7 +1111,6 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
       if (st) return st;
       return run_head(c, h, T, ri, rows, 1, out, s);
   }
-  (void)s1;
   if (st) return st;
   return launch(c, s, VOC_K_EXPORT, 0.0, 8.0 * rows * si.c_out * t_out, "export launch",
                 [&] { return launch_export(h, out, rows, si.c_out, static_cast<int>(t_out), s); });

@@ -29,7 +29,7 @@ VOC_NOT_LOADED = -5
 VOC_F32, VOC_BF16 = 0, 1
 VOC_SNAKE, VOC_SNAKE_BETA = 0, 1
 
-KERNEL_KINDS = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export"]
+KERNEL_KINDS = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused"]
 
 
 class voc_config(ctypes.Structure):

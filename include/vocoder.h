@@ -185,7 +185,8 @@ typedef enum voc_kernel_kind {
   VOC_K_HEAD = 4,     /* Snake + Conv1d to one channel + tanh           */
   VOC_K_IMPORT = 5,   /* latent transpose / tile gather                 */
   VOC_K_EXPORT = 6,   /* debug-stage output transpose                   */
-  VOC_K_COUNT = 7
+  VOC_K_RES_FUSED = 7, /* whole residual unit (conv1, Snake2, conv2, add) */
+  VOC_K_COUNT = 8
 } voc_kernel_kind;
 
 typedef struct voc_profile_stat {
