@@ -165,6 +165,11 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       sal = *reinterpret_cast<const f4*>(a.s_alpha + o);
       sinv = *reinterpret_cast<const f4*>(a.s_invden + o);
     }
+    f4 hsc = f4{0.f, 0.f, 0.f, 0.f}, hsh = f4{0.f, 0.f, 0.f, 0.f};
+    if (a.hs_scale) {
+      hsc = *reinterpret_cast<const f4*>(a.hs_scale + o);
+      hsh = *reinterpret_cast<const f4*>(a.hs_h + o);
+    }
     const int64_t hbase = (static_cast<int64_t>(row) * a.Cout + (o & ~15)) * a.T_out + (o & 15);
     const int64_t sbase = (static_cast<int64_t>(row) * a.Cout + (o / CH) * CH) * a.T_out + (o % CH);
 #pragma unroll
@@ -176,7 +181,16 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       f4 v = acc[mb][nb] + bias;
       const int64_t hidx = hbase + static_cast<int64_t>(tau) * kHChunk;
       if (a.res) v += *reinterpret_cast<const f4*>(a.res + hidx);
-      if (a.h_out) *reinterpret_cast<f4*>(a.h_out + hidx) = v;
+      if (a.h_out) {
+        f4 hv = v;
+        if (a.hs_scale) {
+          hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
+          hv[1] = snake_f32(v[1], hsc[1], hsh[1]);
+          hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
+          hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
+        }
+        *reinterpret_cast<f4*>(a.h_out + hidx) = hv;
+      }
       if (a.s_out) {
         f4 sv;
         sv[0] = snake_f32(v[0], sal[0], sinv[0]);

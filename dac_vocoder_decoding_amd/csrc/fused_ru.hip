@@ -12,7 +12,8 @@
 //            (the same 64-byte chunk rows the GEMM reads);
 //   stage 2  conv2 as a GEMM (M = C, K = C) from U in LDS and conv2 weight
 //            chunks streamed into LDS;
-//   epilogue bias, residual add in place, the next layer's Snake operand.
+//   epilogue bias, residual add in place, the next layer's Snake operand
+//            (for the last unit: the head's Snake applied to the stored h).
 // Compared with separate conv1 and conv2 launches this removes the U round
 // trip through HBM (2 x C x T operands per unit) and the second launch.
 #include "internal.h"
@@ -228,6 +229,11 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
       sc = *reinterpret_cast<const f4*>(a.s_scale + m);
       hh = *reinterpret_cast<const f4*>(a.s_h + m);
     }
+    f4 hsc = f4{0.f, 0.f, 0.f, 0.f}, hsh = f4{0.f, 0.f, 0.f, 0.f};
+    if (a.hs_scale) {
+      hsc = *reinterpret_cast<const f4*>(a.hs_scale + m);
+      hsh = *reinterpret_cast<const f4*>(a.hs_h + m);
+    }
     const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
     const int64_t sbase = (static_cast<int64_t>(row) * C + (m / CH) * CH) * a.T + (m % CH);
 #pragma unroll
@@ -236,7 +242,14 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
       if (n >= Lv) continue;
       const int64_t hidx = hbase + static_cast<int64_t>(n) * kHChunk;
       f4 v = acc[mb][nb] + b2 + *reinterpret_cast<const f4*>(a.h + hidx);
-      *reinterpret_cast<f4*>(a.h + hidx) = v;
+      f4 hv = v;
+      if (a.hs_scale) {
+        hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
+        hv[1] = snake_f32(v[1], hsc[1], hsh[1]);
+        hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
+        hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
+      }
+      *reinterpret_cast<f4*>(a.h + hidx) = hv;
       if (a.s_out) {
         v[0] = snake_f32(v[0], sc[0], hh[0]);
         v[1] = snake_f32(v[1], sc[1], hh[1]);

@@ -62,6 +62,8 @@ struct ConvArgs {
   void* s_out;
   const float* s_alpha;
   const float* s_invden;
+  const float* hs_scale;  // if set, h_out receives Snake(v) with these
+  const float* hs_h;      // parameters instead of v (the head's Snake)
   int T_out, ups, crop;
 };
 
@@ -100,6 +102,8 @@ struct ResUnitArgs {
   void* s_out;           // may be null
   const float* s_scale;
   const float* s_h;
+  const float* hs_scale;  // if set, h receives Snake(h) (the head's Snake)
+  const float* hs_h;
   int n_tiles, rows;
 };
 // Frames per workgroup of the fused kernel for width C, or 0 if there is no
@@ -137,6 +141,8 @@ struct ImportArgs {
   const float* s_alpha;  // null -> identity
   const float* s_invden;
   float* h_out;     // may be null
+  const float* h_scale;  // if set, h_out receives Snake(x) with these parameters
+  const float* h_h;
 };
 hipError_t launch_import(const ImportArgs& a, hipStream_t s);
 
@@ -144,15 +150,14 @@ hipError_t launch_import(const ImportArgs& a, hipStream_t s);
 hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipStream_t s);
 
 // Head: pcm[dst[r] + tau - keep_lo[r]] = tanh(bias + sum_j sum_i w[j][i] *
-//   Snake(h[r][tau + j - 3][i])) for tau in [keep_lo[r], keep_hi[r]).
+//   sh[r][tau + j - 3][i]) for tau in [keep_lo[r], keep_hi[r]), where sh is
+// Snake_out(h), already applied by the last residual unit's epilogue.
 struct HeadArgs {
-  const float* h;   // fp32 chunked
+  const float* h;   // Snake_out(h), fp32 chunked
   int C, T;         // channels, allocated frames per row
   RowInfo rows;
   int nrows;
   int rate;         // frames per latent frame
-  const float* alpha;
-  const float* invden;
   const float* w;   // [7][C]
   float bias;
   float* pcm;

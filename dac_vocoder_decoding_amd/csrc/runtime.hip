@@ -360,6 +360,7 @@ struct ConvIO {
   const float* res;
   void* s_out;
   const SnakeDev* snake_next;  // Snake applied for s_out
+  const SnakeDev* h_snake;     // if set, h_out receives Snake(h) (the head's)
 };
 
 voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, const int* row_len,
@@ -397,6 +398,8 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.s_out = io.s_out;
   a.s_alpha = io.snake_next ? io.snake_next->alpha : nullptr;
   a.s_invden = io.snake_next ? io.snake_next->invden : nullptr;
+  a.hs_scale = io.h_snake ? io.h_snake->alpha : nullptr;
+  a.hs_h = io.h_snake ? io.h_snake->invden : nullptr;
   a.rows = rows;
   int v = pick_variant(c->op, L.taps, L.M, a.N, rows);
   if (c->force_variant[kind] >= 0 && conv_variant_ok(c->force_variant[kind], L.taps))
@@ -419,7 +422,7 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
 
 voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const RowInfo& rows,
                       int nrows, int T, void* s_out, const SnakeDev* sn, float* h_out,
-                      hipStream_t s) {
+                      hipStream_t s, const SnakeDev* h_sn = nullptr) {
   ImportArgs a{};
   a.x = x;
   a.T_src = T_src;
@@ -432,6 +435,8 @@ voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const Ro
   a.s_alpha = sn ? sn->alpha : nullptr;
   a.s_invden = sn ? sn->invden : nullptr;
   a.h_out = h_out;
+  a.h_scale = h_sn ? h_sn->alpha : nullptr;
+  a.h_h = h_sn ? h_sn->invden : nullptr;
   const double el = static_cast<double>(nrows) * T * C;
   const double bytes = el * 4 + (s_out ? el * op_size(c->op) : 0) + (h_out ? el * 4 : 0);
   return launch(c, s, VOC_K_IMPORT, 0.0, bytes, "import launch", [&] { return launch_import(a, s); });
@@ -447,8 +452,6 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
   a.rows = rows;
   a.nrows = nrows;
   a.rate = rate;
-  a.alpha = c->W.head_act.alpha;
-  a.invden = c->W.head_act.invden;
   a.w = c->W.head_w;
   a.bias = c->W.head_bias;
   a.pcm = pcm;
@@ -467,7 +470,7 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
 // two-kernel path (conv1 has finished reading s_in before conv2 runs).
 voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_spare, void* ubuf,
                         float* h, const SnakeDev* next, void** s_next, int T, int rate, int rows,
-                        const int* row_len, hipStream_t s) {
+                        const int* row_len, hipStream_t s, const SnakeDev* h_snake = nullptr) {
   const int C = u.c1.cout;
   const int bn = c->no_fuse ? 0 : res_unit_tile(c->op, C);
   if (s_next) *s_next = nullptr;
@@ -491,6 +494,8 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     a.s_out = s_out;
     a.s_scale = next ? next->alpha : nullptr;
     a.s_h = next ? next->invden : nullptr;
+    a.hs_scale = h_snake ? h_snake->alpha : nullptr;
+    a.hs_h = h_snake ? h_snake->invden : nullptr;
     a.n_tiles = (T + bn - 1) / bn;
     a.rows = rows;
     const double el = static_cast<double>(rows) * T * C;
@@ -519,6 +524,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
   io.res = h;
   io.snake_next = next;
   io.s_out = s_out;
+  io.h_snake = h_snake;
   return run_conv(c, u.c2, io, rows, row_len, VOC_K_RES_K1, s);
 }
 
@@ -561,8 +567,10 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s) 
     rate *= g.stride[b];
     for (int r = 0; r < nr; ++r) {
       void* s_next = nullptr;
+      // The last unit stores the head's Snake of h: nothing else reads h.
+      const SnakeDev* hs = (b == nb - 1 && r == nr - 1) ? &W.head_act : nullptr;
       st = run_res_unit(c, blk.units[r], B.s[cur], B.s[cur ^ 1], B.u, B.h,
-                        next_snake(W, b, r, nb, nr), &s_next, t, rate, rows, B.rows.len, s);
+                        next_snake(W, b, r, nb, nr), &s_next, t, rate, rows, B.rows.len, s, hs);
       if (st) return st;
       if (s_next == B.s[cur ^ 1]) cur ^= 1;
     }
@@ -1107,7 +1115,7 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
       break;
     }
     default:
-      st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s);
+      st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s, &W.head_act);
       if (st) return st;
       return run_head(c, h, T, ri, rows, 1, out, s);
   }

@@ -103,7 +103,12 @@ __global__ __launch_bounds__(256) void import_kernel(const ImportArgs a) {
   if (a.h_out) {
     const int64_t hidx = (static_cast<int64_t>(r) * a.C + (cc & ~15)) * a.T +
                          static_cast<int64_t>(tt) * kHChunk + (cc & 15);
-    *reinterpret_cast<f4*>(a.h_out + hidx) = v;
+    f4 hv = v;
+    if (a.h_scale) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv[e] = snake_f32(v[e], a.h_scale[cc + e], a.h_h[cc + e]);
+    }
+    *reinterpret_cast<f4*>(a.h_out + hidx) = hv;
   }
   if (a.s_out) {
     if (a.s_alpha) {
@@ -163,85 +168,67 @@ hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipSt
 
 // ---------------------------------------------------------------- head
 // Output head (minimaxmusic.cpp ARCHITECTURE, "Flow VAE": snake_out, conv_out
-// k=7 with bias, tanh).  A workgroup takes TT output frames: it stages
-// Snake(h) for frames [t0-3, t0+TT+3) in LDS, computes the seven per-tap
-// projections z_j[f] = sum_i w[j][i] S[f][i] once per staged frame, then
-// y[t] = tanh(bias + sum_j z_j[t + j - 3]).  Frames outside the row's valid
-// range read as zero (Snake(0) = 0, the conv's zero padding).
-__global__ __launch_bounds__(256) void head_kernel(const HeadArgs a, int TT) {
-  extern __shared__ float sm[];
-  const int C = a.C;
-  const int SR = C + 4;  // padded LDS row
-  const int F = TT + 6;
-  float* S = sm;
-  float* Z = sm + F * SR;
+// k=7 with bias, tanh).  Its input already holds Snake_out(h) (the last
+// residual unit's epilogue applies it), so the head is a pure stream:
+//   lane l of a wave reads frame f = o0 - 3 + l (all C channels, 64-byte
+//   chunk rows) and forms the seven per-tap projections
+//   z_j[f] = sum_i w[j][i] x[f][i];
+//   lane l (3 <= l < 61) then owns output o = f and gathers
+//   y[o] = tanh(bias + sum_j z_j[o + j - 3]) from lanes l + j - 3 with
+//   cross-lane shuffles.
+// Each wave emits 58 outputs per 64 frames read; no LDS tile, no barriers.
+// Frames outside the row's valid range read as zero (the conv's zero
+// padding; Snake(0) = 0).  The tile crop of time-tiled decoding is folded
+// into the store.
+constexpr int kHeadOut = 58;  // outputs per wave
+
+__global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   const int r = blockIdx.y;
   const int lo = a.rows.keep_lo[r], hi = a.rows.keep_hi[r];
-  const int t0 = lo + blockIdx.x * TT;
-  if (t0 >= hi) return;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int o0 = lo + wave * kHeadOut;
+  if (o0 >= hi) return;
+  const int C = a.C;
   const int Lr = min(a.rows.len[r] * a.rate, a.T);
-  const int tid = threadIdx.x;
-  const int per_chunk = F * 4;
-  const int units = per_chunk * (C / 16);
-  for (int u = tid; u < units; u += 256) {
-    const int k = u / per_chunk, rem = u - k * per_chunk;
-    const int f = rem >> 2, q = rem & 3;
-    const int c = k * 16 + q * 4;
-    const int tt = t0 - 3 + f;
-    f4 v = f4{0.f, 0.f, 0.f, 0.f};
-    if (tt >= 0 && tt < Lr) {
-      v = *reinterpret_cast<const f4*>(a.h + (static_cast<int64_t>(r) * C + k * 16) * a.T +
-                                       static_cast<int64_t>(tt) * kHChunk + q * 4);
+  const int f = o0 - 3 + lane;
+  const bool valid = f >= 0 && f < Lr;
+  const float* hp = a.h + static_cast<int64_t>(r) * C * a.T + static_cast<int64_t>(f) * kHChunk;
+  const int64_t plane = static_cast<int64_t>(a.T) * kHChunk;
+  float z[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < C / 16; ++k) {
+    f4 x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = snake_f32(v[e], a.alpha[c + e], a.invden[c + e]);
-    }
-    *reinterpret_cast<f4*>(S + f * SR + c) = v;
-  }
-  __syncthreads();
-  for (int f = tid; f < F; f += 256) {
-    float z[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const float* srow = S + f * SR;
-    for (int c = 0; c < C; c += 4) {
-      const f4 x = *reinterpret_cast<const f4*>(srow + c);
+    for (int q = 0; q < 4; ++q)
+      x[q] = valid ? *reinterpret_cast<const f4*>(hp + k * plane + q * 4) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 7; ++j) {
-        const f4 w = *reinterpret_cast<const f4*>(a.w + j * C + c);
-        z[j] = fmaf(w[0], x[0], z[j]);
-        z[j] = fmaf(w[1], x[1], z[j]);
-        z[j] = fmaf(w[2], x[2], z[j]);
-        z[j] = fmaf(w[3], x[3], z[j]);
+    for (int j = 0; j < 7; ++j) {
+      const float* wj = a.w + j * C + k * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 w = *reinterpret_cast<const f4*>(wj + q * 4);
+        z[j] = fmaf(w[0], x[q][0], z[j]);
+        z[j] = fmaf(w[1], x[q][1], z[j]);
+        z[j] = fmaf(w[2], x[q][2], z[j]);
+        z[j] = fmaf(w[3], x[q][3], z[j]);
       }
     }
-#pragma unroll
-    for (int j = 0; j < 7; ++j) Z[j * F + f] = z[j];
   }
-  __syncthreads();
-  const int64_t dst = a.rows.dst[r] - lo;
-  for (int t = tid; t < TT; t += 256) {
-    const int tt = t0 + t;
-    if (tt >= hi) break;
-    float y = a.bias;
+  float y = a.bias;
 #pragma unroll
-    for (int j = 0; j < 7; ++j) y += Z[j * F + t + j];
-    a.pcm[dst + tt] = tanhf(y);
+  for (int j = 0; j < 7; ++j) {
+    const int src = min(max(lane + j - 3, 0), 63);
+    y += __shfl(z[j], src);
   }
-}
-
-static int head_tile(int C) {
-  // Largest TT (<= 128) whose LDS footprint fits 60 KB.
-  int tt = 128;
-  while (tt > 8 && ((tt + 6) * (C + 4) + 7 * (tt + 6)) * 4 > 60 * 1024) tt >>= 1;
-  return tt;
+  const int o = f;
+  if (lane >= 3 && lane < 3 + kHeadOut && o < hi) a.pcm[a.rows.dst[r] - lo + o] = tanhf(y);
 }
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
-  const int TT = head_tile(a.C);
-  int max_keep = 0;
-  // keep ranges are host-known via T; the grid covers the allocated frames.
-  max_keep = a.T;
-  const dim3 grid(static_cast<unsigned>((max_keep + TT - 1) / TT), static_cast<unsigned>(a.nrows));
-  const size_t lds = static_cast<size_t>((TT + 6) * (a.C + 4) + 7 * (TT + 6)) * 4;
-  hipLaunchKernelGGL(head_kernel, grid, dim3(256), lds, s, a, TT);
+  // keep ranges lie inside the allocated frames; the grid covers them.
+  const int waves = (a.T + kHeadOut - 1) / kHeadOut;
+  const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(a.nrows));
+  hipLaunchKernelGGL(head_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
