@@ -58,11 +58,31 @@ _loaded = {}
 def build_library() -> None:
     """Compile both builds of oracle.c with gcc (OpenMP, no fast-math)."""
     for prec, out in _LIBS.items():
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-               "-fno-fast-math", "-ffp-contract=off", *_DEFS[prec], _SRC, "-o",
-               out + ".tmp", "-lm"]
-        subprocess.check_call(cmd)
+        compile_library(_SRC, out + ".tmp", prec)
         os.replace(out + ".tmp", out)
+
+
+def load_library(path: str, prec: str):
+    """Load one build of oracle.c and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    P, I = ctypes.c_void_p, ctypes.c_int64
+    lib.orc_real_size.restype = ctypes.c_int
+    lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_snake.argtypes = [P, P, I, I, I, P, P]
+    lib.orc_weight_norm.argtypes = [P, P, P, I, I, P]
+    lib.orc_conv1d.argtypes = [P, P, I, I, I, P, P, I, I, I]
+    lib.orc_conv_transpose1d.argtypes = [P, P, I, I, I, P, P, I, I, I, I, I]
+    lib.orc_tanh.argtypes = [P, P, I]
+    lib.orc_add.argtypes = [P, P, P, I]
+    assert lib.orc_real_size() == np.dtype(_NP[prec]).itemsize
+    return lib
+
+
+def compile_library(src: str, out: str, prec: str = "f64") -> None:
+    """Compile a C source with the oracle's flags (used for both builds)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-fno-fast-math", "-ffp-contract=off", *_DEFS[prec], src, "-o", out, "-lm"]
+    subprocess.check_call(cmd)
 
 
 def _lib(prec: str):
@@ -70,18 +90,7 @@ def _lib(prec: str):
         path = _LIBS[prec]
         if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
             build_library()
-        lib = ctypes.CDLL(path)
-        P, I = ctypes.c_void_p, ctypes.c_int64
-        lib.orc_real_size.restype = ctypes.c_int
-        lib.orc_num_threads.restype = ctypes.c_int
-        lib.orc_snake.argtypes = [P, P, I, I, I, P, P]
-        lib.orc_weight_norm.argtypes = [P, P, P, I, I, P]
-        lib.orc_conv1d.argtypes = [P, P, I, I, I, P, P, I, I, I]
-        lib.orc_conv_transpose1d.argtypes = [P, P, I, I, I, P, P, I, I, I, I, I]
-        lib.orc_tanh.argtypes = [P, P, I]
-        lib.orc_add.argtypes = [P, P, P, I]
-        assert lib.orc_real_size() == np.dtype(_NP[prec]).itemsize
-        _loaded[prec] = lib
+        _loaded[prec] = load_library(path, prec)
     return _loaded[prec]
 
 

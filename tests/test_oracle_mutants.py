@@ -1,0 +1,82 @@
+"""The pins catch plausible mistakes: each test compiles a copy of oracle.c
+with one planted mistake (on the CPU, in a temporary directory), points the
+oracle module at that build, and requires that at least one pin fails.
+
+A mutation that no pin notices would mean the pins leave that part of the
+oracle unchecked.
+"""
+import os
+
+import pytest
+
+from oracle import oracle as O
+
+import test_oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("snake_no_square", "yr[t] = xr[t] + s * s / den;", "yr[t] = xr[t] + s / den;"),
+    ("snake_no_alpha", "const REAL s = SIN(a * xr[t]);", "const REAL s = SIN(xr[t]);"),
+    ("snakebeta_uses_alpha", "const REAL den = (beta ? beta[c] : alpha[c]) + (REAL)1e-9;",
+     "const REAL den = alpha[c] + (REAL)1e-9;"),
+    ("snake_channel_as_time", "const REAL a = alpha[c];", "const REAL a = alpha[r % C];"),
+    ("fold_no_sqrt", "const REAL n = SQRT(ss);", "const REAL n = ss;"),
+    ("fold_no_g", "w[i * rest + j] = g[i] * v[i * rest + j] / n;", "w[i * rest + j] = v[i * rest + j] / n;"),
+    ("conv_flipped_taps", "const REAL wv = w[(o * Cin + i) * K + j];",
+     "const REAL wv = w[(o * Cin + i) * K + (K - 1 - j)];"),
+    ("conv_no_dilation", "const int64_t sh = j * dil - P;", "const int64_t sh = j - P;"),
+    ("conv_no_bias", "for (int64_t t = 0; t < T; ++t) yr[t] += bias[o];",
+     "for (int64_t t = 0; t < T; ++t) yr[t] += 0;"),
+    ("convt_crop_off_by_one", "const int64_t n = m * s + k - p;", "const int64_t n = m * s + k - p - 1;"),
+    ("convt_transposed_weight", "const REAL *wr = w + (i * Cout + o) * K;",
+     "const REAL *wr = w + ((o % Cin) * Cout + (i % Cout)) * K;"),
+    ("convt_no_bias", "for (int64_t n = 0; n < Tout; ++n) yr[n] += bias[o];",
+     "for (int64_t n = 0; n < Tout; ++n) yr[n] += 0;"),
+    ("no_tanh", "y[k] = TANH(x[k]);", "y[k] = x[k];"),
+    ("residual_sign", "y[k] = a[k] + b[k];", "y[k] = a[k] - b[k];"),
+]
+
+
+def _pins(orc):
+    """The oracle pins, run against whatever build `orc` currently loads."""
+    P.test_snake_closed_form_points(orc)
+    P.test_snake_double_angle_identity_and_bounds(orc)
+    P.test_snake_periodicity(orc)
+    P.test_snakebeta(orc)
+    P.test_snake_channel_indexing(orc)
+    P.test_weight_norm_invariants(orc)
+    P.test_weight_norm_axis0_of_transposed_layout(orc)
+    for d in (1, 3):
+        P.test_conv1d_brute_force(orc, d)
+        P.test_conv1d_torch_float64(orc, d)
+    P.test_conv1d_k1_is_matrix_product(orc)
+    P.test_conv1d_impulse_orientation(orc)
+    for s in (3, 4):
+        P.test_convt_equals_zero_stuffed_conv(orc, s)
+        P.test_convt_torch_float64(orc, s)
+        P.test_convt_polyphase_identity(orc, s)
+    P.test_convt_impulse_response(orc)
+    P.test_residual_unit_zero_conv2_is_identity(orc)
+    P.test_decode_matches_torch_composition(orc, (2, 2), "snake")
+    P.test_decode_matches_torch_composition(orc, (3, 2), "snakebeta")
+    P.test_golden_lengths_and_vocoder_gate(orc)
+
+
+def test_pins_pass_on_the_real_oracle():
+    _pins(O)
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, orig, bad, tmp_path, monkeypatch):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, f"mutation site not unique: {name}"
+    mutant = tmp_path / f"{name}.c"
+    mutant.write_text(src.replace(orig, bad))
+    so = tmp_path / f"{name}.so"
+    O.compile_library(str(mutant), str(so), "f64")
+    lib = O.load_library(str(so), "f64")
+    monkeypatch.setitem(O._loaded, "f64", lib)
+    with pytest.raises(AssertionError):
+        _pins(O)
