@@ -128,6 +128,27 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
 #pragma unroll
     for (int j = 0; j < WNB; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // A residual (the k=1 conv of a residual unit) is read into registers
+  // before the K loop so its HBM latency overlaps the matrix work.
+  f4 rres[WMB][WNB];
+  if constexpr (TAPS == 1) {
+    if (a.res) {
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb) {
+        const int m = m0 + wm * WMB * 16 + mb * 16 + lg * 4;
+        const int o = m % a.Cout;
+        const int64_t hbase = (static_cast<int64_t>(row) * a.Cout + (o & ~15)) * a.T_out + (o & 15);
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) {
+          const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
+          rres[mb][nb] = (m < a.M && n < Lout)
+                             ? *reinterpret_cast<const f4*>(a.res + hbase + static_cast<int64_t>(n) * kHChunk)
+                             : f4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+
   gload(0);
   for (int c = 0; c < nchunks; ++c) {
     lstore();
@@ -180,7 +201,12 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       if (tau < 0 || tau >= Lout) continue;
       f4 v = acc[mb][nb] + bias;
       const int64_t hidx = hbase + static_cast<int64_t>(tau) * kHChunk;
-      if (a.res) v += *reinterpret_cast<const f4*>(a.res + hidx);
+      if (a.res) {
+        if constexpr (TAPS == 1)
+          v += rres[mb][nb];
+        else
+          v += *reinterpret_cast<const f4*>(a.res + hidx);
+      }
       if (a.h_out) {
         f4 hv = v;
         if (a.hs_scale) {

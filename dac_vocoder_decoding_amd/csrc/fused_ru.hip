@@ -75,6 +75,26 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
 #pragma unroll
     for (int j = 0; j < WNB; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // The residual h of this tile is read into registers early, so its HBM
+  // latency overlaps the GEMM stages instead of stalling the final epilogue:
+  // at kernel start for small tiles, after stage 1 otherwise.
+  constexpr bool kEarlyH = WMB * WNB <= 8;
+  f4 hres[WMB][WNB];
+  auto load_h = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int m = wm * WMB * 16 + mb * 16 + lg * 4;
+      const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
+        hres[mb][nb] = n < Lv ? *reinterpret_cast<const f4*>(a.h + hbase + static_cast<int64_t>(n) * kHChunk)
+                              : f4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  if constexpr (kEarlyH) load_h();
+
   // ------------------------------------------------------------ stage 1
   uint4 xr[XU], wr[WU];
   auto load_x = [&](int c) {
@@ -156,6 +176,8 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
       __syncthreads();
     }
   }
+
+  if constexpr (!kEarlyH) load_h();
 
   // Fetch the first conv2 weight chunk while the U epilogue runs.
   uint4 w2r[W2U];
@@ -241,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
       const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
       if (n >= Lv) continue;
       const int64_t hidx = hbase + static_cast<int64_t>(n) * kHChunk;
-      f4 v = acc[mb][nb] + b2 + *reinterpret_cast<const f4*>(a.h + hidx);
+      f4 v = acc[mb][nb] + b2 + hres[mb][nb];
       f4 hv = v;
       if (a.hs_scale) {
         hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
