@@ -56,10 +56,22 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   const int tid = threadIdx.x;
   const int total = a.n_tiles * a.m_tiles * a.rows;
   const int L = xcd_remap(blockIdx.x, total);
-  const int n_tile = L % a.n_tiles;
-  const int rest = L / a.n_tiles;
-  const int m_tile = rest % a.m_tiles;
-  const int row = rest / a.m_tiles;
+  // Each XCD runs a contiguous range of L.  With m_fast the M-tiles that
+  // share an activation tile run side by side on one XCD, so the tile is
+  // fetched from HBM once and the rest hit L2 (chosen when all weights fit
+  // in L2 as well); otherwise one weight slice streams the activations.
+  int n_tile, m_tile, row;
+  if (a.m_fast) {
+    m_tile = L % a.m_tiles;
+    const int rest = L / a.m_tiles;
+    n_tile = rest % a.n_tiles;
+    row = rest / a.n_tiles;
+  } else {
+    n_tile = L % a.n_tiles;
+    const int rest = L / a.n_tiles;
+    m_tile = rest % a.m_tiles;
+    row = rest / a.m_tiles;
+  }
   const int n0 = n_tile * BN;
   const int m0 = m_tile * BM;
   const int len = a.row_len[row];

@@ -56,6 +56,7 @@ struct ConvArgs {
   int off0, offstep, min_off, halo;
   int N;          // GEMM positions per row
   int n_tiles, m_tiles, rows;
+  int m_fast;     // tile order: 1 = the M-tiles of one N-range are adjacent, 0 = N fastest
   const float* bias;
   float* h_out;
   const float* res;

@@ -81,6 +81,7 @@ struct voc_ctx {
   int rows_n = 0;
   int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
+  int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   std::vector<int64_t> meta_dst;  // host copies kept alive for async uploads
   std::vector<int> meta_int;
 };
@@ -406,6 +407,10 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
     v = c->force_variant[kind];
   a.n_tiles = (a.N + conv_variant_bn(v) - 1) / conv_variant_bn(v);
   a.m_tiles = (a.M + conv_variant_bm(v) - 1) / conv_variant_bm(v);
+  // Weights of at most 2 MB stay resident in a 4 MB XCD L2 next to the
+  // activation tiles, so the M-tiles of one N-range can run together.
+  const double wbytes = static_cast<double>(L.taps) * L.M * L.cin * op_size(c->op);
+  a.m_fast = c->m_order >= 0 ? c->m_order : (a.m_tiles > 1 && wbytes <= 2.0 * (1 << 20));
   // Algorithmic work: every input frame meets every tap (direct convolution).
   const double frames_in = static_cast<double>(rows) * io.T_in;
   const double flops = 2.0 * frames_in * L.cin * L.cout * (L.taps == 2 ? 2 * L.ups : L.taps);
@@ -703,6 +708,7 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   for (int k = 0; k < 4; ++k)
     if (const char* v = std::getenv(names[k])) c->force_variant[k] = std::atoi(v);
   if (const char* v = std::getenv("VOC_NO_FUSED_RES")) c->no_fuse = std::atoi(v) != 0;
+  if (const char* v = std::getenv("VOC_CONV_M_FAST")) c->m_order = std::atoi(v) != 0;
   *out = c;
   return VOC_OK;
 }
