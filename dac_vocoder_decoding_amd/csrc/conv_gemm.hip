@@ -50,8 +50,9 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   constexpr int WU = (WROWS * 4 + 255) / 256;
   static_assert(WROWS % 16 == 0, "weight rows come in groups of 16");
   static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
-  __shared__ __attribute__((aligned(16))) unsigned char Xs[XROWS * kLdsRow];
-  __shared__ __attribute__((aligned(16))) unsigned char Ws[WROWS * kLdsRow];
+  static_assert(XROWS % 16 == 0, "LDS tiles come in blocks of 16 rows");
+  __shared__ __attribute__((aligned(16))) unsigned char Xs[XROWS * kRowBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char Ws[WROWS * kRowBytes];
 
   const int tid = threadIdx.x;
   const int total = a.n_tiles * a.m_tiles * a.rows;
@@ -120,13 +121,13 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
     for (int u = 0; u < XU; ++u) {
       const int idx = tid + u * 256;
       const int r = unit_row(idx);
-      if (r < xrows) *reinterpret_cast<uint4*>(Xs + r * kLdsRow + unit_col(idx) * 16) = xr[u];
+      if (r < xrows) *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = xr[u];
     }
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
       const int idx = tid + u * 256;
       const int r = unit_row(idx);
-      if (r < WROWS) *reinterpret_cast<uint4*>(Ws + r * kLdsRow + unit_col(idx) * 16) = wr[u];
+      if (r < WROWS) *reinterpret_cast<uint4*>(Ws + lds_off(r, unit_col(idx))) = wr[u];
     }
   };
 
@@ -166,22 +167,13 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
     lstore();
     __syncthreads();
     if (c + 1 < nchunks) gload(c + 1);
-#pragma unroll
-    for (int j = 0; j < TAPS; ++j) {
-      const int xoff = a.off0 + j * a.offstep - a.min_off + wn * WNB * 16 + lr;
-      uint4 A[WMB], B[WNB];
-#pragma unroll
-      for (int mb = 0; mb < WMB; ++mb)
-        A[mb] = *reinterpret_cast<const uint4*>(
-            Ws + (j * BM + wm * WMB * 16 + mb * 16 + lr) * kLdsRow + lg * 16);
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb)
-        B[nb] = *reinterpret_cast<const uint4*>(Xs + (xoff + nb * 16) * kLdsRow + lg * 16);
-#pragma unroll
-      for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < WNB; ++nb) mfma_frag<OP>(A[mb], B[nb], acc[mb][nb]);
-    }
+    // A rows start on 16-row blocks (lane-linear reads); B rows start at the
+    // tap's shifted frame, any row.
+    const unsigned char* wt = Ws + (wm * WMB * 16) * kRowBytes + lane * 16;
+    const int xr0 = a.off0 - a.min_off + wn * WNB * 16 + lr;
+    mma_steps<OP, WMB, WNB, TAPS, TAPS == 7>(
+        acc, TAPS, [&](int j, int mb) { return wt + (j * BM + mb * 16) * kRowBytes; },
+        [&](int j, int nb) { return Xs + lds_off(xr0 + j * a.offstep, lg) + nb * 1024; });
     __syncthreads();
   }
 

@@ -23,7 +23,9 @@
 namespace voc {
 
 template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG>
-__global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N == 4 ? 2 : 1)
+void res_unit_kernel(const ResUnitArgs a) {
+  constexpr int NTH = 64 * WAVES_M * WAVES_N;  // threads per workgroup
   constexpr int CH = OpT<OP>::CH;
   constexpr int ES = OpT<OP>::ES;
   constexpr int C = WAVES_M * WMB * 16;
@@ -32,18 +34,18 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
   constexpr int NG = (7 + TG - 1) / TG;        // tap groups per channel chunk
   constexpr int WROWS = TG * C;
   constexpr int NCH = C / CH;                  // channel chunks
-  constexpr int S1 = (XROWS + WROWS) * kLdsRow;
-  constexpr int UB = NCH * BN * kLdsRow;       // U tile: [NCH][BN] rows
-  constexpr int S2 = UB + C * kLdsRow;
+  constexpr int S1 = (XROWS + WROWS) * kRowBytes;
+  constexpr int UB = NCH * BN * kRowBytes;     // U tile: [NCH][BN] rows
+  constexpr int S2 = UB + C * kRowBytes;
   constexpr int LDS = S1 > S2 ? S1 : S2;
-  constexpr int XU = (XROWS * 4 + 255) / 256;
-  constexpr int WU = (WROWS * 4 + 255) / 256;
-  constexpr int W2U = (C * 4 + 255) / 256;
-  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  constexpr int XU = (XROWS * 4 + NTH - 1) / NTH;
+  constexpr int WU = (WROWS * 4 + NTH - 1) / NTH;
+  constexpr int W2U = (C * 4 + NTH - 1) / NTH;
+  static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "four or eight waves");
   static_assert(C % CH == 0 && C % 16 == 0, "whole channel chunks");
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
   unsigned char* Xs = smem;
-  unsigned char* Ws = smem + XROWS * kLdsRow;
+  unsigned char* Ws = smem + XROWS * kRowBytes;
   unsigned char* Us = smem;          // stage 2 (after stage 1 is done)
   unsigned char* W2s = smem + UB;
 
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
     const unsigned char* xc = xrow + c * xplane;
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int idx = tid + u * 256;
+      const int idx = tid + u * NTH;
       const int r = unit_row(idx), col = unit_col(idx);
       const int t = tfirst + r;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
   auto load_w = [&](int c, int g) {
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
-      const int idx = tid + u * 256;
+      const int idx = tid + u * NTH;
       const int r = unit_row(idx), col = unit_col(idx);
       const int jj = r / C, m = r - jj * C;
       const int j = g * TG + jj;
@@ -127,17 +129,17 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
   auto store_x = [&]() {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-      const int idx = tid + u * 256;
+      const int idx = tid + u * NTH;
       const int r = unit_row(idx);
-      if (r < xrows) *reinterpret_cast<uint4*>(Xs + r * kLdsRow + unit_col(idx) * 16) = xr[u];
+      if (r < xrows) *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = xr[u];
     }
   };
   auto store_w = [&]() {
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
-      const int idx = tid + u * 256;
+      const int idx = tid + u * NTH;
       const int r = unit_row(idx);
-      if (r < WROWS) *reinterpret_cast<uint4*>(Ws + r * kLdsRow + unit_col(idx) * 16) = wr[u];
+      if (r < WROWS) *reinterpret_cast<uint4*>(Ws + lds_off(r, unit_col(idx))) = wr[u];
     }
   };
 
@@ -155,23 +157,13 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
         load_x(c + 1);
         load_w(c + 1, 0);
       }
-#pragma unroll
-      for (int jj = 0; jj < TG; ++jj) {
-        const int j = g * TG + jj;
-        if (j >= 7) break;
-        const int xoff = j * d + wn * WNB * 16 + lr;
-        uint4 A[WMB], B[WNB];
-#pragma unroll
-        for (int mb = 0; mb < WMB; ++mb)
-          A[mb] = *reinterpret_cast<const uint4*>(
-              Ws + (jj * C + wm * WMB * 16 + mb * 16 + lr) * kLdsRow + lg * 16);
-#pragma unroll
-        for (int nb = 0; nb < WNB; ++nb)
-          B[nb] = *reinterpret_cast<const uint4*>(Xs + (xoff + nb * 16) * kLdsRow + lg * 16);
-#pragma unroll
-        for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < WNB; ++nb) mfma_frag<OP>(A[mb], B[nb], acc[mb][nb]);
+      {
+        const int nt = (g + 1) * TG <= 7 ? TG : 7 - g * TG;  // taps in this group
+        const unsigned char* wt = Ws + (wm * WMB * 16) * kRowBytes + lane * 16;
+        const int xr0 = g * TG * d + wn * WNB * 16 + lr;
+        mma_steps<OP, WMB, WNB, TG, false>(
+            acc, nt, [&](int jj, int mb) { return wt + (jj * C + mb * 16) * kRowBytes; },
+            [&](int jj, int nb) { return Xs + lds_off(xr0 + jj * d, lg) + nb * 1024; });
       }
       __syncthreads();
     }
@@ -184,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
   auto load_w2 = [&](int c) {
 #pragma unroll
     for (int u = 0; u < W2U; ++u) {
-      const int idx = tid + u * 256;
+      const int idx = tid + u * NTH;
       const int r = unit_row(idx), col = unit_col(idx);
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (r < C)
@@ -202,7 +194,10 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
     const f4 b1 = *reinterpret_cast<const f4*>(a.b1 + m);
     const f4 sc = *reinterpret_cast<const f4*>(a.a2_scale + m);
     const f4 hh = *reinterpret_cast<const f4*>(a.a2_h + m);
-    unsigned char* ubase = Us + (m / CH) * BN * kLdsRow + (m % CH) * ES;
+    // U rows are frames of one channel chunk; this lane's 4 channels sit in
+    // unit (m % CH) * ES / 16 of the row, at byte (m % CH) * ES % 16.
+    const int ub = (m % CH) * ES;
+    unsigned char* ubase = Us + (m / CH) * BN * kRowBytes + (ub & 15);
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb) {
       const int nl = wn * WNB * 16 + nb * 16 + lr;
@@ -211,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
       v[1] = snake_f32(v[1], sc[1], hh[1]);
       v[2] = snake_f32(v[2], sc[2], hh[2]);
       v[3] = snake_f32(v[3], sc[3], hh[3]);
-      store_op4<OP>(ubase + nl * kLdsRow, 0, v);
+      store_op4<OP>(ubase + lds_off(nl, ub >> 4), 0, v);
       acc[mb][nb] = f4{0.f, 0.f, 0.f, 0.f};
     }
   }
@@ -220,20 +215,20 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
   for (int c = 0; c < NCH; ++c) {
 #pragma unroll
     for (int u = 0; u < W2U; ++u) {
-      const int idx = tid + u * 256;
+      const int idx = tid + u * NTH;
       const int r = unit_row(idx);
-      if (r < C) *reinterpret_cast<uint4*>(W2s + r * kLdsRow + unit_col(idx) * 16) = w2r[u];
+      if (r < C) *reinterpret_cast<uint4*>(W2s + lds_off(r, unit_col(idx))) = w2r[u];
     }
     __syncthreads();
     if (c + 1 < NCH) load_w2(c + 1);
     uint4 A[WMB], B[WNB];
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb)
-      A[mb] = *reinterpret_cast<const uint4*>(W2s + (wm * WMB * 16 + mb * 16 + lr) * kLdsRow + lg * 16);
+      A[mb] = *reinterpret_cast<const uint4*>(W2s + (wm * WMB * 16 + mb * 16) * kRowBytes + lane * 16);
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb)
       B[nb] = *reinterpret_cast<const uint4*>(
-          Us + (c * BN + wn * WNB * 16 + nb * 16 + lr) * kLdsRow + lg * 16);
+          Us + (c * BN + wn * WNB * 16 + nb * 16) * kRowBytes + lane * 16);
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
@@ -287,22 +282,36 @@ __global__ __launch_bounds__(256, 2) void res_unit_kernel(const ResUnitArgs a) {
 // Only widths where one fused launch beats the conv1 + conv2 pair on MI355X
 // (per-layer kernel traces): at C >= 256 the whole-C tile leaves too few
 // frames per workgroup (LDS holds U for all C), and the pair is faster.
+// bf16 tile per width (m-blocks, n-blocks, waves M, waves N, taps per group);
+// overridable at build time for tile sweeps.
+#ifndef VOC_BF_RU64
+#define VOC_BF_RU64 4, 2, 1, 4, 7
+#endif
+#ifndef VOC_BF_RU96
+#define VOC_BF_RU96 6, 2, 1, 4, 7
+#endif
+#ifndef VOC_BF_RU128
+#define VOC_BF_RU128 4, 4, 2, 2, 4
+#endif
+#ifndef VOC_BF_RU192
+#define VOC_BF_RU192 3, 4, 4, 1, 2
+#endif
+#define VOC_RU_(...) VOC_RU(__VA_ARGS__)
 template <int OP>
 static hipError_t launch_ru(const ResUnitArgs& a, hipStream_t s, int* bn) {
-  const dim3 block(256);
 #define VOC_RU(CW, A, B, WM, WN, TGV)                                                       \
   if (a.C == CW) {                                                                          \
     *bn = WN * B * 16;                                                                      \
     if (a.n_tiles <= 0) return hipSuccess;                                                  \
     hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV>), dim3(a.n_tiles * a.rows), \
-                       block, 0, s, a);                                                     \
+                       dim3(64 * WM * WN), 0, s, a);                                        \
     return hipGetLastError();                                                               \
   }
   if constexpr (OP == OP_BF16) {
-    VOC_RU(64, 4, 2, 1, 4, 7)
-    VOC_RU(96, 6, 2, 1, 4, 7)
-    VOC_RU(128, 4, 4, 2, 2, 4)
-    VOC_RU(192, 6, 4, 2, 2, 1)
+    VOC_RU_(64, VOC_BF_RU64)
+    VOC_RU_(96, VOC_BF_RU96)
+    VOC_RU_(128, VOC_BF_RU128)
+    VOC_RU_(192, VOC_BF_RU192)
   } else {
     VOC_RU(16, 1, 4, 1, 4, 7)
     VOC_RU(32, 2, 2, 1, 4, 7)
@@ -311,6 +320,7 @@ static hipError_t launch_ru(const ResUnitArgs& a, hipStream_t s, int* bn) {
     VOC_RU(128, 4, 2, 2, 2, 4)
   }
 #undef VOC_RU
+#undef VOC_RU_
   return hipErrorInvalidValue;
 }
 

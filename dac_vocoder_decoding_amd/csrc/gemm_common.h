@@ -43,16 +43,73 @@ __device__ __forceinline__ void mfma_frag<OP_BF16>(const uint4& a, const uint4& 
                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
+// nt (<= NT) matrix-core steps over LDS fragments: step t multiplies the WMB
+// A fragments at a_at(t, mb) with the WNB B fragments at b_at(t, nb).  The
+// fragments of step t+1 are read into a second register set before step t's
+// MFMAs issue, so LDS latency overlaps matrix work instead of stalling it.
+// Callers pass an nt that is a constant after unrolling.
+// PIN keeps that order against the scheduler, which otherwise re-serialises
+// the reads to save registers; it pays where the extra registers cost no
+// occupancy that matters (the 7-tap GEMM), not in the fused unit or the
+// 2-tap GEMM (measured per kernel).
+template <int OP, int WMB, int WNB, int NT, bool PIN, typename FA, typename FB>
+__device__ __forceinline__ void mma_steps(f4 (&acc)[WMB][WNB], int nt, FA a_at, FB b_at) {
+  uint4 A[2][WMB], B[2][WNB];
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb) A[0][mb] = *reinterpret_cast<const uint4*>(a_at(0, mb));
+#pragma unroll
+  for (int nb = 0; nb < WNB; ++nb) B[0][nb] = *reinterpret_cast<const uint4*>(b_at(0, nb));
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t >= nt) break;
+    const int cur = t & 1;
+    if (t + 1 < nt) {
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb)
+        A[cur ^ 1][mb] = *reinterpret_cast<const uint4*>(a_at(t + 1, mb));
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+        B[cur ^ 1][nb] = *reinterpret_cast<const uint4*>(b_at(t + 1, nb));
+    }
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) mfma_frag<OP>(A[cur][mb], B[cur][nb], acc[mb][nb]);
+  }
+  if constexpr (PIN) {
+    // Step 0's reads, then per step the next step's reads followed by this
+    // step's MFMAs.
+    constexpr int kMfmaPerFrag = OP == OP_F32 ? 4 : 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, WMB + WNB, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= nt) break;
+      if (t + 1 < nt) __builtin_amdgcn_sched_group_barrier(0x100, WMB + WNB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, WMB * WNB * kMfmaPerFrag, 0);
+    }
+  }
+}
+
 template <int TAPS> struct HaloMax { static constexpr int v = 0; };
 template <> struct HaloMax<7> { static constexpr int v = 54; };  // 6 * dilation 9
 template <> struct HaloMax<2> { static constexpr int v = 1; };
 
-constexpr int kLdsRow = 80;  // 64-byte chunk row + 16 bytes: conflict-free ds_read_b128
+// LDS tiles hold rows of one 64-byte channel chunk in blocks of 16 rows.
+// Inside a block the four 16-byte units of a row are stored unit-major:
+// (row, unit) lives at (row / 16) * 1024 + unit * 256 + (row % 16) * 16.
+// An MFMA fragment read (16 consecutive rows from any first row x 4 units,
+// lane = unit * 16 + row offset) and a wave's staging store (16 rows x 4
+// units) then touch every 256-byte run of LDS once, which gfx950 serves at
+// its full ds_read_b128 rate (~240 B/clk/CU measured); padded row pitches
+// (80, 144 bytes) and plain 64-byte rows measured half that.
+constexpr int kRowBytes = 64;  // LDS bytes per tile row (no padding)
+__device__ __forceinline__ int lds_off(int row, int unit) {
+  return ((row >> 4) << 10) + (unit << 8) + ((row & 15) << 4);
+}
 
 // 16-byte unit idx of a tile of 64-byte rows -> (row, column).  A wave's 64
-// lanes cover 16 consecutive rows x 4 columns, so a global load reads 16
-// whole rows and an LDS store, like the fragment reads, touches 16
-// different rows per column: no bank conflicts with the 80-byte row pitch.
+// lanes cover 16 consecutive rows x 4 columns: a global load reads 16 whole
+// rows, and the LDS store at lds_off(row, column) is one linear 1 KB block.
 __device__ __forceinline__ int unit_row(int idx) { return ((idx >> 6) << 4) + (idx & 15); }
 __device__ __forceinline__ int unit_col(int idx) { return (idx >> 4) & 3; }
 

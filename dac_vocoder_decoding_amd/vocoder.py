@@ -13,7 +13,9 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvocoder.so")
+# VOC_LIBRARY names another build of the same library (e.g. an ablation build).
+LIB_PATH = os.environ.get("VOC_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libvocoder.so")
 
 VOC_ABI_VERSION = 1
 VOC_MAX_BLOCKS = 8
