@@ -19,8 +19,10 @@
 //   X rows [n0 + min_off, n0 + BN + max_off)  (the dilation halo included)
 //   W      [TAPS][BM] rows
 // into LDS once and every tap reads its shifted window of the same X tile.
-// Loads for chunk c+1 are issued into registers before the matrix work of
-// chunk c.  The epilogue adds the bias and optionally the residual, stores
+// Chunks stream through an NS-stage LDS ring by global -> LDS DMA: chunk
+// c + NS - 1 is requested before the matrix work of chunk c, so NS - 1
+// chunks of loads are in flight behind the math (one barrier per chunk).
+// The epilogue adds the bias and optionally the residual, stores
 // the fp32 result and/or the next layer's Snake of it in the operand dtype,
 // so every Snake is evaluated once per element.
 //
@@ -38,7 +40,7 @@ namespace voc {
 
 // TAG only separates kernel names per layer kind (conv_in vs residual k7)
 // so that profilers report them apart; it does not change the code.
-template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG>
+template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG, int NS>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   constexpr int CH = OpT<OP>::CH;
   constexpr int ES = OpT<OP>::ES;
@@ -46,13 +48,13 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   constexpr int BN = WAVES_N * WNB * 16;
   constexpr int XROWS = (BN + HaloMax<TAPS>::v + 15) / 16 * 16;
   constexpr int WROWS = TAPS * BM;
-  constexpr int XU = (XROWS * 4 + 255) / 256;
-  constexpr int WU = (WROWS * 4 + 255) / 256;
-  static_assert(WROWS % 16 == 0, "weight rows come in groups of 16");
+  constexpr int XB = XROWS / 16, WB = WROWS / 16, TB = XB + WB;  // 1 KB blocks per stage
+  constexpr int STAGE = TB * 1024;
+  constexpr int LW = TB / 4;  // fewest blocks any wave issues per stage
+  static_assert(BM % 16 == 0 && XROWS % 16 == 0, "LDS tiles come in blocks of 16 rows");
   static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
-  static_assert(XROWS % 16 == 0, "LDS tiles come in blocks of 16 rows");
-  __shared__ __attribute__((aligned(16))) unsigned char Xs[XROWS * kRowBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char Ws[WROWS * kRowBytes];
+  static_assert(NS == 1 || (NS - 2) * LW <= 63, "loads in flight must fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE];
 
   const int tid = threadIdx.x;
   const int total = a.n_tiles * a.m_tiles * a.rows;
@@ -81,7 +83,6 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   // The whole tile lies beyond this row's valid output: nothing to do.
   if (n0 * a.ups - a.crop >= Lout) return;
 
-  const int xrows = BN + a.halo;
   const int tfirst = n0 + a.min_off;
   const int nchunks = a.Cin / CH;
   const unsigned char* xrow = static_cast<const unsigned char*>(a.x) +
@@ -90,50 +91,35 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   const unsigned char* wbase = static_cast<const unsigned char*>(a.w);
   const int64_t wplane = static_cast<int64_t>(TAPS) * a.M * kChunkBytes;
 
-  uint4 xr[XU], wr[WU];
-  auto gload = [&](int c) {
-    const unsigned char* xc = xrow + c * xplane;
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int idx = tid + u * 256;
-      const int r = unit_row(idx), col = unit_col(idx);
-      const int t = tfirst + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < xrows && t >= 0 && t < Lin)
-        v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
-      xr[u] = v;
-    }
-    const unsigned char* wc = wbase + c * wplane;
-#pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const int idx = tid + u * 256;
-      const int r = unit_row(idx), col = unit_col(idx);
-      const int j = r / BM, mm = r - j * BM;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < WROWS && m0 + mm < a.M)
-        v = *reinterpret_cast<const uint4*>(
-            wc + (static_cast<int64_t>(j) * a.M + m0 + mm) * kChunkBytes + col * 16);
-      wr[u] = v;
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int idx = tid + u * 256;
-      const int r = unit_row(idx);
-      if (r < xrows) *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = xr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const int idx = tid + u * 256;
-      const int r = unit_row(idx);
-      if (r < WROWS) *reinterpret_cast<uint4*>(Ws + lds_off(r, unit_col(idx))) = wr[u];
-    }
-  };
-
-  const int wave = tid >> 6, lane = tid & 63;
+  // The wave index is uniform per wave; readfirstlane lets the compiler keep
+  // it (and the DMA's LDS addresses derived from it) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int lr = lane & 15, lg = lane >> 4;
+
+  // Stage one chunk: block b < XB holds X rows 16b.. (frames tfirst + row;
+  // frames outside [0, Lin) read as zero); block XB + k holds weight rows
+  // 16k.. of the [TAPS][BM] tile (rows past M read the next tap's rows or
+  // zeros and only feed output rows that the epilogue drops).  Block b is
+  // copied by wave b % 4.
+  const uint32_t smem_lds = lds_addr(smem);
+  const uint32_t xv0 = static_cast<uint32_t>((tfirst + lr) * kChunkBytes + lg * 16);
+  const uint32_t wv0 = static_cast<uint32_t>((m0 + lr) * kChunkBytes + lg * 16);
+  auto issue = [&](int c, int stage) {
+    const i4 xs = buf_rsrc(xrow + c * xplane, static_cast<uint32_t>(Lin) * kChunkBytes);
+    const i4 ws = buf_rsrc(wbase + c * wplane, static_cast<uint32_t>(wplane));
+    const uint32_t dst = smem_lds + stage * STAGE;
+#pragma unroll
+    for (int u = 0; u < (TB + 3) / 4; ++u) {
+      const int b = wave + 4 * u;
+      if (b < XB) {
+        dma16(xs, xv0 + b * 1024, dst + b * 1024);
+      } else if (b < TB) {
+        const int k = b - XB, j = (16 * k) / BM;
+        dma16(ws, wv0 + (j * a.M + 16 * k - j * BM) * kChunkBytes, dst + b * 1024);
+      }
+    }
+  };
 
   f4 acc[WMB][WNB];
 #pragma unroll
@@ -162,11 +148,81 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
     }
   }
 
-  gload(0);
+  if constexpr (NS == 1) {
+    // Register-staged single buffer: the loads of chunk c+1 are issued into
+    // registers before chunk c's matrix work and stored to LDS after it.
+    // Fewer LDS bytes per workgroup than the ring (more workgroups per CU),
+    // which pays where the matrix work per chunk is short (bf16).
+    constexpr int XU = (XROWS * 4 + 255) / 256;
+    constexpr int WU = (WROWS * 4 + 255) / 256;
+    const int xrows = BN + a.halo;
+    uint4 xr[XU], wr[WU];
+    auto gload = [&](int c) {
+      const unsigned char* xc = xrow + c * xplane;
+#pragma unroll
+      for (int u = 0; u < XU; ++u) {
+        const int idx = tid + u * 256;
+        const int r = unit_row(idx), col = unit_col(idx);
+        const int t = tfirst + r;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < xrows && t >= 0 && t < Lin)
+          v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
+        xr[u] = v;
+      }
+      const unsigned char* wc = wbase + c * wplane;
+#pragma unroll
+      for (int u = 0; u < WU; ++u) {
+        const int idx = tid + u * 256;
+        const int r = unit_row(idx), col = unit_col(idx);
+        const int j = r / BM, mm = r - j * BM;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < WROWS && m0 + mm < a.M)
+          v = *reinterpret_cast<const uint4*>(
+              wc + (static_cast<int64_t>(j) * a.M + m0 + mm) * kChunkBytes + col * 16);
+        wr[u] = v;
+      }
+    };
+    unsigned char* Xs = smem;
+    unsigned char* Ws = smem + XROWS * kRowBytes;
+    gload(0);
+    for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+      for (int u = 0; u < XU; ++u) {
+        const int idx = tid + u * 256;
+        const int r = unit_row(idx);
+        if (r < xrows) *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = xr[u];
+      }
+#pragma unroll
+      for (int u = 0; u < WU; ++u) {
+        const int idx = tid + u * 256;
+        const int r = unit_row(idx);
+        if (r < WROWS) *reinterpret_cast<uint4*>(Ws + lds_off(r, unit_col(idx))) = wr[u];
+      }
+      __syncthreads();
+      if (c + 1 < nchunks) gload(c + 1);
+      const unsigned char* wt = Ws + (wm * WMB * 16) * kRowBytes + lane * 16;
+      const int xr0 = a.off0 - a.min_off + wn * WNB * 16 + lr;
+      mma_steps<OP, WMB, WNB, TAPS, TAPS == 7>(
+          acc, TAPS, [&](int j, int mb) { return wt + (j * BM + mb * 16) * kRowBytes; },
+          [&](int j, int nb) { return Xs + lds_off(xr0 + j * a.offstep, lg) + nb * 1024; });
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nchunks) issue(s, s);
+  int stage = 0;
   for (int c = 0; c < nchunks; ++c) {
-    lstore();
-    __syncthreads();
-    if (c + 1 < nchunks) gload(c + 1);
+    // Chunk c has landed once at most (NS - 2) newer stages are in flight
+    // (fewer near the end: then wait for everything).
+    if (c + NS - 1 <= nchunks)
+      wait_vm<(NS - 2) * LW>();
+    else
+      wait_vm<0>();
+    lds_barrier();  // every wave's copy of chunk c is in; chunk c-1's reads are done
+    if (c + NS - 1 < nchunks) issue(c + NS - 1, stage == 0 ? NS - 1 : stage - 1);
+    const unsigned char* Xs = smem + stage * STAGE;
+    const unsigned char* Ws = Xs + XROWS * kRowBytes;
     // A rows start on 16-row blocks (lane-linear reads); B rows start at the
     // tap's shifted frame, any row.
     const unsigned char* wt = Ws + (wm * WMB * 16) * kRowBytes + lane * 16;
@@ -174,7 +230,8 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
     mma_steps<OP, WMB, WNB, TAPS, TAPS == 7>(
         acc, TAPS, [&](int j, int mb) { return wt + (j * BM + mb * 16) * kRowBytes; },
         [&](int j, int nb) { return Xs + lds_off(xr0 + j * a.offstep, lg) + nb * 1024; });
-    __syncthreads();
+    stage = stage + 1 == NS ? 0 : stage + 1;
+  }
   }
 
   // Epilogue.
@@ -253,14 +310,29 @@ bool conv_variant_ok(int v, int taps) {
   return true;
 }
 
+// LDS ring depth per tap count: the 7-tap GEMM has long matrix work per
+// chunk, the 1- and 2-tap GEMMs need more chunks in flight to hide latency.
+// NS = 1 selects the register-staged single buffer.
+#ifndef VOC_NS_F32
+#define VOC_NS_F32 2, 3, 4  // taps 7, 2, 1
+#endif
+#ifndef VOC_NS_BF16
+#define VOC_NS_BF16 1, 1, 4
+#endif
+template <int OP, int TAPS> struct Stages {
+  static constexpr int f[3] = {VOC_NS_F32}, b[3] = {VOC_NS_BF16};
+  static constexpr int v = (OP == OP_F32 ? f : b)[TAPS == 7 ? 0 : TAPS == 2 ? 1 : 2];
+};
+
 template <int OP, int TAPS, int TAG>
 static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
+  constexpr int NS = Stages<OP, TAPS>::v;
   const int total = a.n_tiles * a.m_tiles * a.rows;
   const dim3 grid(total), block(256);
   switch (variant) {
 #define VOC_CASE(V, A, B, C, D)                                                            \
   case V:                                                                                  \
-    hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG>), grid, block, 0, s, a); \
+    hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS>), grid, block, 0, s, a); \
     break;
     VOC_CASE(CV_64x256, 4, 4, 1, 4)
     VOC_CASE(CV_96x256, 6, 4, 1, 4)
@@ -269,7 +341,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 #define VOC_CASE(V, A, B, C, D)                                                              \
   case V:                                                                                    \
     if constexpr (TAPS != 7) {                                                               \
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG>), grid, block, 0, s, a); \
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS>), grid, block, 0, s, a); \
       break;                                                                                 \
     }                                                                                        \
     return hipErrorInvalidValue;

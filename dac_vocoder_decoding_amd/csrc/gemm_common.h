@@ -107,6 +107,55 @@ __device__ __forceinline__ int lds_off(int row, int unit) {
   return ((row >> 4) << 10) + (unit << 8) + ((row & 15) << 4);
 }
 
+// ---------------------------------------------------------------- LDS DMA
+// Tiles are copied global -> LDS by buffer loads with the LDS flag: lane l's
+// 16 bytes land at LDS byte (M0 + 16 l), so one wave instruction fills one
+// 1 KB block of 16 rows x 4 units in exactly the lds_off layout when lane l
+// reads row (l % 16), unit (l / 16).  No registers hold the data in flight,
+// which lets a kernel keep several chunks in flight.  A buffer resource
+// bounds every read to [base, base + bytes): offsets at or past the end,
+// including negative ones (they wrap to large unsigned values), read as
+// zero, which is the convolution's zero padding.  The loads count in vmcnt;
+// the compiler does not see them, so kernels wait with wait_vm<N>() and
+// synchronise with lds_barrier().
+typedef int i4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i4 buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));                 // num_records
+  r.w = 0x00020000;                                                               // 32-bit data format
+  return r;
+}
+
+// LDS byte offset of a generic pointer to LDS (its low 32 bits).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// One wave-wide copy: 16 bytes at byte offset voff of rsrc -> LDS lds + 16 * lane.
+// Writing M0 needs one wait state before an LDS-DMA instruction reads it.
+__device__ __forceinline__ void dma16(i4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier after this wave's LDS reads have completed.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // 16-byte unit idx of a tile of 64-byte rows -> (row, column).  A wave's 64
 // lanes cover 16 consecutive rows x 4 columns: a global load reads 16 whole
 // rows, and the LDS store at lds_off(row, column) is one linear 1 KB block.
