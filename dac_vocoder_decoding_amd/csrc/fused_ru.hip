@@ -266,7 +266,7 @@ void res_unit_kernel(const ResUnitArgs a) {
         hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
         hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
       }
-      *reinterpret_cast<f4*>(a.h + hidx) = hv;
+      if (a.store_h) *reinterpret_cast<f4*>(a.h + hidx) = hv;
       if (a.s_out) {
         v[0] = snake_f32(v[0], sc[0], hh[0]);
         v[1] = snake_f32(v[1], sc[1], hh[1]);

@@ -100,6 +100,7 @@ struct ResUnitArgs {
   const void* w2;        // packed [C/CH][1][C][CH]
   const float* b2;
   float* h;              // residual stream, in place
+  int store_h;           // 0: the updated h is not stored (nothing reads it)
   void* s_out;           // may be null
   const float* s_scale;
   const float* s_h;

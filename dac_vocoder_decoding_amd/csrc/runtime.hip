@@ -475,7 +475,8 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
 // two-kernel path (conv1 has finished reading s_in before conv2 runs).
 voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_spare, void* ubuf,
                         float* h, const SnakeDev* next, void** s_next, int T, int rate, int rows,
-                        const int* row_len, hipStream_t s, const SnakeDev* h_snake = nullptr) {
+                        const int* row_len, hipStream_t s, const SnakeDev* h_snake = nullptr,
+                        bool keep_h = true) {
   const int C = u.c1.cout;
   const int bn = c->no_fuse ? 0 : res_unit_tile(c->op, C);
   if (s_next) *s_next = nullptr;
@@ -496,6 +497,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     a.w2 = u.c2.w;
     a.b2 = u.c2.bias;
     a.h = h;
+    a.store_h = keep_h ? 1 : 0;
     a.s_out = s_out;
     a.s_scale = next ? next->alpha : nullptr;
     a.s_h = next ? next->invden : nullptr;
@@ -506,7 +508,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     const double el = static_cast<double>(rows) * T * C;
     const double es = op_size(c->op);
     const double flops = 2.0 * el * C * 8;
-    const double bytes = el * (es + 8 + (s_out ? es : 0)) + 8.0 * C * C * es;
+    const double bytes = el * (es + 4 + (keep_h ? 4 : 0) + (s_out ? es : 0)) + 8.0 * C * C * es;
     const int op = c->op;
     return launch(c, s, VOC_K_RES_FUSED, flops, bytes, "residual unit launch",
                   [&] { return launch_res_unit(op, a, s); });
@@ -525,7 +527,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
   io.x = ubuf;
   io.T_in = T;
   io.rate_in = rate;
-  io.h_out = h;
+  io.h_out = keep_h ? h : nullptr;
   io.res = h;
   io.snake_next = next;
   io.s_out = s_out;
@@ -574,8 +576,12 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s) 
       void* s_next = nullptr;
       // The last unit stores the head's Snake of h: nothing else reads h.
       const SnakeDev* hs = (b == nb - 1 && r == nr - 1) ? &W.head_act : nullptr;
+      // The last unit of any other block feeds the next block only through
+      // its Snake operand; its h is never read again.
+      const bool keep_h = !(r == nr - 1 && b < nb - 1);
       st = run_res_unit(c, blk.units[r], B.s[cur], B.s[cur ^ 1], B.u, B.h,
-                        next_snake(W, b, r, nb, nr), &s_next, t, rate, rows, B.rows.len, s, hs);
+                        next_snake(W, b, r, nb, nr), &s_next, t, rate, rows, B.rows.len, s, hs,
+                        keep_h);
       if (st) return st;
       if (s_next == B.s[cur ^ 1]) cur ^= 1;
     }
