@@ -136,12 +136,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // One wave-wide copy: 16 bytes at byte offset voff of rsrc -> LDS lds + 16 * lane.
-// Writing M0 needs one wait state before an LDS-DMA instruction reads it.
+// M0 carries the LDS address; the compiler reserves M0, so its value is saved
+// and restored around the copy.  Writing M0 needs one wait state before an
+// LDS-DMA instruction reads it.
 __device__ __forceinline__ void dma16(i4 rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(lds)
-               : "memory", "m0");
+  // lds is uniform across the wave; readfirstlane keeps it in an SGPR even
+  // where the compiler cannot prove that.
+  lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds)));
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds)
+      : "memory");
 }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding.
