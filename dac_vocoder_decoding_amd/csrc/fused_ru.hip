@@ -284,6 +284,12 @@ void res_unit_kernel(const ResUnitArgs a) {
 // frames per workgroup (LDS holds U for all C), and the pair is faster.
 // bf16 tile per width (m-blocks, n-blocks, waves M, waves N, taps per group);
 // overridable at build time for tile sweeps.
+#ifndef VOC_F32_RU64
+#define VOC_F32_RU64 4, 4, 1, 4, 7
+#endif
+#ifndef VOC_F32_RU128
+#define VOC_F32_RU128 4, 4, 2, 2, 4
+#endif
 #ifndef VOC_BF_RU64
 #define VOC_BF_RU64 4, 2, 1, 4, 7
 #endif
@@ -315,9 +321,9 @@ static hipError_t launch_ru(const ResUnitArgs& a, hipStream_t s, int* bn) {
   } else {
     VOC_RU(16, 1, 4, 1, 4, 7)
     VOC_RU(32, 2, 2, 1, 4, 7)
-    VOC_RU(64, 4, 2, 1, 4, 7)
+    VOC_RU_(64, VOC_F32_RU64)
     VOC_RU(96, 6, 2, 1, 4, 7)
-    VOC_RU(128, 4, 2, 2, 2, 4)
+    VOC_RU_(128, VOC_F32_RU128)
   }
 #undef VOC_RU
 #undef VOC_RU_
