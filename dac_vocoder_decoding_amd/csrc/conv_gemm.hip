@@ -128,21 +128,22 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
     for (int j = 0; j < WNB; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
   // A residual (the k=1 conv of a residual unit) is read into registers
-  // before the K loop so its HBM latency overlaps the matrix work.
+  // before the K loop so its HBM latency overlaps the matrix work.  The
+  // loads are unconditional (row and frame clamped into range; clamped
+  // values are never stored): conditional loads make the compiler wait for
+  // each one at the branch join, which serialises the prefetch.
   f4 rres[WMB][WNB];
   if constexpr (TAPS == 1) {
     if (a.res) {
 #pragma unroll
       for (int mb = 0; mb < WMB; ++mb) {
-        const int m = m0 + wm * WMB * 16 + mb * 16 + lg * 4;
+        const int m = min(m0 + wm * WMB * 16 + mb * 16 + lg * 4, a.M - 4);
         const int o = m % a.Cout;
         const int64_t hbase = (static_cast<int64_t>(row) * a.Cout + (o & ~15)) * a.T_out + (o & 15);
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb) {
-          const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
-          rres[mb][nb] = (m < a.M && n < Lout)
-                             ? *reinterpret_cast<const f4*>(a.res + hbase + static_cast<int64_t>(n) * kHChunk)
-                             : f4{0.f, 0.f, 0.f, 0.f};
+          const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, a.T_out - 1);
+          rres[mb][nb] = *reinterpret_cast<const f4*>(a.res + hbase + static_cast<int64_t>(n) * kHChunk);
         }
       }
     }

@@ -89,9 +89,10 @@ void res_unit_kernel(const ResUnitArgs a) {
       const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
-        const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
-        hres[mb][nb] = n < Lv ? *reinterpret_cast<const f4*>(a.h + hbase + static_cast<int64_t>(n) * kHChunk)
-                              : f4{0.f, 0.f, 0.f, 0.f};
+        // Unconditional load (frame clamped into the row; clamped values
+        // are never stored), so the prefetch is not serialised.
+        const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, a.T - 1);
+        hres[mb][nb] = *reinterpret_cast<const f4*>(a.h + hbase + static_cast<int64_t>(n) * kHChunk);
       }
     }
   };

@@ -331,7 +331,7 @@ int pick_variant(int op, int taps, int M, int N, int rows) {
   static const double f32[CV_COUNT]   = {0.60, 0.90, 0.85, 0.90, 1.00, 0.70};
   static const double bf_t2[CV_COUNT] = {0.90, 0.80, 0.85, 1.00, 0.75, 0.92};
   static const double bf_t7[CV_COUNT] = {0.00, 1.00, 1.00, 0.00, 0.88, 0.00};
-  static const double bf_t1[CV_COUNT] = {0.46, 0.94, 0.80, 0.95, 1.00, 0.68};
+  static const double bf_t1[CV_COUNT] = {0.46, 0.94, 0.80, 1.00, 0.95, 0.68};
   const double* speed = op == OP_F32 ? f32 : taps == 2 ? bf_t2 : taps == 7 ? bf_t7 : bf_t1;
   int best = CV_64x128;
   double best_score = -1.0;
