@@ -283,8 +283,10 @@ void res_unit_kernel(const ResUnitArgs a) {
 // Only widths where one fused launch beats the conv1 + conv2 pair on MI355X
 // (per-layer kernel traces): at C >= 256 the whole-C tile leaves too few
 // frames per workgroup (LDS holds U for all C), and the pair is faster.
-// bf16 tile per width (m-blocks, n-blocks, waves M, waves N, taps per group);
-// overridable at build time for tile sweeps.
+// Tiles per dtype and width (m-blocks, n-blocks, waves M, waves N, taps per
+// group): a large-frame tile, the fastest in per-layer traces of the full
+// workloads on MI355X, and a half-frame tile for launches too short to give
+// the large one two workgroups per CU.  Overridable at build time for sweeps.
 #ifndef VOC_F32_RU64
 #define VOC_F32_RU64 4, 4, 1, 4, 7
 #endif
@@ -292,22 +294,22 @@ void res_unit_kernel(const ResUnitArgs a) {
 #define VOC_F32_RU128 4, 4, 2, 2, 4
 #endif
 #ifndef VOC_BF_RU64
-#define VOC_BF_RU64 4, 2, 1, 4, 7
+#define VOC_BF_RU64 4, 4, 1, 4, 7
 #endif
 #ifndef VOC_BF_RU96
-#define VOC_BF_RU96 6, 2, 1, 4, 7
+#define VOC_BF_RU96 6, 4, 1, 4, 7
 #endif
 #ifndef VOC_BF_RU128
-#define VOC_BF_RU128 4, 4, 2, 2, 4
+#define VOC_BF_RU128 4, 4, 2, 4, 4
 #endif
 #ifndef VOC_BF_RU192
-#define VOC_BF_RU192 3, 4, 4, 1, 2
+#define VOC_BF_RU192 3, 4, 4, 2, 2
 #endif
 #define VOC_RU_(...) VOC_RU(__VA_ARGS__)
 template <int OP>
-static hipError_t launch_ru(const ResUnitArgs& a, hipStream_t s, int* bn) {
-#define VOC_RU(CW, A, B, WM, WN, TGV)                                                       \
-  if (a.C == CW) {                                                                          \
+static hipError_t launch_ru(const ResUnitArgs& a, bool big, hipStream_t s, int* bn) {
+#define VOC_RU(CW, BIG, A, B, WM, WN, TGV)                                                  \
+  if (a.C == CW && big == BIG) {                                                            \
     *bn = WN * B * 16;                                                                      \
     if (a.n_tiles <= 0) return hipSuccess;                                                  \
     hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV>), dim3(a.n_tiles * a.rows), \
@@ -315,35 +317,41 @@ static hipError_t launch_ru(const ResUnitArgs& a, hipStream_t s, int* bn) {
     return hipGetLastError();                                                               \
   }
   if constexpr (OP == OP_BF16) {
-    VOC_RU_(64, VOC_BF_RU64)
-    VOC_RU_(96, VOC_BF_RU96)
-    VOC_RU_(128, VOC_BF_RU128)
-    VOC_RU_(192, VOC_BF_RU192)
+    VOC_RU_(64, true, VOC_BF_RU64)
+    VOC_RU(64, false, 4, 2, 1, 4, 7)
+    VOC_RU_(96, true, VOC_BF_RU96)
+    VOC_RU(96, false, 6, 2, 1, 4, 7)
+    VOC_RU_(128, true, VOC_BF_RU128)
+    VOC_RU(128, false, 4, 4, 2, 2, 4)
+    VOC_RU_(192, true, VOC_BF_RU192)
+    VOC_RU(192, false, 3, 4, 4, 1, 2)
   } else {
-    VOC_RU(16, 1, 4, 1, 4, 7)
-    VOC_RU(32, 2, 2, 1, 4, 7)
-    VOC_RU_(64, VOC_F32_RU64)
-    VOC_RU(96, 6, 2, 1, 4, 7)
-    VOC_RU_(128, VOC_F32_RU128)
+    VOC_RU(16, false, 1, 4, 1, 4, 7)
+    VOC_RU(32, false, 2, 2, 1, 4, 7)
+    VOC_RU_(64, true, VOC_F32_RU64)
+    VOC_RU(64, false, 4, 2, 1, 4, 7)
+    VOC_RU(96, false, 6, 2, 1, 4, 7)
+    VOC_RU_(128, true, VOC_F32_RU128)
+    VOC_RU(128, false, 4, 2, 2, 2, 4)
   }
 #undef VOC_RU
 #undef VOC_RU_
   return hipErrorInvalidValue;
 }
 
-int res_unit_tile(int op, int C) {
+int res_unit_tile(int op, int C, bool big) {
   int bn = 0;
   ResUnitArgs probe{};
   probe.C = C;
   probe.n_tiles = 0;
-  const hipError_t e = op == OP_F32 ? launch_ru<OP_F32>(probe, nullptr, &bn)
-                                    : launch_ru<OP_BF16>(probe, nullptr, &bn);
+  const hipError_t e = op == OP_F32 ? launch_ru<OP_F32>(probe, big, nullptr, &bn)
+                                    : launch_ru<OP_BF16>(probe, big, nullptr, &bn);
   return e == hipSuccess ? bn : 0;
 }
 
-hipError_t launch_res_unit(int op, const ResUnitArgs& a, hipStream_t s) {
+hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s) {
   int bn = 0;
-  return op == OP_F32 ? launch_ru<OP_F32>(a, s, &bn) : launch_ru<OP_BF16>(a, s, &bn);
+  return op == OP_F32 ? launch_ru<OP_F32>(a, big, s, &bn) : launch_ru<OP_BF16>(a, big, s, &bn);
 }
 
 }  // namespace voc

@@ -110,8 +110,9 @@ struct ResUnitArgs {
 };
 // Frames per workgroup of the fused kernel for width C, or 0 if there is no
 // fused instance for (op, C).
-int res_unit_tile(int op, int C);
-hipError_t launch_res_unit(int op, const ResUnitArgs& a, hipStream_t s);
+// big selects the large-frame tile of that width (0 if it has none).
+int res_unit_tile(int op, int C, bool big);
+hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s);
 
 // Weight-norm fold + cast + repack, one workgroup per axis-0 slice.
 enum PackKind { PACK_CONV = 0, PACK_CONVT = 1, PACK_HEAD = 2 };

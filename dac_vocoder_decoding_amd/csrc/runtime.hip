@@ -478,7 +478,10 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
                         const int* row_len, hipStream_t s, const SnakeDev* h_snake = nullptr,
                         bool keep_h = true) {
   const int C = u.c1.cout;
-  const int bn = c->no_fuse ? 0 : res_unit_tile(c->op, C);
+  // The large-frame tile where it still gives two workgroups per CU.
+  const int bn_big = c->no_fuse ? 0 : res_unit_tile(c->op, C, true);
+  const bool big = bn_big > 0 && static_cast<int64_t>((T + bn_big - 1) / bn_big) * rows >= 2 * 256;
+  const int bn = c->no_fuse ? 0 : (big ? bn_big : res_unit_tile(c->op, C, false));
   if (s_next) *s_next = nullptr;
   if (bn > 0) {
     void* s_out = next ? s_spare : nullptr;
@@ -511,7 +514,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     const double bytes = el * (es + 4 + (keep_h ? 4 : 0) + (s_out ? es : 0)) + 8.0 * C * C * es;
     const int op = c->op;
     return launch(c, s, VOC_K_RES_FUSED, flops, bytes, "residual unit launch",
-                  [&] { return launch_res_unit(op, a, s); });
+                  [&] { return launch_res_unit(op, a, big, s); });
   }
   void* s_out = next ? const_cast<void*>(s_in) : nullptr;
   if (s_next) *s_next = s_out;
