@@ -73,6 +73,7 @@ struct voc_ctx {
   size_t ws_cap = 0;
   // profiling
   bool prof = false;
+  uint32_t prof_kinds = 0;  // kinds timed with events (0 = all)
   std::vector<ProfRec> pending;
   std::vector<hipEvent_t> free_events;
   voc_profile_stat stats[VOC_K_COUNT]{};
@@ -188,16 +189,18 @@ hipEvent_t take_event(voc_ctx* c) {
 voc_status finalize_profile(voc_ctx* c) {
   for (auto& r : c->pending) {
     float ms = 0.f;
-    hipError_t e = hipEventSynchronize(r.e1);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.e0, r.e1);
-    if (e != hipSuccess) return hip_fail(c, e, "profile event");
+    if (r.e0) {  // a timed launch
+      hipError_t e = hipEventSynchronize(r.e1);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.e0, r.e1);
+      if (e != hipSuccess) return hip_fail(c, e, "profile event");
+      c->free_events.push_back(r.e0);
+      c->free_events.push_back(r.e1);
+    }
     auto& st = c->stats[r.kind];
     st.launches += 1;
     st.ms += ms;
     st.flops += r.flops;
     st.bytes += r.bytes;
-    c->free_events.push_back(r.e0);
-    c->free_events.push_back(r.e1);
   }
   c->pending.clear();
   return VOC_OK;
@@ -208,7 +211,8 @@ template <class F>
 voc_status launch(voc_ctx* c, hipStream_t s, int kind, double flops, double bytes, const char* what,
                   F&& fn) {
   ProfRec rec{kind, flops, bytes, nullptr, nullptr};
-  if (c->prof) {
+  const bool timed = c->prof && (c->prof_kinds == 0 || ((c->prof_kinds >> kind) & 1u));
+  if (timed) {
     rec.e0 = take_event(c);
     rec.e1 = take_event(c);
     if (!rec.e0 || !rec.e1) return fail(c, VOC_DEVICE_ERROR, "hipEventCreate failed");
@@ -216,10 +220,8 @@ voc_status launch(voc_ctx* c, hipStream_t s, int kind, double flops, double byte
   }
   hipError_t e = fn();
   if (e != hipSuccess) return hip_fail(c, e, what);
-  if (c->prof) {
-    (void)hipEventRecord(rec.e1, s);
-    c->pending.push_back(rec);
-  }
+  if (timed) (void)hipEventRecord(rec.e1, s);
+  if (c->prof) c->pending.push_back(rec);
   return VOC_OK;
 }
 
@@ -988,6 +990,12 @@ VOC_API void vocoder_destroy(voc_ctx* c) {
 VOC_API voc_status vocoder_profile_enable(voc_ctx* c, int enable) {
   if (!c) return VOC_INVALID_PARAMS;
   c->prof = enable != 0;
+  return VOC_OK;
+}
+
+VOC_API voc_status vocoder_profile_select(voc_ctx* c, uint32_t kinds) {
+  if (!c || (kinds >> VOC_K_COUNT) != 0) return VOC_INVALID_PARAMS;
+  c->prof_kinds = kinds;
   return VOC_OK;
 }
 

@@ -97,6 +97,7 @@ def lib():
             "vocoder_last_error": (ctypes.c_char_p, [P]),
             "vocoder_destroy": (None, [P]),
             "vocoder_profile_enable": (I, [P, I]),
+            "vocoder_profile_select": (I, [P, ctypes.c_uint32]),
             "vocoder_profile_reset": (I, [P]),
             "vocoder_profile_read": (I, [P, I, ctypes.POINTER(voc_profile_stat)]),
             "voc_dbg_stage_count": (I, [P]),
@@ -221,6 +222,11 @@ def vocoder_destroy(ctx) -> None:
 
 def vocoder_profile_enable(ctx, enable: bool) -> int:
     return lib().vocoder_profile_enable(ctx, int(bool(enable)))
+
+
+def vocoder_profile_select(ctx, kinds: int) -> int:
+    """Time only the kernel kinds whose bit (1 << kind) is set; 0 = all."""
+    return lib().vocoder_profile_select(ctx, int(kinds))
 
 
 def vocoder_profile_reset(ctx) -> int:

@@ -197,6 +197,12 @@ typedef struct voc_profile_stat {
 } voc_profile_stat;
 
 voc_status vocoder_profile_enable(voc_ctx *ctx, int enable);
+/* Restrict the event pairs to the kinds whose bit (1u << kind) is set in
+ * `kinds`; 0 (the default) times every kind.  Launches of other kinds are
+ * still counted with their algorithmic work, with ms = 0, and cost no
+ * events (events between launches lengthen the gaps between kernels).
+ * INVALID_PARAMS for a NULL context or bits at or above VOC_K_COUNT. */
+voc_status vocoder_profile_select(voc_ctx *ctx, uint32_t kinds);
 voc_status vocoder_profile_reset(voc_ctx *ctx);
 voc_status vocoder_profile_read(voc_ctx *ctx, int kind, voc_profile_stat *out);
 

@@ -145,3 +145,27 @@ def test_copy_kernel_and_stream_argument():
     s.synchronize()
     assert torch.equal(dst, src)
     assert V.voc_dbg_copy(dst, src, 10, s) == V.VOC_INVALID_PARAMS
+
+
+def test_profile_select_times_only_selected_kinds(weights):
+    ctx = V.open_context(CFG, weights)
+    try:
+        x = to_dev(I.make_latent(CFG, batch=2, frames=20))
+        V.decode(ctx, x)
+        convt = V.KERNEL_KINDS.index("convt")
+        assert V.vocoder_profile_select(ctx, 1 << len(V.KERNEL_KINDS)) == V.VOC_INVALID_PARAMS
+        V.check(V.vocoder_profile_reset(ctx))
+        V.check(V.vocoder_profile_select(ctx, 1 << convt))
+        V.check(V.vocoder_profile_enable(ctx, True))
+        V.decode(ctx, x)
+        V.check(V.vocoder_profile_enable(ctx, False))
+        V.check(V.vocoder_profile_select(ctx, 0))
+        for k, n in enumerate(V.KERNEL_KINDS):
+            st, s = V.vocoder_profile_read(ctx, k)
+            assert st == V.VOC_OK
+            if n == "convt":
+                assert s["launches"] == 4 and s["ms"] > 0
+            elif n in ("conv_in", "head", "import"):
+                assert s["launches"] == 1 and s["ms"] == 0 and (n == "import" or s["flops"] > 0)
+    finally:
+        V.vocoder_destroy(ctx)
