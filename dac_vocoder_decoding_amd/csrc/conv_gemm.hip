@@ -236,56 +236,139 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   }
 
   // Epilogue.
+  if constexpr (OP == OP_BF16 && TAPS == 1) {
+    // bf16: the two 16-row blocks of a 32-channel chunk are finished
+    // together; one lane exchange (lane ^ 16) gives every lane 8 contiguous
+    // channels of the Snake operand, so each frame's 64-byte operand row is
+    // written as four 16-byte stores (not eight 8-byte half-row pieces).
+    // (Measured faster for the 1-tap GEMM, whose epilogue stores dominate;
+    // the 2- and 7-tap GEMMs lose occupancy to the extra registers and keep
+    // the plain path.)
+    static_assert(WMB % 2 == 0, "16-row blocks come in chunk pairs");
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int mb = 0; mb < WMB; ++mb) {
-    const int m = m0 + wm * WMB * 16 + mb * 16 + lg * 4;
-    if (m >= a.M) continue;
-    const int ph = m / a.Cout;
-    const int o = m - ph * a.Cout;
-    const f4 bias = *reinterpret_cast<const f4*>(a.bias + o);
-    f4 sal = f4{0.f, 0.f, 0.f, 0.f}, sinv = f4{0.f, 0.f, 0.f, 0.f};
-    if (a.s_out) {
-      sal = *reinterpret_cast<const f4*>(a.s_alpha + o);
-      sinv = *reinterpret_cast<const f4*>(a.s_invden + o);
-    }
-    f4 hsc = f4{0.f, 0.f, 0.f, 0.f}, hsh = f4{0.f, 0.f, 0.f, 0.f};
-    if (a.hs_scale) {
-      hsc = *reinterpret_cast<const f4*>(a.hs_scale + o);
-      hsh = *reinterpret_cast<const f4*>(a.hs_h + o);
-    }
-    const int64_t hbase = (static_cast<int64_t>(row) * a.Cout + (o & ~15)) * a.T_out + (o & 15);
-    const int64_t sbase = (static_cast<int64_t>(row) * a.Cout + (o / CH) * CH) * a.T_out + (o % CH);
+    for (int mp = 0; mp < WMB; mp += 2) {
+      const int m = m0 + wm * WMB * 16 + mp * 16 + lg * 4;  // first block's rows
+      if (m >= a.M) continue;                               // uniform per wave
+      const int ph = m / a.Cout;
+      const int o = m - ph * a.Cout;                        // channels o.., o+16..
+      f4 bias[2], sal[2], sinv[2], hsc[2], hsh[2];
 #pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) {
-      const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
-      if (n >= a.N) continue;
-      const int tau = n * a.ups + ph - a.crop;
-      if (tau < 0 || tau >= Lout) continue;
-      f4 v = acc[mb][nb] + bias;
-      const int64_t hidx = hbase + static_cast<int64_t>(tau) * kHChunk;
-      if (a.res) {
-        if constexpr (TAPS == 1)
-          v += rres[mb][nb];
-        else
-          v += *reinterpret_cast<const f4*>(a.res + hidx);
-      }
-      if (a.h_out) {
-        f4 hv = v;
-        if (a.hs_scale) {
-          hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
-          hv[1] = snake_f32(v[1], hsc[1], hsh[1]);
-          hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
-          hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
+      for (int q = 0; q < 2; ++q) {
+        bias[q] = *reinterpret_cast<const f4*>(a.bias + o + 16 * q);
+        sal[q] = sinv[q] = hsc[q] = hsh[q] = f4{0.f, 0.f, 0.f, 0.f};
+        if (a.s_out) {
+          sal[q] = *reinterpret_cast<const f4*>(a.s_alpha + o + 16 * q);
+          sinv[q] = *reinterpret_cast<const f4*>(a.s_invden + o + 16 * q);
         }
-        *reinterpret_cast<f4*>(a.h_out + hidx) = hv;
+        if (a.hs_scale) {
+          hsc[q] = *reinterpret_cast<const f4*>(a.hs_scale + o + 16 * q);
+          hsh[q] = *reinterpret_cast<const f4*>(a.hs_h + o + 16 * q);
+        }
       }
+      const int oc = o - lg * 4;                            // chunk's first channel
+      const int cofs = (lg & 1) * 16 + (lg & 2) * 4;        // this lane's 8 channels
+      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout + oc) * a.T_out + cofs;
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
+        const int tau = n * a.ups + ph - a.crop;
+        const bool ok = n < a.N && tau >= 0 && tau < Lout;
+        u4v pk;  // packed Snake operand: blocks 0 and 1 (2 dwords each)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          f4 v = acc[mp + q][nb] + bias[q];
+          const int oq = o + 16 * q;
+          const int64_t hidx = (static_cast<int64_t>(row) * a.Cout + (oq & ~15)) * a.T_out + (oq & 15) +
+                               static_cast<int64_t>(tau) * kHChunk;
+          if (a.res) {
+            if constexpr (TAPS == 1)
+              v += rres[mp + q][nb];
+            else if (ok)
+              v += *reinterpret_cast<const f4*>(a.res + hidx);
+          }
+          if (a.h_out && ok) {
+            f4 hv = v;
+            if (a.hs_scale) {
+              hv[0] = snake_f32(v[0], hsc[q][0], hsh[q][0]);
+              hv[1] = snake_f32(v[1], hsc[q][1], hsh[q][1]);
+              hv[2] = snake_f32(v[2], hsc[q][2], hsh[q][2]);
+              hv[3] = snake_f32(v[3], hsc[q][3], hsh[q][3]);
+            }
+            *reinterpret_cast<f4*>(a.h_out + hidx) = hv;
+          }
+          pk[2 * q] = pack_bf16x2(snake_f32(v[0], sal[q][0], sinv[q][0]), snake_f32(v[1], sal[q][1], sinv[q][1]));
+          pk[2 * q + 1] = pack_bf16x2(snake_f32(v[2], sal[q][2], sinv[q][2]), snake_f32(v[3], sal[q][3], sinv[q][3]));
+        }
+        if (a.s_out) {  // uniform: every lane takes part in the exchange
+          // Even lg keeps block 0 and takes its partner's block 0; odd lg
+          // keeps block 1 and takes its partner's block 1.
+          const bool odd = lg & 1;
+          const uint32_t s0 = __shfl_xor(static_cast<int>(odd ? pk[0] : pk[2]), 16);
+          const uint32_t s1 = __shfl_xor(static_cast<int>(odd ? pk[1] : pk[3]), 16);
+          u4v out;
+          if (odd) {
+            out[0] = s0; out[1] = s1; out[2] = pk[2]; out[3] = pk[3];
+          } else {
+            out[0] = pk[0]; out[1] = pk[1]; out[2] = s0; out[3] = s1;
+          }
+          if (ok)
+            *reinterpret_cast<u4v*>(static_cast<uint16_t*>(a.s_out) + sbase + static_cast<int64_t>(tau) * CH) = out;
+        }
+      }
+    }
+  } else {
+  #pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int m = m0 + wm * WMB * 16 + mb * 16 + lg * 4;
+      if (m >= a.M) continue;
+      const int ph = m / a.Cout;
+      const int o = m - ph * a.Cout;
+      const f4 bias = *reinterpret_cast<const f4*>(a.bias + o);
+      f4 sal = f4{0.f, 0.f, 0.f, 0.f}, sinv = f4{0.f, 0.f, 0.f, 0.f};
       if (a.s_out) {
-        f4 sv;
-        sv[0] = snake_f32(v[0], sal[0], sinv[0]);
-        sv[1] = snake_f32(v[1], sal[1], sinv[1]);
-        sv[2] = snake_f32(v[2], sal[2], sinv[2]);
-        sv[3] = snake_f32(v[3], sal[3], sinv[3]);
-        store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(tau) * CH, sv);
+        sal = *reinterpret_cast<const f4*>(a.s_alpha + o);
+        sinv = *reinterpret_cast<const f4*>(a.s_invden + o);
+      }
+      f4 hsc = f4{0.f, 0.f, 0.f, 0.f}, hsh = f4{0.f, 0.f, 0.f, 0.f};
+      if (a.hs_scale) {
+        hsc = *reinterpret_cast<const f4*>(a.hs_scale + o);
+        hsh = *reinterpret_cast<const f4*>(a.hs_h + o);
+      }
+      const int64_t hbase = (static_cast<int64_t>(row) * a.Cout + (o & ~15)) * a.T_out + (o & 15);
+      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout + (o / CH) * CH) * a.T_out + (o % CH);
+  #pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
+        if (n >= a.N) continue;
+        const int tau = n * a.ups + ph - a.crop;
+        if (tau < 0 || tau >= Lout) continue;
+        f4 v = acc[mb][nb] + bias;
+        const int64_t hidx = hbase + static_cast<int64_t>(tau) * kHChunk;
+        if (a.res) {
+          if constexpr (TAPS == 1)
+            v += rres[mb][nb];
+          else
+            v += *reinterpret_cast<const f4*>(a.res + hidx);
+        }
+        if (a.h_out) {
+          f4 hv = v;
+          if (a.hs_scale) {
+            hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
+            hv[1] = snake_f32(v[1], hsc[1], hsh[1]);
+            hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
+            hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
+          }
+          *reinterpret_cast<f4*>(a.h_out + hidx) = hv;
+        }
+        if (a.s_out) {
+          f4 sv;
+          sv[0] = snake_f32(v[0], sal[0], sinv[0]);
+          sv[1] = snake_f32(v[1], sal[1], sinv[1]);
+          sv[2] = snake_f32(v[2], sal[2], sinv[2]);
+          sv[3] = snake_f32(v[3], sal[3], sinv[3]);
+          store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(tau) * CH, sv);
+        }
       }
     }
   }
