@@ -238,42 +238,108 @@ void res_unit_kernel(const ResUnitArgs a) {
   }
 
   // ----------------------------------- epilogue 2: bias, skip, next Snake
+  if constexpr (OP == OP_BF16 && WMB % 2 == 0) {
+    // The two 16-row blocks of a 32-channel chunk are finished together and
+    // one lane exchange (lane ^ 16) gives each lane 8 contiguous operand
+    // channels: each frame's 64-byte operand row is written as four 16-byte
+    // stores instead of eight 8-byte half-row pieces.
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int mb = 0; mb < WMB; ++mb) {
-    const int m = wm * WMB * 16 + mb * 16 + lg * 4;
-    const f4 b2 = *reinterpret_cast<const f4*>(a.b2 + m);
-    f4 sc = f4{0.f, 0.f, 0.f, 0.f}, hh = f4{0.f, 0.f, 0.f, 0.f};
-    if (a.s_out) {
-      sc = *reinterpret_cast<const f4*>(a.s_scale + m);
-      hh = *reinterpret_cast<const f4*>(a.s_h + m);
-    }
-    f4 hsc = f4{0.f, 0.f, 0.f, 0.f}, hsh = f4{0.f, 0.f, 0.f, 0.f};
-    if (a.hs_scale) {
-      hsc = *reinterpret_cast<const f4*>(a.hs_scale + m);
-      hsh = *reinterpret_cast<const f4*>(a.hs_h + m);
-    }
-    const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
-    const int64_t sbase = (static_cast<int64_t>(row) * C + (m / CH) * CH) * a.T + (m % CH);
+    for (int mp = 0; mp < WMB; mp += 2) {
+      const int m = wm * WMB * 16 + mp * 16 + lg * 4;  // first block's rows
+      f4 b2[2], sc[2], hh[2], hsc[2], hsh[2];
 #pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) {
-      const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
-      if (n >= Lv) continue;
-      const int64_t hidx = hbase + static_cast<int64_t>(n) * kHChunk;
-      f4 v = acc[mb][nb] + b2 + hres[mb][nb];
-      f4 hv = v;
-      if (a.hs_scale) {
-        hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
-        hv[1] = snake_f32(v[1], hsc[1], hsh[1]);
-        hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
-        hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
+      for (int q = 0; q < 2; ++q) {
+        b2[q] = *reinterpret_cast<const f4*>(a.b2 + m + 16 * q);
+        sc[q] = hh[q] = hsc[q] = hsh[q] = f4{0.f, 0.f, 0.f, 0.f};
+        if (a.s_out) {
+          sc[q] = *reinterpret_cast<const f4*>(a.s_scale + m + 16 * q);
+          hh[q] = *reinterpret_cast<const f4*>(a.s_h + m + 16 * q);
+        }
+        if (a.hs_scale) {
+          hsc[q] = *reinterpret_cast<const f4*>(a.hs_scale + m + 16 * q);
+          hsh[q] = *reinterpret_cast<const f4*>(a.hs_h + m + 16 * q);
+        }
       }
-      if (a.store_h) *reinterpret_cast<f4*>(a.h + hidx) = hv;
+      const int mc = m - lg * 4;                       // chunk's first channel
+      const int cofs = (lg & 1) * 16 + (lg & 2) * 4;   // this lane's 8 channels
+      const int64_t sbase = (static_cast<int64_t>(row) * C + mc) * a.T + cofs;
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
+        const bool ok = n < Lv;
+        u4v pk;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int mq = m + 16 * q;
+          const f4 v = acc[mp + q][nb] + b2[q] + hres[mp + q][nb];
+          if (a.store_h && ok) {
+            f4 hv = v;
+            if (a.hs_scale) {
+              hv[0] = snake_f32(v[0], hsc[q][0], hsh[q][0]);
+              hv[1] = snake_f32(v[1], hsc[q][1], hsh[q][1]);
+              hv[2] = snake_f32(v[2], hsc[q][2], hsh[q][2]);
+              hv[3] = snake_f32(v[3], hsc[q][3], hsh[q][3]);
+            }
+            *reinterpret_cast<f4*>(a.h + (static_cast<int64_t>(row) * C + (mq & ~15)) * a.T + (mq & 15) +
+                                   static_cast<int64_t>(n) * kHChunk) = hv;
+          }
+          pk[2 * q] = pack_bf16x2(snake_f32(v[0], sc[q][0], hh[q][0]), snake_f32(v[1], sc[q][1], hh[q][1]));
+          pk[2 * q + 1] = pack_bf16x2(snake_f32(v[2], sc[q][2], hh[q][2]), snake_f32(v[3], sc[q][3], hh[q][3]));
+        }
+        if (a.s_out) {  // uniform: every lane takes part in the exchange
+          const bool odd = lg & 1;
+          const uint32_t s0 = __shfl_xor(static_cast<int>(odd ? pk[0] : pk[2]), 16);
+          const uint32_t s1 = __shfl_xor(static_cast<int>(odd ? pk[1] : pk[3]), 16);
+          u4v out;
+          if (odd) {
+            out[0] = s0; out[1] = s1; out[2] = pk[2]; out[3] = pk[3];
+          } else {
+            out[0] = pk[0]; out[1] = pk[1]; out[2] = s0; out[3] = s1;
+          }
+          if (ok)
+            *reinterpret_cast<u4v*>(static_cast<uint16_t*>(a.s_out) + sbase + static_cast<int64_t>(n) * CH) = out;
+        }
+      }
+    }
+  } else {
+  #pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int m = wm * WMB * 16 + mb * 16 + lg * 4;
+      const f4 b2 = *reinterpret_cast<const f4*>(a.b2 + m);
+      f4 sc = f4{0.f, 0.f, 0.f, 0.f}, hh = f4{0.f, 0.f, 0.f, 0.f};
       if (a.s_out) {
-        v[0] = snake_f32(v[0], sc[0], hh[0]);
-        v[1] = snake_f32(v[1], sc[1], hh[1]);
-        v[2] = snake_f32(v[2], sc[2], hh[2]);
-        v[3] = snake_f32(v[3], sc[3], hh[3]);
-        store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(n) * CH, v);
+        sc = *reinterpret_cast<const f4*>(a.s_scale + m);
+        hh = *reinterpret_cast<const f4*>(a.s_h + m);
+      }
+      f4 hsc = f4{0.f, 0.f, 0.f, 0.f}, hsh = f4{0.f, 0.f, 0.f, 0.f};
+      if (a.hs_scale) {
+        hsc = *reinterpret_cast<const f4*>(a.hs_scale + m);
+        hsh = *reinterpret_cast<const f4*>(a.hs_h + m);
+      }
+      const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
+      const int64_t sbase = (static_cast<int64_t>(row) * C + (m / CH) * CH) * a.T + (m % CH);
+  #pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
+        if (n >= Lv) continue;
+        const int64_t hidx = hbase + static_cast<int64_t>(n) * kHChunk;
+        f4 v = acc[mb][nb] + b2 + hres[mb][nb];
+        f4 hv = v;
+        if (a.hs_scale) {
+          hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
+          hv[1] = snake_f32(v[1], hsc[1], hsh[1]);
+          hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
+          hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
+        }
+        if (a.store_h) *reinterpret_cast<f4*>(a.h + hidx) = hv;
+        if (a.s_out) {
+          v[0] = snake_f32(v[0], sc[0], hh[0]);
+          v[1] = snake_f32(v[1], sc[1], hh[1]);
+          v[2] = snake_f32(v[2], sc[2], hh[2]);
+          v[3] = snake_f32(v[3], sc[3], hh[3]);
+          store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(n) * CH, v);
+        }
       }
     }
   }
