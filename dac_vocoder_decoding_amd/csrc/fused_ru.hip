@@ -12,18 +12,43 @@
 //            (the same 64-byte chunk rows the GEMM reads);
 //   stage 2  conv2 as a GEMM (M = C, K = C) from U in LDS and conv2 weight
 //            chunks streamed into LDS;
-//   epilogue bias, residual add in place, the next layer's Snake operand
-//            (for the last unit: the head's Snake applied to the stored h).
+//   epilogue bias, residual add, the next layer's Snake operand if one is
+//            asked for (for the last unit: the head's Snake applied to the
+//            stored h).
 // Compared with separate conv1 and conv2 launches this removes the U round
 // trip through HBM (2 x C x T operands per unit) and the second launch.
+//
+// Operand source (template flag XH):
+//   XH = false  S is an operand tensor written by the producer's epilogue,
+//               and h is updated in place;
+//   XH = true   S = Snake1(h_in) is computed here while the X tile is staged
+//               from the fp32 residual stream, and the result goes to a
+//               second buffer h (tiles read neighbouring frames of h_in, so
+//               the update cannot be in place).  The producer then writes no
+//               operand tensor: per channel-frame the unit moves 8 bytes of h
+//               (read + write) instead of h plus two operand passes, and the
+//               residual rows of each channel chunk are read right after that
+//               chunk's X tile, from lines the X loads have just brought into
+//               the L2.  Snake1 gives bit-identical operands either way.
 #include "internal.h"
 #include "device_math.h"
 #include "gemm_common.h"
 
 namespace voc {
 
-template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N == 4 ? 2 : 1)
+// Largest accumulator tile (m-blocks x n-blocks per wave) whose residual rows
+// are held in registers from their chunk's X load to the final epilogue.
+#ifndef VOC_RU_CHUNK_H_MAX
+#define VOC_RU_CHUNK_H_MAX 8
+#endif
+
+// Workgroups per CU asked of the register allocator for four-wave instances.
+#ifndef VOC_RU_MINB4
+#define VOC_RU_MINB4 2
+#endif
+
+template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG, bool XH>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N == 4 ? VOC_RU_MINB4 : 1)
 void res_unit_kernel(const ResUnitArgs a) {
   constexpr int NTH = 64 * WAVES_M * WAVES_N;  // threads per workgroup
   constexpr int CH = OpT<OP>::CH;
@@ -37,7 +62,8 @@ void res_unit_kernel(const ResUnitArgs a) {
   constexpr int S1 = (XROWS + WROWS) * kRowBytes;
   constexpr int UB = NCH * BN * kRowBytes;     // U tile: [NCH][BN] rows
   constexpr int S2 = UB + C * kRowBytes;
-  constexpr int LDS = S1 > S2 ? S1 : S2;
+  constexpr int LDS_T = S1 > S2 ? S1 : S2;
+  constexpr int LDS = LDS_T + (XH ? 2 * C * 4 : 0);  // + Snake1 parameters
   constexpr int XU = (XROWS * 4 + NTH - 1) / NTH;
   constexpr int WU = (WROWS * 4 + NTH - 1) / NTH;
   constexpr int W2U = (C * 4 + NTH - 1) / NTH;
@@ -80,37 +106,79 @@ void res_unit_kernel(const ResUnitArgs a) {
   // The residual h of this tile is read into registers early, so its HBM
   // latency overlaps the GEMM stages instead of stalling the final epilogue:
   // at kernel start for small tiles, after stage 1 otherwise.
-  constexpr bool kEarlyH = WMB * WNB <= 8;
+  // With XH the rows of each channel chunk are read right after its X tile
+  // instead (see load_x), register room permitting.
+  constexpr bool kEarlyH = !XH && WMB * WNB <= 8;
+  constexpr bool kChunkH = XH && WMB * WNB <= VOC_RU_CHUNK_H_MAX;
   f4 hres[WMB][WNB];
+  auto load_h_block = [&](int mb) {
+    const int m = wm * WMB * 16 + mb * 16 + lg * 4;
+    const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) {
+      // Unconditional load (frame clamped into the row; clamped values
+      // are never stored), so the prefetch is not serialised.
+      const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, a.T - 1);
+      hres[mb][nb] = *reinterpret_cast<const f4*>(a.h_in + hbase + static_cast<int64_t>(n) * kHChunk);
+    }
+  };
   auto load_h = [&]() {
 #pragma unroll
-    for (int mb = 0; mb < WMB; ++mb) {
-      const int m = wm * WMB * 16 + mb * 16 + lg * 4;
-      const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb) {
-        // Unconditional load (frame clamped into the row; clamped values
-        // are never stored), so the prefetch is not serialised.
-        const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, a.T - 1);
-        hres[mb][nb] = *reinterpret_cast<const f4*>(a.h + hbase + static_cast<int64_t>(n) * kHChunk);
-      }
-    }
+    for (int mb = 0; mb < WMB; ++mb) load_h_block(mb);
   };
   if constexpr (kEarlyH) load_h();
 
   // ------------------------------------------------------------ stage 1
-  uint4 xr[XU], wr[WU];
+  // Staging unit idx covers frame tfirst + unit_row(idx) and the 16 operand
+  // bytes at unit_col(idx) of the chunk row; unit_col(idx) == lg for every u,
+  // so each thread stages the same 16 / ES channels of every chunk row.
+  constexpr int HV = XH ? 16 / ES / 4 : 1;  // fp32 h quads per staging unit
+  uint4 xr[XH ? 1 : XU], wr[WU];
+  f4 xh[XH ? XU : 1][HV];
+  // Snake1 parameters (scale[C], h[C]) in LDS: read at staging time
+  // rather than held in registers across the matrix work.
+  float* P1 = reinterpret_cast<float*>(smem + LDS_T);
+  int xch = 0;  // first channel of this thread's staging units (chunk of the last load_x)
+  if constexpr (XH) {
+    for (int i = tid; i < C / 4; i += NTH) {
+      reinterpret_cast<f4*>(P1)[i] = reinterpret_cast<const f4*>(a.a1_scale)[i];
+      reinterpret_cast<f4*>(P1 + C)[i] = reinterpret_cast<const f4*>(a.a1_h)[i];
+    }
+    __syncthreads();
+  }
   auto load_x = [&](int c) {
-    const unsigned char* xc = xrow + c * xplane;
+    if constexpr (XH) {
+      const int ch = c * CH + lg * (16 / ES);
+      xch = ch;
+      const float* hp = a.h_in + (static_cast<int64_t>(row) * C + (ch & ~15)) * a.T + (ch & 15);
 #pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int idx = tid + u * NTH;
-      const int r = unit_row(idx), col = unit_col(idx);
-      const int t = tfirst + r;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < xrows && t >= 0 && t < Lv)
-        v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
-      xr[u] = v;
+      for (int u = 0; u < XU; ++u) {
+        const int r = unit_row(tid + u * NTH);
+        const int t = tfirst + r;
+        const bool in = r < xrows && t >= 0 && t < Lv;
+#pragma unroll
+        for (int v = 0; v < HV; ++v)
+          xh[u][v] = in ? *reinterpret_cast<const f4*>(hp + static_cast<int64_t>(t) * kHChunk + 4 * v)
+                        : f4{0.f, 0.f, 0.f, 0.f};
+      }
+      // Residual rows of this chunk's channels, while the X lines are in L2.
+      if constexpr (kChunkH) {
+#pragma unroll
+        for (int mb = 0; mb < WMB; ++mb)
+          if ((wm * WMB * 16 + mb * 16) / CH == c) load_h_block(mb);
+      }
+    } else {
+      const unsigned char* xc = xrow + c * xplane;
+#pragma unroll
+      for (int u = 0; u < XU; ++u) {
+        const int idx = tid + u * NTH;
+        const int r = unit_row(idx), col = unit_col(idx);
+        const int t = tfirst + r;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < xrows && t >= 0 && t < Lv)
+          v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
+        xr[u] = v;
+      }
     }
   };
   auto load_w = [&](int c, int g) {
@@ -132,7 +200,34 @@ void res_unit_kernel(const ResUnitArgs a) {
     for (int u = 0; u < XU; ++u) {
       const int idx = tid + u * NTH;
       const int r = unit_row(idx);
-      if (r < xrows) *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = xr[u];
+      if (r >= xrows) continue;
+      uint4 v;
+      if constexpr (XH) {
+        // Snake1 in fp32, then the operand dtype; frames outside the row
+        // are the convolution's zero padding.
+        const int t = tfirst + r;
+        const bool in = t >= 0 && t < Lv;
+        float y[4 * HV];
+#pragma unroll
+        for (int q = 0; q < HV; ++q) {
+          const f4 ps = *reinterpret_cast<const f4*>(P1 + xch + 4 * q);
+          const f4 ph = *reinterpret_cast<const f4*>(P1 + C + xch + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[4 * q + e] = in ? snake_f32(xh[u][q][e], ps[e], ph[e]) : 0.f;
+        }
+        if constexpr (OP == OP_BF16) {
+          v.x = pack_bf16x2(y[0], y[1]);
+          v.y = pack_bf16x2(y[2], y[3]);
+          v.z = pack_bf16x2(y[4], y[5]);
+          v.w = pack_bf16x2(y[6], y[7]);
+        } else {
+          v = make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                         __float_as_uint(y[3]));
+        }
+      } else {
+        v = xr[u];
+      }
+      *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = v;
     }
   };
   auto store_w = [&]() {
@@ -170,7 +265,7 @@ void res_unit_kernel(const ResUnitArgs a) {
     }
   }
 
-  if constexpr (!kEarlyH) load_h();
+  if constexpr (!kEarlyH && !kChunkH) load_h();
 
   // Fetch the first conv2 weight chunk while the U epilogue runs.
   uint4 w2r[W2U];
@@ -284,8 +379,10 @@ void res_unit_kernel(const ResUnitArgs a) {
             *reinterpret_cast<f4*>(a.h + (static_cast<int64_t>(row) * C + (mq & ~15)) * a.T + (mq & 15) +
                                    static_cast<int64_t>(n) * kHChunk) = hv;
           }
-          pk[2 * q] = pack_bf16x2(snake_f32(v[0], sc[q][0], hh[q][0]), snake_f32(v[1], sc[q][1], hh[q][1]));
-          pk[2 * q + 1] = pack_bf16x2(snake_f32(v[2], sc[q][2], hh[q][2]), snake_f32(v[3], sc[q][3], hh[q][3]));
+          if (a.s_out) {
+            pk[2 * q] = pack_bf16x2(snake_f32(v[0], sc[q][0], hh[q][0]), snake_f32(v[1], sc[q][1], hh[q][1]));
+            pk[2 * q + 1] = pack_bf16x2(snake_f32(v[2], sc[q][2], hh[q][2]), snake_f32(v[3], sc[q][3], hh[q][3]));
+          }
         }
         if (a.s_out) {  // uniform: every lane takes part in the exchange
           const bool odd = lg & 1;
@@ -374,13 +471,17 @@ void res_unit_kernel(const ResUnitArgs a) {
 #define VOC_RU_(...) VOC_RU(__VA_ARGS__)
 template <int OP>
 static hipError_t launch_ru(const ResUnitArgs& a, bool big, hipStream_t s, int* bn) {
-#define VOC_RU(CW, BIG, A, B, WM, WN, TGV)                                                  \
-  if (a.C == CW && big == BIG) {                                                            \
-    *bn = WN * B * 16;                                                                      \
-    if (a.n_tiles <= 0) return hipSuccess;                                                  \
-    hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV>), dim3(a.n_tiles * a.rows), \
-                       dim3(64 * WM * WN), 0, s, a);                                        \
-    return hipGetLastError();                                                               \
+#define VOC_RU(CW, BIG, A, B, WM, WN, TGV)                                                          \
+  if (a.C == CW && big == BIG) {                                                                    \
+    *bn = WN * B * 16;                                                                              \
+    if (a.n_tiles <= 0) return hipSuccess;                                                          \
+    if (a.x_from_h)                                                                                 \
+      hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, true>), dim3(a.n_tiles * a.rows),  \
+                         dim3(64 * WM * WN), 0, s, a);                                              \
+    else                                                                                            \
+      hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, false>), dim3(a.n_tiles * a.rows), \
+                         dim3(64 * WM * WN), 0, s, a);                                              \
+    return hipGetLastError();                                                                       \
   }
   if constexpr (OP == OP_BF16) {
     VOC_RU_(64, true, VOC_BF_RU64)
@@ -414,6 +515,14 @@ int res_unit_tile(int op, int C, bool big) {
                                     : launch_ru<OP_BF16>(probe, big, nullptr, &bn);
   return e == hipSuccess ? bn : 0;
 }
+
+// Widths whose units take Snake1 from h (x_from_h).  Per-layer kernel traces
+// of the full workloads on MI355X: the ConvTranspose1d feeding such a block
+// saves 15-23 % (no operand tensor written) and the first two units 2-14 %,
+// while the last unit of a block is 3-9 % slower (Snake1 at staging sits
+// between barriers).  A net gain at every width but bf16 C = 96, whose
+// large tile spills registers with the raw h staging.
+bool res_unit_from_h_ok(int op, int C) { return !(op == OP_BF16 && C == 96); }
 
 hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s) {
   int bn = 0;

@@ -86,10 +86,16 @@ hipError_t launch_conv(int op, int taps, int variant, bool conv_in, const ConvAr
                        hipStream_t s);
 
 // One fused residual unit over all C channels of BN-frame tiles:
-//   h <- h + conv2(Snake2(conv1_dil(x) + b1)) + b2;  s_out <- Snake_next(h).
-// x is Snake1(h) in the operand dtype.  Same layouts as ConvArgs.
+//   h <- h_in + conv2(Snake2(conv1_dil(x) + b1)) + b2;  s_out <- Snake_next(h).
+// x is Snake1(h_in) in the operand dtype: read from the operand tensor x, or
+// (x_from_h) computed in the kernel from h_in with the a1 parameters, in
+// which case h must be a different buffer from h_in.  Same layouts as ConvArgs.
 struct ResUnitArgs {
-  const void* x;
+  const void* x;         // unused when x_from_h
+  int x_from_h;
+  const float* a1_scale;  // Snake1: alpha/pi, 1/(2 den) (x_from_h only)
+  const float* a1_h;
+  const float* h_in;     // residual stream read (equal to h unless x_from_h)
   int T, C;
   const int* row_len;
   int rate, dil;
@@ -99,7 +105,7 @@ struct ResUnitArgs {
   const float* a2_h;
   const void* w2;        // packed [C/CH][1][C][CH]
   const float* b2;
-  float* h;              // residual stream, in place
+  float* h;              // residual stream written
   int store_h;           // 0: the updated h is not stored (nothing reads it)
   void* s_out;           // may be null
   const float* s_scale;
@@ -112,6 +118,8 @@ struct ResUnitArgs {
 // fused instance for (op, C).
 // big selects the large-frame tile of that width (0 if it has none).
 int res_unit_tile(int op, int C, bool big);
+// Whether units of width C run with x_from_h (Snake1 computed in the kernel).
+bool res_unit_from_h_ok(int op, int C);
 hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s);
 
 // Weight-norm fold + cast + repack, one workgroup per axis-0 slice.

@@ -83,6 +83,7 @@ struct voc_ctx {
   int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
+  int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
   std::vector<int64_t> meta_dst;  // host copies kept alive for async uploads
   std::vector<int> meta_int;
 };
@@ -228,10 +229,23 @@ voc_status launch(voc_ctx* c, hipStream_t s, int kind, double flops, double byte
 // ------------------------------------------------------------- workspace
 struct Plan {
   int rows, T;            // rows and allocated latent frames per row
-  size_t off_xlat, off_h, off_s0, off_s1, off_u, off_meta, bytes;
+  size_t off_xlat, off_h, off_h2, off_s0, off_s1, off_u, off_meta, bytes;
 };
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Whether the residual units of width C run fused with their conv1 operand
+// computed from h in the kernel (Snake1 at staging): their producers then
+// write no operand tensor, and h alternates between two buffers.
+bool unit_xh(const voc_ctx* c, int C) {
+  return c->ru_xh && !c->no_fuse && res_unit_tile(c->op, C, false) > 0 && res_unit_from_h_ok(c->op, C);
+}
+
+bool any_unit_xh(const voc_ctx* c) {
+  for (int b = 0; b < c->cfg.n_blocks; ++b)
+    if (unit_xh(c, c->cfg.width[b + 1])) return true;
+  return false;
+}
 
 Plan make_plan(const voc_ctx* c, int rows, int T) {
   const voc_config& g = c->cfg;
@@ -249,6 +263,7 @@ Plan make_plan(const voc_ctx* c, int rows, int T) {
   size_t o = 0;
   p.off_xlat = o; o = align_up(o + es * rows * static_cast<size_t>(g.latent_channels) * T);
   p.off_h = o;    o = align_up(o + 4 * rows * max_act);
+  p.off_h2 = o;   if (any_unit_xh(c)) o = align_up(o + 4 * rows * max_act);
   p.off_s0 = o;   o = align_up(o + es * rows * max_act);
   p.off_s1 = o;   o = align_up(o + es * rows * max_act);
   p.off_u = o;    o = align_up(o + es * rows * max_act);
@@ -281,6 +296,7 @@ voc_status ensure_ws(voc_ctx* c, size_t bytes) {
 struct Bufs {
   void* xlat;
   float* h;
+  float* h2;  // second residual-stream buffer (units with the operand from h)
   void* s[2];
   void* u;
   RowInfo rows;
@@ -291,6 +307,7 @@ Bufs bufs(voc_ctx* c, const Plan& p) {
   Bufs r{};
   r.xlat = b + p.off_xlat;
   r.h = reinterpret_cast<float*>(b + p.off_h);
+  r.h2 = reinterpret_cast<float*>(b + p.off_h2);
   r.s[0] = b + p.off_s0;
   r.s[1] = b + p.off_s1;
   r.u = b + p.off_u;
@@ -470,14 +487,16 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
 
 // One residual unit: fused into one kernel when an instance exists for its
 // width, else conv1 (epilogue: bias + Snake2 -> ubuf) and conv2 (epilogue:
-// bias + residual + next Snake).  s_in holds Snake1(h) in the operand dtype.
+// bias + residual + next Snake).  s_in holds Snake1(h) in the operand dtype,
+// except when h_alt is given: then the fused kernel computes Snake1 from h
+// itself (s_in unused) and writes the updated h to h_alt.
 // When `next` is given, the next layer's Snake operand is written to
 // *s_next: s_spare for the fused kernel (its tiles read neighbouring frames
 // of s_in while others write, so it must not write in place), s_in for the
 // two-kernel path (conv1 has finished reading s_in before conv2 runs).
 voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_spare, void* ubuf,
-                        float* h, const SnakeDev* next, void** s_next, int T, int rate, int rows,
-                        const int* row_len, hipStream_t s, const SnakeDev* h_snake = nullptr,
+                        float* h, float* h_alt, const SnakeDev* next, void** s_next, int T, int rate,
+                        int rows, const int* row_len, hipStream_t s, const SnakeDev* h_snake = nullptr,
                         bool keep_h = true) {
   const int C = u.c1.cout;
   // The large-frame tile where it still gives two workgroups per CU.
@@ -485,11 +504,16 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
   const bool big = bn_big > 0 && static_cast<int64_t>((T + bn_big - 1) / bn_big) * rows >= 2 * 256;
   const int bn = c->no_fuse ? 0 : (big ? bn_big : res_unit_tile(c->op, C, false));
   if (s_next) *s_next = nullptr;
+  if (h_alt && bn <= 0) return fail(c, VOC_DEVICE_ERROR, "no fused residual unit for this width");
   if (bn > 0) {
     void* s_out = next ? s_spare : nullptr;
     if (s_next) *s_next = s_out;
     ResUnitArgs a{};
-    a.x = s_in;
+    a.x = h_alt ? nullptr : s_in;
+    a.x_from_h = h_alt ? 1 : 0;
+    a.a1_scale = u.a1.alpha;
+    a.a1_h = u.a1.invden;
+    a.h_in = h;
     a.T = T;
     a.C = C;
     a.row_len = row_len;
@@ -501,7 +525,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     a.a2_h = u.a2.invden;
     a.w2 = u.c2.w;
     a.b2 = u.c2.bias;
-    a.h = h;
+    a.h = h_alt ? h_alt : h;
     a.store_h = keep_h ? 1 : 0;
     a.s_out = s_out;
     a.s_scale = next ? next->alpha : nullptr;
@@ -513,7 +537,8 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     const double el = static_cast<double>(rows) * T * C;
     const double es = op_size(c->op);
     const double flops = 2.0 * el * C * 8;
-    const double bytes = el * (es + 4 + (keep_h ? 4 : 0) + (s_out ? es : 0)) + 8.0 * C * C * es;
+    // Reads: the operand (or h itself) and h; writes: h if kept, the next operand.
+    const double bytes = el * ((h_alt ? 4 : es + 4) + (keep_h ? 4 : 0) + (s_out ? es : 0)) + 8.0 * C * C * es;
     const int op = c->op;
     return launch(c, s, VOC_K_RES_FUSED, flops, bytes, "residual unit launch",
                   [&] { return launch_res_unit(op, a, big, s); });
@@ -547,8 +572,9 @@ const SnakeDev* next_snake(const Weights& W, int b, int r, int nb, int nr) {
 }
 
 // The whole decoder over `rows` rows of T latent frames (already imported
-// into xlat).  Leaves the last residual stream in B.h.
-voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s) {
+// into xlat).  *h_last receives the buffer holding the last residual stream
+// (B.h or B.h2).
+voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, float** h_last) {
   const voc_config& g = c->cfg;
   const Weights& W = c->W;
   const int nb = g.n_blocks, nr = g.n_res;
@@ -563,18 +589,23 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s) 
   voc_status st = run_conv(c, W.conv_in, io, rows, B.rows.len, VOC_K_CONV_IN, s);
   if (st) return st;
   int t = T, rate = 1;
+  float* hc = B.h;   // current residual stream
+  float* ho = B.h2;  // the other buffer (units with the operand from h)
   for (int b = 0; b < nb; ++b) {
     const BlockDev& blk = W.blocks[b];
+    const bool xh = unit_xh(c, g.width[b + 1]);
     io = ConvIO{};
     io.x = B.s[cur];
     io.T_in = t;
     io.rate_in = rate;
-    io.h_out = B.h;
-    io.s_out = B.s[cur ^ 1];
-    io.snake_next = &blk.units[0].a1;
+    io.h_out = hc;
+    if (!xh) {  // else the first unit computes its Snake operand from h
+      io.s_out = B.s[cur ^ 1];
+      io.snake_next = &blk.units[0].a1;
+    }
     st = run_conv(c, blk.ct, io, rows, B.rows.len, VOC_K_CONVT, s);
     if (st) return st;
-    cur ^= 1;
+    if (!xh) cur ^= 1;
     t *= g.stride[b];
     rate *= g.stride[b];
     for (int r = 0; r < nr; ++r) {
@@ -584,13 +615,17 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s) 
       // The last unit of any other block feeds the next block only through
       // its Snake operand; its h is never read again.
       const bool keep_h = !(r == nr - 1 && b < nb - 1);
-      st = run_res_unit(c, blk.units[r], B.s[cur], B.s[cur ^ 1], B.u, B.h,
-                        next_snake(W, b, r, nb, nr), &s_next, t, rate, rows, B.rows.len, s, hs,
-                        keep_h);
+      // Within a block of such units only the last one writes an operand
+      // tensor (the next block's ConvTranspose1d input).
+      const SnakeDev* next = (xh && r + 1 < nr) ? nullptr : next_snake(W, b, r, nb, nr);
+      st = run_res_unit(c, blk.units[r], xh ? nullptr : B.s[cur], B.s[cur ^ 1], B.u, hc,
+                        xh ? ho : nullptr, next, &s_next, t, rate, rows, B.rows.len, s, hs, keep_h);
       if (st) return st;
       if (s_next == B.s[cur ^ 1]) cur ^= 1;
+      if (xh && keep_h) std::swap(hc, ho);
     }
   }
+  *h_last = hc;
   return VOC_OK;
 }
 
@@ -720,6 +755,8 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
     if (const char* v = std::getenv(names[k])) c->force_variant[k] = std::atoi(v);
   if (const char* v = std::getenv("VOC_NO_FUSED_RES")) c->no_fuse = std::atoi(v) != 0;
   if (const char* v = std::getenv("VOC_CONV_M_FAST")) c->m_order = std::atoi(v) != 0;
+  // Ablation only: 0 makes every fused unit read an operand tensor written by its producer.
+  if (const char* v = std::getenv("VOC_RU_OPERAND_FROM_H")) c->ru_xh = std::atoi(v) != 0;
   *out = c;
   return VOC_OK;
 }
@@ -963,9 +1000,10 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
   st = run_import(c, latent, T, g.latent_channels, Bf.rows, static_cast<int>(rows), T_alloc, Bf.xlat,
                   nullptr, nullptr, s);
   if (st) return st;
-  st = run_stack(c, Bf, static_cast<int>(rows), T_alloc, s);
+  float* h_last = nullptr;
+  st = run_stack(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last);
   if (st) return st;
-  return run_head(c, Bf.h, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
+  return run_head(c, h_last, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
                   static_cast<int>(c->hop), pcm, s);
 }
 
@@ -1078,6 +1116,8 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
   const size_t act_out = static_cast<size_t>(rows) * cmax * t_out;
   size_t o = 0;
   const size_t off_h = o; o = align_up(o + 4 * std::max(act_in, act_out));
+  const bool xh = si.kind == 2 && unit_xh(c, static_cast<int>(si.c_out));
+  const size_t off_h2 = o; if (xh) o = align_up(o + 4 * act_out);
   const size_t off_s0 = o; o = align_up(o + es * act_in);
   const size_t off_s1 = o; o = align_up(o + es * act_out);
   const size_t off_u = o; o = align_up(o + es * act_out);
@@ -1086,6 +1126,7 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
   if (st) return st;
   char* base = static_cast<char*>(c->ws);
   float* h = reinterpret_cast<float*>(base + off_h);
+  float* h2 = reinterpret_cast<float*>(base + off_h2);
   void* s0 = base + off_s0;
   void* s1 = base + off_s1;
   void* u = base + off_u;
@@ -1131,10 +1172,13 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
       st = run_conv(c, W.blocks[si.b].ct, io, rows, ri.len, VOC_K_CONVT, s);
       break;
     case 2: {
+      // The same kernel path as in a decode: with the operand computed from
+      // h, the import writes h only and the unit writes h2.
       const UnitDev& un = W.blocks[si.b].units[si.r];
-      st = run_import(c, in, T_in, si.c_in, ri, rows, T, s0, &un.a1, h, s);
+      st = run_import(c, in, T_in, si.c_in, ri, rows, T, xh ? nullptr : s0, &un.a1, h, s);
       if (st) return st;
-      st = run_res_unit(c, un, s0, s1, u, h, nullptr, nullptr, T, 1, rows, ri.len, s);
+      st = run_res_unit(c, un, s0, s1, u, h, xh ? h2 : nullptr, nullptr, nullptr, T, 1, rows, ri.len, s);
+      if (xh) h = h2;
       break;
     }
     default:

@@ -133,6 +133,29 @@ def test_decode_equals_stage_chain_bitwise():
         V.vocoder_destroy(ctx)
 
 
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_operand_from_h_bitwise_equal(idx, monkeypatch):
+    """Fused units that compute Snake1 from h while staging (h in two
+    buffers, no operand tensor from the producer) give the same bits as the
+    units that read the producer's operand tensor: the same fp32 h values go
+    through the same Snake and rounding either way."""
+    cfg = I.config(idx)
+    t = I.make_weights(cfg, twin=True)
+    frames, rows = SMALL[idx]
+    x = to_dev(I.make_latent(cfg, batch=rows, frames=frames))
+    outs = []
+    for flag in ("1", "0"):
+        monkeypatch.setenv("VOC_RU_OPERAND_FROM_H", flag)
+        ctx = _ctx(cfg, t)
+        try:
+            outs.append(V.decode(ctx, x))
+            torch.cuda.synchronize()
+        finally:
+            V.vocoder_destroy(ctx)
+    monkeypatch.delenv("VOC_RU_OPERAND_FROM_H")
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("idx", [1, 2])
 def test_batch_rows_independent_and_deterministic(idx):
     cfg = I.config(idx)
