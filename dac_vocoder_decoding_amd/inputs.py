@@ -23,10 +23,12 @@ library normal distribution; the same idea seeds every tensor here:
 Distributions (the synthetic configurations): latent ~ N(0,1); Snake alpha
 (and SnakeBeta beta) ~ U(0.5, 2) per channel; weight-norm magnitude
 g ~ U(0.5, 1.5); direction v ~ N(0, 1); every bias ~ N(0, 0.01) read as a
-standard deviation of 0.01.
+standard deviation of 0.01; the plain dec_in_proj weight (no weight norm)
+~ N(0, 1 / C_latent), so its rows have about unit norm like the folded ones.
 
 Tensor naming follows the DAV decoder listing on the minimaxmusic.cpp
-ARCHITECTURE page ("Flow VAE" section): conv_in, blocks.{b}.snake1,
+ARCHITECTURE page ("Flow VAE" section): dec_in_proj (weight, bias; only
+when the configuration has ``in_proj``), conv_in, blocks.{b}.snake1,
 blocks.{b}.conv_t1, blocks.{b}.res_units.{r}.{snake1,conv1,snake2,conv2},
 snake_out, conv_out, each conv stored as weight_g / weight_v / bias with
 PyTorch shapes (Conv1d v: [out, in, k]; ConvTranspose1d v: [in, out, k];
@@ -112,6 +114,17 @@ CONFIGS = {
     4: _cfg(name="mono_codec_bf16", latent_channels=1024, batch=32, frames=250,
             dtype="bf16", sample_rate=24000, stereo=False,
             widths=(1536, 768, 384, 192, 96), strides=(8, 8, 5, 3), seed=1004),
+    # The DAV decoder as the minimaxmusic.cpp ARCHITECTURE page lists it
+    # ("Flow VAE"): dec_in_proj 64 -> 1024 (k=1, no weight norm), conv_in
+    # 1024 -> 1536, widths 1536 ... 96; one stereo window of 689 frames.
+    5: _cfg(name="dav_window_f32", batch=2, frames=689, in_proj=1024,
+            widths=(1536, 768, 384, 192, 96), strides=(8, 8, 4, 2), seed=1005),
+    # A minute of stereo music through the DAV decoder as the pages' pipeline
+    # hands it over ("Inference recipe"): 14 windows of 689 frames (the last
+    # 683), each decoded on its own, cropped 86 / 258 frames and stitched.
+    6: _cfg(name="dav_song_windows_f32", batch=2, frames=689, in_proj=1024,
+            widths=(1536, 768, 384, 192, 96), strides=(8, 8, 4, 2), seed=1006,
+            windows=14, last_frames=683, crop=(86, 258)),
 }
 
 
@@ -142,7 +155,11 @@ def tensor_shapes(cfg: dict) -> dict:
         if beta:
             shapes[prefix + ".beta"] = (1, c, 1)
 
-    conv("conv_in", (w[0], cl, k))
+    p_in = cfg.get("in_proj", 0)
+    if p_in:
+        shapes["dec_in_proj.weight"] = (p_in, cl, 1)
+        shapes["dec_in_proj.bias"] = (p_in,)
+    conv("conv_in", (w[0], p_in or cl, k))
     shapes["conv_in.bias"] = (w[0],)
     for b, s in enumerate(cfg["strides"]):
         cin, cout = w[b], w[b + 1]
@@ -175,6 +192,8 @@ def make_weights(cfg: dict, seed: int | None = None, twin: bool = False) -> dict
     for name, shape in tensor_shapes(cfg).items():
         if name.endswith(".weight_v"):
             out[name] = normal(seed, name, shape)
+        elif name == "dec_in_proj.weight":
+            out[name] = normal(seed, name, shape, std=float(1.0 / np.sqrt(shape[1])))
         elif name.endswith(".weight_g"):
             if twin and ".res_units." in name and ".conv2." in name:
                 n = int(np.prod(shape))
@@ -189,6 +208,21 @@ def make_weights(cfg: dict, seed: int | None = None, twin: bool = False) -> dict
         else:  # pragma: no cover
             raise KeyError(name)
     return out
+
+
+def make_windows(cfg: dict, seed: int | None = None, windows: int | None = None,
+                 frames: int | None = None, last_frames: int | None = None) -> np.ndarray:
+    """Seeded latent windows [n, sides * C_latent, L] ~ N(0, 1), float32, one
+    independent draw per window (the pages' denoiser produces each window on
+    its own); the last window's frames from ``last_frames`` on are zero."""
+    seed = cfg["seed"] if seed is None else seed
+    n = cfg["windows"] if windows is None else windows
+    L = cfg["frames"] if frames is None else frames
+    last = cfg["last_frames"] if last_frames is None else last_frames
+    sides = 2 if cfg["stereo"] else 1
+    x = normal(seed, "windows", (n, sides * cfg["latent_channels"], L))
+    x[-1, :, last:] = 0.0
+    return x
 
 
 def make_latent(cfg: dict, seed: int | None = None, batch: int | None = None,
@@ -212,7 +246,12 @@ def algorithmic_flops(cfg: dict, batch: int, frames: int) -> float:
     w = cfg["widths"]
     k = cfg["kernel"]
     t = frames
-    f = 2.0 * batch * t * w[0] * cfg["latent_channels"] * k
+    cin = cfg["latent_channels"]
+    f = 0.0
+    if cfg.get("in_proj", 0):
+        f += 2.0 * batch * t * cfg["in_proj"] * cin
+        cin = cfg["in_proj"]
+    f += 2.0 * batch * t * w[0] * cin * k
     for b, s in enumerate(cfg["strides"]):
         cin, cout = w[b], w[b + 1]
         f += 2.0 * batch * t * cin * cout * 2 * s  # every input frame meets 2s taps

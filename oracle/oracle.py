@@ -10,7 +10,8 @@ decoder the way the pages state them and holds the readings of points the
 pages leave open.
 
 Decoder (minimaxmusic.cpp ARCHITECTURE, "Flow VAE" listing; DAV decoder):
-    h = conv_in(latent)                                  Conv1d k7, pad 3, bias
+    x = dec_in_proj(latent)        (DAV only)            Conv1d k1, bias, no weight norm
+    h = conv_in(x)                                       Conv1d k7, pad 3, bias
     for each block b (stride s):
         h = conv_t1(Snake_b(h))                          ConvTranspose1d k=2s, stride s
         for d in (1, 3, 9):                              residual units
@@ -25,7 +26,16 @@ Readings of points the pages leave open (each listed in the design notes):
   * the convT weight norm is taken along axis 0 of the stored [in, out, k]
     tensor (per input channel), as the pages' "axis 0" says literally;
   * Snake denominators are alpha + 1e-9 (Snake) and beta + 1e-9 (SnakeBeta);
-  * every conv has a bias; N(0, 0.01) biases use std 0.01;
+  * every conv has a bias, dec_in_proj included; N(0, 0.01) biases use std
+    0.01;
+  * dec_in_proj feeds conv_in directly (the listing puts no activation
+    between them), and its output is zero-padded like any conv input;
+  * windowed decode (ARCHITECTURE, "Inference recipe": "Decode and stitch",
+    "Post-processing"): windows are decoded independently, every window but
+    the first loses crop_left latent frames (x hop samples) on the left, every
+    window but the last crop_right on the right, the kept segments are
+    concatenated in window order and clamped to [-1, 1]; stereo output is
+    planar [L: N][R: N];
   * bf16 configurations: the folded weights are rounded fp64 -> fp32 (the F32
     inference checkpoint) -> bf16 (round to nearest even), the latent is
     rounded to bf16, and everything else stays exact.  Optionally
@@ -223,6 +233,13 @@ class Model:
         def act(prefix):
             return (vec(prefix + ".alpha"), vec(prefix + ".beta") if self.beta else None)
 
+        # dec_in_proj is stored without weight norm: used as given (bf16
+        # configurations round it fp32 -> bf16 like the folded weights).
+        self.in_proj = None
+        if cfg.get("in_proj", 0):
+            w = np.asarray(t["dec_in_proj.weight"], dtype=np.float32)
+            w = round_bf16(w) if self.bf16 else w
+            self.in_proj = (_c(w, prec), vec("dec_in_proj.bias"))
         self.conv_in = (fold("conv_in"), vec("conv_in.bias"))
         self.blocks = []
         for b, s in enumerate(cfg["strides"]):
@@ -252,8 +269,13 @@ class Model:
         return _c(round_bf16(x) if self.bf16 else x, self.prec)
 
     def stage_conv_in(self, latent):
+        x = self._latent(latent)
+        if self.in_proj is not None:
+            x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec)
+            if self.round_operands:  # conv_in's matrix-core operand
+                x = _c(round_bf16(x), self.prec)
         w, b = self.conv_in
-        return conv1d(self._latent(latent), w, b, 1, self.prec)
+        return conv1d(x, w, b, 1, self.prec)
 
     def stage_upsample(self, b, h):
         blk = self.blocks[b]
@@ -298,6 +320,26 @@ class Model:
             for r in range(len(self.cfg["dilations"])):
                 h = self.stage_res_unit(b, r, h)
         return self.stage_head_pre(h) if pre_tanh else self.stage_head(h)
+
+    def decode_windows(self, windows, last_frames, crop_left, crop_right):
+        """Windowed decode and stitch.  windows [n, sides*C, L]: side j of
+        window k is channels [j*C, (j+1)*C); the last window holds
+        last_frames frames.  Returns planar [sides, N] (clamped to [-1, 1])."""
+        windows = np.asarray(windows)
+        n, sc, L = windows.shape
+        c = self.cfg["latent_channels"]
+        sides = sc // c
+        hop = self.cfg["hop"]
+        segments = []
+        for k in range(n):
+            length = last_frames if k == n - 1 else L
+            x = windows[k, :, :length].reshape(sides, c, length)
+            y = self.decode(x)[:, 0, :]                      # [sides, length*hop]
+            lo = crop_left if k > 0 else 0
+            hi = length - (crop_right if k < n - 1 else 0)
+            assert hi > lo, "every window must keep at least one frame"
+            segments.append(y[:, lo * hop:hi * hop])
+        return np.clip(np.concatenate(segments, axis=1), -1.0, 1.0)
 
     def decode_tiled(self, latent, tile, halo):
         """Decode latent frames [t0, t1) of each tile from the window

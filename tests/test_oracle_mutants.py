@@ -1,11 +1,16 @@
 """The pins catch plausible mistakes: each test compiles a copy of oracle.c
 with one planted mistake (on the CPU, in a temporary directory), points the
-oracle module at that build, and requires that at least one pin fails.
+oracle module at that build, and requires that at least one pin fails.  The
+steps oracle.py itself orders (dec_in_proj, windowed decode and stitching)
+get the same treatment: a method of its Model is recompiled from its source
+with one planted mistake and patched in for the test.
 
 A mutation that no pin notices would mean the pins leave that part of the
 oracle unchecked.
 """
+import inspect
 import os
+import textwrap
 
 import pytest
 
@@ -59,8 +64,8 @@ def _pins(orc):
         P.test_convt_polyphase_identity(orc, s)
     P.test_convt_impulse_response(orc)
     P.test_residual_unit_zero_conv2_is_identity(orc)
-    P.test_decode_matches_torch_composition(orc, (2, 2), "snake")
-    P.test_decode_matches_torch_composition(orc, (3, 2), "snakebeta")
+    P.test_decode_matches_torch_composition(orc, (2, 2), "snake", 0)
+    P.test_decode_matches_torch_composition(orc, (3, 2), "snakebeta", 0)
     P.test_golden_lengths_and_vocoder_gate(orc)
 
 
@@ -80,3 +85,49 @@ def test_planted_mistake_is_caught(name, orig, bad, tmp_path, monkeypatch):
     monkeypatch.setitem(O._loaded, "f64", lib)
     with pytest.raises(AssertionError):
         _pins(O)
+
+
+# (name, Model method, original text, planted mistake)
+PY_MUTANTS = [
+    ("window_first_cropped", "decode_windows", "lo = crop_left if k > 0 else 0", "lo = crop_left"),
+    ("window_last_cropped", "decode_windows", "hi = length - (crop_right if k < n - 1 else 0)",
+     "hi = length - crop_right"),
+    ("window_right_off_by_one", "decode_windows", "hi = length - (crop_right if k < n - 1 else 0)",
+     "hi = length - (crop_right + 1 if k < n - 1 else 0)"),
+    ("window_last_full_length", "decode_windows", "length = last_frames if k == n - 1 else L",
+     "length = L"),
+    ("window_sides_interleaved", "decode_windows",
+     "x = windows[k, :, :length].reshape(sides, c, length)",
+     "x = windows[k, :, :length].reshape(c, sides, length).transpose(1, 0, 2)"),
+    ("in_proj_no_bias", "stage_conv_in", "x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec)",
+     "x = conv1d(x, self.in_proj[0], None, 1, self.prec)"),
+    ("in_proj_weight_normed", "__init__", 'w = np.asarray(t["dec_in_proj.weight"], dtype=np.float32)',
+     'w = np.asarray(t["dec_in_proj.weight"], dtype=np.float32); '
+     'w = (w / np.linalg.norm(w, axis=(1, 2), keepdims=True)).astype(np.float32)'),
+    ("in_proj_after_snake", "stage_conv_in", "x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec)",
+     "x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec); "
+     "x = snake(x, np.ones(x.shape[1]), None, self.prec)"),
+]
+
+
+def _py_pins(orc):
+    P.test_decode_matches_torch_composition(orc, (2, 2), "snake", 5)
+    P.test_in_proj_composes_with_conv_in(orc)
+    P.test_window_stitch_bookkeeping_at_the_pages_sizes(orc)
+    P.test_windows_cut_from_one_track_equal_its_decode(orc)
+    P.test_windows_planar_sides_and_single_window(orc)
+
+
+def test_python_pins_pass_on_the_real_oracle():
+    _py_pins(O)
+
+
+@pytest.mark.parametrize("name,method,orig,bad", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_planted_python_mistake_is_caught(name, method, orig, bad, monkeypatch):
+    src = textwrap.dedent(inspect.getsource(getattr(O.Model, method)))
+    assert src.count(orig) == 1, f"mutation site not unique: {name}"
+    ns = dict(vars(O))
+    exec(compile(src.replace(orig, bad), f"<mutant {name}>", "exec"), ns)
+    monkeypatch.setattr(O.Model, method, ns[method])
+    with pytest.raises(AssertionError):
+        _py_pins(O)

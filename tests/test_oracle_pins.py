@@ -21,9 +21,9 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(12345)
 
 
-def tiny_cfg(strides=(2, 2), widths=(8, 6, 4), latent=3, act="snake", dil=(1, 3, 9)):
+def tiny_cfg(strides=(2, 2), widths=(8, 6, 4), latent=3, act="snake", dil=(1, 3, 9), in_proj=0):
     return I.config(0, strides=tuple(strides), widths=tuple(widths), latent_channels=latent,
-                    act=act, dilations=tuple(dil), frames=9, batch=2)
+                    act=act, dilations=tuple(dil), frames=9, batch=2, in_proj=in_proj)
 
 
 # ----------------------------------------------------------------- Snake
@@ -293,7 +293,10 @@ def torch_decode(cfg, t, latent):
         den = (T[p + ".beta"] if cfg["act"] == "snakebeta" else T[p + ".alpha"]).reshape(1, -1, 1)
         return x + torch.sin(a * x) ** 2 / (den + 1e-9)
 
-    h = F.conv1d(torch.from_numpy(latent.astype(np.float64)), w("conv_in"), T["conv_in.bias"], padding=3)
+    x = torch.from_numpy(latent.astype(np.float64))
+    if cfg.get("in_proj", 0):
+        x = F.conv1d(x, T["dec_in_proj.weight"], T["dec_in_proj.bias"])  # plain weight
+    h = F.conv1d(x, w("conv_in"), T["conv_in.bias"], padding=3)
     for b, s in enumerate(cfg["strides"]):
         h = F.conv_transpose1d(sn(h, f"blocks.{b}.snake1"), w(f"blocks.{b}.conv_t1"),
                                T[f"blocks.{b}.conv_t1.bias"], stride=s, padding=(s + 1) // 2,
@@ -306,9 +309,10 @@ def torch_decode(cfg, t, latent):
     return torch.tanh(F.conv1d(sn(h, "snake_out"), w("conv_out"), T["conv_out.bias"], padding=3)).numpy()
 
 
-@pytest.mark.parametrize("strides,act", [((2, 2), "snake"), ((3, 2), "snakebeta"), ((5, 3), "snake")])
-def test_decode_matches_torch_composition(orc, strides, act):
-    cfg = tiny_cfg(strides=strides, act=act)
+@pytest.mark.parametrize("strides,act,in_proj", [((2, 2), "snake", 0), ((3, 2), "snakebeta", 0),
+                                                 ((5, 3), "snake", 0), ((2, 2), "snake", 5)])
+def test_decode_matches_torch_composition(orc, strides, act, in_proj):
+    cfg = tiny_cfg(strides=strides, act=act, in_proj=in_proj)
     t = I.make_weights(cfg, twin=True)
     lat = I.make_latent(cfg)
     y = orc.Model(cfg, t).decode(lat)
@@ -370,3 +374,122 @@ def test_tiling_exact_halo(orc, strides, halo_ok):
     assert np.abs(good - ref).max() <= 1e-10
     bad = m.decode_tiled(lat, 20, halo_ok - 1)
     assert np.abs(bad - ref).max() > 1e-6
+
+
+# ----------------------------------------------------------- dec_in_proj
+def test_in_proj_composes_with_conv_in(orc):
+    """dec_in_proj (k=1, plain weight W1, bias b1) then conv_in (k=7, W7, b7):
+    with b1 = 0 this is one k=7 conv with W[o,i,k] = sum_j W7[o,j,k] W1[j,i];
+    with b1 != 0, b1 enters through the taps that land inside the clip only,
+    since conv_in zero-pads dec_in_proj's output (not its bias)."""
+    cfg = tiny_cfg(in_proj=5, latent=3, widths=(8, 6, 4))
+    t = I.make_weights(cfg)
+    lat = I.make_latent(cfg, batch=2, frames=9)
+    m = orc.Model(cfg, t)
+    W7 = m.conv_in[0]                                   # folded conv_in [8, 5, 7]
+    b7 = t["conv_in.bias"].astype(np.float64)
+    W1 = t["dec_in_proj.weight"].astype(np.float64)[:, :, 0]   # [5, 3], used as stored
+    b1 = t["dec_in_proj.bias"].astype(np.float64)
+    x = lat.astype(np.float64)
+    T = x.shape[2]
+    Weff = np.einsum("ojk,ji->oik", W7, W1)
+    xp = np.pad(x, ((0, 0), (0, 0), (3, 3)))
+    want = np.zeros((2, 8, T))
+    for k in range(7):
+        want += np.einsum("oi,bit->bot", Weff[:, :, k], xp[:, :, k:k + T])
+        inside = ((np.arange(T) + k - 3 >= 0) & (np.arange(T) + k - 3 < T)).astype(float)
+        want += (W7[:, :, k] @ b1)[None, :, None] * inside[None, None, :]
+    want += b7[None, :, None]
+    np.testing.assert_allclose(m.stage_conv_in(lat), want, rtol=1e-12, atol=1e-12)
+    # No weight norm on dec_in_proj: scaling its weight scales its output.
+    t2 = dict(t)
+    t2["dec_in_proj.weight"] = (2.0 * t["dec_in_proj.weight"]).astype(np.float32)
+    t2["dec_in_proj.bias"] = np.zeros_like(t["dec_in_proj.bias"])
+    t3 = dict(t2)
+    t3["dec_in_proj.weight"] = t["dec_in_proj.weight"]
+    z2 = orc.Model(cfg, t2).stage_conv_in(lat) - b7[None, :, None]
+    z3 = orc.Model(cfg, t3).stage_conv_in(lat) - b7[None, :, None]
+    np.testing.assert_allclose(z2, 2.0 * z3, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------ windowed decode
+def _cut_windows(track, L, step):
+    """Windows of L frames every `step` frames of one track [sides*C, T]; the
+    last one ends at the track's end (returns windows [n, sides*C, L] and the
+    last window's length)."""
+    T = track.shape[1]
+    starts = [0]
+    while starts[-1] + L < T:
+        starts.append(starts[-1] + step)
+    out = np.zeros((len(starts), track.shape[0], L), dtype=track.dtype)
+    for k, s0 in enumerate(starts):
+        seg = track[:, s0:s0 + L]
+        out[k, :, :seg.shape[1]] = seg
+    return out, T - starts[-1]
+
+
+def test_window_stitch_bookkeeping_at_the_pages_sizes(orc):
+    """With the pages' window (689 frames) and crops (86 / 258), windows cut
+    345 frames apart from one track stitch back to the track frame for frame:
+    a marker decoder (every sample = its latent frame's marker) shows each
+    frame kept exactly once and in order, on both planes."""
+    with open(os.path.join(GOLDEN, "window_stitch.json")) as f:
+        g = json.load(f)
+    L, cl, cr = g["window_frames"], g["crop_left"], g["crop_right"]
+    step = L - cl - cr
+    assert step == g["window_step"] == g["carry"][0] == L - 344
+    assert g["carry"][1] - g["carry"][0] == g["blend_frames"]
+
+    class Marker(orc.Model):
+        def __init__(self, cfg):        # no weights: decode repeats the marker channel
+            self.cfg = cfg
+
+        def decode(self, x, pre_tanh=False):
+            return np.repeat(np.asarray(x, dtype=np.float64)[:, :1, :], self.cfg["hop"], axis=2)
+
+    cfg = I.config(1, latent_channels=2)
+    hop = cfg["hop"]
+    assert hop == g["samples_per_frame"]
+    for T in (689, 1034, 1500, 2760):
+        marks = np.arange(T) / 10000.0                      # inside the clamp range
+        track = np.zeros((4, T))
+        track[0], track[2] = marks, -marks                  # left / right markers
+        win, last = _cut_windows(track, L, step)
+        y = Marker(cfg).decode_windows(win, last, cl, cr)
+        assert y.shape == (2, T * hop)
+        np.testing.assert_array_equal(y[0], np.repeat(marks, hop))
+        np.testing.assert_array_equal(y[1], -np.repeat(marks, hop))
+
+
+def test_windows_cut_from_one_track_equal_its_decode(orc):
+    """Crops wider than the receptive-field halo (10 frames): every kept sample
+    sees the same inputs as in the decode of the whole track, so stitching
+    windows cut from it reproduces that decode."""
+    cfg = tiny_cfg(strides=(8, 8, 4, 2), widths=(8, 8, 4, 4, 4), latent=4, in_proj=6)
+    t = I.make_weights(cfg, twin=True)
+    m = orc.Model(cfg, t)
+    T, L, cl, cr = 75, 40, 12, 14
+    track = I.normal(5, "track", (8, T))                    # stereo: 2 x 4 channels
+    win, last = _cut_windows(track, L, L - cl - cr)
+    assert win.shape[0] == 4 and last == 33
+    y = m.decode_windows(win, last, cl, cr)
+    ref = m.decode(track.reshape(2, 4, T))[:, 0, :]
+    assert y.shape == ref.shape
+    assert np.abs(y - ref).max() <= 1e-12
+    # Crops narrower than the halo leave window-edge effects in the output.
+    win2, last2 = _cut_windows(track, L, L - 4 - 4)
+    y2 = m.decode_windows(win2, last2, 4, 4)
+    assert np.abs(y2 - ref).max() > 1e-6
+
+
+def test_windows_planar_sides_and_single_window(orc):
+    cfg = tiny_cfg(latent=3, in_proj=5)
+    t = I.make_weights(cfg)
+    m = orc.Model(cfg, t)
+    win = I.normal(9, "win", (2, 6, 11))
+    y = m.decode_windows(win, 9, 2, 3)
+    swapped = np.concatenate([win[:, 3:], win[:, :3]], axis=1)
+    np.testing.assert_array_equal(m.decode_windows(swapped, 9, 2, 3), y[::-1])
+    one = m.decode_windows(win[:1], 11, 2, 3)                # one window: no crops
+    np.testing.assert_array_equal(one, np.clip(m.decode(win[0].reshape(2, 3, 11))[:, 0], -1, 1))
+    assert y.shape == (2, (11 - 3 + 9 - 2) * cfg["hop"])
