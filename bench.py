@@ -3,7 +3,9 @@
 
 One step = one full decode (conv_in, 4 upsampling blocks with 3 residual
 units each, head) of one batch of synthetic latents, with the latent, the
-weights and the output buffer already resident in HBM.
+weights and the output buffer already resident in HBM.  For the windowed
+workload one step is one vocoder_decode_windows call: every window of the
+song decoded as one batch and stitched into planar output.
 
 Prints ONE JSON line: audio-seconds decoded per second (value), whole-decode
 TFLOP/s, the roofline of the dominant kernel measured live with HIP events
@@ -27,7 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "audio-seconds decoded/sec (44.1 kHz stereo) + TFLOP/s as % of MFMA peak"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
-KIND_NAMES = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused"]
+KIND_NAMES = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused",
+              "in_proj"]
 KERNEL_SOURCES = ["dac_vocoder_decoding_amd/csrc/conv_gemm.hip",
                   "dac_vocoder_decoding_amd/csrc/fused_ru.hip",
                   "dac_vocoder_decoding_amd/csrc/gemm_common.h",
@@ -48,7 +51,11 @@ def workload_name(cfg: dict) -> str:
     w = "/".join(str(x) for x in cfg["widths"])
     s = ",".join(str(x) for x in cfg["strides"])
     tile = f", time tiles of {cfg['tile_frames']} frames" if cfg["tile_frames"] else ""
-    return (f"{cfg['name']}: latent {lat} {cfg['dtype']}, widths {w}, strides {s}, "
+    proj = f"dec_in_proj {cfg['latent_channels']}->{cfg['in_proj']}, " if cfg.get("in_proj") else ""
+    if cfg.get("windows"):
+        lat = (f"{cfg['windows']} windows [{cfg['batch']},{cfg['latent_channels']},{cfg['frames']}] "
+               f"(last {cfg['last_frames']} frames), crops {cfg['crop'][0]}/{cfg['crop'][1]}, stitched")
+    return (f"{cfg['name']}: latent {lat} {cfg['dtype']}, {proj}widths {w}, strides {s}, "
             f"{cfg['act']}{tile}")
 
 
@@ -69,7 +76,8 @@ def traffic_for(workload_key: str, kind: str):
 
 def cpu_baseline(cfg: dict, tensors: dict, latent, target_s: float = 15.0) -> dict:
     """The oracle (fp64 direct loops, OpenMP) on a bounded time slice of the
-    same workload: one stereo pair (or one mono row) of the first frames."""
+    same workload: one stereo pair (or one mono row) of the first frames (of
+    the first window, for the windowed workload)."""
     from dac_vocoder_decoding_amd import inputs as I
     from oracle import oracle as O
     rows = 2 if cfg["stereo"] else 1
@@ -114,17 +122,34 @@ def main() -> int:
 
     cfg = I.config(args.config)
     tensors = I.make_weights(cfg)
-    latent_np = I.make_latent(cfg)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     ctx = V.open_context(cfg, tensors, device=0)
-    latent = torch.from_numpy(latent_np).to(dev)
-    B, _, T = latent.shape
-    pcm = torch.empty(B, 1, V.vocoder_output_length(ctx, T), device=dev)
     stream = torch.cuda.current_stream()
+    sides = 2 if cfg["stereo"] else 1
+    if cfg.get("windows"):
+        win_np = I.make_windows(cfg)
+        n, L, last, (cl, cr) = cfg["windows"], cfg["frames"], cfg["last_frames"], cfg["crop"]
+        latent_np = win_np[0].reshape(sides, cfg["latent_channels"], L)  # CPU-baseline sample
+        latent = torch.from_numpy(win_np).to(dev)
+        N = V.vocoder_windows_output_length(ctx, n, L, last, cl, cr)
+        pcm = torch.empty(sides, N, device=dev)
+        B, T = n * sides, L
+        secs = N / cfg["sample_rate"]
+        flops = sum(I.algorithmic_flops(cfg, sides, L if k < n - 1 else last) for k in range(n))
 
-    def step():
-        V.check(V.vocoder_decode(ctx, latent, B, T, pcm, stream), ctx)
+        def step():
+            V.check(V.vocoder_decode_windows(ctx, latent, n, sides, L, last, cl, cr, pcm, stream), ctx)
+    else:
+        latent_np = I.make_latent(cfg)
+        latent = torch.from_numpy(latent_np).to(dev)
+        B, _, T = latent.shape
+        pcm = torch.empty(B, 1, V.vocoder_output_length(ctx, T), device=dev)
+        secs = I.audio_seconds(cfg, B, T)
+        flops = I.algorithmic_flops(cfg, B, T)
+
+        def step():
+            V.check(V.vocoder_decode(ctx, latent, B, T, pcm, stream), ctx)
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20)
@@ -183,8 +208,6 @@ def main() -> int:
         V.check(V.vocoder_profile_select(ctx, 0), ctx)
         kernels = read_stats()
 
-    secs = I.audio_seconds(cfg, B, T)
-    flops = I.algorithmic_flops(cfg, B, T)
     value = secs / (ms_per_step / 1e3)
     tflops = flops / (ms_per_step / 1e3) / 1e12
     peak = PEAK_TFLOPS[cfg["dtype"]]
@@ -238,7 +261,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": cfg["dtype"],
         "data": "synthetic (seeded latents and random-init weights of the stated shapes)",
-        "config": {"workload": workload_name(cfg), "batch": B, "latent_frames": T,
+        "config": {"workload": workload_name(cfg), "rows": B, "latent_frames": T,
                    "audio_seconds_per_step": secs, "parallelism": "single GPU"},
         "tflops": tflops,
         "mfma_peak_frac": tflops / peak,

@@ -38,8 +38,9 @@
 
 namespace voc {
 
-// TAG only separates kernel names per layer kind (conv_in vs residual k7)
-// so that profilers report them apart; it does not change the code.
+// TAG only separates kernel names per layer kind (the input layers conv_in
+// and dec_in_proj vs the residual convs of the same tap count) so that
+// profilers report them apart; it does not change the code.
 template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG, int NS>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   constexpr int CH = OpT<OP>::CH;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       for (int q = 0; q < 2; ++q) {
         bias[q] = *reinterpret_cast<const f4*>(a.bias + o + 16 * q);
         sal[q] = sinv[q] = hsc[q] = hsh[q] = f4{0.f, 0.f, 0.f, 0.f};
-        if (a.s_out) {
+        if (a.s_out && a.s_alpha) {  // else zero parameters: Snake(v; 0, 0) = v exactly
           sal[q] = *reinterpret_cast<const f4*>(a.s_alpha + o + 16 * q);
           sinv[q] = *reinterpret_cast<const f4*>(a.s_invden + o + 16 * q);
         }
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       const int o = m - ph * a.Cout;
       const f4 bias = *reinterpret_cast<const f4*>(a.bias + o);
       f4 sal = f4{0.f, 0.f, 0.f, 0.f}, sinv = f4{0.f, 0.f, 0.f, 0.f};
-      if (a.s_out) {
+      if (a.s_out && a.s_alpha) {  // else zero parameters: Snake(v; 0, 0) = v exactly
         sal = *reinterpret_cast<const f4*>(a.s_alpha + o);
         sinv = *reinterpret_cast<const f4*>(a.s_invden + o);
       }
@@ -440,20 +441,21 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 }
 
 template <int OP>
-static hipError_t launch_op(int taps, int variant, bool conv_in, const ConvArgs& a, hipStream_t s) {
+static hipError_t launch_op(int taps, int variant, bool input_layer, const ConvArgs& a, hipStream_t s) {
   switch (taps) {
     case 7:
-      return conv_in ? launch_taps<OP, 7, 1>(variant, a, s) : launch_taps<OP, 7, 0>(variant, a, s);
+      return input_layer ? launch_taps<OP, 7, 1>(variant, a, s) : launch_taps<OP, 7, 0>(variant, a, s);
     case 2: return launch_taps<OP, 2, 0>(variant, a, s);
-    case 1: return launch_taps<OP, 1, 0>(variant, a, s);
+    case 1:
+      return input_layer ? launch_taps<OP, 1, 1>(variant, a, s) : launch_taps<OP, 1, 0>(variant, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_conv(int op, int taps, int variant, bool conv_in, const ConvArgs& a,
+hipError_t launch_conv(int op, int taps, int variant, bool input_layer, const ConvArgs& a,
                        hipStream_t s) {
-  return op == OP_F32 ? launch_op<OP_F32>(taps, variant, conv_in, a, s)
-                      : launch_op<OP_BF16>(taps, variant, conv_in, a, s);
+  return op == OP_F32 ? launch_op<OP_F32>(taps, variant, input_layer, a, s)
+                      : launch_op<OP_BF16>(taps, variant, input_layer, a, s);
 }
 
 }  // namespace voc

@@ -44,7 +44,8 @@ struct RowInfo {
 // tau = n*ups + m / Cout - crop, channel o = m % Cout, kept if
 // 0 <= tau < min(len*rate_out, T_out).
 // Epilogue: v = acc + bias[o] (+ res); h_out <- v (fp32);
-//           s_out <- Snake(v; s_alpha, s_invden) in the operand dtype.
+//           s_out <- Snake(v; s_alpha, s_invden) in the operand dtype
+//           (v itself when s_alpha is null).
 struct ConvArgs {
   const void* x;
   int T_in;       // allocated frames per row of x
@@ -82,7 +83,8 @@ int conv_variant_bm(int v);
 int conv_variant_bn(int v);
 bool conv_variant_ok(int v, int taps);
 
-hipError_t launch_conv(int op, int taps, int variant, bool conv_in, const ConvArgs& a,
+// input_layer: conv_in or dec_in_proj (a separate kernel name for profilers).
+hipError_t launch_conv(int op, int taps, int variant, bool input_layer, const ConvArgs& a,
                        hipStream_t s);
 
 // One fused residual unit over all C channels of BN-frame tiles:
@@ -126,7 +128,7 @@ hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s
 enum PackKind { PACK_CONV = 0, PACK_CONVT = 1, PACK_HEAD = 2 };
 struct FoldArgs {
   const float* v;
-  const float* g;
+  const float* g;   // null: no weight norm (w = v)
   int64_t d0, rest;
   int kind;
   int op;           // operand dtype of the packed output (head: always fp32 storage)

@@ -42,6 +42,7 @@ struct BlockDev {
   std::vector<UnitDev> units;
 };
 struct Weights {
+  ConvDev in_proj;  // dec_in_proj (cout == 0: none)
   ConvDev conv_in;
   std::vector<BlockDev> blocks;
   SnakeDev head_act;
@@ -78,9 +79,8 @@ struct voc_ctx {
   std::vector<hipEvent_t> free_events;
   voc_profile_stat stats[VOC_K_COUNT]{};
   // cached row metadata of the last decode
-  int64_t rows_B = -1, rows_T = -1;
-  int rows_n = 0;
-  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
+  std::vector<int64_t> rows_key;  // what the uploaded metadata describes (empty: nothing)
+  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
@@ -120,7 +120,10 @@ voc_status validate(const voc_config* c, std::string* why) {
   if (c->convt_crop != 0) return bad("convt_crop must be 0");
   if (c->tile_frames < 0) return bad("tile_frames must be >= 0");
   const int q = c->dtype == VOC_F32 ? 16 : 32;
-  if (c->latent_channels <= 0 || c->latent_channels % q) return bad("latent_channels must be a positive multiple of 16 (F32) / 32 (BF16)");
+  if (c->latent_channels <= 0 || c->latent_channels % q || c->latent_channels > 8192)
+    return bad("latent_channels must be a positive multiple of 16 (F32) / 32 (BF16), at most 8192");
+  if (c->in_proj < 0 || c->in_proj % q || c->in_proj > 8192)
+    return bad("in_proj must be 0 or a positive multiple of 16 (F32) / 32 (BF16), at most 8192");
   for (int b = 0; b <= c->n_blocks; ++b)
     if (c->width[b] <= 0 || c->width[b] % q || c->width[b] > 8192)
       return bad("widths must be positive multiples of 16 (F32) / 32 (BF16), at most 8192");
@@ -253,6 +256,7 @@ Plan make_plan(const voc_ctx* c, int rows, int T) {
   size_t max_act = 0;
   int64_t t = T;
   max_act = std::max<size_t>(max_act, static_cast<size_t>(g.width[0]) * t);
+  max_act = std::max<size_t>(max_act, static_cast<size_t>(g.in_proj) * t);  // dec_in_proj out (in u)
   for (int b = 0; b < g.n_blocks; ++b) {
     t *= g.stride[b];
     max_act = std::max<size_t>(max_act, static_cast<size_t>(g.width[b + 1]) * t);
@@ -283,7 +287,7 @@ voc_status ensure_ws(voc_ctx* c, size_t bytes) {
     c->ws = nullptr;
     c->ws_bytes = 0;
   }
-  c->rows_B = -1;  // row metadata lived in the old workspace
+  c->rows_key.clear();  // row metadata lived in the old workspace
   hipError_t e = hipMalloc(&c->ws, bytes);
   if (e != hipSuccess) {
     c->ws = nullptr;
@@ -441,7 +445,9 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   if (io.s_out) bytes += frames_out * L.cout * es;
   const int op = c->op;
   return launch(c, s, kind, flops, bytes, "conv launch",
-                [&] { return launch_conv(op, L.taps, v, kind == VOC_K_CONV_IN, a, s); });
+                [&] {
+                  return launch_conv(op, L.taps, v, kind == VOC_K_CONV_IN || kind == VOC_K_IN_PROJ, a, s);
+                });
 }
 
 voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const RowInfo& rows,
@@ -479,7 +485,14 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
   a.w = c->W.head_w;
   a.bias = c->W.head_bias;
   a.pcm = pcm;
-  const double frames = static_cast<double>(nrows) * T;
+  // The kernel reads and writes only the kept samples of each row (their
+  // count is in the row metadata last uploaded for these rows).
+  double frames = static_cast<double>(nrows) * T;
+  const std::vector<int>& mi = c->meta_int;
+  if (mi.size() == static_cast<size_t>(5 * nrows)) {
+    frames = 0.0;
+    for (int r = 0; r < nrows; ++r) frames += mi[4 * nrows + r] - mi[3 * nrows + r];
+  }
   const double flops = 2.0 * frames * a.C * 7;
   const double bytes = frames * a.C * 4 + frames * 4;
   return launch(c, s, VOC_K_HEAD, flops, bytes, "head launch", [&] { return launch_head(a, s); });
@@ -580,7 +593,18 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
   const int nb = g.n_blocks, nr = g.n_res;
   int cur = 0;
   ConvIO io{};
-  io.x = B.xlat;
+  const void* x_in = B.xlat;
+  if (W.in_proj.cout > 0) {  // dec_in_proj: operand for conv_in, no activation between
+    io.x = B.xlat;
+    io.T_in = T;
+    io.rate_in = 1;
+    io.s_out = B.u;
+    voc_status st = run_conv(c, W.in_proj, io, rows, B.rows.len, VOC_K_IN_PROJ, s);
+    if (st) return st;
+    x_in = B.u;
+  }
+  io = ConvIO{};
+  io.x = x_in;
   io.T_in = T;
   io.rate_in = 1;
   io.h_out = B.h;
@@ -658,7 +682,11 @@ std::map<std::string, Expect> expected_tensors(const voc_config& g) {
     m[p + ".alpha"] = {sq({ch})};
     if (g.act == VOC_SNAKE_BETA) m[p + ".beta"] = {sq({ch})};
   };
-  conv("conv_in", g.width[0], g.latent_channels, 7, g.width[0]);
+  if (g.in_proj > 0) {  // plain Conv1d k=1, no weight norm
+    m["dec_in_proj.weight"] = {sq({g.in_proj, g.latent_channels, 1})};
+    m["dec_in_proj.bias"] = {sq({g.in_proj})};
+  }
+  conv("conv_in", g.width[0], g.in_proj > 0 ? g.in_proj : g.latent_channels, 7, g.width[0]);
   for (int b = 0; b < g.n_blocks; ++b) {
     const std::string p = "blocks." + std::to_string(b);
     const int cin = g.width[b], cout = g.width[b + 1];
@@ -830,17 +858,19 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     return upload(hh.data(), ch, &sd->invden);
   };
   // Fold one conv: v is uploaded to a staging buffer, folded into the packed layout.
+  // plain: the tensor is p.weight, used as stored (no weight norm).
   auto fold = [&](const std::string& p, int kind, int cin, int cout, int k, int stride,
-                  void** out_w, float** out_bias) -> voc_status {
-    const voc_tensor* tv = got[p + ".weight_v"];
-    const voc_tensor* tg = got[p + ".weight_g"];
+                  void** out_w, float** out_bias, bool plain = false) -> voc_status {
+    const voc_tensor* tv = got[plain ? p + ".weight" : p + ".weight_v"];
     const int64_t cnt = numel(*tv);
     const int64_t d0 = kind == PACK_CONVT ? cin : cout;
     float *dv = nullptr, *dg = nullptr;
     voc_status st = upload(tv->data, cnt, &dv, true);
     if (st) return st;
-    st = upload(tg->data, d0, &dg, true);
-    if (st) return st;
+    if (!plain) {
+      st = upload(got[p + ".weight_g"]->data, d0, &dg, true);
+      if (st) return st;
+    }
     double* dn = nullptr;
     st = dalloc(d0 * sizeof(double), reinterpret_cast<void**>(&dn));
     if (st) return st;
@@ -865,16 +895,26 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     fa.norms = dn;
     hipError_t e = launch_fold(fa, nullptr);
     if (e != hipSuccess) return hip_fail(c, e, "fold launch");
-    norm_bufs.push_back(dn);
-    norm_names.push_back({p, d0});
+    if (!plain) {  // ||v|| must be positive and finite
+      norm_bufs.push_back(dn);
+      norm_names.push_back({p, d0});
+    }
     if (out_bias) return upload(got[p + ".bias"]->data, cout, out_bias);
     return VOC_OK;
   };
 
   auto build = [&]() -> voc_status {
     voc_status st;
+    if (g.in_proj > 0) {
+      ConvDev& ip = W.in_proj;
+      ip.cin = g.latent_channels;
+      ip.cout = ip.M = g.in_proj;
+      ip.taps = 1;
+      st = fold("dec_in_proj", PACK_CONV, ip.cin, ip.cout, 1, 1, &ip.w, &ip.bias, true);
+      if (st) return st;
+    }
     ConvDev& ci = W.conv_in;
-    ci.cin = g.latent_channels;
+    ci.cin = g.in_proj > 0 ? g.in_proj : g.latent_channels;
     ci.cout = ci.M = g.width[0];
     ci.taps = 7;
     st = fold("conv_in", PACK_CONV, ci.cin, ci.cout, 7, 1, &ci.w, &ci.bias);
@@ -951,6 +991,57 @@ VOC_API int64_t vocoder_output_length(const voc_ctx* c, int64_t T) {
   return T * c->hop;
 }
 
+namespace {
+// One batched decode of `rows` rows read from latent [*, C, T_src] through
+// the row metadata (dst, ints = len | src_b | start | keep_lo | keep_hi),
+// which is uploaded unless `key` matches what the workspace already holds.
+voc_status decode_rows(voc_ctx* c, const float* latent, int64_t T_src, int64_t rows, int T_alloc,
+                       std::vector<int64_t>&& dst, std::vector<int>&& ints,
+                       std::vector<int64_t>&& key, float* pcm, hipStream_t s) {
+  const voc_config& g = c->cfg;
+  const Plan p = make_plan(c, static_cast<int>(rows), T_alloc);
+  voc_status st = ensure_ws(c, p.bytes);
+  if (st) return st;
+  if (c->rows_key != key) {
+    st = upload_rows(c, p, std::move(dst), std::move(ints), s);
+    if (st) return st;
+    c->rows_key = std::move(key);
+  }
+  const Bufs Bf = bufs(c, p);
+  st = run_import(c, latent, T_src, g.latent_channels, Bf.rows, static_cast<int>(rows), T_alloc, Bf.xlat,
+                  nullptr, nullptr, s);
+  if (st) return st;
+  float* h_last = nullptr;
+  st = run_stack(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last);
+  if (st) return st;
+  return run_head(c, h_last, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
+                  static_cast<int>(c->hop), pcm, s);
+}
+
+// Kept latent frames [lo, hi) of window k of n (window stitching): every
+// window but the first drops crop_left frames on the left, every window but
+// the last drops crop_right on the right.
+void window_keep(int64_t k, int64_t n, int64_t L, int64_t L_last, int64_t cl, int64_t cr, int64_t* lo,
+                 int64_t* hi) {
+  const int64_t len = k == n - 1 ? L_last : L;
+  *lo = k > 0 ? cl : 0;
+  *hi = len - (k < n - 1 ? cr : 0);
+}
+
+bool windows_valid(int64_t n, int64_t L, int64_t L_last, int64_t cl, int64_t cr) {
+  if (n <= 0 || L <= 0 || L_last <= 0 || L_last > L || cl < 0 || cr < 0) return false;
+  // The first window, a middle one (they are all alike) and the last must
+  // each keep at least one frame.
+  const int64_t ks[3] = {0, n > 2 ? 1 : 0, n - 1};
+  for (int64_t k : ks) {
+    int64_t lo, hi;
+    window_keep(k, n, L, L_last, cl, cr, &lo, &hi);
+    if (hi <= lo) return false;
+  }
+  return true;
+}
+}  // namespace
+
 VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, int64_t T, float* pcm,
                                   void* stream) {
   if (!c) return VOC_INVALID_PARAMS;
@@ -960,7 +1051,6 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
   if (B <= 0 || T <= 0) return fail(c, VOC_INVALID_PARAMS, "B and T must be positive");
   if (T * c->hop > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "T*hop exceeds 2^31-1");
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const voc_config& g = c->cfg;
   // Rows: whole rows, or tiles of tile_frames latent frames with halos.
   const int64_t F = g.tile_frames > 0 ? g.tile_frames : T;
@@ -968,8 +1058,7 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
   const int64_t rows = B * ntile;
   if (rows > 65535) return fail(c, VOC_INVALID_PARAMS, "too many rows (B * tiles > 65535)");
   const int H = g.tile_frames > 0 ? c->halo : 0;
-  int T_alloc = static_cast<int>(std::min<int64_t>(T, F + 2 * H));
-  int64_t work_rows_frames = 0;
+  const int T_alloc = static_cast<int>(std::min<int64_t>(T, F + 2 * H));
   std::vector<int64_t> dst(rows);
   std::vector<int> ints(5 * rows);
   for (int64_t b = 0; b < B; ++b)
@@ -983,28 +1072,61 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
       ints[3 * rows + r] = static_cast<int>((t0 - a) * c->hop);   // keep_lo
       ints[4 * rows + r] = static_cast<int>((t1 - a) * c->hop);   // keep_hi
       dst[r] = b * T * c->hop + t0 * c->hop;
-      work_rows_frames += e - a;
     }
-  (void)work_rows_frames;
-  const Plan p = make_plan(c, static_cast<int>(rows), T_alloc);
-  voc_status st = ensure_ws(c, p.bytes);
-  if (st) return st;
-  if (c->rows_B != B || c->rows_T != T || c->rows_n != rows) {
-    st = upload_rows(c, p, std::move(dst), std::move(ints), s);
-    if (st) return st;
-    c->rows_B = B;
-    c->rows_T = T;
-    c->rows_n = static_cast<int>(rows);
+  return decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {0, B, T, rows}, pcm,
+                     static_cast<hipStream_t>(stream));
+}
+
+VOC_API int64_t vocoder_windows_output_length(const voc_ctx* c, int64_t n, int64_t L, int64_t L_last,
+                                              int64_t cl, int64_t cr) {
+  if (!c || !windows_valid(n, L, L_last, cl, cr)) return -1;
+  int64_t kept = 0;
+  for (int64_t k = 0; k < n; ++k) {
+    int64_t lo, hi;
+    window_keep(k, n, L, L_last, cl, cr, &lo, &hi);
+    kept += hi - lo;
   }
-  const Bufs Bf = bufs(c, p);
-  st = run_import(c, latent, T, g.latent_channels, Bf.rows, static_cast<int>(rows), T_alloc, Bf.xlat,
-                  nullptr, nullptr, s);
-  if (st) return st;
-  float* h_last = nullptr;
-  st = run_stack(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last);
-  if (st) return st;
-  return run_head(c, h_last, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
-                  static_cast<int>(c->hop), pcm, s);
+  return kept * c->hop;
+}
+
+VOC_API voc_status vocoder_decode_windows(voc_ctx* c, const float* latents, int64_t n, int64_t sides,
+                                          int64_t L, int64_t L_last, int64_t cl, int64_t cr, float* pcm,
+                                          void* stream) {
+  if (!c) return VOC_INVALID_PARAMS;
+  if (!latents || !pcm) return fail(c, VOC_INVALID_PARAMS, "NULL latents or pcm");
+  if ((reinterpret_cast<uintptr_t>(latents) | reinterpret_cast<uintptr_t>(pcm)) & 15)
+    return fail(c, VOC_INVALID_PARAMS, "latents and pcm must be 16-byte aligned");
+  if (sides != 1 && sides != 2) return fail(c, VOC_INVALID_PARAMS, "sides must be 1 or 2");
+  if (!windows_valid(n, L, L_last, cl, cr))
+    return fail(c, VOC_INVALID_PARAMS, "bad window count, lengths or crops (every window must keep a frame)");
+  if (c->cfg.tile_frames != 0) return fail(c, VOC_INVALID_PARAMS, "windowed decode needs tile_frames == 0");
+  if (L * c->hop > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "L*hop exceeds 2^31-1");
+  const int64_t rows = n * sides;
+  if (rows > 65535) return fail(c, VOC_INVALID_PARAMS, "too many rows (n_windows * sides > 65535)");
+  if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  const int64_t N = vocoder_windows_output_length(c, n, L, L_last, cl, cr);
+  // Row k*sides + j decodes side j of window k (row k*sides + j of the
+  // [n*sides, C, L] view) and writes its kept samples at
+  // pcm[j*N + hop * (frames kept by windows 0..k-1)].
+  std::vector<int64_t> dst(rows);
+  std::vector<int> ints(5 * rows);
+  int64_t before = 0;
+  for (int64_t k = 0; k < n; ++k) {
+    int64_t lo, hi;
+    window_keep(k, n, L, L_last, cl, cr, &lo, &hi);
+    for (int64_t j = 0; j < sides; ++j) {
+      const int64_t r = k * sides + j;
+      ints[r] = static_cast<int>(k == n - 1 ? L_last : L);        // len
+      ints[rows + r] = static_cast<int>(r);                       // src_b
+      ints[2 * rows + r] = 0;                                     // start
+      ints[3 * rows + r] = static_cast<int>(lo * c->hop);         // keep_lo
+      ints[4 * rows + r] = static_cast<int>(hi * c->hop);         // keep_hi
+      dst[r] = j * N + before * c->hop;
+    }
+    before += hi - lo;
+  }
+  return decode_rows(c, latents, L, rows, static_cast<int>(L), std::move(dst), std::move(ints),
+                     {1, n, sides, L, L_last, cl, cr}, pcm, static_cast<hipStream_t>(stream));
 }
 
 VOC_API const char* vocoder_last_error(const voc_ctx* c) {
@@ -1110,7 +1232,8 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
   const int rows = static_cast<int>(B);
   // Workspace: enough for the stage's input and output at these frames; the
   // row metadata treats each row as a whole clip of T_in frames at rate 1.
-  const int64_t cmax = std::max(si.c_in, si.c_out);
+  int64_t cmax = std::max(si.c_in, si.c_out);
+  if (si.kind == 0) cmax = std::max<int64_t>(cmax, c->cfg.in_proj);  // dec_in_proj output in u
   const size_t es = op_size(c->op);
   const size_t act_in = static_cast<size_t>(rows) * si.c_in * T_in;
   const size_t act_out = static_cast<size_t>(rows) * cmax * t_out;
@@ -1145,7 +1268,7 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
   }
   st = upload_rows(c, p, std::move(dst), std::move(ints), s);
   if (st) return st;
-  c->rows_B = -1;  // the decode's cached metadata is gone
+  c->rows_key.clear();  // the decode's cached metadata is gone
   char* m = base + off_meta;
   RowInfo ri{};
   ri.dst = reinterpret_cast<const int64_t*>(m);
@@ -1162,7 +1285,15 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
     case 0:
       st = run_import(c, in, T_in, si.c_in, ri, rows, T, s0, nullptr, nullptr, s);
       if (st) return st;
-      io.x = s0; io.T_in = T; io.rate_in = 1; io.h_out = h;
+      io.x = s0; io.T_in = T; io.rate_in = 1;
+      if (W.in_proj.cout > 0) {
+        io.s_out = u;
+        st = run_conv(c, W.in_proj, io, rows, ri.len, VOC_K_IN_PROJ, s);
+        if (st) return st;
+        io = ConvIO{};
+        io.x = u; io.T_in = T; io.rate_in = 1;
+      }
+      io.h_out = h;
       st = run_conv(c, W.conv_in, io, rows, ri.len, VOC_K_CONV_IN, s);
       break;
     case 1:

@@ -13,7 +13,8 @@ namespace voc {
 
 // ---------------------------------------------------------------- fold
 // Weight norm (minimaxmusic.cpp ARCHITECTURE, "Models"): w = g v / ||v||,
-// the norm over each slice along axis 0 of the stored tensor.  One workgroup
+// the norm over each slice along axis 0 of the stored tensor; with g NULL
+// (dec_in_proj, which has no weight norm) w = v.  One workgroup
 // per slice; the sum of squares is accumulated in fp64.  The folded value is
 // rounded fp64 -> fp32 (the F32 inference weights), then for bf16 operands
 // to bf16 (round to nearest even), and written at its packed position.
@@ -34,10 +35,11 @@ __global__ __launch_bounds__(256) void fold_kernel(const FoldArgs a) {
   }
   const double n = sqrt(red[0]);
   if (threadIdx.x == 0) a.norms[i] = n;
-  const double g = a.g[i];
+  const bool plain = a.g == nullptr;  // a weight without weight norm: used as stored
+  const double g = plain ? 1.0 : a.g[i];
   const int ch = a.op == OP_F32 ? 16 : 32;
   for (int64_t e = threadIdx.x; e < a.rest; e += 256) {
-    const float wf = static_cast<float>(g * static_cast<double>(v[e]) / n);
+    const float wf = plain ? v[e] : static_cast<float>(g * static_cast<double>(v[e]) / n);
     int64_t idx;
     if (a.kind == PACK_CONV) {  // (Cout, Cin, K), slice = o
       const int ci = static_cast<int>(e / a.k), kk = static_cast<int>(e % a.k);

@@ -17,7 +17,7 @@ import numpy as np
 LIB_PATH = os.environ.get("VOC_LIBRARY") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libvocoder.so")
 
-VOC_ABI_VERSION = 1
+VOC_ABI_VERSION = 2
 VOC_MAX_BLOCKS = 8
 VOC_MAX_RES = 4
 
@@ -31,7 +31,8 @@ VOC_NOT_LOADED = -5
 VOC_F32, VOC_BF16 = 0, 1
 VOC_SNAKE, VOC_SNAKE_BETA = 0, 1
 
-KERNEL_KINDS = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused"]
+KERNEL_KINDS = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused",
+                "in_proj"]
 
 
 class voc_config(ctypes.Structure):
@@ -51,6 +52,7 @@ class voc_config(ctypes.Structure):
         ("snake_log_params", ctypes.c_int),
         ("convt_crop", ctypes.c_int),
         ("tile_frames", ctypes.c_int),
+        ("in_proj", ctypes.c_int),
     ]
 
 
@@ -94,6 +96,8 @@ def lib():
             "vocoder_load_weights": (I, [P, ctypes.POINTER(voc_tensor), I]),
             "vocoder_output_length": (I64, [P, I64]),
             "vocoder_decode": (I, [P, P, I64, I64, P, P]),
+            "vocoder_decode_windows": (I, [P, P, I64, I64, I64, I64, I64, I64, P, P]),
+            "vocoder_windows_output_length": (I64, [P, I64, I64, I64, I64, I64]),
             "vocoder_last_error": (ctypes.c_char_p, [P]),
             "vocoder_destroy": (None, [P]),
             "vocoder_profile_enable": (I, [P, I]),
@@ -156,6 +160,7 @@ def config_from_dict(d: dict) -> voc_config:
     c.dtype = VOC_BF16 if d["dtype"] == "bf16" else VOC_F32
     c.snake_log_params = d.get("snake_log_params", 0)
     c.tile_frames = d.get("tile_frames", 0)
+    c.in_proj = d.get("in_proj", 0)
     return c
 
 
@@ -209,6 +214,17 @@ def vocoder_output_length(ctx, T: int) -> int:
 
 def vocoder_decode(ctx, latent, B: int, T: int, pcm, stream=None) -> int:
     return lib().vocoder_decode(ctx, _ptr(latent), B, T, _ptr(pcm), _stream(stream))
+
+
+def vocoder_decode_windows(ctx, latents, n: int, sides: int, L: int, L_last: int,
+                           crop_left: int, crop_right: int, pcm, stream=None) -> int:
+    return lib().vocoder_decode_windows(ctx, _ptr(latents), n, sides, L, L_last, crop_left,
+                                        crop_right, _ptr(pcm), _stream(stream))
+
+
+def vocoder_windows_output_length(ctx, n: int, L: int, L_last: int, crop_left: int,
+                                  crop_right: int) -> int:
+    return lib().vocoder_windows_output_length(ctx, n, L, L_last, crop_left, crop_right)
 
 
 def vocoder_last_error(ctx) -> str:
@@ -286,6 +302,22 @@ def decode(ctx, latent, stream=None):
     b, _, t = latent.shape
     pcm = torch.empty(b, 1, vocoder_output_length(ctx, t), device=latent.device)
     check(vocoder_decode(ctx, latent, b, t, pcm, stream), ctx)
+    return pcm
+
+
+def decode_windows(ctx, windows, sides: int, last_frames: int, crop_left: int, crop_right: int,
+                   stream=None):
+    """Planar pcm [sides, N] (new CUDA tensor) for CUDA fp32 windows
+    [n, sides * C, L] (vocoder_decode_windows)."""
+    import torch
+    assert windows.is_cuda and windows.dtype == torch.float32 and windows.is_contiguous()
+    n, _, L = windows.shape
+    N = vocoder_windows_output_length(ctx, n, L, last_frames, crop_left, crop_right)
+    if N < 0:
+        raise VocError(VOC_INVALID_PARAMS, "bad window lengths or crops")
+    pcm = torch.empty(sides, N, device=windows.device)
+    check(vocoder_decode_windows(ctx, windows, n, sides, L, last_frames, crop_left, crop_right,
+                                 pcm, stream), ctx)
     return pcm
 
 

@@ -8,7 +8,8 @@
  * The decoder (minimaxmusic.cpp ARCHITECTURE page, section "Flow VAE"; the
  * DAC stack of the qwentts.cpp ARCHITECTURE page, "Audio tokenizer decoder"):
  *
- *   h   = conv_in(latent)                       Conv1d k=7, zero "same" padding, bias
+ *   x   = dec_in_proj(latent)                   optional Conv1d k=1, bias, no weight norm
+ *   h   = conv_in(x)                            Conv1d k=7, zero "same" padding, bias
  *   per block b with stride s:
  *     h = conv_t1(Snake(h))                     ConvTranspose1d k=2s, stride s, crop ceil(s/2)
  *     per residual unit with dilation d (1, 3, 9):
@@ -26,6 +27,8 @@
  * 64-channel tracks, channels 0..63 left (minimaxmusic.cpp ARCHITECTURE,
  * "Flow VAE").  A caller holding [b, 128, t] passes the view [2b, 64, t]
  * (rows 2i = left, 2i+1 = right) and reads the [2b, 1, N] output as [b, 2, N].
+ * vocoder_decode_windows does the same fold per window and writes planar
+ * stereo.
  *
  * Conventions follow the qwentts.cpp public ABI (ARCHITECTURE page, "Public
  * API" and "ABI guarantee"): an opaque context, a parameter struct carrying
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define VOC_ABI_VERSION 1
+#define VOC_ABI_VERSION 2
 #define VOC_MAX_BLOCKS 8
 #define VOC_MAX_RES 4
 
@@ -72,9 +75,9 @@ typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
  * Architecture description.  Constraints (checked by voc_config_validate):
  * abi_version == VOC_ABI_VERSION; 1 <= n_blocks <= VOC_MAX_BLOCKS;
  * 1 <= n_res <= VOC_MAX_RES; 1 <= dilation[r] <= 9; stride[b] >= 1;
- * in_kernel == res_kernel == out_kernel == 7; widths and latent_channels
- * positive multiples of 16 (F32) or 32 (BF16), width[n_blocks] <= 512;
- * convt_crop == 0; tile_frames >= 0.
+ * in_kernel == res_kernel == out_kernel == 7; widths, latent_channels and a
+ * non-zero in_proj positive multiples of 16 (F32) or 32 (BF16), at most 8192,
+ * width[n_blocks] <= 512; convt_crop == 0; tile_frames >= 0; in_proj >= 0.
  */
 typedef struct voc_config {
   int abi_version;
@@ -94,10 +97,17 @@ typedef struct voc_config {
                                    /* (other values reserved)                   */
   int tile_frames;                 /* 0: decode whole rows; F > 0: decode time  */
                                    /* tiles of F latent frames with exact halos */
+  int in_proj;                     /* 0: none; P > 0: dec_in_proj, a Conv1d k=1 */
+                                   /* latent_channels -> P with bias and no     */
+                                   /* weight norm, ahead of conv_in (which then */
+                                   /* has P input channels): the DAV decoder    */
+                                   /* of minimaxmusic.cpp ARCHITECTURE, "Flow   */
+                                   /* VAE" (64 -> 1024, conv_in 1024 -> 1536)   */
 } voc_config;
 
 /* Fill *cfg with the full-width stereo window decoder: latent 64, widths
- * 1024/512/256/128/64, strides 8,8,4,2, dilations 1,3,9, Snake, F32, untiled. */
+ * 1024/512/256/128/64, strides 8,8,4,2, dilations 1,3,9, Snake, F32, untiled,
+ * no dec_in_proj. */
 void voc_config_default(voc_config *cfg);
 
 /* Host-only checks of *cfg (no device is touched). */
@@ -119,7 +129,9 @@ voc_status vocoder_create(const voc_config *cfg, int hip_device, voc_ctx **out);
  * One named host tensor, fp32, contiguous, caller-owned.  Names and shapes
  * (PyTorch conventions; size-1 dims may be dropped, e.g. g as [d0] or
  * [d0,1,1], alpha as [C] or [1,C,1]):
- *   conv_in.{weight_v [W0,Clat,7], weight_g [W0,1,1], bias [W0]}
+ *   dec_in_proj.{weight [P,Clat,1], bias [P]}      (only with in_proj = P > 0)
+ *   conv_in.{weight_v [W0,Cin,7], weight_g [W0,1,1], bias [W0]}
+ *                                     (Cin = in_proj if non-zero, else Clat)
  *   blocks.{b}.snake1.alpha [1,Wb,1]          (+ .beta for SnakeBeta)
  *   blocks.{b}.conv_t1.{weight_v [Wb,Wb+1,2s], weight_g [Wb,1,1], bias [Wb+1]}
  *   blocks.{b}.res_units.{r}.snake1.alpha, .conv1.{weight_v [W,W,7], weight_g, bias},
@@ -163,6 +175,41 @@ int64_t vocoder_output_length(const voc_ctx *ctx, int64_t T);
 voc_status vocoder_decode(voc_ctx *ctx, const float *latent, int64_t B, int64_t T,
                           float *pcm, void *hip_stream);
 
+/*
+ * Windowed decode with stitching (minimaxmusic.cpp ARCHITECTURE, "Inference
+ * recipe", "Decode and stitch" and "Post-processing"): each latent window is
+ * decoded on its own; every window but the first drops crop_left latent
+ * frames (x hop samples) on the left, every window but the last drops
+ * crop_right frames on the right, and the kept segments are concatenated in
+ * window order, clamped to [-1, 1] (the identity after tanh), into planar
+ * output.  With the pages' windows of 689 frames and crops 86 / 258, windows
+ * that start 689 - 86 - 258 = 345 frames apart tile the track seamlessly.
+ *
+ * latents: device fp32 [n_windows, sides * latent_channels, L] contiguous;
+ *   side j of window k is channels [j*C, (j+1)*C) (stereo: 0..63 left), so
+ *   the array is the [n_windows * sides, C, L] rows that vocoder_decode takes.
+ *   The last window holds L_last valid frames (1 <= L_last <= L); its frames
+ *   at and beyond L_last are ignored.
+ * pcm: device fp32 [sides, N] planar ([L: N][R: N] for stereo) with
+ *   N = vocoder_windows_output_length(...) samples per side.
+ * sides is 1 (mono) or 2 (stereo).  Every window must keep at least one
+ * frame (e.g. L > crop_left + crop_right for the middle windows).  Requires
+ * tile_frames == 0.  Same asynchrony and buffer ownership as vocoder_decode;
+ * one batched decode of all n_windows * sides rows.
+ * Errors: VOC_INVALID_PARAMS (NULL/misaligned pointers, bad counts or crops,
+ * a window keeping nothing, tile_frames != 0), VOC_NOT_LOADED, VOC_OOM,
+ * VOC_DEVICE_ERROR.
+ */
+voc_status vocoder_decode_windows(voc_ctx *ctx, const float *latents, int64_t n_windows,
+                                  int64_t sides, int64_t L, int64_t L_last,
+                                  int64_t crop_left, int64_t crop_right, float *pcm,
+                                  void *hip_stream);
+
+/* Samples per side that vocoder_decode_windows writes for these arguments:
+ * hop times the kept latent frames of all windows; -1 if they are invalid. */
+int64_t vocoder_windows_output_length(const voc_ctx *ctx, int64_t n_windows, int64_t L,
+                                      int64_t L_last, int64_t crop_left, int64_t crop_right);
+
 /* Message of the last error on ctx ("" if none); valid until the next call on
  * ctx.  With ctx == NULL, the message of the last failed vocoder_create. */
 const char *vocoder_last_error(const voc_ctx *ctx);
@@ -186,7 +233,8 @@ typedef enum voc_kernel_kind {
   VOC_K_IMPORT = 5,   /* latent transpose / tile gather                 */
   VOC_K_EXPORT = 6,   /* debug-stage output transpose                   */
   VOC_K_RES_FUSED = 7, /* whole residual unit (conv1, Snake2, conv2, add) */
-  VOC_K_COUNT = 8
+  VOC_K_IN_PROJ = 8,  /* dec_in_proj (k=1) GEMM                         */
+  VOC_K_COUNT = 9
 } voc_kernel_kind;
 
 typedef struct voc_profile_stat {
@@ -208,7 +256,7 @@ voc_status vocoder_profile_read(voc_ctx *ctx, int kind, voc_profile_stat *out);
 
 /* ---------------------------------------------------- debug (not ABI-stable)
  * Stage k of the decoder on caller buffers, for teacher-forced checks:
- *   0 = conv_in; for block b: 1 + b*(1+n_res) = Snake + ConvTranspose1d,
+ *   0 = conv_in (after dec_in_proj when in_proj > 0); for block b: 1 + b*(1+n_res) = Snake + ConvTranspose1d,
  *   the next n_res indices = its residual units; count-1 = the head.
  * in: device fp32 [B, C_in(k), T_in] (stage 0: the latent); out: device fp32
  * [B, C_out(k), T_out] (head: [B, 1, T_in]).  Uses the same kernels as

@@ -24,6 +24,12 @@ int main(void) {
   EXPECT(voc_config_validate(&cfg) == VOC_OK);
   EXPECT(voc_config_hop(&cfg) == 512);
   EXPECT(voc_config_halo(&cfg) == 10);
+  EXPECT(cfg.in_proj == 0);
+  cfg.in_proj = 1024;
+  EXPECT(voc_config_validate(&cfg) == VOC_OK);
+  cfg.in_proj = 24;
+  EXPECT(voc_config_validate(&cfg) == VOC_INVALID_PARAMS);
+  cfg.in_proj = 0;
   EXPECT(voc_config_validate(NULL) == VOC_INVALID_PARAMS);
   cfg.abi_version = VOC_ABI_VERSION + 1;
   EXPECT(voc_config_validate(&cfg) == VOC_INVALID_PARAMS);
@@ -35,6 +41,8 @@ int main(void) {
   EXPECT(vocoder_load_weights(NULL, NULL, 0) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_output_length(NULL, 5) == -1);
   EXPECT(vocoder_decode(NULL, dummy, 1, 1, dummy, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_decode_windows(NULL, dummy, 3, 2, 689, 683, 86, 258, dummy, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_windows_output_length(NULL, 3, 689, 683, 86, 258) == -1);
   EXPECT(vocoder_profile_enable(NULL, 1) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_profile_reset(NULL) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_profile_read(NULL, 0, &st) == VOC_INVALID_PARAMS);

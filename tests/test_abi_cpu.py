@@ -45,14 +45,14 @@ def test_c99_consumer(tmp_path):
     assert "abi ok" in res.stdout
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("idx", sorted(I.CONFIGS))
 def test_configs_validate(idx):
     cfg = V.config_from_dict(I.CONFIGS[idx])
     assert V.voc_config_validate(cfg) == V.VOC_OK
     assert V.voc_config_hop(cfg) == I.CONFIGS[idx]["hop"]
 
 
-@pytest.mark.parametrize("idx", [1, 4])
+@pytest.mark.parametrize("idx", [1, 4, 5])
 def test_halo_matches_oracle_brute_force(idx):
     # The oracle's tiling pin shows H = 10 reproduces the untiled decode and
     # H = 9 does not, for both stride stacks; the library's interval
@@ -74,7 +74,7 @@ def _bad(**kw):
     dict(n_blocks=0), dict(n_blocks=9), dict(n_res=0), dict(in_kernel=5), dict(act=7),
     dict(dtype=3), dict(convt_crop=1), dict(tile_frames=-1), dict(latent_channels=60),
     dict(width=(2, 100)), dict(width=(4, 1024)), dict(stride=(0, 0)), dict(dilation=(1, 10)),
-    dict(snake_log_params=2),
+    dict(snake_log_params=2), dict(in_proj=-16), dict(in_proj=24), dict(in_proj=8208),
 ])
 def test_invalid_configs_rejected_before_any_device_call(kw):
     c = _bad(**kw)

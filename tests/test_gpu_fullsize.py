@@ -1,4 +1,5 @@
-"""Parity at the full sizes of the five synthetic workloads, in the launch
+"""Parity at the full sizes of the synthetic single-decode workloads (the
+windowed song is covered in test_gpu_windows.py), in the launch
 configuration the benchmark times.  The oracle cannot decode these whole in
 seconds, so it computes sampled outputs exactly:
 
@@ -26,7 +27,7 @@ pytestmark = pytest.mark.gpu
 HALO = 10
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
 def test_fullsize_stage_parity_sampled(idx):
     cfg = I.config(idx)
     t = I.make_weights(cfg)
@@ -55,7 +56,7 @@ def test_fullsize_stage_parity_sampled(idx):
         V.vocoder_destroy(ctx)
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
 def test_fullsize_twin_decode_sampled(idx):
     cfg = I.config(idx)
     t = I.make_weights(cfg, twin=True)
@@ -84,7 +85,7 @@ def test_fullsize_twin_decode_sampled(idx):
             assert e_rms <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
 def test_fullsize_literal_invariants(idx):
     cfg = I.config(idx)
     t = I.make_weights(cfg)
