@@ -89,14 +89,14 @@ EXPORT void orc_weight_norm(const REAL *v, const REAL *g, REAL *w, int64_t d0,
 }
 
 /*
- * Conv1d with zero "same" padding P = (K-1)/2 * dil (K odd):
+ * Conv1d with zero left padding P, output length T:
  *   y[r][o][t] = bias[o] + sum_i sum_j w[o][i][j] * x[r][i][t + j*dil - P],
- * x outside [0, T) is zero.  w is [Cout][Cin][K]; bias may be NULL.
+ * x outside [0, T) is zero.  P = (K-1)/2 * dil is the "same" convolution,
+ * P = (K-1) * dil the causal one.  w is [Cout][Cin][K]; bias may be NULL.
  */
 EXPORT void orc_conv1d(const REAL *x, REAL *y, int64_t rows, int64_t Cin, int64_t T,
                        const REAL *w, const REAL *bias, int64_t Cout, int64_t K,
-                       int64_t dil) {
-  const int64_t P = (K - 1) / 2 * dil;
+                       int64_t dil, int64_t P) {
 #pragma omp parallel for collapse(2) schedule(static)
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t o = 0; o < Cout; ++o) {

@@ -30,6 +30,13 @@ Readings of points the pages leave open (each listed in the design notes):
     0.01;
   * dec_in_proj feeds conv_in directly (the listing puts no activation
     between them), and its output is zero-padded like any conv input;
+  * causal configurations (qwentts.cpp ARCHITECTURE, "Audio tokenizer
+    decoder": CausalTransConv, and "Streaming decode (stateful path)": every
+    module causal, state cleared to zero at reset = the offline zero left
+    pads): every k=7 conv (conv_in, residual conv1, conv_out) pads (K-1)*d on
+    the left only, and the transposed conv keeps full[n] for n in [0, T*s)
+    (its K - s = s tail on the right is what a stream carries into the next
+    frame);
   * windowed decode (ARCHITECTURE, "Inference recipe": "Decode and stitch",
     "Post-processing"): windows are decoded independently, every window but
     the first loses crop_left latent frames (x hop samples) on the left, every
@@ -80,7 +87,7 @@ def load_library(path: str, prec: str):
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_snake.argtypes = [P, P, I, I, I, P, P]
     lib.orc_weight_norm.argtypes = [P, P, P, I, I, P]
-    lib.orc_conv1d.argtypes = [P, P, I, I, I, P, P, I, I, I]
+    lib.orc_conv1d.argtypes = [P, P, I, I, I, P, P, I, I, I, I]
     lib.orc_conv_transpose1d.argtypes = [P, P, I, I, I, P, P, I, I, I, I, I]
     lib.orc_tanh.argtypes = [P, P, I]
     lib.orc_add.argtypes = [P, P, P, I]
@@ -140,22 +147,25 @@ def weight_norm(v, g, prec="f64"):
     return w, n
 
 
-def conv1d(x, w, bias=None, dilation=1, prec="f64"):
-    """Zero 'same'-padded Conv1d.  x: [R, Cin, T], w: [Cout, Cin, K] (K odd)."""
+def conv1d(x, w, bias=None, dilation=1, prec="f64", causal=False):
+    """Zero-padded Conv1d keeping the length.  x: [R, Cin, T], w: [Cout, Cin, K]
+    (K odd).  'same' padding (K-1)/2*d each side, or causal: (K-1)*d on the left."""
     x = _c(x, prec)
     w = _c(w, prec)
     r, cin, t = x.shape
     cout, cin2, k = w.shape
     assert cin == cin2 and k % 2 == 1
+    pad = (k - 1) * dilation if causal else (k - 1) // 2 * dilation
     b = None if bias is None else _c(np.reshape(bias, -1), prec)
     y = np.empty((r, cout, t), dtype=_NP[prec])
-    _lib(prec).orc_conv1d(_p(x), _p(y), r, cin, t, _p(w), _p(b), cout, k, dilation)
+    _lib(prec).orc_conv1d(_p(x), _p(y), r, cin, t, _p(w), _p(b), cout, k, dilation, pad)
     return y
 
 
-def convt_crop(stride: int) -> int:
-    """Left crop of the transposed conv: ceil(s/2) (s/2 for even s)."""
-    return (stride + 1) // 2
+def convt_crop(stride: int, causal: bool = False) -> int:
+    """Left crop of the transposed conv: ceil(s/2) (s/2 for even s), or 0 for
+    the causal transposed conv (which drops the K - s tail on the right)."""
+    return 0 if causal else (stride + 1) // 2
 
 
 def conv_transpose1d(x, w, bias, stride, pad_left=None, out_len=None, prec="f64"):
@@ -216,6 +226,7 @@ class Model:
         self.bf16 = (cfg["dtype"] == "bf16") if bf16 is None else bf16
         self.round_operands = round_operands and self.bf16
         self.beta = cfg["act"] == "snakebeta"
+        self.causal = bool(cfg.get("causal", 0))
         self.norms = {}
         t = tensors
 
@@ -275,16 +286,16 @@ class Model:
             if self.round_operands:  # conv_in's matrix-core operand
                 x = _c(round_bf16(x), self.prec)
         w, b = self.conv_in
-        return conv1d(x, w, b, 1, self.prec)
+        return conv1d(x, w, b, 1, self.prec, self.causal)
 
     def stage_upsample(self, b, h):
         blk = self.blocks[b]
-        return conv_transpose1d(self._snake(h, blk["act"]), blk["wt"], blk["bt"],
-                                blk["s"], prec=self.prec)
+        return conv_transpose1d(self._snake(h, blk["act"]), blk["wt"], blk["bt"], blk["s"],
+                                pad_left=convt_crop(blk["s"], self.causal), prec=self.prec)
 
     def stage_res_unit(self, b, r, h):
         u = self.blocks[b]["units"][r]
-        v = conv1d(self._snake(h, u["act1"]), u["w1"], u["b1"], u["d"], self.prec)
+        v = conv1d(self._snake(h, u["act1"]), u["w1"], u["b1"], u["d"], self.prec, self.causal)
         return add(h, conv1d(self._snake(v, u["act2"]), u["w2"], u["b2"], 1, self.prec),
                    self.prec)
 
@@ -292,7 +303,7 @@ class Model:
         # The head contracts to one output channel: no matrix-core operand,
         # so its Snake output is not rounded even in round_operands mode.
         a, w, b = self.head
-        return conv1d(self._snake(h, a, operand=False), w, b, 1, self.prec)
+        return conv1d(self._snake(h, a, operand=False), w, b, 1, self.prec, self.causal)
 
     def stage_head(self, h):
         return tanh(self.stage_head_pre(h), self.prec)

@@ -64,8 +64,8 @@ def _pins(orc):
         P.test_convt_polyphase_identity(orc, s)
     P.test_convt_impulse_response(orc)
     P.test_residual_unit_zero_conv2_is_identity(orc)
-    P.test_decode_matches_torch_composition(orc, (2, 2), "snake", 0)
-    P.test_decode_matches_torch_composition(orc, (3, 2), "snakebeta", 0)
+    P.test_decode_matches_torch_composition(orc, (2, 2), "snake", 0, 0)
+    P.test_decode_matches_torch_composition(orc, (3, 2), "snakebeta", 0, 0)
     P.test_golden_lengths_and_vocoder_gate(orc)
 
 
@@ -104,6 +104,14 @@ PY_MUTANTS = [
     ("in_proj_weight_normed", "__init__", 'w = np.asarray(t["dec_in_proj.weight"], dtype=np.float32)',
      'w = np.asarray(t["dec_in_proj.weight"], dtype=np.float32); '
      'w = (w / np.linalg.norm(w, axis=(1, 2), keepdims=True)).astype(np.float32)'),
+    ("causal_conv1_centered", "stage_res_unit",
+     'u["d"], self.prec, self.causal)', 'u["d"], self.prec, False)'),
+    ("causal_convt_centered", "stage_upsample", "pad_left=convt_crop(blk[\"s\"], self.causal)",
+     "pad_left=convt_crop(blk[\"s\"], False)"),
+    ("causal_head_centered", "stage_head_pre", "w, b, 1, self.prec, self.causal)",
+     "w, b, 1, self.prec, False)"),
+    ("causal_conv_in_centered", "stage_conv_in", "return conv1d(x, w, b, 1, self.prec, self.causal)",
+     "return conv1d(x, w, b, 1, self.prec, False)"),
     ("in_proj_after_snake", "stage_conv_in", "x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec)",
      "x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec); "
      "x = snake(x, np.ones(x.shape[1]), None, self.prec)"),
@@ -111,7 +119,9 @@ PY_MUTANTS = [
 
 
 def _py_pins(orc):
-    P.test_decode_matches_torch_composition(orc, (2, 2), "snake", 5)
+    P.test_decode_matches_torch_composition(orc, (2, 2), "snake", 5, 0)
+    P.test_decode_matches_torch_composition(orc, (3, 2), "snakebeta", 0, 1)
+    P.test_causal_decode_of_a_prefix_is_a_prefix(orc, (8, 5))
     P.test_in_proj_composes_with_conv_in(orc)
     P.test_window_stitch_bookkeeping_at_the_pages_sizes(orc)
     P.test_windows_cut_from_one_track_equal_its_decode(orc)

@@ -21,9 +21,11 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(12345)
 
 
-def tiny_cfg(strides=(2, 2), widths=(8, 6, 4), latent=3, act="snake", dil=(1, 3, 9), in_proj=0):
+def tiny_cfg(strides=(2, 2), widths=(8, 6, 4), latent=3, act="snake", dil=(1, 3, 9), in_proj=0,
+             causal=0):
     return I.config(0, strides=tuple(strides), widths=tuple(widths), latent_channels=latent,
-                    act=act, dilations=tuple(dil), frames=9, batch=2, in_proj=in_proj)
+                    act=act, dilations=tuple(dil), frames=9, batch=2, in_proj=in_proj,
+                    causal=causal)
 
 
 # ----------------------------------------------------------------- Snake
@@ -293,26 +295,38 @@ def torch_decode(cfg, t, latent):
         den = (T[p + ".beta"] if cfg["act"] == "snakebeta" else T[p + ".alpha"]).reshape(1, -1, 1)
         return x + torch.sin(a * x) ** 2 / (den + 1e-9)
 
+    causal = bool(cfg.get("causal", 0))
+
+    def conv(x, wt, b, d):  # k=7: "same" padding, or (K-1)*d on the left
+        if causal:
+            return F.conv1d(F.pad(x, (6 * d, 0)), wt, b, dilation=d)
+        return F.conv1d(x, wt, b, padding=3 * d, dilation=d)
+
     x = torch.from_numpy(latent.astype(np.float64))
     if cfg.get("in_proj", 0):
         x = F.conv1d(x, T["dec_in_proj.weight"], T["dec_in_proj.bias"])  # plain weight
-    h = F.conv1d(x, w("conv_in"), T["conv_in.bias"], padding=3)
+    h = conv(x, w("conv_in"), T["conv_in.bias"], 1)
     for b, s in enumerate(cfg["strides"]):
-        h = F.conv_transpose1d(sn(h, f"blocks.{b}.snake1"), w(f"blocks.{b}.conv_t1"),
-                               T[f"blocks.{b}.conv_t1.bias"], stride=s, padding=(s + 1) // 2,
-                               output_padding=s % 2)
+        t_in = h.shape[-1]
+        if causal:  # full transposed conv, the K - s tail on the right dropped
+            h = F.conv_transpose1d(sn(h, f"blocks.{b}.snake1"), w(f"blocks.{b}.conv_t1"),
+                                   T[f"blocks.{b}.conv_t1.bias"], stride=s)[..., :t_in * s]
+        else:
+            h = F.conv_transpose1d(sn(h, f"blocks.{b}.snake1"), w(f"blocks.{b}.conv_t1"),
+                                   T[f"blocks.{b}.conv_t1.bias"], stride=s, padding=(s + 1) // 2,
+                                   output_padding=s % 2)
         for r, d in enumerate(cfg["dilations"]):
             p = f"blocks.{b}.res_units.{r}"
-            u = F.conv1d(sn(h, p + ".snake1"), w(p + ".conv1"), T[p + ".conv1.bias"],
-                         padding=3 * d, dilation=d)
+            u = conv(sn(h, p + ".snake1"), w(p + ".conv1"), T[p + ".conv1.bias"], d)
             h = h + F.conv1d(sn(u, p + ".snake2"), w(p + ".conv2"), T[p + ".conv2.bias"])
-    return torch.tanh(F.conv1d(sn(h, "snake_out"), w("conv_out"), T["conv_out.bias"], padding=3)).numpy()
+    return torch.tanh(conv(sn(h, "snake_out"), w("conv_out"), T["conv_out.bias"], 1)).numpy()
 
 
-@pytest.mark.parametrize("strides,act,in_proj", [((2, 2), "snake", 0), ((3, 2), "snakebeta", 0),
-                                                 ((5, 3), "snake", 0), ((2, 2), "snake", 5)])
-def test_decode_matches_torch_composition(orc, strides, act, in_proj):
-    cfg = tiny_cfg(strides=strides, act=act, in_proj=in_proj)
+@pytest.mark.parametrize("strides,act,in_proj,causal", [
+    ((2, 2), "snake", 0, 0), ((3, 2), "snakebeta", 0, 0), ((5, 3), "snake", 0, 0),
+    ((2, 2), "snake", 5, 0), ((3, 2), "snakebeta", 0, 1), ((8, 5), "snake", 0, 1)])
+def test_decode_matches_torch_composition(orc, strides, act, in_proj, causal):
+    cfg = tiny_cfg(strides=strides, act=act, in_proj=in_proj, causal=causal)
     t = I.make_weights(cfg, twin=True)
     lat = I.make_latent(cfg)
     y = orc.Model(cfg, t).decode(lat)
@@ -493,3 +507,57 @@ def test_windows_planar_sides_and_single_window(orc):
     one = m.decode_windows(win[:1], 11, 2, 3)                # one window: no crops
     np.testing.assert_array_equal(one, np.clip(m.decode(win[0].reshape(2, 3, 11))[:, 0], -1, 1))
     assert y.shape == (2, (11 - 3 + 9 - 2) * cfg["hop"])
+
+
+# ----------------------------------------------------------------- causal
+@pytest.mark.parametrize("d", [1, 3, 9])
+def test_causal_conv1d_brute_force_and_torch(orc, d):
+    x = RNG.normal(0, 1, (2, 3, 23))
+    w = RNG.normal(0, 1, (4, 3, 7))
+    b = RNG.normal(0, 1, 4)
+    y = orc.conv1d(x, w, b, d, causal=True)
+    ref = np.zeros_like(y)
+    for r in range(2):
+        for o in range(4):
+            for t in range(23):
+                acc = b[o]
+                for i in range(3):
+                    for j in range(7):
+                        src = t + j * d - 6 * d          # only the past and the present
+                        if 0 <= src < 23:
+                            acc += w[o, i, j] * x[r, i, src]
+                ref[r, o, t] = acc
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+    F = torch.nn.functional
+    tt = F.conv1d(F.pad(torch.from_numpy(x), (6 * d, 0)), torch.from_numpy(w), torch.from_numpy(b),
+                  dilation=d).numpy()
+    np.testing.assert_allclose(y, tt, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("s", [2, 3, 4, 5, 8])
+def test_causal_convt_keeps_the_head_of_the_full_output(orc, s):
+    x = RNG.normal(0, 1, (2, 3, 9))
+    w = RNG.normal(0, 1, (3, 4, 2 * s))
+    b = RNG.normal(0, 1, 4)
+    y = orc.conv_transpose1d(x, w, b, s, pad_left=orc.convt_crop(s, causal=True))
+    full = torch.nn.functional.conv_transpose1d(torch.from_numpy(x), torch.from_numpy(w),
+                                                torch.from_numpy(b), stride=s).numpy()
+    assert y.shape[-1] == 9 * s and full.shape[-1] == 9 * s + s   # the K - s tail
+    np.testing.assert_allclose(y, full[..., :9 * s], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("strides", [(2, 2), (8, 5)])
+def test_causal_decode_of_a_prefix_is_a_prefix(orc, strides):
+    """Causal stack: decoding the first t frames gives exactly the first t*hop
+    samples of the whole decode (what makes frame-by-frame streaming equal
+    the offline decode); the "same"-padded stack does not have this property."""
+    cfg = tiny_cfg(strides=strides, causal=1)
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg, batch=2, frames=13)
+    m = orc.Model(cfg, t)
+    full = m.decode(lat)
+    hop = cfg["hop"]
+    for n in (1, 2, 5, 12):
+        np.testing.assert_array_equal(m.decode(lat[:, :, :n]), full[:, :, :n * hop])
+    mc = orc.Model(tiny_cfg(strides=strides), t)
+    assert np.abs(mc.decode(lat[:, :, :5]) - mc.decode(lat)[:, :, :5 * hop]).max() > 1e-6
