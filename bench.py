@@ -5,7 +5,9 @@ One step = one full decode (conv_in, 4 upsampling blocks with 3 residual
 units each, head) of one batch of synthetic latents, with the latent, the
 weights and the output buffer already resident in HBM.  For the windowed
 workload one step is one vocoder_decode_windows call: every window of the
-song decoded as one batch and stitched into planar output.
+song decoded as one batch and stitched into planar output.  For the
+streaming workload one step is one pass of every stream through the clip:
+a reset, then the clip's latent frames in fixed-size chunks.
 
 Prints ONE JSON line: audio-seconds decoded per second (value), whole-decode
 TFLOP/s, the roofline of the dominant kernel measured live with HIP events
@@ -22,6 +24,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -52,6 +56,8 @@ def workload_name(cfg: dict) -> str:
     s = ",".join(str(x) for x in cfg["strides"])
     tile = f", time tiles of {cfg['tile_frames']} frames" if cfg["tile_frames"] else ""
     proj = f"dec_in_proj {cfg['latent_channels']}->{cfg['in_proj']}, " if cfg.get("in_proj") else ""
+    if cfg.get("chunk"):
+        lat += f" streamed in chunks of {cfg['chunk']} frames, causal"
     if cfg.get("windows"):
         lat = (f"{cfg['windows']} windows [{cfg['batch']},{cfg['latent_channels']},{cfg['frames']}] "
                f"(last {cfg['last_frames']} frames), crops {cfg['crop'][0]}/{cfg['crop'][1]}, stitched")
@@ -145,6 +151,23 @@ def main() -> int:
 
         def step():
             V.check(V.vocoder_decode_windows(ctx, latent, n, sides, L, last, cl, cr, pcm, stream), ctx)
+    elif cfg.get("chunk"):
+        latent_np = I.make_latent(cfg)
+        B, _, T = latent_np.shape
+        ck = cfg["chunk"]
+        assert T % ck == 0
+        chunks = [torch.from_numpy(np.ascontiguousarray(latent_np[:, :, k:k + ck])).to(dev)
+                  for k in range(0, T, ck)]
+        outs = [torch.empty(B, 1, V.vocoder_output_length(ctx, ck), device=dev) for _ in chunks]
+        pcm = outs[-1]
+        secs = I.audio_seconds(cfg, B, T)
+        flops = I.algorithmic_flops(cfg, B, T)   # the clip's own work (context re-decodes excluded)
+        kept_frac = 1.0
+
+        def step():
+            V.check(V.vocoder_stream_reset(ctx, B), ctx)
+            for x, y in zip(chunks, outs):
+                V.check(V.vocoder_stream_decode(ctx, x, ck, y, stream), ctx)
     else:
         latent_np = I.make_latent(cfg)
         latent = torch.from_numpy(latent_np).to(dev)

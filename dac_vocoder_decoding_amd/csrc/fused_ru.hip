@@ -86,7 +86,7 @@ void res_unit_kernel(const ResUnitArgs a) {
 
   const int d = a.dil;
   const int xrows = BN + 6 * d;
-  const int tfirst = n0 - 3 * d;
+  const int tfirst = n0 - a.pad;  // tap j reads frame n + j*d - pad
   const unsigned char* xrow = static_cast<const unsigned char*>(a.x) +
                               static_cast<int64_t>(row) * C * a.T * ES;
   const int64_t xplane = static_cast<int64_t>(a.T) * kChunkBytes;

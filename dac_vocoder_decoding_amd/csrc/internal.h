@@ -114,6 +114,7 @@ struct ResUnitArgs {
   const float* s_h;
   const float* hs_scale;  // if set, h receives Snake(h) (the head's Snake)
   const float* hs_h;
+  int pad;               // conv1 left padding: 3*dil ("same") or 6*dil (causal)
   int n_tiles, rows;
 };
 // Frames per workgroup of the fused kernel for width C, or 0 if there is no
@@ -171,6 +172,7 @@ struct HeadArgs {
   RowInfo rows;
   int nrows;
   int rate;         // frames per latent frame
+  int pad;          // left padding of the k=7 conv: 3 ("same") or 6 (causal)
   const float* w;   // [7][C]
   float bias;
   float* pcm;
@@ -178,5 +180,16 @@ struct HeadArgs {
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+
+// Streaming: build one chunk's decode input from a stream's history and
+// roll the history forward (fp32 [rows][C][*] layouts).
+struct StreamPrepArgs {
+  const float* hist_old;  // [rows][C][H]: the last `avail` frames right-aligned
+  float* hist_new;        // [rows][C][H]: receives the last `keep` frames of cat
+  const float* chunk;     // [rows][C][t]
+  float* cat;             // [rows][C][avail + t]
+  int64_t rows, C, H, avail, t, keep;
+};
+hipError_t launch_stream_prep(const StreamPrepArgs& a, hipStream_t s);
 
 }  // namespace voc

@@ -64,7 +64,7 @@ struct voc_ctx {
   int device = 0;
   int op = OP_F32;
   int64_t hop = 1;
-  int halo = 0;
+  int halo_l = 0, halo_r = 0;  // receptive-field halos in latent frames (left, right)
   std::string err;
   bool loaded = false;
   Weights W;
@@ -84,6 +84,13 @@ struct voc_ctx {
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
+  // streaming (causal configurations)
+  int64_t st_rows = 0;          // streams since the last reset (0: none)
+  int64_t st_avail = 0;         // history frames held per stream (<= halo_l)
+  int st_par = 0;               // which history buffer holds the current history
+  float* st_hist[2] = {nullptr, nullptr};  // [st_rows][C][halo_l] each
+  float* st_cat = nullptr;      // [st_rows][C][st_avail + t] decode input
+  size_t st_hist_bytes = 0, st_cat_bytes = 0;
   std::vector<int64_t> meta_dst;  // host copies kept alive for async uploads
   std::vector<int> meta_int;
 };
@@ -124,6 +131,7 @@ voc_status validate(const voc_config* c, std::string* why) {
     return bad("latent_channels must be a positive multiple of 16 (F32) / 32 (BF16), at most 8192");
   if (c->in_proj < 0 || c->in_proj % q || c->in_proj > 8192)
     return bad("in_proj must be 0 or a positive multiple of 16 (F32) / 32 (BF16), at most 8192");
+  if (c->causal != 0 && c->causal != 1) return bad("causal must be 0 or 1");
   for (int b = 0; b <= c->n_blocks; ++b)
     if (c->width[b] <= 0 || c->width[b] % q || c->width[b] > 8192)
       return bad("widths must be positive multiples of 16 (F32) / 32 (BF16), at most 8192");
@@ -141,41 +149,55 @@ voc_status validate(const voc_config* c, std::string* why) {
 
 int64_t floordiv(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
-// Smallest H such that, for every output sample of latent frame F, the
-// dependency interval at the input of every layer lies inside the frames the
-// tile [F - H, F + 1 + H) holds at that layer's rate.  Intervals are
-// propagated backwards: k=7 conv at dilation d widens by 3d each side;
-// ConvTranspose1d (stride s, k = 2s, crop p) maps outputs [lo, hi] to inputs
-// [ceil((lo + p - 2s + 1)/s), floor((hi + p)/s)].
-int compute_halo(const voc_config& c) {
+// Smallest halos (H_left, H_right) such that, for every output sample of
+// latent frame F, the dependency interval at the input of every layer lies
+// inside the frames the tile [F - H_left, F + 1 + H_right) holds at that
+// layer's rate.  Intervals are propagated backwards: a k=7 conv at dilation d
+// widens them by 3d each side ("same"), or by 6d on the left only (causal);
+// ConvTranspose1d (stride s, k = 2s, left crop p = ceil(s/2), or 0 when
+// causal) maps outputs [lo, hi] to inputs [ceil((lo + p - 2s + 1)/s),
+// floor((hi + p)/s)].  The two ends propagate independently.
+void compute_halos(const voc_config& c, int* h_left, int* h_right) {
   const int64_t hop = total_stride(c);
   const int64_t F = 4096;
+  const bool causal = c.causal != 0;
+  const int64_t kl = causal ? 6 : 3, kr = causal ? 0 : 3;  // k=7 conv reach per unit dilation
   std::vector<int64_t> rate(c.n_blocks + 1);
   rate[0] = 1;
   for (int b = 0; b < c.n_blocks; ++b) rate[b + 1] = rate[b] * c.stride[b];
-  for (int H = 0; H < 4096; ++H) {
-    bool ok = true;
-    for (int64_t ph = 0; ph < hop && ok; ++ph) {
+  *h_left = *h_right = -1;
+  for (int H = 0; H < 4096 && (*h_left < 0 || *h_right < 0); ++H) {
+    bool ok_l = true, ok_r = true;
+    for (int64_t ph = 0; ph < hop; ++ph) {
       int64_t lo = F * hop + ph, hi = lo;
-      auto inside = [&](int64_t R) { return lo >= (F - H) * R && hi < (F + 1 + H) * R; };
-      lo -= 3, hi += 3;  // head conv k=7
-      ok = ok && inside(rate[c.n_blocks]);
-      for (int b = c.n_blocks - 1; b >= 0 && ok; --b) {
-        for (int r = c.n_res - 1; r >= 0 && ok; --r) {
-          lo -= 3 * c.dilation[r], hi += 3 * c.dilation[r];
-          ok = inside(rate[b + 1]);
+      auto check = [&](int64_t R) {
+        ok_l = ok_l && lo >= (F - H) * R;
+        ok_r = ok_r && hi < (F + 1 + H) * R;
+      };
+      lo -= kl, hi += kr;  // head conv k=7
+      check(rate[c.n_blocks]);
+      for (int b = c.n_blocks - 1; b >= 0; --b) {
+        for (int r = c.n_res - 1; r >= 0; --r) {
+          lo -= kl * c.dilation[r], hi += kr * c.dilation[r];
+          check(rate[b + 1]);
         }
-        const int64_t s = c.stride[b], p = (s + 1) / 2;
+        const int64_t s = c.stride[b], p = causal ? 0 : (s + 1) / 2;
         lo = -floordiv(-(lo + p - 2 * s + 1), s);
         hi = floordiv(hi + p, s);
-        ok = ok && inside(rate[b]);
+        check(rate[b]);
       }
-      lo -= 3, hi += 3;  // conv_in
-      ok = ok && inside(1);
+      lo -= kl, hi += kr;  // conv_in
+      check(1);
     }
-    if (ok) return H;
+    if (ok_l && *h_left < 0) *h_left = H;
+    if (ok_r && *h_right < 0) *h_right = H;
   }
-  return -1;
+}
+
+int compute_halo(const voc_config& c) {
+  int hl, hr;
+  compute_halos(c, &hl, &hr);
+  return hl < 0 || hr < 0 ? -1 : std::max(hl, hr);
 }
 
 // ------------------------------------------------------------- profiling
@@ -404,13 +426,13 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
     a.offstep = -1;
     a.min_off = -1;
     a.halo = 1;
-    a.N = io.T_in + 1;
-  } else {
-    const int P = (L.taps - 1) / 2 * L.dil;
+    a.N = io.T_in + (L.crop > 0 ? 1 : 0);  // a left crop shifts the last outputs to n = T_in
+  } else {  // taps at x[n + j*dil - P]: "same" P = (taps-1)/2*dil, causal P = (taps-1)*dil
+    const int P = (c->cfg.causal ? L.taps - 1 : (L.taps - 1) / 2) * L.dil;
     a.off0 = -P;
     a.offstep = L.dil;
     a.min_off = -P;
-    a.halo = 2 * P;
+    a.halo = (L.taps - 1) * L.dil;
     a.N = io.T_in;
   }
   a.T_out = io.T_in * L.ups;
@@ -482,6 +504,7 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
   a.rows = rows;
   a.nrows = nrows;
   a.rate = rate;
+  a.pad = c->cfg.causal ? 6 : 3;
   a.w = c->W.head_w;
   a.bias = c->W.head_bias;
   a.pcm = pcm;
@@ -532,6 +555,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     a.row_len = row_len;
     a.rate = rate;
     a.dil = u.c1.dil;
+    a.pad = (c->cfg.causal ? 6 : 3) * u.c1.dil;
     a.w1 = u.c1.w;
     a.b1 = u.c1.bias;
     a.a2_scale = u.a2.alpha;
@@ -774,7 +798,7 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   c->device = hip_device;
   c->op = cfg->dtype == VOC_F32 ? OP_F32 : OP_BF16;
   c->hop = total_stride(*cfg);
-  c->halo = compute_halo(*cfg);
+  compute_halos(*cfg, &c->halo_l, &c->halo_r);
   if (const char* cap = std::getenv("VOC_MAX_WORKSPACE_BYTES")) c->ws_cap = std::strtoull(cap, nullptr, 10);
   // Ablation only: VOC_VARIANT_{CONV_IN,CONVT,RES_K7,RES_K1}=<tile family index>.
   const char* names[4] = {"VOC_VARIANT_CONV_IN", "VOC_VARIANT_CONVT", "VOC_VARIANT_RES_K7",
@@ -930,7 +954,7 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
       blk.ct.cout = cout;
       blk.ct.taps = 2;
       blk.ct.ups = s;
-      blk.ct.crop = (s + 1) / 2;
+      blk.ct.crop = g.causal ? 0 : (s + 1) / 2;  // causal: keep full[0, T*s)
       blk.ct.M = s * cout;
       st = fold(p + ".conv_t1", PACK_CONVT, cin, cout, 2 * s, s, &blk.ct.w, &blk.ct.bias);
       if (st) return st;
@@ -1057,15 +1081,16 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
   const int64_t ntile = (T + F - 1) / F;
   const int64_t rows = B * ntile;
   if (rows > 65535) return fail(c, VOC_INVALID_PARAMS, "too many rows (B * tiles > 65535)");
-  const int H = g.tile_frames > 0 ? c->halo : 0;
-  const int T_alloc = static_cast<int>(std::min<int64_t>(T, F + 2 * H));
+  const int HL = g.tile_frames > 0 ? c->halo_l : 0;
+  const int HR = g.tile_frames > 0 ? c->halo_r : 0;
+  const int T_alloc = static_cast<int>(std::min<int64_t>(T, F + HL + HR));
   std::vector<int64_t> dst(rows);
   std::vector<int> ints(5 * rows);
   for (int64_t b = 0; b < B; ++b)
     for (int64_t k = 0; k < ntile; ++k) {
       const int64_t r = b * ntile + k;
       const int64_t t0 = k * F, t1 = std::min(T, t0 + F);
-      const int64_t a = std::max<int64_t>(0, t0 - H), e = std::min(T, t1 + H);
+      const int64_t a = std::max<int64_t>(0, t0 - HL), e = std::min(T, t1 + HR);
       ints[r] = static_cast<int>(e - a);                          // len
       ints[rows + r] = static_cast<int>(b);                       // src_b
       ints[2 * rows + r] = static_cast<int>(a);                   // start
@@ -1075,6 +1100,97 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
     }
   return decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {0, B, T, rows}, pcm,
                      static_cast<hipStream_t>(stream));
+}
+
+namespace {
+// Device buffer of at least `bytes` (contents not kept when it grows).
+voc_status grow(voc_ctx* c, float** p, size_t* cap, size_t bytes, const char* what) {
+  if (bytes <= *cap) return VOC_OK;
+  if (*p) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(*p);
+    *p = nullptr;
+    *cap = 0;
+  }
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(p), bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return hip_fail(c, e, what);
+  }
+  *cap = bytes;
+  return VOC_OK;
+}
+}  // namespace
+
+VOC_API voc_status vocoder_stream_reset(voc_ctx* c, int64_t rows) {
+  if (!c) return VOC_INVALID_PARAMS;
+  if (!c->cfg.causal) return fail(c, VOC_INVALID_PARAMS, "streaming needs a causal configuration");
+  if (c->cfg.tile_frames != 0) return fail(c, VOC_INVALID_PARAMS, "streaming needs tile_frames == 0");
+  if (rows <= 0 || rows > 65535) return fail(c, VOC_INVALID_PARAMS, "rows must be in [1, 65535]");
+  const size_t bytes = static_cast<size_t>(rows) * c->cfg.latent_channels * std::max(c->halo_l, 1) * 4;
+  for (int k = 0; k < 2; ++k) {
+    size_t cap = c->st_hist[k] ? c->st_hist_bytes : 0;
+    voc_status st = grow(c, &c->st_hist[k], &cap, bytes, "stream history hipMalloc");
+    if (st) {
+      c->st_rows = 0;
+      return st;
+    }
+  }
+  c->st_hist_bytes = std::max(c->st_hist_bytes, bytes);
+  c->st_rows = rows;
+  c->st_avail = 0;
+  c->st_par = 0;
+  return VOC_OK;
+}
+
+VOC_API voc_status vocoder_stream_decode(voc_ctx* c, const float* latent, int64_t t, float* pcm,
+                                         void* stream) {
+  if (!c) return VOC_INVALID_PARAMS;
+  if (c->st_rows <= 0) return fail(c, VOC_INVALID_PARAMS, "vocoder_stream_reset has not been called");
+  if (!latent || !pcm) return fail(c, VOC_INVALID_PARAMS, "NULL latent or pcm");
+  if ((reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(pcm)) & 15)
+    return fail(c, VOC_INVALID_PARAMS, "latent and pcm must be 16-byte aligned");
+  const int64_t H = c->halo_l;
+  if (t <= 0 || (H + t) * c->hop > (int64_t(1) << 31) - 1)
+    return fail(c, VOC_INVALID_PARAMS, "t must be positive with (halo + t) * hop below 2^31");
+  if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rows = c->st_rows, C = c->cfg.latent_channels;
+  const int64_t avail = c->st_avail, Lw = avail + t, keep = std::min(H, Lw);
+  voc_status st = grow(c, &c->st_cat, &c->st_cat_bytes, static_cast<size_t>(rows) * C * Lw * 4,
+                       "stream staging hipMalloc");
+  if (st) return st;
+  StreamPrepArgs pa{};
+  pa.hist_old = c->st_hist[c->st_par];
+  pa.hist_new = c->st_hist[c->st_par ^ 1];
+  pa.chunk = latent;
+  pa.cat = c->st_cat;
+  pa.rows = rows;
+  pa.C = C;
+  pa.H = std::max<int64_t>(H, 1);
+  pa.avail = avail;
+  pa.t = t;
+  pa.keep = keep;
+  st = launch(c, s, VOC_K_IMPORT, 0.0, 4.0 * rows * C * (avail + 2 * t + keep), "stream launch",
+              [&] { return launch_stream_prep(pa, s); });
+  if (st) return st;
+  // Row r decodes its history and the chunk, keeping the chunk's samples.
+  std::vector<int64_t> dst(rows);
+  std::vector<int> ints(5 * rows);
+  for (int64_t r = 0; r < rows; ++r) {
+    ints[r] = static_cast<int>(Lw);                         // len
+    ints[rows + r] = static_cast<int>(r);                   // src_b
+    ints[2 * rows + r] = 0;                                 // start
+    ints[3 * rows + r] = static_cast<int>(avail * c->hop);  // keep_lo
+    ints[4 * rows + r] = static_cast<int>(Lw * c->hop);     // keep_hi
+    dst[r] = r * t * c->hop;
+  }
+  st = decode_rows(c, c->st_cat, Lw, rows, static_cast<int>(Lw), std::move(dst), std::move(ints),
+                   {2, rows, Lw, avail}, pcm, s);
+  if (st) return st;
+  c->st_par ^= 1;
+  c->st_avail = keep;
+  return VOC_OK;
 }
 
 VOC_API int64_t vocoder_windows_output_length(const voc_ctx* c, int64_t n, int64_t L, int64_t L_last,
@@ -1139,6 +1255,8 @@ VOC_API void vocoder_destroy(voc_ctx* c) {
   (void)hipDeviceSynchronize();
   free_weights(c->W);
   if (c->ws) (void)hipFree(c->ws);
+  for (float* p : {c->st_hist[0], c->st_hist[1], c->st_cat})
+    if (p) (void)hipFree(p);
   for (auto& r : c->pending) {
     (void)hipEventDestroy(r.e0);
     (void)hipEventDestroy(r.e1);

@@ -9,6 +9,8 @@
 #include "internal.h"
 #include "device_math.h"
 
+#include <algorithm>
+
 namespace voc {
 
 // ---------------------------------------------------------------- fold
@@ -168,16 +170,48 @@ hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipSt
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- stream history
+// One chunk of a stream: cat[r][c] = (the last `avail` frames of hist_old[r][c],
+// then the t frames of chunk[r][c]), and hist_new[r][c] receives the last
+// `keep` frames of that concatenation, right-aligned in its H frames.  The
+// two history buffers alternate between chunks, so no element is read and
+// written by the same launch.
+__global__ __launch_bounds__(256) void stream_prep_kernel(const StreamPrepArgs a) {
+  const int64_t Lw = a.avail + a.t;
+  const int64_t per = Lw + a.keep;  // cat elements, then history elements, per (r, c)
+  const int64_t total = a.rows * a.C * per;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t rc = i / per, j = i - rc * per;
+    // Position in the concatenation that this element reads.
+    const int64_t q = j < Lw ? j : Lw - a.keep + (j - Lw);
+    const float v = q < a.avail ? a.hist_old[rc * a.H + a.H - a.avail + q] : a.chunk[rc * a.t + (q - a.avail)];
+    if (j < Lw)
+      a.cat[rc * Lw + j] = v;
+    else
+      a.hist_new[rc * a.H + a.H - a.keep + (j - Lw)] = v;
+  }
+}
+
+hipError_t launch_stream_prep(const StreamPrepArgs& a, hipStream_t s) {
+  const int64_t total = a.rows * a.C * (a.avail + a.t + a.keep);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 2048);
+  hipLaunchKernelGGL(stream_prep_kernel, dim3(static_cast<unsigned>(std::max<int64_t>(blocks, 1))), dim3(256), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- head
 // Output head (minimaxmusic.cpp ARCHITECTURE, "Flow VAE": snake_out, conv_out
 // k=7 with bias, tanh).  Its input already holds Snake_out(h) (the last
 // residual unit's epilogue applies it), so the head is a pure stream:
-//   lane l of a wave reads frame f = o0 - 3 + l (all C channels, 64-byte
+//   lane l of a wave reads frame f = o0 - P + l (all C channels, 64-byte
 //   chunk rows) and forms the seven per-tap projections
 //   z_j[f] = sum_i w[j][i] x[f][i];
-//   lane l (3 <= l < 61) then owns output o = f and gathers
-//   y[o] = tanh(bias + sum_j z_j[o + j - 3]) from lanes l + j - 3 with
-//   cross-lane shuffles.
+//   lane l (P <= l < P + 58) then owns output o = f and gathers
+//   y[o] = tanh(bias + sum_j z_j[o + j - P]) from lanes l + j - P with
+//   cross-lane shuffles.  P = 3 for the "same" conv, 6 for the causal one
+//   (qwentts.cpp ARCHITECTURE, "Streaming decode": every module causal).
 // Each wave emits 58 outputs per 64 frames read; no LDS tile, no barriers.
 // Frames outside the row's valid range read as zero (the conv's zero
 // padding; Snake(0) = 0).  The tile crop of time-tiled decoding is folded
@@ -193,7 +227,8 @@ __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   if (o0 >= hi) return;
   const int C = a.C;
   const int Lr = min(a.rows.len[r] * a.rate, a.T);
-  const int f = o0 - 3 + lane;
+  const int P = a.pad;  // 3, or 6 for the causal head
+  const int f = o0 - P + lane;
   const bool valid = f >= 0 && f < Lr;
   const float* hp = a.h + static_cast<int64_t>(r) * C * a.T + static_cast<int64_t>(f) * kHChunk;
   const int64_t plane = static_cast<int64_t>(a.T) * kHChunk;
@@ -219,11 +254,11 @@ __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   float y = a.bias;
 #pragma unroll
   for (int j = 0; j < 7; ++j) {
-    const int src = min(max(lane + j - 3, 0), 63);
+    const int src = min(max(lane + j - P, 0), 63);
     y += __shfl(z[j], src);
   }
   const int o = f;
-  if (lane >= 3 && lane < 3 + kHeadOut && o < hi) a.pcm[a.rows.dst[r] - lo + o] = tanhf(y);
+  if (lane >= P && lane < P + kHeadOut && o < hi) a.pcm[a.rows.dst[r] - lo + o] = tanhf(y);
 }
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {

@@ -125,6 +125,14 @@ CONFIGS = {
     6: _cfg(name="dav_song_windows_f32", batch=2, frames=689, in_proj=1024,
             widths=(1536, 768, 384, 192, 96), strides=(8, 8, 4, 2), seed=1006,
             windows=14, last_frames=683, crop=(86, 258)),
+    # The causal DAC stage of the Qwen3-TTS codec decoder (qwentts.cpp
+    # ARCHITECTURE, "Audio tokenizer decoder": conv_pre 1024 -> 1536, strides
+    # 8/5/4/3, widths 1536 ... 96, SnakeBeta, CausalTransConv) streamed as
+    # its stateful path does ("Streaming decode"): 32 mono streams of 250
+    # frames (5 s at 24 kHz) arriving in chunks of 25 frames.
+    7: _cfg(name="causal_codec_stream_bf16", latent_channels=1024, batch=32, frames=250,
+            dtype="bf16", sample_rate=24000, stereo=False, act="snakebeta", causal=1,
+            widths=(1536, 768, 384, 192, 96), strides=(8, 5, 4, 3), seed=1007, chunk=25),
 }
 
 

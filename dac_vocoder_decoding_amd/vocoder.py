@@ -53,6 +53,7 @@ class voc_config(ctypes.Structure):
         ("convt_crop", ctypes.c_int),
         ("tile_frames", ctypes.c_int),
         ("in_proj", ctypes.c_int),
+        ("causal", ctypes.c_int),
     ]
 
 
@@ -98,6 +99,8 @@ def lib():
             "vocoder_decode": (I, [P, P, I64, I64, P, P]),
             "vocoder_decode_windows": (I, [P, P, I64, I64, I64, I64, I64, I64, P, P]),
             "vocoder_windows_output_length": (I64, [P, I64, I64, I64, I64, I64]),
+            "vocoder_stream_reset": (I, [P, I64]),
+            "vocoder_stream_decode": (I, [P, P, I64, P, P]),
             "vocoder_last_error": (ctypes.c_char_p, [P]),
             "vocoder_destroy": (None, [P]),
             "vocoder_profile_enable": (I, [P, I]),
@@ -161,6 +164,7 @@ def config_from_dict(d: dict) -> voc_config:
     c.snake_log_params = d.get("snake_log_params", 0)
     c.tile_frames = d.get("tile_frames", 0)
     c.in_proj = d.get("in_proj", 0)
+    c.causal = int(d.get("causal", 0))
     return c
 
 
@@ -225,6 +229,14 @@ def vocoder_decode_windows(ctx, latents, n: int, sides: int, L: int, L_last: int
 def vocoder_windows_output_length(ctx, n: int, L: int, L_last: int, crop_left: int,
                                   crop_right: int) -> int:
     return lib().vocoder_windows_output_length(ctx, n, L, L_last, crop_left, crop_right)
+
+
+def vocoder_stream_reset(ctx, rows: int) -> int:
+    return lib().vocoder_stream_reset(ctx, rows)
+
+
+def vocoder_stream_decode(ctx, latent, t: int, pcm, stream=None) -> int:
+    return lib().vocoder_stream_decode(ctx, _ptr(latent), t, _ptr(pcm), _stream(stream))
 
 
 def vocoder_last_error(ctx) -> str:
@@ -318,6 +330,17 @@ def decode_windows(ctx, windows, sides: int, last_frames: int, crop_left: int, c
     pcm = torch.empty(sides, N, device=windows.device)
     check(vocoder_decode_windows(ctx, windows, n, sides, L, last_frames, crop_left, crop_right,
                                  pcm, stream), ctx)
+    return pcm
+
+
+def stream_decode(ctx, latent, stream=None):
+    """pcm [rows, 1, t*hop] (new CUDA tensor) for the next chunk [rows, C, t]
+    of the streams started by vocoder_stream_reset."""
+    import torch
+    assert latent.is_cuda and latent.dtype == torch.float32 and latent.is_contiguous()
+    rows, _, t = latent.shape
+    pcm = torch.empty(rows, 1, vocoder_output_length(ctx, t), device=latent.device)
+    check(vocoder_stream_decode(ctx, latent, t, pcm, stream), ctx)
     return pcm
 
 

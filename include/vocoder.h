@@ -12,6 +12,9 @@
  *   h   = conv_in(x)                            Conv1d k=7, zero "same" padding, bias
  *   per block b with stride s:
  *     h = conv_t1(Snake(h))                     ConvTranspose1d k=2s, stride s, crop ceil(s/2)
+ *   (causal configurations: every k=7 conv pads (K-1)*d on the left only and
+ *    the ConvTranspose1d keeps full[0, T*s), qwentts.cpp ARCHITECTURE, "Audio
+ *    tokenizer decoder" and "Streaming decode (stateful path)")
  *     per residual unit with dilation d (1, 3, 9):
  *       h = h + conv2(Snake2(conv1_d(Snake1(h))))   conv1 k=7 dilation d, conv2 k=1
  *   pcm = tanh(conv_out(Snake(h)))              Conv1d k=7 to one channel, bias
@@ -77,7 +80,8 @@ typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
  * 1 <= n_res <= VOC_MAX_RES; 1 <= dilation[r] <= 9; stride[b] >= 1;
  * in_kernel == res_kernel == out_kernel == 7; widths, latent_channels and a
  * non-zero in_proj positive multiples of 16 (F32) or 32 (BF16), at most 8192,
- * width[n_blocks] <= 512; convt_crop == 0; tile_frames >= 0; in_proj >= 0.
+ * width[n_blocks] <= 512; convt_crop == 0; tile_frames >= 0; in_proj >= 0;
+ * causal is 0 or 1.
  */
 typedef struct voc_config {
   int abi_version;
@@ -103,6 +107,9 @@ typedef struct voc_config {
                                    /* has P input channels): the DAV decoder    */
                                    /* of minimaxmusic.cpp ARCHITECTURE, "Flow   */
                                    /* VAE" (64 -> 1024, conv_in 1024 -> 1536)   */
+  int causal;                      /* 0: "same" padding and centered crop; 1:   */
+                                   /* causal k=7 convs (left pad (K-1)*d) and   */
+                                   /* ConvTranspose1d keeping full[0, T*s)      */
 } voc_config;
 
 /* Fill *cfg with the full-width stereo window decoder: latent 64, widths
@@ -118,7 +125,8 @@ int64_t voc_config_hop(const voc_config *cfg);
 
 /* Exact receptive-field halo H in latent frames (host-only): decoding latent
  * frames [t0-H, t1+H) (clamped to the clip) reproduces the untiled output on
- * samples [t0*hop, t1*hop).  Negative status if *cfg is invalid. */
+ * samples [t0*hop, t1*hop).  For causal configurations H is the left halo
+ * and no frames to the right are needed.  Negative status if *cfg is invalid. */
 int voc_config_halo(const voc_config *cfg);
 
 /* Create a context on HIP device hip_device.  Validates *cfg first (no device
@@ -204,6 +212,30 @@ voc_status vocoder_decode_windows(voc_ctx *ctx, const float *latents, int64_t n_
                                   int64_t sides, int64_t L, int64_t L_last,
                                   int64_t crop_left, int64_t crop_right, float *pcm,
                                   void *hip_stream);
+
+/*
+ * Streaming decode (causal configurations; qwentts.cpp ARCHITECTURE,
+ * "Streaming decode (stateful path)"): `rows` independent streams decoded
+ * chunk by chunk, each chunk's output equal bit for bit to the matching
+ * samples of the offline decode of everything the stream has received.
+ *
+ * vocoder_stream_reset(ctx, rows) starts `rows` streams with empty history
+ * (the next chunk decodes as the start of a clip: zero left padding).
+ * vocoder_stream_decode decodes the next t >= 1 latent frames of every
+ * stream, latent: device fp32 [rows, latent_channels, t] contiguous, into
+ * pcm: device fp32 [rows, 1, t*hop] contiguous.  The library keeps the last
+ * H latent frames of each stream (H = voc_config_halo, the causal receptive
+ * field) and decodes them ahead of the chunk, keeping only the chunk's own
+ * samples; the history is the whole stream state.  Same asynchrony and
+ * ownership as vocoder_decode (the history lives in library memory, grown
+ * with hipMalloc on first use).
+ * Errors: VOC_INVALID_PARAMS (non-causal or tiled configuration, rows or t
+ * out of range, NULL/misaligned pointers, decode before reset),
+ * VOC_NOT_LOADED, VOC_OOM, VOC_DEVICE_ERROR.
+ */
+voc_status vocoder_stream_reset(voc_ctx *ctx, int64_t rows);
+voc_status vocoder_stream_decode(voc_ctx *ctx, const float *latent, int64_t t, float *pcm,
+                                 void *hip_stream);
 
 /* Samples per side that vocoder_decode_windows writes for these arguments:
  * hop times the kept latent frames of all windows; -1 if they are invalid. */

@@ -30,6 +30,13 @@ int main(void) {
   cfg.in_proj = 24;
   EXPECT(voc_config_validate(&cfg) == VOC_INVALID_PARAMS);
   cfg.in_proj = 0;
+  EXPECT(cfg.causal == 0);
+  cfg.causal = 1;
+  EXPECT(voc_config_validate(&cfg) == VOC_OK);
+  EXPECT(voc_config_halo(&cfg) > 10);
+  cfg.causal = 2;
+  EXPECT(voc_config_validate(&cfg) == VOC_INVALID_PARAMS);
+  cfg.causal = 0;
   EXPECT(voc_config_validate(NULL) == VOC_INVALID_PARAMS);
   cfg.abi_version = VOC_ABI_VERSION + 1;
   EXPECT(voc_config_validate(&cfg) == VOC_INVALID_PARAMS);
@@ -43,6 +50,8 @@ int main(void) {
   EXPECT(vocoder_decode(NULL, dummy, 1, 1, dummy, NULL) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_decode_windows(NULL, dummy, 3, 2, 689, 683, 86, 258, dummy, NULL) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_windows_output_length(NULL, 3, 689, 683, 86, 258) == -1);
+  EXPECT(vocoder_stream_reset(NULL, 4) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_stream_decode(NULL, dummy, 1, dummy, NULL) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_profile_enable(NULL, 1) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_profile_reset(NULL) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_profile_read(NULL, 0, &st) == VOC_INVALID_PARAMS);

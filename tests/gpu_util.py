@@ -30,24 +30,28 @@ def to_dev(a):
 
 
 def stage_halo(cfg, k):
-    """(ups, input frames needed each side) of debug stage k."""
+    """(ups, input frames needed on the left, on the right) of debug stage k;
+    a causal stack's k=7 convs reach (K-1)*d frames left and none right."""
     nr = len(cfg["dilations"])
     n = 2 + len(cfg["strides"]) * (1 + nr)
+    c = 2 if cfg.get("causal", 0) else 1
+    r = 0 if cfg.get("causal", 0) else 1
     if k == 0 or k == n - 1:
-        return 1, 3
+        return 1, 3 * c, 3 * r
     b, j = divmod(k - 1, 1 + nr)
     if j == 0:
-        return cfg["strides"][b], 2
-    return 1, 3 * cfg["dilations"][j - 1]
+        return cfg["strides"][b], 2, 2
+    d = cfg["dilations"][j - 1]
+    return 1, 3 * d * c, 3 * d * r
 
 
 def oracle_stage_window(model, k, x_gpu, rows, a, e):
     """Oracle output of stage k for input frames [a, e) of the given rows,
     computed from the GPU's own stage input on [a - h, e + h) (clamped), so
     the kept outputs are exact.  Returns (oracle [R, C, (e-a)*ups], slice)."""
-    ups, h = stage_halo(model.cfg, k)
+    ups, hl, hr = stage_halo(model.cfg, k)
     t_in = x_gpu.shape[-1]
-    i0, i1 = max(0, a - h), min(t_in, e + h)
+    i0, i1 = max(0, a - hl), min(t_in, e + hr)
     xin = x_gpu[rows, :, i0:i1].cpu().numpy()
     y = model.run_stage(k, xin)
     lo = (a - i0) * ups

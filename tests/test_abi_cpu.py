@@ -52,12 +52,16 @@ def test_configs_validate(idx):
     assert V.voc_config_hop(cfg) == I.CONFIGS[idx]["hop"]
 
 
-@pytest.mark.parametrize("idx", [1, 4, 5])
-def test_halo_matches_oracle_brute_force(idx):
-    # The oracle's tiling pin shows H = 10 reproduces the untiled decode and
-    # H = 9 does not, for both stride stacks; the library's interval
-    # propagation must land on the same value.
-    assert V.voc_config_halo(V.config_from_dict(I.CONFIGS[idx])) == 10
+@pytest.mark.parametrize("idx,strides,halo", [(1, None, 10), (4, None, 10), (5, None, 10),
+                                              (7, None, 20), (7, (8, 8, 4, 2), 19)])
+def test_halo_matches_oracle_brute_force(idx, strides, halo):
+    # The oracle's tiling pin shows these halos reproduce the untiled decode
+    # and one frame less does not (causal stacks: the left halo); the
+    # library's interval propagation must land on the same values.
+    d = dict(I.CONFIGS[idx])
+    if strides:
+        d["strides"] = strides
+    assert V.voc_config_halo(V.config_from_dict(d)) == halo
 
 
 def _bad(**kw):
@@ -75,6 +79,7 @@ def _bad(**kw):
     dict(dtype=3), dict(convt_crop=1), dict(tile_frames=-1), dict(latent_channels=60),
     dict(width=(2, 100)), dict(width=(4, 1024)), dict(stride=(0, 0)), dict(dilation=(1, 10)),
     dict(snake_log_params=2), dict(in_proj=-16), dict(in_proj=24), dict(in_proj=8208),
+    dict(causal=2), dict(causal=-1),
 ])
 def test_invalid_configs_rejected_before_any_device_call(kw):
     c = _bad(**kw)

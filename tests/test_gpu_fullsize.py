@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 HALO = 10
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5, 7])
 def test_fullsize_stage_parity_sampled(idx):
     cfg = I.config(idx)
     t = I.make_weights(cfg)
@@ -56,7 +56,7 @@ def test_fullsize_stage_parity_sampled(idx):
         V.vocoder_destroy(ctx)
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5, 7])
 def test_fullsize_twin_decode_sampled(idx):
     cfg = I.config(idx)
     t = I.make_weights(cfg, twin=True)
@@ -69,12 +69,14 @@ def test_fullsize_twin_decode_sampled(idx):
     finally:
         V.vocoder_destroy(ctx)
     m = O.Model(cfg, t)
-    w = 2 if idx == 4 else 3
+    w = 2 if idx in (4, 7) else 3
     cases = [(0, 0, w), (B - 1, T - w, T)]
     if cfg["tile_frames"]:   # a tile seam: frames around 512
         cases.append((1, cfg["tile_frames"] - 2, cfg["tile_frames"] + 1))
+    halo_l = 2 * HALO if cfg.get("causal") else HALO      # the causal stack reaches 19-20 left
+    halo_r = 0 if cfg.get("causal") else HALO
     for r, t0, t1 in cases:
-        a, e = max(0, t0 - HALO), min(T, t1 + HALO)
+        a, e = max(0, t0 - halo_l), min(T, t1 + halo_r)
         ref = m.decode(lat[r:r + 1, :, a:e])[0, 0, (t0 - a) * hop:(t1 - a) * hop]
         got = pcm[r, 0, t0 * hop:t1 * hop].cpu().numpy()
         e_max, e_rms = rel_maxabs(got, ref), rel_rms(got, ref)
@@ -85,7 +87,7 @@ def test_fullsize_twin_decode_sampled(idx):
             assert e_rms <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5, 7])
 def test_fullsize_literal_invariants(idx):
     cfg = I.config(idx)
     t = I.make_weights(cfg)

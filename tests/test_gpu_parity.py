@@ -14,7 +14,7 @@ from gpu_util import TOL, rel_maxabs, rel_rms, to_dev
 pytestmark = pytest.mark.gpu
 
 # (config, latent frames, rows) of the short cases; full channel widths.
-SMALL = {0: (86, 2), 1: (16, 2), 2: (8, 2), 3: (16, 2), 4: (4, 2), 5: (8, 2)}
+SMALL = {0: (86, 2), 1: (16, 2), 2: (8, 2), 3: (16, 2), 4: (4, 2), 5: (8, 2), 7: (4, 2)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -63,7 +63,7 @@ def test_stage_parity_teacher_forced(idx):
         V.vocoder_destroy(ctx)
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5, 7])
 def test_twin_decode_end_to_end(idx):
     """Conditioned twin (residual conv2 g x 0.3), whole decode vs the oracle."""
     cfg = I.config(idx)
@@ -133,7 +133,7 @@ def test_decode_equals_stage_chain_bitwise():
         V.vocoder_destroy(ctx)
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5, 7])
 def test_operand_from_h_bitwise_equal(idx, monkeypatch):
     """Fused units that compute Snake1 from h while staging (h in two
     buffers, no operand tensor from the producer) give the same bits as the

@@ -372,16 +372,20 @@ def test_precision_floor_build_is_float32(orc):
 
 
 # --------------------------------------------------------------- tiling
-def _halo_case(strides, widths, frames, tile):
-    cfg = I.config(0, strides=tuple(strides), widths=tuple(widths), latent_channels=4)
+def _halo_case(strides, widths, frames, tile, causal=0):
+    cfg = I.config(0, strides=tuple(strides), widths=tuple(widths), latent_channels=4, causal=causal)
     t = I.make_weights(cfg, twin=True)
     lat = I.make_latent(cfg, batch=1, frames=frames)
     return cfg, t, lat
 
 
-@pytest.mark.parametrize("strides,halo_ok", [((8, 8, 4, 2), 10), ((8, 8, 5, 3), 10)])
-def test_tiling_exact_halo(orc, strides, halo_ok):
-    cfg, t, lat = _halo_case(strides, (8, 8, 4, 4, 4), 60, 20)
+@pytest.mark.parametrize("strides,halo_ok,causal", [((8, 8, 4, 2), 10, 0), ((8, 8, 5, 3), 10, 0),
+                                                    ((8, 5, 4, 3), 20, 1), ((8, 8, 4, 2), 19, 1)])
+def test_tiling_exact_halo(orc, strides, halo_ok, causal):
+    """Tiles decoded with halo_ok frames of context each side reproduce the
+    untiled decode and one frame less does not (for a causal stack only the
+    left context matters)."""
+    cfg, t, lat = _halo_case(strides, (8, 8, 4, 4, 4), 60, 20, causal)
     m = orc.Model(cfg, t)
     ref = m.decode(lat)
     good = m.decode_tiled(lat, 20, halo_ok)
