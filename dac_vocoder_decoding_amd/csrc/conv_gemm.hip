@@ -99,15 +99,18 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   const int lr = lane & 15, lg = lane >> 4;
 
   // Stage one chunk: block b < XB holds X rows 16b.. (frames tfirst + row;
-  // frames outside [0, Lin) read as zero); block XB + k holds weight rows
+  // frames outside [-lb, Lin) read as zero); block XB + k holds weight rows
   // 16k.. of the [TAPS][BM] tile (rows past M read the next tap's rows or
   // zeros and only feed output rows that the epilogue drops).  Block b is
   // copied by wave b % 4.
   const uint32_t smem_lds = lds_addr(smem);
-  const uint32_t xv0 = static_cast<uint32_t>((tfirst + lr) * kChunkBytes + lg * 16);
+  // Frames in [-lb, 0) are read from memory (a stream's carried context);
+  // the buffer resource then starts lb frames before frame 0.
+  const uint32_t xv0 = static_cast<uint32_t>((tfirst + a.lb + lr) * kChunkBytes + lg * 16);
   const uint32_t wv0 = static_cast<uint32_t>((m0 + lr) * kChunkBytes + lg * 16);
   auto issue = [&](int c, int stage) {
-    const i4 xs = buf_rsrc(xrow + c * xplane, static_cast<uint32_t>(Lin) * kChunkBytes);
+    const i4 xs = buf_rsrc(xrow + c * xplane - static_cast<int64_t>(a.lb) * kChunkBytes,
+                           static_cast<uint32_t>(Lin + a.lb) * kChunkBytes);
     const i4 ws = buf_rsrc(wbase + c * wplane, static_cast<uint32_t>(wplane));
     const uint32_t dst = smem_lds + stage * STAGE;
 #pragma unroll
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
         const int64_t hbase = (static_cast<int64_t>(row) * a.Cout + (o & ~15)) * a.T_out + (o & 15);
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb) {
-          const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, a.T_out - 1);
+          const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, Lout - 1);
           rres[mb][nb] = *reinterpret_cast<const f4*>(a.res + hbase + static_cast<int64_t>(n) * kHChunk);
         }
       }
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
         const int r = unit_row(idx), col = unit_col(idx);
         const int t = tfirst + r;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < xrows && t >= 0 && t < Lin)
+        if (r < xrows && t >= -a.lb && t < Lin)
           v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
         xr[u] = v;
       }

@@ -118,7 +118,7 @@ void res_unit_kernel(const ResUnitArgs a) {
     for (int nb = 0; nb < WNB; ++nb) {
       // Unconditional load (frame clamped into the row; clamped values
       // are never stored), so the prefetch is not serialised.
-      const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, a.T - 1);
+      const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, Lv - 1);
       hres[mb][nb] = *reinterpret_cast<const f4*>(a.h_in + hbase + static_cast<int64_t>(n) * kHChunk);
     }
   };
@@ -155,7 +155,7 @@ void res_unit_kernel(const ResUnitArgs a) {
       for (int u = 0; u < XU; ++u) {
         const int r = unit_row(tid + u * NTH);
         const int t = tfirst + r;
-        const bool in = r < xrows && t >= 0 && t < Lv;
+        const bool in = r < xrows && t >= -a.lb && t < Lv;
 #pragma unroll
         for (int v = 0; v < HV; ++v)
           xh[u][v] = in ? *reinterpret_cast<const f4*>(hp + static_cast<int64_t>(t) * kHChunk + 4 * v)
@@ -175,7 +175,7 @@ void res_unit_kernel(const ResUnitArgs a) {
         const int r = unit_row(idx), col = unit_col(idx);
         const int t = tfirst + r;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < xrows && t >= 0 && t < Lv)
+        if (r < xrows && t >= -a.lb && t < Lv)
           v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
         xr[u] = v;
       }
@@ -203,10 +203,10 @@ void res_unit_kernel(const ResUnitArgs a) {
       if (r >= xrows) continue;
       uint4 v;
       if constexpr (XH) {
-        // Snake1 in fp32, then the operand dtype; frames outside the row
+        // Snake1 in fp32, then the operand dtype; frames outside [-lb, Lv)
         // are the convolution's zero padding.
         const int t = tfirst + r;
-        const bool in = t >= 0 && t < Lv;
+        const bool in = t >= -a.lb && t < Lv;
         float y[4 * HV];
 #pragma unroll
         for (int q = 0; q < HV; ++q) {

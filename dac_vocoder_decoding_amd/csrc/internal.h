@@ -67,6 +67,7 @@ struct ConvArgs {
   const float* hs_scale;  // if set, h_out receives Snake(v) with these
   const float* hs_h;      // parameters instead of v (the head's Snake)
   int T_out, ups, crop;
+  int lb;         // frames in [-lb, 0) of x are read from memory (a stream's context), else zero
 };
 
 // Tile shape families of the conv GEMM kernel.
@@ -115,6 +116,7 @@ struct ResUnitArgs {
   const float* hs_scale;  // if set, h receives Snake(h) (the head's Snake)
   const float* hs_h;
   int pad;               // conv1 left padding: 3*dil ("same") or 6*dil (causal)
+  int lb;                // frames in [-lb, 0) of the input are read from memory, else zero
   int n_tiles, rows;
 };
 // Frames per workgroup of the fused kernel for width C, or 0 if there is no
@@ -149,7 +151,8 @@ struct ImportArgs {
   int C;
   RowInfo rows;
   int nrows;
-  int T;            // allocated frames per output row
+  int T;            // allocated frames per output row (plane length)
+  int T_write;      // frames written per row (0: T)
   int op;
   void* s_out;      // may be null
   const float* s_alpha;  // null -> identity
@@ -173,6 +176,7 @@ struct HeadArgs {
   int nrows;
   int rate;         // frames per latent frame
   int pad;          // left padding of the k=7 conv: 3 ("same") or 6 (causal)
+  int lb;           // frames in [-lb, 0) of h are read from memory, else zero
   const float* w;   // [7][C]
   float bias;
   float* pcm;
@@ -181,15 +185,18 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
 
-// Streaming: build one chunk's decode input from a stream's history and
-// roll the history forward (fp32 [rows][C][*] layouts).
-struct StreamPrepArgs {
-  const float* hist_old;  // [rows][C][H]: the last `avail` frames right-aligned
-  float* hist_new;        // [rows][C][H]: receives the last `keep` frames of cat
-  const float* chunk;     // [rows][C][t]
-  float* cat;             // [rows][C][avail + t]
-  int64_t rows, C, H, avail, t, keep;
+// Streaming: one layer's carried context.  buf points at frame 0 of the
+// first plane of the layer's input; planes of plane_bytes bytes hold 64-byte
+// frame rows, the chunk in frames [0, Tr) and ctx margin frames before it.
+// The margin receives old_state; new_state receives the last ctx frames of
+// (old_state, chunk).  States are [planes][ctx][64 bytes].
+struct LayerStateArgs {
+  unsigned char* buf;
+  int64_t plane_bytes, planes;
+  int ctx, Tr;
+  const unsigned char* old_state;
+  unsigned char* new_state;
 };
-hipError_t launch_stream_prep(const StreamPrepArgs& a, hipStream_t s);
+hipError_t launch_layer_state(const LayerStateArgs& a, hipStream_t s);
 
 }  // namespace voc

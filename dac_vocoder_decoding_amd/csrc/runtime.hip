@@ -84,13 +84,22 @@ struct voc_ctx {
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
-  // streaming (causal configurations)
+  // streaming (causal configurations): the carried context of every layer
+  // with one ([planes][ctx][64 bytes], two copies that alternate by chunk),
+  // in the order conv_in, per block: ConvTranspose1d then its units, head.
+  struct LayerState {
+    int ctx = 0;                  // frames of context
+    int64_t planes_per_row = 0;   // 64-byte frame-row planes of the layer's input
+    size_t off[2] = {0, 0};       // byte offsets of the two copies in st_mem
+  };
+  std::vector<LayerState> st_layers;
+  void* st_mem = nullptr;
+  size_t st_mem_bytes = 0;
   int64_t st_rows = 0;          // streams since the last reset (0: none)
-  int64_t st_avail = 0;         // history frames held per stream (<= halo_l)
-  int st_par = 0;               // which history buffer holds the current history
-  float* st_hist[2] = {nullptr, nullptr};  // [st_rows][C][halo_l] each
-  float* st_cat = nullptr;      // [st_rows][C][st_avail + t] decode input
-  size_t st_hist_bytes = 0, st_cat_bytes = 0;
+  int st_par = 0;               // which copy holds the current context
+  int st_margin = 0;            // margin frames in front of every activation plane
+  bool st_active = false;       // the stack runs a stream chunk (exchanges on)
+  int mg = 0;                   // margin frames of the activation planes being decoded
   std::vector<int64_t> meta_dst;  // host copies kept alive for async uploads
   std::vector<int> meta_int;
 };
@@ -253,7 +262,8 @@ voc_status launch(voc_ctx* c, hipStream_t s, int kind, double flops, double byte
 
 // ------------------------------------------------------------- workspace
 struct Plan {
-  int rows, T;            // rows and allocated latent frames per row
+  int rows, T;            // rows and latent frames per row
+  int mg;                 // margin frames in front of every activation plane (streams)
   size_t off_xlat, off_h, off_h2, off_s0, off_s1, off_u, off_meta, bytes;
 };
 
@@ -272,22 +282,23 @@ bool any_unit_xh(const voc_ctx* c) {
   return false;
 }
 
-Plan make_plan(const voc_ctx* c, int rows, int T) {
+Plan make_plan(const voc_ctx* c, int rows, int T, int mg = 0) {
   const voc_config& g = c->cfg;
   const size_t es = op_size(c->op);
   size_t max_act = 0;
   int64_t t = T;
-  max_act = std::max<size_t>(max_act, static_cast<size_t>(g.width[0]) * t);
-  max_act = std::max<size_t>(max_act, static_cast<size_t>(g.in_proj) * t);  // dec_in_proj out (in u)
+  max_act = std::max<size_t>(max_act, static_cast<size_t>(g.width[0]) * (t + mg));
+  max_act = std::max<size_t>(max_act, static_cast<size_t>(g.in_proj) * (t + mg));  // dec_in_proj out (in u)
   for (int b = 0; b < g.n_blocks; ++b) {
     t *= g.stride[b];
-    max_act = std::max<size_t>(max_act, static_cast<size_t>(g.width[b + 1]) * t);
+    max_act = std::max<size_t>(max_act, static_cast<size_t>(g.width[b + 1]) * (t + mg));
   }
   Plan p{};
   p.rows = rows;
   p.T = T;
+  p.mg = mg;
   size_t o = 0;
-  p.off_xlat = o; o = align_up(o + es * rows * static_cast<size_t>(g.latent_channels) * T);
+  p.off_xlat = o; o = align_up(o + es * rows * static_cast<size_t>(g.latent_channels) * (T + mg));
   p.off_h = o;    o = align_up(o + 4 * rows * max_act);
   p.off_h2 = o;   if (any_unit_xh(c)) o = align_up(o + 4 * rows * max_act);
   p.off_s0 = o;   o = align_up(o + es * rows * max_act);
@@ -331,12 +342,15 @@ struct Bufs {
 Bufs bufs(voc_ctx* c, const Plan& p) {
   char* b = static_cast<char*>(c->ws);
   Bufs r{};
-  r.xlat = b + p.off_xlat;
-  r.h = reinterpret_cast<float*>(b + p.off_h);
-  r.h2 = reinterpret_cast<float*>(b + p.off_h2);
-  r.s[0] = b + p.off_s0;
-  r.s[1] = b + p.off_s1;
-  r.u = b + p.off_u;
+  // Activation pointers address frame 0 of the first plane; with a margin
+  // every plane starts mg frames (64-byte rows) earlier.
+  const size_t mgb = static_cast<size_t>(p.mg) * kChunkBytes;
+  r.xlat = b + p.off_xlat + mgb;
+  r.h = reinterpret_cast<float*>(b + p.off_h + mgb);
+  r.h2 = reinterpret_cast<float*>(b + p.off_h2 + mgb);
+  r.s[0] = b + p.off_s0 + mgb;
+  r.s[1] = b + p.off_s1 + mgb;
+  r.u = b + p.off_u + mgb;
   char* m = b + p.off_meta;
   r.rows.dst = reinterpret_cast<const int64_t*>(m);
   const int* ib = reinterpret_cast<const int*>(m + sizeof(int64_t) * p.rows);
@@ -413,7 +427,7 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
                     int kind, hipStream_t s) {
   ConvArgs a{};
   a.x = io.x;
-  a.T_in = io.T_in;
+  a.T_in = io.T_in + c->mg;  // plane length (margin included)
   a.Cin = L.cin;
   a.row_len = row_len;
   a.rate_in = io.rate_in;
@@ -435,9 +449,12 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
     a.halo = (L.taps - 1) * L.dil;
     a.N = io.T_in;
   }
-  a.T_out = io.T_in * L.ups;
+  a.T_out = io.T_in * L.ups + c->mg;
   a.ups = L.ups;
   a.crop = L.crop;
+  // A stream chunk reads its carried context: x[n - 1] for the transposed
+  // conv, (K-1)*d frames for a causal k=7 conv.
+  a.lb = c->st_active ? (L.taps == 2 ? 1 : -a.min_off) : 0;
   a.bias = L.bias;
   a.h_out = io.h_out;
   a.res = io.res;
@@ -481,7 +498,8 @@ voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const Ro
   a.C = C;
   a.rows = rows;
   a.nrows = nrows;
-  a.T = T;
+  a.T = T + c->mg;
+  a.T_write = T;
   a.op = c->op;
   a.s_out = s_out;
   a.s_alpha = sn ? sn->alpha : nullptr;
@@ -500,11 +518,12 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
   const voc_config& g = c->cfg;
   a.h = h;
   a.C = g.width[g.n_blocks];
-  a.T = T;
+  a.T = T + c->mg;
   a.rows = rows;
   a.nrows = nrows;
   a.rate = rate;
   a.pad = c->cfg.causal ? 6 : 3;
+  a.lb = c->st_active ? a.pad : 0;
   a.w = c->W.head_w;
   a.bias = c->W.head_bias;
   a.pcm = pcm;
@@ -550,12 +569,13 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     a.a1_scale = u.a1.alpha;
     a.a1_h = u.a1.invden;
     a.h_in = h;
-    a.T = T;
+    a.T = T + c->mg;
     a.C = C;
     a.row_len = row_len;
     a.rate = rate;
     a.dil = u.c1.dil;
     a.pad = (c->cfg.causal ? 6 : 3) * u.c1.dil;
+    a.lb = c->st_active ? a.pad : 0;
     a.w1 = u.c1.w;
     a.b1 = u.c1.bias;
     a.a2_scale = u.a2.alpha;
@@ -616,6 +636,25 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
   const Weights& W = c->W;
   const int nb = g.n_blocks, nr = g.n_res;
   int cur = 0;
+  // Stream chunks: before each layer with context, its input's margin gets
+  // the context carried from the previous chunk and the new context is saved
+  // (layer index li in the order of voc_ctx::st_layers).
+  int li = 0;
+  auto xchg = [&](const void* buf, int64_t frames) -> voc_status {
+    if (!c->st_active) return VOC_OK;
+    const voc_ctx::LayerState& L = c->st_layers[li++];
+    LayerStateArgs a{};
+    a.buf = static_cast<unsigned char*>(const_cast<void*>(buf));
+    a.plane_bytes = (c->mg + frames) * kChunkBytes;
+    a.planes = static_cast<int64_t>(rows) * L.planes_per_row;
+    a.ctx = L.ctx;
+    a.Tr = static_cast<int>(frames);
+    a.old_state = static_cast<const unsigned char*>(c->st_mem) + L.off[c->st_par];
+    a.new_state = static_cast<unsigned char*>(c->st_mem) + L.off[c->st_par ^ 1];
+    const double bytes = 3.0 * a.planes * a.ctx * kChunkBytes;
+    return launch(c, s, VOC_K_IMPORT, 0.0, bytes, "stream state launch",
+                  [&] { return launch_layer_state(a, s); });
+  };
   ConvIO io{};
   const void* x_in = B.xlat;
   if (W.in_proj.cout > 0) {  // dec_in_proj: operand for conv_in, no activation between
@@ -634,7 +673,9 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
   io.h_out = B.h;
   io.s_out = B.s[cur];
   io.snake_next = &W.blocks[0].act;
-  voc_status st = run_conv(c, W.conv_in, io, rows, B.rows.len, VOC_K_CONV_IN, s);
+  voc_status st = xchg(x_in, T);
+  if (st) return st;
+  st = run_conv(c, W.conv_in, io, rows, B.rows.len, VOC_K_CONV_IN, s);
   if (st) return st;
   int t = T, rate = 1;
   float* hc = B.h;   // current residual stream
@@ -651,6 +692,8 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
       io.s_out = B.s[cur ^ 1];
       io.snake_next = &blk.units[0].a1;
     }
+    st = xchg(B.s[cur], t);
+    if (st) return st;
     st = run_conv(c, blk.ct, io, rows, B.rows.len, VOC_K_CONVT, s);
     if (st) return st;
     if (!xh) cur ^= 1;
@@ -666,6 +709,8 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
       // Within a block of such units only the last one writes an operand
       // tensor (the next block's ConvTranspose1d input).
       const SnakeDev* next = (xh && r + 1 < nr) ? nullptr : next_snake(W, b, r, nb, nr);
+      st = xchg(xh ? static_cast<const void*>(hc) : B.s[cur], t);  // conv1's input
+      if (st) return st;
       st = run_res_unit(c, blk.units[r], xh ? nullptr : B.s[cur], B.s[cur ^ 1], B.u, hc,
                         xh ? ho : nullptr, next, &s_next, t, rate, rows, B.rows.len, s, hs, keep_h);
       if (st) return st;
@@ -674,7 +719,7 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
     }
   }
   *h_last = hc;
-  return VOC_OK;
+  return xchg(hc, t);  // the head's input
 }
 
 // ----------------------------------------------------------- weight names
@@ -1103,22 +1148,28 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
 }
 
 namespace {
-// Device buffer of at least `bytes` (contents not kept when it grows).
-voc_status grow(voc_ctx* c, float** p, size_t* cap, size_t bytes, const char* what) {
-  if (bytes <= *cap) return VOC_OK;
-  if (*p) {
-    (void)hipDeviceSynchronize();
-    (void)hipFree(*p);
-    *p = nullptr;
-    *cap = 0;
+// The layers with carried context and their input layouts, in the order
+// run_stack visits them: conv_in (k=7), per block the ConvTranspose1d (one
+// input frame) and each unit's conv1 (6d frames of h when the unit computes
+// its operand from h, else of the operand tensor), and the head (k=7 on h).
+std::vector<voc_ctx::LayerState> stream_layers(const voc_ctx* c) {
+  const voc_config& g = c->cfg;
+  const int op_rows = 64 / op_size(c->op);  // channels per 64-byte operand row
+  std::vector<voc_ctx::LayerState> v;
+  auto add = [&](int ctx, int64_t planes) {
+    voc_ctx::LayerState L;
+    L.ctx = ctx;
+    L.planes_per_row = planes;
+    v.push_back(L);
+  };
+  add(6, (g.in_proj > 0 ? g.in_proj : g.latent_channels) / op_rows);
+  for (int b = 0; b < g.n_blocks; ++b) {
+    add(1, g.width[b] / op_rows);
+    const int C = g.width[b + 1];
+    for (int r = 0; r < g.n_res; ++r) add(6 * g.dilation[r], unit_xh(c, C) ? C / 16 : C / op_rows);
   }
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(p), bytes);
-  if (e != hipSuccess) {
-    *p = nullptr;
-    return hip_fail(c, e, what);
-  }
-  *cap = bytes;
-  return VOC_OK;
+  add(6, g.width[g.n_blocks] / 16);
+  return v;
 }
 }  // namespace
 
@@ -1127,19 +1178,41 @@ VOC_API voc_status vocoder_stream_reset(voc_ctx* c, int64_t rows) {
   if (!c->cfg.causal) return fail(c, VOC_INVALID_PARAMS, "streaming needs a causal configuration");
   if (c->cfg.tile_frames != 0) return fail(c, VOC_INVALID_PARAMS, "streaming needs tile_frames == 0");
   if (rows <= 0 || rows > 65535) return fail(c, VOC_INVALID_PARAMS, "rows must be in [1, 65535]");
-  const size_t bytes = static_cast<size_t>(rows) * c->cfg.latent_channels * std::max(c->halo_l, 1) * 4;
-  for (int k = 0; k < 2; ++k) {
-    size_t cap = c->st_hist[k] ? c->st_hist_bytes : 0;
-    voc_status st = grow(c, &c->st_hist[k], &cap, bytes, "stream history hipMalloc");
-    if (st) {
-      c->st_rows = 0;
-      return st;
-    }
+  std::vector<voc_ctx::LayerState> L = stream_layers(c);
+  size_t o = 0;
+  int margin = 0;
+  for (auto& l : L) {
+    const size_t bytes = static_cast<size_t>(rows) * l.planes_per_row * l.ctx * kChunkBytes;
+    l.off[0] = o;
+    o = align_up(o + bytes);
+    l.off[1] = o;
+    o = align_up(o + bytes);
+    margin = std::max(margin, l.ctx);
   }
-  c->st_hist_bytes = std::max(c->st_hist_bytes, bytes);
+  c->st_rows = 0;
+  if (o > c->st_mem_bytes) {
+    if (c->st_mem) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(c->st_mem);
+      c->st_mem = nullptr;
+      c->st_mem_bytes = 0;
+    }
+    hipError_t e = hipMalloc(&c->st_mem, o);
+    if (e != hipSuccess) {
+      c->st_mem = nullptr;
+      return hip_fail(c, e, "stream state hipMalloc");
+    }
+    c->st_mem_bytes = o;
+  }
+  // Zero context: a new stream starts like the offline decode's zero left
+  // padding.  (Synchronous: nothing of an earlier stream is in flight.)
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemset(c->st_mem, 0, o);
+  if (e != hipSuccess) return hip_fail(c, e, "stream state clear");
+  c->st_layers = std::move(L);
   c->st_rows = rows;
-  c->st_avail = 0;
   c->st_par = 0;
+  c->st_margin = margin;
   return VOC_OK;
 }
 
@@ -1150,46 +1223,46 @@ VOC_API voc_status vocoder_stream_decode(voc_ctx* c, const float* latent, int64_
   if (!latent || !pcm) return fail(c, VOC_INVALID_PARAMS, "NULL latent or pcm");
   if ((reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(pcm)) & 15)
     return fail(c, VOC_INVALID_PARAMS, "latent and pcm must be 16-byte aligned");
-  const int64_t H = c->halo_l;
-  if (t <= 0 || (H + t) * c->hop > (int64_t(1) << 31) - 1)
-    return fail(c, VOC_INVALID_PARAMS, "t must be positive with (halo + t) * hop below 2^31");
+  if (t <= 0 || t * c->hop + c->st_margin > (int64_t(1) << 31) - 1)
+    return fail(c, VOC_INVALID_PARAMS, "t must be positive with t * hop below 2^31");
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t rows = c->st_rows, C = c->cfg.latent_channels;
-  const int64_t avail = c->st_avail, Lw = avail + t, keep = std::min(H, Lw);
-  voc_status st = grow(c, &c->st_cat, &c->st_cat_bytes, static_cast<size_t>(rows) * C * Lw * 4,
-                       "stream staging hipMalloc");
+  const int64_t rows = c->st_rows;
+  const int mg = c->st_margin;
+  const Plan p = make_plan(c, static_cast<int>(rows), static_cast<int>(t), mg);
+  voc_status st = ensure_ws(c, p.bytes);
   if (st) return st;
-  StreamPrepArgs pa{};
-  pa.hist_old = c->st_hist[c->st_par];
-  pa.hist_new = c->st_hist[c->st_par ^ 1];
-  pa.chunk = latent;
-  pa.cat = c->st_cat;
-  pa.rows = rows;
-  pa.C = C;
-  pa.H = std::max<int64_t>(H, 1);
-  pa.avail = avail;
-  pa.t = t;
-  pa.keep = keep;
-  st = launch(c, s, VOC_K_IMPORT, 0.0, 4.0 * rows * C * (avail + 2 * t + keep), "stream launch",
-              [&] { return launch_stream_prep(pa, s); });
-  if (st) return st;
-  // Row r decodes its history and the chunk, keeping the chunk's samples.
-  std::vector<int64_t> dst(rows);
-  std::vector<int> ints(5 * rows);
-  for (int64_t r = 0; r < rows; ++r) {
-    ints[r] = static_cast<int>(Lw);                         // len
-    ints[rows + r] = static_cast<int>(r);                   // src_b
-    ints[2 * rows + r] = 0;                                 // start
-    ints[3 * rows + r] = static_cast<int>(avail * c->hop);  // keep_lo
-    ints[4 * rows + r] = static_cast<int>(Lw * c->hop);     // keep_hi
-    dst[r] = r * t * c->hop;
+  // Row r is stream r: the chunk's t frames, all of its samples kept.
+  const std::vector<int64_t> key = {3, rows, t};
+  if (c->rows_key != key) {
+    std::vector<int64_t> dst(rows);
+    std::vector<int> ints(5 * rows);
+    for (int64_t r = 0; r < rows; ++r) {
+      ints[r] = static_cast<int>(t);                          // len
+      ints[rows + r] = static_cast<int>(r);                   // src_b
+      ints[2 * rows + r] = 0;                                 // start
+      ints[3 * rows + r] = 0;                                 // keep_lo
+      ints[4 * rows + r] = static_cast<int>(t * c->hop);      // keep_hi
+      dst[r] = r * t * c->hop;
+    }
+    st = upload_rows(c, p, std::move(dst), std::move(ints), s);
+    if (st) return st;
+    c->rows_key = key;
   }
-  st = decode_rows(c, c->st_cat, Lw, rows, static_cast<int>(Lw), std::move(dst), std::move(ints),
-                   {2, rows, Lw, avail}, pcm, s);
+  const Bufs Bf = bufs(c, p);
+  c->mg = mg;
+  c->st_active = true;
+  float* h_last = nullptr;
+  st = run_import(c, latent, t, c->cfg.latent_channels, Bf.rows, static_cast<int>(rows),
+                  static_cast<int>(t), Bf.xlat, nullptr, nullptr, s);
+  if (!st) st = run_stack(c, Bf, static_cast<int>(rows), static_cast<int>(t), s, &h_last);
+  if (!st)
+    st = run_head(c, h_last, static_cast<int>(t * c->hop), Bf.rows, static_cast<int>(rows),
+                  static_cast<int>(c->hop), pcm, s);
+  c->mg = 0;
+  c->st_active = false;
   if (st) return st;
   c->st_par ^= 1;
-  c->st_avail = keep;
   return VOC_OK;
 }
 
@@ -1255,8 +1328,7 @@ VOC_API void vocoder_destroy(voc_ctx* c) {
   (void)hipDeviceSynchronize();
   free_weights(c->W);
   if (c->ws) (void)hipFree(c->ws);
-  for (float* p : {c->st_hist[0], c->st_hist[1], c->st_cat})
-    if (p) (void)hipFree(p);
+  if (c->st_mem) (void)hipFree(c->st_mem);
   for (auto& r : c->pending) {
     (void)hipEventDestroy(r.e0);
     (void)hipEventDestroy(r.e1);

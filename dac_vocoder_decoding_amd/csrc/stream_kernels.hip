@@ -82,7 +82,8 @@ __global__ __launch_bounds__(256) void import_kernel(const ImportArgs a) {
   const int cblocks = a.C / 16;
   const int c0 = (blockIdx.x % cblocks) * 16;
   const int t0 = (blockIdx.x / cblocks) * 64;
-  const int len = min(a.rows.len[r], a.T);
+  const int Tw = a.T_write > 0 ? a.T_write : a.T;  // frames written per row
+  const int len = min(a.rows.len[r], Tw);
   const int sb = a.rows.src_b[r];
   const int64_t st = a.rows.start[r];
   const int tid = threadIdx.x;
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void import_kernel(const ImportArgs a) {
   __syncthreads();
   const int t = tid >> 2, c = (tid & 3) * 4;
   const int tt = t0 + t;
-  if (tt >= a.T) return;
+  if (tt >= Tw) return;
   f4 v;
   v[0] = tile[c][t];
   v[1] = tile[c + 1][t];
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(256) void import_kernel(const ImportArgs a) {
 }
 
 hipError_t launch_import(const ImportArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((a.C / 16) * ((a.T + 63) / 64)),
+  const int Tw = a.T_write > 0 ? a.T_write : a.T;
+  const dim3 grid(static_cast<unsigned>((a.C / 16) * ((Tw + 63) / 64)),
                   static_cast<unsigned>(a.nrows));
   if (a.op == OP_F32)
     hipLaunchKernelGGL(import_kernel<OP_F32>, grid, dim3(256), 0, s, a);
@@ -170,34 +172,36 @@ hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipSt
   return hipGetLastError();
 }
 
-// ------------------------------------------------------- stream history
-// One chunk of a stream: cat[r][c] = (the last `avail` frames of hist_old[r][c],
-// then the t frames of chunk[r][c]), and hist_new[r][c] receives the last
-// `keep` frames of that concatenation, right-aligned in its H frames.  The
-// two history buffers alternate between chunks, so no element is read and
-// written by the same launch.
-__global__ __launch_bounds__(256) void stream_prep_kernel(const StreamPrepArgs a) {
-  const int64_t Lw = a.avail + a.t;
-  const int64_t per = Lw + a.keep;  // cat elements, then history elements, per (r, c)
-  const int64_t total = a.rows * a.C * per;
+// ---------------------------------------------------- stream layer state
+// One layer's carried context in a stream (qwentts.cpp ARCHITECTURE,
+// "Streaming decode (stateful path)": each causal conv keeps the last
+// (K-1)*d rows of its input).  The layer's input buffer holds, per plane of
+// 64-byte frame rows, the chunk in frames [0, Tr) and room for ctx frames
+// before it.  The margin receives the saved context (old), and the new
+// context (the last ctx frames of old followed by the chunk) is saved for the
+// next chunk.  Margin writes (frames < 0) and chunk reads (frames >= 0) never
+// overlap; old and new are separate buffers.
+__global__ __launch_bounds__(256) void layer_state_kernel(const LayerStateArgs a) {
+  const int64_t total = a.planes * a.ctx * 4;  // 16-byte units
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t rc = i / per, j = i - rc * per;
-    // Position in the concatenation that this element reads.
-    const int64_t q = j < Lw ? j : Lw - a.keep + (j - Lw);
-    const float v = q < a.avail ? a.hist_old[rc * a.H + a.H - a.avail + q] : a.chunk[rc * a.t + (q - a.avail)];
-    if (j < Lw)
-      a.cat[rc * Lw + j] = v;
-    else
-      a.hist_new[rc * a.H + a.H - a.keep + (j - Lw)] = v;
+    const int64_t p = i / (a.ctx * 4);
+    const int k = static_cast<int>((i / 4) % a.ctx), u = static_cast<int>(i % 4);
+    const uint4* old_row = reinterpret_cast<const uint4*>(a.old_state + (p * a.ctx + k) * kChunkBytes) + u;
+    unsigned char* plane = a.buf + p * a.plane_bytes;
+    const uint4 o = *old_row;
+    const int q = a.Tr + k;  // position in (old context, chunk)
+    const uint4 nv = q < a.ctx ? *(reinterpret_cast<const uint4*>(a.old_state + (p * a.ctx + q) * kChunkBytes) + u)
+                               : *(reinterpret_cast<const uint4*>(plane + static_cast<int64_t>(q - a.ctx) * kChunkBytes) + u);
+    *(reinterpret_cast<uint4*>(plane + static_cast<int64_t>(k - a.ctx) * kChunkBytes) + u) = o;
+    *(reinterpret_cast<uint4*>(a.new_state + (p * a.ctx + k) * kChunkBytes) + u) = nv;
   }
 }
 
-hipError_t launch_stream_prep(const StreamPrepArgs& a, hipStream_t s) {
-  const int64_t total = a.rows * a.C * (a.avail + a.t + a.keep);
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 2048);
-  hipLaunchKernelGGL(stream_prep_kernel, dim3(static_cast<unsigned>(std::max<int64_t>(blocks, 1))), dim3(256), 0,
-                     s, a);
+hipError_t launch_layer_state(const LayerStateArgs& a, hipStream_t s) {
+  const int64_t total = a.planes * a.ctx * 4;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 2048));
+  hipLaunchKernelGGL(layer_state_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -213,8 +217,8 @@ hipError_t launch_stream_prep(const StreamPrepArgs& a, hipStream_t s) {
 //   cross-lane shuffles.  P = 3 for the "same" conv, 6 for the causal one
 //   (qwentts.cpp ARCHITECTURE, "Streaming decode": every module causal).
 // Each wave emits 58 outputs per 64 frames read; no LDS tile, no barriers.
-// Frames outside the row's valid range read as zero (the conv's zero
-// padding; Snake(0) = 0).  The tile crop of time-tiled decoding is folded
+// Frames outside the row's valid range [-lb, len) read as zero (the conv's
+// zero padding; Snake(0) = 0; lb > 0 only for a stream's carried context).  The tile crop of time-tiled decoding is folded
 // into the store.
 constexpr int kHeadOut = 58;  // outputs per wave
 
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   const int Lr = min(a.rows.len[r] * a.rate, a.T);
   const int P = a.pad;  // 3, or 6 for the causal head
   const int f = o0 - P + lane;
-  const bool valid = f >= 0 && f < Lr;
+  const bool valid = f >= -a.lb && f < Lr;
   const float* hp = a.h + static_cast<int64_t>(r) * C * a.T + static_cast<int64_t>(f) * kHChunk;
   const int64_t plane = static_cast<int64_t>(a.T) * kHChunk;
   float z[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};

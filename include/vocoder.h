@@ -223,12 +223,13 @@ voc_status vocoder_decode_windows(voc_ctx *ctx, const float *latents, int64_t n_
  * (the next chunk decodes as the start of a clip: zero left padding).
  * vocoder_stream_decode decodes the next t >= 1 latent frames of every
  * stream, latent: device fp32 [rows, latent_channels, t] contiguous, into
- * pcm: device fp32 [rows, 1, t*hop] contiguous.  The library keeps the last
- * H latent frames of each stream (H = voc_config_halo, the causal receptive
- * field) and decodes them ahead of the chunk, keeping only the chunk's own
- * samples; the history is the whole stream state.  Same asynchrony and
- * ownership as vocoder_decode (the history lives in library memory, grown
- * with hipMalloc on first use).
+ * pcm: device fp32 [rows, 1, t*hop] contiguous.  Each layer with context
+ * carries its last input frames from chunk to chunk ((K-1)*d frames for a
+ * causal k=7 conv, one input frame for a ConvTranspose1d, whose polyphase
+ * form needs x[n-1] where the pages carry the col2im tail), so every chunk
+ * decodes only its own frames.  Same asynchrony and ownership as
+ * vocoder_decode; the state lives in library memory (hipMalloc at reset,
+ * cleared to zero there, which is the offline decode's zero left padding).
  * Errors: VOC_INVALID_PARAMS (non-causal or tiled configuration, rows or t
  * out of range, NULL/misaligned pointers, decode before reset),
  * VOC_NOT_LOADED, VOC_OOM, VOC_DEVICE_ERROR.
