@@ -133,6 +133,13 @@ CONFIGS = {
     7: _cfg(name="causal_codec_stream_bf16", latent_channels=1024, batch=32, frames=250,
             dtype="bf16", sample_rate=24000, stereo=False, act="snakebeta", causal=1,
             widths=(1536, 768, 384, 192, 96), strides=(8, 5, 4, 3), seed=1007, chunk=25),
+    # The DAV encoder (minimaxmusic.cpp ARCHITECTURE, "Flow VAE": conv_in
+    # 1 -> 64, blocks doubling to 1024 with strides 2/4/8/8, conv_out
+    # 1024 -> 1024 k=3, posterior mean 1024 -> 64) on one stereo window:
+    # 689 x 512 samples per side -> latent [2, 64, 689].
+    8: _cfg(name="dav_encode_window_f32", batch=2, frames=689, in_proj=1024,
+            widths=(1536, 768, 384, 192, 96), strides=(8, 8, 4, 2), seed=1008,
+            enc_widths=(64, 128, 256, 512, 1024), encode=True),
 }
 
 
@@ -185,6 +192,28 @@ def tensor_shapes(cfg: dict) -> dict:
     snake("snake_out", w[-1])
     conv("conv_out", (1, w[-1], k))
     shapes["conv_out.bias"] = (1,)
+    ew = cfg.get("enc_widths")
+    if ew:  # the encoder: the decoder's strides in reverse order
+        conv("encoder.conv_in", (ew[0], 1, k))
+        shapes["encoder.conv_in.bias"] = (ew[0],)
+        for b, s in enumerate(reversed(cfg["strides"])):
+            q = f"encoder.blocks.{b}"
+            for r in range(len(cfg["dilations"])):
+                u = f"{q}.res_units.{r}"
+                snake(u + ".snake1", ew[b])
+                conv(u + ".conv1", (ew[b], ew[b], k))
+                shapes[u + ".conv1.bias"] = (ew[b],)
+                snake(u + ".snake2", ew[b])
+                conv(u + ".conv2", (ew[b], ew[b], 1))
+                shapes[u + ".conv2.bias"] = (ew[b],)
+            snake(q + ".snake", ew[b])
+            conv(q + ".down", (ew[b + 1], ew[b], 2 * s))
+            shapes[q + ".down.bias"] = (ew[b + 1],)
+        snake("encoder.snake_out", ew[-1])
+        conv("encoder.conv_out", (ew[-1], ew[-1], 3))
+        shapes["encoder.conv_out.bias"] = (ew[-1],)
+        conv("encoder.proj", (cl, ew[-1], 1))
+        shapes["encoder.proj.bias"] = (cl,)
     return shapes
 
 
@@ -242,11 +271,35 @@ def make_latent(cfg: dict, seed: int | None = None, batch: int | None = None,
     return normal(seed, "latent", (b, cfg["latent_channels"], t))
 
 
+def make_audio(cfg: dict, seed: int | None = None, batch: int | None = None,
+               frames: int | None = None) -> np.ndarray:
+    """Seeded audio [B, 1, frames * hop] ~ 0.5 * N(0, 1), float32 (music-like
+    level: unit-variance noise scaled to an RMS of 0.5)."""
+    seed = cfg["seed"] if seed is None else seed
+    b = cfg["batch"] if batch is None else batch
+    t = cfg["frames"] if frames is None else frames
+    return normal(seed, "audio", (b, 1, t * cfg["hop"]), std=0.5)
+
+
 def audio_seconds(cfg: dict, batch: int, frames: int) -> float:
     """Decoded audio-seconds: stereo pairs count once (two rows per stereo second)."""
     samples = frames * cfg["hop"]
     rows = batch / 2 if cfg["stereo"] else batch
     return rows * samples / cfg["sample_rate"]
+
+
+def encode_flops(cfg: dict, batch: int, frames: int) -> float:
+    """Direct-convolution multiply-adds x 2 of one encode of frames * hop samples."""
+    ew, k = cfg["enc_widths"], cfg["kernel"]
+    t = frames * cfg["hop"]
+    f = 2.0 * batch * t * ew[0] * k
+    for b, s in enumerate(reversed(cfg["strides"])):
+        for _ in cfg["dilations"]:
+            f += 2.0 * batch * t * ew[b] * ew[b] * (k + 1)
+        t //= s
+        f += 2.0 * batch * t * ew[b + 1] * ew[b] * 2 * s
+    f += 2.0 * batch * t * ew[-1] * ew[-1] * 3 + 2.0 * batch * t * cfg["latent_channels"] * ew[-1]
+    return f
 
 
 def algorithmic_flops(cfg: dict, batch: int, frames: int) -> float:

@@ -118,6 +118,33 @@ EXPORT void orc_conv1d(const REAL *x, REAL *y, int64_t rows, int64_t Cin, int64_
 }
 
 /*
+ * Strided Conv1d (the encoder's downsampling conv): zero padding P on the
+ * left, stride s, output length Tout:
+ *   y[r][o][t] = bias[o] + sum_i sum_j w[o][i][j] * x[r][i][t*s + j - P],
+ * x outside [0, T) is zero.  w is [Cout][Cin][K]; bias may be NULL.
+ */
+EXPORT void orc_conv1d_strided(const REAL *x, REAL *y, int64_t rows, int64_t Cin, int64_t T,
+                               const REAL *w, const REAL *bias, int64_t Cout, int64_t K,
+                               int64_t s, int64_t P, int64_t Tout) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t o = 0; o < Cout; ++o) {
+      REAL *yr = y + (r * Cout + o) * Tout;
+      for (int64_t t = 0; t < Tout; ++t) {
+        REAL acc = 0;
+        for (int64_t i = 0; i < Cin; ++i) {
+          const REAL *xr = x + (r * Cin + i) * T;
+          for (int64_t j = 0; j < K; ++j) {
+            const int64_t src = t * s + j - P;
+            if (src >= 0 && src < T) acc += w[(o * Cin + i) * K + j] * xr[src];
+          }
+        }
+        yr[t] = acc + (bias ? bias[o] : (REAL)0);
+      }
+    }
+}
+
+/*
  * ConvTranspose1d with stride s, kernel K, left crop p, output length Tout:
  * every input sample x[i][m] adds w[i][o][:] * x[i][m] into the full output
  * starting at m*s; the kept output is full[n + p] for n in [0, Tout):

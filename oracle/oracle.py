@@ -89,6 +89,7 @@ def load_library(path: str, prec: str):
     lib.orc_weight_norm.argtypes = [P, P, P, I, I, P]
     lib.orc_conv1d.argtypes = [P, P, I, I, I, P, P, I, I, I, I]
     lib.orc_conv_transpose1d.argtypes = [P, P, I, I, I, P, P, I, I, I, I, I]
+    lib.orc_conv1d_strided.argtypes = [P, P, I, I, I, P, P, I, I, I, I, I]
     lib.orc_tanh.argtypes = [P, P, I]
     lib.orc_add.argtypes = [P, P, P, I]
     assert lib.orc_real_size() == np.dtype(_NP[prec]).itemsize
@@ -159,6 +160,21 @@ def conv1d(x, w, bias=None, dilation=1, prec="f64", causal=False):
     b = None if bias is None else _c(np.reshape(bias, -1), prec)
     y = np.empty((r, cout, t), dtype=_NP[prec])
     _lib(prec).orc_conv1d(_p(x), _p(y), r, cin, t, _p(w), _p(b), cout, k, dilation, pad)
+    return y
+
+
+def conv1d_strided(x, w, bias, stride, pad, prec="f64"):
+    """Strided Conv1d with zero padding `pad` on both sides.  x: [R, Cin, T],
+    w: [Cout, Cin, K]; output length (T + 2 pad - K) // stride + 1."""
+    x = _c(x, prec)
+    w = _c(w, prec)
+    r, cin, t = x.shape
+    cout, cin2, k = w.shape
+    assert cin == cin2
+    tout = (t + 2 * pad - k) // stride + 1
+    b = None if bias is None else _c(np.reshape(bias, -1), prec)
+    y = np.empty((r, cout, tout), dtype=_NP[prec])
+    _lib(prec).orc_conv1d_strided(_p(x), _p(y), r, cin, t, _p(w), _p(b), cout, k, stride, pad, tout)
     return y
 
 
@@ -366,6 +382,77 @@ class Model:
             y = self.decode(latent[:, :, a:e])
             out[:, :, t0 * hop:t1 * hop] = y[:, :, (t0 - a) * hop:(t1 - a) * hop]
         return out
+
+
+class Encoder:
+    """The DAV encoder (minimaxmusic.cpp ARCHITECTURE, "Flow VAE": the mirror
+    of the decoder), per side:
+        h = conv_in(audio)                          Conv1d 1 -> E0, k=7, "same" padding
+        for each block b (stride s = the decoder's strides reversed):
+            h = residual units (dilations 1, 3, 9) at width E_b
+            h = down(Snake(h))                      Conv1d E_b -> E_{b+1}, k=2s, stride s, pad s/2
+        z = conv_out(Snake_out(h))                  Conv1d k=3, "same" padding
+        mean = proj(z)                              Conv1d k=1 to the latent channels
+    Readings: every encoder conv is weight-normed (the page says all convs
+    of the checkpoint are); no activation between conv_out and proj; the
+    encode is the posterior mean (the page: deterministic, no sampling)."""
+
+    def __init__(self, cfg: dict, tensors: dict, prec: str = "f64", round_operands: bool = False):
+        self.cfg = cfg
+        self.prec = prec
+        self.bf16 = cfg["dtype"] == "bf16"
+        self.round_operands = round_operands and self.bf16
+        self.beta = cfg["act"] == "snakebeta"
+        t = tensors
+
+        def fold(prefix):
+            w, _ = weight_norm(t[prefix + ".weight_v"], t[prefix + ".weight_g"], "f64")
+            if self.bf16:
+                w = round_bf16(w.astype(np.float32))
+            return _c(w, prec)
+
+        def vec(name):
+            return _c(np.reshape(t[name], -1), prec)
+
+        def act(prefix):
+            return (vec(prefix + ".alpha"), vec(prefix + ".beta") if self.beta else None)
+
+        p = "encoder"
+        self.conv_in = (fold(p + ".conv_in"), vec(p + ".conv_in.bias"))
+        self.blocks = []
+        for b, s in enumerate(reversed(cfg["strides"])):
+            q = f"{p}.blocks.{b}"
+            units = []
+            for r, d in enumerate(cfg["dilations"]):
+                u = f"{q}.res_units.{r}"
+                units.append(dict(d=d, act1=act(u + ".snake1"), w1=fold(u + ".conv1"),
+                                  b1=vec(u + ".conv1.bias"), act2=act(u + ".snake2"),
+                                  w2=fold(u + ".conv2"), b2=vec(u + ".conv2.bias")))
+            self.blocks.append(dict(s=s, units=units, act=act(q + ".snake"),
+                                    wd=fold(q + ".down"), bd=vec(q + ".down.bias")))
+        self.out = (act(p + ".snake_out"), fold(p + ".conv_out"), vec(p + ".conv_out.bias"))
+        self.proj = (fold(p + ".proj"), vec(p + ".proj.bias"))
+
+    def _op(self, y):
+        return _c(round_bf16(y), self.prec) if self.round_operands else y
+
+    def _snake(self, x, a):
+        return self._op(snake(x, a[0], a[1], self.prec))
+
+    def encode(self, audio):
+        """audio [B, 1, T*hop] -> posterior mean [B, C_latent, T]."""
+        x = np.asarray(audio, dtype=np.float32)
+        x = _c(round_bf16(x) if self.bf16 else x, self.prec)
+        h = conv1d(x, self.conv_in[0], self.conv_in[1], 1, self.prec)
+        for blk in self.blocks:
+            for u in blk["units"]:
+                v = conv1d(self._snake(h, u["act1"]), u["w1"], u["b1"], u["d"], self.prec)
+                h = add(h, conv1d(self._snake(v, u["act2"]), u["w2"], u["b2"], 1, self.prec), self.prec)
+            s = blk["s"]
+            h = conv1d_strided(self._snake(h, blk["act"]), blk["wd"], blk["bd"], s, s // 2, self.prec)
+        a, w, b = self.out
+        z = conv1d(self._snake(h, a), w, b, 1, self.prec)
+        return conv1d(self._op(z), self.proj[0], self.proj[1], 1, self.prec)
 
 
 def num_threads(prec: str = "f64") -> int:

@@ -41,6 +41,9 @@ MUTANTS = [
      "for (int64_t n = 0; n < Tout; ++n) yr[n] += 0;"),
     ("no_tanh", "y[k] = TANH(x[k]);", "y[k] = x[k];"),
     ("residual_sign", "y[k] = a[k] + b[k];", "y[k] = a[k] - b[k];"),
+    ("strided_conv_no_stride", "const int64_t src = t * s + j - P;", "const int64_t src = t + j - P;"),
+    ("strided_conv_pad_off_by_one", "const int64_t src = t * s + j - P;",
+     "const int64_t src = t * s + j - P + 1;"),
 ]
 
 
@@ -67,6 +70,9 @@ def _pins(orc):
     P.test_decode_matches_torch_composition(orc, (2, 2), "snake", 0, 0)
     P.test_decode_matches_torch_composition(orc, (3, 2), "snakebeta", 0, 0)
     P.test_golden_lengths_and_vocoder_gate(orc)
+    for s in (2, 8):
+        P.test_strided_conv_brute_force_and_torch(orc, s)
+    P.test_encoder_matches_torch_composition(orc, (8, 4))
 
 
 def test_pins_pass_on_the_real_oracle():
@@ -112,6 +118,13 @@ PY_MUTANTS = [
      "w, b, 1, self.prec, False)"),
     ("causal_conv_in_centered", "stage_conv_in", "return conv1d(x, w, b, 1, self.prec, self.causal)",
      "return conv1d(x, w, b, 1, self.prec, False)"),
+    ("encoder_strides_not_reversed", "Encoder.__init__", "enumerate(reversed(cfg[\"strides\"]))",
+     "enumerate(cfg[\"strides\"])"),
+    ("encoder_no_snake_before_down", "Encoder.encode",
+     "h = conv1d_strided(self._snake(h, blk[\"act\"]), blk[\"wd\"]",
+     "h = conv1d_strided(h, blk[\"wd\"]"),
+    ("encoder_proj_no_bias", "Encoder.encode", "self.proj[0], self.proj[1], 1, self.prec)",
+     "self.proj[0], None, 1, self.prec)"),
     ("in_proj_after_snake", "stage_conv_in", "x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec)",
      "x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec); "
      "x = snake(x, np.ones(x.shape[1]), None, self.prec)"),
@@ -119,6 +132,7 @@ PY_MUTANTS = [
 
 
 def _py_pins(orc):
+    P.test_encoder_matches_torch_composition(orc, (8, 4))
     P.test_decode_matches_torch_composition(orc, (2, 2), "snake", 5, 0)
     P.test_decode_matches_torch_composition(orc, (3, 2), "snakebeta", 0, 1)
     P.test_causal_decode_of_a_prefix_is_a_prefix(orc, (8, 5))
@@ -134,10 +148,11 @@ def test_python_pins_pass_on_the_real_oracle():
 
 @pytest.mark.parametrize("name,method,orig,bad", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
 def test_planted_python_mistake_is_caught(name, method, orig, bad, monkeypatch):
-    src = textwrap.dedent(inspect.getsource(getattr(O.Model, method)))
+    cls, meth = method.split(".") if "." in method else ("Model", method)
+    src = textwrap.dedent(inspect.getsource(getattr(getattr(O, cls), meth)))
     assert src.count(orig) == 1, f"mutation site not unique: {name}"
     ns = dict(vars(O))
     exec(compile(src.replace(orig, bad), f"<mutant {name}>", "exec"), ns)
-    monkeypatch.setattr(O.Model, method, ns[method])
+    monkeypatch.setattr(getattr(O, cls), meth, ns[meth])
     with pytest.raises(AssertionError):
         _py_pins(O)

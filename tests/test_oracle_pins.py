@@ -565,3 +565,67 @@ def test_causal_decode_of_a_prefix_is_a_prefix(orc, strides):
         np.testing.assert_array_equal(m.decode(lat[:, :, :n]), full[:, :, :n * hop])
     mc = orc.Model(tiny_cfg(strides=strides), t)
     assert np.abs(mc.decode(lat[:, :, :5]) - mc.decode(lat)[:, :, :5 * hop]).max() > 1e-6
+
+
+# ---------------------------------------------------------------- encoder
+@pytest.mark.parametrize("s", [2, 4, 8])
+def test_strided_conv_brute_force_and_torch(orc, s):
+    x = RNG.normal(0, 1, (2, 3, 8 * s))
+    w = RNG.normal(0, 1, (4, 3, 2 * s))
+    b = RNG.normal(0, 1, 4)
+    y = orc.conv1d_strided(x, w, b, s, s // 2)
+    assert y.shape == (2, 4, 8)                               # length T / s
+    ref = np.zeros_like(y)
+    for r in range(2):
+        for o in range(4):
+            for t in range(8):
+                acc = b[o]
+                for i in range(3):
+                    for j in range(2 * s):
+                        src = t * s + j - s // 2
+                        if 0 <= src < 8 * s:
+                            acc += w[o, i, j] * x[r, i, src]
+                ref[r, o, t] = acc
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+    tt = torch.nn.functional.conv1d(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b),
+                                    stride=s, padding=s // 2).numpy()
+    np.testing.assert_allclose(y, tt, rtol=1e-13, atol=1e-13)
+
+
+def torch_encode(cfg, t, audio):
+    """The encoder composed from PyTorch float64 CPU library routines."""
+    F = torch.nn.functional
+    T = {k: torch.from_numpy(v.astype(np.float64)) for k, v in t.items()}
+
+    def w(p):
+        v, g = T[p + ".weight_v"], T[p + ".weight_g"].reshape(-1)
+        n = v.reshape(v.shape[0], -1).norm(dim=1)
+        return v * (g / n).reshape(-1, 1, 1)
+
+    def sn(x, p):
+        a = T[p + ".alpha"].reshape(1, -1, 1)
+        return x + torch.sin(a * x) ** 2 / (a + 1e-9)
+
+    h = F.conv1d(torch.from_numpy(audio.astype(np.float64)), w("encoder.conv_in"),
+                 T["encoder.conv_in.bias"], padding=3)
+    for b, s in enumerate(reversed(cfg["strides"])):
+        q = f"encoder.blocks.{b}"
+        for r, d in enumerate(cfg["dilations"]):
+            u = f"{q}.res_units.{r}"
+            v = F.conv1d(sn(h, u + ".snake1"), w(u + ".conv1"), T[u + ".conv1.bias"],
+                         padding=3 * d, dilation=d)
+            h = h + F.conv1d(sn(v, u + ".snake2"), w(u + ".conv2"), T[u + ".conv2.bias"])
+        h = F.conv1d(sn(h, q + ".snake"), w(q + ".down"), T[q + ".down.bias"], stride=s, padding=s // 2)
+    z = F.conv1d(sn(h, "encoder.snake_out"), w("encoder.conv_out"), T["encoder.conv_out.bias"], padding=1)
+    return F.conv1d(z, w("encoder.proj"), T["encoder.proj.bias"]).numpy()
+
+
+@pytest.mark.parametrize("strides", [(2, 2), (8, 4)])
+def test_encoder_matches_torch_composition(orc, strides):
+    cfg = tiny_cfg(strides=strides)
+    cfg["enc_widths"] = (4, 6, 8)
+    t = I.make_weights(cfg, twin=True)
+    audio = I.make_audio(cfg, batch=2, frames=5)
+    z = orc.Encoder(cfg, t).encode(audio)
+    assert z.shape == (2, cfg["latent_channels"], 5)         # hop x fewer frames
+    np.testing.assert_allclose(z, torch_encode(cfg, t, audio), rtol=1e-11, atol=1e-11)
