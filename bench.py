@@ -7,7 +7,8 @@ weights and the output buffer already resident in HBM.  For the windowed
 workload one step is one vocoder_decode_windows call: every window of the
 song decoded as one batch and stitched into planar output.  For the
 streaming workload one step is one pass of every stream through the clip:
-a reset, then the clip's latent frames in fixed-size chunks.
+a reset, then the clip's latent frames in fixed-size chunks.  For the encode
+workload one step is one vocoder_encode of the audio batch.
 
 Prints ONE JSON line: audio-seconds decoded per second (value), whole-decode
 TFLOP/s, the roofline of the dominant kernel measured live with HIP events
@@ -34,7 +35,7 @@ METRIC = "audio-seconds decoded/sec (44.1 kHz stereo) + TFLOP/s as % of MFMA pea
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 KIND_NAMES = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused",
-              "in_proj"]
+              "in_proj", "enc_down", "enc_out"]
 KERNEL_SOURCES = ["dac_vocoder_decoding_amd/csrc/conv_gemm.hip",
                   "dac_vocoder_decoding_amd/csrc/fused_ru.hip",
                   "dac_vocoder_decoding_amd/csrc/gemm_common.h",
@@ -61,6 +62,12 @@ def workload_name(cfg: dict) -> str:
     if cfg.get("windows"):
         lat = (f"{cfg['windows']} windows [{cfg['batch']},{cfg['latent_channels']},{cfg['frames']}] "
                f"(last {cfg['last_frames']} frames), crops {cfg['crop'][0]}/{cfg['crop'][1]}, stitched")
+    if cfg.get("encode"):
+        ew = "/".join(str(x) for x in cfg["enc_widths"])
+        es = ",".join(str(x) for x in reversed(cfg["strides"]))
+        return (f"{cfg['name']}: audio [{cfg['batch']},1,{cfg['frames'] * cfg['hop']}] -> latent {lat} "
+                f"{cfg['dtype']}, encoder widths {ew}, strides {es}, conv_out k=3, projection to "
+                f"{cfg['latent_channels']}, {cfg['act']}")
     return (f"{cfg['name']}: latent {lat} {cfg['dtype']}, {proj}widths {w}, strides {s}, "
             f"{cfg['act']}{tile}")
 
@@ -89,20 +96,26 @@ def cpu_baseline(cfg: dict, tensors: dict, latent, target_s: float = 15.0,
     from dac_vocoder_decoding_amd import inputs as I
     from oracle import oracle as O
     rows = 2 if cfg["stereo"] else 1
-    model = O.Model(cfg, tensors)
+    hop = cfg["hop"]
+    if cfg.get("encode"):   # `latent` is the audio [B, 1, T*hop]
+        enc = O.Encoder(cfg, tensors)
+        run = lambda n: enc.encode(latent[:rows, :, :n * hop])   # noqa: E731
+    else:
+        model = O.Model(cfg, tensors)
+        run = lambda n: model.decode(latent[:rows, :, :n])       # noqa: E731
     t0 = time.perf_counter()
-    model.decode(latent[:rows, :, :4])
+    run(4)
     t4 = time.perf_counter() - t0
     frames = int(max(4, min(cfg["frames"], round(4 * target_s / max(t4, 1e-3)))))
     t0 = time.perf_counter()
-    model.decode(latent[:rows, :, :frames])
+    run(frames)
     wall = time.perf_counter() - t0
     secs = I.audio_seconds(cfg, rows, frames)
     note = "" if kept_frac == 1.0 else (f"; rate x {kept_frac:.4f}, the share of decoded window "
                                         "frames that the stitching keeps")
     return {"value": secs / wall * kept_frac, "unit": "audio-s/s", "cores": O.num_threads(),
             "kind": "oracle",
-            "sample": f"{rows} row(s) x {frames} latent frames of the same latent "
+            "sample": f"{rows} row(s) x {frames} latent frames of the same input "
                       f"({secs:.3f} audio-s) decoded by the fp64 oracle in {wall:.2f} s{note}"}
 
 
@@ -137,7 +150,19 @@ def main() -> int:
     ctx = V.open_context(cfg, tensors, device=0)
     stream = torch.cuda.current_stream()
     sides = 2 if cfg["stereo"] else 1
-    if cfg.get("windows"):
+    if cfg.get("encode"):
+        audio_np = I.make_audio(cfg)
+        B, T = cfg["batch"], cfg["frames"]
+        latent_np = audio_np                       # the CPU-baseline sample (audio)
+        audio = torch.from_numpy(audio_np).to(dev)
+        pcm = torch.empty(B, cfg["latent_channels"], T, device=dev)
+        secs = I.audio_seconds(cfg, B, T)
+        flops = I.encode_flops(cfg, B, T)
+        kept_frac = 1.0
+
+        def step():
+            V.check(V.vocoder_encode(ctx, audio, B, T, pcm, stream), ctx)
+    elif cfg.get("windows"):
         win_np = I.make_windows(cfg)
         n, L, last, (cl, cr) = cfg["windows"], cfg["frames"], cfg["last_frames"], cfg["crop"]
         latent_np = win_np[0].reshape(sides, cfg["latent_channels"], L)  # CPU-baseline sample
@@ -240,7 +265,7 @@ def main() -> int:
     value = secs / (ms_per_step / 1e3)
     tflops = flops / (ms_per_step / 1e3) / 1e12
     peak = PEAK_TFLOPS[cfg["dtype"]]
-    ok = bool(torch.isfinite(pcm).all().item()) and float(pcm.abs().max()) <= 1.0
+    ok = bool(torch.isfinite(pcm).all().item()) and (cfg.get("encode") or float(pcm.abs().max()) <= 1.0)
 
     roofline = None
     per_kernel = {}

@@ -3,7 +3,14 @@
 // One kernel template serves every convolution of the decoder:
 //   * Conv1d k=7 at dilation d (conv_in, residual conv1): 7 taps at frame
 //     offsets j*d - 3d;
-//   * Conv1d k=1 (residual conv2): 1 tap;
+//   * Conv1d k=1 (residual conv2, dec_in_proj, the encoder's projection):
+//     1 tap;
+//   * Conv1d k=3 (the encoder's conv_out): 3 taps at offsets -1, 0, 1;
+//   * the encoder's strided Conv1d k=2s, stride s, pad s/2 (minimaxmusic.cpp
+//     ARCHITECTURE, "Flow VAE"): with x_p[m] = x[m*s + p] the output is
+//     y[n] = sum_p sum_{q=-1..1} w[q*s + p + s/2] x_p[n + q] (terms with a
+//     kernel index outside [0, 2s) are zero), i.e. a 3-tap conv over s*C
+//     phase channels read with an input row stride of s;
 //   * ConvTranspose1d k=2s stride s as a polyphase GEMM: output phase r of
 //     input frame q is x[q] w[:, :, r] + x[q-1] w[:, :, s+r], i.e. 2 taps at
 //     offsets 0 and -1 with M = s*Cout rows m = r*Cout + o.  The transposed
@@ -85,7 +92,11 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   if (n0 * a.ups - a.crop >= Lout) return;
 
   const int tfirst = n0 + a.min_off;
-  const int nchunks = a.Cin / CH;
+  // A strided conv (stride S) reads its input as S phase streams per
+  // channel chunk: virtual chunk c is phase c % S of chunk c / S, whose frame
+  // m is input row m * S + c % S.  S = 1 is the plain conv.
+  const int S = a.in_stride > 1 ? a.in_stride : 1;
+  const int nchunks = a.Cin / CH * S;
   const unsigned char* xrow = static_cast<const unsigned char*>(a.x) +
                               static_cast<int64_t>(row) * a.Cin * a.T_in * ES;
   const int64_t xplane = static_cast<int64_t>(a.T_in) * kChunkBytes;
@@ -106,18 +117,19 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   const uint32_t smem_lds = lds_addr(smem);
   // Frames in [-lb, 0) are read from memory (a stream's carried context);
   // the buffer resource then starts lb frames before frame 0.
-  const uint32_t xv0 = static_cast<uint32_t>((tfirst + a.lb + lr) * kChunkBytes + lg * 16);
+  const uint32_t xv0 = static_cast<uint32_t>(((tfirst + lr) * S + a.lb) * kChunkBytes + lg * 16);
   const uint32_t wv0 = static_cast<uint32_t>((m0 + lr) * kChunkBytes + lg * 16);
   auto issue = [&](int c, int stage) {
-    const i4 xs = buf_rsrc(xrow + c * xplane - static_cast<int64_t>(a.lb) * kChunkBytes,
+    const i4 xs = buf_rsrc(xrow + (c / S) * xplane - static_cast<int64_t>(a.lb) * kChunkBytes,
                            static_cast<uint32_t>(Lin + a.lb) * kChunkBytes);
+    const uint32_t xv = xv0 + static_cast<uint32_t>((c % S) * kChunkBytes);
     const i4 ws = buf_rsrc(wbase + c * wplane, static_cast<uint32_t>(wplane));
     const uint32_t dst = smem_lds + stage * STAGE;
 #pragma unroll
     for (int u = 0; u < (TB + 3) / 4; ++u) {
       const int b = wave + 4 * u;
       if (b < XB) {
-        dma16(xs, xv0 + b * 1024, dst + b * 1024);
+        dma16(xs, xv + b * 1024 * S, dst + b * 1024);
       } else if (b < TB) {
         const int k = b - XB, j = (16 * k) / BM;
         dma16(ws, wv0 + (j * a.M + 16 * k - j * BM) * kChunkBytes, dst + b * 1024);
@@ -163,12 +175,13 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
     const int xrows = BN + a.halo;
     uint4 xr[XU], wr[WU];
     auto gload = [&](int c) {
-      const unsigned char* xc = xrow + c * xplane;
+      const unsigned char* xc = xrow + (c / S) * xplane;
+      const int ph = c % S;
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
         const int idx = tid + u * 256;
         const int r = unit_row(idx), col = unit_col(idx);
-        const int t = tfirst + r;
+        const int t = (tfirst + r) * S + ph;  // input row
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (r < xrows && t >= -a.lb && t < Lin)
           v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
@@ -394,7 +407,7 @@ int conv_variant_bn(int v) { return kVariants[v].wav_n * kVariants[v].wnb * 16; 
 bool conv_variant_ok(int v, int taps) {
   if (v < 0 || v >= CV_COUNT) return false;
   // All taps' weight rows of a chunk live in LDS: keep two workgroups per CU.
-  if (taps == 7) return v == CV_64x256 || v == CV_96x256 || v == CV_64x128;
+  if (taps == 7 || taps == 3) return v == CV_64x256 || v == CV_96x256 || v == CV_64x128;
   return true;
 }
 
@@ -409,7 +422,7 @@ bool conv_variant_ok(int v, int taps) {
 #endif
 template <int OP, int TAPS> struct Stages {
   static constexpr int f[3] = {VOC_NS_F32}, b[3] = {VOC_NS_BF16};
-  static constexpr int v = (OP == OP_F32 ? f : b)[TAPS == 7 ? 0 : TAPS == 2 ? 1 : 2];
+  static constexpr int v = (OP == OP_F32 ? f : b)[TAPS == 7 ? 0 : TAPS == 1 ? 2 : 1];  // 2 and 3 taps alike
 };
 
 template <int OP, int TAPS, int TAG>
@@ -428,7 +441,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 #undef VOC_CASE
 #define VOC_CASE(V, A, B, C, D)                                                              \
   case V:                                                                                    \
-    if constexpr (TAPS != 7) {                                                               \
+    if constexpr (TAPS == 1 || TAPS == 2) {                                                  \
       hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS>), grid, block, 0, s, a); \
       break;                                                                                 \
     }                                                                                        \
@@ -449,6 +462,7 @@ static hipError_t launch_op(int taps, int variant, bool input_layer, const ConvA
     case 7:
       return input_layer ? launch_taps<OP, 7, 1>(variant, a, s) : launch_taps<OP, 7, 0>(variant, a, s);
     case 2: return launch_taps<OP, 2, 0>(variant, a, s);
+    case 3: return launch_taps<OP, 3, 0>(variant, a, s);
     case 1:
       return input_layer ? launch_taps<OP, 1, 1>(variant, a, s) : launch_taps<OP, 1, 0>(variant, a, s);
     default: return hipErrorInvalidValue;

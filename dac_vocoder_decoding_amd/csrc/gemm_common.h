@@ -93,6 +93,7 @@ __device__ __forceinline__ void mma_steps(f4 (&acc)[WMB][WNB], int nt, FA a_at, 
 template <int TAPS> struct HaloMax { static constexpr int v = 0; };
 template <> struct HaloMax<7> { static constexpr int v = 54; };  // 6 * dilation 9
 template <> struct HaloMax<2> { static constexpr int v = 1; };
+template <> struct HaloMax<3> { static constexpr int v = 2; };   // k=3, or a strided conv's 3 frame groups
 
 // LDS tiles hold rows of one 64-byte channel chunk in blocks of 16 rows.
 // Inside a block the four 16-byte units of a row are stored unit-major:

@@ -68,6 +68,8 @@ struct ConvArgs {
   const float* hs_h;      // parameters instead of v (the head's Snake)
   int T_out, ups, crop;
   int lb;         // frames in [-lb, 0) of x are read from memory (a stream's context), else zero
+  int in_stride;  // > 1: strided conv; GEMM frame m of virtual chunk c reads input row
+                  // m * in_stride + c % in_stride of chunk c / in_stride (Cin counts real channels)
 };
 
 // Tile shape families of the conv GEMM kernel.
@@ -128,7 +130,7 @@ bool res_unit_from_h_ok(int op, int C);
 hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s);
 
 // Weight-norm fold + cast + repack, one workgroup per axis-0 slice.
-enum PackKind { PACK_CONV = 0, PACK_CONVT = 1, PACK_HEAD = 2 };
+enum PackKind { PACK_CONV = 0, PACK_CONVT = 1, PACK_HEAD = 2, PACK_DOWN = 3 };
 struct FoldArgs {
   const float* v;
   const float* g;   // null: no weight norm (w = v)
@@ -162,6 +164,9 @@ struct ImportArgs {
   const float* h_h;
 };
 hipError_t launch_import(const ImportArgs& a, hipStream_t s);
+
+// Mono audio x fp32 [rows][T] -> operand [rows][1][T][CH] with channel 0 = x.
+hipError_t launch_audio_import(int op, const float* x, void* out, int64_t T, int rows, hipStream_t s);
 
 // h fp32 chunked [rows][C/16][T][16] -> y fp32 [rows][C][T].
 hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipStream_t s);

@@ -31,6 +31,8 @@ struct ConvDev {
   void* w = nullptr;
   float* bias = nullptr;
   int cin = 0, cout = 0, taps = 0, dil = 1, ups = 1, crop = 0, M = 0;
+  int causal = 0;  // k=7: left padding (K-1)*d instead of "same"
+  int down = 1;    // > 1: strided conv (k = 2*down, stride down, pad down/2) as 3 taps
 };
 struct UnitDev {
   SnakeDev a1, a2;
@@ -41,7 +43,19 @@ struct BlockDev {
   ConvDev ct;
   std::vector<UnitDev> units;
 };
+struct EncBlockDev {
+  std::vector<UnitDev> units;
+  SnakeDev act;     // Snake ahead of the strided conv
+  ConvDev down;
+};
+struct EncoderDev {
+  ConvDev conv_in;  // 1 input channel, packed as one zero-padded chunk
+  std::vector<EncBlockDev> blocks;
+  SnakeDev out_act;
+  ConvDev conv_out, proj;
+};
 struct Weights {
+  EncoderDev enc;   // (enc.conv_in.cout == 0: no encoder)
   ConvDev in_proj;  // dec_in_proj (cout == 0: none)
   ConvDev conv_in;
   std::vector<BlockDev> blocks;
@@ -80,7 +94,7 @@ struct voc_ctx {
   voc_profile_stat stats[VOC_K_COUNT]{};
   // cached row metadata of the last decode
   std::vector<int64_t> rows_key;  // what the uploaded metadata describes (empty: nothing)
-  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
+  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
@@ -141,6 +155,14 @@ voc_status validate(const voc_config* c, std::string* why) {
   if (c->in_proj < 0 || c->in_proj % q || c->in_proj > 8192)
     return bad("in_proj must be 0 or a positive multiple of 16 (F32) / 32 (BF16), at most 8192");
   if (c->causal != 0 && c->causal != 1) return bad("causal must be 0 or 1");
+  if (c->enc_width[0] != 0) {
+    for (int b = 0; b <= c->n_blocks; ++b)
+      if (c->enc_width[b] <= 0 || c->enc_width[b] % q || c->enc_width[b] > 8192)
+        return bad("encoder widths must be positive multiples of 16 (F32) / 32 (BF16), at most 8192");
+    for (int b = 0; b < c->n_blocks; ++b)
+      if (c->stride[b] % 2) return bad("an encoder needs even strides (pad s/2)");
+    if (c->causal) return bad("the encoder is not causal");
+  }
   for (int b = 0; b <= c->n_blocks; ++b)
     if (c->width[b] <= 0 || c->width[b] % q || c->width[b] > 8192)
       return bad("widths must be positive multiples of 16 (F32) / 32 (BF16), at most 8192");
@@ -309,6 +331,36 @@ Plan make_plan(const voc_ctx* c, int rows, int T, int mg = 0) {
   return p;
 }
 
+// The encoder's workspace: the audio as a one-chunk operand, then the same
+// activation buffers as a decode, sized for the encoder's widths and rates.
+Plan make_enc_plan(const voc_ctx* c, int rows, int T) {
+  const voc_config& g = c->cfg;
+  const size_t es = op_size(c->op);
+  int64_t t = T * c->hop;
+  size_t max_act = static_cast<size_t>(g.latent_channels) * T;
+  bool xh = false;
+  for (int b = 0; b <= g.n_blocks; ++b) {
+    max_act = std::max<size_t>(max_act, static_cast<size_t>(g.enc_width[b]) * t);
+    if (b < g.n_blocks) {
+      xh = xh || unit_xh(c, g.enc_width[b]);
+      t /= g.stride[g.n_blocks - 1 - b];
+    }
+  }
+  Plan p{};
+  p.rows = rows;
+  p.T = T;
+  size_t o = 0;
+  p.off_xlat = o; o = align_up(o + static_cast<size_t>(rows) * T * c->hop * kChunkBytes);
+  p.off_h = o;    o = align_up(o + 4 * rows * max_act);
+  p.off_h2 = o;   if (xh) o = align_up(o + 4 * rows * max_act);
+  p.off_s0 = o;   o = align_up(o + es * rows * max_act);
+  p.off_s1 = o;   o = align_up(o + es * rows * max_act);
+  p.off_u = o;    o = align_up(o + es * rows * max_act);
+  p.off_meta = o; o = align_up(o + static_cast<size_t>(rows) * (5 * sizeof(int) + sizeof(int64_t)) + 64);
+  p.bytes = o;
+  return p;
+}
+
 voc_status ensure_ws(voc_ctx* c, size_t bytes) {
   if (bytes <= c->ws_bytes) return VOC_OK;
   if (c->ws_cap && bytes > c->ws_cap)
@@ -431,7 +483,8 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.Cin = L.cin;
   a.row_len = row_len;
   a.rate_in = io.rate_in;
-  a.rate_out = io.rate_in * L.ups;
+  a.rate_out = L.down > 1 ? io.rate_in / L.down : io.rate_in * L.ups;
+  a.in_stride = L.down;
   a.w = L.w;
   a.M = L.M;
   a.Cout = L.cout;
@@ -442,14 +495,16 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
     a.halo = 1;
     a.N = io.T_in + (L.crop > 0 ? 1 : 0);  // a left crop shifts the last outputs to n = T_in
   } else {  // taps at x[n + j*dil - P]: "same" P = (taps-1)/2*dil, causal P = (taps-1)*dil
-    const int P = (c->cfg.causal ? L.taps - 1 : (L.taps - 1) / 2) * L.dil;
+    // (a strided conv: 3 taps at frame groups n-1, n, n+1 of its phase streams)
+    const int P = (L.causal ? L.taps - 1 : (L.taps - 1) / 2) * L.dil;
     a.off0 = -P;
     a.offstep = L.dil;
     a.min_off = -P;
     a.halo = (L.taps - 1) * L.dil;
-    a.N = io.T_in;
+    a.N = io.T_in / L.down;
   }
-  a.T_out = io.T_in * L.ups + c->mg;
+  const int t_out = L.down > 1 ? io.T_in / L.down : io.T_in * L.ups;
+  a.T_out = t_out + c->mg;
   a.ups = L.ups;
   a.crop = L.crop;
   // A stream chunk reads its carried context: x[n - 1] for the transposed
@@ -471,14 +526,16 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.m_tiles = (a.M + conv_variant_bm(v) - 1) / conv_variant_bm(v);
   // Weights of at most 2 MB stay resident in a 4 MB XCD L2 next to the
   // activation tiles, so the M-tiles of one N-range can run together.
-  const double wbytes = static_cast<double>(L.taps) * L.M * L.cin * op_size(c->op);
+  const double wbytes = static_cast<double>(L.taps) * L.M * L.cin * L.down * op_size(c->op);
   a.m_fast = c->m_order >= 0 ? c->m_order : (a.m_tiles > 1 && wbytes <= 2.0 * (1 << 20));
-  // Algorithmic work: every input frame meets every tap (direct convolution).
+  // Algorithmic work: every input frame meets every tap (direct convolution;
+  // a strided conv: every output frame meets its 2s taps).
   const double frames_in = static_cast<double>(rows) * io.T_in;
-  const double flops = 2.0 * frames_in * L.cin * L.cout * (L.taps == 2 ? 2 * L.ups : L.taps);
+  const double frames_out = static_cast<double>(rows) * t_out;
+  const double flops = L.down > 1 ? 2.0 * frames_out * L.cin * L.cout * 2 * L.down
+                                  : 2.0 * frames_in * L.cin * L.cout * (L.taps == 2 ? 2 * L.ups : L.taps);
   const double es = op_size(c->op);
-  const double frames_out = frames_in * L.ups;
-  double bytes = frames_in * L.cin * es + static_cast<double>(L.taps) * L.M * L.cin * es;
+  double bytes = frames_in * L.cin * es + wbytes;
   if (io.h_out) bytes += frames_out * L.cout * 4;
   if (io.res) bytes += frames_out * L.cout * 4;
   if (io.s_out) bytes += frames_out * L.cout * es;
@@ -574,7 +631,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     a.row_len = row_len;
     a.rate = rate;
     a.dil = u.c1.dil;
-    a.pad = (c->cfg.causal ? 6 : 3) * u.c1.dil;
+    a.pad = (u.c1.causal ? 6 : 3) * u.c1.dil;
     a.lb = c->st_active ? a.pad : 0;
     a.w1 = u.c1.w;
     a.b1 = u.c1.bias;
@@ -771,6 +828,25 @@ std::map<std::string, Expect> expected_tensors(const voc_config& g) {
   }
   snake("snake_out", g.width[g.n_blocks]);
   conv("conv_out", 1, g.width[g.n_blocks], 7, 1);
+  if (g.enc_width[0] > 0) {  // the encoder: decoder strides in reverse order
+    const int* E = g.enc_width;
+    conv("encoder.conv_in", E[0], 1, 7, E[0]);
+    for (int b = 0; b < g.n_blocks; ++b) {
+      const std::string q = "encoder.blocks." + std::to_string(b);
+      for (int r = 0; r < g.n_res; ++r) {
+        const std::string u = q + ".res_units." + std::to_string(r);
+        snake(u + ".snake1", E[b]);
+        conv(u + ".conv1", E[b], E[b], 7, E[b]);
+        snake(u + ".snake2", E[b]);
+        conv(u + ".conv2", E[b], E[b], 1, E[b]);
+      }
+      snake(q + ".snake", E[b]);
+      conv(q + ".down", E[b + 1], E[b], 2 * g.stride[g.n_blocks - 1 - b], E[b + 1]);
+    }
+    snake("encoder.snake_out", E[g.n_blocks]);
+    conv("encoder.conv_out", E[g.n_blocks], E[g.n_blocks], 3, E[g.n_blocks]);
+    conv("encoder.proj", g.latent_channels, E[g.n_blocks], 1, g.latent_channels);
+  }
   return m;
 }
 
@@ -928,8 +1004,9 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
   };
   // Fold one conv: v is uploaded to a staging buffer, folded into the packed layout.
   // plain: the tensor is p.weight, used as stored (no weight norm).
+  // cin_alloc > cin: packed with cin_alloc input channels, the extra ones zero.
   auto fold = [&](const std::string& p, int kind, int cin, int cout, int k, int stride,
-                  void** out_w, float** out_bias, bool plain = false) -> voc_status {
+                  void** out_w, float** out_bias, bool plain = false, int cin_alloc = 0) -> voc_status {
     const voc_tensor* tv = got[plain ? p + ".weight" : p + ".weight_v"];
     const int64_t cnt = numel(*tv);
     const int64_t d0 = kind == PACK_CONVT ? cin : cout;
@@ -946,8 +1023,15 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     W.allocs.pop_back();
     staging.push_back(dn);
     const size_t es = kind == PACK_HEAD ? 4 : op_size(op);
-    st = dalloc(cnt * es, out_w);
+    size_t out_elems = static_cast<size_t>(cnt);
+    if (kind == PACK_DOWN) out_elems = static_cast<size_t>(cout) * cin * 3 * stride;  // 3 taps x s phases
+    if (cin_alloc > cin) out_elems = static_cast<size_t>(cout) * k * cin_alloc;
+    st = dalloc(out_elems * es, out_w);
     if (st) return st;
+    if (out_elems != static_cast<size_t>(cnt)) {  // entries no weight maps to stay zero
+      hipError_t e = hipMemset(*out_w, 0, out_elems * es);
+      if (e != hipSuccess) return hip_fail(c, e, "weight clear");
+    }
     FoldArgs fa{};
     fa.v = dv;
     fa.g = dg;
@@ -986,6 +1070,7 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     ci.cin = g.in_proj > 0 ? g.in_proj : g.latent_channels;
     ci.cout = ci.M = g.width[0];
     ci.taps = 7;
+    ci.causal = g.causal;
     st = fold("conv_in", PACK_CONV, ci.cin, ci.cout, 7, 1, &ci.w, &ci.bias);
     if (st) return st;
     W.blocks.resize(g.n_blocks);
@@ -1014,6 +1099,7 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
         u.c1.cin = u.c1.cout = u.c1.M = cout;
         u.c1.taps = 7;
         u.c1.dil = g.dilation[r];
+        u.c1.causal = g.causal;
         st = fold(q + ".conv1", PACK_CONV, cout, cout, 7, 1, &u.c1.w, &u.c1.bias);
         if (st) return st;
         u.c2.cin = u.c2.cout = u.c2.M = cout;
@@ -1029,6 +1115,59 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     if (st) return st;
     W.head_w = static_cast<float*>(hw);
     W.head_bias = got["conv_out.bias"]->data[0];
+    if (g.enc_width[0] > 0) {
+      const int* E = g.enc_width;
+      const int CHn = op_chunk(op);
+      EncoderDev& en = W.enc;
+      en.conv_in.cin = CHn;  // one real channel in a zero-padded chunk
+      en.conv_in.cout = en.conv_in.M = E[0];
+      en.conv_in.taps = 7;
+      st = fold("encoder.conv_in", PACK_CONV, 1, E[0], 7, 1, &en.conv_in.w, &en.conv_in.bias, false, CHn);
+      if (st) return st;
+      en.blocks.resize(g.n_blocks);
+      for (int b = 0; b < g.n_blocks; ++b) {
+        const std::string q = "encoder.blocks." + std::to_string(b);
+        EncBlockDev& eb = en.blocks[b];
+        eb.units.resize(g.n_res);
+        for (int r = 0; r < g.n_res; ++r) {
+          const std::string u = q + ".res_units." + std::to_string(r);
+          UnitDev& ud = eb.units[r];
+          st = snake(u + ".snake1", E[b], &ud.a1);
+          if (!st) st = snake(u + ".snake2", E[b], &ud.a2);
+          if (st) return st;
+          ud.c1.cin = ud.c1.cout = ud.c1.M = E[b];
+          ud.c1.taps = 7;
+          ud.c1.dil = g.dilation[r];
+          st = fold(u + ".conv1", PACK_CONV, E[b], E[b], 7, 1, &ud.c1.w, &ud.c1.bias);
+          if (st) return st;
+          ud.c2.cin = ud.c2.cout = ud.c2.M = E[b];
+          ud.c2.taps = 1;
+          st = fold(u + ".conv2", PACK_CONV, E[b], E[b], 1, 1, &ud.c2.w, &ud.c2.bias);
+          if (st) return st;
+        }
+        st = snake(q + ".snake", E[b], &eb.act);
+        if (st) return st;
+        const int sb = g.stride[g.n_blocks - 1 - b];
+        eb.down.cin = E[b];
+        eb.down.cout = eb.down.M = E[b + 1];
+        eb.down.taps = 3;
+        eb.down.down = sb;
+        st = fold(q + ".down", PACK_DOWN, E[b], E[b + 1], 2 * sb, sb, &eb.down.w, &eb.down.bias);
+        if (st) return st;
+      }
+      const int En = E[g.n_blocks];
+      st = snake("encoder.snake_out", En, &en.out_act);
+      if (st) return st;
+      en.conv_out.cin = en.conv_out.cout = en.conv_out.M = En;
+      en.conv_out.taps = 3;
+      st = fold("encoder.conv_out", PACK_CONV, En, En, 3, 1, &en.conv_out.w, &en.conv_out.bias);
+      if (st) return st;
+      en.proj.cin = En;
+      en.proj.cout = en.proj.M = g.latent_channels;
+      en.proj.taps = 1;
+      st = fold("encoder.proj", PACK_CONV, En, g.latent_channels, 1, 1, &en.proj.w, &en.proj.bias);
+      if (st) return st;
+    }
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(c, e, "fold");
     for (size_t i = 0; i < norm_bufs.size(); ++i) {
@@ -1145,6 +1284,119 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
     }
   return decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {0, B, T, rows}, pcm,
                      static_cast<hipStream_t>(stream));
+}
+
+VOC_API voc_status vocoder_encode(voc_ctx* c, const float* audio, int64_t B, int64_t T, float* latent,
+                                  void* stream) {
+  if (!c) return VOC_INVALID_PARAMS;
+  const voc_config& g = c->cfg;
+  if (g.enc_width[0] == 0) return fail(c, VOC_INVALID_PARAMS, "no encoder configured (enc_width)");
+  if (!audio || !latent) return fail(c, VOC_INVALID_PARAMS, "NULL audio or latent");
+  if ((reinterpret_cast<uintptr_t>(audio) | reinterpret_cast<uintptr_t>(latent)) & 15)
+    return fail(c, VOC_INVALID_PARAMS, "audio and latent must be 16-byte aligned");
+  if (B <= 0 || T <= 0 || B > 65535) return fail(c, VOC_INVALID_PARAMS, "B in [1, 65535] and T > 0 required");
+  if (T * c->hop > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "T*hop exceeds 2^31-1");
+  if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rows = static_cast<int>(B), nb = g.n_blocks, nr = g.n_res;
+  const int* E = g.enc_width;
+  const EncoderDev& en = c->W.enc;
+  const Plan p = make_enc_plan(c, rows, static_cast<int>(T));
+  voc_status st = ensure_ws(c, p.bytes);
+  if (st) return st;
+  const std::vector<int64_t> key = {4, B, T};
+  if (c->rows_key != key) {
+    std::vector<int64_t> dst(rows);
+    std::vector<int> ints(5 * rows);
+    for (int r = 0; r < rows; ++r) {
+      ints[r] = static_cast<int>(T);                       // len (latent frames)
+      ints[rows + r] = r;                                  // src_b
+      ints[2 * rows + r] = 0;                              // start
+      ints[3 * rows + r] = 0;                              // keep_lo
+      ints[4 * rows + r] = static_cast<int>(T * c->hop);   // keep_hi
+      dst[r] = r * T * c->hop;
+    }
+    st = upload_rows(c, p, std::move(dst), std::move(ints), s);
+    if (st) return st;
+    c->rows_key = key;
+  }
+  const Bufs Bf = bufs(c, p);
+  const int* len = Bf.rows.len;
+  int64_t t = T * c->hop;
+  int rate = static_cast<int>(c->hop);
+  const int op = c->op;
+  st = launch(c, s, VOC_K_IMPORT, 0.0, static_cast<double>(rows) * t * (4 + kChunkBytes), "audio import launch",
+              [&] { return launch_audio_import(op, audio, Bf.xlat, t, rows, s); });
+  if (st) return st;
+  // conv_in -> h and (unless the first unit takes it from h) its Snake1 operand.
+  int cur = 0;
+  float* hc = Bf.h;
+  float* ho = Bf.h2;
+  ConvIO io{};
+  io.x = Bf.xlat;
+  io.T_in = static_cast<int>(t);
+  io.rate_in = rate;
+  io.h_out = hc;
+  if (!unit_xh(c, E[0])) {
+    io.s_out = Bf.s[cur];
+    io.snake_next = &en.blocks[0].units[0].a1;
+  }
+  st = run_conv(c, en.conv_in, io, rows, len, VOC_K_CONV_IN, s);
+  if (st) return st;
+  for (int b = 0; b < nb; ++b) {
+    const EncBlockDev& eb = en.blocks[b];
+    const bool xh = unit_xh(c, E[b]);
+    for (int r = 0; r < nr; ++r) {
+      // The last unit feeds the strided conv only through the block Snake.
+      const bool keep_h = r + 1 < nr;
+      const SnakeDev* next = keep_h ? (xh ? nullptr : &eb.units[r + 1].a1) : &eb.act;
+      void* s_next = nullptr;
+      st = run_res_unit(c, eb.units[r], xh ? nullptr : Bf.s[cur], Bf.s[cur ^ 1], Bf.u, hc, xh ? ho : nullptr,
+                        next, &s_next, static_cast<int>(t), rate, rows, len, s, nullptr, keep_h);
+      if (st) return st;
+      if (s_next == Bf.s[cur ^ 1]) cur ^= 1;
+      if (xh && keep_h) std::swap(hc, ho);
+    }
+    // Strided conv on Snake(h) -> the next block's h and first operand (the
+    // last block: Snake_out of it, conv_out's operand).
+    io = ConvIO{};
+    io.x = Bf.s[cur];
+    io.T_in = static_cast<int>(t);
+    io.rate_in = rate;
+    if (b + 1 < nb) {
+      io.h_out = hc;
+      if (!unit_xh(c, E[b + 1])) {
+        io.s_out = Bf.s[cur ^ 1];
+        io.snake_next = &en.blocks[b + 1].units[0].a1;
+      }
+    } else {
+      io.s_out = Bf.s[cur ^ 1];
+      io.snake_next = &en.out_act;
+    }
+    st = run_conv(c, eb.down, io, rows, len, VOC_K_ENC_DOWN, s);
+    if (st) return st;
+    if (io.s_out) cur ^= 1;
+    t /= eb.down.down;
+    rate /= eb.down.down;
+  }
+  // conv_out (k=3) -> its output as the projection's operand (no activation).
+  io = ConvIO{};
+  io.x = Bf.s[cur];
+  io.T_in = static_cast<int>(t);
+  io.rate_in = rate;
+  io.s_out = Bf.u;
+  st = run_conv(c, en.conv_out, io, rows, len, VOC_K_ENC_OUT, s);
+  if (st) return st;
+  io = ConvIO{};
+  io.x = Bf.u;
+  io.T_in = static_cast<int>(t);
+  io.rate_in = rate;
+  io.h_out = hc;
+  st = run_conv(c, en.proj, io, rows, len, VOC_K_ENC_OUT, s);
+  if (st) return st;
+  const int C = g.latent_channels;
+  return launch(c, s, VOC_K_EXPORT, 0.0, 8.0 * rows * C * T, "export launch",
+                [&] { return launch_export(hc, latent, rows, C, static_cast<int>(T), s); });
 }
 
 namespace {

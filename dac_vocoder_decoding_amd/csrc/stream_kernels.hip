@@ -46,6 +46,15 @@ __global__ __launch_bounds__(256) void fold_kernel(const FoldArgs a) {
     if (a.kind == PACK_CONV) {  // (Cout, Cin, K), slice = o
       const int ci = static_cast<int>(e / a.k), kk = static_cast<int>(e % a.k);
       idx = ((static_cast<int64_t>(ci / ch) * a.k + kk) * a.cout + i) * ch + ci % ch;
+    } else if (a.kind == PACK_DOWN) {  // strided conv (Cout, Cin, 2s), slice = o
+      // Kernel index j = q*s + p + s/2 - s (q in 0..2) of phase p: virtual
+      // chunk (ci / ch) * s + p, tap q (the strided form in conv_gemm.hip).
+      const int ci = static_cast<int>(e / a.k), j = static_cast<int>(e % a.k);
+      const int jj = j - a.stride / 2;  // in [-s/2, 3s/2)
+      const int qm = jj >= 0 ? jj / a.stride : -1;
+      const int ph = jj - qm * a.stride, q = qm + 1;
+      const int64_t vc = static_cast<int64_t>(ci / ch) * a.stride + ph;
+      idx = ((vc * 3 + q) * a.cout + i) * ch + ci % ch;
     } else if (a.kind == PACK_CONVT) {  // (Cin, Cout, 2s), slice = ci
       const int o = static_cast<int>(e / (2 * a.stride));
       const int kk = static_cast<int>(e % (2 * a.stride));
@@ -134,6 +143,38 @@ hipError_t launch_import(const ImportArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(import_kernel<OP_F32>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(import_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------- audio import
+// Mono audio rows [src][T] -> an operand tensor of one 64-byte channel chunk
+// per frame whose channel 0 is the sample and the others zero (the
+// encoder's conv_in has one input channel; its packed weights are zero past
+// channel 0).
+template <int OP>
+__global__ __launch_bounds__(256) void audio_import_kernel(const float* x, void* out, int64_t T, int rows) {
+  const int64_t total = static_cast<int64_t>(rows) * T;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    uint4* row = reinterpret_cast<uint4*>(static_cast<unsigned char*>(out) + i * kChunkBytes);
+    uint4 first = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (OP == OP_F32)
+      first.x = __float_as_uint(x[i]);
+    else
+      first.x = pack_bf16x2(x[i], 0.f);
+    row[0] = first;
+    row[1] = row[2] = row[3] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+hipError_t launch_audio_import(int op, const float* x, void* out, int64_t T, int rows, hipStream_t s) {
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((rows * T + 255) / 256, 4096));
+  if (op == OP_F32)
+    hipLaunchKernelGGL(audio_import_kernel<OP_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, x,
+                       out, T, rows);
+  else
+    hipLaunchKernelGGL(audio_import_kernel<OP_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, x,
+                       out, T, rows);
   return hipGetLastError();
 }
 

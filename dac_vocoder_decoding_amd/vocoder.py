@@ -32,7 +32,7 @@ VOC_F32, VOC_BF16 = 0, 1
 VOC_SNAKE, VOC_SNAKE_BETA = 0, 1
 
 KERNEL_KINDS = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused",
-                "in_proj"]
+                "in_proj", "enc_down", "enc_out"]
 
 
 class voc_config(ctypes.Structure):
@@ -54,6 +54,7 @@ class voc_config(ctypes.Structure):
         ("tile_frames", ctypes.c_int),
         ("in_proj", ctypes.c_int),
         ("causal", ctypes.c_int),
+        ("enc_width", ctypes.c_int * (VOC_MAX_BLOCKS + 1)),
     ]
 
 
@@ -100,6 +101,7 @@ def lib():
             "vocoder_decode_windows": (I, [P, P, I64, I64, I64, I64, I64, I64, P, P]),
             "vocoder_windows_output_length": (I64, [P, I64, I64, I64, I64, I64]),
             "vocoder_stream_reset": (I, [P, I64]),
+            "vocoder_encode": (I, [P, P, I64, I64, P, P]),
             "vocoder_stream_decode": (I, [P, P, I64, P, P]),
             "vocoder_last_error": (ctypes.c_char_p, [P]),
             "vocoder_destroy": (None, [P]),
@@ -165,6 +167,8 @@ def config_from_dict(d: dict) -> voc_config:
     c.tile_frames = d.get("tile_frames", 0)
     c.in_proj = d.get("in_proj", 0)
     c.causal = int(d.get("causal", 0))
+    for i, w in enumerate(d.get("enc_widths") or ()):
+        c.enc_width[i] = w
     return c
 
 
@@ -229,6 +233,23 @@ def vocoder_decode_windows(ctx, latents, n: int, sides: int, L: int, L_last: int
 def vocoder_windows_output_length(ctx, n: int, L: int, L_last: int, crop_left: int,
                                   crop_right: int) -> int:
     return lib().vocoder_windows_output_length(ctx, n, L, L_last, crop_left, crop_right)
+
+
+def vocoder_encode(ctx, audio, B: int, T: int, latent, stream=None) -> int:
+    return lib().vocoder_encode(ctx, _ptr(audio), B, T, _ptr(latent), _stream(stream))
+
+
+def encode(ctx, audio, latent_channels: int, stream=None):
+    """latent [B, latent_channels, T] (new CUDA tensor) for CUDA fp32 audio
+    [B, 1, T * hop]."""
+    import torch
+    assert audio.is_cuda and audio.dtype == torch.float32 and audio.is_contiguous()
+    b, _, n = audio.shape
+    hop = vocoder_output_length(ctx, 1)
+    assert n % hop == 0
+    z = torch.empty(b, latent_channels, n // hop, device=audio.device)
+    check(vocoder_encode(ctx, audio, b, n // hop, z, stream), ctx)
+    return z
 
 
 def vocoder_stream_reset(ctx, rows: int) -> int:

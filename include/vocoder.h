@@ -81,7 +81,9 @@ typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
  * in_kernel == res_kernel == out_kernel == 7; widths, latent_channels and a
  * non-zero in_proj positive multiples of 16 (F32) or 32 (BF16), at most 8192,
  * width[n_blocks] <= 512; convt_crop == 0; tile_frames >= 0; in_proj >= 0;
- * causal is 0 or 1.
+ * causal is 0 or 1; an encoder (enc_width[0] > 0) needs every enc_width[b]
+ * (b <= n_blocks) a positive multiple of 16 (F32) or 32 (BF16), at most
+ * 8192, even strides and causal == 0.
  */
 typedef struct voc_config {
   int abi_version;
@@ -110,6 +112,10 @@ typedef struct voc_config {
   int causal;                      /* 0: "same" padding and centered crop; 1:   */
                                    /* causal k=7 convs (left pad (K-1)*d) and   */
                                    /* ConvTranspose1d keeping full[0, T*s)      */
+  int enc_width[VOC_MAX_BLOCKS + 1]; /* encoder widths (all 0: no encoder):     */
+                                   /* conv_in 1 -> enc_width[0], block b        */
+                                   /* enc_width[b] -> enc_width[b+1] with the   */
+                                   /* decoder's strides in reverse order        */
 } voc_config;
 
 /* Fill *cfg with the full-width stereo window decoder: latent 64, widths
@@ -145,6 +151,12 @@ voc_status vocoder_create(const voc_config *cfg, int hip_device, voc_ctx **out);
  *   blocks.{b}.res_units.{r}.snake1.alpha, .conv1.{weight_v [W,W,7], weight_g, bias},
  *                           .snake2.alpha, .conv2.{weight_v [W,W,1], weight_g, bias}
  *   snake_out.alpha [1,Wn,1];  conv_out.{weight_v [1,Wn,7], weight_g [1,1,1], bias [1]}
+ * and with an encoder (E = enc_width, s_b = stride[n_blocks-1-b]):
+ *   encoder.conv_in.{weight_v [E0,1,7], weight_g, bias}
+ *   encoder.blocks.{b}.res_units.{r}.{snake1, conv1 [Eb,Eb,7], snake2, conv2 [Eb,Eb,1]}
+ *   encoder.blocks.{b}.snake.alpha [1,Eb,1]; encoder.blocks.{b}.down.{weight_v [Eb+1,Eb,2s_b], ...}
+ *   encoder.snake_out.alpha [1,En,1]; encoder.conv_out.{weight_v [En,En,3], ...}
+ *   encoder.proj.{weight_v [Clat,En,1], weight_g, bias}
  */
 typedef struct voc_tensor {
   const char *name;
@@ -238,6 +250,22 @@ voc_status vocoder_stream_reset(voc_ctx *ctx, int64_t rows);
 voc_status vocoder_stream_decode(voc_ctx *ctx, const float *latent, int64_t t, float *pcm,
                                  void *hip_stream);
 
+/*
+ * Encode (minimaxmusic.cpp ARCHITECTURE, "Flow VAE": the encoder mirrors the
+ * decoder; its output is the posterior mean, no sampling): audio (device,
+ * fp32, [B, 1, T*hop] contiguous, one mono row per side) -> latent (device,
+ * fp32, [B, latent_channels, T] contiguous).  Per row: conv_in (k=7), per
+ * block three residual units, Snake and a strided Conv1d (k = 2s, stride s,
+ * pad s/2), then Snake, conv_out (k=3) and the projection (k=1).  Same
+ * asynchrony and ownership as vocoder_decode.  BF16 configs round the audio
+ * to bf16 as a matrix-core operand.
+ * Errors: VOC_INVALID_PARAMS (no encoder configured, NULL/misaligned
+ * pointers, B or T <= 0, T*hop beyond 2^31), VOC_NOT_LOADED, VOC_OOM,
+ * VOC_DEVICE_ERROR.
+ */
+voc_status vocoder_encode(voc_ctx *ctx, const float *audio, int64_t B, int64_t T, float *latent,
+                          void *hip_stream);
+
 /* Samples per side that vocoder_decode_windows writes for these arguments:
  * hop times the kept latent frames of all windows; -1 if they are invalid. */
 int64_t vocoder_windows_output_length(const voc_ctx *ctx, int64_t n_windows, int64_t L,
@@ -252,7 +280,8 @@ const char *vocoder_last_error(const voc_ctx *ctx);
 void vocoder_destroy(voc_ctx *ctx);
 
 /* ------------------------------------------------------------ profiling
- * When enabled, every kernel launch of vocoder_decode and voc_dbg_run_stage
+ * When enabled, every kernel launch of the decode, encode and stream calls
+ * and of voc_dbg_run_stage
  * is bracketed by two hipEvents recorded on the launch stream, and the
  * algorithmic work of the launch (direct-convolution flops, minimum HBM
  * bytes) is recorded beside them.  vocoder_profile_read synchronizes on the
@@ -267,7 +296,9 @@ typedef enum voc_kernel_kind {
   VOC_K_EXPORT = 6,   /* debug-stage output transpose                   */
   VOC_K_RES_FUSED = 7, /* whole residual unit (conv1, Snake2, conv2, add) */
   VOC_K_IN_PROJ = 8,  /* dec_in_proj (k=1) GEMM                         */
-  VOC_K_COUNT = 9
+  VOC_K_ENC_DOWN = 9, /* encoder strided Conv1d GEMM                    */
+  VOC_K_ENC_OUT = 10, /* encoder conv_out (k=3) and projection (k=1)    */
+  VOC_K_COUNT = 11
 } voc_kernel_kind;
 
 typedef struct voc_profile_stat {

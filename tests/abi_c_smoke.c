@@ -51,6 +51,14 @@ int main(void) {
   EXPECT(vocoder_decode_windows(NULL, dummy, 3, 2, 689, 683, 86, 258, dummy, NULL) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_windows_output_length(NULL, 3, 689, 683, 86, 258) == -1);
   EXPECT(vocoder_stream_reset(NULL, 4) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_encode(NULL, dummy, 1, 1, dummy, NULL) == VOC_INVALID_PARAMS);
+  voc_config_default(&cfg);
+  cfg.enc_width[0] = 64; cfg.enc_width[1] = 128; cfg.enc_width[2] = 256; cfg.enc_width[3] = 512;
+  cfg.enc_width[4] = 1024;
+  EXPECT(voc_config_validate(&cfg) == VOC_OK);
+  cfg.enc_width[2] = 24;
+  EXPECT(voc_config_validate(&cfg) == VOC_INVALID_PARAMS);
+  memset(cfg.enc_width, 0, sizeof(cfg.enc_width));
   EXPECT(vocoder_stream_decode(NULL, dummy, 1, dummy, NULL) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_profile_enable(NULL, 1) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_profile_reset(NULL) == VOC_INVALID_PARAMS);

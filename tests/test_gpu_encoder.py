@@ -1,0 +1,96 @@
+"""GPU parity of the DAV encoder (vocoder_encode: conv_in 1 -> 64, blocks
+doubling to 1024 with strided convs of strides 2/4/8/8, conv_out k=3,
+posterior-mean projection to 64 channels) against the oracle's encoder:
+
+* short clips end to end, fp32 and bf16 (conditioned twin weights);
+* the full stereo window (689 x 512 samples per side) on sampled latent
+  frames: the oracle encodes audio windows with an 8-frame halo, which
+  reproduces its whole-clip encode exactly (measured on the CPU: 8 frames
+  give 0 difference, 7 frames 6e-7);
+* argument checks.
+"""
+import numpy as np
+import pytest
+import torch
+
+from dac_vocoder_decoding_amd import inputs as I
+from dac_vocoder_decoding_amd import vocoder as V
+from oracle import oracle as O
+
+from gpu_util import TOL, rel_maxabs, rel_rms, to_dev
+
+pytestmark = pytest.mark.gpu
+
+HALO = 8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    V.lib()
+
+
+@pytest.mark.parametrize("dtype,frames", [("f32", 4), ("f32", 11), ("bf16", 6)])
+def test_encode_vs_oracle(dtype, frames):
+    cfg = I.config(8, dtype=dtype)
+    t = I.make_weights(cfg, twin=True)
+    audio = I.make_audio(cfg, batch=2, frames=frames)
+    ctx = V.open_context(cfg, t)
+    try:
+        z = V.encode(ctx, to_dev(audio), cfg["latent_channels"]).cpu().numpy()
+    finally:
+        V.vocoder_destroy(ctx)
+    ref = O.Encoder(cfg, t).encode(audio)
+    assert z.shape == ref.shape == (2, 64, frames)
+    e_max, e_rms = rel_maxabs(z, ref), rel_rms(z, ref)
+    print(f"encode {dtype} {frames} frames: max-abs/RMS {e_max:.2e} rel-RMS {e_rms:.2e}")
+    if dtype == "f32":
+        assert e_max <= TOL["f32"]
+    else:
+        assert e_rms <= TOL["bf16"]
+
+
+def test_fullsize_encode_sampled():
+    cfg = I.config(8)
+    t = I.make_weights(cfg, twin=True)
+    audio = I.make_audio(cfg)
+    B, T, hop = cfg["batch"], cfg["frames"], cfg["hop"]
+    ctx = V.open_context(cfg, t)
+    try:
+        x = to_dev(audio)
+        z = V.encode(ctx, x, cfg["latent_channels"])
+        again = V.encode(ctx, x, cfg["latent_channels"])
+        torch.cuda.synchronize()
+    finally:
+        V.vocoder_destroy(ctx)
+    assert z.shape == (B, 64, T) and bool(torch.isfinite(z).all())
+    assert torch.equal(z, again)
+    m = O.Encoder(cfg, t)
+    for r, a, e in [(0, 0, 3), (1, 340, 343), (1, T - 3, T)]:
+        lo, hi = max(0, a - HALO), min(T, e + HALO)
+        ref = m.encode(audio[r:r + 1, :, lo * hop:hi * hop])[0, :, a - lo:e - lo]
+        got = z[r, :, a:e].cpu().numpy()
+        err = rel_maxabs(got, ref)
+        print(f"row {r} frames [{a},{e}): max-abs/RMS {err:.2e}")
+        assert err <= TOL["f32"]
+
+
+def test_encode_argument_checks():
+    cfg = I.config(8)
+    t = I.make_weights(cfg)
+    ctx = V.open_context(cfg, t)
+    x = torch.zeros(2, 1, 4 * 512, device="cuda")
+    z = torch.zeros(2, 64, 4, device="cuda")
+    try:
+        assert V.vocoder_encode(ctx, x, 2, 0, z) == V.VOC_INVALID_PARAMS
+        assert V.vocoder_encode(ctx, None, 2, 4, z) == V.VOC_INVALID_PARAMS
+        assert V.vocoder_encode(ctx, x, 2, 4, z) == V.VOC_OK
+        torch.cuda.synchronize()
+    finally:
+        V.vocoder_destroy(ctx)
+    plain = V.open_context(I.config(1), I.make_weights(I.config(1)))
+    try:
+        assert V.vocoder_encode(plain, x, 2, 4, z) == V.VOC_INVALID_PARAMS
+        assert "encoder" in V.vocoder_last_error(plain)
+    finally:
+        V.vocoder_destroy(plain)
