@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   // A strided conv (stride S) reads its input as S phase streams per
   // channel chunk: virtual chunk c is phase c % S of chunk c / S, whose frame
   // m is input row m * S + c % S.  S = 1 is the plain conv.
-  const int S = a.in_stride > 1 ? a.in_stride : 1;
+  const int S = TAPS == 3 && a.in_stride > 1 ? a.in_stride : 1;  // compile-time 1 for the other convs
   const int nchunks = a.Cin / CH * S;
   const unsigned char* xrow = static_cast<const unsigned char*>(a.x) +
                               static_cast<int64_t>(row) * a.Cin * a.T_in * ES;
