@@ -7,10 +7,10 @@
 //     1 tap;
 //   * Conv1d k=3 (the encoder's conv_out): 3 taps at offsets -1, 0, 1;
 //   * the encoder's strided Conv1d k=2s, stride s, pad s/2 (minimaxmusic.cpp
-//     ARCHITECTURE, "Flow VAE"): with x_p[m] = x[m*s + p] the output is
-//     y[n] = sum_p sum_{q=-1..1} w[q*s + p + s/2] x_p[n + q] (terms with a
-//     kernel index outside [0, 2s) are zero), i.e. a 3-tap conv over s*C
-//     phase channels read with an input row stride of s;
+//     ARCHITECTURE, "Flow VAE"): with the phase streams
+//     x'_p[m] = x[m*s + p - s/2] the output is
+//     y[n] = sum_p (w[p] x'_p[n] + w[s + p] x'_p[n + 1]), i.e. a 2-tap conv
+//     over s*C phase channels read with an input row stride of s (TAG 2);
 //   * ConvTranspose1d k=2s stride s as a polyphase GEMM: output phase r of
 //     input frame q is x[q] w[:, :, r] + x[q-1] w[:, :, s+r], i.e. 2 taps at
 //     offsets 0 and -1 with M = s*Cout rows m = r*Cout + o.  The transposed
@@ -45,9 +45,10 @@
 
 namespace voc {
 
-// TAG only separates kernel names per layer kind (the input layers conv_in
-// and dec_in_proj vs the residual convs of the same tap count) so that
-// profilers report them apart; it does not change the code.
+// TAG 0/1 only separates kernel names per layer kind (the input layers
+// conv_in and dec_in_proj vs the residual convs of the same tap count) so
+// that profilers report them apart.  TAG 2 is the strided conv: its input
+// rows are read through phase streams (a runtime stride; 1 elsewhere).
 template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG, int NS>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   constexpr int CH = OpT<OP>::CH;
@@ -94,8 +95,9 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   const int tfirst = n0 + a.min_off;
   // A strided conv (stride S) reads its input as S phase streams per
   // channel chunk: virtual chunk c is phase c % S of chunk c / S, whose frame
-  // m is input row m * S + c % S.  S = 1 is the plain conv.
-  const int S = TAPS == 3 && a.in_stride > 1 ? a.in_stride : 1;  // compile-time 1 for the other convs
+  // m is input row m * S + c % S - S/2.  S = 1 is the plain conv.
+  const int S = TAG == 2 ? a.in_stride : 1;  // compile-time 1 for the other convs
+  const int ph0 = TAG == 2 ? -(S / 2) : 0;    // phase streams start s/2 rows early
   const int nchunks = a.Cin / CH * S;
   const unsigned char* xrow = static_cast<const unsigned char*>(a.x) +
                               static_cast<int64_t>(row) * a.Cin * a.T_in * ES;
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   const uint32_t smem_lds = lds_addr(smem);
   // Frames in [-lb, 0) are read from memory (a stream's carried context);
   // the buffer resource then starts lb frames before frame 0.
-  const uint32_t xv0 = static_cast<uint32_t>(((tfirst + lr) * S + a.lb) * kChunkBytes + lg * 16);
+  const uint32_t xv0 = static_cast<uint32_t>(((tfirst + lr) * S + ph0 + a.lb) * kChunkBytes + lg * 16);
   const uint32_t wv0 = static_cast<uint32_t>((m0 + lr) * kChunkBytes + lg * 16);
   auto issue = [&](int c, int stage) {
     const i4 xs = buf_rsrc(xrow + (c / S) * xplane - static_cast<int64_t>(a.lb) * kChunkBytes,
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       for (int u = 0; u < XU; ++u) {
         const int idx = tid + u * 256;
         const int r = unit_row(idx), col = unit_col(idx);
-        const int t = (tfirst + r) * S + ph;  // input row
+        const int t = (tfirst + r) * S + ph0 + ph;  // input row
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (r < xrows && t >= -a.lb && t < Lin)
           v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
@@ -461,7 +463,8 @@ static hipError_t launch_op(int taps, int variant, bool input_layer, const ConvA
   switch (taps) {
     case 7:
       return input_layer ? launch_taps<OP, 7, 1>(variant, a, s) : launch_taps<OP, 7, 0>(variant, a, s);
-    case 2: return launch_taps<OP, 2, 0>(variant, a, s);
+    case 2:
+      return a.in_stride > 1 ? launch_taps<OP, 2, 2>(variant, a, s) : launch_taps<OP, 2, 0>(variant, a, s);
     case 3: return launch_taps<OP, 3, 0>(variant, a, s);
     case 1:
       return input_layer ? launch_taps<OP, 1, 1>(variant, a, s) : launch_taps<OP, 1, 0>(variant, a, s);

@@ -68,8 +68,8 @@ struct ConvArgs {
   const float* hs_h;      // parameters instead of v (the head's Snake)
   int T_out, ups, crop;
   int lb;         // frames in [-lb, 0) of x are read from memory (a stream's context), else zero
-  int in_stride;  // > 1: strided conv; GEMM frame m of virtual chunk c reads input row
-                  // m * in_stride + c % in_stride of chunk c / in_stride (Cin counts real channels)
+  int in_stride;  // > 1: strided conv (2 taps); GEMM frame m of virtual chunk c reads input row
+                  // m * s + c % s - s/2 of chunk c / s, s = in_stride (Cin counts real channels)
 };
 
 // Tile shape families of the conv GEMM kernel.

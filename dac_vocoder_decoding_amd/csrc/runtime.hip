@@ -32,7 +32,7 @@ struct ConvDev {
   float* bias = nullptr;
   int cin = 0, cout = 0, taps = 0, dil = 1, ups = 1, crop = 0, M = 0;
   int causal = 0;  // k=7: left padding (K-1)*d instead of "same"
-  int down = 1;    // > 1: strided conv (k = 2*down, stride down, pad down/2) as 3 taps
+  int down = 1;    // > 1: strided conv (k = 2*down, stride down, pad down/2) as 2 taps
 };
 struct UnitDev {
   SnakeDev a1, a2;
@@ -488,20 +488,25 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.w = L.w;
   a.M = L.M;
   a.Cout = L.cout;
-  if (L.taps == 2) {  // polyphase ConvTranspose1d: taps at x[q], x[q-1]
+  if (L.down > 1) {  // strided conv: taps at phase-stream frames n and n+1
+    a.off0 = 0;
+    a.offstep = 1;
+    a.min_off = 0;
+    a.halo = 1;
+    a.N = io.T_in / L.down;
+  } else if (L.taps == 2) {  // polyphase ConvTranspose1d: taps at x[q], x[q-1]
     a.off0 = 0;
     a.offstep = -1;
     a.min_off = -1;
     a.halo = 1;
     a.N = io.T_in + (L.crop > 0 ? 1 : 0);  // a left crop shifts the last outputs to n = T_in
   } else {  // taps at x[n + j*dil - P]: "same" P = (taps-1)/2*dil, causal P = (taps-1)*dil
-    // (a strided conv: 3 taps at frame groups n-1, n, n+1 of its phase streams)
     const int P = (L.causal ? L.taps - 1 : (L.taps - 1) / 2) * L.dil;
     a.off0 = -P;
     a.offstep = L.dil;
     a.min_off = -P;
     a.halo = (L.taps - 1) * L.dil;
-    a.N = io.T_in / L.down;
+    a.N = io.T_in;
   }
   const int t_out = L.down > 1 ? io.T_in / L.down : io.T_in * L.ups;
   a.T_out = t_out + c->mg;
@@ -1024,7 +1029,7 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     staging.push_back(dn);
     const size_t es = kind == PACK_HEAD ? 4 : op_size(op);
     size_t out_elems = static_cast<size_t>(cnt);
-    if (kind == PACK_DOWN) out_elems = static_cast<size_t>(cout) * cin * 3 * stride;  // 3 taps x s phases
+    if (kind == PACK_DOWN) out_elems = static_cast<size_t>(cout) * cin * 2 * stride;  // 2 taps x s phases
     if (cin_alloc > cin) out_elems = static_cast<size_t>(cout) * k * cin_alloc;
     st = dalloc(out_elems * es, out_w);
     if (st) return st;
@@ -1150,7 +1155,7 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
         const int sb = g.stride[g.n_blocks - 1 - b];
         eb.down.cin = E[b];
         eb.down.cout = eb.down.M = E[b + 1];
-        eb.down.taps = 3;
+        eb.down.taps = 2;
         eb.down.down = sb;
         st = fold(q + ".down", PACK_DOWN, E[b], E[b + 1], 2 * sb, sb, &eb.down.w, &eb.down.bias);
         if (st) return st;

@@ -47,14 +47,12 @@ __global__ __launch_bounds__(256) void fold_kernel(const FoldArgs a) {
       const int ci = static_cast<int>(e / a.k), kk = static_cast<int>(e % a.k);
       idx = ((static_cast<int64_t>(ci / ch) * a.k + kk) * a.cout + i) * ch + ci % ch;
     } else if (a.kind == PACK_DOWN) {  // strided conv (Cout, Cin, 2s), slice = o
-      // Kernel index j = q*s + p + s/2 - s (q in 0..2) of phase p: virtual
-      // chunk (ci / ch) * s + p, tap q (the strided form in conv_gemm.hip).
+      // Kernel index j = q*s + p: phase p, tap q in {0, 1} of virtual chunk
+      // (ci / ch) * s + p (the strided form in conv_gemm.hip).
       const int ci = static_cast<int>(e / a.k), j = static_cast<int>(e % a.k);
-      const int jj = j - a.stride / 2;  // in [-s/2, 3s/2)
-      const int qm = jj >= 0 ? jj / a.stride : -1;
-      const int ph = jj - qm * a.stride, q = qm + 1;
+      const int q = j / a.stride, ph = j % a.stride;
       const int64_t vc = static_cast<int64_t>(ci / ch) * a.stride + ph;
-      idx = ((vc * 3 + q) * a.cout + i) * ch + ci % ch;
+      idx = ((vc * 2 + q) * a.cout + i) * ch + ci % ch;
     } else if (a.kind == PACK_CONVT) {  // (Cin, Cout, 2s), slice = ci
       const int o = static_cast<int>(e / (2 * a.stride));
       const int kk = static_cast<int>(e % (2 * a.stride));
