@@ -45,10 +45,11 @@
 
 namespace voc {
 
-// TAG 0/1 only separates kernel names per layer kind (the input layers
-// conv_in and dec_in_proj vs the residual convs of the same tap count) so
-// that profilers report them apart.  TAG 2 is the strided conv: its input
-// rows are read through phase streams (a runtime stride; 1 elsewhere).
+// TAG 0/1/3 only separates kernel names per layer kind (1: the input layers
+// conv_in and dec_in_proj; 3: the encoder's conv_out and projection; 0: the
+// residual convs) so that profilers report them apart.  TAG 2 is the
+// strided conv: its input rows are read through phase streams (a runtime
+// stride; 1 elsewhere).
 template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG, int NS>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   constexpr int CH = OpT<OP>::CH;
@@ -459,23 +460,23 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 }
 
 template <int OP>
-static hipError_t launch_op(int taps, int variant, bool input_layer, const ConvArgs& a, hipStream_t s) {
+static hipError_t launch_op(int taps, int variant, int tag, const ConvArgs& a, hipStream_t s) {
   switch (taps) {
     case 7:
-      return input_layer ? launch_taps<OP, 7, 1>(variant, a, s) : launch_taps<OP, 7, 0>(variant, a, s);
+      return tag == 1 ? launch_taps<OP, 7, 1>(variant, a, s) : launch_taps<OP, 7, 0>(variant, a, s);
     case 2:
       return a.in_stride > 1 ? launch_taps<OP, 2, 2>(variant, a, s) : launch_taps<OP, 2, 0>(variant, a, s);
-    case 3: return launch_taps<OP, 3, 0>(variant, a, s);
+    case 3: return launch_taps<OP, 3, 3>(variant, a, s);  // only the encoder's conv_out
     case 1:
-      return input_layer ? launch_taps<OP, 1, 1>(variant, a, s) : launch_taps<OP, 1, 0>(variant, a, s);
+      return tag == 1   ? launch_taps<OP, 1, 1>(variant, a, s)
+             : tag == 3 ? launch_taps<OP, 1, 3>(variant, a, s)
+                        : launch_taps<OP, 1, 0>(variant, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_conv(int op, int taps, int variant, bool input_layer, const ConvArgs& a,
-                       hipStream_t s) {
-  return op == OP_F32 ? launch_op<OP_F32>(taps, variant, input_layer, a, s)
-                      : launch_op<OP_BF16>(taps, variant, input_layer, a, s);
+hipError_t launch_conv(int op, int taps, int variant, int tag, const ConvArgs& a, hipStream_t s) {
+  return op == OP_F32 ? launch_op<OP_F32>(taps, variant, tag, a, s) : launch_op<OP_BF16>(taps, variant, tag, a, s);
 }
 
 }  // namespace voc

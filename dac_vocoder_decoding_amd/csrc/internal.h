@@ -86,9 +86,9 @@ int conv_variant_bm(int v);
 int conv_variant_bn(int v);
 bool conv_variant_ok(int v, int taps);
 
-// input_layer: conv_in or dec_in_proj (a separate kernel name for profilers).
-hipError_t launch_conv(int op, int taps, int variant, bool input_layer, const ConvArgs& a,
-                       hipStream_t s);
+// tag: 1 conv_in / dec_in_proj, 3 the encoder's conv_out / projection, else
+// 0 (separate kernel names for profilers; the strided conv picks its own).
+hipError_t launch_conv(int op, int taps, int variant, int tag, const ConvArgs& a, hipStream_t s);
 
 // One fused residual unit over all C channels of BN-frame tiles:
 //   h <- h_in + conv2(Snake2(conv1_dil(x) + b1)) + b2;  s_out <- Snake_next(h).

@@ -547,7 +547,8 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   const int op = c->op;
   return launch(c, s, kind, flops, bytes, "conv launch",
                 [&] {
-                  return launch_conv(op, L.taps, v, kind == VOC_K_CONV_IN || kind == VOC_K_IN_PROJ, a, s);
+                  const int tag = kind == VOC_K_CONV_IN || kind == VOC_K_IN_PROJ ? 1 : kind == VOC_K_ENC_OUT ? 3 : 0;
+                  return launch_conv(op, L.taps, v, tag, a, s);
                 });
 }
 
