@@ -1,8 +1,10 @@
 // runtime.hip -- host side of libvocoder: the C ABI declared in vocoder.h.
 //
-// Validation, the exact tiling halo, weight ingestion (device-side fold and
-// repack), workspace management, the launch sequence of one decode, per-launch
-// profiling and the debug stage runner.  No exception crosses the ABI.
+// Validation, the exact tiling halos, weight ingestion (device-side fold and
+// repack), workspace management, the launch sequences of a decode, a windowed
+// decode, a stream chunk (with the per-layer carried context) and an encode,
+// per-launch profiling and the debug stage runner.  No exception crosses the
+// ABI.
 #include "../../include/vocoder.h"
 #include "internal.h"
 

@@ -1,11 +1,14 @@
 // stream_kernels.hip -- the bandwidth-bound kernels of libvocoder:
-//   fold_kernel    weight-norm fold (fp64 norms), cast and repack (load time)
-//   import_kernel  [row][C][T] fp32 -> chunked operand / residual layouts,
-//                  with the tile gather of time-tiled decoding
-//   export_kernel  chunked fp32 -> [row][C][T] (debug stage runner)
-//   head_kernel    Snake -> Conv1d k=7 to one channel -> bias -> tanh, with
-//                  the tile crop folded into the store
-//   copy_kernel    plain 16-byte vector copy (byte-counter calibration)
+//   fold_kernel          weight-norm fold (fp64 norms), cast and repack (load
+//                        time), including the encoder's phase-packed strided conv
+//   import_kernel        [row][C][T] fp32 -> chunked operand / residual layouts,
+//                        with the row gather of tiles, windows and streams
+//   audio_import_kernel  mono audio -> a one-chunk operand (the encoder's input)
+//   layer_state_kernel   a stream layer's carried context in and out
+//   export_kernel        chunked fp32 -> [row][C][T] (stage runner, encoder output)
+//   head_kernel          Snake -> Conv1d k=7 to one channel -> bias -> tanh, with
+//                        the tile / window crop folded into the store
+//   copy_kernel          plain 16-byte vector copy (byte-counter calibration)
 #include "internal.h"
 #include "device_math.h"
 
