@@ -86,6 +86,12 @@ def test_decode_argument_checks(weights):
         assert V.vocoder_decode(ctx, None, 2, 4, y) == V.VOC_INVALID_PARAMS
         assert V.vocoder_decode(ctx, x.data_ptr() + 4, 2, 4, y) == V.VOC_INVALID_PARAMS
         assert V.vocoder_decode(ctx, x, 2, 4, y.data_ptr() + 8) == V.VOC_INVALID_PARAMS
+        # Size limits, rejected before any allocation or kernel: a row of
+        # 2^31 samples, and more than 65535 rows.
+        assert V.vocoder_decode(ctx, x, 2, 1 << 22, y) == V.VOC_INVALID_PARAMS
+        assert "2^31" in V.vocoder_last_error(ctx)
+        assert V.vocoder_decode(ctx, x, 70000, 4, y) == V.VOC_INVALID_PARAMS
+        assert "rows" in V.vocoder_last_error(ctx)
         assert V.vocoder_output_length(ctx, 7) == 7 * 512
         assert V.voc_dbg_run_stage(ctx, 99, x, 2, 4, y) == V.VOC_INVALID_PARAMS
     finally:
