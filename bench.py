@@ -35,9 +35,11 @@ METRIC = "audio-seconds decoded/sec (44.1 kHz stereo) + TFLOP/s as % of MFMA pea
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 KIND_NAMES = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused",
-              "in_proj", "enc_down", "enc_out"]
+              "in_proj", "enc_down", "enc_out", "af_snake"]
+HBM_KINDS = ("head", "af_snake")   # stencil kernels: priced against HBM bandwidth
 KERNEL_SOURCES = ["dac_vocoder_decoding_amd/csrc/conv_gemm.hip",
                   "dac_vocoder_decoding_amd/csrc/fused_ru.hip",
+                  "dac_vocoder_decoding_amd/csrc/stream_kernels.hip",
                   "dac_vocoder_decoding_amd/csrc/gemm_common.h",
                   "dac_vocoder_decoding_amd/csrc/device_math.h",
                   "dac_vocoder_decoding_amd/csrc/internal.h"]
@@ -68,8 +70,10 @@ def workload_name(cfg: dict) -> str:
         return (f"{cfg['name']}: audio [{cfg['batch']},1,{cfg['frames'] * cfg['hop']}] -> latent {lat} "
                 f"{cfg['dtype']}, encoder widths {ew}, strides {es}, conv_out k=3, projection to "
                 f"{cfg['latent_channels']}, {cfg['act']}")
+    af = ", alias-free Snake (2x up / Snake / 2x down)" if cfg.get("af_snake") else ""
+    out = ", 2 output channels" if cfg.get("out_channels", 1) == 2 else ""
     return (f"{cfg['name']}: latent {lat} {cfg['dtype']}, {proj}widths {w}, strides {s}, "
-            f"{cfg['act']}{tile}")
+            f"{cfg['act']}{af}{out}{tile}")
 
 
 def traffic_for(workload_key: str, kind: str):
@@ -95,7 +99,7 @@ def cpu_baseline(cfg: dict, tensors: dict, latent, target_s: float = 15.0,
     the fraction of decoded frames the stitching keeps)."""
     from dac_vocoder_decoding_amd import inputs as I
     from oracle import oracle as O
-    rows = 2 if cfg["stereo"] else 1
+    rows = 2 if cfg["stereo"] and cfg.get("out_channels", 1) == 1 else 1
     hop = cfg["hop"]
     if cfg.get("encode"):   # `latent` is the audio [B, 1, T*hop]
         enc = O.Encoder(cfg, tensors)
@@ -149,7 +153,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     ctx = V.open_context(cfg, tensors, device=0)
     stream = torch.cuda.current_stream()
-    sides = 2 if cfg["stereo"] else 1
+    nout = cfg.get("out_channels", 1)
+    sides = 2 if cfg["stereo"] and nout == 1 else 1
     if cfg.get("encode"):
         audio_np = I.make_audio(cfg)
         B, T = cfg["batch"], cfg["frames"]
@@ -168,7 +173,7 @@ def main() -> int:
         latent_np = win_np[0].reshape(sides, cfg["latent_channels"], L)  # CPU-baseline sample
         latent = torch.from_numpy(win_np).to(dev)
         N = V.vocoder_windows_output_length(ctx, n, L, last, cl, cr)
-        pcm = torch.empty(sides, N, device=dev)
+        pcm = torch.empty(sides * nout, N, device=dev)
         B, T = n * sides, L
         secs = N / cfg["sample_rate"]
         kept_frac = N / (cfg["hop"] * (L * (n - 1) + last))
@@ -183,7 +188,7 @@ def main() -> int:
         assert T % ck == 0
         chunks = [torch.from_numpy(np.ascontiguousarray(latent_np[:, :, k:k + ck])).to(dev)
                   for k in range(0, T, ck)]
-        outs = [torch.empty(B, 1, V.vocoder_output_length(ctx, ck), device=dev) for _ in chunks]
+        outs = [torch.empty(B, nout, V.vocoder_output_length(ctx, ck), device=dev) for _ in chunks]
         pcm = outs[-1]
         secs = I.audio_seconds(cfg, B, T)
         flops = I.algorithmic_flops(cfg, B, T)   # the clip's own work (context re-decodes excluded)
@@ -197,7 +202,7 @@ def main() -> int:
         latent_np = I.make_latent(cfg)
         latent = torch.from_numpy(latent_np).to(dev)
         B, _, T = latent.shape
-        pcm = torch.empty(B, 1, V.vocoder_output_length(ctx, T), device=dev)
+        pcm = torch.empty(B, nout, V.vocoder_output_length(ctx, T), device=dev)
         secs = I.audio_seconds(cfg, B, T)
         flops = I.algorithmic_flops(cfg, B, T)
         kept_frac = 1.0
@@ -281,7 +286,7 @@ def main() -> int:
                 "alg_gbs": round(s["bytes"] / (s["ms"] / 1e3) / 1e9, 1),
             }
         s = kernels[dom]  # the dominant kind, timed over the timed steps
-        if dom == "head":
+        if dom in HBM_KINDS:
             achieved = s["bytes"] / (s["ms"] / 1e3) / 1e9
             roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
@@ -305,7 +310,9 @@ def main() -> int:
     rec = {
         "metric": METRIC,
         "value": value,
-        "unit": "audio-s/s" if cfg["stereo"] else "audio-s/s (mono 24 kHz)",
+        "unit": ("audio-s/s" if cfg["sample_rate"] == 44100 else
+                 f"audio-s/s (stereo {cfg['sample_rate'] / 1000:g} kHz)") if cfg["stereo"]
+                else "audio-s/s (mono 24 kHz)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -13,7 +13,7 @@
 //   Conv1d  (Cout, Cin, K):  tap = k,           M = Cout, m = o
 //   ConvT   (Cin, Cout, 2s): tap t in {0,1},    M = s*Cout, m = r*Cout + o,
 //                            value w[i][o][t*s + r]   (polyphase split)
-// Head weights: fp32 [k][C] (bf16-rounded values for BF16 configs).
+// Head weights: fp32 [out channel][k][C] (bf16-rounded values for BF16 configs).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -171,9 +171,11 @@ hipError_t launch_audio_import(int op, const float* x, void* out, int64_t T, int
 // h fp32 chunked [rows][C/16][T][16] -> y fp32 [rows][C][T].
 hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipStream_t s);
 
-// Head: pcm[dst[r] + tau - keep_lo[r]] = tanh(bias + sum_j sum_i w[j][i] *
-//   sh[r][tau + j - 3][i]) for tau in [keep_lo[r], keep_hi[r]), where sh is
-// Snake_out(h), already applied by the last residual unit's epilogue.
+// Head: pcm[dst[r] + o * ch_stride + tau - keep_lo[r]] = tanh(bias[o] +
+//   sum_j sum_i w[o][j][i] * sh[r][tau + j - pad][i]) for tau in
+// [keep_lo[r], keep_hi[r]) and output channel o < nout, where sh is
+// Snake_out(h), already applied by the producer (the last residual unit's
+// epilogue, or the alias-free Snake kernel).
 struct HeadArgs {
   const float* h;   // Snake_out(h), fp32 chunked
   int C, T;         // channels, allocated frames per row
@@ -182,13 +184,40 @@ struct HeadArgs {
   int rate;         // frames per latent frame
   int pad;          // left padding of the k=7 conv: 3 ("same") or 6 (causal)
   int lb;           // frames in [-lb, 0) of h are read from memory, else zero
-  const float* w;   // [7][C]
-  float bias;
+  int nout;         // output channels (1 or 2)
+  int64_t ch_stride;  // pcm elements between the output channels of a row
+  const float* w;   // [nout][7][C]
+  float bias[2];
   float* pcm;
 };
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+
+// Alias-free Snake over a residual-stream tensor (fp32 chunked, 16 channels
+// per 64-byte frame row): per row r with valid frames [0, len), len =
+// min(row_len[r] * rate, T),
+//   u = up2(x)   x replicate-padded;  u[2m]   = sum_k fe[k] x[m - 3 + k],
+//                                      u[2m+1] = sum_k fo[k] x[m - 2 + k]
+//   v = Snake(u) (scale, hh as for every Snake)
+//   y[t] = sum_j fd[j] v[2t - 5 + j]   v replicate-padded over [0, 2 len)
+// written for t < len to out in the out_op layout (fp32 16-channel chunks,
+// or bf16 32-channel chunks).  fe[k] = 2 f[11 - 2k], fo[k] = 2 f[10 - 2k],
+// fd = f (the 12-tap low-pass).
+constexpr int kAfTaps = 12;
+struct AfArgs {
+  const float* x;
+  void* out;
+  int out_op;
+  int C, T;           // channels, allocated frames per row (plane length)
+  const int* row_len;
+  int rate;
+  const float* scale;  // alpha / pi per channel
+  const float* hh;     // 1 / (2 den) per channel
+  float fe[6], fo[6], fd[kAfTaps];
+  int rows;
+};
+hipError_t launch_af_snake(const AfArgs& a, hipStream_t s);
 
 // Streaming: one layer's carried context.  buf points at frame 0 of the
 // first plane of the layer's input; planes of plane_bytes bytes hold 64-byte

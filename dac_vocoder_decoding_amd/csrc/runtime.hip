@@ -1,8 +1,9 @@
 // runtime.hip -- host side of libvocoder: the C ABI declared in vocoder.h.
 //
 // Validation, the exact tiling halos, weight ingestion (device-side fold and
-// repack), workspace management, the launch sequences of a decode, a windowed
-// decode, a stream chunk (with the per-layer carried context) and an encode,
+// repack), the alias-free Snake's low-pass design, workspace management, the
+// launch sequences of a decode (plain or alias-free), a windowed decode, a
+// stream chunk (with the per-layer carried context) and an encode,
 // per-launch profiling and the debug stage runner.  No exception crosses the
 // ABI.
 #include "../../include/vocoder.h"
@@ -63,7 +64,7 @@ struct Weights {
   std::vector<BlockDev> blocks;
   SnakeDev head_act;
   float* head_w = nullptr;
-  float head_bias = 0.f;
+  float head_bias[2] = {0.f, 0.f};
   std::vector<void*> allocs;
 };
 
@@ -81,6 +82,9 @@ struct voc_ctx {
   int op = OP_F32;
   int64_t hop = 1;
   int halo_l = 0, halo_r = 0;  // receptive-field halos in latent frames (left, right)
+  // Alias-free Snake low-pass (af_snake): polyphase upsampling taps and the
+  // downsampling taps, fp32 (see design_af_filter).
+  float af_fe[6] = {}, af_fo[6] = {}, af_fd[kAfTaps] = {};
   std::string err;
   bool loaded = false;
   Weights W;
@@ -96,7 +100,7 @@ struct voc_ctx {
   voc_profile_stat stats[VOC_K_COUNT]{};
   // cached row metadata of the last decode
   std::vector<int64_t> rows_key;  // what the uploaded metadata describes (empty: nothing)
-  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
+  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
@@ -165,6 +169,10 @@ voc_status validate(const voc_config* c, std::string* why) {
       if (c->stride[b] % 2) return bad("an encoder needs even strides (pad s/2)");
     if (c->causal) return bad("the encoder is not causal");
   }
+  if (c->af_snake != 0 && c->af_snake != 1) return bad("af_snake must be 0 or 1");
+  if (c->af_snake && c->causal) return bad("the alias-free Snake is built for non-causal decoders");
+  if (c->af_snake && c->enc_width[0] != 0) return bad("the alias-free Snake is built for the decoder only");
+  if (c->out_channels != 1 && c->out_channels != 2) return bad("out_channels must be 1 or 2");
   for (int b = 0; b <= c->n_blocks; ++b)
     if (c->width[b] <= 0 || c->width[b] % q || c->width[b] > 8192)
       return bad("widths must be positive multiples of 16 (F32) / 32 (BF16), at most 8192");
@@ -189,12 +197,14 @@ int64_t floordiv(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) 
 // widens them by 3d each side ("same"), or by 6d on the left only (causal);
 // ConvTranspose1d (stride s, k = 2s, left crop p = ceil(s/2), or 0 when
 // causal) maps outputs [lo, hi] to inputs [ceil((lo + p - 2s + 1)/s),
-// floor((hi + p)/s)].  The two ends propagate independently.
+// floor((hi + p)/s)].  An alias-free Snake widens them by 5 frames each side
+// at its rate.  The two ends propagate independently.
 void compute_halos(const voc_config& c, int* h_left, int* h_right) {
   const int64_t hop = total_stride(c);
   const int64_t F = 4096;
   const bool causal = c.causal != 0;
   const int64_t kl = causal ? 6 : 3, kr = causal ? 0 : 3;  // k=7 conv reach per unit dilation
+  const int64_t af = c.af_snake ? 5 : 0;                   // alias-free Snake reach
   std::vector<int64_t> rate(c.n_blocks + 1);
   rate[0] = 1;
   for (int b = 0; b < c.n_blocks; ++b) rate[b + 1] = rate[b] * c.stride[b];
@@ -207,16 +217,17 @@ void compute_halos(const voc_config& c, int* h_left, int* h_right) {
         ok_l = ok_l && lo >= (F - H) * R;
         ok_r = ok_r && hi < (F + 1 + H) * R;
       };
-      lo -= kl, hi += kr;  // head conv k=7
+      lo -= kl + af, hi += kr + af;  // head conv k=7, snake_out
       check(rate[c.n_blocks]);
       for (int b = c.n_blocks - 1; b >= 0; --b) {
-        for (int r = c.n_res - 1; r >= 0; --r) {
-          lo -= kl * c.dilation[r], hi += kr * c.dilation[r];
+        for (int r = c.n_res - 1; r >= 0; --r) {  // Snake2, conv1, Snake1 (conv2 is k=1)
+          lo -= kl * c.dilation[r] + 2 * af, hi += kr * c.dilation[r] + 2 * af;
           check(rate[b + 1]);
         }
         const int64_t s = c.stride[b], p = causal ? 0 : (s + 1) / 2;
         lo = -floordiv(-(lo + p - 2 * s + 1), s);
         hi = floordiv(hi + p, s);
+        lo -= af, hi += af;  // the block's Snake
         check(rate[b]);
       }
       lo -= kl, hi += kr;  // conv_in
@@ -297,7 +308,7 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // computed from h in the kernel (Snake1 at staging): their producers then
 // write no operand tensor, and h alternates between two buffers.
 bool unit_xh(const voc_ctx* c, int C) {
-  return c->ru_xh && !c->no_fuse && res_unit_tile(c->op, C, false) > 0 && res_unit_from_h_ok(c->op, C);
+  return !c->cfg.af_snake && c->ru_xh && !c->no_fuse && res_unit_tile(c->op, C, false) > 0 && res_unit_from_h_ok(c->op, C);
 }
 
 bool any_unit_xh(const voc_ctx* c) {
@@ -324,7 +335,7 @@ Plan make_plan(const voc_ctx* c, int rows, int T, int mg = 0) {
   size_t o = 0;
   p.off_xlat = o; o = align_up(o + es * rows * static_cast<size_t>(g.latent_channels) * (T + mg));
   p.off_h = o;    o = align_up(o + 4 * rows * max_act);
-  p.off_h2 = o;   if (any_unit_xh(c)) o = align_up(o + 4 * rows * max_act);
+  p.off_h2 = o;   if (any_unit_xh(c) || g.af_snake) o = align_up(o + 4 * rows * max_act);
   p.off_s0 = o;   o = align_up(o + es * rows * max_act);
   p.off_s1 = o;   o = align_up(o + es * rows * max_act);
   p.off_u = o;    o = align_up(o + es * rows * max_act);
@@ -578,7 +589,7 @@ voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const Ro
 }
 
 voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int nrows, int rate,
-                    float* pcm, hipStream_t s) {
+                    float* pcm, int64_t ch_stride, hipStream_t s) {
   HeadArgs a{};
   const voc_config& g = c->cfg;
   a.h = h;
@@ -589,8 +600,11 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
   a.rate = rate;
   a.pad = c->cfg.causal ? 6 : 3;
   a.lb = c->st_active ? a.pad : 0;
+  a.nout = g.out_channels;
+  a.ch_stride = ch_stride;
   a.w = c->W.head_w;
-  a.bias = c->W.head_bias;
+  a.bias[0] = c->W.head_bias[0];
+  a.bias[1] = c->W.head_bias[1];
   a.pcm = pcm;
   // The kernel reads and writes only the kept samples of each row (their
   // count is in the row metadata last uploaded for these rows).
@@ -600,9 +614,35 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
     frames = 0.0;
     for (int r = 0; r < nrows; ++r) frames += mi[4 * nrows + r] - mi[3 * nrows + r];
   }
-  const double flops = 2.0 * frames * a.C * 7;
-  const double bytes = frames * a.C * 4 + frames * 4;
+  const double flops = 2.0 * frames * a.C * 7 * a.nout;
+  const double bytes = frames * a.C * 4 + frames * 4 * a.nout;
   return launch(c, s, VOC_K_HEAD, flops, bytes, "head launch", [&] { return launch_head(a, s); });
+}
+
+// Alias-free Snake of x (fp32 residual-stream layout, C channels, T frames
+// per row at `rate` frames per latent frame) into out (operand layout of
+// out_op).  Algorithmic work per element: two upsampled samples of six taps,
+// two Snakes, one twelve-tap output (48 flops counting an FMA as two);
+// bytes: the fp32 read and the operand write.
+voc_status run_af(voc_ctx* c, const SnakeDev& sn, const float* x, int C, int T, int rate, int rows,
+                  const int* row_len, void* out, int out_op, hipStream_t s) {
+  AfArgs a{};
+  a.x = x;
+  a.out = out;
+  a.out_op = out_op;
+  a.C = C;
+  a.T = T + c->mg;
+  a.row_len = row_len;
+  a.rate = rate;
+  a.scale = sn.alpha;
+  a.hh = sn.invden;
+  std::memcpy(a.fe, c->af_fe, sizeof(a.fe));
+  std::memcpy(a.fo, c->af_fo, sizeof(a.fo));
+  std::memcpy(a.fd, c->af_fd, sizeof(a.fd));
+  a.rows = rows;
+  const double el = static_cast<double>(rows) * T * C;
+  return launch(c, s, VOC_K_AF_SNAKE, 48.0 * el, el * (4 + op_size(out_op)), "alias-free Snake launch",
+                [&] { return launch_af_snake(a, s); });
 }
 
 // One residual unit: fused into one kernel when an instance exists for its
@@ -684,6 +724,32 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
   io.snake_next = next;
   io.s_out = s_out;
   io.h_snake = h_snake;
+  return run_conv(c, u.c2, io, rows, row_len, VOC_K_RES_K1, s);
+}
+
+// One residual unit with alias-free Snakes (four launches; the Snakes read
+// neighbouring frames, so neither fits a GEMM epilogue or the fused unit):
+//   AF1(h) -> s_buf;  conv1 -> h2 (fp32);  AF2(h2) -> u_buf;  h += conv2(u_buf).
+voc_status run_res_unit_af(voc_ctx* c, const UnitDev& u, float* h, float* h2, void* s_buf, void* u_buf,
+                           int T, int rate, int rows, const int* row_len, hipStream_t s) {
+  const int C = u.c1.cout;
+  voc_status st = run_af(c, u.a1, h, C, T, rate, rows, row_len, s_buf, c->op, s);
+  if (st) return st;
+  ConvIO io{};
+  io.x = s_buf;
+  io.T_in = T;
+  io.rate_in = rate;
+  io.h_out = h2;
+  st = run_conv(c, u.c1, io, rows, row_len, VOC_K_RES_K7, s);
+  if (st) return st;
+  st = run_af(c, u.a2, h2, C, T, rate, rows, row_len, u_buf, c->op, s);
+  if (st) return st;
+  io = ConvIO{};
+  io.x = u_buf;
+  io.T_in = T;
+  io.rate_in = rate;
+  io.h_out = h;
+  io.res = h;
   return run_conv(c, u.c2, io, rows, row_len, VOC_K_RES_K1, s);
 }
 
@@ -787,6 +853,57 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
   return xchg(hc, t);  // the head's input
 }
 
+// The alias-free decoder (TensorSharp minimax-h3 page, audio VAE): producers
+// write the residual stream h only, and every Snake is an alias-free Snake
+// launch that writes the next GEMM's operand.  The head's input, AF(h), goes
+// to h2 in fp32; *h_last receives h2.
+voc_status run_stack_af(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, float** h_last) {
+  const voc_config& g = c->cfg;
+  const Weights& W = c->W;
+  ConvIO io{};
+  const void* x_in = B.xlat;
+  voc_status st;
+  if (W.in_proj.cout > 0) {
+    io.x = B.xlat;
+    io.T_in = T;
+    io.rate_in = 1;
+    io.s_out = B.u;
+    st = run_conv(c, W.in_proj, io, rows, B.rows.len, VOC_K_IN_PROJ, s);
+    if (st) return st;
+    x_in = B.u;
+  }
+  io = ConvIO{};
+  io.x = x_in;
+  io.T_in = T;
+  io.rate_in = 1;
+  io.h_out = B.h;
+  st = run_conv(c, W.conv_in, io, rows, B.rows.len, VOC_K_CONV_IN, s);
+  if (st) return st;
+  int t = T, rate = 1;
+  for (int b = 0; b < g.n_blocks; ++b) {
+    const BlockDev& blk = W.blocks[b];
+    st = run_af(c, blk.act, B.h, g.width[b], t, rate, rows, B.rows.len, B.s[0], c->op, s);
+    if (st) return st;
+    io = ConvIO{};
+    io.x = B.s[0];
+    io.T_in = t;
+    io.rate_in = rate;
+    io.h_out = B.h;  // the Snake above has consumed h
+    st = run_conv(c, blk.ct, io, rows, B.rows.len, VOC_K_CONVT, s);
+    if (st) return st;
+    t *= g.stride[b];
+    rate *= g.stride[b];
+    for (int r = 0; r < g.n_res; ++r) {
+      st = run_res_unit_af(c, blk.units[r], B.h, B.h2, B.s[0], B.u, t, rate, rows, B.rows.len, s);
+      if (st) return st;
+    }
+  }
+  st = run_af(c, W.head_act, B.h, g.width[g.n_blocks], t, rate, rows, B.rows.len, B.h2, OP_F32, s);
+  if (st) return st;
+  *h_last = B.h2;
+  return VOC_OK;
+}
+
 // ----------------------------------------------------------- weight names
 struct Expect {
   std::vector<int64_t> shape;  // squeezed (size-1 dims removed)
@@ -835,7 +952,7 @@ std::map<std::string, Expect> expected_tensors(const voc_config& g) {
     }
   }
   snake("snake_out", g.width[g.n_blocks]);
-  conv("conv_out", 1, g.width[g.n_blocks], 7, 1);
+  conv("conv_out", g.out_channels, g.width[g.n_blocks], 7, g.out_channels);
   if (g.enc_width[0] > 0) {  // the encoder: decoder strides in reverse order
     const int* E = g.enc_width;
     conv("encoder.conv_in", E[0], 1, 7, E[0]);
@@ -879,6 +996,53 @@ void free_weights(Weights& W) {
 
 // =================================================================== ABI
 
+namespace {
+// Modified Bessel function of the first kind, order 0, from its power series
+// I0(x) = sum_k ((x/2)^k / k!)^2 (all terms positive; converges fast for the
+// arguments of a Kaiser window).
+double bessel_i0(double x) {
+  double term = 1.0, sum = 1.0;
+  for (int k = 1; k < 64; ++k) {
+    term *= (x / (2.0 * k)) * (x / (2.0 * k));
+    sum += term;
+    if (term < 1e-17 * sum) break;
+  }
+  return sum;
+}
+
+// The alias-free Snake's low-pass (a windowed-sinc design, Kaiser's window,
+// as the BigVGAN anti-aliased activation uses it): 12 taps, cutoff 0.25
+// cycles per sample of the 2x rate (the original Nyquist frequency),
+// transition half-width 0.3; Kaiser's empirical formulas give the window
+// parameter beta from the attenuation
+// A = 2.285 (taps/2 - 1) pi (4 * half-width) + 7.95 dB; the taps sit at
+// half-integer times -5.5 .. 5.5 and are normalised to unit sum.  fe and fo
+// are the polyphase taps of the upsampler (gain 2): output sample 2m uses
+// 2 f[11 - 2k] on x[m - 3 + k], sample 2m+1 uses 2 f[10 - 2k] on x[m - 2 + k].
+void design_af_filter(float* fe, float* fo, float* fd) {
+  const int K = kAfTaps, half = K / 2;
+  const double cutoff = 0.25, half_width = 0.3;
+  const double A = 2.285 * (half - 1) * M_PI * (4.0 * half_width) + 7.95;
+  const double beta = A > 50.0 ? 0.1102 * (A - 8.7)
+                      : A >= 21.0 ? 0.5842 * std::pow(A - 21.0, 0.4) + 0.07886 * (A - 21.0)
+                                  : 0.0;
+  double f[kAfTaps], sum = 0.0;
+  for (int n = 0; n < K; ++n) {
+    const double r = 2.0 * n / (K - 1) - 1.0;
+    const double w = bessel_i0(beta * std::sqrt(std::max(0.0, 1.0 - r * r))) / bessel_i0(beta);
+    const double t = 2.0 * cutoff * (n - half + 0.5);
+    const double sinc = std::sin(M_PI * t) / (M_PI * t);  // t is never 0 (half-integer times)
+    f[n] = 2.0 * cutoff * w * sinc;
+    sum += f[n];
+  }
+  for (int n = 0; n < K; ++n) fd[n] = static_cast<float>(f[n] / sum);
+  for (int k = 0; k < 6; ++k) {
+    fe[k] = static_cast<float>(2.0 * f[11 - 2 * k] / sum);
+    fo[k] = static_cast<float>(2.0 * f[10 - 2 * k] / sum);
+  }
+}
+}  // namespace
+
 VOC_API void voc_config_default(voc_config* cfg) {
   if (!cfg) return;
   std::memset(cfg, 0, sizeof(*cfg));
@@ -896,6 +1060,7 @@ VOC_API void voc_config_default(voc_config* cfg) {
   cfg->dilation[2] = 9;
   cfg->act = VOC_SNAKE;
   cfg->dtype = VOC_F32;
+  cfg->out_channels = 1;
 }
 
 VOC_API voc_status voc_config_validate(const voc_config* cfg) { return validate(cfg, nullptr); }
@@ -928,6 +1093,7 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   c->op = cfg->dtype == VOC_F32 ? OP_F32 : OP_BF16;
   c->hop = total_stride(*cfg);
   compute_halos(*cfg, &c->halo_l, &c->halo_r);
+  if (cfg->af_snake) design_af_filter(c->af_fe, c->af_fo, c->af_fd);
   if (const char* cap = std::getenv("VOC_MAX_WORKSPACE_BYTES")) c->ws_cap = std::strtoull(cap, nullptr, 10);
   // Ablation only: VOC_VARIANT_{CONV_IN,CONVT,RES_K7,RES_K1}=<tile family index>.
   const char* names[4] = {"VOC_VARIANT_CONV_IN", "VOC_VARIANT_CONVT", "VOC_VARIANT_RES_K7",
@@ -1119,10 +1285,10 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     st = snake("snake_out", g.width[g.n_blocks], &W.head_act);
     if (st) return st;
     void* hw = nullptr;
-    st = fold("conv_out", PACK_HEAD, g.width[g.n_blocks], 1, 7, 1, &hw, nullptr);
+    st = fold("conv_out", PACK_HEAD, g.width[g.n_blocks], g.out_channels, 7, 1, &hw, nullptr);
     if (st) return st;
     W.head_w = static_cast<float*>(hw);
-    W.head_bias = got["conv_out.bias"]->data[0];
+    for (int o = 0; o < g.out_channels; ++o) W.head_bias[o] = got["conv_out.bias"]->data[o];
     if (g.enc_width[0] > 0) {
       const int* E = g.enc_width;
       const int CHn = op_chunk(op);
@@ -1211,9 +1377,10 @@ namespace {
 // One batched decode of `rows` rows read from latent [*, C, T_src] through
 // the row metadata (dst, ints = len | src_b | start | keep_lo | keep_hi),
 // which is uploaded unless `key` matches what the workspace already holds.
+// Output channel o of row r starts at pcm[dst[r] + o * ch_stride].
 voc_status decode_rows(voc_ctx* c, const float* latent, int64_t T_src, int64_t rows, int T_alloc,
                        std::vector<int64_t>&& dst, std::vector<int>&& ints,
-                       std::vector<int64_t>&& key, float* pcm, hipStream_t s) {
+                       std::vector<int64_t>&& key, float* pcm, int64_t ch_stride, hipStream_t s) {
   const voc_config& g = c->cfg;
   const Plan p = make_plan(c, static_cast<int>(rows), T_alloc);
   voc_status st = ensure_ws(c, p.bytes);
@@ -1228,10 +1395,11 @@ voc_status decode_rows(voc_ctx* c, const float* latent, int64_t T_src, int64_t r
                   nullptr, nullptr, s);
   if (st) return st;
   float* h_last = nullptr;
-  st = run_stack(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last);
+  st = g.af_snake ? run_stack_af(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last)
+                  : run_stack(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last);
   if (st) return st;
   return run_head(c, h_last, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
-                  static_cast<int>(c->hop), pcm, s);
+                  static_cast<int>(c->hop), pcm, ch_stride, s);
 }
 
 // Kept latent frames [lo, hi) of window k of n (window stitching): every
@@ -1288,10 +1456,10 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
       ints[2 * rows + r] = static_cast<int>(a);                   // start
       ints[3 * rows + r] = static_cast<int>((t0 - a) * c->hop);   // keep_lo
       ints[4 * rows + r] = static_cast<int>((t1 - a) * c->hop);   // keep_hi
-      dst[r] = b * T * c->hop + t0 * c->hop;
+      dst[r] = (b * g.out_channels * T + t0) * c->hop;
     }
   return decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {0, B, T, rows}, pcm,
-                     static_cast<hipStream_t>(stream));
+                     T * c->hop, static_cast<hipStream_t>(stream));
 }
 
 VOC_API voc_status vocoder_encode(voc_ctx* c, const float* audio, int64_t B, int64_t T, float* latent,
@@ -1503,7 +1671,7 @@ VOC_API voc_status vocoder_stream_decode(voc_ctx* c, const float* latent, int64_
       ints[2 * rows + r] = 0;                                 // start
       ints[3 * rows + r] = 0;                                 // keep_lo
       ints[4 * rows + r] = static_cast<int>(t * c->hop);      // keep_hi
-      dst[r] = r * t * c->hop;
+      dst[r] = r * c->cfg.out_channels * t * c->hop;
     }
     st = upload_rows(c, p, std::move(dst), std::move(ints), s);
     if (st) return st;
@@ -1518,7 +1686,7 @@ VOC_API voc_status vocoder_stream_decode(voc_ctx* c, const float* latent, int64_
   if (!st) st = run_stack(c, Bf, static_cast<int>(rows), static_cast<int>(t), s, &h_last);
   if (!st)
     st = run_head(c, h_last, static_cast<int>(t * c->hop), Bf.rows, static_cast<int>(rows),
-                  static_cast<int>(c->hop), pcm, s);
+                  static_cast<int>(c->hop), pcm, t * c->hop, s);
   c->mg = 0;
   c->st_active = false;
   if (st) return st;
@@ -1555,8 +1723,9 @@ VOC_API voc_status vocoder_decode_windows(voc_ctx* c, const float* latents, int6
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
   const int64_t N = vocoder_windows_output_length(c, n, L, L_last, cl, cr);
   // Row k*sides + j decodes side j of window k (row k*sides + j of the
-  // [n*sides, C, L] view) and writes its kept samples at
-  // pcm[j*N + hop * (frames kept by windows 0..k-1)].
+  // [n*sides, C, L] view) and writes the kept samples of its output channel
+  // o at pcm[(j*O + o)*N + hop * (frames kept by windows 0..k-1)], O =
+  // out_channels.
   std::vector<int64_t> dst(rows);
   std::vector<int> ints(5 * rows);
   int64_t before = 0;
@@ -1570,12 +1739,12 @@ VOC_API voc_status vocoder_decode_windows(voc_ctx* c, const float* latents, int6
       ints[2 * rows + r] = 0;                                     // start
       ints[3 * rows + r] = static_cast<int>(lo * c->hop);         // keep_lo
       ints[4 * rows + r] = static_cast<int>(hi * c->hop);         // keep_hi
-      dst[r] = j * N + before * c->hop;
+      dst[r] = j * c->cfg.out_channels * N + before * c->hop;
     }
     before += hi - lo;
   }
   return decode_rows(c, latents, L, rows, static_cast<int>(L), std::move(dst), std::move(ints),
-                     {1, n, sides, L, L_last, cl, cr}, pcm, static_cast<hipStream_t>(stream));
+                     {1, n, sides, L, L_last, cl, cr}, pcm, N, static_cast<hipStream_t>(stream));
 }
 
 VOC_API const char* vocoder_last_error(const voc_ctx* c) {
@@ -1641,7 +1810,7 @@ bool stage_info(const voc_ctx* c, int k, StageInfo* si) {
     return true;
   }
   if (k == n - 1) {
-    *si = {3, 0, 0, g.width[g.n_blocks], 1, 1};
+    *si = {3, 0, 0, g.width[g.n_blocks], g.out_channels, 1};
     return true;
   }
   const int b = (k - 1) / (1 + g.n_res), j = (k - 1) % (1 + g.n_res);
@@ -1690,7 +1859,8 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
   size_t o = 0;
   const size_t off_h = o; o = align_up(o + 4 * std::max(act_in, act_out));
   const bool xh = si.kind == 2 && unit_xh(c, static_cast<int>(si.c_out));
-  const size_t off_h2 = o; if (xh) o = align_up(o + 4 * act_out);
+  const bool af = c->cfg.af_snake != 0;
+  const size_t off_h2 = o; if (xh || af) o = align_up(o + 4 * std::max(act_in, act_out));
   const size_t off_s0 = o; o = align_up(o + es * act_in);
   const size_t off_s1 = o; o = align_up(o + es * act_out);
   const size_t off_u = o; o = align_up(o + es * act_out);
@@ -1714,7 +1884,7 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
     ints[2 * rows + r] = 0;
     ints[3 * rows + r] = 0;
     ints[4 * rows + r] = static_cast<int>(T_in);
-    dst[r] = static_cast<int64_t>(r) * T_in;
+    dst[r] = static_cast<int64_t>(r) * c->cfg.out_channels * T_in;
   }
   st = upload_rows(c, p, std::move(dst), std::move(ints), s);
   if (st) return st;
@@ -1747,7 +1917,12 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
       st = run_conv(c, W.conv_in, io, rows, ri.len, VOC_K_CONV_IN, s);
       break;
     case 1:
-      st = run_import(c, in, T_in, si.c_in, ri, rows, T, s0, &W.blocks[si.b].act, nullptr, s);
+      if (af) {  // import h, then its alias-free Snake into the operand
+        st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s);
+        if (!st) st = run_af(c, W.blocks[si.b].act, h, si.c_in, T, 1, rows, ri.len, s0, c->op, s);
+      } else {
+        st = run_import(c, in, T_in, si.c_in, ri, rows, T, s0, &W.blocks[si.b].act, nullptr, s);
+      }
       if (st) return st;
       io.x = s0; io.T_in = T; io.rate_in = 1; io.h_out = h;
       st = run_conv(c, W.blocks[si.b].ct, io, rows, ri.len, VOC_K_CONVT, s);
@@ -1756,6 +1931,11 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
       // The same kernel path as in a decode: with the operand computed from
       // h, the import writes h only and the unit writes h2.
       const UnitDev& un = W.blocks[si.b].units[si.r];
+      if (af) {
+        st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s);
+        if (!st) st = run_res_unit_af(c, un, h, h2, s0, u, T, 1, rows, ri.len, s);
+        break;
+      }
       st = run_import(c, in, T_in, si.c_in, ri, rows, T, xh ? nullptr : s0, &un.a1, h, s);
       if (st) return st;
       st = run_res_unit(c, un, s0, s1, u, h, xh ? h2 : nullptr, nullptr, nullptr, T, 1, rows, ri.len, s);
@@ -1763,9 +1943,15 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
       break;
     }
     default:
+      if (af) {  // the head reads AF(h), computed into h2
+        st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s);
+        if (!st) st = run_af(c, W.head_act, h, si.c_in, T, 1, rows, ri.len, h2, OP_F32, s);
+        if (st) return st;
+        return run_head(c, h2, T, ri, rows, 1, out, T_in, s);
+      }
       st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s, &W.head_act);
       if (st) return st;
-      return run_head(c, h, T, ri, rows, 1, out, s);
+      return run_head(c, h, T, ri, rows, 1, out, T_in, s);
   }
   if (st) return st;
   return launch(c, s, VOC_K_EXPORT, 0.0, 8.0 * rows * si.c_out * t_out, "export launch",

@@ -6,8 +6,9 @@
 //   audio_import_kernel  mono audio -> a one-chunk operand (the encoder's input)
 //   layer_state_kernel   a stream layer's carried context in and out
 //   export_kernel        chunked fp32 -> [row][C][T] (stage runner, encoder output)
-//   head_kernel          Snake -> Conv1d k=7 to one channel -> bias -> tanh, with
-//                        the tile / window crop folded into the store
+//   af_snake_kernel      alias-free Snake: 2x upsample, Snake, 2x downsample
+//   head_kernel          Snake -> Conv1d k=7 to one or two channels -> bias ->
+//                        tanh, with the tile / window crop folded into the store
 //   copy_kernel          plain 16-byte vector copy (byte-counter calibration)
 #include "internal.h"
 #include "device_math.h"
@@ -63,10 +64,9 @@ __global__ __launch_bounds__(256) void fold_kernel(const FoldArgs a) {
       const int64_t M = static_cast<int64_t>(a.stride) * a.cout;
       idx = ((static_cast<int64_t>(i / ch) * 2 + t) * M + static_cast<int64_t>(r) * a.cout + o) * ch +
             i % ch;
-    } else {  // PACK_HEAD (1, C, K) -> fp32 [K][C]
+    } else {  // PACK_HEAD (O, C, K), slice = o -> fp32 [O][K][C]
       const int ci = static_cast<int>(e / a.k), kk = static_cast<int>(e % a.k);
-      static_cast<float*>(a.out)[static_cast<int64_t>(kk) * a.cin + ci] =
-          a.round_bf16 ? bf16_round(wf) : wf;
+      static_cast<float*>(a.out)[(i * a.k + kk) * a.cin + ci] = a.round_bf16 ? bf16_round(wf) : wf;
       continue;
     }
     if (a.op == OP_F32)
@@ -249,11 +249,13 @@ hipError_t launch_layer_state(const LayerStateArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------- head
 // Output head (minimaxmusic.cpp ARCHITECTURE, "Flow VAE": snake_out, conv_out
-// k=7 with bias, tanh).  Its input already holds Snake_out(h) (the last
-// residual unit's epilogue applies it), so the head is a pure stream:
+// k=7 with bias, tanh; two output channels for a decoder that writes stereo
+// from one latent, as the H3 audio VAE of the TensorSharp minimax-h3 page
+// does).  Its input already holds Snake_out(h) (applied by its producer), so
+// the head is a pure stream:
 //   lane l of a wave reads frame f = o0 - P + l (all C channels, 64-byte
-//   chunk rows) and forms the seven per-tap projections
-//   z_j[f] = sum_i w[j][i] x[f][i];
+//   chunk rows) and forms the seven per-tap projections of each output
+//   channel, z_j[f] = sum_i w[j][i] x[f][i];
 //   lane l (P <= l < P + 58) then owns output o = f and gathers
 //   y[o] = tanh(bias + sum_j z_j[o + j - P]) from lanes l + j - P with
 //   cross-lane shuffles.  P = 3 for the "same" conv, 6 for the causal one
@@ -264,6 +266,7 @@ hipError_t launch_layer_state(const LayerStateArgs& a, hipStream_t s) {
 // into the store.
 constexpr int kHeadOut = 58;  // outputs per wave
 
+template <int NOUT>
 __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   const int r = blockIdx.y;
   const int lo = a.rows.keep_lo[r], hi = a.rows.keep_hi[r];
@@ -278,40 +281,165 @@ __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   const bool valid = f >= -a.lb && f < Lr;
   const float* hp = a.h + static_cast<int64_t>(r) * C * a.T + static_cast<int64_t>(f) * kHChunk;
   const int64_t plane = static_cast<int64_t>(a.T) * kHChunk;
-  float z[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float z[NOUT][7];
+#pragma unroll
+  for (int oc = 0; oc < NOUT; ++oc)
+#pragma unroll
+    for (int j = 0; j < 7; ++j) z[oc][j] = 0.f;
   for (int k = 0; k < C / 16; ++k) {
     f4 x[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       x[q] = valid ? *reinterpret_cast<const f4*>(hp + k * plane + q * 4) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 7; ++j) {
-      const float* wj = a.w + j * C + k * 16;
+    for (int oc = 0; oc < NOUT; ++oc)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 w = *reinterpret_cast<const f4*>(wj + q * 4);
-        z[j] = fmaf(w[0], x[q][0], z[j]);
-        z[j] = fmaf(w[1], x[q][1], z[j]);
-        z[j] = fmaf(w[2], x[q][2], z[j]);
-        z[j] = fmaf(w[3], x[q][3], z[j]);
+      for (int j = 0; j < 7; ++j) {
+        const float* wj = a.w + (oc * 7 + j) * C + k * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f4 w = *reinterpret_cast<const f4*>(wj + q * 4);
+          z[oc][j] = fmaf(w[0], x[q][0], z[oc][j]);
+          z[oc][j] = fmaf(w[1], x[q][1], z[oc][j]);
+          z[oc][j] = fmaf(w[2], x[q][2], z[oc][j]);
+          z[oc][j] = fmaf(w[3], x[q][3], z[oc][j]);
+        }
       }
-    }
-  }
-  float y = a.bias;
-#pragma unroll
-  for (int j = 0; j < 7; ++j) {
-    const int src = min(max(lane + j - P, 0), 63);
-    y += __shfl(z[j], src);
   }
   const int o = f;
-  if (lane >= P && lane < P + kHeadOut && o < hi) a.pcm[a.rows.dst[r] - lo + o] = tanhf(y);
+  const bool store = lane >= P && lane < P + kHeadOut && o < hi;
+#pragma unroll
+  for (int oc = 0; oc < NOUT; ++oc) {
+    float y = a.bias[oc];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const int src = min(max(lane + j - P, 0), 63);
+      y += __shfl(z[oc][j], src);
+    }
+    if (store) a.pcm[a.rows.dst[r] + oc * a.ch_stride - lo + o] = tanhf(y);
+  }
 }
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
   // keep ranges lie inside the allocated frames; the grid covers them.
   const int waves = (a.T + kHeadOut - 1) / kHeadOut;
   const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(a.nrows));
-  hipLaunchKernelGGL(head_kernel, grid, dim3(256), 0, s, a);
+  if (a.nout == 2)
+    hipLaunchKernelGGL(head_kernel<2>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(head_kernel<1>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ af snake
+// Alias-free Snake (TensorSharp minimax-h3 page, audio VAE: every
+// nonlinearity between a 2x upsample and a 2x downsample; the 12-tap
+// low-pass and its phases are described with AfArgs).  A thread owns four
+// channels of one 16-channel chunk and a run of kAfRun consecutive output
+// frames.  Output t needs the activated 2x-rate samples v[2t-5 .. 2t+6] and
+// the next two, v[2t+7] and v[2t+8], both come from input frames
+// x[t+1 .. t+6].  So a run warms up on x[t0-5 .. t0+5] (twelve v samples)
+// and then slides: per frame one new input frame, two upsampled samples,
+// two Snakes and one 12-tap output.  Frames read outside [0, len) repeat the
+// edge frame (replicate padding of the upsampler); 2x-rate samples outside
+// [0, 2 len) repeat the edge sample (replicate padding of the downsampler).
+// Lanes 4k .. 4k+3 read one 64-byte frame row, the 16 runs of a wave sit
+// kAfRun frames apart; the sliding reads walk each row's cache lines in
+// order.
+constexpr int kAfRun = 16;
+
+template <int OUT_OP>
+__global__ __launch_bounds__(256) void af_snake_kernel(const AfArgs a) {
+  const int r = blockIdx.y;
+  const int nchunk = a.C / 16;
+  const int chunk = blockIdx.x % nchunk;
+  const int run = (blockIdx.x / nchunk) * 64 + (threadIdx.x >> 2);
+  const int q = threadIdx.x & 3;
+  const int len = min(a.row_len[r] * a.rate, a.T);
+  const int t0 = run * kAfRun;
+  if (t0 >= len) return;
+  const int c = chunk * 16 + q * 4;
+  const float* xp = a.x + (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * 4;
+  auto ld = [&](int t) -> f4 {
+    t = min(max(t, 0), len - 1);
+    return *reinterpret_cast<const f4*>(xp + static_cast<int64_t>(t) * kHChunk);
+  };
+  const f4 sc = *reinterpret_cast<const f4*>(a.scale + c);
+  const f4 hh = *reinterpret_cast<const f4*>(a.hh + c);
+  auto snake4 = [&](f4 u) -> f4 {
+    f4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = snake_f32(u[e], sc[e], hh[e]);
+    return v;
+  };
+  // Warm-up.  X[k] = x[t0 - 5 + k]; V[i] = v[n], n = 2 t0 - 5 + i:
+  //   i odd  (n = 2m,   m = t0 + (i - 5) / 2): fe taps on X[(i - 1) / 2 .. + 5]
+  //   i even (n = 2m+1, m = t0 + (i - 6) / 2): fo taps on X[i / 2 .. + 5]
+  f4 X[11];
+#pragma unroll
+  for (int k = 0; k < 11; ++k) X[k] = ld(t0 - 5 + k);
+  f4 V[12];
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const int b = (i & 1) ? (i - 1) / 2 : i / 2;
+    f4 u = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 6; ++k) u += ((i & 1) ? a.fe[k] : a.fo[k]) * X[b + k];
+    V[i] = snake4(u);
+  }
+  const int n_last = 2 * len - 1;
+#pragma unroll
+  for (int i = 10; i >= 0; --i)
+    if (2 * t0 - 5 + i < 0) V[i] = V[i + 1];
+#pragma unroll
+  for (int i = 1; i < 12; ++i)
+    if (2 * t0 - 5 + i > n_last) V[i] = V[i - 1];
+  // R[k] = x[t + 1 + k] while output t is formed (R[5] loaded per frame).
+  f4 R[6];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) R[k] = X[6 + k];
+  const int nvalid = min(kAfRun, len - t0);
+  char* obase = static_cast<char*>(a.out);
+#pragma unroll
+  for (int s = 0; s < kAfRun; ++s) {
+    const int t = t0 + s;
+    f4 y = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kAfTaps; ++j) y += a.fd[j] * V[j];
+    if (s < nvalid) {
+      if constexpr (OUT_OP == OP_F32) {
+        const int64_t idx = (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + static_cast<int64_t>(t) * 16 + q * 4;
+        store_op4<OP_F32>(obase, idx, y);
+      } else {
+        const int64_t idx = (static_cast<int64_t>(r) * a.C + (c / 32) * 32) * a.T + static_cast<int64_t>(t) * 32 + c % 32;
+        store_op4<OP_BF16>(obase, idx, y);
+      }
+    }
+    if (s + 1 < kAfRun) {
+      R[5] = ld(t + 6);
+      f4 uo = f4{0.f, 0.f, 0.f, 0.f}, ue = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        uo += a.fo[k] * R[k];  // v[2t + 7]: m = t + 3
+        ue += a.fe[k] * R[k];  // v[2t + 8]: m = t + 4
+      }
+#pragma unroll
+      for (int i = 0; i < 10; ++i) V[i] = V[i + 2];
+      V[10] = 2 * t + 7 > n_last ? V[9] : snake4(uo);
+      V[11] = 2 * t + 8 > n_last ? V[10] : snake4(ue);
+#pragma unroll
+      for (int k = 0; k < 5; ++k) R[k] = R[k + 1];
+    }
+  }
+}
+
+hipError_t launch_af_snake(const AfArgs& a, hipStream_t s) {
+  const int runs = (a.T + kAfRun - 1) / kAfRun;
+  const dim3 grid(static_cast<unsigned>((a.C / 16) * ((runs + 63) / 64)), static_cast<unsigned>(a.rows));
+  if (a.out_op == OP_F32)
+    hipLaunchKernelGGL(af_snake_kernel<OP_F32>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(af_snake_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

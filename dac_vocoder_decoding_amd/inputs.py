@@ -140,6 +140,16 @@ CONFIGS = {
     8: _cfg(name="dav_encode_window_f32", batch=2, frames=689, in_proj=1024,
             widths=(1536, 768, 384, 192, 96), strides=(8, 8, 4, 2), seed=1008,
             enc_widths=(64, 128, 256, 512, 1024), encode=True),
+    # The H3 audio VAE decoder (TensorSharp minimax-h3 page, "audio VAE":
+    # DAC/BigVGAN, 32 latent channels -> stereo 32 kHz, upsample rates
+    # 5,5,2,2,2,2,2 = 800 samples per 40 Hz latent frame, every nonlinearity
+    # alias-free; Snake parameters stored as logs) on the longest clip H3
+    # generates, 15 s: latent [1, 32, 600] -> pcm [1, 2, 480000].  Widths
+    # halve per block from 2048 to 16 (a reading: the page gives none).
+    9: _cfg(name="h3_audio_vae_af_f32", latent_channels=32, batch=1, frames=600,
+            sample_rate=32000, act="snakebeta", snake_log_params=1, af_snake=1,
+            out_channels=2, widths=(2048, 1024, 512, 256, 128, 64, 32, 16),
+            strides=(5, 5, 2, 2, 2, 2, 2), seed=1009),
 }
 
 
@@ -190,8 +200,9 @@ def tensor_shapes(cfg: dict) -> dict:
             conv(p + ".conv2", (cout, cout, 1))
             shapes[p + ".conv2.bias"] = (cout,)
     snake("snake_out", w[-1])
-    conv("conv_out", (1, w[-1], k))
-    shapes["conv_out.bias"] = (1,)
+    nout = cfg.get("out_channels", 1)
+    conv("conv_out", (nout, w[-1], k))
+    shapes["conv_out.bias"] = (nout,)
     ew = cfg.get("enc_widths")
     if ew:  # the encoder: the decoder's strides in reverse order
         conv("encoder.conv_in", (ew[0], 1, k))
@@ -242,6 +253,8 @@ def make_weights(cfg: dict, seed: int | None = None, twin: bool = False) -> dict
             out[name] = normal(seed, name, shape, std=0.01)
         elif name.endswith(".alpha") or name.endswith(".beta"):
             out[name] = uniform(seed, name, shape, 0.5, 2.0)
+            if cfg.get("snake_log_params", 0):  # stored as logs of the same draws
+                out[name] = np.log(out[name].astype(np.float64)).astype(np.float32)
         else:  # pragma: no cover
             raise KeyError(name)
     return out
@@ -251,12 +264,14 @@ def make_windows(cfg: dict, seed: int | None = None, windows: int | None = None,
                  frames: int | None = None, last_frames: int | None = None) -> np.ndarray:
     """Seeded latent windows [n, sides * C_latent, L] ~ N(0, 1), float32, one
     independent draw per window (the pages' denoiser produces each window on
-    its own); the last window's frames from ``last_frames`` on are zero."""
+    its own); the last window's frames from ``last_frames`` on are zero.
+    sides is 2 for a stereo pair of latents, 1 for a mono latent or one that
+    decodes to both channels."""
     seed = cfg["seed"] if seed is None else seed
     n = cfg["windows"] if windows is None else windows
     L = cfg["frames"] if frames is None else frames
     last = cfg["last_frames"] if last_frames is None else last_frames
-    sides = 2 if cfg["stereo"] else 1
+    sides = 2 if cfg["stereo"] and cfg.get("out_channels", 1) == 1 else 1
     x = normal(seed, "windows", (n, sides * cfg["latent_channels"], L))
     x[-1, :, last:] = 0.0
     return x
@@ -282,9 +297,10 @@ def make_audio(cfg: dict, seed: int | None = None, batch: int | None = None,
 
 
 def audio_seconds(cfg: dict, batch: int, frames: int) -> float:
-    """Decoded audio-seconds: stereo pairs count once (two rows per stereo second)."""
+    """Decoded audio-seconds: stereo pairs count once (two rows per stereo
+    second, or one row when the decoder writes both channels)."""
     samples = frames * cfg["hop"]
-    rows = batch / 2 if cfg["stereo"] else batch
+    rows = batch / 2 if cfg["stereo"] and cfg.get("out_channels", 1) == 1 else batch
     return rows * samples / cfg["sample_rate"]
 
 
@@ -319,5 +335,16 @@ def algorithmic_flops(cfg: dict, batch: int, frames: int) -> float:
         t *= s
         for _ in cfg["dilations"]:
             f += 2.0 * batch * t * cout * cout * k + 2.0 * batch * t * cout * cout
-    f += 2.0 * batch * t * w[-1] * k
+    f += 2.0 * batch * t * w[-1] * k * cfg.get("out_channels", 1)
     return f
+
+
+def af_elements(cfg: dict, batch: int, frames: int) -> float:
+    """Activation elements that pass through a Snake in one decode (each one
+    alias-free Snake output element in an af_snake configuration)."""
+    w, t, n = cfg["widths"], frames, 0.0
+    for b, s in enumerate(cfg["strides"]):
+        n += batch * t * w[b]                            # the block's Snake
+        t *= s
+        n += batch * t * w[b + 1] * 2 * len(cfg["dilations"])
+    return n + batch * t * w[-1]                         # snake_out

@@ -17,7 +17,7 @@ import numpy as np
 LIB_PATH = os.environ.get("VOC_LIBRARY") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libvocoder.so")
 
-VOC_ABI_VERSION = 2
+VOC_ABI_VERSION = 3
 VOC_MAX_BLOCKS = 8
 VOC_MAX_RES = 4
 
@@ -32,7 +32,7 @@ VOC_F32, VOC_BF16 = 0, 1
 VOC_SNAKE, VOC_SNAKE_BETA = 0, 1
 
 KERNEL_KINDS = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused",
-                "in_proj", "enc_down", "enc_out"]
+                "in_proj", "enc_down", "enc_out", "af_snake"]
 
 
 class voc_config(ctypes.Structure):
@@ -55,6 +55,8 @@ class voc_config(ctypes.Structure):
         ("in_proj", ctypes.c_int),
         ("causal", ctypes.c_int),
         ("enc_width", ctypes.c_int * (VOC_MAX_BLOCKS + 1)),
+        ("af_snake", ctypes.c_int),
+        ("out_channels", ctypes.c_int),
     ]
 
 
@@ -169,6 +171,8 @@ def config_from_dict(d: dict) -> voc_config:
     c.causal = int(d.get("causal", 0))
     for i, w in enumerate(d.get("enc_widths") or ()):
         c.enc_width[i] = w
+    c.af_snake = int(d.get("af_snake", 0))
+    c.out_channels = int(d.get("out_channels", 1))
     return c
 
 
@@ -328,39 +332,46 @@ def open_context(cfg_dict: dict, tensors: dict, device: int = 0, **overrides):
     return ctx
 
 
+def out_channels(ctx) -> int:
+    """Output channels of the context's head (the last debug stage's c_out)."""
+    st, _, c_out, _ = voc_dbg_stage_shape(ctx, voc_dbg_stage_count(ctx) - 1, 1)
+    check(st, ctx)
+    return c_out
+
+
 def decode(ctx, latent, stream=None):
-    """pcm [B, 1, T*hop] (new CUDA tensor) for a CUDA fp32 latent [B, C, T]."""
+    """pcm [B, out_channels, T*hop] (new CUDA tensor) for a CUDA fp32 latent [B, C, T]."""
     import torch
     assert latent.is_cuda and latent.dtype == torch.float32 and latent.is_contiguous()
     b, _, t = latent.shape
-    pcm = torch.empty(b, 1, vocoder_output_length(ctx, t), device=latent.device)
+    pcm = torch.empty(b, out_channels(ctx), vocoder_output_length(ctx, t), device=latent.device)
     check(vocoder_decode(ctx, latent, b, t, pcm, stream), ctx)
     return pcm
 
 
 def decode_windows(ctx, windows, sides: int, last_frames: int, crop_left: int, crop_right: int,
                    stream=None):
-    """Planar pcm [sides, N] (new CUDA tensor) for CUDA fp32 windows
-    [n, sides * C, L] (vocoder_decode_windows)."""
+    """Planar pcm [sides * out_channels, N] (new CUDA tensor) for CUDA fp32
+    windows [n, sides * C, L] (vocoder_decode_windows)."""
     import torch
     assert windows.is_cuda and windows.dtype == torch.float32 and windows.is_contiguous()
     n, _, L = windows.shape
     N = vocoder_windows_output_length(ctx, n, L, last_frames, crop_left, crop_right)
     if N < 0:
         raise VocError(VOC_INVALID_PARAMS, "bad window lengths or crops")
-    pcm = torch.empty(sides, N, device=windows.device)
+    pcm = torch.empty(sides * out_channels(ctx), N, device=windows.device)
     check(vocoder_decode_windows(ctx, windows, n, sides, L, last_frames, crop_left, crop_right,
                                  pcm, stream), ctx)
     return pcm
 
 
 def stream_decode(ctx, latent, stream=None):
-    """pcm [rows, 1, t*hop] (new CUDA tensor) for the next chunk [rows, C, t]
-    of the streams started by vocoder_stream_reset."""
+    """pcm [rows, out_channels, t*hop] (new CUDA tensor) for the next chunk
+    [rows, C, t] of the streams started by vocoder_stream_reset."""
     import torch
     assert latent.is_cuda and latent.dtype == torch.float32 and latent.is_contiguous()
     rows, _, t = latent.shape
-    pcm = torch.empty(rows, 1, vocoder_output_length(ctx, t), device=latent.device)
+    pcm = torch.empty(rows, out_channels(ctx), vocoder_output_length(ctx, t), device=latent.device)
     check(vocoder_stream_decode(ctx, latent, t, pcm, stream), ctx)
     return pcm
 

@@ -17,10 +17,21 @@
  *    tokenizer decoder" and "Streaming decode (stateful path)")
  *     per residual unit with dilation d (1, 3, 9):
  *       h = h + conv2(Snake2(conv1_d(Snake1(h))))   conv1 k=7 dilation d, conv2 k=1
- *   pcm = tanh(conv_out(Snake(h)))              Conv1d k=7 to one channel, bias
+ *   pcm = tanh(conv_out(Snake(h)))              Conv1d k=7 to out_channels (1 or 2), bias
  *
  *   Snake(x)     = x + sin^2(alpha x) / (alpha + 1e-9)   alpha read verbatim
  *   SnakeBeta(x) = x + sin^2(alpha x) / (beta  + 1e-9)
+ *
+ * Alias-free configurations (af_snake = 1; the H3 audio VAE of the
+ * TensorSharp minimax-h3 page: every nonlinearity inside a 2x upsample /
+ * activate / 2x downsample sandwich) replace every Snake above by
+ *   AF(x) = down2(Snake(up2(x)))
+ * with one 12-tap Kaiser-windowed sinc low-pass f (cutoff a quarter of the
+ * 2x rate, transition half-width 0.3 of its sample rate, unit DC gain):
+ *   up2:   replicate-pad 5 frames, zero-stuff, filter with 2f, keep the 2T
+ *          samples aligned with x (u[n] sits at time n/2 - 1/4);
+ *   down2: replicate-pad 5 / 6 samples, filter with f, keep every second.
+ * Each AF output frame depends on input frames t-5 .. t+5.
  *
  * Weight norm is folded once at load: w = g * v / ||v||, the norm taken over
  * each slice along axis 0 of the stored tensor (minimaxmusic.cpp ARCHITECTURE,
@@ -50,7 +61,7 @@
 extern "C" {
 #endif
 
-#define VOC_ABI_VERSION 2
+#define VOC_ABI_VERSION 3
 #define VOC_MAX_BLOCKS 8
 #define VOC_MAX_RES 4
 
@@ -83,7 +94,8 @@ typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
  * width[n_blocks] <= 512; convt_crop == 0; tile_frames >= 0; in_proj >= 0;
  * causal is 0 or 1; an encoder (enc_width[0] > 0) needs every enc_width[b]
  * (b <= n_blocks) a positive multiple of 16 (F32) or 32 (BF16), at most
- * 8192, even strides and causal == 0.
+ * 8192, even strides and causal == 0; af_snake is 0 or 1, and 1 needs
+ * causal == 0 and no encoder; out_channels is 1 or 2.
  */
 typedef struct voc_config {
   int abi_version;
@@ -116,11 +128,17 @@ typedef struct voc_config {
                                    /* conv_in 1 -> enc_width[0], block b        */
                                    /* enc_width[b] -> enc_width[b+1] with the   */
                                    /* decoder's strides in reverse order        */
+  int af_snake;                    /* 0: plain Snake; 1: every Snake alias-free */
+                                   /* (the 2x up / Snake / 2x down sandwich     */
+                                   /* described above)                          */
+  int out_channels;                /* conv_out output channels: 1 (mono rows)   */
+                                   /* or 2 (one row decodes to stereo; the H3   */
+                                   /* audio VAE, 32 channels -> stereo 32 kHz)  */
 } voc_config;
 
 /* Fill *cfg with the full-width stereo window decoder: latent 64, widths
  * 1024/512/256/128/64, strides 8,8,4,2, dilations 1,3,9, Snake, F32, untiled,
- * no dec_in_proj. */
+ * no dec_in_proj, plain Snake, one output channel. */
 void voc_config_default(voc_config *cfg);
 
 /* Host-only checks of *cfg (no device is touched). */
@@ -150,7 +168,8 @@ voc_status vocoder_create(const voc_config *cfg, int hip_device, voc_ctx **out);
  *   blocks.{b}.conv_t1.{weight_v [Wb,Wb+1,2s], weight_g [Wb,1,1], bias [Wb+1]}
  *   blocks.{b}.res_units.{r}.snake1.alpha, .conv1.{weight_v [W,W,7], weight_g, bias},
  *                           .snake2.alpha, .conv2.{weight_v [W,W,1], weight_g, bias}
- *   snake_out.alpha [1,Wn,1];  conv_out.{weight_v [1,Wn,7], weight_g [1,1,1], bias [1]}
+ *   snake_out.alpha [1,Wn,1];  conv_out.{weight_v [O,Wn,7], weight_g [O,1,1], bias [O]}
+ *                                     (O = out_channels)
  * and with an encoder (E = enc_width, s_b = stride[n_blocks-1-b]):
  *   encoder.conv_in.{weight_v [E0,1,7], weight_g, bias}
  *   encoder.blocks.{b}.res_units.{r}.{snake1, conv1 [Eb,Eb,7], snake2, conv2 [Eb,Eb,1]}
@@ -181,7 +200,7 @@ int64_t vocoder_output_length(const voc_ctx *ctx, int64_t T);
 
 /*
  * Decode latent (device, fp32, [B, latent_channels, T] contiguous) into pcm
- * (device, fp32, [B, 1, T*hop] contiguous) on hip_stream (a hipStream_t;
+ * (device, fp32, [B, out_channels, T*hop] contiguous) on hip_stream (a hipStream_t;
  * NULL = the null stream).  Asynchronous: enqueues kernels and returns; no
  * host synchronization except when the library-owned workspace has to grow
  * (hipMalloc), the first time a larger B*T is seen.  Both buffers stay owned
@@ -210,8 +229,9 @@ voc_status vocoder_decode(voc_ctx *ctx, const float *latent, int64_t B, int64_t 
  *   the array is the [n_windows * sides, C, L] rows that vocoder_decode takes.
  *   The last window holds L_last valid frames (1 <= L_last <= L); its frames
  *   at and beyond L_last are ignored.
- * pcm: device fp32 [sides, N] planar ([L: N][R: N] for stereo) with
- *   N = vocoder_windows_output_length(...) samples per side.
+ * pcm: device fp32 [sides * out_channels, N] planar ([L: N][R: N] for
+ *   stereo; output channel o of side j is plane j * out_channels + o) with
+ *   N = vocoder_windows_output_length(...) samples per plane.
  * sides is 1 (mono) or 2 (stereo).  Every window must keep at least one
  * frame (e.g. L > crop_left + crop_right for the middle windows).  Requires
  * tile_frames == 0.  Same asynchrony and buffer ownership as vocoder_decode;
@@ -235,7 +255,7 @@ voc_status vocoder_decode_windows(voc_ctx *ctx, const float *latents, int64_t n_
  * (the next chunk decodes as the start of a clip: zero left padding).
  * vocoder_stream_decode decodes the next t >= 1 latent frames of every
  * stream, latent: device fp32 [rows, latent_channels, t] contiguous, into
- * pcm: device fp32 [rows, 1, t*hop] contiguous.  Each layer with context
+ * pcm: device fp32 [rows, out_channels, t*hop] contiguous.  Each layer with context
  * carries its last input frames from chunk to chunk ((K-1)*d frames for a
  * causal k=7 conv, one input frame for a ConvTranspose1d, whose polyphase
  * form needs x[n-1] where the pages carry the col2im tail), so every chunk
@@ -298,7 +318,8 @@ typedef enum voc_kernel_kind {
   VOC_K_IN_PROJ = 8,  /* dec_in_proj (k=1) GEMM                         */
   VOC_K_ENC_DOWN = 9, /* encoder strided Conv1d GEMM                    */
   VOC_K_ENC_OUT = 10, /* encoder conv_out (k=3) and projection (k=1)    */
-  VOC_K_COUNT = 11
+  VOC_K_AF_SNAKE = 11, /* alias-free Snake (2x up, Snake, 2x down)      */
+  VOC_K_COUNT = 12
 } voc_kernel_kind;
 
 typedef struct voc_profile_stat {

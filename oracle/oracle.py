@@ -216,6 +216,78 @@ def add(a, b, prec="f64"):
     return y
 
 
+# --------------------------------------------------------------------------
+# Alias-free Snake (TensorSharp minimax-h3.md: the H3 audio VAE wraps every
+# nonlinearity in a 2x upsample / activate / 2x downsample sandwich).  The
+# page gives no filter; the reading is the textbook windowed-sinc low-pass:
+# a Kaiser window (Kaiser's beta for the attenuation of the transition
+# band), 12 taps, cutoff at half the original Nyquist, transition half-width
+# 0.3 of it, normalised to unit DC gain, replicate padding at the clip ends.
+# --------------------------------------------------------------------------
+AF_TAPS = 12
+
+
+def kaiser_beta(atten_db: float) -> float:
+    """Kaiser's window parameter for a stop-band attenuation of atten_db."""
+    if atten_db > 50.0:
+        return 0.1102 * (atten_db - 8.7)
+    if atten_db >= 21.0:
+        return 0.5842 * (atten_db - 21.0) ** 0.4 + 0.07886 * (atten_db - 21.0)
+    return 0.0
+
+
+def af_filter(taps: int = AF_TAPS, cutoff: float = 0.25, half_width: float = 0.3) -> np.ndarray:
+    """Kaiser-windowed sinc low-pass, even length, centred between taps
+    (cutoff and half_width in cycles per sample at the 2x rate)."""
+    half = taps // 2
+    atten = 2.285 * (half - 1) * np.pi * (4.0 * half_width) + 7.95
+    beta = kaiser_beta(atten)
+    n = np.arange(taps)
+    window = np.i0(beta * np.sqrt(1.0 - ((2.0 * n) / (taps - 1) - 1.0) ** 2)) / np.i0(beta)
+    t = np.arange(-half, half) + 0.5
+    f = 2.0 * cutoff * window * np.sinc(2.0 * cutoff * t)
+    return f / f.sum()
+
+
+def upsample2(x, f=None):
+    """x [R, C, T] -> [R, C, 2T]: replicate-pad by half the taps / 2, insert a
+    zero after every sample, filter with 2 f (unit DC gain at the 2x rate),
+    keep the 2T samples aligned with x."""
+    f = af_filter() if f is None else f
+    k = f.size
+    pad = k // 2 - 1                              # 5 input samples each side
+    x = np.asarray(x, dtype=np.float64)
+    r, c, t = x.shape
+    xp = np.concatenate([np.repeat(x[:, :, :1], pad, 2), x, np.repeat(x[:, :, -1:], pad, 2)], axis=2)
+    z = np.zeros((r, c, 2 * xp.shape[2]))
+    z[:, :, ::2] = xp
+    full = np.zeros((r, c, z.shape[2] + k - 1))
+    for j in range(k):                            # full[n] = sum_j 2 f[j] z[n - j]
+        full[:, :, j:j + z.shape[2]] += 2.0 * f[j] * z
+    lo = 2 * pad + (k - 2) // 2                   # 15: the sample aligned with x[0]
+    return full[:, :, lo:lo + 2 * t]
+
+
+def downsample2(v, f=None):
+    """v [R, C, 2T] -> [R, C, T]: replicate-pad k/2 - 1 left and k/2 right,
+    filter with f and keep every second sample."""
+    f = af_filter() if f is None else f
+    k = f.size
+    v = np.asarray(v, dtype=np.float64)
+    n2 = v.shape[2]
+    vp = np.concatenate([np.repeat(v[:, :, :1], k // 2 - 1, 2), v, np.repeat(v[:, :, -1:], k // 2, 2)], axis=2)
+    out = np.zeros(v.shape[:2] + (n2 // 2,))
+    for j in range(k):                            # out[t] = sum_j f[j] vp[2t + j]
+        out += f[j] * vp[:, :, j:j + n2:2]
+    return out
+
+
+def af_snake(x, alpha, beta=None, prec="f64"):
+    """down2(Snake(up2(x))), per channel."""
+    u = upsample2(x)
+    return _c(downsample2(snake(u, alpha, beta, "f64")), prec)
+
+
 def round_bf16(x) -> np.ndarray:
     """Round to the nearest bfloat16 (ties to even) via float32; returns float64.
 
@@ -243,6 +315,7 @@ class Model:
         self.round_operands = round_operands and self.bf16
         self.beta = cfg["act"] == "snakebeta"
         self.causal = bool(cfg.get("causal", 0))
+        self.af = bool(cfg.get("af_snake", 0))
         self.norms = {}
         t = tensors
 
@@ -257,8 +330,16 @@ class Model:
         def vec(name):
             return _c(np.reshape(t[name], -1), prec)
 
+        # Snake parameters stored as logs (the H3 audio VAE of the TensorSharp
+        # minimax-h3 page keeps alpha and beta in log scale) are exponentiated
+        # once, at load.
+        log_params = bool(cfg.get("snake_log_params", 0))
+
         def act(prefix):
-            return (vec(prefix + ".alpha"), vec(prefix + ".beta") if self.beta else None)
+            def p(name):
+                v = np.reshape(np.asarray(t[name], dtype=np.float64), -1)
+                return _c(np.exp(v) if log_params else v, prec)
+            return (p(prefix + ".alpha"), p(prefix + ".beta") if self.beta else None)
 
         # dec_in_proj is stored without weight norm: used as given (bf16
         # configurations round it fp32 -> bf16 like the folded weights).
@@ -285,8 +366,9 @@ class Model:
 
     # ---- stages -----------------------------------------------------------
     def _snake(self, x, a, operand=True):
-        """Snake; in round_operands mode a matrix-core operand is rounded to bf16."""
-        y = snake(x, a[0], a[1], self.prec)
+        """Snake (alias-free when configured); in round_operands mode a
+        matrix-core operand is rounded to bf16."""
+        y = af_snake(x, a[0], a[1], self.prec) if self.af else snake(x, a[0], a[1], self.prec)
         if self.round_operands and operand:
             y = _c(round_bf16(y), self.prec)
         return y
@@ -340,7 +422,7 @@ class Model:
         return self.stage_upsample(b, x) if j == 0 else self.stage_res_unit(b, j - 1, x)
 
     def decode(self, latent, pre_tanh=False):
-        """latent [B, C_latent, T] -> pcm [B, 1, T*hop] (or the pre-tanh value)."""
+        """latent [B, C_latent, T] -> pcm [B, out_channels, T*hop] (or the pre-tanh value)."""
         h = self.stage_conv_in(latent)
         for b in range(len(self.blocks)):
             h = self.stage_upsample(b, h)
@@ -351,7 +433,8 @@ class Model:
     def decode_windows(self, windows, last_frames, crop_left, crop_right):
         """Windowed decode and stitch.  windows [n, sides*C, L]: side j of
         window k is channels [j*C, (j+1)*C); the last window holds
-        last_frames frames.  Returns planar [sides, N] (clamped to [-1, 1])."""
+        last_frames frames.  Returns planar [sides * out_channels, N] (output
+        channel o of side j in plane j * out_channels + o), clamped to [-1, 1]."""
         windows = np.asarray(windows)
         n, sc, L = windows.shape
         c = self.cfg["latent_channels"]
@@ -361,7 +444,8 @@ class Model:
         for k in range(n):
             length = last_frames if k == n - 1 else L
             x = windows[k, :, :length].reshape(sides, c, length)
-            y = self.decode(x)[:, 0, :]                      # [sides, length*hop]
+            y = self.decode(x)                               # [sides, O, length*hop]
+            y = y.reshape(-1, y.shape[-1])                   # plane j*O + o
             lo = crop_left if k > 0 else 0
             hi = length - (crop_right if k < n - 1 else 0)
             assert hi > lo, "every window must keep at least one frame"
@@ -375,7 +459,7 @@ class Model:
         latent = np.asarray(latent)
         bsz, _, t = latent.shape
         hop = self.cfg["hop"]
-        out = np.empty((bsz, 1, t * hop), dtype=_NP[self.prec])
+        out = np.empty((bsz, self.head[1].shape[0], t * hop), dtype=_NP[self.prec])
         for t0 in range(0, t, tile):
             t1 = min(t, t0 + tile)
             a, e = max(0, t0 - halo), min(t, t1 + halo)

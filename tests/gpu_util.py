@@ -31,18 +31,22 @@ def to_dev(a):
 
 def stage_halo(cfg, k):
     """(ups, input frames needed on the left, on the right) of debug stage k;
-    a causal stack's k=7 convs reach (K-1)*d frames left and none right."""
+    a causal stack's k=7 convs reach (K-1)*d frames left and none right; an
+    alias-free Snake reaches 5 frames each side at its rate."""
     nr = len(cfg["dilations"])
     n = 2 + len(cfg["strides"]) * (1 + nr)
     c = 2 if cfg.get("causal", 0) else 1
     r = 0 if cfg.get("causal", 0) else 1
-    if k == 0 or k == n - 1:
+    af = 5 if cfg.get("af_snake", 0) else 0
+    if k == 0:
         return 1, 3 * c, 3 * r
+    if k == n - 1:
+        return 1, 3 * c + af, 3 * r + af
     b, j = divmod(k - 1, 1 + nr)
     if j == 0:
-        return cfg["strides"][b], 2, 2
+        return cfg["strides"][b], 2 + af, 2 + af
     d = cfg["dilations"][j - 1]
-    return 1, 3 * d * c, 3 * d * r
+    return 1, 3 * d * c + 2 * af, 3 * d * r + 2 * af
 
 
 def oracle_stage_window(model, k, x_gpu, rows, a, e):

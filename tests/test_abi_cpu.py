@@ -53,14 +53,17 @@ def test_configs_validate(idx):
 
 
 @pytest.mark.parametrize("idx,strides,halo", [(1, None, 10), (4, None, 10), (5, None, 10),
-                                              (7, None, 20), (7, (8, 8, 4, 2), 19)])
+                                              (7, None, 20), (7, (8, 8, 4, 2), 19),
+                                              (9, None, 30), (9, (8, 8, 4, 2), 20)])
 def test_halo_matches_oracle_brute_force(idx, strides, halo):
-    # The oracle's tiling pin shows these halos reproduce the untiled decode
-    # and one frame less does not (causal stacks: the left halo); the
-    # library's interval propagation must land on the same values.
+    # The oracle's tiling pins show these halos reproduce the untiled decode
+    # and one frame less does not (causal stacks: the left halo; alias-free
+    # stacks: the structural reach a NaN marker shows); the library's
+    # interval propagation must land on the same values.
     d = dict(I.CONFIGS[idx])
     if strides:
         d["strides"] = strides
+        d["widths"] = d["widths"][:len(strides) + 1]
     assert V.voc_config_halo(V.config_from_dict(d)) == halo
 
 
@@ -79,7 +82,8 @@ def _bad(**kw):
     dict(dtype=3), dict(convt_crop=1), dict(tile_frames=-1), dict(latent_channels=60),
     dict(width=(2, 100)), dict(width=(4, 1024)), dict(stride=(0, 0)), dict(dilation=(1, 10)),
     dict(snake_log_params=2), dict(in_proj=-16), dict(in_proj=24), dict(in_proj=8208),
-    dict(causal=2), dict(causal=-1),
+    dict(causal=2), dict(causal=-1), dict(af_snake=2), dict(out_channels=0), dict(out_channels=3),
+    dict(af_snake=1, causal=1), dict(af_snake=1, enc_width=(0, 64)),
 ])
 def test_invalid_configs_rejected_before_any_device_call(kw):
     c = _bad(**kw)
@@ -102,3 +106,15 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(V, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         V.lib()
+
+
+def test_alias_free_snake_needs_a_plain_decoder():
+    """The alias-free Snake is built for non-causal decoders without an
+    encoder; the configurations that combine them are rejected on the host."""
+    for idx, why in ((8, "decoder only"), (7, "non-causal")):
+        c = V.config_from_dict(dict(I.CONFIGS[idx], af_snake=1))
+        assert V.voc_config_validate(c) == V.VOC_INVALID_PARAMS
+        st, ctx = V.vocoder_create(c, 0)
+        assert st == V.VOC_INVALID_PARAMS and not ctx.value
+        assert why in V.vocoder_last_error(None)
+    assert V.voc_config_validate(V.config_from_dict(I.CONFIGS[9])) == V.VOC_OK

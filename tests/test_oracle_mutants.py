@@ -1,9 +1,10 @@
 """The pins catch plausible mistakes: each test compiles a copy of oracle.c
 with one planted mistake (on the CPU, in a temporary directory), points the
 oracle module at that build, and requires that at least one pin fails.  The
-steps oracle.py itself orders (dec_in_proj, windowed decode and stitching)
-get the same treatment: a method of its Model is recompiled from its source
-with one planted mistake and patched in for the test.
+steps oracle.py itself orders (dec_in_proj, windowed decode and stitching,
+the alias-free Snake and its filter) get the same treatment: a method of
+its Model, or a function of the module, is recompiled from its source with
+one planted mistake and patched in for the test.
 
 A mutation that no pin notices would mean the pins leave that part of the
 oracle unchecked.
@@ -93,8 +94,30 @@ def test_planted_mistake_is_caught(name, orig, bad, tmp_path, monkeypatch):
         _pins(O)
 
 
-# (name, Model method, original text, planted mistake)
+# (name, Model method / "Class.method" / "fn:function", original text, planted mistake)
 PY_MUTANTS = [
+    ("af_up_crop_off_by_one", "fn:upsample2", "lo = 2 * pad + (k - 2) // 2", "lo = 2 * pad + (k - 2) // 2 + 1"),
+    ("af_up_gain_missing_2", "fn:upsample2", "+= 2.0 * f[j] * z", "+= f[j] * z"),
+    ("af_up_zero_pad", "fn:upsample2", "np.repeat(x[:, :, :1], pad, 2), x,",
+     "np.zeros(x.shape[:2] + (pad,)), x,"),
+    ("af_down_pads_swapped", "fn:downsample2",
+     "np.repeat(v[:, :, :1], k // 2 - 1, 2), v, np.repeat(v[:, :, -1:], k // 2, 2)",
+     "np.repeat(v[:, :, :1], k // 2, 2), v, np.repeat(v[:, :, -1:], k // 2 - 1, 2)"),
+    ("af_down_zero_pad", "fn:downsample2", "np.repeat(v[:, :, :1], k // 2 - 1, 2)",
+     "np.zeros(v.shape[:2] + (k // 2 - 1,))"),
+    ("af_filter_no_window", "fn:af_filter", "f = 2.0 * cutoff * window * np.sinc(2.0 * cutoff * t)",
+     "f = 2.0 * cutoff * np.sinc(2.0 * cutoff * t)"),
+    ("af_filter_not_normalised", "fn:af_filter", "return f / f.sum()", "return f"),
+    ("af_filter_centred_on_a_tap", "fn:af_filter", "t = np.arange(-half, half) + 0.5",
+     "t = np.arange(-half, half) + 1.0"),
+    ("kaiser_beta_wrong_branch", "fn:kaiser_beta", "return 0.1102 * (atten_db - 8.7)",
+     "return 0.5842 * (atten_db - 21.0) ** 0.4 + 0.07886 * (atten_db - 21.0)"),
+    ("af_snake_is_plain", "fn:af_snake", 'return _c(downsample2(snake(u, alpha, beta, "f64")), prec)',
+     'return _c(snake(x, alpha, beta, "f64"), prec)'),
+    ("model_ignores_af", "_snake", "y = af_snake(x, a[0], a[1], self.prec) if self.af else",
+     "y = snake(x, a[0], a[1], self.prec) if self.af else"),
+    ("log_params_not_exponentiated", "__init__", "return _c(np.exp(v) if log_params else v, prec)",
+     "return _c(v, prec)"),
     ("window_first_cropped", "decode_windows", "lo = crop_left if k > 0 else 0", "lo = crop_left"),
     ("window_last_cropped", "decode_windows", "hi = length - (crop_right if k < n - 1 else 0)",
      "hi = length - crop_right"),
@@ -140,6 +163,12 @@ def _py_pins(orc):
     P.test_window_stitch_bookkeeping_at_the_pages_sizes(orc)
     P.test_windows_cut_from_one_track_equal_its_decode(orc)
     P.test_windows_planar_sides_and_single_window(orc)
+    P.test_af_filter_is_the_kaiser_windowed_sinc(orc)
+    P.test_af_resamplers_match_torch_routines(orc)
+    P.test_af_upsampler_delay_and_gain(orc)
+    P.test_af_snake_reach_is_five_frames(orc)
+    P.test_alias_free_decode_matches_torch_composition(orc, (5, 2), "snakebeta")
+    P.test_log_stored_snake_parameters_are_exponentiated(orc)
 
 
 def test_python_pins_pass_on_the_real_oracle():
@@ -148,11 +177,15 @@ def test_python_pins_pass_on_the_real_oracle():
 
 @pytest.mark.parametrize("name,method,orig,bad", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
 def test_planted_python_mistake_is_caught(name, method, orig, bad, monkeypatch):
-    cls, meth = method.split(".") if "." in method else ("Model", method)
-    src = textwrap.dedent(inspect.getsource(getattr(getattr(O, cls), meth)))
+    if method.startswith("fn:"):
+        owner, meth = O, method[3:]
+    else:
+        cls, meth = method.split(".") if "." in method else ("Model", method)
+        owner = getattr(O, cls)
+    src = textwrap.dedent(inspect.getsource(getattr(owner, meth)))
     assert src.count(orig) == 1, f"mutation site not unique: {name}"
     ns = dict(vars(O))
     exec(compile(src.replace(orig, bad), f"<mutant {name}>", "exec"), ns)
-    monkeypatch.setattr(getattr(O, cls), meth, ns[meth])
+    monkeypatch.setattr(owner, meth, ns[meth])
     with pytest.raises(AssertionError):
         _py_pins(O)

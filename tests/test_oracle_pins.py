@@ -5,7 +5,10 @@ closed forms, brute-force sums written independently on tiny inputs,
 textbook identities (matrix product, polyphase decomposition, zero-stuffed
 convolution via numpy.convolve), PyTorch's float64 CPU convolutions (a library
 routine), and invariants the pages state (output length T*hop, the 12-frame
-vocoder gate, L != R, tanh range, exact halo tiling).
+vocoder gate, L != R, tanh range, exact halo tiling).  The alias-free Snake
+is held to SciPy's Kaiser window design and to PyTorch's resampling
+convolutions, to the delay and gain a linear-phase filter must have, to its
+reach, and to the aliasing it exists to remove.
 """
 import json
 import math
@@ -22,10 +25,10 @@ RNG = np.random.default_rng(12345)
 
 
 def tiny_cfg(strides=(2, 2), widths=(8, 6, 4), latent=3, act="snake", dil=(1, 3, 9), in_proj=0,
-             causal=0):
+             causal=0, **kw):
     return I.config(0, strides=tuple(strides), widths=tuple(widths), latent_channels=latent,
                     act=act, dilations=tuple(dil), frames=9, batch=2, in_proj=in_proj,
-                    causal=causal)
+                    causal=causal, **kw)
 
 
 # ----------------------------------------------------------------- Snake
@@ -290,10 +293,17 @@ def torch_decode(cfg, t, latent):
         n = v.reshape(v.shape[0], -1).norm(dim=1)
         return v * (g / n).reshape(-1, 1, 1)
 
+    logp = bool(cfg.get("snake_log_params", 0))
+
+    def par(name):
+        v = T[name].reshape(1, -1, 1)
+        return torch.exp(v) if logp else v
+
     def sn(x, p):
-        a = T[p + ".alpha"].reshape(1, -1, 1)
-        den = (T[p + ".beta"] if cfg["act"] == "snakebeta" else T[p + ".alpha"]).reshape(1, -1, 1)
-        return x + torch.sin(a * x) ** 2 / (den + 1e-9)
+        a = par(p + ".alpha")
+        den = par(p + ".beta") if cfg["act"] == "snakebeta" else a
+        y = lambda z: z + torch.sin(a * z) ** 2 / (den + 1e-9)  # noqa: E731
+        return torch_af(x, y) if cfg.get("af_snake", 0) else y(x)
 
     causal = bool(cfg.get("causal", 0))
 
@@ -331,6 +341,19 @@ def test_decode_matches_torch_composition(orc, strides, act, in_proj, causal):
     lat = I.make_latent(cfg)
     y = orc.Model(cfg, t).decode(lat)
     np.testing.assert_allclose(y, torch_decode(cfg, t, lat), atol=1e-11)
+
+
+@pytest.mark.parametrize("strides,act", [((5, 2), "snakebeta"), ((2, 2), "snake")])
+def test_alias_free_decode_matches_torch_composition(orc, strides, act):
+    """The H3 audio VAE shape: every Snake alias-free, Snake parameters
+    stored as logs, two output channels."""
+    cfg = tiny_cfg(strides=strides, act=act, af_snake=1, snake_log_params=1, out_channels=2)
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg)
+    y = orc.Model(cfg, t).decode(lat)
+    assert y.shape == (2, 2, 9 * cfg["hop"])
+    np.testing.assert_allclose(y, torch_decode(cfg, t, lat), atol=1e-11)
+    assert np.abs(y[:, 0] - y[:, 1]).max() > 1e-3      # two distinct channels
 
 
 def test_golden_lengths_and_vocoder_gate(orc):
@@ -371,9 +394,127 @@ def test_precision_floor_build_is_float32(orc):
     assert 1e-9 < err < 1e-4
 
 
+# ---------------------------------------------------- alias-free Snake
+# Reading (TensorSharp minimax-h3 page, audio VAE; the page names no filter):
+# the windowed-sinc low-pass of the BigVGAN anti-aliased activation --
+# 12 taps, Kaiser window, cutoff a quarter of the 2x sample rate, transition
+# half-width 0.3 -- with replicate padding at the clip ends.
+AF_ATTEN = 2.285 * 5 * math.pi * 1.2 + 7.95    # Kaiser's attenuation formula, 6 half-taps
+
+
+def scipy_af_filter():
+    from scipy import signal
+    return signal.firwin(12, 0.5, window=("kaiser", signal.kaiser_beta(AF_ATTEN)))
+
+
+def torch_af(x, act):
+    """down2(act(up2(x))) from PyTorch's strided (transposed) convolutions."""
+    F = torch.nn.functional
+    f = torch.from_numpy(scipy_af_filter())
+    c = x.shape[1]
+    t = x.shape[-1]
+    up = F.conv_transpose1d(F.pad(x, (5, 5), mode="replicate"), (2 * f).repeat(c, 1, 1), stride=2,
+                            groups=c)[..., 15:15 + 2 * t]
+    return F.conv1d(F.pad(act(up), (5, 6), mode="replicate"), f.repeat(c, 1, 1), stride=2, groups=c)
+
+
+def test_af_filter_is_the_kaiser_windowed_sinc(orc):
+    from scipy import signal
+    for a in (10.0, 21.0, 30.0, 45.0, 50.0, AF_ATTEN, 70.0):
+        assert orc.kaiser_beta(a) == pytest.approx(signal.kaiser_beta(a), rel=1e-12, abs=1e-15)
+    f = orc.af_filter()
+    np.testing.assert_allclose(f, scipy_af_filter(), rtol=1e-12, atol=1e-15)
+    assert f.sum() == pytest.approx(1.0, abs=1e-15)
+    np.testing.assert_allclose(f, f[::-1], rtol=0, atol=1e-16)   # linear phase
+    # Both polyphase halves sum to 1/2: a constant passes the upsampler exactly.
+    assert f[0::2].sum() == pytest.approx(0.5, abs=1e-15) and f[1::2].sum() == pytest.approx(0.5, abs=1e-15)
+
+
+def test_af_resamplers_match_torch_routines(orc):
+    x = RNG.normal(0, 1, (2, 3, 17))
+    ident = lambda z: z                                 # noqa: E731
+    np.testing.assert_allclose(orc.downsample2(orc.upsample2(x)), torch_af(torch.from_numpy(x), ident).numpy(),
+                               atol=1e-14)
+    u = orc.upsample2(x)
+    assert u.shape == (2, 3, 34)
+    np.testing.assert_allclose(orc.downsample2(u * 0 + 1.5), np.full((2, 3, 17), 1.5), atol=1e-14)
+    np.testing.assert_allclose(orc.upsample2(x * 0 - 0.75), np.full((2, 3, 34), -0.75), atol=1e-14)
+
+
+def test_af_upsampler_delay_and_gain(orc):
+    """A tone cos(w n) comes out of the 2x upsampler as G cos(w (n/2 - 1/4)):
+    the filter is linear phase with its centre 5.5 samples into 12 taps, and
+    the crop puts sample n at time n/2 - 1/4.  Zero-stuffing halves the
+    tone's amplitude and the filter's gain of 2 restores it, so G is the
+    filter's amplitude response at w/2 (DTFT about its centre); the image at
+    pi - w/2 is left at the stop-band level."""
+    f = orc.af_filter()
+    for w in (0.2 * np.pi, 0.45 * np.pi):
+        n = np.arange(200)
+        x = np.cos(w * n)[None, None, :]
+        u = orc.upsample2(x)[0, 0, 40:360]
+        m = np.arange(40, 360)
+        G = np.sum(f * np.cos(w / 2 * (np.arange(12) - 5.5)))
+        assert np.abs(u - G * np.cos(w * (m / 2 - 0.25))).max() < 6e-3
+        for wrong in (0.0, 0.5):                         # other alignments miss by far more
+            assert np.abs(u - G * np.cos(w * (m / 2 - wrong))).max() > 0.05
+    # Round trip of a low tone: the same response once per filter, no delay.
+    x = np.cos(0.1 * np.pi * np.arange(200))[None, None, :]
+    y = orc.downsample2(orc.upsample2(x))[0, 0, 20:180]
+    g = np.sum(f * np.cos(0.05 * np.pi * (np.arange(12) - 5.5)))
+    np.testing.assert_allclose(y, g * g * x[0, 0, 20:180], atol=3e-3)
+
+
+def test_af_snake_reach_is_five_frames(orc):
+    x = RNG.normal(0, 1, (1, 3, 40))
+    a, b = np.array([1.0, 0.7, 1.5]), np.array([0.9, 1.2, 0.6])
+    y0 = orc.af_snake(x, a, b)
+    for d, moves in ((5, True), (6, False)):
+        for sgn in (1, -1):
+            x2 = x.copy()
+            x2[..., 20 + sgn * d] += 1.0
+            diff = np.abs(orc.af_snake(x2, a, b) - y0)[..., 20].max()
+            assert (diff > 1e-8) == moves, (d, sgn, diff)
+
+
+def test_af_snake_suppresses_the_alias_plain_snake_makes(orc):
+    """Snake adds even harmonics of a tone.  For a tone at 0.23 cycles per
+    sample, plain Snake folds the fourth harmonic (0.92) back to 0.08; the
+    alias-free Snake forms it at the 2x rate (0.46 cycles there), where the
+    low-pass removes it before the decimation, so the level at 0.08 drops by
+    more than 30x while the tone itself passes unchanged."""
+    n = np.arange(4096)
+    x = 0.8 * np.cos(2 * np.pi * 0.23 * n)[None, None, :]
+    alpha = np.array([2.0])
+
+    def level(y, nu):
+        z = y[0, 0, 512:-512]
+        k = np.arange(z.size)
+        return abs(np.sum(z * np.exp(-2j * np.pi * nu * k))) / z.size
+
+    plain = orc.snake(x, alpha, None)
+    af = orc.af_snake(x, alpha, None)
+    assert level(plain, 0.08) > 0.03
+    assert level(af, 0.08) < level(plain, 0.08) / 30
+    assert level(af, 0.23) == pytest.approx(level(plain, 0.23), rel=0.02)
+
+
+def test_log_stored_snake_parameters_are_exponentiated(orc):
+    cfg = tiny_cfg(act="snakebeta")
+    t = I.make_weights(cfg)
+    tl = dict(t)
+    for k in t:
+        if k.endswith(".alpha") or k.endswith(".beta"):
+            tl[k] = np.log(t[k].astype(np.float64))
+    lat = I.make_latent(cfg)
+    ref = orc.Model(cfg, t).decode(lat)
+    got = orc.Model(dict(cfg, snake_log_params=1), tl).decode(lat)
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
 # --------------------------------------------------------------- tiling
-def _halo_case(strides, widths, frames, tile, causal=0):
-    cfg = I.config(0, strides=tuple(strides), widths=tuple(widths), latent_channels=4, causal=causal)
+def _halo_case(strides, widths, frames, tile, causal=0, **kw):
+    cfg = I.config(0, strides=tuple(strides), widths=tuple(widths), latent_channels=4, causal=causal, **kw)
     t = I.make_weights(cfg, twin=True)
     lat = I.make_latent(cfg, batch=1, frames=frames)
     return cfg, t, lat
@@ -392,6 +533,30 @@ def test_tiling_exact_halo(orc, strides, halo_ok, causal):
     assert np.abs(good - ref).max() <= 1e-10
     bad = m.decode_tiled(lat, 20, halo_ok - 1)
     assert np.abs(bad - ref).max() > 1e-6
+
+
+@pytest.mark.parametrize("strides,halo,frames", [((8, 8, 4, 2), 20, 50), ((5, 5, 2, 2, 2, 2, 2), 30, 66)])
+def test_alias_free_tiling_exact_halo(orc, strides, halo, frames):
+    """Alias-free Snakes widen the receptive field by 5 frames each side per
+    Snake at its rate.  A NaN placed in one latent frame marks every output
+    that depends on it, however weakly: it reaches exactly `halo` frames each
+    way.  (The outermost dependencies pass through the low-pass's smallest
+    taps many times over and fall below double precision, so a numerical
+    search would stop short of the structural halo.)  Tiles with that halo
+    reproduce the untiled decode bit for bit; half of it does not."""
+    widths = (8,) * (len(strides) + 1)
+    cfg, t, lat = _halo_case(strides, widths, frames, 10, 0, af_snake=1)
+    m = orc.Model(cfg, t)
+    hop = cfg["hop"]
+    j = frames // 2
+    marked = lat.copy()
+    marked[:, :, j] = np.nan
+    with np.errstate(invalid="ignore"):
+        hit = np.where(np.isnan(m.decode(marked)[0, 0]))[0] // hop - j
+    assert (hit.min(), hit.max()) == (-halo, halo)
+    ref = m.decode(lat)
+    assert np.array_equal(m.decode_tiled(lat, 10, halo), ref)
+    assert np.abs(m.decode_tiled(lat, 10, halo // 2) - ref).max() > 1e-10
 
 
 # ----------------------------------------------------------- dec_in_proj
