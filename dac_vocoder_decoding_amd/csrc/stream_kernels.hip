@@ -336,20 +336,34 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
 // nonlinearity between a 2x upsample and a 2x downsample; the 12-tap
 // low-pass and its phases are described with AfArgs).  A thread owns four
 // channels of one 16-channel chunk and a run of kAfRun consecutive output
-// frames.  Output t needs the activated 2x-rate samples v[2t-5 .. 2t+6] and
-// the next two, v[2t+7] and v[2t+8], both come from input frames
-// x[t+1 .. t+6].  So a run warms up on x[t0-5 .. t0+5] (twelve v samples)
-// and then slides: per frame one new input frame, two upsampled samples,
-// two Snakes and one 12-tap output.  Frames read outside [0, len) repeat the
-// edge frame (replicate padding of the upsampler); 2x-rate samples outside
-// [0, 2 len) repeat the edge sample (replicate padding of the downsampler).
-// Lanes 4k .. 4k+3 read one 64-byte frame row, the 16 runs of a wave sit
-// kAfRun frames apart; the sliding reads walk each row's cache lines in
-// order.
+// frames.  Output t sums fd[j] v[2t-5+j], j = 0 .. 11, over the activated
+// 2x-rate samples v; the samples v[2t+7], v[2t+8] that output t+1 adds both
+// come from input frames x[t+1 .. t+6].  A run warms up on x[t0-5 .. t0+5]
+// (twelve samples) and then slides: per frame one new input frame, two
+// upsampled samples of six taps, two Snakes.  It keeps no samples, only the
+// six outputs they feed, partially summed: each new pair is added to
+// outputs t+1 .. t+6 with their taps, after which output t+1 is complete.
+// Every output thus sums its twelve terms in tap order from zero with FMAs,
+// whichever run computes it, so tiles and windows of a clip give the same
+// bits as the whole clip.
+// Edges without branches: input frames outside [0, len) repeat the edge
+// frame (clamped loads; the upsampler's replicate padding), and a 2x-rate
+// sample past either end repeats the edge sample (the downsampler's): one
+// select per sample (v[n < 0] = v[0], which only a run starting at frame 0
+// meets, as its sixth warm-up sample; v[n > 2 len - 1] = the previous
+// sample).  Lanes 4k .. 4k+3 read one 64-byte frame row; the 16 runs of a
+// wave sit kAfRun frames apart, each walking its rows' cache lines in order.
 constexpr int kAfRun = 16;
+#ifndef VOC_AF_PREFETCH
+#define VOC_AF_PREFETCH 1
+#endif
+#ifndef VOC_AF_MIN_WAVES
+#define VOC_AF_MIN_WAVES 4  // launch bound: fewest waves per SIMD the registers must allow
+#endif
+constexpr int kAfPrefetch = VOC_AF_PREFETCH;  // input frames requested ahead of their use
 
 template <int OUT_OP>
-__global__ __launch_bounds__(256) void af_snake_kernel(const AfArgs a) {
+__global__ __launch_bounds__(256, VOC_AF_MIN_WAVES) void af_snake_kernel(const AfArgs a) {
   const int r = blockIdx.y;
   const int nchunk = a.C / 16;
   const int chunk = blockIdx.x % nchunk;
@@ -360,73 +374,97 @@ __global__ __launch_bounds__(256) void af_snake_kernel(const AfArgs a) {
   if (t0 >= len) return;
   const int c = chunk * 16 + q * 4;
   const float* xp = a.x + (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * 4;
+  const f4 sc = *reinterpret_cast<const f4*>(a.scale + c);
+  const f4 hh = *reinterpret_cast<const f4*>(a.hh + c);
+  // Output element index of frame 0 of this thread's four channels.
+  const int64_t orow = OUT_OP == OP_F32 ? (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * 4
+                                        : (static_cast<int64_t>(r) * a.C + (c / 32) * 32) * a.T + c % 32;
+  char* obase = static_cast<char*>(a.out);
+  const int n_last = 2 * len - 1;
   auto ld = [&](int t) -> f4 {
     t = min(max(t, 0), len - 1);
     return *reinterpret_cast<const f4*>(xp + static_cast<int64_t>(t) * kHChunk);
   };
-  const f4 sc = *reinterpret_cast<const f4*>(a.scale + c);
-  const f4 hh = *reinterpret_cast<const f4*>(a.hh + c);
   auto snake4 = [&](f4 u) -> f4 {
     f4 v;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = snake_f32(u[e], sc[e], hh[e]);
     return v;
   };
-  // Warm-up.  X[k] = x[t0 - 5 + k]; V[i] = v[n], n = 2 t0 - 5 + i:
-  //   i odd  (n = 2m,   m = t0 + (i - 5) / 2): fe taps on X[(i - 1) / 2 .. + 5]
-  //   i even (n = 2m+1, m = t0 + (i - 6) / 2): fo taps on X[i / 2 .. + 5]
-  f4 X[11];
+  auto pick = [](bool cond, f4 x, f4 y) -> f4 {  // cond ? x : y, per element
+    f4 o;
 #pragma unroll
-  for (int k = 0; k < 11; ++k) X[k] = ld(t0 - 5 + k);
-  f4 V[12];
+    for (int e = 0; e < 4; ++e) o[e] = cond ? x[e] : y[e];
+    return o;
+  };
+  // A[k] collects output t + k (t = t0 at the start).
+  f4 A[6];
 #pragma unroll
-  for (int i = 0; i < 12; ++i) {
-    const int b = (i & 1) ? (i - 1) / 2 : i / 2;
-    f4 u = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 6; ++k) u += ((i & 1) ? a.fe[k] : a.fo[k]) * X[b + k];
-    V[i] = snake4(u);
-  }
-  const int n_last = 2 * len - 1;
-#pragma unroll
-  for (int i = 10; i >= 0; --i)
-    if (2 * t0 - 5 + i < 0) V[i] = V[i + 1];
-#pragma unroll
-  for (int i = 1; i < 12; ++i)
-    if (2 * t0 - 5 + i > n_last) V[i] = V[i - 1];
-  // R[k] = x[t + 1 + k] while output t is formed (R[5] loaded per frame).
+  for (int k = 0; k < 6; ++k) A[k] = f4{0.f, 0.f, 0.f, 0.f};
   f4 R[6];
+  f4 vlast;
+  {
+    // Warm-up.  X[k] = x[t0 - 5 + k]; sample i is v[n], n = 2 t0 - 5 + i:
+    //   i odd  (n = 2m,   m = t0 + (i - 5) / 2): fe taps on X[(i - 1) / 2 .. + 5]
+    //   i even (n = 2m+1, m = t0 + (i - 6) / 2): fo taps on X[i / 2 .. + 5]
+    f4 X[11];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) R[k] = X[6 + k];
-  const int nvalid = min(kAfRun, len - t0);
-  char* obase = static_cast<char*>(a.out);
+    for (int k = 0; k < 11; ++k) X[k] = ld(t0 - 5 + k);
+    auto sample = [&](int i) -> f4 {
+      const int b = (i & 1) ? (i - 1) / 2 : i / 2;
+      f4 u = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 6; ++k) u += ((i & 1) ? a.fe[k] : a.fo[k]) * X[b + k];
+      return snake4(u);
+    };
+    const f4 v5 = sample(5);  // v[2 t0]: v[0] for the run that starts the row
+    vlast = v5;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      const int n = 2 * t0 - 5 + i;
+      f4 v = i == 5 ? v5 : sample(i);
+      v = pick(n < 0, v5, v);
+      v = pick(n > n_last, vlast, v);
+      vlast = v;
+#pragma unroll
+      for (int k = 0; k < 6; ++k)
+        if (i - 2 * k >= 0) A[k] += a.fd[i - 2 * k] * v;  // tap i - 2k of output t0 + k
+    }
+#pragma unroll
+    for (int k = 0; k < 5; ++k) R[k] = X[6 + k];
+  }
+  f4 nx[kAfRun];  // nx[s] = x[t0 + s + 6]
+#pragma unroll
+  for (int s = 0; s < kAfPrefetch; ++s) nx[s] = ld(t0 + s + 6);
 #pragma unroll
   for (int s = 0; s < kAfRun; ++s) {
     const int t = t0 + s;
-    f4 y = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < kAfTaps; ++j) y += a.fd[j] * V[j];
-    if (s < nvalid) {
-      if constexpr (OUT_OP == OP_F32) {
-        const int64_t idx = (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + static_cast<int64_t>(t) * 16 + q * 4;
-        store_op4<OP_F32>(obase, idx, y);
-      } else {
-        const int64_t idx = (static_cast<int64_t>(r) * a.C + (c / 32) * 32) * a.T + static_cast<int64_t>(t) * 32 + c % 32;
-        store_op4<OP_BF16>(obase, idx, y);
-      }
+    if (s + kAfPrefetch < kAfRun - 1) nx[s + kAfPrefetch] = ld(t + kAfPrefetch + 6);
+    if (t < len) {
+      if constexpr (OUT_OP == OP_F32)
+        store_op4<OP_F32>(obase, orow + static_cast<int64_t>(t) * 16, A[0]);
+      else
+        store_op4<OP_BF16>(obase, orow + static_cast<int64_t>(t) * 32, A[0]);
     }
     if (s + 1 < kAfRun) {
-      R[5] = ld(t + 6);
+      R[5] = nx[s];
       f4 uo = f4{0.f, 0.f, 0.f, 0.f}, ue = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < 6; ++k) {
-        uo += a.fo[k] * R[k];  // v[2t + 7]: m = t + 3
-        ue += a.fe[k] * R[k];  // v[2t + 8]: m = t + 4
+        uo += a.fo[k] * R[k];  // v[2t + 7]
+        ue += a.fe[k] * R[k];  // v[2t + 8]
       }
+      const f4 vo = pick(2 * t + 7 > n_last, vlast, snake4(uo));
+      const f4 ve = pick(2 * t + 8 > n_last, vo, snake4(ue));
+      vlast = ve;
 #pragma unroll
-      for (int i = 0; i < 10; ++i) V[i] = V[i + 2];
-      V[10] = 2 * t + 7 > n_last ? V[9] : snake4(uo);
-      V[11] = 2 * t + 8 > n_last ? V[10] : snake4(ue);
+      for (int k = 0; k < 5; ++k) A[k] = A[k + 1];
+      A[5] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {  // output t + 1 + k: taps 10 - 2k and 11 - 2k
+        A[k] += a.fd[10 - 2 * k] * vo;
+        A[k] += a.fd[11 - 2 * k] * ve;
+      }
 #pragma unroll
       for (int k = 0; k < 5; ++k) R[k] = R[k + 1];
     }
