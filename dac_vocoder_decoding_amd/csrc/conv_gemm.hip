@@ -395,6 +395,12 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
 }
 
 // Block-tile families: {m-blocks per wave, n-blocks per wave, waves along M, waves along N}.
+#ifndef VOC_NARROW16
+#define VOC_NARROW16 1, 2, 1, 4
+#endif
+#ifndef VOC_NARROW32
+#define VOC_NARROW32 2, 2, 1, 4
+#endif
 struct VariantShape { int wmb, wnb, wav_m, wav_n; };
 static constexpr VariantShape kVariants[CV_COUNT] = {
     {4, 8, 2, 2},  // CV_128x256
@@ -403,12 +409,16 @@ static constexpr VariantShape kVariants[CV_COUNT] = {
     {4, 4, 2, 2},  // CV_128x128
     {4, 2, 1, 4},  // CV_64x128
     {6, 4, 2, 2},  // CV_192x128
+    {VOC_NARROW16},  // CV_16x128
+    {VOC_NARROW32},  // CV_32x128
 };
 
 int conv_variant_bm(int v) { return kVariants[v].wav_m * kVariants[v].wmb * 16; }
 int conv_variant_bn(int v) { return kVariants[v].wav_n * kVariants[v].wnb * 16; }
 bool conv_variant_ok(int v, int taps) {
   if (v < 0 || v >= CV_COUNT) return false;
+  // The narrow-M tiles serve the k=7 convs of narrow units only.
+  if (v == CV_16x128 || v == CV_32x128) return taps == 7;
   // All taps' weight rows of a chunk live in LDS: keep two workgroups per CU.
   if (taps == 7 || taps == 3) return v == CV_64x256 || v == CV_96x256 || v == CV_64x128;
   return true;
@@ -452,6 +462,18 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
     VOC_CASE(CV_128x256, 4, 8, 2, 2)
     VOC_CASE(CV_128x128, 4, 4, 2, 2)
     VOC_CASE(CV_192x128, 6, 4, 2, 2)
+#undef VOC_CASE
+#define VOC_CASE(V, A, B, C, D)                                                              \
+  case V:                                                                                    \
+    if constexpr (TAPS == 7) {                                                               \
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS>), grid, block, 0, s, a); \
+      break;                                                                                 \
+    }                                                                                        \
+    return hipErrorInvalidValue;
+#define VOC_CASE_SHAPE(V, ...) VOC_CASE(V, __VA_ARGS__)  // expands the shape macro first
+    VOC_CASE_SHAPE(CV_16x128, VOC_NARROW16)
+    VOC_CASE_SHAPE(CV_32x128, VOC_NARROW32)
+#undef VOC_CASE_SHAPE
 #undef VOC_CASE
     default:
       return hipErrorInvalidValue;

@@ -80,7 +80,9 @@ enum ConvVariant {
   CV_128x128 = 3,
   CV_64x128 = 4,
   CV_192x128 = 5,
-  CV_COUNT = 6
+  CV_16x128 = 6,   // narrow-M tiles for the k=7 convs of 16- and 32-channel units
+  CV_32x128 = 7,
+  CV_COUNT = 8
 };
 int conv_variant_bm(int v);
 int conv_variant_bn(int v);
