@@ -196,6 +196,13 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
 
+// Matrix-core loop microbenchmark: mfma_loop_blocks() workgroups of 256
+// threads each run `iters` iterations of independent MFMA chains of the
+// operand dtype op; out receives one float per thread.
+int mfma_loop_blocks();
+double mfma_loop_flops(int op, int64_t iters);
+hipError_t launch_mfma_loop(int op, int64_t iters, float* out, hipStream_t s);
+
 // Alias-free Snake over a residual-stream tensor (fp32 chunked, 16 channels
 // per 64-byte frame row): per row r with valid frames [0, len), len =
 // min(row_len[r] * rate, T),

@@ -1,0 +1,59 @@
+// peak_kernels.hip -- microbenchmarks of what the MI355X delivers, reported
+// beside the published peaks: a matrix-core loop per operand dtype (the
+// same 16x16 MFMA fragments the convolutions issue).  The HBM side uses the
+// plain copy kernel of stream_kernels.hip.
+#include "internal.h"
+#include "gemm_common.h"
+
+namespace voc {
+
+// Each wave runs kChains independent accumulator chains of mfma_frag (four
+// 16x16x4 fp32 MFMAs, or one 16x16x32 bf16 MFMA) so that the matrix pipe
+// never waits on a result; operands stay in registers; the sums are
+// written out so that nothing is dead code.
+constexpr int kChains = 8;
+
+template <int OP>
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int64_t iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  uint4 a, b;
+  if constexpr (OP == OP_F32) {
+    const float x = 1e-3f * static_cast<float>(lane + 1), y = 1e-3f * static_cast<float>(64 - lane);
+    a = make_uint4(__float_as_uint(x), __float_as_uint(y), __float_as_uint(x), __float_as_uint(y));
+    b = make_uint4(__float_as_uint(y), __float_as_uint(x), __float_as_uint(y), __float_as_uint(x));
+  } else {
+    const uint32_t x = pack_bf16x2(1e-3f * static_cast<float>(lane + 1), 1e-3f);
+    const uint32_t y = pack_bf16x2(1e-3f, 1e-3f * static_cast<float>(64 - lane));
+    a = make_uint4(x, y, x, y);
+    b = make_uint4(y, x, y, x);
+  }
+  f4 acc[kChains];
+#pragma unroll
+  for (int k = 0; k < kChains; ++k) acc[k] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) mfma_frag<OP>(a, b, acc[k]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kChains; ++k) s += acc[k][0] + acc[k][1] + acc[k][2] + acc[k][3];
+  out[static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x] = s;
+}
+
+int mfma_loop_blocks() { return 256 * 8; }  // 8 workgroups of 4 waves per CU
+
+double mfma_loop_flops(int op, int64_t iters) {
+  const double per_frag = op == OP_F32 ? 4.0 * 16 * 16 * 4 * 2 : 16.0 * 16 * 32 * 2;
+  return static_cast<double>(mfma_loop_blocks()) * 4 * iters * kChains * per_frag;
+}
+
+hipError_t launch_mfma_loop(int op, int64_t iters, float* out, hipStream_t s) {
+  const dim3 grid(mfma_loop_blocks()), block(256);
+  if (op == OP_F32)
+    hipLaunchKernelGGL(mfma_loop_kernel<OP_F32>, grid, block, 0, s, iters, out);
+  else
+    hipLaunchKernelGGL(mfma_loop_kernel<OP_BF16>, grid, block, 0, s, iters, out);
+  return hipGetLastError();
+}
+
+}  // namespace voc

@@ -1961,6 +1961,56 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
                 [&] { return launch_export(h, out, rows, si.c_out, static_cast<int>(t_out), s); });
 }
 
+VOC_API voc_status voc_dbg_peak(int what, int64_t n, double* value, void* stream) {
+  if (!value || n <= 0 || what < 0 || what > 2) return VOC_INVALID_PARAMS;
+  if (what == 0 && (n & 15)) return VOC_INVALID_PARAMS;
+  *value = 0.0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* b0 = nullptr;
+  void* b1 = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  voc_status st = VOC_DEVICE_ERROR;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (what == 0) {  // HBM: a plain copy of n bytes; reads + writes counted
+    if (e == hipSuccess) e = hipMalloc(&b0, static_cast<size_t>(n));
+    if (e == hipSuccess) e = hipMalloc(&b1, static_cast<size_t>(n));
+    if (e == hipSuccess) e = hipMemsetAsync(b0, 1, static_cast<size_t>(n), s);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = launch_copy(b1, b0, n, s);
+    const int reps = 5;
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    for (int i = 0; i < reps && e == hipSuccess; ++i) e = launch_copy(b1, b0, n, s);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e == hipSuccess && ms > 0.f) {
+      *value = 2.0 * reps * static_cast<double>(n) / (ms * 1e-3) / 1e9;
+      st = VOC_OK;
+    }
+  } else {  // matrix cores: n iterations of the MFMA loop, fp32 (1) or bf16 (2)
+    const int op = what == 1 ? OP_F32 : OP_BF16;
+    if (e == hipSuccess) e = hipMalloc(&b0, static_cast<size_t>(mfma_loop_blocks()) * 256 * sizeof(float));
+    if (e == hipSuccess) e = launch_mfma_loop(op, std::max<int64_t>(1, n / 10), static_cast<float*>(b0), s);
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    if (e == hipSuccess) e = launch_mfma_loop(op, n, static_cast<float*>(b0), s);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e == hipSuccess && ms > 0.f) {
+      *value = mfma_loop_flops(op, n) / (ms * 1e-3) / 1e12;
+      st = VOC_OK;
+    }
+  }
+  (void)hipStreamSynchronize(s);
+  if (b0) (void)hipFree(b0);
+  if (b1) (void)hipFree(b1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  return st;
+}
+
 VOC_API voc_status voc_dbg_copy(void* dst, const void* src, int64_t bytes, void* stream) {
   if (!dst || !src || bytes <= 0 || (bytes & 15) ||
       ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15))

@@ -353,7 +353,14 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
 // meets, as its sixth warm-up sample; v[n > 2 len - 1] = the previous
 // sample).  Lanes 4k .. 4k+3 read one 64-byte frame row; the 16 runs of a
 // wave sit kAfRun frames apart, each walking its rows' cache lines in order.
-constexpr int kAfRun = 16;
+#ifndef VOC_AF_RUN
+#define VOC_AF_RUN 16
+#endif
+#ifndef VOC_AF_CPT
+#define VOC_AF_CPT 4
+#endif
+constexpr int kAfRun = VOC_AF_RUN;
+constexpr int kAfCpt = VOC_AF_CPT;  // channels per thread (2 or 4)
 #ifndef VOC_AF_PREFETCH
 #define VOC_AF_PREFETCH 1
 #endif
@@ -362,67 +369,94 @@ constexpr int kAfRun = 16;
 #endif
 constexpr int kAfPrefetch = VOC_AF_PREFETCH;  // input frames requested ahead of their use
 
+template <int N> struct AfVec;
+template <> struct AfVec<2> {
+  typedef float T __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ void store_bf16(uint16_t* p, T y) {
+    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(y[0], y[1]);
+  }
+};
+template <> struct AfVec<4> {
+  typedef f4 T;
+  static __device__ __forceinline__ void store_bf16(uint16_t* p, T y) {
+    uint2 v;
+    v.x = pack_bf16x2(y[0], y[1]);
+    v.y = pack_bf16x2(y[2], y[3]);
+    *reinterpret_cast<uint2*>(p) = v;
+  }
+};
+
 template <int OUT_OP>
 __global__ __launch_bounds__(256, VOC_AF_MIN_WAVES) void af_snake_kernel(const AfArgs a) {
+  typedef typename AfVec<kAfCpt>::T fv;
+  constexpr int LPR = 16 / kAfCpt;   // lanes per 64-byte frame row
+  constexpr int RPW = 256 / LPR;     // runs per workgroup
   const int r = blockIdx.y;
   const int nchunk = a.C / 16;
   const int chunk = blockIdx.x % nchunk;
-  const int run = (blockIdx.x / nchunk) * 64 + (threadIdx.x >> 2);
-  const int q = threadIdx.x & 3;
+  const int run = (blockIdx.x / nchunk) * RPW + static_cast<int>(threadIdx.x) / LPR;
+  const int q = threadIdx.x % LPR;
   const int len = min(a.row_len[r] * a.rate, a.T);
   const int t0 = run * kAfRun;
   if (t0 >= len) return;
-  const int c = chunk * 16 + q * 4;
-  const float* xp = a.x + (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * 4;
-  const f4 sc = *reinterpret_cast<const f4*>(a.scale + c);
-  const f4 hh = *reinterpret_cast<const f4*>(a.hh + c);
-  // Output element index of frame 0 of this thread's four channels.
-  const int64_t orow = OUT_OP == OP_F32 ? (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * 4
+  const int c = chunk * 16 + q * kAfCpt;
+  const float* xp = a.x + (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * kAfCpt;
+  const fv sc = *reinterpret_cast<const fv*>(a.scale + c);
+  const fv hh = *reinterpret_cast<const fv*>(a.hh + c);
+  // Output element index of frame 0 of this thread's channels.
+  const int64_t orow = OUT_OP == OP_F32 ? (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * kAfCpt
                                         : (static_cast<int64_t>(r) * a.C + (c / 32) * 32) * a.T + c % 32;
   char* obase = static_cast<char*>(a.out);
   const int n_last = 2 * len - 1;
-  auto ld = [&](int t) -> f4 {
+  const fv zero = fv(0.f);
+  auto ld = [&](int t) -> fv {
     t = min(max(t, 0), len - 1);
-    return *reinterpret_cast<const f4*>(xp + static_cast<int64_t>(t) * kHChunk);
+    return *reinterpret_cast<const fv*>(xp + static_cast<int64_t>(t) * kHChunk);
   };
-  auto snake4 = [&](f4 u) -> f4 {
-    f4 v;
+  auto snake_v = [&](fv u) -> fv {
+    fv v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = snake_f32(u[e], sc[e], hh[e]);
+    for (int e = 0; e < kAfCpt; ++e) v[e] = snake_f32(u[e], sc[e], hh[e]);
     return v;
   };
-  auto pick = [](bool cond, f4 x, f4 y) -> f4 {  // cond ? x : y, per element
-    f4 o;
+  auto pick = [](bool cond, fv x, fv y) -> fv {  // cond ? x : y, per element
+    fv o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = cond ? x[e] : y[e];
+    for (int e = 0; e < kAfCpt; ++e) o[e] = cond ? x[e] : y[e];
     return o;
   };
+  auto store = [&](int t, fv y) {
+    if constexpr (OUT_OP == OP_F32)
+      *reinterpret_cast<fv*>(reinterpret_cast<float*>(obase) + orow + static_cast<int64_t>(t) * 16) = y;
+    else
+      AfVec<kAfCpt>::store_bf16(reinterpret_cast<uint16_t*>(obase) + orow + static_cast<int64_t>(t) * 32, y);
+  };
   // A[k] collects output t + k (t = t0 at the start).
-  f4 A[6];
+  fv A[6];
 #pragma unroll
-  for (int k = 0; k < 6; ++k) A[k] = f4{0.f, 0.f, 0.f, 0.f};
-  f4 R[6];
-  f4 vlast;
+  for (int k = 0; k < 6; ++k) A[k] = zero;
+  fv R[6];
+  fv vlast;
   {
     // Warm-up.  X[k] = x[t0 - 5 + k]; sample i is v[n], n = 2 t0 - 5 + i:
     //   i odd  (n = 2m,   m = t0 + (i - 5) / 2): fe taps on X[(i - 1) / 2 .. + 5]
     //   i even (n = 2m+1, m = t0 + (i - 6) / 2): fo taps on X[i / 2 .. + 5]
-    f4 X[11];
+    fv X[11];
 #pragma unroll
     for (int k = 0; k < 11; ++k) X[k] = ld(t0 - 5 + k);
-    auto sample = [&](int i) -> f4 {
+    auto sample = [&](int i) -> fv {
       const int b = (i & 1) ? (i - 1) / 2 : i / 2;
-      f4 u = f4{0.f, 0.f, 0.f, 0.f};
+      fv u = zero;
 #pragma unroll
       for (int k = 0; k < 6; ++k) u += ((i & 1) ? a.fe[k] : a.fo[k]) * X[b + k];
-      return snake4(u);
+      return snake_v(u);
     };
-    const f4 v5 = sample(5);  // v[2 t0]: v[0] for the run that starts the row
+    const fv v5 = sample(5);  // v[2 t0]: v[0] for the run that starts the row
     vlast = v5;
 #pragma unroll
     for (int i = 0; i < 12; ++i) {
       const int n = 2 * t0 - 5 + i;
-      f4 v = i == 5 ? v5 : sample(i);
+      fv v = i == 5 ? v5 : sample(i);
       v = pick(n < 0, v5, v);
       v = pick(n > n_last, vlast, v);
       vlast = v;
@@ -433,33 +467,28 @@ __global__ __launch_bounds__(256, VOC_AF_MIN_WAVES) void af_snake_kernel(const A
 #pragma unroll
     for (int k = 0; k < 5; ++k) R[k] = X[6 + k];
   }
-  f4 nx[kAfRun];  // nx[s] = x[t0 + s + 6]
+  fv nx[kAfRun];  // nx[s] = x[t0 + s + 6]
 #pragma unroll
   for (int s = 0; s < kAfPrefetch; ++s) nx[s] = ld(t0 + s + 6);
 #pragma unroll
   for (int s = 0; s < kAfRun; ++s) {
     const int t = t0 + s;
     if (s + kAfPrefetch < kAfRun - 1) nx[s + kAfPrefetch] = ld(t + kAfPrefetch + 6);
-    if (t < len) {
-      if constexpr (OUT_OP == OP_F32)
-        store_op4<OP_F32>(obase, orow + static_cast<int64_t>(t) * 16, A[0]);
-      else
-        store_op4<OP_BF16>(obase, orow + static_cast<int64_t>(t) * 32, A[0]);
-    }
+    if (t < len) store(t, A[0]);
     if (s + 1 < kAfRun) {
       R[5] = nx[s];
-      f4 uo = f4{0.f, 0.f, 0.f, 0.f}, ue = f4{0.f, 0.f, 0.f, 0.f};
+      fv uo = zero, ue = zero;
 #pragma unroll
       for (int k = 0; k < 6; ++k) {
         uo += a.fo[k] * R[k];  // v[2t + 7]
         ue += a.fe[k] * R[k];  // v[2t + 8]
       }
-      const f4 vo = pick(2 * t + 7 > n_last, vlast, snake4(uo));
-      const f4 ve = pick(2 * t + 8 > n_last, vo, snake4(ue));
+      const fv vo = pick(2 * t + 7 > n_last, vlast, snake_v(uo));
+      const fv ve = pick(2 * t + 8 > n_last, vo, snake_v(ue));
       vlast = ve;
 #pragma unroll
       for (int k = 0; k < 5; ++k) A[k] = A[k + 1];
-      A[5] = f4{0.f, 0.f, 0.f, 0.f};
+      A[5] = zero;
 #pragma unroll
       for (int k = 0; k < 6; ++k) {  // output t + 1 + k: taps 10 - 2k and 11 - 2k
         A[k] += a.fd[10 - 2 * k] * vo;
@@ -472,8 +501,9 @@ __global__ __launch_bounds__(256, VOC_AF_MIN_WAVES) void af_snake_kernel(const A
 }
 
 hipError_t launch_af_snake(const AfArgs& a, hipStream_t s) {
+  constexpr int RPW = 256 / (16 / kAfCpt);
   const int runs = (a.T + kAfRun - 1) / kAfRun;
-  const dim3 grid(static_cast<unsigned>((a.C / 16) * ((runs + 63) / 64)), static_cast<unsigned>(a.rows));
+  const dim3 grid(static_cast<unsigned>((a.C / 16) * ((runs + RPW - 1) / RPW)), static_cast<unsigned>(a.rows));
   if (a.out_op == OP_F32)
     hipLaunchKernelGGL(af_snake_kernel<OP_F32>, grid, dim3(256), 0, s, a);
   else

@@ -116,6 +116,7 @@ def lib():
                                         ctypes.POINTER(I64)]),
             "voc_dbg_run_stage": (I, [P, I, P, I64, I64, P, P]),
             "voc_dbg_copy": (I, [P, P, I64, P]),
+            "voc_dbg_peak": (I, [I, I64, ctypes.POINTER(ctypes.c_double), P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -310,6 +311,14 @@ def voc_dbg_run_stage(ctx, stage: int, x, B: int, T_in: int, out, stream=None) -
 
 def voc_dbg_copy(dst, src, nbytes: int, stream=None) -> int:
     return lib().voc_dbg_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream))
+
+
+def voc_dbg_peak(what: int, n: int, stream=None):
+    """(status, value): measured HBM copy GB/s (what=0, n bytes) or MFMA
+    TFLOP/s (what=1 fp32 / 2 bf16, n loop iterations)."""
+    v = ctypes.c_double(0.0)
+    st = lib().voc_dbg_peak(what, n, ctypes.byref(v), _stream(stream))
+    return st, v.value
 
 
 def check(st: int, ctx=None) -> None:

@@ -344,7 +344,7 @@ voc_status vocoder_profile_read(voc_ctx *ctx, int kind, voc_profile_stat *out);
  *   0 = conv_in (after dec_in_proj when in_proj > 0); for block b: 1 + b*(1+n_res) = Snake + ConvTranspose1d,
  *   the next n_res indices = its residual units; count-1 = the head.
  * in: device fp32 [B, C_in(k), T_in] (stage 0: the latent); out: device fp32
- * [B, C_out(k), T_out] (head: [B, 1, T_in]).  Uses the same kernels as
+ * [B, C_out(k), T_out] (head: [B, out_channels, T_in]).  Uses the same kernels as
  * vocoder_decode, untiled.  Asynchronous on hip_stream. */
 int voc_dbg_stage_count(const voc_ctx *ctx);
 voc_status voc_dbg_stage_shape(const voc_ctx *ctx, int stage, int64_t T_in,
@@ -356,6 +356,17 @@ voc_status voc_dbg_run_stage(voc_ctx *ctx, int stage, const float *in, int64_t B
  * stores), used to calibrate HBM byte counters.  bytes must be a multiple
  * of 16 and both pointers 16-byte aligned. */
 voc_status voc_dbg_copy(void *dst, const void *src, int64_t bytes, void *hip_stream);
+
+/* What the device delivers, measured now, beside its published peaks.
+ * what = 0: HBM, a plain copy of n bytes (n a multiple of 16; 2 warm-up
+ *   copies, then 5 timed): *value = GB/s counting the bytes read and written.
+ * what = 1 / 2: matrix cores, n iterations of a loop of independent 16x16
+ *   MFMA chains (fp32 16x16x4 / bf16 16x16x32) on 8 workgroups of 4 waves
+ *   per CU, after a warm-up of n/10: *value = TFLOP/s.
+ * Allocates its own buffers, runs on hip_stream and synchronizes it; for
+ * measurement only, not for a decode loop.  Errors: VOC_INVALID_PARAMS
+ * (NULL value, n <= 0, unknown `what`), VOC_DEVICE_ERROR. */
+voc_status voc_dbg_peak(int what, int64_t n, double *value, void *hip_stream);
 
 #ifdef __cplusplus
 }

@@ -18,6 +18,7 @@ int main(void) {
   voc_ctx *ctx = (voc_ctx *)0;
   voc_profile_stat st;
   int64_t a, b, c;
+  double peak = 0.0;
   float dummy[4];
   voc_config_default(&cfg);
   EXPECT(cfg.abi_version == VOC_ABI_VERSION);
@@ -67,6 +68,9 @@ int main(void) {
   EXPECT(voc_dbg_stage_shape(NULL, 0, 1, &a, &b, &c) == VOC_INVALID_PARAMS);
   EXPECT(voc_dbg_run_stage(NULL, 0, dummy, 1, 1, dummy, NULL) == VOC_INVALID_PARAMS);
   EXPECT(voc_dbg_copy(NULL, dummy, 16, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(voc_dbg_peak(0, 16, NULL, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(voc_dbg_peak(3, 16, &peak, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(voc_dbg_peak(0, 10, &peak, NULL) == VOC_INVALID_PARAMS);
   vocoder_destroy(NULL);
   puts("abi ok");
   return 0;

@@ -175,3 +175,19 @@ def test_profile_select_times_only_selected_kinds(weights):
                 assert s["launches"] == 1 and s["ms"] == 0 and (n == "import" or s["flops"] > 0)
     finally:
         V.vocoder_destroy(ctx)
+
+
+def test_measured_peaks_are_plausible():
+    """voc_dbg_peak: a copy and the matrix-core loops land below the published
+    peaks (8 TB/s, 157.3 and 2500 TFLOP/s) and well above nothing; bad
+    arguments are rejected."""
+    st, gbs = V.voc_dbg_peak(0, 64 << 20)
+    assert st == V.VOC_OK and 500 < gbs < 8000, gbs
+    st, f32 = V.voc_dbg_peak(1, 200)
+    assert st == V.VOC_OK and 20 < f32 < 157.3, f32
+    st, bf16 = V.voc_dbg_peak(2, 2000)
+    assert st == V.VOC_OK and 200 < bf16 < 2500, bf16
+    print(f"copy {gbs:.0f} GB/s, fp32 MFMA {f32:.1f} TFLOP/s, bf16 MFMA {bf16:.0f} TFLOP/s")
+    assert V.voc_dbg_peak(0, 100)[0] == V.VOC_INVALID_PARAMS
+    assert V.voc_dbg_peak(3, 100)[0] == V.VOC_INVALID_PARAMS
+    assert V.voc_dbg_peak(1, 0)[0] == V.VOC_INVALID_PARAMS
