@@ -117,10 +117,11 @@ def cpu_baseline(cfg: dict, tensors: dict, latent, target_s: float = 15.0,
     run(frames)
     wall = time.perf_counter() - t0
     secs = I.audio_seconds(cfg, rows, frames)
+    flops = I.encode_flops(cfg, rows, frames) if cfg.get("encode") else I.algorithmic_flops(cfg, rows, frames)
     note = "" if kept_frac == 1.0 else (f"; rate x {kept_frac:.4f}, the share of decoded window "
                                         "frames that the stitching keeps")
     return {"value": secs / wall * kept_frac, "unit": "audio-s/s", "cores": O.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "gflops_fp64": flops / wall / 1e9,
             "sample": f"{rows} row(s) x {frames} latent frames of the same input "
                       f"({secs:.3f} audio-s) decoded by the fp64 oracle in {wall:.2f} s{note}"}
 
