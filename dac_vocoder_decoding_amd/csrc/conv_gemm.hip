@@ -417,8 +417,8 @@ int conv_variant_bm(int v) { return kVariants[v].wav_m * kVariants[v].wmb * 16; 
 int conv_variant_bn(int v) { return kVariants[v].wav_n * kVariants[v].wnb * 16; }
 bool conv_variant_ok(int v, int taps) {
   if (v < 0 || v >= CV_COUNT) return false;
-  // The narrow-M tiles serve the k=7 convs of narrow units only.
-  if (v == CV_16x128 || v == CV_32x128) return taps == 7;
+  // Narrow-M tiles: the 7-tap convs, and (fp32 only) the 1- and 2-tap ones.
+  if (v == CV_16x128 || v == CV_32x128) return taps == 7 || taps == 1 || taps == 2;
   // All taps' weight rows of a chunk live in LDS: keep two workgroups per CU.
   if (taps == 7 || taps == 3) return v == CV_64x256 || v == CV_96x256 || v == CV_64x128;
   return true;
@@ -465,7 +465,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 #undef VOC_CASE
 #define VOC_CASE(V, A, B, C, D)                                                              \
   case V:                                                                                    \
-    if constexpr (TAPS == 7) {                                                               \
+    if constexpr (TAPS == 7 || (OP == OP_F32 && (TAPS == 1 || TAPS == 2))) {                 \
       hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS>), grid, block, 0, s, a); \
       break;                                                                                 \
     }                                                                                        \

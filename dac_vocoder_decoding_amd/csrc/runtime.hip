@@ -449,17 +449,23 @@ voc_status upload_rows(voc_ctx* c, const Plan& p, std::vector<int64_t>&& dst_in,
 // Tile choice: padding efficiency of M and N x wave quantization over two
 // workgroups per CU x a relative speed of the tile family for the operand
 // dtype and tap count, measured on MI355X (a sweep forcing each family on
-// the full-window fp32 and batched-window bf16 decodes; the narrow 16- and
-// 32-row tiles from the k=7 convs of the 16- and 32-channel units of the
-// alias-free H3 decode, where they take 23 and 36 us against 67 us for the
-// 64-row tile, whose rows would be three quarters or half empty).
+// the full-window fp32 and batched-window bf16 decodes).  The narrow fp32
+// tiles: for 7 taps the 32-row tile (26 KB of LDS per stage, three
+// workgroups per CU against two for the 64-row tile) is 1-3 % faster on
+// every k=7 layer of the fp32 workloads and 23 % faster where one row of
+// 3000 frames leaves the 64-row tiles short of workgroups; the 16-row tile
+// serves 16-channel units (23 us against 67 us for a 64-row tile three
+// quarters empty).  For 1 and 2 taps the narrow tiles measured level with
+// the 64-row ones and are taken when they fill the chip better.
 int pick_variant(int op, int taps, int M, int N, int rows) {
   //                                  128x256 64x256 96x256 128x128 64x128 192x128 16x128 32x128
-  static const double f32[CV_COUNT]   = {0.60, 0.90, 0.85, 0.90, 1.00, 0.70, 0.60, 0.60};
+  static const double f32[CV_COUNT]   = {0.60, 0.90, 0.85, 0.90, 1.00, 0.70, 0.50, 0.90};
+  static const double f32_t7[CV_COUNT] = {0.00, 0.90, 0.85, 0.00, 1.00, 0.00, 0.60, 1.05};
   static const double bf_t2[CV_COUNT] = {0.90, 0.80, 0.85, 1.00, 0.75, 0.92, 0.00, 0.00};
   static const double bf_t7[CV_COUNT] = {0.00, 1.00, 1.00, 0.00, 0.88, 0.00, 0.00, 0.00};
   static const double bf_t1[CV_COUNT] = {0.46, 0.94, 0.80, 1.00, 0.95, 0.68, 0.00, 0.00};
-  const double* speed = op == OP_F32 ? f32 : taps == 2 ? bf_t2 : taps == 7 ? bf_t7 : bf_t1;
+  const double* speed = op == OP_F32 ? (taps == 7 ? f32_t7 : f32)
+                                     : taps == 2 ? bf_t2 : taps == 7 ? bf_t7 : bf_t1;
   int best = CV_64x128;
   double best_score = -1.0;
   for (int v = 0; v < CV_COUNT; ++v) {
