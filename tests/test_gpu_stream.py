@@ -177,3 +177,23 @@ def test_stream_argument_checks():
         assert "causal" in V.vocoder_last_error(centered)
     finally:
         V.vocoder_destroy(centered)
+
+
+def test_two_channel_causal_stream():
+    """A causal decoder with two output channels: the stream writes both
+    channels of every chunk, equal bit for bit to the offline decode, which
+    matches the oracle."""
+    cfg = I.config(7, dtype="f32", widths=(64, 32, 32, 32, 32), latent_channels=32, out_channels=2)
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg, batch=2, frames=30)
+    ctx = V.open_context(cfg, t)
+    try:
+        x = to_dev(lat)
+        offline = V.decode(ctx, x)
+        got = _stream(ctx, x, [7, 1, 12, 10])
+    finally:
+        V.vocoder_destroy(ctx)
+    assert offline.shape == (2, 2, 30 * cfg["hop"])
+    assert torch.equal(got, offline)
+    ref = O.Model(cfg, t).decode(lat)
+    assert rel_maxabs(offline.cpu().numpy(), ref) <= TOL["f32"]

@@ -145,3 +145,20 @@ def test_windows_argument_checks():
         assert "tile_frames" in V.vocoder_last_error(tiled)
     finally:
         V.vocoder_destroy(tiled)
+
+
+def test_stereo_windows_with_two_output_channels():
+    """sides = 2 and two output channels per side: planes (side, channel) in
+    the order j * 2 + o, against the oracle's windowed decode."""
+    cfg = I.config(5, out_channels=2, widths=(256, 128, 64, 32, 16), in_proj=0)
+    t = I.make_weights(cfg, twin=True)
+    win = I.normal(cfg["seed"], "win2", (3, 2 * cfg["latent_channels"], 10))
+    win[-1, :, 7:] = 0.0
+    ctx = V.open_context(cfg, t)
+    try:
+        pcm = V.decode_windows(ctx, to_dev(win), 2, 7, 2, 3).cpu().numpy()
+    finally:
+        V.vocoder_destroy(ctx)
+    ref = O.Model(cfg, t).decode_windows(win, 7, 2, 3)
+    assert pcm.shape == ref.shape == (4, (7 + 5 + 5) * cfg["hop"])
+    assert rel_maxabs(pcm, ref) <= TOL["f32"]
