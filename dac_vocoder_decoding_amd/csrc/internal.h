@@ -202,6 +202,9 @@ hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s)
 int mfma_loop_blocks();
 double mfma_loop_flops(int op, int64_t iters);
 hipError_t launch_mfma_loop(int op, int64_t iters, float* out, hipStream_t s);
+// The same with 32x32 MFMAs (fp32 32x32x2, bf16 32x32x16).
+double mfma32_loop_flops(int op, int64_t iters);
+hipError_t launch_mfma32_loop(int op, int64_t iters, float* out, hipStream_t s);
 
 // Alias-free Snake over a residual-stream tensor (fp32 chunked, 16 channels
 // per 64-byte frame row): per row r with valid frames [0, len), len =

@@ -1968,7 +1968,7 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
 }
 
 VOC_API voc_status voc_dbg_peak(int what, int64_t n, double* value, void* stream) {
-  if (!value || n <= 0 || what < 0 || what > 2) return VOC_INVALID_PARAMS;
+  if (!value || n <= 0 || what < 0 || what > 4) return VOC_INVALID_PARAMS;
   if (what == 0 && (n & 15)) return VOC_INVALID_PARAMS;
   *value = 0.0;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1994,18 +1994,23 @@ VOC_API voc_status voc_dbg_peak(int what, int64_t n, double* value, void* stream
       *value = 2.0 * reps * static_cast<double>(n) / (ms * 1e-3) / 1e9;
       st = VOC_OK;
     }
-  } else {  // matrix cores: n iterations of the MFMA loop, fp32 (1) or bf16 (2)
-    const int op = what == 1 ? OP_F32 : OP_BF16;
+  } else {  // matrix cores: n iterations of an MFMA loop, fp32 (1, 3) or bf16 (2, 4), 16x16 or 32x32
+    const int op = what == 1 || what == 3 ? OP_F32 : OP_BF16;
+    const bool wide = what >= 3;
+    auto loop = [&](int64_t it) {
+      return wide ? launch_mfma32_loop(op, it, static_cast<float*>(b0), s)
+                  : launch_mfma_loop(op, it, static_cast<float*>(b0), s);
+    };
     if (e == hipSuccess) e = hipMalloc(&b0, static_cast<size_t>(mfma_loop_blocks()) * 256 * sizeof(float));
-    if (e == hipSuccess) e = launch_mfma_loop(op, std::max<int64_t>(1, n / 10), static_cast<float*>(b0), s);
+    if (e == hipSuccess) e = loop(std::max<int64_t>(1, n / 10));
     if (e == hipSuccess) e = hipEventRecord(e0, s);
-    if (e == hipSuccess) e = launch_mfma_loop(op, n, static_cast<float*>(b0), s);
+    if (e == hipSuccess) e = loop(n);
     if (e == hipSuccess) e = hipEventRecord(e1, s);
     float ms = 0.f;
     if (e == hipSuccess) e = hipEventSynchronize(e1);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
     if (e == hipSuccess && ms > 0.f) {
-      *value = mfma_loop_flops(op, n) / (ms * 1e-3) / 1e12;
+      *value = (wide ? mfma32_loop_flops(op, n) : mfma_loop_flops(op, n)) / (ms * 1e-3) / 1e12;
       st = VOC_OK;
     }
   }

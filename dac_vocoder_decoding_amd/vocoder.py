@@ -315,7 +315,8 @@ def voc_dbg_copy(dst, src, nbytes: int, stream=None) -> int:
 
 def voc_dbg_peak(what: int, n: int, stream=None):
     """(status, value): measured HBM copy GB/s (what=0, n bytes) or MFMA
-    TFLOP/s (what=1 fp32 / 2 bf16, n loop iterations)."""
+    TFLOP/s (what=1 fp32 / 2 bf16 with 16x16 MFMAs, 3 / 4 with 32x32 ones;
+    n loop iterations)."""
     v = ctypes.c_double(0.0)
     st = lib().voc_dbg_peak(what, n, ctypes.byref(v), _stream(stream))
     return st, v.value

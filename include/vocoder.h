@@ -363,6 +363,7 @@ voc_status voc_dbg_copy(void *dst, const void *src, int64_t bytes, void *hip_str
  * what = 1 / 2: matrix cores, n iterations of a loop of independent 16x16
  *   MFMA chains (fp32 16x16x4 / bf16 16x16x32) on 8 workgroups of 4 waves
  *   per CU, after a warm-up of n/10: *value = TFLOP/s.
+ * what = 3 / 4: the same with 32x32 MFMAs (fp32 32x32x2 / bf16 32x32x16).
  * Allocates its own buffers, runs on hip_stream and synchronizes it; for
  * measurement only, not for a decode loop.  Errors: VOC_INVALID_PARAMS
  * (NULL value, n <= 0, unknown `what`), VOC_DEVICE_ERROR. */

@@ -69,7 +69,7 @@ int main(void) {
   EXPECT(voc_dbg_run_stage(NULL, 0, dummy, 1, 1, dummy, NULL) == VOC_INVALID_PARAMS);
   EXPECT(voc_dbg_copy(NULL, dummy, 16, NULL) == VOC_INVALID_PARAMS);
   EXPECT(voc_dbg_peak(0, 16, NULL, NULL) == VOC_INVALID_PARAMS);
-  EXPECT(voc_dbg_peak(3, 16, &peak, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(voc_dbg_peak(5, 16, &peak, NULL) == VOC_INVALID_PARAMS);
   EXPECT(voc_dbg_peak(0, 10, &peak, NULL) == VOC_INVALID_PARAMS);
   vocoder_destroy(NULL);
   puts("abi ok");

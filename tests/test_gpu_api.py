@@ -187,7 +187,10 @@ def test_measured_peaks_are_plausible():
     assert st == V.VOC_OK and 20 < f32 < 157.3, f32
     st, bf16 = V.voc_dbg_peak(2, 2000)
     assert st == V.VOC_OK and 200 < bf16 < 2500, bf16
+    for what, n, lo, hi in ((3, 100, 20, 157.3), (4, 1000, 200, 2500)):
+        st, v = V.voc_dbg_peak(what, n)
+        assert st == V.VOC_OK and lo < v < hi, (what, v)
     print(f"copy {gbs:.0f} GB/s, fp32 MFMA {f32:.1f} TFLOP/s, bf16 MFMA {bf16:.0f} TFLOP/s")
     assert V.voc_dbg_peak(0, 100)[0] == V.VOC_INVALID_PARAMS
-    assert V.voc_dbg_peak(3, 100)[0] == V.VOC_INVALID_PARAMS
+    assert V.voc_dbg_peak(5, 100)[0] == V.VOC_INVALID_PARAMS
     assert V.voc_dbg_peak(1, 0)[0] == V.VOC_INVALID_PARAMS
