@@ -460,16 +460,20 @@ voc_status upload_rows(voc_ctx* c, const Plan& p, std::vector<int64_t>&& dst_in,
 int pick_variant(int op, int taps, int M, int N, int rows) {
   //                                  128x256 64x256 96x256 128x128 64x128 192x128 16x128 32x128
   static const double f32[CV_COUNT]   = {0.60, 0.90, 0.85, 0.90, 1.00, 0.70, 0.50, 0.90};
-  static const double f32_t7[CV_COUNT] = {0.00, 0.90, 0.85, 0.00, 1.00, 0.00, 0.60, 1.05};
+  static const double f32_t7[CV_COUNT] = {0.00, 0.90, 0.85, 0.00, 1.00, 0.00, 0.00, 1.05};
   static const double bf_t2[CV_COUNT] = {0.90, 0.80, 0.85, 1.00, 0.75, 0.92, 0.00, 0.00};
   static const double bf_t7[CV_COUNT] = {0.00, 1.00, 1.00, 0.00, 0.88, 0.00, 0.00, 0.00};
   static const double bf_t1[CV_COUNT] = {0.46, 0.94, 0.80, 1.00, 0.95, 0.68, 0.00, 0.00};
   const double* speed = op == OP_F32 ? (taps == 7 ? f32_t7 : f32)
                                      : taps == 2 ? bf_t2 : taps == 7 ? bf_t7 : bf_t1;
+  // The 16-row 7-tap tile exactly when M <= 16 (the other families would
+  // leave at least three quarters of their rows empty).
+  if (taps == 7 && op == OP_F32 && M <= 16) return CV_16x128;
   int best = CV_64x128;
   double best_score = -1.0;
   for (int v = 0; v < CV_COUNT; ++v) {
     if (!conv_variant_ok(v, taps)) continue;
+    if (taps == 7 && v == CV_16x128) continue;
     const int bm = conv_variant_bm(v), bn = conv_variant_bn(v);
     const int64_t mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn;
     const int64_t tiles = mt * nt * rows;
