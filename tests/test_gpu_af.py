@@ -159,3 +159,20 @@ def test_af_log_params_match_plain_params():
         V.vocoder_destroy(a)
         V.vocoder_destroy(b)
     assert float((ya - yb).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_af_decode_short_clips(T):
+    """Clips of 1, 2 and 5 latent frames: every alias-free Snake's replicate
+    padding meets both row ends within one run."""
+    cfg = small()
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg, batch=1, frames=T)
+    ctx = V.open_context(cfg, t)
+    try:
+        pcm = V.decode(ctx, to_dev(lat)).cpu().numpy()
+    finally:
+        V.vocoder_destroy(ctx)
+    ref = O.Model(cfg, t).decode(lat)
+    assert pcm.shape == ref.shape == (1, 2, T * 800)
+    assert rel_maxabs(pcm, ref) <= TOL["f32"]
