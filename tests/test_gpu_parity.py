@@ -156,7 +156,7 @@ def test_operand_from_h_bitwise_equal(idx, monkeypatch):
     assert torch.equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("idx", [1, 2])
+@pytest.mark.parametrize("idx", [1, 2, 9])
 def test_batch_rows_independent_and_deterministic(idx):
     cfg = I.config(idx)
     t = I.make_weights(cfg)
