@@ -230,6 +230,9 @@ struct AfArgs {
   int rows;
 };
 hipError_t launch_af_snake(const AfArgs& a, hipStream_t s);
+// Plain Snake of the same tensors, elementwise (the filter fields unused):
+// the standalone Snake stage of the split ablation.
+hipError_t launch_snake(const AfArgs& a, hipStream_t s);
 
 // Streaming: one layer's carried context.  buf points at frame 0 of the
 // first plane of the layer's input; planes of plane_bytes bytes hold 64-byte

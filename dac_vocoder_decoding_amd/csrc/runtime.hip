@@ -100,10 +100,11 @@ struct voc_ctx {
   voc_profile_stat stats[VOC_K_COUNT]{};
   // cached row metadata of the last decode
   std::vector<int64_t> rows_key;  // what the uploaded metadata describes (empty: nothing)
-  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
+  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
+  bool split_snake = false;             // ablation: every plain Snake as a launch of its own
   // streaming (causal configurations): the carried context of every layer
   // with one ([planes][ctx][64 bytes], two copies that alternate by chunk),
   // in the order conv_in, per block: ConvTranspose1d then its units, head.
@@ -308,7 +309,7 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // computed from h in the kernel (Snake1 at staging): their producers then
 // write no operand tensor, and h alternates between two buffers.
 bool unit_xh(const voc_ctx* c, int C) {
-  return !c->cfg.af_snake && c->ru_xh && !c->no_fuse && res_unit_tile(c->op, C, false) > 0 && res_unit_from_h_ok(c->op, C);
+  return !c->cfg.af_snake && !c->split_snake && c->ru_xh && !c->no_fuse && res_unit_tile(c->op, C, false) > 0 && res_unit_from_h_ok(c->op, C);
 }
 
 bool any_unit_xh(const voc_ctx* c) {
@@ -335,7 +336,7 @@ Plan make_plan(const voc_ctx* c, int rows, int T, int mg = 0) {
   size_t o = 0;
   p.off_xlat = o; o = align_up(o + es * rows * static_cast<size_t>(g.latent_channels) * (T + mg));
   p.off_h = o;    o = align_up(o + 4 * rows * max_act);
-  p.off_h2 = o;   if (any_unit_xh(c) || g.af_snake) o = align_up(o + 4 * rows * max_act);
+  p.off_h2 = o;   if (any_unit_xh(c) || g.af_snake || c->split_snake) o = align_up(o + 4 * rows * max_act);
   p.off_s0 = o;   o = align_up(o + es * rows * max_act);
   p.off_s1 = o;   o = align_up(o + es * rows * max_act);
   p.off_u = o;    o = align_up(o + es * rows * max_act);
@@ -632,11 +633,13 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
   return launch(c, s, VOC_K_HEAD, flops, bytes, "head launch", [&] { return launch_head(a, s); });
 }
 
-// Alias-free Snake of x (fp32 residual-stream layout, C channels, T frames
-// per row at `rate` frames per latent frame) into out (operand layout of
-// out_op).  Algorithmic work per element: two upsampled samples of six taps,
-// two Snakes, one twelve-tap output (48 flops counting an FMA as two);
-// bytes: the fp32 read and the operand write.
+// A Snake as a launch of its own: x (fp32 residual-stream layout, C
+// channels, T frames per row at `rate` frames per latent frame) into out
+// (operand layout of out_op).  Alias-free configurations run the alias-free
+// Snake (algorithmic work per element: two upsampled samples of six taps,
+// two Snakes, one twelve-tap output, 48 flops counting an FMA as two); the
+// split ablation runs the plain elementwise Snake.  Bytes: the fp32 read
+// and the operand write.
 voc_status run_af(voc_ctx* c, const SnakeDev& sn, const float* x, int C, int T, int rate, int rows,
                   const int* row_len, void* out, int out_op, hipStream_t s) {
   AfArgs a{};
@@ -654,6 +657,9 @@ voc_status run_af(voc_ctx* c, const SnakeDev& sn, const float* x, int C, int T, 
   std::memcpy(a.fd, c->af_fd, sizeof(a.fd));
   a.rows = rows;
   const double el = static_cast<double>(rows) * T * C;
+  if (!c->cfg.af_snake)
+    return launch(c, s, VOC_K_SNAKE, 0.0, el * (4 + op_size(out_op)), "Snake launch",
+                  [&] { return launch_snake(a, s); });
   return launch(c, s, VOC_K_AF_SNAKE, 48.0 * el, el * (4 + op_size(out_op)), "alias-free Snake launch",
                 [&] { return launch_af_snake(a, s); });
 }
@@ -869,7 +875,8 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
 // The alias-free decoder (TensorSharp minimax-h3 page, audio VAE): producers
 // write the residual stream h only, and every Snake is an alias-free Snake
 // launch that writes the next GEMM's operand.  The head's input, AF(h), goes
-// to h2 in fp32; *h_last receives h2.
+// to h2 in fp32; *h_last receives h2.  The split ablation runs the same
+// sequence with plain Snake launches (the standalone Snake stage).
 voc_status run_stack_af(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, float** h_last) {
   const voc_config& g = c->cfg;
   const Weights& W = c->W;
@@ -1117,6 +1124,9 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   if (const char* v = std::getenv("VOC_CONV_M_FAST")) c->m_order = std::atoi(v) != 0;
   // Ablation only: 0 makes every fused unit read an operand tensor written by its producer.
   if (const char* v = std::getenv("VOC_RU_OPERAND_FROM_H")) c->ru_xh = std::atoi(v) != 0;
+  // Ablation only: 1 runs every Snake of a plain decode as a launch of its own
+  // (producers write h only), to measure the standalone Snake stage.
+  if (const char* v = std::getenv("VOC_SPLIT_SNAKE")) c->split_snake = std::atoi(v) != 0 && !cfg->causal;
   *out = c;
   return VOC_OK;
 }
@@ -1408,8 +1418,8 @@ voc_status decode_rows(voc_ctx* c, const float* latent, int64_t T_src, int64_t r
                   nullptr, nullptr, s);
   if (st) return st;
   float* h_last = nullptr;
-  st = g.af_snake ? run_stack_af(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last)
-                  : run_stack(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last);
+  st = g.af_snake || c->split_snake ? run_stack_af(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last)
+                                    : run_stack(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last);
   if (st) return st;
   return run_head(c, h_last, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
                   static_cast<int>(c->hop), pcm, ch_stride, s);
@@ -1872,7 +1882,7 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
   size_t o = 0;
   const size_t off_h = o; o = align_up(o + 4 * std::max(act_in, act_out));
   const bool xh = si.kind == 2 && unit_xh(c, static_cast<int>(si.c_out));
-  const bool af = c->cfg.af_snake != 0;
+  const bool af = c->cfg.af_snake != 0 || c->split_snake;  // every Snake a launch of its own
   const size_t off_h2 = o; if (xh || af) o = align_up(o + 4 * std::max(act_in, act_out));
   const size_t off_s0 = o; o = align_up(o + es * act_in);
   const size_t off_s1 = o; o = align_up(o + es * act_out);

@@ -7,6 +7,7 @@
 //   layer_state_kernel   a stream layer's carried context in and out
 //   export_kernel        chunked fp32 -> [row][C][T] (stage runner, encoder output)
 //   af_snake_kernel      alias-free Snake: 2x upsample, Snake, 2x downsample
+//   snake_kernel         plain elementwise Snake (the split ablation)
 //   head_kernel          Snake -> Conv1d k=7 to one or two channels -> bias ->
 //                        tanh, with the tile / window crop folded into the store
 //   copy_kernel          plain 16-byte vector copy (byte-counter calibration)
@@ -508,6 +509,59 @@ hipError_t launch_af_snake(const AfArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(af_snake_kernel<OP_F32>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(af_snake_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- plain Snake
+// The standalone elementwise Snake (an ablation: the decoder normally
+// applies Snake in the producer's epilogue or the consumer's staging).  A
+// thread handles one 16-byte unit of one output frame row: four fp32
+// channels, or eight bf16 channels (read from two fp32 units).  A wave
+// covers 16 consecutive frames of an output chunk, so reads and writes are
+// whole 64-byte rows.
+template <int OUT_OP>
+__global__ __launch_bounds__(256) void snake_kernel(const AfArgs a) {
+  constexpr int CH = OUT_OP == OP_F32 ? 16 : 32;  // channels per output row
+  constexpr int CPT = CH / 4;                     // channels per thread
+  const int r = blockIdx.y;
+  const int nchunk = a.C / CH;
+  const int chunk = blockIdx.x % nchunk;
+  const int t = (blockIdx.x / nchunk) * 64 + static_cast<int>(threadIdx.x >> 2);
+  const int q = threadIdx.x & 3;
+  const int len = min(a.row_len[r] * a.rate, a.T);
+  if (t >= len) return;
+  const int c = chunk * CH + q * CPT;  // first channel of this thread
+  f4 y[CPT / 4];
+#pragma unroll
+  for (int k = 0; k < CPT / 4; ++k) {
+    const int ck = c + 4 * k;
+    const f4 x = *reinterpret_cast<const f4*>(a.x + (static_cast<int64_t>(r) * a.C + (ck & ~15)) * a.T +
+                                              static_cast<int64_t>(t) * kHChunk + (ck & 15));
+    const f4 sc = *reinterpret_cast<const f4*>(a.scale + ck);
+    const f4 hh = *reinterpret_cast<const f4*>(a.hh + ck);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[k][e] = snake_f32(x[e], sc[e], hh[e]);
+  }
+  const int64_t idx = (static_cast<int64_t>(r) * a.C + chunk * CH) * a.T + static_cast<int64_t>(t) * CH + q * CPT;
+  if constexpr (OUT_OP == OP_F32) {
+    *reinterpret_cast<f4*>(static_cast<float*>(a.out) + idx) = y[0];
+  } else {
+    uint4 v;
+    v.x = pack_bf16x2(y[0][0], y[0][1]);
+    v.y = pack_bf16x2(y[0][2], y[0][3]);
+    v.z = pack_bf16x2(y[1][0], y[1][1]);
+    v.w = pack_bf16x2(y[1][2], y[1][3]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + idx) = v;
+  }
+}
+
+hipError_t launch_snake(const AfArgs& a, hipStream_t s) {
+  const int ch = a.out_op == OP_F32 ? 16 : 32;
+  const dim3 grid(static_cast<unsigned>((a.C / ch) * ((a.T + 63) / 64)), static_cast<unsigned>(a.rows));
+  if (a.out_op == OP_F32)
+    hipLaunchKernelGGL(snake_kernel<OP_F32>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(snake_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

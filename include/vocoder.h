@@ -319,7 +319,8 @@ typedef enum voc_kernel_kind {
   VOC_K_ENC_DOWN = 9, /* encoder strided Conv1d GEMM                    */
   VOC_K_ENC_OUT = 10, /* encoder conv_out (k=3) and projection (k=1)    */
   VOC_K_AF_SNAKE = 11, /* alias-free Snake (2x up, Snake, 2x down)      */
-  VOC_K_COUNT = 12
+  VOC_K_SNAKE = 12,   /* standalone Snake (only in the split ablation)   */
+  VOC_K_COUNT = 13
 } voc_kernel_kind;
 
 typedef struct voc_profile_stat {

@@ -246,3 +246,32 @@ def test_snake_log_params():
         V.vocoder_destroy(a)
         V.vocoder_destroy(b)
     assert rel_maxabs(yb, ya) <= 1e-5
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 5])
+def test_split_snake_equals_epilogue_snake(idx, monkeypatch):
+    """The split ablation (every Snake a standalone launch reading the fp32
+    residual stream) gives the same bits as the GEMM pairs that apply the
+    Snake in their epilogues: the same fp32 values go through the same Snake
+    and rounding either way; the standalone Snake stage's bytes are timed."""
+    cfg = I.config(idx)
+    t = I.make_weights(cfg, twin=True)
+    frames, rows = SMALL[idx]
+    x = to_dev(I.make_latent(cfg, batch=rows, frames=frames))
+    outs = []
+    for env in ({"VOC_SPLIT_SNAKE": "1"}, {"VOC_NO_FUSED_RES": "1"}):
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        ctx = _ctx(cfg, t)
+        try:
+            V.check(V.vocoder_profile_enable(ctx, True), ctx)
+            outs.append(V.decode(ctx, x))
+            torch.cuda.synchronize()
+            st, sn = V.vocoder_profile_read(ctx, V.KERNEL_KINDS.index("snake"))
+            V.check(st, ctx)
+            assert (sn["launches"] > 0) == ("VOC_SPLIT_SNAKE" in env)
+        finally:
+            V.vocoder_destroy(ctx)
+        for k in env:
+            monkeypatch.delenv(k)
+    assert torch.equal(outs[0], outs[1])
