@@ -230,6 +230,28 @@ struct AfArgs {
   int rows;
 };
 hipError_t launch_af_snake(const AfArgs& a, hipStream_t s);
+// col2im overlap-add of a ConvTranspose1d computed as a plain GEMM into a
+// column matrix (an ablation of the polyphase GEMM): col holds, per row, the
+// fp32 [2s*Cout / 16][T_col][16] products z[k*Cout + o][n] = sum_i w[i][o][k]
+// x[i][n]; output frame tau, channel o receives bias[o] + z[k][n] over the
+// (n, k) with n*s + k = tau + crop (two of them), then the epilogue of the
+// polyphase GEMM: h_out (fp32) and/or s_out = Snake(v) in the operand dtype.
+struct Col2imArgs {
+  const float* col;
+  int T_col;            // allocated frames per row of col
+  int Cout, s, crop;
+  const float* bias;
+  float* h_out;
+  void* s_out;
+  const float* s_alpha;  // null: s_out receives v itself
+  const float* s_invden;
+  int T_out;            // allocated frames per row of the outputs
+  const int* row_len;
+  int rate_in;          // input frames per latent frame
+  int rows, op;
+};
+hipError_t launch_col2im(const Col2imArgs& a, hipStream_t s);
+
 // Plain Snake of the same tensors, elementwise (the filter fields unused):
 // the standalone Snake stage of the split ablation.
 hipError_t launch_snake(const AfArgs& a, hipStream_t s);

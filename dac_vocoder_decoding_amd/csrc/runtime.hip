@@ -100,11 +100,15 @@ struct voc_ctx {
   voc_profile_stat stats[VOC_K_COUNT]{};
   // cached row metadata of the last decode
   std::vector<int64_t> rows_key;  // what the uploaded metadata describes (empty: nothing)
-  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
+  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
   bool split_snake = false;             // ablation: every plain Snake as a launch of its own
+  bool col2im = false;                  // ablation: ConvTranspose1d as GEMM + col2im
+  float* col_buf = nullptr;             // its column matrix (and a zero bias), grown on demand
+  size_t col_bytes = 0;
+  float* col_zero = nullptr;
   // streaming (causal configurations): the carried context of every layer
   // with one ([planes][ctx][64 bytes], two copies that alternate by chunk),
   // in the order conv_in, per block: ConvTranspose1d then its units, head.
@@ -579,6 +583,64 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
                 });
 }
 
+// A ConvTranspose1d launch: the polyphase GEMM, or in the col2im ablation a
+// plain GEMM into the column matrix z[k*Cout + o][n] (the polyphase packing
+// read with 2s*Cout rows and one tap is exactly that GEMM's weight) followed
+// by the overlap-add, which applies the polyphase GEMM's epilogue.
+voc_status run_convt(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, const int* row_len,
+                     hipStream_t s) {
+  if (!c->col2im) return run_conv(c, L, io, rows, row_len, VOC_K_CONVT, s);
+  const int mcol = 2 * L.ups * L.cout;
+  const size_t need = static_cast<size_t>(rows) * mcol * (io.T_in + c->mg) * sizeof(float);
+  if (need > c->col_bytes || !c->col_zero) {
+    (void)hipDeviceSynchronize();
+    if (c->col_buf) (void)hipFree(c->col_buf);
+    c->col_buf = nullptr;
+    c->col_bytes = 0;
+    hipError_t e = hipMalloc(&c->col_buf, need);
+    if (e != hipSuccess) return hip_fail(c, e, "column matrix hipMalloc");
+    c->col_bytes = need;
+    if (!c->col_zero) {  // a zero bias for the column GEMM, as long as any of its M
+      const size_t zb = static_cast<size_t>(2) * 64 * 8192 * sizeof(float);
+      e = hipMalloc(&c->col_zero, zb);
+      if (e == hipSuccess) e = hipMemset(c->col_zero, 0, zb);
+      if (e != hipSuccess) return hip_fail(c, e, "column matrix bias");
+    }
+  }
+  ConvDev G = L;
+  G.taps = 1;
+  G.M = G.cout = mcol;
+  G.ups = 1;
+  G.crop = 0;
+  G.bias = c->col_zero;
+  ConvIO gio{};
+  gio.x = io.x;
+  gio.T_in = io.T_in;
+  gio.rate_in = io.rate_in;
+  gio.h_out = c->col_buf;
+  voc_status st = run_conv(c, G, gio, rows, row_len, VOC_K_CONVT, s);
+  if (st) return st;
+  Col2imArgs a{};
+  a.col = c->col_buf;
+  a.T_col = io.T_in + c->mg;
+  a.Cout = L.cout;
+  a.s = L.ups;
+  a.crop = L.crop;
+  a.bias = L.bias;
+  a.h_out = io.h_out;
+  a.s_out = io.s_out;
+  a.s_alpha = io.snake_next ? io.snake_next->alpha : nullptr;
+  a.s_invden = io.snake_next ? io.snake_next->invden : nullptr;
+  a.T_out = io.T_in * L.ups + c->mg;
+  a.row_len = row_len;
+  a.rate_in = io.rate_in;
+  a.rows = rows;
+  a.op = c->op;
+  const double el = static_cast<double>(rows) * io.T_in * L.ups * L.cout;
+  const double bytes = el * (8.0 + (io.h_out ? 4.0 : 0.0) + (io.s_out ? op_size(c->op) : 0.0));
+  return launch(c, s, VOC_K_COL2IM, 0.0, bytes, "col2im launch", [&] { return launch_col2im(a, s); });
+}
+
 voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const RowInfo& rows,
                       int nrows, int T, void* s_out, const SnakeDev* sn, float* h_out,
                       hipStream_t s, const SnakeDev* h_sn = nullptr) {
@@ -844,7 +906,7 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
     }
     st = xchg(B.s[cur], t);
     if (st) return st;
-    st = run_conv(c, blk.ct, io, rows, B.rows.len, VOC_K_CONVT, s);
+    st = run_convt(c, blk.ct, io, rows, B.rows.len, s);
     if (st) return st;
     if (!xh) cur ^= 1;
     t *= g.stride[b];
@@ -909,7 +971,7 @@ voc_status run_stack_af(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t 
     io.T_in = t;
     io.rate_in = rate;
     io.h_out = B.h;  // the Snake above has consumed h
-    st = run_conv(c, blk.ct, io, rows, B.rows.len, VOC_K_CONVT, s);
+    st = run_convt(c, blk.ct, io, rows, B.rows.len, s);
     if (st) return st;
     t *= g.stride[b];
     rate *= g.stride[b];
@@ -1127,6 +1189,9 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   // Ablation only: 1 runs every Snake of a plain decode as a launch of its own
   // (producers write h only), to measure the standalone Snake stage.
   if (const char* v = std::getenv("VOC_SPLIT_SNAKE")) c->split_snake = std::atoi(v) != 0 && !cfg->causal;
+  // Ablation only: 1 runs every ConvTranspose1d as a GEMM into a column
+  // matrix followed by a col2im overlap-add (the pages' lowering).
+  if (const char* v = std::getenv("VOC_CONVT_COL2IM")) c->col2im = std::atoi(v) != 0 && !cfg->causal;
   *out = c;
   return VOC_OK;
 }
@@ -1781,6 +1846,8 @@ VOC_API void vocoder_destroy(voc_ctx* c) {
   free_weights(c->W);
   if (c->ws) (void)hipFree(c->ws);
   if (c->st_mem) (void)hipFree(c->st_mem);
+  if (c->col_buf) (void)hipFree(c->col_buf);
+  if (c->col_zero) (void)hipFree(c->col_zero);
   for (auto& r : c->pending) {
     (void)hipEventDestroy(r.e0);
     (void)hipEventDestroy(r.e1);
@@ -1948,7 +2015,7 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
       }
       if (st) return st;
       io.x = s0; io.T_in = T; io.rate_in = 1; io.h_out = h;
-      st = run_conv(c, W.blocks[si.b].ct, io, rows, ri.len, VOC_K_CONVT, s);
+      st = run_convt(c, W.blocks[si.b].ct, io, rows, ri.len, s);
       break;
     case 2: {
       // The same kernel path as in a decode: with the operand computed from

@@ -8,6 +8,7 @@
 //   export_kernel        chunked fp32 -> [row][C][T] (stage runner, encoder output)
 //   af_snake_kernel      alias-free Snake: 2x upsample, Snake, 2x downsample
 //   snake_kernel         plain elementwise Snake (the split ablation)
+//   col2im_kernel        overlap-add of a GEMM + col2im ConvTranspose1d (ablation)
 //   head_kernel          Snake -> Conv1d k=7 to one or two channels -> bias ->
 //                        tanh, with the tile / window crop folded into the store
 //   copy_kernel          plain 16-byte vector copy (byte-counter calibration)
@@ -562,6 +563,58 @@ hipError_t launch_snake(const AfArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(snake_kernel<OP_F32>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(snake_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------- col2im
+// The overlap-add half of a ConvTranspose1d computed as GEMM + col2im (the
+// pages' GGML lowering, kept as an ablation of the polyphase GEMM; qwentts.cpp
+// ARCHITECTURE, "Custom GGML ops").  With K = 2s every output frame tau
+// gathers exactly two products: k = (tau + crop) mod s at input frame
+// n = (tau + crop) / s, and k + s at n - 1.  A thread handles four channels
+// of one output frame (whole 64-byte rows per wave).
+template <int OP>
+__global__ __launch_bounds__(256) void col2im_kernel(const Col2imArgs a) {
+  const int r = blockIdx.y;
+  const int nchunk = a.Cout / 16;
+  const int chunk = blockIdx.x % nchunk;
+  const int tau = (blockIdx.x / nchunk) * 64 + static_cast<int>(threadIdx.x >> 2);
+  const int q = threadIdx.x & 3;
+  const int lin = min(a.row_len[r] * a.rate_in, a.T_col);
+  const int lout = min(a.row_len[r] * a.rate_in * a.s, a.T_out);
+  if (tau >= lout) return;
+  const int o = chunk * 16 + q * 4;
+  const int mcol = 2 * a.s * a.Cout;
+  const float* colr = a.col + static_cast<int64_t>(r) * mcol * a.T_col;
+  auto z = [&](int k, int n) -> f4 {  // z[k*Cout + o .. + 3][n]
+    const int m = k * a.Cout + o;
+    return *reinterpret_cast<const f4*>(colr + static_cast<int64_t>(m & ~15) * a.T_col +
+                                        static_cast<int64_t>(n) * kHChunk + (m & 15));
+  };
+  const int n = (tau + a.crop) / a.s, k = tau + a.crop - n * a.s;
+  f4 v = *reinterpret_cast<const f4*>(a.bias + o);
+  if (n < lin) v += z(k, n);
+  if (n >= 1 && n - 1 < lin) v += z(k + a.s, n - 1);
+  if (a.h_out)
+    *reinterpret_cast<f4*>(a.h_out + (static_cast<int64_t>(r) * a.Cout + chunk * 16) * a.T_out +
+                           static_cast<int64_t>(tau) * kHChunk + q * 4) = v;
+  if (a.s_out) {
+    if (a.s_alpha) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = snake_f32(v[e], a.s_alpha[o + e], a.s_invden[o + e]);
+    }
+    constexpr int CH = OP == OP_F32 ? 16 : 32;
+    store_op4<OP>(a.s_out, (static_cast<int64_t>(r) * a.Cout + (o / CH) * CH) * a.T_out +
+                               static_cast<int64_t>(tau) * CH + o % CH, v);
+  }
+}
+
+hipError_t launch_col2im(const Col2imArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.Cout / 16) * ((a.T_out + 63) / 64)), static_cast<unsigned>(a.rows));
+  if (a.op == OP_F32)
+    hipLaunchKernelGGL(col2im_kernel<OP_F32>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(col2im_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -320,7 +320,9 @@ typedef enum voc_kernel_kind {
   VOC_K_ENC_OUT = 10, /* encoder conv_out (k=3) and projection (k=1)    */
   VOC_K_AF_SNAKE = 11, /* alias-free Snake (2x up, Snake, 2x down)      */
   VOC_K_SNAKE = 12,   /* standalone Snake (only in the split ablation)   */
-  VOC_K_COUNT = 13
+  VOC_K_COL2IM = 13,  /* col2im overlap-add (only in the GEMM + col2im    */
+                      /* ablation of the ConvTranspose1d)                 */
+  VOC_K_COUNT = 14
 } voc_kernel_kind;
 
 typedef struct voc_profile_stat {

@@ -275,3 +275,32 @@ def test_split_snake_equals_epilogue_snake(idx, monkeypatch):
         for k in env:
             monkeypatch.delenv(k)
     assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 4])
+def test_gemm_col2im_convt_ablation_vs_oracle(idx, monkeypatch):
+    """The ConvTranspose1d as a plain GEMM into a column matrix plus a col2im
+    overlap-add (the pages' lowering, an ablation of the polyphase GEMM)
+    decodes to the oracle's output within the same gates."""
+    cfg = I.config(idx)
+    t = I.make_weights(cfg, twin=True)
+    frames, rows = SMALL[idx]
+    lat = I.make_latent(cfg, batch=rows, frames=frames)
+    monkeypatch.setenv("VOC_CONVT_COL2IM", "1")
+    ctx = _ctx(cfg, t)
+    try:
+        V.check(V.vocoder_profile_enable(ctx, True), ctx)
+        pcm = V.decode(ctx, to_dev(lat))
+        torch.cuda.synchronize()
+        st, ci = V.vocoder_profile_read(ctx, V.KERNEL_KINDS.index("col2im"))
+        V.check(st, ctx)
+        assert ci["launches"] == len(cfg["strides"])
+    finally:
+        V.vocoder_destroy(ctx)
+        monkeypatch.delenv("VOC_CONVT_COL2IM")
+    ref = O.Model(cfg, t).decode(lat)
+    got = pcm.cpu().numpy()
+    if cfg["dtype"] == "f32":
+        assert rel_maxabs(got, ref) <= TOL["f32"]
+    else:
+        assert rel_rms(got, ref) <= TOL["bf16"]
