@@ -119,20 +119,24 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   // copied by wave b % 4.
   const uint32_t smem_lds = lds_addr(smem);
   // Frames in [-lb, 0) are read from memory (a stream's carried context);
-  // the buffer resource then starts lb frames before frame 0.
-  const uint32_t xv0 = static_cast<uint32_t>(((tfirst + lr) * S + ph0 + a.lb) * kChunkBytes + lg * 16);
-  const uint32_t wv0 = static_cast<uint32_t>((m0 + lr) * kChunkBytes + lg * 16);
+  // the buffer resource then starts lb frames before frame 0.  Offsets are
+  // 32-bit unsigned: a row before the plane wraps to a value past its end
+  // (read as zero).  The host keeps every plane and the rows a tile reads
+  // past it below 2^32 bytes, so no offset wraps into the plane.
+  const uint32_t xv0 = static_cast<uint32_t>((tfirst + lr) * S + ph0 + a.lb) * uint32_t(kChunkBytes) +
+                       static_cast<uint32_t>(lg * 16);
+  const uint32_t wv0 = static_cast<uint32_t>(m0 + lr) * uint32_t(kChunkBytes) + static_cast<uint32_t>(lg * 16);
   auto issue = [&](int c, int stage) {
     const i4 xs = buf_rsrc(xrow + (c / S) * xplane - static_cast<int64_t>(a.lb) * kChunkBytes,
                            static_cast<uint32_t>(Lin + a.lb) * kChunkBytes);
-    const uint32_t xv = xv0 + static_cast<uint32_t>((c % S) * kChunkBytes);
+    const uint32_t xv = xv0 + static_cast<uint32_t>(c % S) * uint32_t(kChunkBytes);
     const i4 ws = buf_rsrc(wbase + c * wplane, static_cast<uint32_t>(wplane));
     const uint32_t dst = smem_lds + stage * STAGE;
 #pragma unroll
     for (int u = 0; u < (TB + 3) / 4; ++u) {
       const int b = wave + 4 * u;
       if (b < XB) {
-        dma16(xs, xv + b * 1024 * S, dst + b * 1024);
+        dma16(xs, xv + static_cast<uint32_t>(b * 1024 * S), dst + b * 1024);
       } else if (b < TB) {
         const int k = b - XB, j = (16 * k) / BM;
         dma16(ws, wv0 + (j * a.M + 16 * k - j * BM) * kChunkBytes, dst + b * 1024);

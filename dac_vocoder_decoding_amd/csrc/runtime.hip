@@ -127,6 +127,12 @@ struct voc_ctx {
   int mg = 0;                   // margin frames of the activation planes being decoded
   std::vector<int64_t> meta_dst;  // host copies kept alive for async uploads
   std::vector<int> meta_int;
+  // cancellation hook (vocoder_set_cancel): polled before a call enqueues
+  // work and between groups of cancel_group units
+  int64_t frames_cap = 0;        // test switch: a lower row-frame limit (0: none)
+  voc_cancel_fn cancel_fn = nullptr;
+  void* cancel_user = nullptr;
+  int64_t cancel_group = 1;
 };
 
 namespace {
@@ -249,6 +255,43 @@ int compute_halo(const voc_config& c) {
   return hl < 0 || hr < 0 ? -1 : std::max(hl, hr);
 }
 
+// The GEMM stages activation tiles through buffer loads with 32-bit byte
+// offsets into one 64-byte-row channel plane.  A launch is addressable when
+// its plane (frames, the lb context frames before it, and the 512 * S rows
+// a tile may read past its end, S the input stride) stays below 2^32 bytes
+// with a 64 KB guard, so that the offsets of rows before the plane (tiles at
+// the left edge) wrap to values past its end and read as zero.
+constexpr int64_t kPlaneLimitBytes = (int64_t(1) << 32) - (int64_t(1) << 16);
+constexpr int64_t kStreamCtxMax = 54;  // the longest carried context: 6 * dilation 9
+
+bool gemm_plane_ok(int64_t plane_frames, int64_t lb, int64_t S) {
+  return plane_frames >= 0 && (plane_frames + lb + 512 * S) * kChunkBytes <= kPlaneLimitBytes;
+}
+
+// Largest GEMM input rate (frames per latent frame) of the decoder stack:
+// the ConvTranspose1d of block b reads frames at rate_b, and the residual
+// convs of block b run as GEMMs at rate_{b+1} unless the unit is fused
+// (the fused unit addresses h with 64-bit pointers).  Alias-free (and
+// split-Snake) stacks run every unit as a GEMM pair.
+int64_t gemm_rate_max(const voc_config& g, int op, bool units_unfused) {
+  int64_t rate = 1, mx = 1;
+  for (int b = 0; b < g.n_blocks; ++b) {
+    mx = std::max(mx, rate);
+    rate *= g.stride[b];
+    const bool fused = !units_unfused && res_unit_tile(op, g.width[b + 1], false) > 0;
+    if (!fused) mx = std::max(mx, rate);
+  }
+  return mx;
+}
+
+// Largest latent frames per decoded row (a whole row, or a tile with its
+// halos) whose GEMM planes are all addressable (streams' context included).
+int64_t max_row_frames(const voc_config& g, int op, bool units_unfused) {
+  const int64_t per = gemm_rate_max(g, op, units_unfused);
+  const int64_t frames = kPlaneLimitBytes / kChunkBytes - kStreamCtxMax - 512;
+  return frames / per;
+}
+
 // ------------------------------------------------------------- profiling
 hipEvent_t take_event(voc_ctx* c) {
   if (!c->free_events.empty()) {
@@ -314,6 +357,13 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // write no operand tensor, and h alternates between two buffers.
 bool unit_xh(const voc_ctx* c, int C) {
   return !c->cfg.af_snake && !c->split_snake && c->ru_xh && !c->no_fuse && res_unit_tile(c->op, C, false) > 0 && res_unit_from_h_ok(c->op, C);
+}
+
+// Largest latent frames per decoded row this context's decoder can address
+// (its GEMM planes below 4 GiB; the ablation switches move units onto GEMMs).
+int64_t row_frames_limit(const voc_ctx* c) {
+  const int64_t m = max_row_frames(c->cfg, c->op, c->cfg.af_snake || c->split_snake || c->no_fuse);
+  return c->frames_cap > 0 ? std::min(m, c->frames_cap) : m;
 }
 
 bool any_unit_xh(const voc_ctx* c) {
@@ -555,6 +605,10 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.hs_scale = io.h_snake ? io.h_snake->alpha : nullptr;
   a.hs_h = io.h_snake ? io.h_snake->invden : nullptr;
   a.rows = rows;
+  if (!gemm_plane_ok(a.T_in, a.lb, L.down))
+    return fail(c, VOC_INVALID_PARAMS,
+                "a convolution's input plane exceeds the 4 GiB range of the GEMM's 32-bit buffer offsets "
+                "(decode in time tiles)");
   int v = pick_variant(c->op, L.taps, L.M, a.N, rows);
   if (c->force_variant[kind] >= 0 && conv_variant_ok(c->force_variant[kind], L.taps))
     v = c->force_variant[kind];
@@ -1157,6 +1211,11 @@ VOC_API int voc_config_halo(const voc_config* cfg) {
   return compute_halo(*cfg);
 }
 
+VOC_API int64_t voc_config_max_frames(const voc_config* cfg) {
+  if (validate(cfg, nullptr) != VOC_OK) return VOC_INVALID_PARAMS;
+  return max_row_frames(*cfg, cfg->dtype == VOC_F32 ? OP_F32 : OP_BF16, cfg->af_snake != 0);
+}
+
 VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx** out) {
   if (!out) return fail(nullptr, VOC_INVALID_PARAMS, "out is NULL");
   *out = nullptr;
@@ -1183,6 +1242,9 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   for (int k = 0; k < 4; ++k)
     if (const char* v = std::getenv(names[k])) c->force_variant[k] = std::atoi(v);
   if (const char* v = std::getenv("VOC_NO_FUSED_RES")) c->no_fuse = std::atoi(v) != 0;
+  // Test switch: VOC_MAX_ROW_FRAMES lowers the row-frame limit, so that the
+  // automatic time tiling of long rows can be exercised at small sizes.
+  if (const char* v = std::getenv("VOC_MAX_ROW_FRAMES")) c->frames_cap = std::atoll(v);
   if (const char* v = std::getenv("VOC_CONV_M_FAST")) c->m_order = std::atoi(v) != 0;
   // Ablation only: 0 makes every fused unit read an operand tensor written by its producer.
   if (const char* v = std::getenv("VOC_RU_OPERAND_FROM_H")) c->ru_xh = std::atoi(v) != 0;
@@ -1462,13 +1524,18 @@ VOC_API int64_t vocoder_output_length(const voc_ctx* c, int64_t T) {
 }
 
 namespace {
+// The cancel hook's answer (false without a hook).
+bool cancel_requested(voc_ctx* c) { return c->cancel_fn && c->cancel_fn(c->cancel_user) != 0; }
+
+voc_status cancelled(voc_ctx* c) { return fail(c, VOC_CANCELLED, "cancelled by the cancel hook"); }
+
 // One batched decode of `rows` rows read from latent [*, C, T_src] through
 // the row metadata (dst, ints = len | src_b | start | keep_lo | keep_hi),
 // which is uploaded unless `key` matches what the workspace already holds.
 // Output channel o of row r starts at pcm[dst[r] + o * ch_stride].
-voc_status decode_rows(voc_ctx* c, const float* latent, int64_t T_src, int64_t rows, int T_alloc,
-                       std::vector<int64_t>&& dst, std::vector<int>&& ints,
-                       std::vector<int64_t>&& key, float* pcm, int64_t ch_stride, hipStream_t s) {
+voc_status decode_batch(voc_ctx* c, const float* latent, int64_t T_src, int64_t rows, int T_alloc,
+                        std::vector<int64_t>&& dst, std::vector<int>&& ints,
+                        std::vector<int64_t>&& key, float* pcm, int64_t ch_stride, hipStream_t s) {
   const voc_config& g = c->cfg;
   const Plan p = make_plan(c, static_cast<int>(rows), T_alloc);
   voc_status st = ensure_ws(c, p.bytes);
@@ -1488,6 +1555,39 @@ voc_status decode_rows(voc_ctx* c, const float* latent, int64_t T_src, int64_t r
   if (st) return st;
   return run_head(c, h_last, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
                   static_cast<int>(c->hop), pcm, ch_stride, s);
+}
+
+// decode_batch over the rows in groups of `group` rows (all at once when
+// group >= rows).  With a cancel hook, the hook is polled before every group
+// and the stream is synchronized after each, so a cancel lands between
+// groups of finished rows.  Rows are independent, so grouping changes no
+// output bit.
+voc_status decode_rows(voc_ctx* c, const float* latent, int64_t T_src, int64_t rows, int T_alloc,
+                       std::vector<int64_t>&& dst, std::vector<int>&& ints,
+                       std::vector<int64_t>&& key, float* pcm, int64_t ch_stride, hipStream_t s,
+                       int64_t group) {
+  if (group >= rows && !c->cancel_fn)
+    return decode_batch(c, latent, T_src, rows, T_alloc, std::move(dst), std::move(ints), std::move(key),
+                        pcm, ch_stride, s);
+  for (int64_t r0 = 0; r0 < rows; r0 += group) {
+    if (cancel_requested(c)) return cancelled(c);
+    const int64_t n = std::min(group, rows - r0);
+    std::vector<int64_t> gd(dst.begin() + r0, dst.begin() + r0 + n);
+    std::vector<int> gi(5 * n);
+    for (int f = 0; f < 5; ++f)
+      std::copy(ints.begin() + f * rows + r0, ints.begin() + f * rows + r0 + n, gi.begin() + f * n);
+    std::vector<int64_t> gk = key;
+    gk.push_back(r0);
+    gk.push_back(n);
+    voc_status st = decode_batch(c, latent, T_src, n, T_alloc, std::move(gd), std::move(gi), std::move(gk),
+                                 pcm, ch_stride, s);
+    if (st) return st;
+    if (c->cancel_fn) {
+      const hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(c, e, "stream synchronize between groups");
+    }
+  }
+  return VOC_OK;
 }
 
 // Kept latent frames [lo, hi) of window k of n (window stitching): every
@@ -1525,12 +1625,23 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
   const voc_config& g = c->cfg;
   // Rows: whole rows, or tiles of tile_frames latent frames with halos.
-  const int64_t F = g.tile_frames > 0 ? g.tile_frames : T;
+  // Untiled rows beyond what the GEMMs can address are tiled here, with
+  // the largest tile whose halos still fit (the same samples, bit for bit).
+  const int64_t max_frames = row_frames_limit(c);
+  int64_t F = g.tile_frames > 0 ? g.tile_frames : T;
+  bool tiled = g.tile_frames > 0;
+  if (!tiled && T > max_frames) {
+    F = max_frames - c->halo_l - c->halo_r;
+    tiled = true;
+  }
+  if (tiled && F + c->halo_l + c->halo_r > max_frames)
+    return fail(c, VOC_INVALID_PARAMS, "tile_frames plus the halos exceed the frames the GEMMs can address "
+                                       "(voc_config_max_frames)");
   const int64_t ntile = (T + F - 1) / F;
   const int64_t rows = B * ntile;
   if (rows > 65535) return fail(c, VOC_INVALID_PARAMS, "too many rows (B * tiles > 65535)");
-  const int HL = g.tile_frames > 0 ? c->halo_l : 0;
-  const int HR = g.tile_frames > 0 ? c->halo_r : 0;
+  const int HL = tiled ? c->halo_l : 0;
+  const int HR = tiled ? c->halo_r : 0;
   const int T_alloc = static_cast<int>(std::min<int64_t>(T, F + HL + HR));
   std::vector<int64_t> dst(rows);
   std::vector<int> ints(5 * rows);
@@ -1546,8 +1657,9 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
       ints[4 * rows + r] = static_cast<int>((t1 - a) * c->hop);   // keep_hi
       dst[r] = (b * g.out_channels * T + t0) * c->hop;
     }
+  const int64_t group = c->cancel_fn ? c->cancel_group : rows;
   return decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {0, B, T, rows}, pcm,
-                     T * c->hop, static_cast<hipStream_t>(stream));
+                     T * c->hop, static_cast<hipStream_t>(stream), group);
 }
 
 VOC_API voc_status vocoder_encode(voc_ctx* c, const float* audio, int64_t B, int64_t T, float* latent,
@@ -1559,8 +1671,12 @@ VOC_API voc_status vocoder_encode(voc_ctx* c, const float* audio, int64_t B, int
   if ((reinterpret_cast<uintptr_t>(audio) | reinterpret_cast<uintptr_t>(latent)) & 15)
     return fail(c, VOC_INVALID_PARAMS, "audio and latent must be 16-byte aligned");
   if (B <= 0 || T <= 0 || B > 65535) return fail(c, VOC_INVALID_PARAMS, "B in [1, 65535] and T > 0 required");
-  if (T * c->hop > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "T*hop exceeds 2^31-1");
+  // The audio-rate layers read 64-byte rows per sample through the GEMM's
+  // 32-bit buffer offsets: keep those planes below 4 GiB.
+  if (T * c->hop > (int64_t(1) << 26) - (int64_t(1) << 16))
+    return fail(c, VOC_INVALID_PARAMS, "T*hop exceeds 2^26 - 2^16 samples per row");
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  if (cancel_requested(c)) return cancelled(c);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int rows = static_cast<int>(B), nb = g.n_blocks, nr = g.n_res;
   const int* E = g.enc_width;
@@ -1741,7 +1857,10 @@ VOC_API voc_status vocoder_stream_decode(voc_ctx* c, const float* latent, int64_
     return fail(c, VOC_INVALID_PARAMS, "latent and pcm must be 16-byte aligned");
   if (t <= 0 || t * c->hop + c->st_margin > (int64_t(1) << 31) - 1)
     return fail(c, VOC_INVALID_PARAMS, "t must be positive with t * hop below 2^31");
+  if (t > row_frames_limit(c))
+    return fail(c, VOC_INVALID_PARAMS, "t exceeds the frames the GEMMs can address (voc_config_max_frames)");
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  if (cancel_requested(c)) return cancelled(c);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = c->st_rows;
   const int mg = c->st_margin;
@@ -1806,6 +1925,8 @@ VOC_API voc_status vocoder_decode_windows(voc_ctx* c, const float* latents, int6
     return fail(c, VOC_INVALID_PARAMS, "bad window count, lengths or crops (every window must keep a frame)");
   if (c->cfg.tile_frames != 0) return fail(c, VOC_INVALID_PARAMS, "windowed decode needs tile_frames == 0");
   if (L * c->hop > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "L*hop exceeds 2^31-1");
+  if (L > row_frames_limit(c))
+    return fail(c, VOC_INVALID_PARAMS, "L exceeds the frames the GEMMs can address (voc_config_max_frames)");
   const int64_t rows = n * sides;
   if (rows > 65535) return fail(c, VOC_INVALID_PARAMS, "too many rows (n_windows * sides > 65535)");
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
@@ -1831,8 +1952,18 @@ VOC_API voc_status vocoder_decode_windows(voc_ctx* c, const float* latents, int6
     }
     before += hi - lo;
   }
+  const int64_t group = c->cancel_fn ? c->cancel_group * sides : rows;
   return decode_rows(c, latents, L, rows, static_cast<int>(L), std::move(dst), std::move(ints),
-                     {1, n, sides, L, L_last, cl, cr}, pcm, N, static_cast<hipStream_t>(stream));
+                     {1, n, sides, L, L_last, cl, cr}, pcm, N, static_cast<hipStream_t>(stream), group);
+}
+
+VOC_API voc_status vocoder_set_cancel(voc_ctx* c, voc_cancel_fn fn, void* user, int64_t group) {
+  if (!c) return VOC_INVALID_PARAMS;
+  if (group < 1) return fail(c, VOC_INVALID_PARAMS, "group must be at least 1");
+  c->cancel_fn = fn;
+  c->cancel_user = user;
+  c->cancel_group = group;
+  return VOC_OK;
 }
 
 VOC_API const char* vocoder_last_error(const voc_ctx* c) {

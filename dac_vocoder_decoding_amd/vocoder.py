@@ -27,6 +27,7 @@ VOC_BAD_WEIGHTS = -2
 VOC_OOM = -3
 VOC_DEVICE_ERROR = -4
 VOC_NOT_LOADED = -5
+VOC_CANCELLED = -6
 
 VOC_F32, VOC_BF16 = 0, 1
 VOC_SNAKE, VOC_SNAKE_BETA = 0, 1
@@ -80,6 +81,15 @@ class voc_profile_stat(ctypes.Structure):
 
 _lib = None
 
+# int (*voc_cancel_fn)(void *user)
+CANCEL_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p)
+
+# Per-context host state the C calls do not return: the rows of the streams
+# started by vocoder_stream_reset, and the installed cancel callback (kept
+# referenced while the library holds its pointer).
+_stream_rows: dict = {}
+_cancel_keep: dict = {}
+
 
 def lib():
     """The loaded libvocoder.so.  Raises if it has not been built."""
@@ -96,6 +106,8 @@ def lib():
             "voc_config_validate": (I, [CFG]),
             "voc_config_hop": (I64, [CFG]),
             "voc_config_halo": (I, [CFG]),
+            "voc_config_max_frames": (I64, [CFG]),
+            "vocoder_set_cancel": (I, [P, CANCEL_FN, P, I64]),
             "vocoder_create": (I, [CFG, I, ctypes.POINTER(P)]),
             "vocoder_load_weights": (I, [P, ctypes.POINTER(voc_tensor), I]),
             "vocoder_output_length": (I64, [P, I64]),
@@ -130,6 +142,19 @@ class VocError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"status {status}: {msg}")
         self.status = status
+
+
+def _key(ctx):
+    return ctx.value if isinstance(ctx, ctypes.c_void_p) else int(ctx or 0)
+
+
+def expect_dim(what: str, shape, dim: int, want: int) -> None:
+    """Raise ValueError unless shape[dim] == want (checked before any call
+    that would let the library read or write past a buffer)."""
+    if len(shape) != 3:
+        raise ValueError(f"{what}: expected a 3-d tensor, got shape {tuple(shape)}")
+    if shape[dim] != want:
+        raise ValueError(f"{what}: dimension {dim} is {shape[dim]}, the context needs {want}")
 
 
 def _ptr(t):
@@ -195,6 +220,10 @@ def voc_config_halo(cfg: voc_config) -> int:
     return lib().voc_config_halo(ctypes.byref(cfg))
 
 
+def voc_config_max_frames(cfg: voc_config) -> int:
+    return lib().voc_config_max_frames(ctypes.byref(cfg))
+
+
 # ----------------------------------------------------------------- context
 def vocoder_create(cfg: voc_config, device: int = 0):
     """Returns (status, ctx)."""
@@ -249,6 +278,7 @@ def encode(ctx, audio, latent_channels: int, stream=None):
     [B, 1, T * hop]."""
     import torch
     assert audio.is_cuda and audio.dtype == torch.float32 and audio.is_contiguous()
+    expect_dim("audio", audio.shape, 1, 1)
     b, _, n = audio.shape
     hop = vocoder_output_length(ctx, 1)
     assert n % hop == 0
@@ -258,7 +288,22 @@ def encode(ctx, audio, latent_channels: int, stream=None):
 
 
 def vocoder_stream_reset(ctx, rows: int) -> int:
-    return lib().vocoder_stream_reset(ctx, rows)
+    st = lib().vocoder_stream_reset(ctx, rows)
+    _stream_rows[_key(ctx)] = rows if st == VOC_OK else 0
+    return st
+
+
+def vocoder_set_cancel(ctx, fn, group: int = 1) -> int:
+    """Install fn() -> bool as the cancel hook (None removes it); see
+    vocoder_set_cancel in vocoder.h for when it is polled."""
+    if fn is None:
+        cb = CANCEL_FN()
+    else:
+        cb = CANCEL_FN(lambda _user: 1 if fn() else 0)
+    st = lib().vocoder_set_cancel(ctx, cb, None, group)
+    if st == VOC_OK:
+        _cancel_keep[_key(ctx)] = cb
+    return st
 
 
 def vocoder_stream_decode(ctx, latent, t: int, pcm, stream=None) -> int:
@@ -272,6 +317,8 @@ def vocoder_last_error(ctx) -> str:
 
 def vocoder_destroy(ctx) -> None:
     lib().vocoder_destroy(ctx)
+    _stream_rows.pop(_key(ctx), None)
+    _cancel_keep.pop(_key(ctx), None)
 
 
 def vocoder_profile_enable(ctx, enable: bool) -> int:
@@ -349,10 +396,18 @@ def out_channels(ctx) -> int:
     return c_out
 
 
+def latent_channels(ctx) -> int:
+    """Latent channels the context decodes (stage 0's c_in)."""
+    st, c_in, _, _ = voc_dbg_stage_shape(ctx, 0, 1)
+    check(st, ctx)
+    return c_in
+
+
 def decode(ctx, latent, stream=None):
     """pcm [B, out_channels, T*hop] (new CUDA tensor) for a CUDA fp32 latent [B, C, T]."""
     import torch
     assert latent.is_cuda and latent.dtype == torch.float32 and latent.is_contiguous()
+    expect_dim("latent", latent.shape, 1, latent_channels(ctx))
     b, _, t = latent.shape
     pcm = torch.empty(b, out_channels(ctx), vocoder_output_length(ctx, t), device=latent.device)
     check(vocoder_decode(ctx, latent, b, t, pcm, stream), ctx)
@@ -365,6 +420,7 @@ def decode_windows(ctx, windows, sides: int, last_frames: int, crop_left: int, c
     windows [n, sides * C, L] (vocoder_decode_windows)."""
     import torch
     assert windows.is_cuda and windows.dtype == torch.float32 and windows.is_contiguous()
+    expect_dim("windows", windows.shape, 1, sides * latent_channels(ctx))
     n, _, L = windows.shape
     N = vocoder_windows_output_length(ctx, n, L, last_frames, crop_left, crop_right)
     if N < 0:
@@ -380,6 +436,8 @@ def stream_decode(ctx, latent, stream=None):
     [rows, C, t] of the streams started by vocoder_stream_reset."""
     import torch
     assert latent.is_cuda and latent.dtype == torch.float32 and latent.is_contiguous()
+    expect_dim("latent", latent.shape, 0, _stream_rows.get(_key(ctx), 0))
+    expect_dim("latent", latent.shape, 1, latent_channels(ctx))
     rows, _, t = latent.shape
     pcm = torch.empty(rows, out_channels(ctx), vocoder_output_length(ctx, t), device=latent.device)
     check(vocoder_stream_decode(ctx, latent, t, pcm, stream), ctx)
@@ -391,8 +449,9 @@ def run_stage(ctx, stage: int, x, stream=None):
     import torch
     assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous()
     b, _, t = x.shape
-    st, _, c_out, t_out = voc_dbg_stage_shape(ctx, stage, t)
+    st, c_in, c_out, t_out = voc_dbg_stage_shape(ctx, stage, t)
     check(st, ctx)
+    expect_dim("stage input", x.shape, 1, c_in)
     out = torch.empty(b, c_out, t_out, device=x.device)
     check(voc_dbg_run_stage(ctx, stage, x, b, t, out, stream), ctx)
     return out

@@ -74,7 +74,8 @@ typedef enum voc_status {
                            /* or a non-finite value                          */
   VOC_OOM = -3,            /* device allocation failed or exceeds the cap    */
   VOC_DEVICE_ERROR = -4,   /* a HIP call or kernel launch failed             */
-  VOC_NOT_LOADED = -5      /* decode before a successful load_weights        */
+  VOC_NOT_LOADED = -5,     /* decode before a successful load_weights        */
+  VOC_CANCELLED = -6       /* the cancel hook asked to stop (vocoder_set_cancel) */
 } voc_status;
 
 typedef enum voc_dtype {
@@ -153,6 +154,18 @@ int64_t voc_config_hop(const voc_config *cfg);
  * and no frames to the right are needed.  Negative status if *cfg is invalid. */
 int voc_config_halo(const voc_config *cfg);
 
+/* Largest latent frames per decoded row that the matrix-core kernels can
+ * address (host-only): a whole row of an untiled decode, a window of
+ * vocoder_decode_windows, a stream chunk, or a time tile plus its two halos.
+ * The GEMMs read each activation channel plane (64 bytes per frame) through
+ * buffer loads with 32-bit byte offsets, so a plane must stay below 4 GiB;
+ * the bound is set by the highest-rate layer that runs as a GEMM (for the
+ * default decoder the last ConvTranspose1d, at hop/2 frames per latent
+ * frame: 262 k latent frames, about 50 min of 44.1 kHz audio).
+ * vocoder_decode splits longer untiled rows into time tiles on its own.
+ * Negative status if *cfg is invalid. */
+int64_t voc_config_max_frames(const voc_config *cfg);
+
 /* Create a context on HIP device hip_device.  Validates *cfg first (no device
  * call happens if it is invalid).  *out receives the context or NULL. */
 voc_status vocoder_create(const voc_config *cfg, int hip_device, voc_ctx **out);
@@ -208,8 +221,12 @@ int64_t vocoder_output_length(const voc_ctx *ctx, int64_t T);
  * to bf16 as a matrix-core operand.  With tile_frames > 0 the rows are cut
  * into tiles of tile_frames latent frames plus the exact halo on each side
  * and all tiles are decoded as one batch.
- * Errors: VOC_INVALID_PARAMS (NULL/misaligned pointers, B or T <= 0, sizes
- * beyond 2^31 elements per row), VOC_NOT_LOADED, VOC_OOM, VOC_DEVICE_ERROR.
+ * Untiled rows longer than voc_config_max_frames() are decoded in time
+ * tiles with exact halos as well (the same samples, bit for bit).
+ * Errors: VOC_INVALID_PARAMS (NULL/misaligned pointers, B or T <= 0, T*hop
+ * beyond 2^31 - 1 samples per row, a tile plus halos beyond
+ * voc_config_max_frames(), more than 65535 rows of tiles),
+ * VOC_NOT_LOADED, VOC_OOM, VOC_DEVICE_ERROR, VOC_CANCELLED.
  */
 voc_status vocoder_decode(voc_ctx *ctx, const float *latent, int64_t B, int64_t T,
                           float *pcm, void *hip_stream);
@@ -237,8 +254,9 @@ voc_status vocoder_decode(voc_ctx *ctx, const float *latent, int64_t B, int64_t 
  * tile_frames == 0.  Same asynchrony and buffer ownership as vocoder_decode;
  * one batched decode of all n_windows * sides rows.
  * Errors: VOC_INVALID_PARAMS (NULL/misaligned pointers, bad counts or crops,
- * a window keeping nothing, tile_frames != 0), VOC_NOT_LOADED, VOC_OOM,
- * VOC_DEVICE_ERROR.
+ * a window keeping nothing, tile_frames != 0, L beyond
+ * voc_config_max_frames()), VOC_NOT_LOADED, VOC_OOM, VOC_DEVICE_ERROR,
+ * VOC_CANCELLED.
  */
 voc_status vocoder_decode_windows(voc_ctx *ctx, const float *latents, int64_t n_windows,
                                   int64_t sides, int64_t L, int64_t L_last,
@@ -263,8 +281,9 @@ voc_status vocoder_decode_windows(voc_ctx *ctx, const float *latents, int64_t n_
  * vocoder_decode; the state lives in library memory (hipMalloc at reset,
  * cleared to zero there, which is the offline decode's zero left padding).
  * Errors: VOC_INVALID_PARAMS (non-causal or tiled configuration, rows or t
- * out of range, NULL/misaligned pointers, decode before reset),
- * VOC_NOT_LOADED, VOC_OOM, VOC_DEVICE_ERROR.
+ * out of range (t at most voc_config_max_frames()), NULL/misaligned
+ * pointers, decode before reset), VOC_NOT_LOADED, VOC_OOM, VOC_DEVICE_ERROR,
+ * VOC_CANCELLED (before the chunk: the stream state is unchanged).
  */
 voc_status vocoder_stream_reset(voc_ctx *ctx, int64_t rows);
 voc_status vocoder_stream_decode(voc_ctx *ctx, const float *latent, int64_t t, float *pcm,
@@ -280,8 +299,9 @@ voc_status vocoder_stream_decode(voc_ctx *ctx, const float *latent, int64_t t, f
  * asynchrony and ownership as vocoder_decode.  BF16 configs round the audio
  * to bf16 as a matrix-core operand.
  * Errors: VOC_INVALID_PARAMS (no encoder configured, NULL/misaligned
- * pointers, B or T <= 0, T*hop beyond 2^31), VOC_NOT_LOADED, VOC_OOM,
- * VOC_DEVICE_ERROR.
+ * pointers, B or T <= 0, T*hop beyond 2^26 - 2^16 samples per row, which
+ * keeps the audio-rate layers' planes below 4 GiB), VOC_NOT_LOADED, VOC_OOM,
+ * VOC_DEVICE_ERROR, VOC_CANCELLED.
  */
 voc_status vocoder_encode(voc_ctx *ctx, const float *audio, int64_t B, int64_t T, float *latent,
                           void *hip_stream);
@@ -290,6 +310,29 @@ voc_status vocoder_encode(voc_ctx *ctx, const float *audio, int64_t B, int64_t T
  * hop times the kept latent frames of all windows; -1 if they are invalid. */
 int64_t vocoder_windows_output_length(const voc_ctx *ctx, int64_t n_windows, int64_t L,
                                       int64_t L_last, int64_t crop_left, int64_t crop_right);
+
+/*
+ * Cancellation (minimaxmusic.cpp ARCHITECTURE, "mm-server reference",
+ * "Concurrency": a job's cancel flag is polled between VAE windows;
+ * qwentts.cpp ARCHITECTURE, "Public API": a polled cancel returns a
+ * CANCELLED status).  With a hook installed (fn != NULL), vocoder_decode,
+ * vocoder_decode_windows, vocoder_encode and vocoder_stream_decode call
+ * fn(user) on the calling thread before they enqueue any work, and
+ * vocoder_decode / vocoder_decode_windows decode their rows in groups of
+ * `group` units (decode: rows of the batch, or with tile_frames > 0 time
+ * tiles, batch-row major; windows: whole windows with all their sides),
+ * wait for each group to finish on the stream and call fn again before the
+ * next.  A non-zero return stops the call with VOC_CANCELLED: the groups
+ * already decoded are in pcm, the rest of pcm is untouched, and the context
+ * (weights, workspace, stream state) stays valid for the next call; a
+ * cancelled stream chunk leaves the stream where it was.  Rows are decoded
+ * independently, so the samples written equal those of an uncancelled call
+ * bit for bit.  Without a hook (fn == NULL, the default) calls stay
+ * asynchronous and decode all rows as one batch.
+ * Errors: VOC_INVALID_PARAMS (NULL ctx, group < 1).
+ */
+typedef int (*voc_cancel_fn)(void *user);
+voc_status vocoder_set_cancel(voc_ctx *ctx, voc_cancel_fn fn, void *user, int64_t group);
 
 /* Message of the last error on ctx ("" if none); valid until the next call on
  * ctx.  With ctx == NULL, the message of the last failed vocoder_create. */
@@ -363,9 +406,9 @@ voc_status voc_dbg_copy(void *dst, const void *src, int64_t bytes, void *hip_str
 /* What the device delivers, measured now, beside its published peaks.
  * what = 0: HBM, a plain copy of n bytes (n a multiple of 16; 2 warm-up
  *   copies, then 5 timed): *value = GB/s counting the bytes read and written.
- * what = 1 / 2: matrix cores, n iterations of a loop of independent 16x16
- *   MFMA chains (fp32 16x16x4 / bf16 16x16x32) on 8 workgroups of 4 waves
- *   per CU, after a warm-up of n/10: *value = TFLOP/s.
+ * what = 1 / 2: matrix cores, n iterations of a loop of 16 independent
+ *   16x16 MFMA chains per wave (fp32 16x16x4 / bf16 16x16x32) on 4
+ *   workgroups of 4 waves per CU, after a warm-up of n/10: *value = TFLOP/s.
  * what = 3 / 4: the same with 32x32 MFMAs (fp32 32x32x2 / bf16 32x32x16).
  * Allocates its own buffers, runs on hip_stream and synchronizes it; for
  * measurement only, not for a decode loop.  Errors: VOC_INVALID_PARAMS

@@ -25,6 +25,9 @@ int main(void) {
   EXPECT(voc_config_validate(&cfg) == VOC_OK);
   EXPECT(voc_config_hop(&cfg) == 512);
   EXPECT(voc_config_halo(&cfg) == 10);
+  /* the last ConvTranspose1d reads 256 frames per latent frame */
+  EXPECT(voc_config_max_frames(&cfg) > 200000 && voc_config_max_frames(&cfg) < 270000);
+  EXPECT(voc_config_max_frames(NULL) == VOC_INVALID_PARAMS);
   EXPECT(cfg.in_proj == 0);
   cfg.in_proj = 1024;
   EXPECT(voc_config_validate(&cfg) == VOC_OK);
@@ -53,6 +56,8 @@ int main(void) {
   EXPECT(vocoder_windows_output_length(NULL, 3, 689, 683, 86, 258) == -1);
   EXPECT(vocoder_stream_reset(NULL, 4) == VOC_INVALID_PARAMS);
   EXPECT(vocoder_encode(NULL, dummy, 1, 1, dummy, NULL) == VOC_INVALID_PARAMS);
+  EXPECT(vocoder_set_cancel(NULL, (voc_cancel_fn)0, NULL, 1) == VOC_INVALID_PARAMS);
+  EXPECT(VOC_CANCELLED == -6);
   voc_config_default(&cfg);
   cfg.enc_width[0] = 64; cfg.enc_width[1] = 128; cfg.enc_width[2] = 256; cfg.enc_width[3] = 512;
   cfg.enc_width[4] = 1024;

@@ -118,3 +118,62 @@ def test_alias_free_snake_needs_a_plain_decoder():
         assert st == V.VOC_INVALID_PARAMS and not ctx.value
         assert why in V.vocoder_last_error(None)
     assert V.voc_config_validate(V.config_from_dict(I.CONFIGS[9])) == V.VOC_OK
+
+
+def _rate_max(d):
+    """Largest input rate (frames per latent frame) among the decoder's GEMM
+    launches: every ConvTranspose1d at its input rate, and the residual convs
+    of the blocks whose units have no fused kernel (fp32: widths up to 128;
+    bf16: 64, 96, 128, 192) at the block's output rate; alias-free decoders
+    run every unit as a GEMM pair."""
+    fused = {"f32": {16, 32, 64, 96, 128}, "bf16": {64, 96, 128, 192}}[d["dtype"]]
+    rate, mx = 1, 1
+    for b, s in enumerate(d["strides"]):
+        mx = max(mx, rate)
+        rate *= s
+        if d.get("af_snake", 0) or d["widths"][b + 1] not in fused:
+            mx = max(mx, rate)
+    return mx
+
+
+@pytest.mark.parametrize("idx", sorted(I.CONFIGS))
+def test_max_frames_keeps_every_gemm_plane_below_4gib(idx):
+    """The GEMMs address a 64-byte-per-frame channel plane with 32-bit byte
+    offsets: the plane, the 54 context frames a stream carries and the 512
+    rows a tile reads past its end must stay under 2^32 - 2^16 bytes.  The
+    limit is set by the highest-rate GEMM layer."""
+    d = I.CONFIGS[idx]
+    m = V.voc_config_max_frames(V.config_from_dict(d))
+    r = _rate_max(d)
+    limit = (2 ** 32 - 2 ** 16) // 64 - 54 - 512
+    assert m == limit // r, (m, r)
+    assert (m * r + 54 + 512) * 64 <= 2 ** 32 - 2 ** 16
+    assert ((m + 1) * r + 54 + 512) * 64 > 2 ** 32 - 2 ** 16
+
+
+def test_max_frames_default_decoder():
+    # widths 1024..64 fp32: units at 128 and 64 channels are fused, so the
+    # last ConvTranspose1d (input rate 512 / 2 = 256) bounds the rows.
+    c = V.voc_config_default()
+    assert V.voc_config_max_frames(c) == ((2 ** 32 - 2 ** 16) // 64 - 566) // 256
+    c.width[4] = 256       # the last block's units now run as GEMMs at rate 512
+    c.width[3] = 256
+    assert V.voc_config_max_frames(c) == ((2 ** 32 - 2 ** 16) // 64 - 566) // 512
+
+
+def test_set_cancel_validates_arguments():
+    assert V.lib().vocoder_set_cancel(None, V.CANCEL_FN(), None, 1) == V.VOC_INVALID_PARAMS
+
+
+@pytest.mark.parametrize("shape,dim,want,ok", [
+    ((2, 64, 9), 1, 64, True), ((2, 63, 9), 1, 64, False), ((3, 64, 9), 0, 2, False),
+    ((2, 64), 1, 64, False), ((2, 128, 4), 1, 128, True)])
+def test_binding_shape_check(shape, dim, want, ok):
+    """The binding's helpers check the channel count (and a stream's row
+    count) against the context before any call that would let the library
+    read or write past the caller's buffers."""
+    if ok:
+        V.expect_dim("latent", shape, dim, want)
+    else:
+        with pytest.raises(ValueError):
+            V.expect_dim("latent", shape, dim, want)
