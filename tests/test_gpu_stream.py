@@ -17,7 +17,7 @@ from dac_vocoder_decoding_amd import inputs as I
 from dac_vocoder_decoding_amd import vocoder as V
 from oracle import oracle as O
 
-from gpu_util import TOL, rel_maxabs, rel_rms, to_dev
+from gpu_util import BF16_E2E_MAXABS_WIDE, TOL, bf16_stage_ok, rel_maxabs, rel_rms, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -66,15 +66,17 @@ def test_causal_stages_and_decode_vs_oracle(dtype):
         assert e_max <= TOL["f32"]
     else:
         assert e_rms <= TOL["bf16"]
+        assert e_max <= BF16_E2E_MAXABS_WIDE, e_max
 
 
 def test_causal_literal_bf16_stages_vs_floor():
     """Literal weights, bf16, every stage on the GPU's own input.  Against the
     oracle that rounds the same operands to bf16 the kernels must agree
     closely (rel-RMS <= 1e-3, max-abs <= 1e-2 of the stage RMS).  Against the
-    exact oracle the bf16 operands alone cost up to 1.75e-2 of the RMS on
+    exact oracle the bf16 operands alone cost up to 2.05e-2 of the RMS on
     this workload (the operand-rounded oracle's own error), so the 2e-2 gate
-    is held where that floor leaves room and 1.5x the floor elsewhere."""
+    is held where that floor leaves room and the floor plus 1e-3 elsewhere
+    (bf16_stage_ok)."""
     cfg = I.config(7)
     t = I.make_weights(cfg)
     lat = I.make_latent(cfg, batch=2, frames=4)
@@ -91,7 +93,7 @@ def test_causal_literal_bf16_stages_vs_floor():
             floor = rel_maxabs(ref_r, ref)
             e = rel_maxabs(got, ref)
             print(f"stage {k}: GPU {e:.2e}, bf16 operand floor {floor:.2e}")
-            assert e <= max(TOL["bf16"], 1.5 * floor), (k, e, floor)
+            assert bf16_stage_ok(e, floor), (k, e, floor)
             assert rel_rms(got, ref_r) <= 1e-3, (k, rel_rms(got, ref_r))
             assert rel_maxabs(got, ref_r) <= 1e-2, (k, rel_maxabs(got, ref_r))
             x = y

@@ -17,7 +17,7 @@ from dac_vocoder_decoding_amd import inputs as I
 from dac_vocoder_decoding_amd import vocoder as V
 from oracle import oracle as O
 
-from gpu_util import TOL, rel_maxabs, rel_rms, to_dev
+from gpu_util import BF16_E2E_MAXABS, TOL, rel_maxabs, rel_rms, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,7 @@ def test_windows_parity_vs_oracle(idx):
         assert e_max <= TOL["f32"]
     else:
         assert e_rms <= TOL["bf16"]
+        assert e_max <= BF16_E2E_MAXABS, e_max
 
 
 def test_windows_mono():
