@@ -15,6 +15,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -25,6 +26,18 @@ using namespace voc;
 namespace {
 
 std::string g_create_error;
+
+// The no-allocation decode's workspace (vocoder_decode_noalloc): a fixed
+// device array, one copy per GPU, held until the process ends.  Host code
+// never passes this name to a kernel or a copy: the address of each
+// device's copy comes from hipGetSymbolAddress, taken once per device at
+// vocoder_create with that device current.
+constexpr size_t kScratchBytes = VOC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 struct SnakeDev {
   float* alpha = nullptr;   // alpha / pi per channel
@@ -127,6 +140,11 @@ struct voc_ctx {
   int mg = 0;                   // margin frames of the activation planes being decoded
   std::vector<int64_t> meta_dst;  // host copies kept alive for async uploads
   std::vector<int> meta_int;
+  // the no-allocation decode: this device's copy of the scratch array, and
+  // while such a call runs the workspace it substitutes for ws
+  void* scratch = nullptr;
+  void* ws_override = nullptr;
+  size_t ws_override_bytes = 0;
   // cancellation hook (vocoder_set_cancel): polled before a call enqueues
   // work and between groups of cancel_group units
   int64_t frames_cap = 0;        // test switch: a lower row-frame limit (0: none)
@@ -429,7 +447,16 @@ Plan make_enc_plan(const voc_ctx* c, int rows, int T) {
   return p;
 }
 
+// The workspace base: the library-owned allocation, or the scratch array
+// during a no-allocation decode.
+char* ws_base(const voc_ctx* c) { return static_cast<char*>(c->ws_override ? c->ws_override : c->ws); }
+
 voc_status ensure_ws(voc_ctx* c, size_t bytes) {
+  if (c->ws_override) {  // never allocates: the caller has sized the rows to fit
+    if (bytes <= c->ws_override_bytes) return VOC_OK;
+    return fail(c, VOC_INVALID_PARAMS, "workspace of " + std::to_string(bytes) +
+                                           " bytes exceeds the no-allocation scratch");
+  }
   if (bytes <= c->ws_bytes) return VOC_OK;
   if (c->ws_cap && bytes > c->ws_cap)
     return fail(c, VOC_OOM, "workspace of " + std::to_string(bytes) +
@@ -460,7 +487,7 @@ struct Bufs {
 };
 
 Bufs bufs(voc_ctx* c, const Plan& p) {
-  char* b = static_cast<char*>(c->ws);
+  char* b = ws_base(c);
   Bufs r{};
   // Activation pointers address frame 0 of the first plane; with a margin
   // every plane starts mg frames (64-byte rows) earlier.
@@ -491,7 +518,7 @@ voc_status upload_rows(voc_ctx* c, const Plan& p, std::vector<int64_t>&& dst_in,
   c->meta_int = std::move(ints_in);
   const std::vector<int64_t>& dst = c->meta_dst;
   const std::vector<int>& ints = c->meta_int;
-  char* m = static_cast<char*>(c->ws) + p.off_meta;
+  char* m = ws_base(c) + p.off_meta;
   hipError_t e = hipMemcpyAsync(m, dst.data(), dst.size() * sizeof(int64_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(m + sizeof(int64_t) * p.rows, ints.data(), ints.size() * sizeof(int),
@@ -1227,8 +1254,24 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   if (hip_device < 0 || hip_device >= ndev) return fail(nullptr, VOC_INVALID_PARAMS, "bad device index");
   e = hipSetDevice(hip_device);
   if (e != hipSuccess) return fail(nullptr, VOC_DEVICE_ERROR, "hipSetDevice failed");
+  // This device's copy of the no-allocation scratch array: its address is
+  // taken once per device, with the device current, and kept.
+  void* scratch_ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (hip_device < kMaxDevices && !g_scratch_ptr[hip_device]) {
+      e = hipGetSymbolAddress(&g_scratch_ptr[hip_device], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        g_scratch_ptr[hip_device] = nullptr;
+        return fail(nullptr, VOC_DEVICE_ERROR,
+                    std::string("hipGetSymbolAddress of the scratch array: ") + hipGetErrorString(e));
+      }
+    }
+    if (hip_device < kMaxDevices) scratch_ptr = g_scratch_ptr[hip_device];
+  }
   voc_ctx* c = new (std::nothrow) voc_ctx();
   if (!c) return fail(nullptr, VOC_OOM, "host allocation failed");
+  c->scratch = scratch_ptr;
   c->cfg = *cfg;
   c->device = hip_device;
   c->op = cfg->dtype == VOC_F32 ? OP_F32 : OP_BF16;
@@ -1540,10 +1583,15 @@ voc_status decode_batch(voc_ctx* c, const float* latent, int64_t T_src, int64_t 
   const Plan p = make_plan(c, static_cast<int>(rows), T_alloc);
   voc_status st = ensure_ws(c, p.bytes);
   if (st) return st;
-  if (c->rows_key != key) {
+  if (c->ws_override || c->rows_key != key) {
+    // The scratch is shared by every context on the device: its metadata
+    // is uploaded by every call and never cached.
     st = upload_rows(c, p, std::move(dst), std::move(ints), s);
     if (st) return st;
-    c->rows_key = std::move(key);
+    if (c->ws_override)
+      c->rows_key.clear();
+    else
+      c->rows_key = std::move(key);
   }
   const Bufs Bf = bufs(c, p);
   st = run_import(c, latent, T_src, g.latent_channels, Bf.rows, static_cast<int>(rows), T_alloc, Bf.xlat,
@@ -1614,35 +1662,30 @@ bool windows_valid(int64_t n, int64_t L, int64_t L_last, int64_t cl, int64_t cr)
 }
 }  // namespace
 
-VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, int64_t T, float* pcm,
-                                  void* stream) {
-  if (!c) return VOC_INVALID_PARAMS;
+namespace {
+// Argument checks shared by vocoder_decode and vocoder_decode_noalloc.
+voc_status check_decode_args(voc_ctx* c, const float* latent, int64_t B, int64_t T, const float* pcm) {
   if (!latent || !pcm) return fail(c, VOC_INVALID_PARAMS, "NULL latent or pcm");
   if ((reinterpret_cast<uintptr_t>(latent) | reinterpret_cast<uintptr_t>(pcm)) & 15)
     return fail(c, VOC_INVALID_PARAMS, "latent and pcm must be 16-byte aligned");
   if (B <= 0 || T <= 0) return fail(c, VOC_INVALID_PARAMS, "B and T must be positive");
   if (T * c->hop > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "T*hop exceeds 2^31-1");
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  return VOC_OK;
+}
+
+// The rows of a decode of B rows of T latent frames: whole rows (tiled ==
+// false, F == T), or tiles of F latent frames with the exact halos, b-major.
+// Fills the row metadata (dst, ints = len | src_b | start | keep_lo |
+// keep_hi) and the frames each row allocates.
+voc_status decode_row_plan(voc_ctx* c, int64_t B, int64_t T, int64_t F, bool tiled, int64_t* rows_out,
+                           int* T_alloc_out, std::vector<int64_t>* dst_out, std::vector<int>* ints_out) {
   const voc_config& g = c->cfg;
-  // Rows: whole rows, or tiles of tile_frames latent frames with halos.
-  // Untiled rows beyond what the GEMMs can address are tiled here, with
-  // the largest tile whose halos still fit (the same samples, bit for bit).
-  const int64_t max_frames = row_frames_limit(c);
-  int64_t F = g.tile_frames > 0 ? g.tile_frames : T;
-  bool tiled = g.tile_frames > 0;
-  if (!tiled && T > max_frames) {
-    F = max_frames - c->halo_l - c->halo_r;
-    tiled = true;
-  }
-  if (tiled && F + c->halo_l + c->halo_r > max_frames)
-    return fail(c, VOC_INVALID_PARAMS, "tile_frames plus the halos exceed the frames the GEMMs can address "
-                                       "(voc_config_max_frames)");
   const int64_t ntile = (T + F - 1) / F;
   const int64_t rows = B * ntile;
   if (rows > 65535) return fail(c, VOC_INVALID_PARAMS, "too many rows (B * tiles > 65535)");
   const int HL = tiled ? c->halo_l : 0;
   const int HR = tiled ? c->halo_r : 0;
-  const int T_alloc = static_cast<int>(std::min<int64_t>(T, F + HL + HR));
   std::vector<int64_t> dst(rows);
   std::vector<int> ints(5 * rows);
   for (int64_t b = 0; b < B; ++b)
@@ -1657,9 +1700,111 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
       ints[4 * rows + r] = static_cast<int>((t1 - a) * c->hop);   // keep_hi
       dst[r] = (b * g.out_channels * T + t0) * c->hop;
     }
+  *rows_out = rows;
+  *T_alloc_out = static_cast<int>(std::min<int64_t>(T, F + HL + HR));
+  *dst_out = std::move(dst);
+  *ints_out = std::move(ints);
+  return VOC_OK;
+}
+
+// Tile frames of a decode: the configured tile_frames, else whole rows when
+// the GEMMs can address them, else the largest tile whose halos still fit.
+voc_status decode_tiles(voc_ctx* c, int64_t T, int64_t* F_out, bool* tiled_out) {
+  const voc_config& g = c->cfg;
+  const int64_t max_frames = row_frames_limit(c);
+  int64_t F = g.tile_frames > 0 ? g.tile_frames : T;
+  bool tiled = g.tile_frames > 0;
+  if (!tiled && T > max_frames) {
+    F = max_frames - c->halo_l - c->halo_r;
+    tiled = true;
+  }
+  if (tiled && F + c->halo_l + c->halo_r > max_frames)
+    return fail(c, VOC_INVALID_PARAMS, "tile_frames plus the halos exceed the frames the GEMMs can address "
+                                       "(voc_config_max_frames)");
+  *F_out = F;
+  *tiled_out = tiled;
+  return VOC_OK;
+}
+}  // namespace
+
+VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, int64_t T, float* pcm,
+                                  void* stream) {
+  if (!c) return VOC_INVALID_PARAMS;
+  voc_status st = check_decode_args(c, latent, B, T, pcm);
+  if (st) return st;
+  // Rows: whole rows, or tiles of tile_frames latent frames with halos.
+  // Untiled rows beyond what the GEMMs can address are tiled here, with
+  // the largest tile whose halos still fit (the same samples, bit for bit).
+  int64_t F = 0, rows = 0;
+  bool tiled = false;
+  st = decode_tiles(c, T, &F, &tiled);
+  if (st) return st;
+  int T_alloc = 0;
+  std::vector<int64_t> dst;
+  std::vector<int> ints;
+  st = decode_row_plan(c, B, T, F, tiled, &rows, &T_alloc, &dst, &ints);
+  if (st) return st;
   const int64_t group = c->cancel_fn ? c->cancel_group : rows;
   return decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {0, B, T, rows}, pcm,
                      T * c->hop, static_cast<hipStream_t>(stream), group);
+}
+
+VOC_API voc_status vocoder_decode_noalloc(voc_ctx* c, const float* latent, int64_t B, int64_t T, float* pcm,
+                                          void* stream) {
+  if (!c) return VOC_INVALID_PARAMS;
+  voc_status st = check_decode_args(c, latent, B, T, pcm);
+  if (st) return st;
+  if (!c->scratch) return fail(c, VOC_DEVICE_ERROR, "no scratch array on this device");
+  int64_t F = 0;
+  bool tiled = false;
+  st = decode_tiles(c, T, &F, &tiled);
+  if (st) return st;
+  // One row must fit the scratch: shrink the tile (tiles with exact halos
+  // decode the same samples bit for bit) until it does.
+  auto row_bytes = [&](int64_t f, bool t) {
+    const int64_t ta = std::min<int64_t>(T, f + (t ? c->halo_l + c->halo_r : 0));
+    return make_plan(c, 1, static_cast<int>(ta)).bytes;
+  };
+  if (row_bytes(F, tiled) > kScratchBytes) {
+    if (row_bytes(1, true) > kScratchBytes)
+      return fail(c, VOC_INVALID_PARAMS,
+                  "one latent frame with its halos needs " + std::to_string(row_bytes(1, true)) +
+                      " bytes of workspace, more than the " + std::to_string(kScratchBytes) +
+                      "-byte no-allocation scratch");
+    int64_t lo = 1, hi = F;  // row_bytes(lo) fits, row_bytes(hi) does not
+    while (hi - lo > 1) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      (row_bytes(mid, true) <= kScratchBytes ? lo : hi) = mid;
+    }
+    F = lo;
+    tiled = true;
+  }
+  int64_t rows = 0;
+  int T_alloc = 0;
+  std::vector<int64_t> dst;
+  std::vector<int> ints;
+  st = decode_row_plan(c, B, T, F, tiled, &rows, &T_alloc, &dst, &ints);
+  if (st) return st;
+  // Rows per pass: as many as the scratch holds (passes run in stream order
+  // on the same scratch).
+  int64_t lo = 1, hi = rows + 1;  // lo rows fit, hi rows do not (or exceed the count)
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    (make_plan(c, static_cast<int>(mid), T_alloc).bytes <= kScratchBytes ? lo : hi) = mid;
+  }
+  int64_t group = lo;
+  if (c->cancel_fn) group = std::min(group, c->cancel_group);
+  // No profiling events here (creating one may allocate).
+  const bool prof = c->prof;
+  c->prof = false;
+  c->ws_override = c->scratch;
+  c->ws_override_bytes = kScratchBytes;
+  st = decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {5, B, T, rows}, pcm,
+                   T * c->hop, static_cast<hipStream_t>(stream), group);
+  c->ws_override = nullptr;
+  c->ws_override_bytes = 0;
+  c->prof = prof;
+  return st;
 }
 
 VOC_API voc_status vocoder_encode(voc_ctx* c, const float* audio, int64_t B, int64_t T, float* latent,

@@ -112,6 +112,7 @@ def lib():
             "vocoder_load_weights": (I, [P, ctypes.POINTER(voc_tensor), I]),
             "vocoder_output_length": (I64, [P, I64]),
             "vocoder_decode": (I, [P, P, I64, I64, P, P]),
+            "vocoder_decode_noalloc": (I, [P, P, I64, I64, P, P]),
             "vocoder_decode_windows": (I, [P, P, I64, I64, I64, I64, I64, I64, P, P]),
             "vocoder_windows_output_length": (I64, [P, I64, I64, I64, I64, I64]),
             "vocoder_stream_reset": (I, [P, I64]),
@@ -256,6 +257,10 @@ def vocoder_output_length(ctx, T: int) -> int:
 
 def vocoder_decode(ctx, latent, B: int, T: int, pcm, stream=None) -> int:
     return lib().vocoder_decode(ctx, _ptr(latent), B, T, _ptr(pcm), _stream(stream))
+
+
+def vocoder_decode_noalloc(ctx, latent, B: int, T: int, pcm, stream=None) -> int:
+    return lib().vocoder_decode_noalloc(ctx, _ptr(latent), B, T, _ptr(pcm), _stream(stream))
 
 
 def vocoder_decode_windows(ctx, latents, n: int, sides: int, L: int, L_last: int,

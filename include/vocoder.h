@@ -64,6 +64,9 @@ extern "C" {
 #define VOC_ABI_VERSION 3
 #define VOC_MAX_BLOCKS 8
 #define VOC_MAX_RES 4
+/* Bytes of the device array vocoder_decode_noalloc uses as its workspace
+ * (one copy per GPU the library runs on, held until the process ends). */
+#define VOC_NOALLOC_SCRATCH_BYTES 268435456
 
 typedef struct voc_ctx voc_ctx;
 
@@ -230,6 +233,28 @@ int64_t vocoder_output_length(const voc_ctx *ctx, int64_t T);
  */
 voc_status vocoder_decode(voc_ctx *ctx, const float *latent, int64_t B, int64_t T,
                           float *pcm, void *hip_stream);
+
+/*
+ * vocoder_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, checks and output, bit for bit, but no hipMalloc,
+ * hipFree or other allocating call.  The workspace is a fixed device array
+ * of VOC_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU inside the library: rows
+ * (time tiles with exact halos when one whole row does not fit, the same
+ * samples bit for bit) are decoded in passes of as many rows as it holds,
+ * in stream order.  Nothing in it needs clearing between calls: every
+ * kernel reads only what the same call has written (the convolutions' zero
+ * padding comes from bounds, not memory).  Every context and stream on one
+ * GPU shares that GPU's array, so calls that overlap on one GPU (different
+ * streams, or host threads) race and must be serialized by the caller.  The
+ * row metadata is copied from host memory with hipMemcpyAsync; profiling
+ * events are not recorded.  Same cancel hook behaviour as vocoder_decode.
+ * Errors: those of vocoder_decode, and VOC_INVALID_PARAMS when one latent
+ * frame with its halos needs more workspace than the array holds (a message
+ * gives the size), VOC_DEVICE_ERROR when the array is unavailable.
+ */
+voc_status vocoder_decode_noalloc(voc_ctx *ctx, const float *latent, int64_t B, int64_t T,
+                                  float *pcm, void *hip_stream);
 
 /*
  * Windowed decode with stitching (minimaxmusic.cpp ARCHITECTURE, "Inference
