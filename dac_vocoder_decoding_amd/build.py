@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libvocoder.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["conv_gemm.hip", "fused_ru.hip", "stream_kernels.hip", "peak_kernels.hip", "runtime.hip"]
+SOURCES = ["conv_gemm.hip", "fused_ru.hip", "stream_kernels.hip", "peak_kernels.hip", "runtime.hip",
+           "host_config.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -18,12 +18,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "host_config.h"  // kChunkBytes, kHChunk, OpType, kAfTaps, res_unit_tile
+
 namespace voc {
-
-constexpr int kChunkBytes = 64;
-constexpr int kHChunk = 16;  // fp32 residual stream channels per chunk
-
-enum OpType { OP_F32 = 0, OP_BF16 = 1 };
 
 inline int op_chunk(int op) { return op == OP_F32 ? 16 : 32; }
 inline int op_size(int op) { return op == OP_F32 ? 4 : 2; }
@@ -123,10 +120,9 @@ struct ResUnitArgs {
   int lb;                // frames in [-lb, 0) of the input are read from memory, else zero
   int n_tiles, rows;
 };
-// Frames per workgroup of the fused kernel for width C, or 0 if there is no
-// fused instance for (op, C).
+// res_unit_tile(op, C, big) (host_config.h): frames per workgroup of the
+// fused kernel for width C, or 0 if there is no fused instance for (op, C);
 // big selects the large-frame tile of that width (0 if it has none).
-int res_unit_tile(int op, int C, bool big);
 // Whether units of width C run with x_from_h (Snake1 computed in the kernel).
 bool res_unit_from_h_ok(int op, int C);
 hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s);
@@ -216,7 +212,6 @@ hipError_t launch_mfma32_loop(int op, int64_t iters, float* out, hipStream_t s);
 // written for t < len to out in the out_op layout (fp32 16-channel chunks,
 // or bf16 32-channel chunks).  fe[k] = 2 f[11 - 2k], fo[k] = 2 f[10 - 2k],
 // fd = f (the 12-tap low-pass).
-constexpr int kAfTaps = 12;
 struct AfArgs {
   const float* x;
   void* out;

@@ -65,8 +65,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIBS = {"f64": os.path.join(_HERE, "liboracle_f64.so"),
-         "f32": os.path.join(_HERE, "liboracle_f32.so")}
+# VOC_ORACLE_LIBDIR names a directory holding other builds of oracle.c under
+# the same file names (the sanitizer test builds them with ASan and UBSan);
+# those are loaded as they are, never rebuilt.
+_LIBDIR = os.environ.get("VOC_ORACLE_LIBDIR")
+_LIBS = {"f64": os.path.join(_LIBDIR or _HERE, "liboracle_f64.so"),
+         "f32": os.path.join(_LIBDIR or _HERE, "liboracle_f32.so")}
 _DEFS = {"f64": ["-DREAL=double"], "f32": ["-DREAL=float", "-DORACLE_FLOAT"]}
 _NP = {"f64": np.float64, "f32": np.float32}
 _loaded = {}
@@ -96,17 +100,18 @@ def load_library(path: str, prec: str):
     return lib
 
 
-def compile_library(src: str, out: str, prec: str = "f64") -> None:
-    """Compile a C source with the oracle's flags (used for both builds)."""
+def compile_library(src: str, out: str, prec: str = "f64", extra=()) -> None:
+    """Compile a C source with the oracle's flags (used for both builds);
+    `extra` adds flags (e.g. the sanitizers)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           "-fno-fast-math", "-ffp-contract=off", *_DEFS[prec], src, "-o", out, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", *_DEFS[prec], *extra, src, "-o", out, "-lm"]
     subprocess.check_call(cmd)
 
 
 def _lib(prec: str):
     if prec not in _loaded:
         path = _LIBS[prec]
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        if not _LIBDIR and (not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC)):
             build_library()
         _loaded[prec] = load_library(path, prec)
     return _loaded[prec]
