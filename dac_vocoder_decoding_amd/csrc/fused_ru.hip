@@ -205,6 +205,8 @@ void res_unit_kernel(const ResUnitArgs a) {
       if constexpr (XH) {
         // Snake1 in fp32, then the operand dtype; frames outside [-lb, Lv)
         // are the convolution's zero padding.
+        // (The padding is applied to the packed operand bits: one select per
+        // 32-bit word.)
         const int t = tfirst + r;
         const bool in = t >= -a.lb && t < Lv;
         float y[4 * HV];
@@ -213,7 +215,7 @@ void res_unit_kernel(const ResUnitArgs a) {
           const f4 ps = *reinterpret_cast<const f4*>(P1 + xch + 4 * q);
           const f4 ph = *reinterpret_cast<const f4*>(P1 + C + xch + 4 * q);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[4 * q + e] = in ? snake_f32(xh[u][q][e], ps[e], ph[e]) : 0.f;
+          for (int e = 0; e < 4; ++e) y[4 * q + e] = snake_f32(xh[u][q][e], ps[e], ph[e]);
         }
         if constexpr (OP == OP_BF16) {
           v.x = pack_bf16x2(y[0], y[1]);
@@ -224,6 +226,7 @@ void res_unit_kernel(const ResUnitArgs a) {
           v = make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
                          __float_as_uint(y[3]));
         }
+        if (!in) v = make_uint4(0u, 0u, 0u, 0u);
       } else {
         v = xr[u];
       }
