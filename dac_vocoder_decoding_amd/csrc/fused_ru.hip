@@ -469,7 +469,7 @@ void res_unit_kernel(const ResUnitArgs a) {
 #define VOC_BF_RU128 4, 4, 2, 4, 4
 #endif
 #ifndef VOC_BF_RU192
-#define VOC_BF_RU192 3, 4, 4, 2, 2
+#define VOC_BF_RU192 3, 4, 4, 2, 4
 #endif
 #define VOC_RU_(...) VOC_RU(__VA_ARGS__)
 template <int OP>

@@ -288,25 +288,38 @@ __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   for (int oc = 0; oc < NOUT; ++oc)
 #pragma unroll
     for (int j = 0; j < 7; ++j) z[oc][j] = 0.f;
-  for (int k = 0; k < C / 16; ++k) {
-    f4 x[4];
+  // Chunks are read four at a time (256 bytes per lane in flight): 3 %
+  // faster than one at a time on the batched bf16 windows (4.7 against 4.55
+  // TB/s).  Non-temporal loads were 1.7x slower: each lane reads a 64-byte
+  // row as four 16-byte pieces, which then reach HBM unmerged.
+  constexpr int U = 4;
+  const int nk = C / 16;
+  for (int k0 = 0; k0 < nk; k0 += U) {
+    f4 x[U][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      x[q] = valid ? *reinterpret_cast<const f4*>(hp + k * plane + q * 4) : f4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int oc = 0; oc < NOUT; ++oc)
+      for (int q = 0; q < 4; ++q)
+        x[u][q] = valid && k0 + u < nk ? *reinterpret_cast<const f4*>(hp + (k0 + u) * plane + q * 4)
+                                       : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 7; ++j) {
-        const float* wj = a.w + (oc * 7 + j) * C + k * 16;
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u >= nk) break;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f4 w = *reinterpret_cast<const f4*>(wj + q * 4);
-          z[oc][j] = fmaf(w[0], x[q][0], z[oc][j]);
-          z[oc][j] = fmaf(w[1], x[q][1], z[oc][j]);
-          z[oc][j] = fmaf(w[2], x[q][2], z[oc][j]);
-          z[oc][j] = fmaf(w[3], x[q][3], z[oc][j]);
+      for (int oc = 0; oc < NOUT; ++oc)
+#pragma unroll
+        for (int j = 0; j < 7; ++j) {
+          const float* wj = a.w + (oc * 7 + j) * C + (k0 + u) * 16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f4 w = *reinterpret_cast<const f4*>(wj + q * 4);
+            z[oc][j] = fmaf(w[0], x[u][q][0], z[oc][j]);
+            z[oc][j] = fmaf(w[1], x[u][q][1], z[oc][j]);
+            z[oc][j] = fmaf(w[2], x[u][q][2], z[oc][j]);
+            z[oc][j] = fmaf(w[3], x[u][q][3], z[oc][j]);
+          }
         }
-      }
+    }
   }
   const int o = f;
   const bool store = lane >= P && lane < P + kHeadOut && o < hi;
