@@ -47,6 +47,19 @@ namespace voc {
 #define VOC_RU_MINB4 2
 #endif
 
+// Eight-wave instances (one workgroup per CU) stage stage 1 through two LDS
+// buffers: the next tap group (and channel chunk) is stored while the
+// current one is multiplied, with one barrier per group instead of two.
+#ifndef VOC_RU_DB
+#define VOC_RU_DB 1
+#endif
+// With two buffers, the waves of the workgroup's second half multiply first
+// and stage second, the first half the other way round, so that the two
+// waves a SIMD holds are in opposite halves of each group's work.
+#ifndef VOC_RU_PINGPONG
+#define VOC_RU_PINGPONG 1
+#endif
+
 template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG, bool XH>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N == 4 ? VOC_RU_MINB4 : 1)
 void res_unit_kernel(const ResUnitArgs a) {
@@ -59,7 +72,9 @@ void res_unit_kernel(const ResUnitArgs a) {
   constexpr int NG = (7 + TG - 1) / TG;        // tap groups per channel chunk
   constexpr int WROWS = TG * C;
   constexpr int NCH = C / CH;                  // channel chunks
-  constexpr int S1 = (XROWS + WROWS) * kRowBytes;
+  constexpr bool kDB = VOC_RU_DB && WAVES_M * WAVES_N == 8;
+  constexpr int NB = kDB ? 2 : 1;              // stage-1 LDS buffers
+  constexpr int S1 = NB * (XROWS + WROWS) * kRowBytes;
   constexpr int UB = NCH * BN * kRowBytes;     // U tile: [NCH][BN] rows
   constexpr int S2 = UB + C * kRowBytes;
   constexpr int LDS_T = S1 > S2 ? S1 : S2;
@@ -70,8 +85,9 @@ void res_unit_kernel(const ResUnitArgs a) {
   static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "four or eight waves");
   static_assert(C % CH == 0 && C % 16 == 0, "whole channel chunks");
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
+  // Stage-1 buffers: X tiles [NB][XROWS], then weight groups [NB][WROWS].
   unsigned char* Xs = smem;
-  unsigned char* Ws = smem + XROWS * kRowBytes;
+  unsigned char* Ws = smem + NB * XROWS * kRowBytes;
   unsigned char* Us = smem;          // stage 2 (after stage 1 is done)
   unsigned char* W2s = smem + UB;
 
@@ -195,7 +211,7 @@ void res_unit_kernel(const ResUnitArgs a) {
       wr[u] = v;
     }
   };
-  auto store_x = [&]() {
+  auto store_x = [&](unsigned char* Xs) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
       const int idx = tid + u * NTH;
@@ -233,7 +249,7 @@ void res_unit_kernel(const ResUnitArgs a) {
       *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = v;
     }
   };
-  auto store_w = [&]() {
+  auto store_w = [&](unsigned char* Ws) {
 #pragma unroll
     for (int u = 0; u < WU; ++u) {
       const int idx = tid + u * NTH;
@@ -242,29 +258,74 @@ void res_unit_kernel(const ResUnitArgs a) {
     }
   };
 
+  // Matrix steps of tap group g from the X tile at xs and the weights at ws.
+  auto mma_group = [&](int g, const unsigned char* xs, const unsigned char* ws) {
+    const int nt = (g + 1) * TG <= 7 ? TG : 7 - g * TG;  // taps in this group
+    const unsigned char* wt = ws + (wm * WMB * 16) * kRowBytes + lane * 16;
+    const int xr0 = g * TG * d + wn * WNB * 16 + lr;
+    mma_steps<OP, WMB, WNB, TG, false>(
+        acc, nt, [&](int jj, int mb) { return wt + (jj * C + mb * 16) * kRowBytes; },
+        [&](int jj, int nb) { return xs + lds_off(xr0 + jj * d, lg) + nb * 1024; });
+  };
   load_x(0);
   load_w(0, 0);
-  for (int c = 0; c < NCH; ++c) {
+  if constexpr (kDB) {
+    // Group p = c * NG + g uses X buffer c & 1 and weight buffer p & 1.  In
+    // group p the waves store group p + 1 (loaded during group p - 1) into
+    // the other buffers, request group p + 2, and multiply group p; the
+    // barrier at its end makes group p + 1 visible and frees group p's
+    // buffers for group p + 2.
+    store_x(Xs);
+    store_w(Ws);
+    if (NG > 1) {
+      load_w(0, 1);
+    } else if (NCH > 1) {
+      load_x(1);
+      load_w(1, 0);
+    }
+    __syncthreads();
+    for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (g == 0) store_x();
-      store_w();
-      __syncthreads();
-      if (g + 1 < NG) {
-        load_w(c, g + 1);
-      } else if (c + 1 < NCH) {
-        load_x(c + 1);
-        load_w(c + 1, 0);
+      for (int g = 0; g < NG; ++g) {
+        const int p = c * NG + g;
+        const int c1 = g + 1 < NG ? c : c + 1, g1 = g + 1 < NG ? g + 1 : 0;
+        auto stage_next = [&]() {
+          if (c1 < NCH) {
+            if (g1 == 0) store_x(Xs + (c1 & 1) * XROWS * kRowBytes);
+            store_w(Ws + ((p + 1) & 1) * WROWS * kRowBytes);
+            const int c2 = g1 + 1 < NG ? c1 : c1 + 1, g2 = g1 + 1 < NG ? g1 + 1 : 0;
+            if (c2 < NCH) {
+              if (g2 == 0) load_x(c2);
+              load_w(c2, g2);
+            }
+          }
+        };
+        if (VOC_RU_PINGPONG && wave >= WAVES_M * WAVES_N / 2) {
+          mma_group(g, Xs + (c & 1) * XROWS * kRowBytes, Ws + (p & 1) * WROWS * kRowBytes);
+          stage_next();
+        } else {
+          stage_next();
+          mma_group(g, Xs + (c & 1) * XROWS * kRowBytes, Ws + (p & 1) * WROWS * kRowBytes);
+        }
+        __syncthreads();
       }
-      {
-        const int nt = (g + 1) * TG <= 7 ? TG : 7 - g * TG;  // taps in this group
-        const unsigned char* wt = Ws + (wm * WMB * 16) * kRowBytes + lane * 16;
-        const int xr0 = g * TG * d + wn * WNB * 16 + lr;
-        mma_steps<OP, WMB, WNB, TG, false>(
-            acc, nt, [&](int jj, int mb) { return wt + (jj * C + mb * 16) * kRowBytes; },
-            [&](int jj, int nb) { return Xs + lds_off(xr0 + jj * d, lg) + nb * 1024; });
+    }
+  } else {
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g == 0) store_x(Xs);
+        store_w(Ws);
+        __syncthreads();
+        if (g + 1 < NG) {
+          load_w(c, g + 1);
+        } else if (c + 1 < NCH) {
+          load_x(c + 1);
+          load_w(c + 1, 0);
+        }
+        mma_group(g, Xs, Ws);
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
 

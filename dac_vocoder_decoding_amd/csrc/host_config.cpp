@@ -28,7 +28,8 @@ voc_status validate(const voc_config* c, std::string* why) {
   if (c->act != VOC_SNAKE && c->act != VOC_SNAKE_BETA) return bad("unknown act");
   if (c->dtype != VOC_F32 && c->dtype != VOC_BF16) return bad("unknown dtype");
   if (c->snake_log_params != 0 && c->snake_log_params != 1) return bad("snake_log_params must be 0 or 1");
-  if (c->convt_crop != 0) return bad("convt_crop must be 0");
+  if (c->convt_crop != 0 && !(c->convt_crop == 1 && c->causal == 1))
+    return bad("convt_crop must be 0, or 1 together with causal = 1");
   if (c->tile_frames < 0) return bad("tile_frames must be >= 0");
   const int q = c->dtype == VOC_F32 ? 16 : 32;
   if (c->latent_channels <= 0 || c->latent_channels % q || c->latent_channels > 8192)

@@ -95,7 +95,8 @@ typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
  * 1 <= n_res <= VOC_MAX_RES; 1 <= dilation[r] <= 9; stride[b] >= 1;
  * in_kernel == res_kernel == out_kernel == 7; widths, latent_channels and a
  * non-zero in_proj positive multiples of 16 (F32) or 32 (BF16), at most 8192,
- * width[n_blocks] <= 512; convt_crop == 0; tile_frames >= 0; in_proj >= 0;
+ * width[n_blocks] <= 512; convt_crop == 0, or 1 with causal == 1;
+ * tile_frames >= 0; in_proj >= 0;
  * causal is 0 or 1; an encoder (enc_width[0] > 0) needs every enc_width[b]
  * (b <= n_blocks) a positive multiple of 16 (F32) or 32 (BF16), at most
  * 8192, even strides and causal == 0; af_snake is 0 or 1, and 1 needs
@@ -115,8 +116,12 @@ typedef struct voc_config {
   int dtype;                       /* voc_dtype                                 */
   int snake_log_params;            /* 0: alpha/beta used as given; 1: the       */
                                    /* stored values are logs, exp() at load     */
-  int convt_crop;                  /* 0: keep full[n + ceil(s/2)], n < T*s      */
-                                   /* (other values reserved)                   */
+  int convt_crop;                  /* 0: the crop that goes with `causal`:      */
+                                   /* keep full[n + ceil(s/2)], n < T*s, or     */
+                                   /* full[0, T*s) for a causal decoder; 1: the */
+                                   /* causal crop, named explicitly (accepted   */
+                                   /* with causal = 1 only: the pages pair the  */
+                                   /* causal crop with causal convs)            */
   int tile_frames;                 /* 0: decode whole rows; F > 0: decode time  */
                                    /* tiles of F latent frames with exact halos */
   int in_proj;                     /* 0: none; P > 0: dec_in_proj, a Conv1d k=1 */

@@ -83,6 +83,7 @@ def _bad(**kw):
     dict(width=(2, 100)), dict(width=(4, 1024)), dict(stride=(0, 0)), dict(dilation=(1, 10)),
     dict(snake_log_params=2), dict(in_proj=-16), dict(in_proj=24), dict(in_proj=8208),
     dict(causal=2), dict(causal=-1), dict(af_snake=2), dict(out_channels=0), dict(out_channels=3),
+    dict(convt_crop=2, causal=1), dict(convt_crop=-1),
     dict(af_snake=1, causal=1), dict(af_snake=1, enc_width=(0, 64)),
 ])
 def test_invalid_configs_rejected_before_any_device_call(kw):
@@ -91,6 +92,19 @@ def test_invalid_configs_rejected_before_any_device_call(kw):
     st, ctx = V.vocoder_create(c, 0)
     assert st == V.VOC_INVALID_PARAMS and not ctx.value
     assert V.vocoder_last_error(None)
+
+
+def test_causal_crop_named_explicitly():
+    """convt_crop = 1 names the causal ConvTranspose1d crop; it is the crop a
+    causal decoder takes anyway, so it validates exactly with causal = 1."""
+    d = dict(I.CONFIGS[7])
+    c = V.config_from_dict(d)
+    assert c.causal == 1 and c.convt_crop == 0
+    assert V.voc_config_validate(c) == V.VOC_OK
+    c.convt_crop = 1
+    assert V.voc_config_validate(c) == V.VOC_OK
+    assert V.voc_config_hop(c) == V.voc_config_hop(V.config_from_dict(d))
+    assert V.voc_config_halo(c) == V.voc_config_halo(V.config_from_dict(d))
 
 
 def test_bf16_width_granularity():
