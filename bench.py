@@ -37,8 +37,8 @@ METRIC = "audio-seconds decoded/sec (44.1 kHz stereo) + TFLOP/s as % of MFMA pea
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 KIND_NAMES = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused",
-              "in_proj", "enc_down", "enc_out", "af_snake", "snake", "col2im"]
-HBM_KINDS = ("head", "af_snake", "snake", "col2im")   # stream / stencil kernels: priced against HBM bandwidth
+              "in_proj", "enc_down", "enc_out", "af_snake", "snake", "col2im", "tanh"]
+HBM_KINDS = ("head", "af_snake", "snake", "col2im", "tanh")   # stream / stencil kernels: priced against HBM bandwidth
 KERNEL_SOURCES = ["dac_vocoder_decoding_amd/csrc/conv_gemm.hip",
                   "dac_vocoder_decoding_amd/csrc/fused_ru.hip",
                   "dac_vocoder_decoding_amd/csrc/stream_kernels.hip",

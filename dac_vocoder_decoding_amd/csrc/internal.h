@@ -187,8 +187,12 @@ struct HeadArgs {
   const float* w;   // [nout][7][C]
   float bias[2];
   float* pcm;
+  int no_tanh;      // 1: store the pre-tanh sum (the split tanh ablation)
 };
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
+
+// x[i] = tanh(x[i]) for i < n, in place (x 16-byte aligned).
+hipError_t launch_tanh(float* x, int64_t n, hipStream_t s);
 
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
 

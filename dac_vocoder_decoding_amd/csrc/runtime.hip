@@ -113,11 +113,13 @@ struct voc_ctx {
   voc_profile_stat stats[VOC_K_COUNT]{};
   // cached row metadata of the last decode
   std::vector<int64_t> rows_key;  // what the uploaded metadata describes (empty: nothing)
-  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
+  int force_variant[VOC_K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};  // ablation overrides
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
   bool split_snake = false;             // ablation: every plain Snake as a launch of its own
+  bool split_tanh = false;              // ablation: tanh as a pass of its own after the head
+  bool head_no_tanh = false;            // set during a split-tanh decode
   bool col2im = false;                  // ablation: ConvTranspose1d as GEMM + col2im
   float* col_buf = nullptr;             // its column matrix (and a zero bias), grown on demand
   size_t col_bytes = 0;
@@ -618,6 +620,7 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
   a.bias[0] = c->W.head_bias[0];
   a.bias[1] = c->W.head_bias[1];
   a.pcm = pcm;
+  a.no_tanh = c->head_no_tanh ? 1 : 0;
   // The kernel reads and writes only the kept samples of each row (their
   // count is in the row metadata last uploaded for these rows).
   double frames = static_cast<double>(nrows) * T;
@@ -986,6 +989,10 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   // Ablation only: 1 runs every ConvTranspose1d as a GEMM into a column
   // matrix followed by a col2im overlap-add (the pages' lowering).
   if (const char* v = std::getenv("VOC_CONVT_COL2IM")) c->col2im = std::atoi(v) != 0 && !cfg->causal;
+  // Ablation only: 1 makes vocoder_decode's head store the pre-tanh sums and
+  // applies tanh in a pass of its own over the pcm (untiled decodes without a
+  // cancel hook; otherwise the head applies it as usual).
+  if (const char* v = std::getenv("VOC_SPLIT_TANH")) c->split_tanh = std::atoi(v) != 0;
   *out = c;
   return VOC_OK;
 }
@@ -1412,8 +1419,15 @@ VOC_API voc_status vocoder_decode(voc_ctx* c, const float* latent, int64_t B, in
   st = decode_row_plan(c, B, T, F, tiled, &rows, &T_alloc, &dst, &ints);
   if (st) return st;
   const int64_t group = c->cancel_fn ? c->cancel_group : rows;
-  return decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {0, B, T, rows}, pcm,
-                     T * c->hop, static_cast<hipStream_t>(stream), group);
+  const bool split_tanh = c->split_tanh && !tiled && !c->cancel_fn;
+  c->head_no_tanh = split_tanh;
+  st = decode_rows(c, latent, T, rows, T_alloc, std::move(dst), std::move(ints), {0, B, T, rows}, pcm,
+                   T * c->hop, static_cast<hipStream_t>(stream), group);
+  c->head_no_tanh = false;
+  if (st || !split_tanh) return st;
+  const int64_t n = B * c->cfg.out_channels * T * c->hop;
+  return launch(c, static_cast<hipStream_t>(stream), VOC_K_TANH, 0.0, 8.0 * static_cast<double>(n),
+                "tanh launch", [&] { return launch_tanh(pcm, n, static_cast<hipStream_t>(stream)); });
 }
 
 VOC_API voc_status vocoder_decode_noalloc(voc_ctx* c, const float* latent, int64_t B, int64_t T, float* pcm,

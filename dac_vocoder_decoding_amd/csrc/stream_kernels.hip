@@ -11,6 +11,7 @@
 //   col2im_kernel        overlap-add of a GEMM + col2im ConvTranspose1d (ablation)
 //   head_kernel          Snake -> Conv1d k=7 to one or two channels -> bias ->
 //                        tanh, with the tile / window crop folded into the store
+//   tanh_kernel          standalone in-place tanh (the split tanh ablation)
 //   copy_kernel          plain 16-byte vector copy (byte-counter calibration)
 #include "internal.h"
 #include "device_math.h"
@@ -331,8 +332,36 @@ __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
       const int src = min(max(lane + j - P, 0), 63);
       y += __shfl(z[oc][j], src);
     }
-    if (store) a.pcm[a.rows.dst[r] + oc * a.ch_stride - lo + o] = tanhf(y);
+    if (store) a.pcm[a.rows.dst[r] + oc * a.ch_stride - lo + o] = a.no_tanh ? y : tanhf(y);
   }
+}
+
+// ------------------------------------------------------------------ tanh
+// The decoder's last step, tanh after conv_out (minimaxmusic.cpp
+// ARCHITECTURE, "Flow VAE"), as a pass of its own over the stored pcm: the
+// split tanh ablation, which measures what folding it into the head saves.
+// Four consecutive samples per thread, 16-byte loads and stores, the ragged
+// end element by element; the same tanhf of the same fp32 sums as the head.
+__global__ __launch_bounds__(256) void tanh_kernel(float* x, int64_t n) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    f4 v = *reinterpret_cast<const f4*>(x + i);
+    v[0] = tanhf(v[0]);
+    v[1] = tanhf(v[1]);
+    v[2] = tanhf(v[2]);
+    v[3] = tanhf(v[3]);
+    *reinterpret_cast<f4*>(x + i) = v;
+  } else {
+    for (int64_t j = i; j < n; ++j) x[j] = tanhf(x[j]);
+  }
+}
+
+hipError_t launch_tanh(float* x, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 1023) / 1024;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tanh_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, x, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {

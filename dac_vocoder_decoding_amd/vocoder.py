@@ -33,7 +33,7 @@ VOC_F32, VOC_BF16 = 0, 1
 VOC_SNAKE, VOC_SNAKE_BETA = 0, 1
 
 KERNEL_KINDS = ["conv_in", "convt", "res_k7", "res_k1", "head", "import", "export", "res_fused",
-                "in_proj", "enc_down", "enc_out", "af_snake", "snake", "col2im"]
+                "in_proj", "enc_down", "enc_out", "af_snake", "snake", "col2im", "tanh"]
 
 
 class voc_config(ctypes.Structure):

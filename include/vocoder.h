@@ -384,7 +384,7 @@ typedef enum voc_kernel_kind {
   VOC_K_CONVT = 1,    /* polyphase ConvTranspose1d GEMM                 */
   VOC_K_RES_K7 = 2,   /* residual unit conv1 (k=7, dilated) GEMM        */
   VOC_K_RES_K1 = 3,   /* residual unit conv2 (k=1) GEMM + residual add  */
-  VOC_K_HEAD = 4,     /* Snake + Conv1d to one channel + tanh           */
+  VOC_K_HEAD = 4,     /* Snake + Conv1d to one or two channels + tanh   */
   VOC_K_IMPORT = 5,   /* latent transpose / tile gather                 */
   VOC_K_EXPORT = 6,   /* debug-stage output transpose                   */
   VOC_K_RES_FUSED = 7, /* whole residual unit (conv1, Snake2, conv2, add) */
@@ -395,7 +395,9 @@ typedef enum voc_kernel_kind {
   VOC_K_SNAKE = 12,   /* standalone Snake (only in the split ablation)   */
   VOC_K_COL2IM = 13,  /* col2im overlap-add (only in the GEMM + col2im    */
                       /* ablation of the ConvTranspose1d)                 */
-  VOC_K_COUNT = 14
+  VOC_K_TANH = 14,    /* standalone tanh over the pcm (only in the split  */
+                      /* tanh ablation; the head applies tanh otherwise)  */
+  VOC_K_COUNT = 15
 } voc_kernel_kind;
 
 typedef struct voc_profile_stat {

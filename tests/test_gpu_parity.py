@@ -296,6 +296,47 @@ def test_split_snake_equals_epilogue_snake(idx, monkeypatch):
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2, 4])
+def test_split_tanh_equals_head_tanh(idx, monkeypatch):
+    """tanh as a pass of its own over the stored pcm (VOC_SPLIT_TANH=1: the
+    head stores conv_out's sums, the standalone tanh stage maps them) gives
+    the bits of the head that applies tanh in registers, and the oracle's
+    output within the end-to-end gates; the standalone pass is one launch
+    that moves 8 bytes per sample.  A tiled decode keeps the head's tanh."""
+    cfg = I.config(idx)
+    t = I.make_weights(cfg, twin=True)
+    frames, rows = SMALL[idx]
+    lat = I.make_latent(cfg, batch=rows, frames=frames)
+    x = to_dev(lat)
+    outs = []
+    for flag, tile in (("1", 0), ("0", 0), ("1", 3)):
+        monkeypatch.setenv("VOC_SPLIT_TANH", flag)
+        ctx = _ctx(cfg, t, tile_frames=tile)
+        try:
+            V.check(V.vocoder_profile_enable(ctx, True), ctx)
+            outs.append(V.decode(ctx, x))
+            torch.cuda.synchronize()
+            st, tn = V.vocoder_profile_read(ctx, V.KERNEL_KINDS.index("tanh"))
+            V.check(st, ctx)
+            split = flag == "1" and tile == 0
+            assert tn["launches"] == (1 if split else 0), (flag, tile)
+            if split:
+                assert tn["bytes"] == 8 * outs[-1].numel()
+        finally:
+            V.vocoder_destroy(ctx)
+    monkeypatch.delenv("VOC_SPLIT_TANH")
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[2], outs[1])
+    ref = O.Model(cfg, t).decode(lat)
+    got = outs[0].cpu().numpy()
+    print(f"split tanh cfg{idx}: max-abs/RMS {rel_maxabs(got, ref):.2e} rel-RMS {rel_rms(got, ref):.2e}")
+    if cfg["dtype"] == "f32":
+        assert rel_maxabs(got, ref) <= TOL["f32"]
+    else:
+        assert rel_rms(got, ref) <= TOL["bf16"]
+        assert rel_maxabs(got, ref) <= BF16_E2E_MAXABS
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 4])
 def test_gemm_col2im_convt_ablation_vs_oracle(idx, monkeypatch):
     """The ConvTranspose1d as a plain GEMM into a column matrix plus a col2im
     overlap-add (the pages' lowering, an ablation of the polyphase GEMM)
