@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb) {
           const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, Lout - 1);
-          rres[mb][nb] = *reinterpret_cast<const f4*>(a.res + hbase + static_cast<int64_t>(n) * kHChunk);
+          rres[mb][nb] = load_h4<OP>(a.res, hbase + static_cast<int64_t>(n) * kHChunk);
         }
       }
     }
@@ -309,8 +309,9 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
             if constexpr (TAPS == 1)
               v += rres[mp + q][nb];
             else if (ok)
-              v += *reinterpret_cast<const f4*>(a.res + hidx);
+              v += load_h4<OP>(a.res, hidx);
           }
+          if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
           if (a.h_out && ok) {
             f4 hv = v;
             if (a.hs_scale) {
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
               hv[2] = snake_f32(v[2], hsc[q][2], hsh[q][2]);
               hv[3] = snake_f32(v[3], hsc[q][3], hsh[q][3]);
             }
-            *reinterpret_cast<f4*>(a.h_out + hidx) = hv;
+            store_h4<OP>(a.h_out, hidx, hv);
           }
           pk[2 * q] = pack_bf16x2(snake_f32(v[0], sal[q][0], sinv[q][0]), snake_f32(v[1], sal[q][1], sinv[q][1]));
           pk[2 * q + 1] = pack_bf16x2(snake_f32(v[2], sal[q][2], sinv[q][2]), snake_f32(v[3], sal[q][3], sinv[q][3]));
@@ -373,8 +374,9 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
           if constexpr (TAPS == 1)
             v += rres[mb][nb];
           else
-            v += *reinterpret_cast<const f4*>(a.res + hidx);
+            v += load_h4<OP>(a.res, hidx);
         }
+        if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
         if (a.h_out) {
           f4 hv = v;
           if (a.hs_scale) {
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
             hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
             hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
           }
-          *reinterpret_cast<f4*>(a.h_out + hidx) = hv;
+          store_h4<OP>(a.h_out, hidx, hv);
         }
         if (a.s_out) {
           f4 sv;

@@ -63,4 +63,42 @@ __device__ __forceinline__ void store_op4<1>(void* base, int64_t idx, f4 v) {
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = p;
 }
 
+// The residual stream h, in the same [row][C/16][T][16] element layout for
+// both operand dtypes: fp32 elements for fp32 operands, fp16 elements for
+// bf16 operands (16-bit activations, at fp16's 11-bit mantissa: rounding h
+// to fp16 after every stage moves the decode by under 2 % of the bf16
+// operands' own error, where bf16 storage would add 40 %).  Arithmetic on h
+// stays fp32; stores round to nearest even.  idx counts elements.
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+
+template <int OP>
+__device__ __forceinline__ f4 load_h4(const void* base, int64_t idx) {
+  if constexpr (OP == 0) {
+    return *reinterpret_cast<const f4*>(static_cast<const float*>(base) + idx);
+  } else {
+    return __builtin_convertvector(*reinterpret_cast<const h4v*>(static_cast<const _Float16*>(base) + idx), f4);
+  }
+}
+
+// A freshly produced residual value as the stream holds it: every consumer
+// (the stored h, the next layer's Snake operand, the head's Snake) starts
+// from the same rounded value, so that an operand computed in a producer's
+// epilogue equals one computed from the stored h.
+template <int OP>
+__device__ __forceinline__ f4 round_h4(f4 v) {
+  if constexpr (OP == 0)
+    return v;
+  else
+    return __builtin_convertvector(__builtin_convertvector(v, h4v), f4);
+}
+
+template <int OP>
+__device__ __forceinline__ void store_h4(void* base, int64_t idx, f4 v) {
+  if constexpr (OP == 0) {
+    *reinterpret_cast<f4*>(static_cast<float*>(base) + idx) = v;
+  } else {
+    *reinterpret_cast<h4v*>(static_cast<_Float16*>(base) + idx) = __builtin_convertvector(v, h4v);
+  }
+}
+
 }  // namespace voc

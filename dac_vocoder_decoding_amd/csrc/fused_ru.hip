@@ -135,7 +135,7 @@ void res_unit_kernel(const ResUnitArgs a) {
       // Unconditional load (frame clamped into the row; clamped values
       // are never stored), so the prefetch is not serialised.
       const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, Lv - 1);
-      hres[mb][nb] = *reinterpret_cast<const f4*>(a.h_in + hbase + static_cast<int64_t>(n) * kHChunk);
+      hres[mb][nb] = load_h4<OP>(a.h_in, hbase + static_cast<int64_t>(n) * kHChunk);
     }
   };
   auto load_h = [&]() {
@@ -166,7 +166,7 @@ void res_unit_kernel(const ResUnitArgs a) {
     if constexpr (XH) {
       const int ch = c * CH + lg * (16 / ES);
       xch = ch;
-      const float* hp = a.h_in + (static_cast<int64_t>(row) * C + (ch & ~15)) * a.T + (ch & 15);
+      const int64_t hp = (static_cast<int64_t>(row) * C + (ch & ~15)) * a.T + (ch & 15);
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
         const int r = unit_row(tid + u * NTH);
@@ -174,7 +174,7 @@ void res_unit_kernel(const ResUnitArgs a) {
         const bool in = r < xrows && t >= -a.lb && t < Lv;
 #pragma unroll
         for (int v = 0; v < HV; ++v)
-          xh[u][v] = in ? *reinterpret_cast<const f4*>(hp + static_cast<int64_t>(t) * kHChunk + 4 * v)
+          xh[u][v] = in ? load_h4<OP>(a.h_in, hp + static_cast<int64_t>(t) * kHChunk + 4 * v)
                         : f4{0.f, 0.f, 0.f, 0.f};
       }
       // Residual rows of this chunk's channels, while the X lines are in L2.
@@ -431,7 +431,8 @@ void res_unit_kernel(const ResUnitArgs a) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int mq = m + 16 * q;
-          const f4 v = acc[mp + q][nb] + b2[q] + hres[mp + q][nb];
+          f4 v = acc[mp + q][nb] + b2[q] + hres[mp + q][nb];
+          if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
           if (a.store_h && ok) {
             f4 hv = v;
             if (a.hs_scale) {
@@ -440,8 +441,9 @@ void res_unit_kernel(const ResUnitArgs a) {
               hv[2] = snake_f32(v[2], hsc[q][2], hsh[q][2]);
               hv[3] = snake_f32(v[3], hsc[q][3], hsh[q][3]);
             }
-            *reinterpret_cast<f4*>(a.h + (static_cast<int64_t>(row) * C + (mq & ~15)) * a.T + (mq & 15) +
-                                   static_cast<int64_t>(n) * kHChunk) = hv;
+            const int64_t hi = (static_cast<int64_t>(row) * C + (mq & ~15)) * a.T + (mq & 15) +
+                               static_cast<int64_t>(n) * kHChunk;
+            store_h4<OP>(a.h, hi, hv);
           }
           if (a.s_out) {
             pk[2 * q] = pack_bf16x2(snake_f32(v[0], sc[q][0], hh[q][0]), snake_f32(v[1], sc[q][1], hh[q][1]));
@@ -486,6 +488,7 @@ void res_unit_kernel(const ResUnitArgs a) {
         if (n >= Lv) continue;
         const int64_t hidx = hbase + static_cast<int64_t>(n) * kHChunk;
         f4 v = acc[mb][nb] + b2 + hres[mb][nb];
+        if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
         f4 hv = v;
         if (a.hs_scale) {
           hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
@@ -493,7 +496,7 @@ void res_unit_kernel(const ResUnitArgs a) {
           hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
           hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
         }
-        if (a.store_h) *reinterpret_cast<f4*>(a.h + hidx) = hv;
+        if (a.store_h) store_h4<OP>(a.h, hidx, hv);
         if (a.s_out) {
           v[0] = snake_f32(v[0], sc[0], hh[0]);
           v[1] = snake_f32(v[1], sc[1], hh[1]);

@@ -15,7 +15,9 @@
 namespace voc {
 
 constexpr int kChunkBytes = 64;
-constexpr int kHChunk = 16;  // fp32 residual stream channels per chunk
+constexpr int kHChunk = 16;  // residual stream channels per chunk row
+// Bytes per residual-stream element: fp32 for fp32 operands, fp16 for bf16.
+constexpr int h_size(int op) { return op == 0 ? 4 : 2; }
 constexpr int kAfTaps = 12;  // taps of the alias-free Snake's low-pass
 
 enum OpType { OP_F32 = 0, OP_BF16 = 1 };

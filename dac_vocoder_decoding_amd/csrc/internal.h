@@ -167,7 +167,7 @@ hipError_t launch_import(const ImportArgs& a, hipStream_t s);
 hipError_t launch_audio_import(int op, const float* x, void* out, int64_t T, int rows, hipStream_t s);
 
 // h fp32 chunked [rows][C/16][T][16] -> y fp32 [rows][C][T].
-hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipStream_t s);
+hipError_t launch_export(int op, const void* h, float* y, int rows, int C, int T, hipStream_t s);
 
 // Head: pcm[dst[r] + o * ch_stride + tau - keep_lo[r]] = tanh(bias[o] +
 //   sum_j sum_i w[o][j][i] * sh[r][tau + j - pad][i]) for tau in
@@ -175,7 +175,9 @@ hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipSt
 // Snake_out(h), already applied by the producer (the last residual unit's
 // epilogue, or the alias-free Snake kernel).
 struct HeadArgs {
-  const float* h;   // Snake_out(h), fp32 chunked
+  const float* h;   // Snake_out(h) in fp32, or with s_scale set the fp16 residual stream h
+  const float* s_scale;  // Snake_out parameters (alpha / pi, 1 / (2 den)) applied at load,
+  const float* s_h;      // or null
   int C, T;         // channels, allocated frames per row
   RowInfo rows;
   int nrows;
@@ -227,6 +229,7 @@ struct AfArgs {
   const float* hh;     // 1 / (2 den) per channel
   float fe[6], fo[6], fd[kAfTaps];
   int rows;
+  int h16;             // x holds fp16 elements (the bf16 decoders' residual stream)
 };
 hipError_t launch_af_snake(const AfArgs& a, hipStream_t s);
 // col2im overlap-add of a ConvTranspose1d computed as a plain GEMM into a
@@ -264,6 +267,7 @@ struct LayerStateArgs {
   unsigned char* buf;
   int64_t plane_bytes, planes;
   int ctx, Tr;
+  int row_bytes;    // bytes per frame row of a plane: 64 (operand), or 16 residual elements
   const unsigned char* old_state;
   unsigned char* new_state;
 };

@@ -129,7 +129,8 @@ struct voc_ctx {
   // in the order conv_in, per block: ConvTranspose1d then its units, head.
   struct LayerState {
     int ctx = 0;                  // frames of context
-    int64_t planes_per_row = 0;   // 64-byte frame-row planes of the layer's input
+    int64_t planes_per_row = 0;   // frame-row planes of the layer's input
+    int row_bytes = kChunkBytes;  // bytes per frame row (operand 64; residual 16 elements)
     size_t off[2] = {0, 0};       // byte offsets of the two copies in st_mem
   };
   std::vector<LayerState> st_layers;
@@ -247,6 +248,13 @@ bool any_unit_xh(const voc_ctx* c) {
   return false;
 }
 
+// The head's Snake_out, when the head applies it while loading the fp16
+// residual stream (bf16 decoders without standalone Snake launches); null
+// when the last producer stores Snake_out(h) in fp32 for it.
+const SnakeDev* head_snake_at_load(const voc_ctx* c) {
+  return c->op == OP_BF16 && !c->cfg.af_snake && !c->split_snake ? &c->W.head_act : nullptr;
+}
+
 Plan make_plan(const voc_ctx* c, int rows, int T, int mg = 0) {
   const voc_config& g = c->cfg;
   const size_t es = op_size(c->op);
@@ -264,6 +272,8 @@ Plan make_plan(const voc_ctx* c, int rows, int T, int mg = 0) {
   p.mg = mg;
   size_t o = 0;
   p.off_xlat = o; o = align_up(o + es * rows * static_cast<size_t>(g.latent_channels) * (T + mg));
+  // The residual-stream buffers are sized for fp32 elements: the last one
+  // holds the head's input, Snake_out(h), in fp32 also for bf16 decoders.
   p.off_h = o;    o = align_up(o + 4 * rows * max_act);
   p.off_h2 = o;   if (any_unit_xh(c) || g.af_snake || c->split_snake) o = align_up(o + 4 * rows * max_act);
   p.off_s0 = o;   o = align_up(o + es * rows * max_act);
@@ -350,6 +360,8 @@ Bufs bufs(voc_ctx* c, const Plan& p) {
   // every plane starts mg frames (64-byte rows) earlier.
   const size_t mgb = static_cast<size_t>(p.mg) * kChunkBytes;
   r.xlat = b + p.off_xlat + mgb;
+  // (The residual-stream buffers keep fp32-sized margins: fp16 planes use
+  // half of each margin, the head's fp32 input all of it.)
   r.h = reinterpret_cast<float*>(b + p.off_h + mgb);
   r.h2 = reinterpret_cast<float*>(b + p.off_h2 + mgb);
   r.s[0] = b + p.off_s0 + mgb;
@@ -510,8 +522,8 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
                                   : 2.0 * frames_in * L.cin * L.cout * (L.taps == 2 ? 2 * L.ups : L.taps);
   const double es = op_size(c->op);
   double bytes = frames_in * L.cin * es + wbytes;
-  if (io.h_out) bytes += frames_out * L.cout * 4;
-  if (io.res) bytes += frames_out * L.cout * 4;
+  if (io.h_out) bytes += frames_out * L.cout * h_size(c->op);
+  if (io.res) bytes += frames_out * L.cout * h_size(c->op);
   if (io.s_out) bytes += frames_out * L.cout * es;
   const int op = c->op;
   return launch(c, s, kind, flops, bytes, "conv launch",
@@ -575,7 +587,8 @@ voc_status run_convt(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, c
   a.rows = rows;
   a.op = c->op;
   const double el = static_cast<double>(rows) * io.T_in * L.ups * L.cout;
-  const double bytes = el * (8.0 + (io.h_out ? 4.0 : 0.0) + (io.s_out ? op_size(c->op) : 0.0));
+  const double hs = h_size(c->op);  // the column matrix and h use the residual element type
+  const double bytes = el * (2.0 * hs + (io.h_out ? hs : 0.0) + (io.s_out ? op_size(c->op) : 0.0));
   return launch(c, s, VOC_K_COL2IM, 0.0, bytes, "col2im launch", [&] { return launch_col2im(a, s); });
 }
 
@@ -598,13 +611,18 @@ voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const Ro
   a.h_scale = h_sn ? h_sn->alpha : nullptr;
   a.h_h = h_sn ? h_sn->invden : nullptr;
   const double el = static_cast<double>(nrows) * T * C;
-  const double bytes = el * 4 + (s_out ? el * op_size(c->op) : 0) + (h_out ? el * 4 : 0);
+  const double bytes = el * 4 + (s_out ? el * op_size(c->op) : 0) + (h_out ? el * h_size(c->op) : 0);
   return launch(c, s, VOC_K_IMPORT, 0.0, bytes, "import launch", [&] { return launch_import(a, s); });
 }
 
+// With `snake`, h is the fp16 residual stream and the head applies that
+// Snake_out while loading (bf16 decoders); without, h holds Snake_out(h) in
+// fp32.
 voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int nrows, int rate,
-                    float* pcm, int64_t ch_stride, hipStream_t s) {
+                    float* pcm, int64_t ch_stride, hipStream_t s, const SnakeDev* snake = nullptr) {
   HeadArgs a{};
+  a.s_scale = snake ? snake->alpha : nullptr;
+  a.s_h = snake ? snake->invden : nullptr;
   const voc_config& g = c->cfg;
   a.h = h;
   a.C = g.width[g.n_blocks];
@@ -630,7 +648,7 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
     for (int r = 0; r < nrows; ++r) frames += mi[4 * nrows + r] - mi[3 * nrows + r];
   }
   const double flops = 2.0 * frames * a.C * 7 * a.nout;
-  const double bytes = frames * a.C * 4 + frames * 4 * a.nout;
+  const double bytes = frames * a.C * (snake ? h_size(c->op) : 4) + frames * 4 * a.nout;
   return launch(c, s, VOC_K_HEAD, flops, bytes, "head launch", [&] { return launch_head(a, s); });
 }
 
@@ -657,11 +675,14 @@ voc_status run_af(voc_ctx* c, const SnakeDev& sn, const float* x, int C, int T, 
   std::memcpy(a.fo, c->af_fo, sizeof(a.fo));
   std::memcpy(a.fd, c->af_fd, sizeof(a.fd));
   a.rows = rows;
+  a.h16 = c->op == OP_BF16 ? 1 : 0;
   const double el = static_cast<double>(rows) * T * C;
+  const double hs = h_size(c->op);
+  const double ob = op_size(out_op);  // OP_F32: fp32 (the head's input, or fp32 operands)
   if (!c->cfg.af_snake)
-    return launch(c, s, VOC_K_SNAKE, 0.0, el * (4 + op_size(out_op)), "Snake launch",
+    return launch(c, s, VOC_K_SNAKE, 0.0, el * (hs + ob), "Snake launch",
                   [&] { return launch_snake(a, s); });
-  return launch(c, s, VOC_K_AF_SNAKE, 48.0 * el, el * (4 + op_size(out_op)), "alias-free Snake launch",
+  return launch(c, s, VOC_K_AF_SNAKE, 48.0 * el, el * (hs + ob), "alias-free Snake launch",
                 [&] { return launch_af_snake(a, s); });
 }
 
@@ -720,7 +741,8 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     const double es = op_size(c->op);
     const double flops = 2.0 * el * C * 8;
     // Reads: the operand (or h itself) and h; writes: h if kept, the next operand.
-    const double bytes = el * ((h_alt ? 4 : es + 4) + (keep_h ? 4 : 0) + (s_out ? es : 0)) + 8.0 * C * C * es;
+    const double hs = h_size(c->op);
+    const double bytes = el * ((h_alt ? hs : es + hs) + (keep_h ? hs : 0) + (s_out ? es : 0)) + 8.0 * C * C * es;
     const int op = c->op;
     return launch(c, s, VOC_K_RES_FUSED, flops, bytes, "residual unit launch",
                   [&] { return launch_res_unit(op, a, big, s); });
@@ -796,13 +818,14 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
     const voc_ctx::LayerState& L = c->st_layers[li++];
     LayerStateArgs a{};
     a.buf = static_cast<unsigned char*>(const_cast<void*>(buf));
-    a.plane_bytes = (c->mg + frames) * kChunkBytes;
+    a.plane_bytes = (c->mg + frames) * L.row_bytes;
     a.planes = static_cast<int64_t>(rows) * L.planes_per_row;
     a.ctx = L.ctx;
     a.Tr = static_cast<int>(frames);
+    a.row_bytes = L.row_bytes;
     a.old_state = static_cast<const unsigned char*>(c->st_mem) + L.off[c->st_par];
     a.new_state = static_cast<unsigned char*>(c->st_mem) + L.off[c->st_par ^ 1];
-    const double bytes = 3.0 * a.planes * a.ctx * kChunkBytes;
+    const double bytes = 3.0 * a.planes * a.ctx * L.row_bytes;
     return launch(c, s, VOC_K_IMPORT, 0.0, bytes, "stream state launch",
                   [&] { return launch_layer_state(a, s); });
   };
@@ -853,7 +876,7 @@ voc_status run_stack(voc_ctx* c, const Bufs& B, int rows, int T, hipStream_t s, 
     for (int r = 0; r < nr; ++r) {
       void* s_next = nullptr;
       // The last unit stores the head's Snake of h: nothing else reads h.
-      const SnakeDev* hs = (b == nb - 1 && r == nr - 1) ? &W.head_act : nullptr;
+      const SnakeDev* hs = (b == nb - 1 && r == nr - 1 && !head_snake_at_load(c)) ? &W.head_act : nullptr;
       // The last unit of any other block feeds the next block only through
       // its Snake operand; its h is never read again.
       const bool keep_h = !(r == nr - 1 && b < nb - 1);
@@ -1298,7 +1321,7 @@ voc_status decode_batch(voc_ctx* c, const float* latent, int64_t T_src, int64_t 
                                     : run_stack(c, Bf, static_cast<int>(rows), T_alloc, s, &h_last);
   if (st) return st;
   return run_head(c, h_last, static_cast<int>(T_alloc * c->hop), Bf.rows, static_cast<int>(rows),
-                  static_cast<int>(c->hop), pcm, ch_stride, s);
+                  static_cast<int>(c->hop), pcm, ch_stride, s, head_snake_at_load(c));
 }
 
 // decode_batch over the rows in groups of `group` rows (all at once when
@@ -1602,7 +1625,7 @@ VOC_API voc_status vocoder_encode(voc_ctx* c, const float* audio, int64_t B, int
   if (st) return st;
   const int C = g.latent_channels;
   return launch(c, s, VOC_K_EXPORT, 0.0, 8.0 * rows * C * T, "export launch",
-                [&] { return launch_export(hc, latent, rows, C, static_cast<int>(T), s); });
+                [&] { return launch_export(c->op, hc, latent, rows, C, static_cast<int>(T), s); });
 }
 
 namespace {
@@ -1614,19 +1637,23 @@ std::vector<voc_ctx::LayerState> stream_layers(const voc_ctx* c) {
   const voc_config& g = c->cfg;
   const int op_rows = 64 / op_size(c->op);  // channels per 64-byte operand row
   std::vector<voc_ctx::LayerState> v;
-  auto add = [&](int ctx, int64_t planes) {
+  const int h_rows = kHChunk * h_size(c->op);  // bytes per residual-stream frame row
+  auto add = [&](int ctx, int64_t planes, int row_bytes) {
     voc_ctx::LayerState L;
     L.ctx = ctx;
     L.planes_per_row = planes;
+    L.row_bytes = row_bytes;
     v.push_back(L);
   };
-  add(6, (g.in_proj > 0 ? g.in_proj : g.latent_channels) / op_rows);
+  add(6, (g.in_proj > 0 ? g.in_proj : g.latent_channels) / op_rows, kChunkBytes);
   for (int b = 0; b < g.n_blocks; ++b) {
-    add(1, g.width[b] / op_rows);
+    add(1, g.width[b] / op_rows, kChunkBytes);
     const int C = g.width[b + 1];
-    for (int r = 0; r < g.n_res; ++r) add(6 * g.dilation[r], unit_xh(c, C) ? C / 16 : C / op_rows);
+    for (int r = 0; r < g.n_res; ++r)
+      add(6 * g.dilation[r], unit_xh(c, C) ? C / 16 : C / op_rows, unit_xh(c, C) ? h_rows : kChunkBytes);
   }
-  add(6, g.width[g.n_blocks] / 16);
+  // The head reads h (fp16, bf16 decoders) or Snake_out(h) in fp32.
+  add(6, g.width[g.n_blocks] / 16, head_snake_at_load(c) ? h_rows : kChunkBytes);
   return v;
 }
 }  // namespace
@@ -1640,7 +1667,7 @@ VOC_API voc_status vocoder_stream_reset(voc_ctx* c, int64_t rows) {
   size_t o = 0;
   int margin = 0;
   for (auto& l : L) {
-    const size_t bytes = static_cast<size_t>(rows) * l.planes_per_row * l.ctx * kChunkBytes;
+    const size_t bytes = static_cast<size_t>(rows) * l.planes_per_row * l.ctx * l.row_bytes;
     l.off[0] = o;
     o = align_up(o + bytes);
     l.off[1] = o;
@@ -1719,7 +1746,7 @@ VOC_API voc_status vocoder_stream_decode(voc_ctx* c, const float* latent, int64_
   if (!st) st = run_stack(c, Bf, static_cast<int>(rows), static_cast<int>(t), s, &h_last);
   if (!st)
     st = run_head(c, h_last, static_cast<int>(t * c->hop), Bf.rows, static_cast<int>(rows),
-                  static_cast<int>(c->hop), pcm, t * c->hop, s);
+                  static_cast<int>(c->hop), pcm, t * c->hop, s, head_snake_at_load(c));
   c->mg = 0;
   c->st_active = false;
   if (st) return st;
@@ -1996,13 +2023,18 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
         if (st) return st;
         return run_head(c, h2, T, ri, rows, 1, out, T_in, s);
       }
+      if (const SnakeDev* hs = head_snake_at_load(c)) {  // the head applies Snake_out to h
+        st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s);
+        if (st) return st;
+        return run_head(c, h, T, ri, rows, 1, out, T_in, s, hs);
+      }
       st = run_import(c, in, T_in, si.c_in, ri, rows, T, nullptr, nullptr, h, s, &W.head_act);
       if (st) return st;
       return run_head(c, h, T, ri, rows, 1, out, T_in, s);
   }
   if (st) return st;
   return launch(c, s, VOC_K_EXPORT, 0.0, 8.0 * rows * si.c_out * t_out, "export launch",
-                [&] { return launch_export(h, out, rows, si.c_out, static_cast<int>(t_out), s); });
+                [&] { return launch_export(c->op, h, out, rows, si.c_out, static_cast<int>(t_out), s); });
 }
 
 VOC_API voc_status voc_dbg_peak(int what, int64_t n, double* value, void* stream) {

@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256) void import_kernel(const ImportArgs a) {
   v[3] = tile[c + 3][t];
   const int cc = c0 + c;
   if (a.h_out) {
+    if (a.s_out) v = round_h4<OP>(v);  // x is a residual value: the operand starts from the stored one
     const int64_t hidx = (static_cast<int64_t>(r) * a.C + (cc & ~15)) * a.T +
                          static_cast<int64_t>(tt) * kHChunk + (cc & 15);
     f4 hv = v;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void import_kernel(const ImportArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) hv[e] = snake_f32(v[e], a.h_scale[cc + e], a.h_h[cc + e]);
     }
-    *reinterpret_cast<f4*>(a.h_out + hidx) = hv;
+    store_h4<OP>(a.h_out, hidx, hv);
   }
   if (a.s_out) {
     if (a.s_alpha) {
@@ -183,7 +184,8 @@ hipError_t launch_audio_import(int op, const float* x, void* out, int64_t T, int
 }
 
 // -------------------------------------------------------------- export
-__global__ __launch_bounds__(256) void export_kernel(const float* h, float* y, int C, int T) {
+template <int OP>
+__global__ __launch_bounds__(256) void export_kernel(const void* h, float* y, int C, int T) {
   __shared__ float tile[16][65];
   const int r = blockIdx.y;
   const int cblocks = C / 16;
@@ -195,8 +197,7 @@ __global__ __launch_bounds__(256) void export_kernel(const float* h, float* y, i
     const int tt = t0 + t;
     f4 v = f4{0.f, 0.f, 0.f, 0.f};
     if (tt < T)
-      v = *reinterpret_cast<const f4*>(h + (static_cast<int64_t>(r) * C + c0) * T +
-                                       static_cast<int64_t>(tt) * kHChunk + c);
+      v = load_h4<OP>(h, (static_cast<int64_t>(r) * C + c0) * T + static_cast<int64_t>(tt) * kHChunk + c);
     tile[c][t] = v[0];
     tile[c + 1][t] = v[1];
     tile[c + 2][t] = v[2];
@@ -211,9 +212,12 @@ __global__ __launch_bounds__(256) void export_kernel(const float* h, float* y, i
   }
 }
 
-hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipStream_t s) {
+hipError_t launch_export(int op, const void* h, float* y, int rows, int C, int T, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((C / 16) * ((T + 63) / 64)), static_cast<unsigned>(rows));
-  hipLaunchKernelGGL(export_kernel, grid, dim3(256), 0, s, h, y, C, T);
+  if (op == OP_F32)
+    hipLaunchKernelGGL(export_kernel<OP_F32>, grid, dim3(256), 0, s, h, y, C, T);
+  else
+    hipLaunchKernelGGL(export_kernel<OP_BF16>, grid, dim3(256), 0, s, h, y, C, T);
   return hipGetLastError();
 }
 
@@ -221,30 +225,33 @@ hipError_t launch_export(const float* h, float* y, int rows, int C, int T, hipSt
 // One layer's carried context in a stream (qwentts.cpp ARCHITECTURE,
 // "Streaming decode (stateful path)": each causal conv keeps the last
 // (K-1)*d rows of its input).  The layer's input buffer holds, per plane of
-// 64-byte frame rows, the chunk in frames [0, Tr) and room for ctx frames
-// before it.  The margin receives the saved context (old), and the new
+// frame rows (64-byte operand rows, or 16 residual-stream elements), the
+// chunk in frames [0, Tr) and room for ctx frames before it.  The margin receives the saved context (old), and the new
 // context (the last ctx frames of old followed by the chunk) is saved for the
 // next chunk.  Margin writes (frames < 0) and chunk reads (frames >= 0) never
 // overlap; old and new are separate buffers.
 __global__ __launch_bounds__(256) void layer_state_kernel(const LayerStateArgs a) {
-  const int64_t total = a.planes * a.ctx * 4;  // 16-byte units
+  const int U = a.row_bytes / 16;  // 16-byte units per frame row
+  const int64_t rb = a.row_bytes;
+  const int64_t total = a.planes * a.ctx * U;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t p = i / (a.ctx * 4);
-    const int k = static_cast<int>((i / 4) % a.ctx), u = static_cast<int>(i % 4);
-    const uint4* old_row = reinterpret_cast<const uint4*>(a.old_state + (p * a.ctx + k) * kChunkBytes) + u;
+    const int64_t p = i / (a.ctx * U);
+    const int k = static_cast<int>((i / U) % a.ctx), u = static_cast<int>(i % U);
+    const uint4* old_row = reinterpret_cast<const uint4*>(a.old_state + (p * a.ctx + k) * rb) + u;
     unsigned char* plane = a.buf + p * a.plane_bytes;
     const uint4 o = *old_row;
     const int q = a.Tr + k;  // position in (old context, chunk)
-    const uint4 nv = q < a.ctx ? *(reinterpret_cast<const uint4*>(a.old_state + (p * a.ctx + q) * kChunkBytes) + u)
-                               : *(reinterpret_cast<const uint4*>(plane + static_cast<int64_t>(q - a.ctx) * kChunkBytes) + u);
-    *(reinterpret_cast<uint4*>(plane + static_cast<int64_t>(k - a.ctx) * kChunkBytes) + u) = o;
-    *(reinterpret_cast<uint4*>(a.new_state + (p * a.ctx + k) * kChunkBytes) + u) = nv;
+    const uint4 nv = q < a.ctx ? *(reinterpret_cast<const uint4*>(a.old_state + (p * a.ctx + q) * rb) + u)
+                               : *(reinterpret_cast<const uint4*>(plane + static_cast<int64_t>(q - a.ctx) * rb) + u);
+    *(reinterpret_cast<uint4*>(plane + static_cast<int64_t>(k - a.ctx) * rb) + u) = o;
+    *(reinterpret_cast<uint4*>(a.new_state + (p * a.ctx + k) * rb) + u) = nv;
   }
 }
 
 hipError_t launch_layer_state(const LayerStateArgs& a, hipStream_t s) {
-  const int64_t total = a.planes * a.ctx * 4;
+  if (a.row_bytes <= 0 || a.row_bytes % 16) return hipErrorInvalidValue;
+  const int64_t total = a.planes * a.ctx * (a.row_bytes / 16);
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 2048));
   hipLaunchKernelGGL(layer_state_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -254,8 +261,10 @@ hipError_t launch_layer_state(const LayerStateArgs& a, hipStream_t s) {
 // Output head (minimaxmusic.cpp ARCHITECTURE, "Flow VAE": snake_out, conv_out
 // k=7 with bias, tanh; two output channels for a decoder that writes stereo
 // from one latent, as the H3 audio VAE of the TensorSharp minimax-h3 page
-// does).  Its input already holds Snake_out(h) (applied by its producer), so
-// the head is a pure stream:
+// does).  Its input holds Snake_out(h) in fp32 (applied by its producer), or
+// (SNK, bf16 decoders) the fp16 residual stream h itself, to which the head
+// applies Snake_out as it loads: half the bytes, and the Snake starts from
+// the stored h as every other consumer's does.  The head is a pure stream:
 //   lane l of a wave reads frame f = o0 - P + l (all C channels, 64-byte
 //   chunk rows) and forms the seven per-tap projections of each output
 //   channel, z_j[f] = sum_i w[j][i] x[f][i];
@@ -269,7 +278,7 @@ hipError_t launch_layer_state(const LayerStateArgs& a, hipStream_t s) {
 // into the store.
 constexpr int kHeadOut = 58;  // outputs per wave
 
-template <int NOUT>
+template <int NOUT, int SNK>
 __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   const int r = blockIdx.y;
   const int lo = a.rows.keep_lo[r], hi = a.rows.keep_hi[r];
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
   const int P = a.pad;  // 3, or 6 for the causal head
   const int f = o0 - P + lane;
   const bool valid = f >= -a.lb && f < Lr;
-  const float* hp = a.h + static_cast<int64_t>(r) * C * a.T + static_cast<int64_t>(f) * kHChunk;
+  const int64_t hp = static_cast<int64_t>(r) * C * a.T + static_cast<int64_t>(f) * kHChunk;
   const int64_t plane = static_cast<int64_t>(a.T) * kHChunk;
   float z[NOUT][7];
 #pragma unroll
@@ -301,8 +310,22 @@ __global__ __launch_bounds__(256) void head_kernel(const HeadArgs a) {
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        x[u][q] = valid && k0 + u < nk ? *reinterpret_cast<const f4*>(hp + (k0 + u) * plane + q * 4)
+        x[u][q] = valid && k0 + u < nk ? load_h4<SNK>(a.h, hp + (k0 + u) * plane + q * 4)
                                        : f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (SNK) {  // Snake_out at load (parameters uniform across the wave)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k0 + u >= nk) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = (k0 + u) * 16 + q * 4;
+          const f4 sc = *reinterpret_cast<const f4*>(a.s_scale + ch);
+          const f4 sh = *reinterpret_cast<const f4*>(a.s_h + ch);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[u][q][e] = snake_f32(x[u][q][e], sc[e], sh[e]);
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (k0 + u >= nk) break;
@@ -368,10 +391,14 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
   // keep ranges lie inside the allocated frames; the grid covers them.
   const int waves = (a.T + kHeadOut - 1) / kHeadOut;
   const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(a.nrows));
-  if (a.nout == 2)
-    hipLaunchKernelGGL(head_kernel<2>, grid, dim3(256), 0, s, a);
+  if (a.nout == 2 && a.s_scale)
+    hipLaunchKernelGGL((head_kernel<2, 1>), grid, dim3(256), 0, s, a);
+  else if (a.nout == 2)
+    hipLaunchKernelGGL((head_kernel<2, 0>), grid, dim3(256), 0, s, a);
+  else if (a.s_scale)
+    hipLaunchKernelGGL((head_kernel<1, 1>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(head_kernel<1>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((head_kernel<1, 0>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -416,12 +443,14 @@ constexpr int kAfPrefetch = VOC_AF_PREFETCH;  // input frames requested ahead of
 template <int N> struct AfVec;
 template <> struct AfVec<2> {
   typedef float T __attribute__((ext_vector_type(2)));
+  typedef _Float16 H __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ void store_bf16(uint16_t* p, T y) {
     *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(y[0], y[1]);
   }
 };
 template <> struct AfVec<4> {
   typedef f4 T;
+  typedef _Float16 H __attribute__((ext_vector_type(4)));
   static __device__ __forceinline__ void store_bf16(uint16_t* p, T y) {
     uint2 v;
     v.x = pack_bf16x2(y[0], y[1]);
@@ -430,9 +459,12 @@ template <> struct AfVec<4> {
   }
 };
 
-template <int OUT_OP>
+// H16: the input (the residual stream, or conv1's output in its layout) holds
+// fp16 elements.  An OUT_OP == OP_F32 output is fp32 (the head's input).
+template <int OUT_OP, int H16>
 __global__ __launch_bounds__(256, VOC_AF_MIN_WAVES) void af_snake_kernel(const AfArgs a) {
   typedef typename AfVec<kAfCpt>::T fv;
+  typedef typename AfVec<kAfCpt>::H hv;
   constexpr int LPR = 16 / kAfCpt;   // lanes per 64-byte frame row
   constexpr int RPW = 256 / LPR;     // runs per workgroup
   const int r = blockIdx.y;
@@ -444,7 +476,7 @@ __global__ __launch_bounds__(256, VOC_AF_MIN_WAVES) void af_snake_kernel(const A
   const int t0 = run * kAfRun;
   if (t0 >= len) return;
   const int c = chunk * 16 + q * kAfCpt;
-  const float* xp = a.x + (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * kAfCpt;
+  const int64_t xp = (static_cast<int64_t>(r) * a.C + chunk * 16) * a.T + q * kAfCpt;
   const fv sc = *reinterpret_cast<const fv*>(a.scale + c);
   const fv hh = *reinterpret_cast<const fv*>(a.hh + c);
   // Output element index of frame 0 of this thread's channels.
@@ -455,7 +487,11 @@ __global__ __launch_bounds__(256, VOC_AF_MIN_WAVES) void af_snake_kernel(const A
   const fv zero = fv(0.f);
   auto ld = [&](int t) -> fv {
     t = min(max(t, 0), len - 1);
-    return *reinterpret_cast<const fv*>(xp + static_cast<int64_t>(t) * kHChunk);
+    const int64_t i = xp + static_cast<int64_t>(t) * kHChunk;
+    if constexpr (H16)
+      return __builtin_convertvector(*reinterpret_cast<const hv*>(reinterpret_cast<const _Float16*>(a.x) + i), fv);
+    else
+      return *reinterpret_cast<const fv*>(a.x + i);
   };
   auto snake_v = [&](fv u) -> fv {
     fv v;
@@ -548,10 +584,14 @@ hipError_t launch_af_snake(const AfArgs& a, hipStream_t s) {
   constexpr int RPW = 256 / (16 / kAfCpt);
   const int runs = (a.T + kAfRun - 1) / kAfRun;
   const dim3 grid(static_cast<unsigned>((a.C / 16) * ((runs + RPW - 1) / RPW)), static_cast<unsigned>(a.rows));
-  if (a.out_op == OP_F32)
-    hipLaunchKernelGGL(af_snake_kernel<OP_F32>, grid, dim3(256), 0, s, a);
+  if (a.out_op == OP_F32 && a.h16)
+    hipLaunchKernelGGL((af_snake_kernel<OP_F32, 1>), grid, dim3(256), 0, s, a);
+  else if (a.out_op == OP_F32)
+    hipLaunchKernelGGL((af_snake_kernel<OP_F32, 0>), grid, dim3(256), 0, s, a);
+  else if (a.h16)
+    hipLaunchKernelGGL((af_snake_kernel<OP_BF16, 1>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(af_snake_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
+    return hipErrorInvalidValue;  // bf16 operands always come with an fp16 residual stream
   return hipGetLastError();
 }
 
@@ -562,7 +602,7 @@ hipError_t launch_af_snake(const AfArgs& a, hipStream_t s) {
 // channels, or eight bf16 channels (read from two fp32 units).  A wave
 // covers 16 consecutive frames of an output chunk, so reads and writes are
 // whole 64-byte rows.
-template <int OUT_OP>
+template <int OUT_OP, int H16>
 __global__ __launch_bounds__(256) void snake_kernel(const AfArgs a) {
   constexpr int CH = OUT_OP == OP_F32 ? 16 : 32;  // channels per output row
   constexpr int CPT = CH / 4;                     // channels per thread
@@ -578,8 +618,8 @@ __global__ __launch_bounds__(256) void snake_kernel(const AfArgs a) {
 #pragma unroll
   for (int k = 0; k < CPT / 4; ++k) {
     const int ck = c + 4 * k;
-    const f4 x = *reinterpret_cast<const f4*>(a.x + (static_cast<int64_t>(r) * a.C + (ck & ~15)) * a.T +
-                                              static_cast<int64_t>(t) * kHChunk + (ck & 15));
+    const f4 x = load_h4<H16>(a.x, (static_cast<int64_t>(r) * a.C + (ck & ~15)) * a.T +
+                                        static_cast<int64_t>(t) * kHChunk + (ck & 15));
     const f4 sc = *reinterpret_cast<const f4*>(a.scale + ck);
     const f4 hh = *reinterpret_cast<const f4*>(a.hh + ck);
 #pragma unroll
@@ -587,7 +627,7 @@ __global__ __launch_bounds__(256) void snake_kernel(const AfArgs a) {
   }
   const int64_t idx = (static_cast<int64_t>(r) * a.C + chunk * CH) * a.T + static_cast<int64_t>(t) * CH + q * CPT;
   if constexpr (OUT_OP == OP_F32) {
-    *reinterpret_cast<f4*>(static_cast<float*>(a.out) + idx) = y[0];
+    store_h4<OP_F32>(a.out, idx, y[0]);  // fp32: the head's input (or fp32 operands)
   } else {
     uint4 v;
     v.x = pack_bf16x2(y[0][0], y[0][1]);
@@ -601,10 +641,14 @@ __global__ __launch_bounds__(256) void snake_kernel(const AfArgs a) {
 hipError_t launch_snake(const AfArgs& a, hipStream_t s) {
   const int ch = a.out_op == OP_F32 ? 16 : 32;
   const dim3 grid(static_cast<unsigned>((a.C / ch) * ((a.T + 63) / 64)), static_cast<unsigned>(a.rows));
-  if (a.out_op == OP_F32)
-    hipLaunchKernelGGL(snake_kernel<OP_F32>, grid, dim3(256), 0, s, a);
+  if (a.out_op == OP_F32 && a.h16)
+    hipLaunchKernelGGL((snake_kernel<OP_F32, 1>), grid, dim3(256), 0, s, a);
+  else if (a.out_op == OP_F32)
+    hipLaunchKernelGGL((snake_kernel<OP_F32, 0>), grid, dim3(256), 0, s, a);
+  else if (a.h16)
+    hipLaunchKernelGGL((snake_kernel<OP_BF16, 1>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(snake_kernel<OP_BF16>, grid, dim3(256), 0, s, a);
+    return hipErrorInvalidValue;  // bf16 operands always come with an fp16 residual stream
   return hipGetLastError();
 }
 
@@ -627,19 +671,22 @@ __global__ __launch_bounds__(256) void col2im_kernel(const Col2imArgs a) {
   if (tau >= lout) return;
   const int o = chunk * 16 + q * 4;
   const int mcol = 2 * a.s * a.Cout;
-  const float* colr = a.col + static_cast<int64_t>(r) * mcol * a.T_col;
+  // The column matrix is in the residual-stream layout of the column GEMM's
+  // output (fp16 elements for bf16 operands).
+  const int64_t colr = static_cast<int64_t>(r) * mcol * a.T_col;
   auto z = [&](int k, int n) -> f4 {  // z[k*Cout + o .. + 3][n]
     const int m = k * a.Cout + o;
-    return *reinterpret_cast<const f4*>(colr + static_cast<int64_t>(m & ~15) * a.T_col +
-                                        static_cast<int64_t>(n) * kHChunk + (m & 15));
+    return load_h4<OP>(a.col, colr + static_cast<int64_t>(m & ~15) * a.T_col +
+                                  static_cast<int64_t>(n) * kHChunk + (m & 15));
   };
   const int n = (tau + a.crop) / a.s, k = tau + a.crop - n * a.s;
   f4 v = *reinterpret_cast<const f4*>(a.bias + o);
   if (n < lin) v += z(k, n);
   if (n >= 1 && n - 1 < lin) v += z(k + a.s, n - 1);
+  if (a.s_out) v = round_h4<OP>(v);  // the Snake below starts from the stored h
   if (a.h_out)
-    *reinterpret_cast<f4*>(a.h_out + (static_cast<int64_t>(r) * a.Cout + chunk * 16) * a.T_out +
-                           static_cast<int64_t>(tau) * kHChunk + q * 4) = v;
+    store_h4<OP>(a.h_out, (static_cast<int64_t>(r) * a.Cout + chunk * 16) * a.T_out +
+                              static_cast<int64_t>(tau) * kHChunk + q * 4, v);
   if (a.s_out) {
     if (a.s_alpha) {
 #pragma unroll
