@@ -42,10 +42,6 @@ namespace voc {
 #define VOC_RU_CHUNK_H_MAX 8
 #endif
 
-// Workgroups per CU asked of the register allocator for four-wave instances.
-#ifndef VOC_RU_MINB4
-#define VOC_RU_MINB4 2
-#endif
 
 // Eight-wave instances (one workgroup per CU) stage stage 1 through two LDS
 // buffers: the next tap group (and channel chunk) is stored while the
@@ -60,8 +56,9 @@ namespace voc {
 #define VOC_RU_PINGPONG 1
 #endif
 
-template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG, bool XH>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N == 4 ? VOC_RU_MINB4 : 1)
+// MINB: workgroups per CU the register allocator must leave room for.
+template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG, bool XH, int MINB>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB)
 void res_unit_kernel(const ResUnitArgs a) {
   constexpr int NTH = 64 * WAVES_M * WAVES_N;  // threads per workgroup
   constexpr int CH = OpT<OP>::CH;
@@ -509,64 +506,75 @@ void res_unit_kernel(const ResUnitArgs a) {
   }
 }
 
-// Instances: channel width C -> {m-blocks per wave, n-blocks, waves M, waves N, taps per group}.
+// Instances: channel width C -> {m-blocks per wave, n-blocks, waves M, waves N,
+// taps per group, workgroups per CU}.
 // Only widths where one fused launch beats the conv1 + conv2 pair on MI355X
 // (per-layer kernel traces): at C >= 256 the whole-C tile leaves too few
-// frames per workgroup (LDS holds U for all C), and the pair is faster.
-// Tiles per dtype and width (m-blocks, n-blocks, waves M, waves N, taps per
-// group): a large-frame tile, the fastest in per-layer traces of the full
-// workloads on MI355X, and a half-frame tile for launches too short to give
-// the large one two workgroups per CU.  Overridable at build time for sweeps.
+// frames per workgroup (LDS holds U for all C), and the pair is faster (a
+// 256-channel eight-wave tile measured 1040 us per unit against 1000 us for
+// the pair on the batched bf16 windows).
+// Per dtype and width: a large-frame tile, the fastest in per-layer traces of
+// the full workloads on MI355X, and a half-frame tile for launches too short
+// to give the large one two workgroups per CU.  The bf16 64-channel large tile
+// trades frames for occupancy: 128 frames, one tap per LDS group and 128
+// VGPRs give four workgroups per CU (16 waves), whose staging, Snake and
+// epilogue phases then overlap other workgroups' matrix phases; 10 % faster
+// per unit than 256 frames at two workgroups.  Overridable at build time for
+// sweeps.
 #ifndef VOC_F32_RU64
-#define VOC_F32_RU64 4, 4, 1, 4, 7
+#define VOC_F32_RU64 4, 2, 1, 4, 1, 4
+#endif
+#ifndef VOC_F32_RU96
+#define VOC_F32_RU96 6, 2, 1, 4, 7, 2
 #endif
 #ifndef VOC_F32_RU128
-#define VOC_F32_RU128 4, 4, 2, 2, 4
+#define VOC_F32_RU128 4, 4, 2, 2, 4, 2
 #endif
 #ifndef VOC_BF_RU64
-#define VOC_BF_RU64 4, 4, 1, 4, 7
+#define VOC_BF_RU64 4, 2, 1, 4, 1, 4
 #endif
 #ifndef VOC_BF_RU96
-#define VOC_BF_RU96 6, 4, 1, 4, 7
+#define VOC_BF_RU96 6, 4, 1, 4, 7, 2
 #endif
 #ifndef VOC_BF_RU128
-#define VOC_BF_RU128 4, 4, 2, 4, 4
+#define VOC_BF_RU128 4, 4, 2, 4, 4, 1
 #endif
 #ifndef VOC_BF_RU192
-#define VOC_BF_RU192 3, 4, 4, 2, 4
+#define VOC_BF_RU192 3, 4, 4, 2, 4, 1
 #endif
 #define VOC_RU_(...) VOC_RU(__VA_ARGS__)
 template <int OP>
 static hipError_t launch_ru(const ResUnitArgs& a, bool big, hipStream_t s, int* bn) {
-#define VOC_RU(CW, BIG, A, B, WM, WN, TGV)                                                          \
-  if (a.C == CW && big == BIG) {                                                                    \
-    *bn = WN * B * 16;                                                                              \
-    if (a.n_tiles <= 0) return hipSuccess;                                                          \
-    if (a.x_from_h)                                                                                 \
-      hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, true>), dim3(a.n_tiles * a.rows),  \
-                         dim3(64 * WM * WN), 0, s, a);                                              \
-    else                                                                                            \
-      hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, false>), dim3(a.n_tiles * a.rows), \
-                         dim3(64 * WM * WN), 0, s, a);                                              \
-    return hipGetLastError();                                                                       \
+#define VOC_RU(CW, BIG, A, B, WM, WN, TGV, MB)                                                          \
+  if (a.C == CW && big == BIG) {                                                                        \
+    *bn = WN * B * 16;                                                                                  \
+    if (a.n_tiles <= 0) return hipSuccess;                                                              \
+    if (a.x_from_h)                                                                                     \
+      hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, true, MB>), dim3(a.n_tiles * a.rows),  \
+                         dim3(64 * WM * WN), 0, s, a);                                                  \
+    else                                                                                                \
+      hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, false, MB>), dim3(a.n_tiles * a.rows), \
+                         dim3(64 * WM * WN), 0, s, a);                                                  \
+    return hipGetLastError();                                                                           \
   }
   if constexpr (OP == OP_BF16) {
     VOC_RU_(64, true, VOC_BF_RU64)
-    VOC_RU(64, false, 4, 2, 1, 4, 7)
+    VOC_RU(64, false, 4, 2, 1, 4, 7, 2)
     VOC_RU_(96, true, VOC_BF_RU96)
-    VOC_RU(96, false, 6, 2, 1, 4, 7)
+    VOC_RU(96, false, 6, 2, 1, 4, 7, 2)
     VOC_RU_(128, true, VOC_BF_RU128)
-    VOC_RU(128, false, 4, 4, 2, 2, 4)
+    VOC_RU(128, false, 4, 4, 2, 2, 4, 2)
     VOC_RU_(192, true, VOC_BF_RU192)
-    VOC_RU(192, false, 3, 4, 4, 1, 2)
+    VOC_RU(192, false, 3, 4, 4, 1, 2, 2)
   } else {
-    VOC_RU(16, false, 1, 4, 1, 4, 7)
-    VOC_RU(32, false, 2, 2, 1, 4, 7)
+    VOC_RU(16, false, 1, 4, 1, 4, 7, 2)
+    VOC_RU(32, false, 2, 2, 1, 4, 7, 2)
     VOC_RU_(64, true, VOC_F32_RU64)
-    VOC_RU(64, false, 4, 2, 1, 4, 7)
-    VOC_RU(96, false, 6, 2, 1, 4, 7)
+    VOC_RU(64, false, 4, 2, 1, 4, 7, 2)
+    VOC_RU_(96, true, VOC_F32_RU96)
+    VOC_RU(96, false, 6, 2, 1, 4, 7, 2)
     VOC_RU_(128, true, VOC_F32_RU128)
-    VOC_RU(128, false, 4, 2, 2, 2, 4)
+    VOC_RU(128, false, 4, 2, 2, 2, 4, 2)
   }
 #undef VOC_RU
 #undef VOC_RU_
