@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   // loads are unconditional (row and frame clamped into range; clamped
   // values are never stored): conditional loads make the compiler wait for
   // each one at the branch join, which serialises the prefetch.
-  f4 rres[WMB][WNB];
+  typename HQuad<OP>::T rres[WMB][WNB];  // converted in the epilogue
   if constexpr (TAPS == 1) {
     if (a.res) {
 #pragma unroll
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb) {
           const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, Lout - 1);
-          rres[mb][nb] = load_h4<OP>(a.res, hbase + static_cast<int64_t>(n) * kHChunk);
+          rres[mb][nb] = load_h4_raw<OP>(a.res, hbase + static_cast<int64_t>(n) * kHChunk);
         }
       }
     }
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
                                static_cast<int64_t>(tau) * kHChunk;
           if (a.res) {
             if constexpr (TAPS == 1)
-              v += rres[mp + q][nb];
+              v += h4_to_f4<OP>(rres[mp + q][nb]);
             else if (ok)
               v += load_h4<OP>(a.res, hidx);
           }
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
         const int64_t hidx = hbase + static_cast<int64_t>(tau) * kHChunk;
         if (a.res) {
           if constexpr (TAPS == 1)
-            v += rres[mb][nb];
+            v += h4_to_f4<OP>(rres[mb][nb]);
           else
             v += load_h4<OP>(a.res, hidx);
         }

@@ -92,6 +92,28 @@ __device__ __forceinline__ f4 round_h4(f4 v) {
     return __builtin_convertvector(__builtin_convertvector(v, h4v), f4);
 }
 
+// Four residual values as loaded, converted only where they are used: fp16
+// quads held this way take two VGPRs instead of four while they wait in
+// registers (prefetched residuals, staged X tiles).  load_h4 == to_f4(load).
+template <int OP> struct HQuad { typedef f4 T; };
+template <> struct HQuad<1> { typedef h4v T; };
+
+template <int OP>
+__device__ __forceinline__ typename HQuad<OP>::T load_h4_raw(const void* base, int64_t idx) {
+  if constexpr (OP == 0)
+    return *reinterpret_cast<const f4*>(static_cast<const float*>(base) + idx);
+  else
+    return *reinterpret_cast<const h4v*>(static_cast<const _Float16*>(base) + idx);
+}
+
+template <int OP>
+__device__ __forceinline__ f4 h4_to_f4(typename HQuad<OP>::T v) {
+  if constexpr (OP == 0)
+    return v;
+  else
+    return __builtin_convertvector(v, f4);
+}
+
 template <int OP>
 __device__ __forceinline__ void store_h4(void* base, int64_t idx, f4 v) {
   if constexpr (OP == 0) {

@@ -123,7 +123,7 @@ void res_unit_kernel(const ResUnitArgs a) {
   // instead (see load_x), register room permitting.
   constexpr bool kEarlyH = !XH && WMB * WNB <= 8;
   constexpr bool kChunkH = XH && WMB * WNB <= VOC_RU_CHUNK_H_MAX;
-  f4 hres[WMB][WNB];
+  typename HQuad<OP>::T hres[WMB][WNB];  // converted in the final epilogue
   auto load_h_block = [&](int mb) {
     const int m = wm * WMB * 16 + mb * 16 + lg * 4;
     const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
@@ -132,7 +132,7 @@ void res_unit_kernel(const ResUnitArgs a) {
       // Unconditional load (frame clamped into the row; clamped values
       // are never stored), so the prefetch is not serialised.
       const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, Lv - 1);
-      hres[mb][nb] = load_h4<OP>(a.h_in, hbase + static_cast<int64_t>(n) * kHChunk);
+      hres[mb][nb] = load_h4_raw<OP>(a.h_in, hbase + static_cast<int64_t>(n) * kHChunk);
     }
   };
   auto load_h = [&]() {
@@ -147,7 +147,7 @@ void res_unit_kernel(const ResUnitArgs a) {
   // so each thread stages the same 16 / ES channels of every chunk row.
   constexpr int HV = XH ? 16 / ES / 4 : 1;  // fp32 h quads per staging unit
   uint4 xr[XH ? 1 : XU], wr[WU];
-  f4 xh[XH ? XU : 1][HV];
+  typename HQuad<OP>::T xh[XH ? XU : 1][HV];  // raw h, converted at staging
   // Snake1 parameters (scale[C], h[C]) in LDS: read at staging time
   // rather than held in registers across the matrix work.
   float* P1 = reinterpret_cast<float*>(smem + LDS_T);
@@ -171,8 +171,8 @@ void res_unit_kernel(const ResUnitArgs a) {
         const bool in = r < xrows && t >= -a.lb && t < Lv;
 #pragma unroll
         for (int v = 0; v < HV; ++v)
-          xh[u][v] = in ? load_h4<OP>(a.h_in, hp + static_cast<int64_t>(t) * kHChunk + 4 * v)
-                        : f4{0.f, 0.f, 0.f, 0.f};
+          xh[u][v] = in ? load_h4_raw<OP>(a.h_in, hp + static_cast<int64_t>(t) * kHChunk + 4 * v)
+                        : typename HQuad<OP>::T{};
       }
       // Residual rows of this chunk's channels, while the X lines are in L2.
       if constexpr (kChunkH) {
@@ -227,8 +227,9 @@ void res_unit_kernel(const ResUnitArgs a) {
         for (int q = 0; q < HV; ++q) {
           const f4 ps = *reinterpret_cast<const f4*>(P1 + xch + 4 * q);
           const f4 ph = *reinterpret_cast<const f4*>(P1 + C + xch + 4 * q);
+          const f4 xq = h4_to_f4<OP>(xh[u][q]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[4 * q + e] = snake_f32(xh[u][q][e], ps[e], ph[e]);
+          for (int e = 0; e < 4; ++e) y[4 * q + e] = snake_f32(xq[e], ps[e], ph[e]);
         }
         if constexpr (OP == OP_BF16) {
           v.x = pack_bf16x2(y[0], y[1]);
@@ -428,7 +429,7 @@ void res_unit_kernel(const ResUnitArgs a) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int mq = m + 16 * q;
-          f4 v = acc[mp + q][nb] + b2[q] + hres[mp + q][nb];
+          f4 v = acc[mp + q][nb] + b2[q] + h4_to_f4<OP>(hres[mp + q][nb]);
           if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
           if (a.store_h && ok) {
             f4 hv = v;
@@ -484,7 +485,7 @@ void res_unit_kernel(const ResUnitArgs a) {
         const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
         if (n >= Lv) continue;
         const int64_t hidx = hbase + static_cast<int64_t>(n) * kHChunk;
-        f4 v = acc[mb][nb] + b2 + hres[mb][nb];
+        f4 v = acc[mb][nb] + b2 + h4_to_f4<OP>(hres[mb][nb]);
         if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
         f4 hv = v;
         if (a.hs_scale) {
@@ -590,14 +591,6 @@ int res_unit_tile(int op, int C, bool big) {
                                     : launch_ru<OP_BF16>(probe, big, nullptr, &bn);
   return e == hipSuccess ? bn : 0;
 }
-
-// Widths whose units take Snake1 from h (x_from_h).  Per-layer kernel traces
-// of the full workloads on MI355X: the ConvTranspose1d feeding such a block
-// saves 15-23 % (no operand tensor written) and the first two units 2-14 %,
-// while the last unit of a block is 3-9 % slower (Snake1 at staging sits
-// between barriers).  A net gain at every width but bf16 C = 96, whose
-// large tile spills registers with the raw h staging.
-bool res_unit_from_h_ok(int op, int C) { return !(op == OP_BF16 && C == 96); }
 
 hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s) {
   int bn = 0;

@@ -124,7 +124,6 @@ struct ResUnitArgs {
 // fused kernel for width C, or 0 if there is no fused instance for (op, C);
 // big selects the large-frame tile of that width (0 if it has none).
 // Whether units of width C run with x_from_h (Snake1 computed in the kernel).
-bool res_unit_from_h_ok(int op, int C);
 hipError_t launch_res_unit(int op, const ResUnitArgs& a, bool big, hipStream_t s);
 
 // Weight-norm fold + cast + repack, one workgroup per axis-0 slice.
