@@ -516,12 +516,12 @@ void res_unit_kernel(const ResUnitArgs a) {
 // the pair on the batched bf16 windows).
 // Per dtype and width: a large-frame tile, the fastest in per-layer traces of
 // the full workloads on MI355X, and a half-frame tile for launches too short
-// to give the large one two workgroups per CU.  The bf16 64-channel large tile
-// trades frames for occupancy: 128 frames, one tap per LDS group and 128
-// VGPRs give four workgroups per CU (16 waves), whose staging, Snake and
-// epilogue phases then overlap other workgroups' matrix phases; 10 % faster
-// per unit than 256 frames at two workgroups.  Overridable at build time for
-// sweeps.
+// to give the large one two workgroups per CU.  The 64-channel large tiles
+// trade frames for occupancy: 128 frames, one or two taps per LDS group and
+// at most 128 VGPRs give four workgroups per CU (16 waves), whose staging,
+// Snake and epilogue phases then overlap other workgroups' matrix phases;
+// 10 % (bf16) and 4 % (fp32) faster per unit than 256 frames at two
+// workgroups.  Overridable at build time for sweeps.
 #ifndef VOC_F32_RU64
 #define VOC_F32_RU64 4, 2, 1, 4, 1, 4
 #endif
@@ -532,7 +532,7 @@ void res_unit_kernel(const ResUnitArgs a) {
 #define VOC_F32_RU128 4, 4, 2, 2, 4, 2
 #endif
 #ifndef VOC_BF_RU64
-#define VOC_BF_RU64 4, 2, 1, 4, 1, 4
+#define VOC_BF_RU64 4, 2, 1, 4, 2, 4
 #endif
 #ifndef VOC_BF_RU96
 #define VOC_BF_RU96 6, 4, 1, 4, 7, 2
