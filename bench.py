@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -48,10 +49,13 @@ KERNEL_SOURCES = ["dac_vocoder_decoding_amd/csrc/conv_gemm.hip",
 
 
 def kernel_source_sha() -> str:
+    """Hash of the kernel sources' code: comments and layout are dropped, so
+    stored counter readings stay attached to the code they were taken on."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = re.sub(r"//[^\n]*", "", f.read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

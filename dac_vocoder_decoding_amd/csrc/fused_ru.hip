@@ -56,7 +56,9 @@ namespace voc {
 #define VOC_RU_PINGPONG 1
 #endif
 
-// MINB: workgroups per CU the register allocator must leave room for.
+// MINB: waves per SIMD the register allocator must leave room for (the
+// launch bound's second argument); for a four-wave workgroup that is the
+// number of workgroups per CU.
 template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG, bool XH, int MINB>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB)
 void res_unit_kernel(const ResUnitArgs a) {
@@ -508,7 +510,7 @@ void res_unit_kernel(const ResUnitArgs a) {
 }
 
 // Instances: channel width C -> {m-blocks per wave, n-blocks, waves M, waves N,
-// taps per group, workgroups per CU}.
+// taps per group, waves per SIMD}.
 // Only widths where one fused launch beats the conv1 + conv2 pair on MI355X
 // (per-layer kernel traces): at C >= 256 the whole-C tile leaves too few
 // frames per workgroup (LDS holds U for all C), and the pair is faster (a
