@@ -71,7 +71,10 @@ void res_unit_kernel(const ResUnitArgs a) {
   constexpr int NG = (7 + TG - 1) / TG;        // tap groups per channel chunk
   constexpr int WROWS = TG * C;
   constexpr int NCH = C / CH;                  // channel chunks
-  constexpr bool kDB = VOC_RU_DB && WAVES_M * WAVES_N == 8;
+  // Eight-wave instances at two workgroups per CU (MINB 4) keep one buffer
+  // and no held residual rows: their registers must fit 128 VGPRs.
+  constexpr bool kTwoWG8 = WAVES_M * WAVES_N == 8 && MINB > 2;
+  constexpr bool kDB = VOC_RU_DB && WAVES_M * WAVES_N == 8 && !kTwoWG8;
   constexpr int NB = kDB ? 2 : 1;              // stage-1 LDS buffers
   constexpr int S1 = NB * (XROWS + WROWS) * kRowBytes;
   constexpr int UB = NCH * BN * kRowBytes;     // U tile: [NCH][BN] rows
@@ -124,7 +127,7 @@ void res_unit_kernel(const ResUnitArgs a) {
   // With XH the rows of each channel chunk are read right after its X tile
   // instead (see load_x), register room permitting.
   constexpr bool kEarlyH = !XH && WMB * WNB <= 8;
-  constexpr bool kChunkH = XH && WMB * WNB <= VOC_RU_CHUNK_H_MAX;
+  constexpr bool kChunkH = XH && WMB * WNB <= VOC_RU_CHUNK_H_MAX && !kTwoWG8;
   typename HQuad<OP>::T hres[WMB][WNB];  // converted in the final epilogue
   auto load_h_block = [&](int mb) {
     const int m = wm * WMB * 16 + mb * 16 + lg * 4;
@@ -519,11 +522,13 @@ void res_unit_kernel(const ResUnitArgs a) {
 // Per dtype and width: a large-frame tile, the fastest in per-layer traces of
 // the full workloads on MI355X, and a half-frame tile for launches too short
 // to give the large one two workgroups per CU.  The 64-channel large tiles
-// trade frames for occupancy: 128 frames, one or two taps per LDS group and
-// at most 128 VGPRs give four workgroups per CU (16 waves), whose staging,
-// Snake and epilogue phases then overlap other workgroups' matrix phases;
-// 10 % (bf16) and 4 % (fp32) faster per unit than 256 frames at two
-// workgroups.  Overridable at build time for sweeps.
+// are sized for occupancy: at most 128 VGPRs give 16 waves per CU, whose
+// staging, Snake and epilogue phases then overlap other workgroups' matrix
+// phases.  fp32: four four-wave workgroups of 128 frames (4 % faster per unit
+// than 256 frames at two workgroups); bf16: two eight-wave workgroups of 256
+// frames, one stage-1 buffer (22 % faster than 256 frames at one four-wave
+// workgroup pair, 12 % faster than four 128-frame workgroups).  Overridable
+// at build time for sweeps.
 #ifndef VOC_F32_RU64
 #define VOC_F32_RU64 4, 2, 1, 4, 1, 4
 #endif
@@ -534,7 +539,7 @@ void res_unit_kernel(const ResUnitArgs a) {
 #define VOC_F32_RU128 4, 4, 2, 2, 4, 2
 #endif
 #ifndef VOC_BF_RU64
-#define VOC_BF_RU64 4, 2, 1, 4, 2, 4
+#define VOC_BF_RU64 2, 4, 2, 4, 2, 4
 #endif
 #ifndef VOC_BF_RU96
 #define VOC_BF_RU96 6, 4, 1, 4, 7, 2
