@@ -22,10 +22,11 @@
 //   XH = false  S is an operand tensor written by the producer's epilogue,
 //               and h is updated in place;
 //   XH = true   S = Snake1(h_in) is computed here while the X tile is staged
-//               from the fp32 residual stream, and the result goes to a
+//               from the residual stream, and the result goes to a
 //               second buffer h (tiles read neighbouring frames of h_in, so
 //               the update cannot be in place).  The producer then writes no
-//               operand tensor: per channel-frame the unit moves 8 bytes of h
+//               operand tensor: per channel-frame the unit moves 2 x 4 (fp32)
+//               or 2 x 2 (fp16) bytes of h
 //               (read + write) instead of h plus two operand passes, and the
 //               residual rows of each channel chunk are read right after that
 //               chunk's X tile, from lines the X loads have just brought into
@@ -150,7 +151,7 @@ void res_unit_kernel(const ResUnitArgs a) {
   // Staging unit idx covers frame tfirst + unit_row(idx) and the 16 operand
   // bytes at unit_col(idx) of the chunk row; unit_col(idx) == lg for every u,
   // so each thread stages the same 16 / ES channels of every chunk row.
-  constexpr int HV = XH ? 16 / ES / 4 : 1;  // fp32 h quads per staging unit
+  constexpr int HV = XH ? 16 / ES / 4 : 1;  // h quads per staging unit
   uint4 xr[XH ? 1 : XU], wr[WU];
   typename HQuad<OP>::T xh[XH ? XU : 1][HV];  // raw h, converted at staging
   // Snake1 parameters (scale[C], h[C]) in LDS: read at staging time

@@ -5,7 +5,9 @@
 //   operand tensors (matrix-core inputs, fp32 or bf16):
 //       [row][C / CH][T][CH] with CH = 64 bytes / element size
 //       (16 fp32 or 32 bf16 channels per chunk)
-//   residual stream h (always fp32): [row][C / 16][T][16]
+//   residual stream h: [row][C / 16][T][16], fp32 elements with fp32
+//       operands, fp16 elements with bf16 operands (arithmetic on h is fp32;
+//       the float* members below then point at fp16 data)
 // One 64-byte chunk row holds CH consecutive channels of one time frame, so a
 // GEMM tile of a channel chunk over consecutive frames is one contiguous span.
 //
