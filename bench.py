@@ -78,7 +78,8 @@ def workload_name(cfg: dict) -> str:
                 f"{cfg['latent_channels']}, {cfg['act']}")
     af = ", alias-free Snake (2x up / Snake / 2x down)" if cfg.get("af_snake") else ""
     out = ", 2 output channels" if cfg.get("out_channels", 1) == 2 else ""
-    return (f"{cfg['name']}: latent {lat} {cfg['dtype']}, {proj}widths {w}, strides {s}, "
+    terms = ", two-term bf16 operands" if cfg.get("operand_terms", 0) == 2 else ""
+    return (f"{cfg['name']}: latent {lat} {cfg['dtype']}{terms}, {proj}widths {w}, strides {s}, "
             f"{cfg['act']}{af}{out}{tile}")
 
 
@@ -140,6 +141,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip the per-launch event profiler (roofline becomes null)")
+    ap.add_argument("--operand-terms", type=int, default=1, choices=(1, 2),
+                    help="2: two-term bf16 matrix-core operands (bf16 workloads)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the decode, run the library's plain copy kernel 3 times "
                          "over MIB MiB (a known byte count for HBM counter calibration)")
@@ -155,6 +158,11 @@ def main() -> int:
     from dac_vocoder_decoding_amd import vocoder as V
 
     cfg = I.config(args.config)
+    if args.operand_terms == 2:
+        if cfg["dtype"] != "bf16":
+            print("--operand-terms 2 applies to the bf16 workloads", file=sys.stderr)
+            return 2
+        cfg = dict(cfg, name=cfg["name"] + "_two_term", operand_terms=2)
     tensors = I.make_weights(cfg)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

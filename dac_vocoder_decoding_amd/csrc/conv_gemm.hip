@@ -50,8 +50,12 @@ namespace voc {
 // residual convs) so that profilers report them apart.  TAG 2 is the
 // strided conv: its input rows are read through phase streams (a runtime
 // stride; 1 elsewhere).
-template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG, int NS>
+// H32: the residual stream h (res, h_out) holds fp32 elements with bf16
+// operands (decoders with two-term operands); otherwise its element type
+// follows the operands (fp32, or fp16 with bf16).
+template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG, int NS, bool H32>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
+  constexpr int HO = H32 ? OP_F32 : OP;
   constexpr int CH = OpT<OP>::CH;
   constexpr int ES = OpT<OP>::ES;
   constexpr int BM = WAVES_M * WMB * 16;
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   // loads are unconditional (row and frame clamped into range; clamped
   // values are never stored): conditional loads make the compiler wait for
   // each one at the branch join, which serialises the prefetch.
-  typename HQuad<OP>::T rres[WMB][WNB];  // converted in the epilogue
+  typename HQuad<HO>::T rres[WMB][WNB];  // converted in the epilogue
   if constexpr (TAPS == 1) {
     if (a.res) {
 #pragma unroll
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb) {
           const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, Lout - 1);
-          rres[mb][nb] = load_h4_raw<OP>(a.res, hbase + static_cast<int64_t>(n) * kHChunk);
+          rres[mb][nb] = load_h4_raw<HO>(a.res, hbase + static_cast<int64_t>(n) * kHChunk);
         }
       }
     }
@@ -292,13 +296,14 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       }
       const int oc = o - lg * 4;                            // chunk's first channel
       const int cofs = (lg & 1) * 16 + (lg & 2) * 4;        // this lane's 8 channels
-      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout + oc) * a.T_out + cofs;
+      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout * (a.s_terms == 2 ? 2 : 1) + oc) * a.T_out + cofs;
+      const int64_t slo = static_cast<int64_t>(a.Cout) * a.T_out;  // low-term planes (two terms)
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
         const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
         const int tau = n * a.ups + ph - a.crop;
         const bool ok = n < a.N && tau >= 0 && tau < Lout;
-        u4v pk;  // packed Snake operand: blocks 0 and 1 (2 dwords each)
+        u4v pk, pl;  // packed Snake operand (and its low term): blocks 0 and 1 (2 dwords each)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           f4 v = acc[mp + q][nb] + bias[q];
@@ -307,11 +312,11 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
                                static_cast<int64_t>(tau) * kHChunk;
           if (a.res) {
             if constexpr (TAPS == 1)
-              v += h4_to_f4<OP>(rres[mp + q][nb]);
+              v += h4_to_f4<HO>(rres[mp + q][nb]);
             else if (ok)
-              v += load_h4<OP>(a.res, hidx);
+              v += load_h4<HO>(a.res, hidx);
           }
-          if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
+          if (a.s_out || a.hs_scale) v = round_h4<HO>(v);  // a Snake follows: start from the stored h
           if (a.h_out && ok) {
             f4 hv = v;
             if (a.hs_scale) {
@@ -320,25 +325,45 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
               hv[2] = snake_f32(v[2], hsc[q][2], hsh[q][2]);
               hv[3] = snake_f32(v[3], hsc[q][3], hsh[q][3]);
             }
-            store_h4<OP>(a.h_out, hidx, hv);
+            store_h4<HO>(a.h_out, hidx, hv);
           }
-          pk[2 * q] = pack_bf16x2(snake_f32(v[0], sal[q][0], sinv[q][0]), snake_f32(v[1], sal[q][1], sinv[q][1]));
-          pk[2 * q + 1] = pack_bf16x2(snake_f32(v[2], sal[q][2], sinv[q][2]), snake_f32(v[3], sal[q][3], sinv[q][3]));
+          f4 sv;
+          sv[0] = snake_f32(v[0], sal[q][0], sinv[q][0]);
+          sv[1] = snake_f32(v[1], sal[q][1], sinv[q][1]);
+          sv[2] = snake_f32(v[2], sal[q][2], sinv[q][2]);
+          sv[3] = snake_f32(v[3], sal[q][3], sinv[q][3]);
+          pk[2 * q] = pack_bf16x2(sv[0], sv[1]);
+          pk[2 * q + 1] = pack_bf16x2(sv[2], sv[3]);
+          if (a.s_terms == 2) {
+            const f4 lv = bf16_lo4(sv);
+            pl[2 * q] = pack_bf16x2(lv[0], lv[1]);
+            pl[2 * q + 1] = pack_bf16x2(lv[2], lv[3]);
+          }
         }
         if (a.s_out) {  // uniform: every lane takes part in the exchange
           // Even lg keeps block 0 and takes its partner's block 0; odd lg
           // keeps block 1 and takes its partner's block 1.
           const bool odd = lg & 1;
-          const uint32_t s0 = __shfl_xor(static_cast<int>(odd ? pk[0] : pk[2]), 16);
-          const uint32_t s1 = __shfl_xor(static_cast<int>(odd ? pk[1] : pk[3]), 16);
-          u4v out;
-          if (odd) {
-            out[0] = s0; out[1] = s1; out[2] = pk[2]; out[3] = pk[3];
-          } else {
-            out[0] = pk[0]; out[1] = pk[1]; out[2] = s0; out[3] = s1;
-          }
+          auto exchange = [&](const u4v& p) {
+            const uint32_t s0 = __shfl_xor(static_cast<int>(odd ? p[0] : p[2]), 16);
+            const uint32_t s1 = __shfl_xor(static_cast<int>(odd ? p[1] : p[3]), 16);
+            u4v out;
+            if (odd) {
+              out[0] = s0; out[1] = s1; out[2] = p[2]; out[3] = p[3];
+            } else {
+              out[0] = p[0]; out[1] = p[1]; out[2] = s0; out[3] = s1;
+            }
+            return out;
+          };
+          const u4v out = exchange(pk);
           if (ok)
             *reinterpret_cast<u4v*>(static_cast<uint16_t*>(a.s_out) + sbase + static_cast<int64_t>(tau) * CH) = out;
+          if (a.s_terms == 2) {
+            const u4v outl = exchange(pl);
+            if (ok)
+              *reinterpret_cast<u4v*>(static_cast<uint16_t*>(a.s_out) + sbase + slo +
+                                      static_cast<int64_t>(tau) * CH) = outl;
+          }
         }
       }
     }
@@ -361,7 +386,8 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
         hsh = *reinterpret_cast<const f4*>(a.hs_h + o);
       }
       const int64_t hbase = (static_cast<int64_t>(row) * a.Cout + (o & ~15)) * a.T_out + (o & 15);
-      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout + (o / CH) * CH) * a.T_out + (o % CH);
+      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout * (a.s_terms == 2 ? 2 : 1) + (o / CH) * CH) * a.T_out + (o % CH);
+      const int64_t slo = static_cast<int64_t>(a.Cout) * a.T_out;  // low-term planes (two terms)
   #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
         const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
@@ -372,11 +398,11 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
         const int64_t hidx = hbase + static_cast<int64_t>(tau) * kHChunk;
         if (a.res) {
           if constexpr (TAPS == 1)
-            v += h4_to_f4<OP>(rres[mb][nb]);
+            v += h4_to_f4<HO>(rres[mb][nb]);
           else
-            v += load_h4<OP>(a.res, hidx);
+            v += load_h4<HO>(a.res, hidx);
         }
-        if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
+        if (a.s_out || a.hs_scale) v = round_h4<HO>(v);  // a Snake follows: start from the stored h
         if (a.h_out) {
           f4 hv = v;
           if (a.hs_scale) {
@@ -385,7 +411,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
             hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
             hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
           }
-          store_h4<OP>(a.h_out, hidx, hv);
+          store_h4<HO>(a.h_out, hidx, hv);
         }
         if (a.s_out) {
           f4 sv;
@@ -394,6 +420,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
           sv[2] = snake_f32(v[2], sal[2], sinv[2]);
           sv[3] = snake_f32(v[3], sal[3], sinv[3]);
           store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(tau) * CH, sv);
+          if (a.s_terms == 2) store_op4<OP>(a.s_out, sbase + slo + static_cast<int64_t>(tau) * CH, bf16_lo4(sv));
         }
       }
     }
@@ -444,7 +471,7 @@ template <int OP, int TAPS> struct Stages {
   static constexpr int v = (OP == OP_F32 ? f : b)[TAPS == 7 ? 0 : TAPS == 1 ? 2 : 1];  // 2 and 3 taps alike
 };
 
-template <int OP, int TAPS, int TAG>
+template <int OP, int TAPS, int TAG, bool H32 = false>
 static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
   constexpr int NS = Stages<OP, TAPS>::v;
   const int total = a.n_tiles * a.m_tiles * a.rows;
@@ -452,7 +479,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
   switch (variant) {
 #define VOC_CASE(V, A, B, C, D)                                                            \
   case V:                                                                                  \
-    hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS>), grid, block, 0, s, a); \
+    hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, H32>), grid, block, 0, s, a); \
     break;
     VOC_CASE(CV_64x256, 4, 4, 1, 4)
     VOC_CASE(CV_96x256, 6, 4, 1, 4)
@@ -461,7 +488,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 #define VOC_CASE(V, A, B, C, D)                                                              \
   case V:                                                                                    \
     if constexpr (TAPS == 1 || TAPS == 2) {                                                  \
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS>), grid, block, 0, s, a); \
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, H32>), grid, block, 0, s, a); \
       break;                                                                                 \
     }                                                                                        \
     return hipErrorInvalidValue;
@@ -472,7 +499,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 #define VOC_CASE(V, A, B, C, D)                                                              \
   case V:                                                                                    \
     if constexpr (TAPS == 7 || (OP == OP_F32 && (TAPS == 1 || TAPS == 2))) {                 \
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS>), grid, block, 0, s, a); \
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, H32>), grid, block, 0, s, a); \
       break;                                                                                 \
     }                                                                                        \
     return hipErrorInvalidValue;
@@ -489,6 +516,19 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 
 template <int OP>
 static hipError_t launch_op(int taps, int variant, int tag, const ConvArgs& a, hipStream_t s) {
+  if (a.h32) {  // bf16 operands with an fp32 residual stream: the decoder's convs only
+    if constexpr (OP == OP_BF16) {
+      if (a.in_stride > 1 || (tag != 0 && tag != 1)) return hipErrorInvalidValue;
+      switch (taps) {
+        case 7:
+          return tag == 1 ? launch_taps<OP, 7, 1, true>(variant, a, s) : launch_taps<OP, 7, 0, true>(variant, a, s);
+        case 2: return launch_taps<OP, 2, 0, true>(variant, a, s);
+        case 1: return launch_taps<OP, 1, 0, true>(variant, a, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   switch (taps) {
     case 7:
       return tag == 1 ? launch_taps<OP, 7, 1>(variant, a, s) : launch_taps<OP, 7, 0>(variant, a, s);

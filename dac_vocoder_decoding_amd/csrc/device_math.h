@@ -63,6 +63,17 @@ __device__ __forceinline__ void store_op4<1>(void* base, int64_t idx, f4 v) {
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = p;
 }
 
+// Two-term bf16 operands: x is carried as hi = bf16(x) and lo = bf16(x - hi)
+// (the difference is exact in fp32), and both terms meet the same bf16
+// weights; the pair holds x to about 2^-17 of its magnitude.  bf16_lo4 gives
+// the low term's fp32 value before its own rounding.
+__device__ __forceinline__ f4 bf16_lo4(f4 v) {
+  f4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = v[e] - bf16_round(v[e]);
+  return r;
+}
+
 // The residual stream h, in the same [row][C/16][T][16] element layout for
 // both operand dtypes: fp32 elements for fp32 operands, fp16 elements for
 // bf16 operands (16-bit activations, at fp16's 11-bit mantissa: rounding h

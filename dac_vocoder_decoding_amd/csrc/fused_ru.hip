@@ -59,8 +59,11 @@ namespace voc {
 
 // MINB: waves per SIMD the register allocator must leave room for (the
 // launch bound's second argument); for a four-wave workgroup that is the
-// number of workgroups per CU.
-template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG, bool XH, int MINB>
+// number of workgroups per CU.  TERMS = 2 (bf16): two-term operands (hi and
+// lo planes, see bf16_lo4): the conv1 and conv2 reductions run over 2 x C
+// channels, the low-term channels meeting a second copy of each weight
+// chunk, and the operand written for a consumer holds both terms.
+template <int OP, int WMB, int WNB, int WAVES_M, int WAVES_N, int TG, bool XH, int MINB, int TERMS>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB)
 void res_unit_kernel(const ResUnitArgs a) {
   constexpr int NTH = 64 * WAVES_M * WAVES_N;  // threads per workgroup
@@ -72,13 +75,15 @@ void res_unit_kernel(const ResUnitArgs a) {
   constexpr int NG = (7 + TG - 1) / TG;        // tap groups per channel chunk
   constexpr int WROWS = TG * C;
   constexpr int NCH = C / CH;                  // channel chunks
+  constexpr int KCH = TERMS * NCH;             // reduction chunks (the low terms after the high)
+  constexpr int HO = TERMS == 2 ? OP_F32 : OP;  // residual-stream element type (fp32 with two terms)
   // Eight-wave instances at two workgroups per CU (MINB 4) keep one buffer
   // and no held residual rows: their registers must fit 128 VGPRs.
   constexpr bool kTwoWG8 = WAVES_M * WAVES_N == 8 && MINB > 2;
   constexpr bool kDB = VOC_RU_DB && WAVES_M * WAVES_N == 8 && !kTwoWG8;
   constexpr int NB = kDB ? 2 : 1;              // stage-1 LDS buffers
   constexpr int S1 = NB * (XROWS + WROWS) * kRowBytes;
-  constexpr int UB = NCH * BN * kRowBytes;     // U tile: [NCH][BN] rows
+  constexpr int UB = KCH * BN * kRowBytes;     // U tile: [KCH][BN] rows
   constexpr int S2 = UB + C * kRowBytes;
   constexpr int LDS_T = S1 > S2 ? S1 : S2;
   constexpr int LDS = LDS_T + (XH ? 2 * C * 4 : 0);  // + Snake1 parameters
@@ -107,7 +112,7 @@ void res_unit_kernel(const ResUnitArgs a) {
   const int xrows = BN + 6 * d;
   const int tfirst = n0 - a.pad;  // tap j reads frame n + j*d - pad
   const unsigned char* xrow = static_cast<const unsigned char*>(a.x) +
-                              static_cast<int64_t>(row) * C * a.T * ES;
+                              static_cast<int64_t>(row) * TERMS * C * a.T * ES;
   const int64_t xplane = static_cast<int64_t>(a.T) * kChunkBytes;
   const unsigned char* w1 = static_cast<const unsigned char*>(a.w1);
   const unsigned char* w2 = static_cast<const unsigned char*>(a.w2);
@@ -129,7 +134,7 @@ void res_unit_kernel(const ResUnitArgs a) {
   // instead (see load_x), register room permitting.
   constexpr bool kEarlyH = !XH && WMB * WNB <= 8;
   constexpr bool kChunkH = XH && WMB * WNB <= VOC_RU_CHUNK_H_MAX && !kTwoWG8;
-  typename HQuad<OP>::T hres[WMB][WNB];  // converted in the final epilogue
+  typename HQuad<HO>::T hres[WMB][WNB];  // converted in the final epilogue
   auto load_h_block = [&](int mb) {
     const int m = wm * WMB * 16 + mb * 16 + lg * 4;
     const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
@@ -138,7 +143,7 @@ void res_unit_kernel(const ResUnitArgs a) {
       // Unconditional load (frame clamped into the row; clamped values
       // are never stored), so the prefetch is not serialised.
       const int n = min(n0 + wn * WNB * 16 + nb * 16 + lr, Lv - 1);
-      hres[mb][nb] = load_h4_raw<OP>(a.h_in, hbase + static_cast<int64_t>(n) * kHChunk);
+      hres[mb][nb] = load_h4_raw<HO>(a.h_in, hbase + static_cast<int64_t>(n) * kHChunk);
     }
   };
   auto load_h = [&]() {
@@ -153,11 +158,12 @@ void res_unit_kernel(const ResUnitArgs a) {
   // so each thread stages the same 16 / ES channels of every chunk row.
   constexpr int HV = XH ? 16 / ES / 4 : 1;  // h quads per staging unit
   uint4 xr[XH ? 1 : XU], wr[WU];
-  typename HQuad<OP>::T xh[XH ? XU : 1][HV];  // raw h, converted at staging
+  typename HQuad<HO>::T xh[XH ? XU : 1][HV];  // raw h, converted at staging
   // Snake1 parameters (scale[C], h[C]) in LDS: read at staging time
   // rather than held in registers across the matrix work.
   float* P1 = reinterpret_cast<float*>(smem + LDS_T);
   int xch = 0;  // first channel of this thread's staging units (chunk of the last load_x)
+  bool xlo = false;  // the last load_x staged a low-term chunk (two terms)
   if constexpr (XH) {
     for (int i = tid; i < C / 4; i += NTH) {
       reinterpret_cast<f4*>(P1)[i] = reinterpret_cast<const f4*>(a.a1_scale)[i];
@@ -167,8 +173,9 @@ void res_unit_kernel(const ResUnitArgs a) {
   }
   auto load_x = [&](int c) {
     if constexpr (XH) {
-      const int ch = c * CH + lg * (16 / ES);
+      const int ch = (TERMS == 2 && c >= NCH ? c - NCH : c) * CH + lg * (16 / ES);
       xch = ch;
+      xlo = TERMS == 2 && c >= NCH;
       const int64_t hp = (static_cast<int64_t>(row) * C + (ch & ~15)) * a.T + (ch & 15);
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
@@ -177,8 +184,8 @@ void res_unit_kernel(const ResUnitArgs a) {
         const bool in = r < xrows && t >= -a.lb && t < Lv;
 #pragma unroll
         for (int v = 0; v < HV; ++v)
-          xh[u][v] = in ? load_h4_raw<OP>(a.h_in, hp + static_cast<int64_t>(t) * kHChunk + 4 * v)
-                        : typename HQuad<OP>::T{};
+          xh[u][v] = in ? load_h4_raw<HO>(a.h_in, hp + static_cast<int64_t>(t) * kHChunk + 4 * v)
+                        : typename HQuad<HO>::T{};
       }
       // Residual rows of this chunk's channels, while the X lines are in L2.
       if constexpr (kChunkH) {
@@ -233,9 +240,15 @@ void res_unit_kernel(const ResUnitArgs a) {
         for (int q = 0; q < HV; ++q) {
           const f4 ps = *reinterpret_cast<const f4*>(P1 + xch + 4 * q);
           const f4 ph = *reinterpret_cast<const f4*>(P1 + C + xch + 4 * q);
-          const f4 xq = h4_to_f4<OP>(xh[u][q]);
+          const f4 xq = h4_to_f4<HO>(xh[u][q]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[4 * q + e] = snake_f32(xq[e], ps[e], ph[e]);
+        }
+        if constexpr (TERMS == 2) {
+          if (xlo) {
+#pragma unroll
+            for (int k = 0; k < 4 * HV; ++k) y[k] -= bf16_round(y[k]);
+          }
         }
         if constexpr (OP == OP_BF16) {
           v.x = pack_bf16x2(y[0], y[1]);
@@ -283,22 +296,22 @@ void res_unit_kernel(const ResUnitArgs a) {
     store_w(Ws);
     if (NG > 1) {
       load_w(0, 1);
-    } else if (NCH > 1) {
+    } else if (KCH > 1) {
       load_x(1);
       load_w(1, 0);
     }
     __syncthreads();
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < KCH; ++c) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const int p = c * NG + g;
         const int c1 = g + 1 < NG ? c : c + 1, g1 = g + 1 < NG ? g + 1 : 0;
         auto stage_next = [&]() {
-          if (c1 < NCH) {
+          if (c1 < KCH) {
             if (g1 == 0) store_x(Xs + (c1 & 1) * XROWS * kRowBytes);
             store_w(Ws + ((p + 1) & 1) * WROWS * kRowBytes);
             const int c2 = g1 + 1 < NG ? c1 : c1 + 1, g2 = g1 + 1 < NG ? g1 + 1 : 0;
-            if (c2 < NCH) {
+            if (c2 < KCH) {
               if (g2 == 0) load_x(c2);
               load_w(c2, g2);
             }
@@ -315,7 +328,7 @@ void res_unit_kernel(const ResUnitArgs a) {
       }
     }
   } else {
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < KCH; ++c) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if (g == 0) store_x(Xs);
@@ -323,7 +336,7 @@ void res_unit_kernel(const ResUnitArgs a) {
         __syncthreads();
         if (g + 1 < NG) {
           load_w(c, g + 1);
-        } else if (c + 1 < NCH) {
+        } else if (c + 1 < KCH) {
           load_x(c + 1);
           load_w(c + 1, 0);
         }
@@ -371,12 +384,14 @@ void res_unit_kernel(const ResUnitArgs a) {
       v[2] = snake_f32(v[2], sc[2], hh[2]);
       v[3] = snake_f32(v[3], sc[3], hh[3]);
       store_op4<OP>(ubase + lds_off(nl, ub >> 4), 0, v);
+      if constexpr (TERMS == 2)  // the low terms: chunk rows NCH.. of the U tile
+        store_op4<OP>(ubase + NCH * BN * kRowBytes + lds_off(nl, ub >> 4), 0, bf16_lo4(v));
       acc[mb][nb] = f4{0.f, 0.f, 0.f, 0.f};
     }
   }
 
   // ------------------------------------------------------------ stage 2
-  for (int c = 0; c < NCH; ++c) {
+  for (int c = 0; c < KCH; ++c) {
 #pragma unroll
     for (int u = 0; u < W2U; ++u) {
       const int idx = tid + u * NTH;
@@ -384,7 +399,7 @@ void res_unit_kernel(const ResUnitArgs a) {
       if (r < C) *reinterpret_cast<uint4*>(W2s + lds_off(r, unit_col(idx))) = w2r[u];
     }
     __syncthreads();
-    if (c + 1 < NCH) load_w2(c + 1);
+    if (c + 1 < KCH) load_w2(c + 1);
     uint4 A[WMB], B[WNB];
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb)
@@ -426,17 +441,18 @@ void res_unit_kernel(const ResUnitArgs a) {
       }
       const int mc = m - lg * 4;                       // chunk's first channel
       const int cofs = (lg & 1) * 16 + (lg & 2) * 4;   // this lane's 8 channels
-      const int64_t sbase = (static_cast<int64_t>(row) * C + mc) * a.T + cofs;
+      const int64_t sbase = (static_cast<int64_t>(row) * TERMS * C + mc) * a.T + cofs;
+      const int64_t slo = static_cast<int64_t>(C) * a.T;  // low-term planes (two terms)
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
         const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
         const bool ok = n < Lv;
-        u4v pk;
+        u4v pk, pl;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int mq = m + 16 * q;
-          f4 v = acc[mp + q][nb] + b2[q] + h4_to_f4<OP>(hres[mp + q][nb]);
-          if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
+          f4 v = acc[mp + q][nb] + b2[q] + h4_to_f4<HO>(hres[mp + q][nb]);
+          if (a.s_out || a.hs_scale) v = round_h4<HO>(v);  // a Snake follows: start from the stored h
           if (a.store_h && ok) {
             f4 hv = v;
             if (a.hs_scale) {
@@ -447,25 +463,45 @@ void res_unit_kernel(const ResUnitArgs a) {
             }
             const int64_t hi = (static_cast<int64_t>(row) * C + (mq & ~15)) * a.T + (mq & 15) +
                                static_cast<int64_t>(n) * kHChunk;
-            store_h4<OP>(a.h, hi, hv);
+            store_h4<HO>(a.h, hi, hv);
           }
           if (a.s_out) {
-            pk[2 * q] = pack_bf16x2(snake_f32(v[0], sc[q][0], hh[q][0]), snake_f32(v[1], sc[q][1], hh[q][1]));
-            pk[2 * q + 1] = pack_bf16x2(snake_f32(v[2], sc[q][2], hh[q][2]), snake_f32(v[3], sc[q][3], hh[q][3]));
+            f4 sv;
+            sv[0] = snake_f32(v[0], sc[q][0], hh[q][0]);
+            sv[1] = snake_f32(v[1], sc[q][1], hh[q][1]);
+            sv[2] = snake_f32(v[2], sc[q][2], hh[q][2]);
+            sv[3] = snake_f32(v[3], sc[q][3], hh[q][3]);
+            pk[2 * q] = pack_bf16x2(sv[0], sv[1]);
+            pk[2 * q + 1] = pack_bf16x2(sv[2], sv[3]);
+            if constexpr (TERMS == 2) {
+              const f4 lv = bf16_lo4(sv);
+              pl[2 * q] = pack_bf16x2(lv[0], lv[1]);
+              pl[2 * q + 1] = pack_bf16x2(lv[2], lv[3]);
+            }
           }
         }
         if (a.s_out) {  // uniform: every lane takes part in the exchange
           const bool odd = lg & 1;
-          const uint32_t s0 = __shfl_xor(static_cast<int>(odd ? pk[0] : pk[2]), 16);
-          const uint32_t s1 = __shfl_xor(static_cast<int>(odd ? pk[1] : pk[3]), 16);
-          u4v out;
-          if (odd) {
-            out[0] = s0; out[1] = s1; out[2] = pk[2]; out[3] = pk[3];
-          } else {
-            out[0] = pk[0]; out[1] = pk[1]; out[2] = s0; out[3] = s1;
-          }
+          auto exchange = [&](const u4v& p) {
+            const uint32_t s0 = __shfl_xor(static_cast<int>(odd ? p[0] : p[2]), 16);
+            const uint32_t s1 = __shfl_xor(static_cast<int>(odd ? p[1] : p[3]), 16);
+            u4v out;
+            if (odd) {
+              out[0] = s0; out[1] = s1; out[2] = p[2]; out[3] = p[3];
+            } else {
+              out[0] = p[0]; out[1] = p[1]; out[2] = s0; out[3] = s1;
+            }
+            return out;
+          };
+          const u4v out = exchange(pk);
           if (ok)
             *reinterpret_cast<u4v*>(static_cast<uint16_t*>(a.s_out) + sbase + static_cast<int64_t>(n) * CH) = out;
+          if constexpr (TERMS == 2) {
+            const u4v outl = exchange(pl);
+            if (ok)
+              *reinterpret_cast<u4v*>(static_cast<uint16_t*>(a.s_out) + sbase + slo + static_cast<int64_t>(n) * CH) =
+                  outl;
+          }
         }
       }
     }
@@ -485,14 +521,14 @@ void res_unit_kernel(const ResUnitArgs a) {
         hsh = *reinterpret_cast<const f4*>(a.hs_h + m);
       }
       const int64_t hbase = (static_cast<int64_t>(row) * C + (m & ~15)) * a.T + (m & 15);
-      const int64_t sbase = (static_cast<int64_t>(row) * C + (m / CH) * CH) * a.T + (m % CH);
+      const int64_t sbase = (static_cast<int64_t>(row) * TERMS * C + (m / CH) * CH) * a.T + (m % CH);
   #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
         const int n = n0 + wn * WNB * 16 + nb * 16 + lr;
         if (n >= Lv) continue;
         const int64_t hidx = hbase + static_cast<int64_t>(n) * kHChunk;
-        f4 v = acc[mb][nb] + b2 + h4_to_f4<OP>(hres[mb][nb]);
-        if (a.s_out || a.hs_scale) v = round_h4<OP>(v);  // a Snake follows: start from the stored h
+        f4 v = acc[mb][nb] + b2 + h4_to_f4<HO>(hres[mb][nb]);
+        if (a.s_out || a.hs_scale) v = round_h4<HO>(v);  // a Snake follows: start from the stored h
         f4 hv = v;
         if (a.hs_scale) {
           hv[0] = snake_f32(v[0], hsc[0], hsh[0]);
@@ -500,13 +536,16 @@ void res_unit_kernel(const ResUnitArgs a) {
           hv[2] = snake_f32(v[2], hsc[2], hsh[2]);
           hv[3] = snake_f32(v[3], hsc[3], hsh[3]);
         }
-        if (a.store_h) store_h4<OP>(a.h, hidx, hv);
+        if (a.store_h) store_h4<HO>(a.h, hidx, hv);
         if (a.s_out) {
           v[0] = snake_f32(v[0], sc[0], hh[0]);
           v[1] = snake_f32(v[1], sc[1], hh[1]);
           v[2] = snake_f32(v[2], sc[2], hh[2]);
           v[3] = snake_f32(v[3], sc[3], hh[3]);
           store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(n) * CH, v);
+          if constexpr (TERMS == 2)
+            store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(C) * a.T + static_cast<int64_t>(n) * CH,
+                          bf16_lo4(v));
         }
       }
     }
@@ -554,22 +593,43 @@ void res_unit_kernel(const ResUnitArgs a) {
 #define VOC_RU_(...) VOC_RU(__VA_ARGS__)
 template <int OP>
 static hipError_t launch_ru(const ResUnitArgs& a, bool big, hipStream_t s, int* bn) {
-#define VOC_RU(CW, BIG, A, B, WM, WN, TGV, MB)                                                          \
-  if (a.C == CW && big == BIG) {                                                                        \
-    *bn = WN * B * 16;                                                                                  \
-    if (a.n_tiles <= 0) return hipSuccess;                                                              \
-    if (a.x_from_h)                                                                                     \
-      hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, true, MB>), dim3(a.n_tiles * a.rows),  \
-                         dim3(64 * WM * WN), 0, s, a);                                                  \
-    else                                                                                                \
-      hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, false, MB>), dim3(a.n_tiles * a.rows), \
-                         dim3(64 * WM * WN), 0, s, a);                                                  \
-    return hipGetLastError();                                                                           \
+  if (a.terms < 0 || a.terms > 2 || (a.terms == 2 && OP != OP_BF16)) return hipErrorInvalidValue;
+  // With two-term operands the 96-channel large tile's U tile (2 x 3 chunks x
+  // 256 frames) would leave one workgroup per CU: the half-frame tile serves.
+  if (a.terms == 2 && a.C == 96) big = false;
+#define VOC_RU_T(A, B, WM, WN, TGV, MB, TM)                                                     \
+  if (a.x_from_h)                                                                                 \
+    hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, true, MB, TM>),                    \
+                       dim3(a.n_tiles * a.rows), dim3(64 * WM * WN), 0, s, a);                    \
+  else                                                                                            \
+    hipLaunchKernelGGL((res_unit_kernel<OP, A, B, WM, WN, TGV, false, MB, TM>),                   \
+                       dim3(a.n_tiles * a.rows), dim3(64 * WM * WN), 0, s, a);
+#define VOC_RU(CW, BIG, A, B, WM, WN, TGV, MB)                                                    \
+  if (a.C == CW && big == BIG) {                                                                  \
+    *bn = WN * B * 16;                                                                            \
+    if (a.n_tiles <= 0) return hipSuccess;                                                        \
+    if constexpr (OP == OP_BF16) {                                                                \
+      if (a.terms == 2) {                                                                         \
+        VOC_RU_T(A, B, WM, WN, TGV, MB, 2)                                                        \
+        return hipGetLastError();                                                                 \
+      }                                                                                           \
+    }                                                                                             \
+    VOC_RU_T(A, B, WM, WN, TGV, MB, 1)                                                            \
+    return hipGetLastError();                                                                     \
   }
+// A tile used with one-term operands only.
+#define VOC_RU1(CW, BIG, A, B, WM, WN, TGV, MB)                                                   \
+  if (a.C == CW && big == BIG && a.terms != 2) {                                                  \
+    *bn = WN * B * 16;                                                                            \
+    if (a.n_tiles <= 0) return hipSuccess;                                                        \
+    VOC_RU_T(A, B, WM, WN, TGV, MB, 1)                                                            \
+    return hipGetLastError();                                                                     \
+  }
+#define VOC_RU1_(...) VOC_RU1(__VA_ARGS__)
   if constexpr (OP == OP_BF16) {
     VOC_RU_(64, true, VOC_BF_RU64)
     VOC_RU(64, false, 4, 2, 1, 4, 7, 2)
-    VOC_RU_(96, true, VOC_BF_RU96)
+    VOC_RU1_(96, true, VOC_BF_RU96)
     VOC_RU(96, false, 6, 2, 1, 4, 7, 2)
     VOC_RU_(128, true, VOC_BF_RU128)
     VOC_RU(128, false, 4, 4, 2, 2, 4, 2)
@@ -587,13 +647,17 @@ static hipError_t launch_ru(const ResUnitArgs& a, bool big, hipStream_t s, int* 
   }
 #undef VOC_RU
 #undef VOC_RU_
+#undef VOC_RU1
+#undef VOC_RU1_
+#undef VOC_RU_T
   return hipErrorInvalidValue;
 }
 
-int res_unit_tile(int op, int C, bool big) {
+int res_unit_tile(int op, int C, bool big, int terms) {
   int bn = 0;
   ResUnitArgs probe{};
   probe.C = C;
+  probe.terms = terms;
   probe.n_tiles = 0;
   const hipError_t e = op == OP_F32 ? launch_ru<OP_F32>(probe, big, nullptr, &bn)
                                     : launch_ru<OP_BF16>(probe, big, nullptr, &bn);

@@ -24,7 +24,7 @@ enum OpType { OP_F32 = 0, OP_BF16 = 1 };
 
 // Frames per workgroup of the fused residual-unit kernel for width C (0: no
 // fused instance); defined with the kernels.
-int res_unit_tile(int op, int C, bool big);
+int res_unit_tile(int op, int C, bool big, int terms = 1);
 
 int total_stride(const voc_config& c);
 voc_status validate(const voc_config* c, std::string* why);

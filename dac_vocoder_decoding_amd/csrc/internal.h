@@ -69,6 +69,10 @@ struct ConvArgs {
   int lb;         // frames in [-lb, 0) of x are read from memory (a stream's context), else zero
   int in_stride;  // > 1: strided conv (2 taps); GEMM frame m of virtual chunk c reads input row
                   // m * s + c % s - s/2 of chunk c / s, s = in_stride (Cin counts real channels)
+  int s_terms;    // 2: s_out holds two-term bf16 operands, [row][2 * Cout / CH][T][CH] with
+                  // the low terms in channel planes Cout / CH.. (0 or 1: one term)
+  int h32;        // 1 (bf16 operands): res and h_out hold fp32 elements (decoders with
+                  // two-term operands keep an fp32 residual stream)
 };
 
 // Tile shape families of the conv GEMM kernel.
@@ -112,6 +116,8 @@ struct ResUnitArgs {
   const void* w2;        // packed [C/CH][1][C][CH]
   const float* b2;
   float* h;              // residual stream written
+  int terms;             // 1, or 2 (bf16): two-term operands (x / s_out planes [row][2C/CH][T][CH],
+                         // w1 / w2 with every channel chunk plane present twice); 0 counts as 1
   int store_h;           // 0: the updated h is not stored (nothing reads it)
   void* s_out;           // may be null
   const float* s_scale;

@@ -49,6 +49,8 @@ struct ConvDev {
   int cin = 0, cout = 0, taps = 0, dil = 1, ups = 1, crop = 0, M = 0;
   int causal = 0;  // k=7: left padding (K-1)*d instead of "same"
   int down = 1;    // > 1: strided conv (k = 2*down, stride down, pad down/2) as 2 taps
+  int terms = 1;   // 2: its input is a two-term operand (2 * cin channels; w holds every
+                   // input chunk plane twice)
 };
 struct UnitDev {
   SnakeDev a1, a2;
@@ -117,6 +119,7 @@ struct voc_ctx {
   bool no_fuse = false;                 // ablation: always run conv1 and conv2 apart
   int m_order = -1;                     // ablation: conv tile order (-1 auto, 0 N fastest, 1 M fastest)
   int ru_xh = 1;                        // fused units compute Snake1 from h (0: read an operand tensor)
+  int terms = 1;                        // matrix-core operand terms (voc_config::operand_terms)
   bool split_snake = false;             // ablation: every plain Snake as a launch of its own
   bool split_tanh = false;              // ablation: tanh as a pass of its own after the head
   bool head_no_tanh = false;            // set during a split-tanh decode
@@ -236,7 +239,7 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // the last unit of a block is 3-9 % slower; the mono codec's 96-channel
 // block as a whole 3.5 % faster).
 bool unit_xh(const voc_ctx* c, int C) {
-  return !c->cfg.af_snake && !c->split_snake && c->ru_xh && !c->no_fuse && res_unit_tile(c->op, C, false) > 0;
+  return !c->cfg.af_snake && !c->split_snake && c->ru_xh && !c->no_fuse && res_unit_tile(c->op, C, false, c->terms) > 0;
 }
 
 // Largest latent frames per decoded row this context's decoder can address
@@ -256,8 +259,12 @@ bool any_unit_xh(const voc_ctx* c) {
 // residual stream (bf16 decoders without standalone Snake launches); null
 // when the last producer stores Snake_out(h) in fp32 for it.
 const SnakeDev* head_snake_at_load(const voc_ctx* c) {
-  return c->op == OP_BF16 && !c->cfg.af_snake && !c->split_snake ? &c->W.head_act : nullptr;
+  return c->op == OP_BF16 && c->terms == 1 && !c->cfg.af_snake && !c->split_snake ? &c->W.head_act : nullptr;
 }
+
+// Bytes per residual-stream element: fp32, or fp16 for one-term bf16 decoders
+// (two-term decoders keep h in fp32, whose precision their operands need).
+int hsz(const voc_ctx* c) { return c->terms == 2 ? 4 : h_size(c->op); }
 
 Plan make_plan(const voc_ctx* c, int rows, int T, int mg = 0) {
   const voc_config& g = c->cfg;
@@ -280,9 +287,11 @@ Plan make_plan(const voc_ctx* c, int rows, int T, int mg = 0) {
   // holds the head's input, Snake_out(h), in fp32 also for bf16 decoders.
   p.off_h = o;    o = align_up(o + 4 * rows * max_act);
   p.off_h2 = o;   if (any_unit_xh(c) || g.af_snake || c->split_snake) o = align_up(o + 4 * rows * max_act);
-  p.off_s0 = o;   o = align_up(o + es * rows * max_act);
-  p.off_s1 = o;   o = align_up(o + es * rows * max_act);
-  p.off_u = o;    o = align_up(o + es * rows * max_act);
+  // Operand tensors hold c->terms bf16 terms per element (two-term operands).
+  const size_t eo = es * c->terms;
+  p.off_s0 = o;   o = align_up(o + eo * rows * max_act);
+  p.off_s1 = o;   o = align_up(o + eo * rows * max_act);
+  p.off_u = o;    o = align_up(o + eo * rows * max_act);
   p.off_meta = o; o = align_up(o + static_cast<size_t>(rows) * (5 * sizeof(int) + sizeof(int64_t)) + 64);
   p.bytes = o;
   return p;
@@ -461,7 +470,7 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   ConvArgs a{};
   a.x = io.x;
   a.T_in = io.T_in + c->mg;  // plane length (margin included)
-  a.Cin = L.cin;
+  a.Cin = L.cin * L.terms;   // a two-term operand: the low terms as further channels
   a.row_len = row_len;
   a.rate_in = io.rate_in;
   a.rate_out = L.down > 1 ? io.rate_in / L.down : io.rate_in * L.ups;
@@ -500,6 +509,8 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.h_out = io.h_out;
   a.res = io.res;
   a.s_out = io.s_out;
+  a.s_terms = io.s_out ? c->terms : 1;  // every operand a decoder writes feeds a two-term input
+  a.h32 = c->terms == 2 ? 1 : 0;
   a.s_alpha = io.snake_next ? io.snake_next->alpha : nullptr;
   a.s_invden = io.snake_next ? io.snake_next->invden : nullptr;
   a.hs_scale = io.h_snake ? io.h_snake->alpha : nullptr;
@@ -516,7 +527,7 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.m_tiles = (a.M + conv_variant_bm(v) - 1) / conv_variant_bm(v);
   // Weights of at most 2 MB stay resident in a 4 MB XCD L2 next to the
   // activation tiles, so the M-tiles of one N-range can run together.
-  const double wbytes = static_cast<double>(L.taps) * L.M * L.cin * L.down * op_size(c->op);
+  const double wbytes = static_cast<double>(L.taps) * L.M * L.cin * L.terms * L.down * op_size(c->op);
   a.m_fast = c->m_order >= 0 ? c->m_order : (a.m_tiles > 1 && wbytes <= 2.0 * (1 << 20));
   // Algorithmic work: every input frame meets every tap (direct convolution;
   // a strided conv: every output frame meets its 2s taps).
@@ -525,10 +536,10 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   const double flops = L.down > 1 ? 2.0 * frames_out * L.cin * L.cout * 2 * L.down
                                   : 2.0 * frames_in * L.cin * L.cout * (L.taps == 2 ? 2 * L.ups : L.taps);
   const double es = op_size(c->op);
-  double bytes = frames_in * L.cin * es + wbytes;
-  if (io.h_out) bytes += frames_out * L.cout * h_size(c->op);
-  if (io.res) bytes += frames_out * L.cout * h_size(c->op);
-  if (io.s_out) bytes += frames_out * L.cout * es;
+  double bytes = frames_in * L.cin * L.terms * es + wbytes;
+  if (io.h_out) bytes += frames_out * L.cout * hsz(c);
+  if (io.res) bytes += frames_out * L.cout * hsz(c);
+  if (io.s_out) bytes += frames_out * L.cout * es * a.s_terms;
   const int op = c->op;
   return launch(c, s, kind, flops, bytes, "conv launch",
                 [&] {
@@ -591,7 +602,7 @@ voc_status run_convt(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, c
   a.rows = rows;
   a.op = c->op;
   const double el = static_cast<double>(rows) * io.T_in * L.ups * L.cout;
-  const double hs = h_size(c->op);  // the column matrix and h use the residual element type
+  const double hs = hsz(c);  // the column matrix and h use the residual element type
   const double bytes = el * (2.0 * hs + (io.h_out ? hs : 0.0) + (io.s_out ? op_size(c->op) : 0.0));
   return launch(c, s, VOC_K_COL2IM, 0.0, bytes, "col2im launch", [&] { return launch_col2im(a, s); });
 }
@@ -615,7 +626,7 @@ voc_status run_import(voc_ctx* c, const float* x, int64_t T_src, int C, const Ro
   a.h_scale = h_sn ? h_sn->alpha : nullptr;
   a.h_h = h_sn ? h_sn->invden : nullptr;
   const double el = static_cast<double>(nrows) * T * C;
-  const double bytes = el * 4 + (s_out ? el * op_size(c->op) : 0) + (h_out ? el * h_size(c->op) : 0);
+  const double bytes = el * 4 + (s_out ? el * op_size(c->op) : 0) + (h_out ? el * hsz(c) : 0);
   return launch(c, s, VOC_K_IMPORT, 0.0, bytes, "import launch", [&] { return launch_import(a, s); });
 }
 
@@ -652,7 +663,7 @@ voc_status run_head(voc_ctx* c, const float* h, int T, const RowInfo& rows, int 
     for (int r = 0; r < nrows; ++r) frames += mi[4 * nrows + r] - mi[3 * nrows + r];
   }
   const double flops = 2.0 * frames * a.C * 7 * a.nout;
-  const double bytes = frames * a.C * (snake ? h_size(c->op) : 4) + frames * 4 * a.nout;
+  const double bytes = frames * a.C * (snake ? hsz(c) : 4) + frames * 4 * a.nout;
   return launch(c, s, VOC_K_HEAD, flops, bytes, "head launch", [&] { return launch_head(a, s); });
 }
 
@@ -681,7 +692,7 @@ voc_status run_af(voc_ctx* c, const SnakeDev& sn, const float* x, int C, int T, 
   a.rows = rows;
   a.h16 = c->op == OP_BF16 ? 1 : 0;
   const double el = static_cast<double>(rows) * T * C;
-  const double hs = h_size(c->op);
+  const double hs = hsz(c);
   const double ob = op_size(out_op);  // OP_F32: fp32 (the head's input, or fp32 operands)
   if (!c->cfg.af_snake)
     return launch(c, s, VOC_K_SNAKE, 0.0, el * (hs + ob), "Snake launch",
@@ -705,9 +716,9 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
                         bool keep_h = true) {
   const int C = u.c1.cout;
   // The large-frame tile where it still gives two workgroups per CU.
-  const int bn_big = c->no_fuse ? 0 : res_unit_tile(c->op, C, true);
+  const int bn_big = c->no_fuse ? 0 : res_unit_tile(c->op, C, true, c->terms);
   const bool big = bn_big > 0 && static_cast<int64_t>((T + bn_big - 1) / bn_big) * rows >= 2 * 256;
-  const int bn = c->no_fuse ? 0 : (big ? bn_big : res_unit_tile(c->op, C, false));
+  const int bn = c->no_fuse ? 0 : (big ? bn_big : res_unit_tile(c->op, C, false, c->terms));
   if (s_next) *s_next = nullptr;
   if (h_alt && bn <= 0) return fail(c, VOC_DEVICE_ERROR, "no fused residual unit for this width");
   if (bn > 0) {
@@ -733,6 +744,7 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     a.w2 = u.c2.w;
     a.b2 = u.c2.bias;
     a.h = h_alt ? h_alt : h;
+    a.terms = c->terms;
     a.store_h = keep_h ? 1 : 0;
     a.s_out = s_out;
     a.s_scale = next ? next->alpha : nullptr;
@@ -742,10 +754,11 @@ voc_status run_res_unit(voc_ctx* c, const UnitDev& u, const void* s_in, void* s_
     a.n_tiles = (T + bn - 1) / bn;
     a.rows = rows;
     const double el = static_cast<double>(rows) * T * C;
-    const double es = op_size(c->op);
+    const double es = op_size(c->op) * c->terms;  // operand bytes per element
     const double flops = 2.0 * el * C * 8;
     // Reads: the operand (or h itself) and h; writes: h if kept, the next operand.
-    const double hs = h_size(c->op);
+    const double hs = hsz(c);
+    // (With two-term operands the operand tensors and the packed weights are twice as large.)
     const double bytes = el * ((h_alt ? hs : es + hs) + (keep_h ? hs : 0) + (s_out ? es : 0)) + 8.0 * C * C * es;
     const int op = c->op;
     return launch(c, s, VOC_K_RES_FUSED, flops, bytes, "residual unit launch",
@@ -1020,6 +1033,11 @@ VOC_API voc_status vocoder_create(const voc_config* cfg, int hip_device, voc_ctx
   // applies tanh in a pass of its own over the pcm (untiled decodes without a
   // cancel hook; otherwise the head applies it as usual).
   if (const char* v = std::getenv("VOC_SPLIT_TANH")) c->split_tanh = std::atoi(v) != 0;
+  // Two-term operands: every kernel that writes a matrix-core operand in a
+  // decode writes both terms; the standalone Snake and col2im ablations
+  // write one and are off for such a decoder.
+  c->terms = cfg->operand_terms == 2 ? 2 : 1;
+  if (c->terms == 2) c->split_snake = c->col2im = false;
   *out = c;
   return VOC_OK;
 }
@@ -1095,8 +1113,11 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
   // Fold one conv: v is uploaded to a staging buffer, folded into the packed layout.
   // plain: the tensor is p.weight, used as stored (no weight norm).
   // cin_alloc > cin: packed with cin_alloc input channels, the extra ones zero.
+  // copies = 2: the packed tensor is stored twice in a row (two-term operands:
+  // the low-term input channels meet the same weights).
   auto fold = [&](const std::string& p, int kind, int cin, int cout, int k, int stride,
-                  void** out_w, float** out_bias, bool plain = false, int cin_alloc = 0) -> voc_status {
+                  void** out_w, float** out_bias, bool plain = false, int cin_alloc = 0,
+                  int copies = 1) -> voc_status {
     const voc_tensor* tv = got[plain ? p + ".weight" : p + ".weight_v"];
     const int64_t cnt = numel(*tv);
     const int64_t d0 = kind == PACK_CONVT ? cin : cout;
@@ -1116,7 +1137,7 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     size_t out_elems = static_cast<size_t>(cnt);
     if (kind == PACK_DOWN) out_elems = static_cast<size_t>(cout) * cin * 2 * stride;  // 2 taps x s phases
     if (cin_alloc > cin) out_elems = static_cast<size_t>(cout) * k * cin_alloc;
-    st = dalloc(out_elems * es, out_w);
+    st = dalloc(out_elems * es * copies, out_w);
     if (st) return st;
     if (out_elems != static_cast<size_t>(cnt)) {  // entries no weight maps to stay zero
       hipError_t e = hipMemset(*out_w, 0, out_elems * es);
@@ -1138,6 +1159,11 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
     fa.norms = dn;
     hipError_t e = launch_fold(fa, nullptr);
     if (e != hipSuccess) return hip_fail(c, e, "fold launch");
+    for (int k2 = 1; k2 < copies; ++k2) {
+      e = hipMemcpy(static_cast<char*>(*out_w) + k2 * out_elems * es, *out_w, out_elems * es,
+                    hipMemcpyDeviceToDevice);
+      if (e != hipSuccess) return hip_fail(c, e, "weight copy");
+    }
     if (!plain) {  // ||v|| must be positive and finite
       norm_bufs.push_back(dn);
       norm_names.push_back({p, d0});
@@ -1176,7 +1202,8 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
       blk.ct.ups = s;
       blk.ct.crop = g.causal ? 0 : (s + 1) / 2;  // causal: keep full[0, T*s)
       blk.ct.M = s * cout;
-      st = fold(p + ".conv_t1", PACK_CONVT, cin, cout, 2 * s, s, &blk.ct.w, &blk.ct.bias);
+      blk.ct.terms = c->terms;
+      st = fold(p + ".conv_t1", PACK_CONVT, cin, cout, 2 * s, s, &blk.ct.w, &blk.ct.bias, false, 0, c->terms);
       if (st) return st;
       blk.units.resize(g.n_res);
       for (int r = 0; r < g.n_res; ++r) {
@@ -1190,11 +1217,12 @@ VOC_API voc_status vocoder_load_weights(voc_ctx* c, const voc_tensor* t, int n) 
         u.c1.taps = 7;
         u.c1.dil = g.dilation[r];
         u.c1.causal = g.causal;
-        st = fold(q + ".conv1", PACK_CONV, cout, cout, 7, 1, &u.c1.w, &u.c1.bias);
+        u.c1.terms = u.c2.terms = c->terms;
+        st = fold(q + ".conv1", PACK_CONV, cout, cout, 7, 1, &u.c1.w, &u.c1.bias, false, 0, c->terms);
         if (st) return st;
         u.c2.cin = u.c2.cout = u.c2.M = cout;
         u.c2.taps = 1;
-        st = fold(q + ".conv2", PACK_CONV, cout, cout, 1, 1, &u.c2.w, &u.c2.bias);
+        st = fold(q + ".conv2", PACK_CONV, cout, cout, 1, 1, &u.c2.w, &u.c2.bias, false, 0, c->terms);
         if (st) return st;
       }
     }
@@ -1641,7 +1669,7 @@ std::vector<voc_ctx::LayerState> stream_layers(const voc_ctx* c) {
   const voc_config& g = c->cfg;
   const int op_rows = 64 / op_size(c->op);  // channels per 64-byte operand row
   std::vector<voc_ctx::LayerState> v;
-  const int h_rows = kHChunk * h_size(c->op);  // bytes per residual-stream frame row
+  const int h_rows = kHChunk * hsz(c);  // bytes per residual-stream frame row
   auto add = [&](int ctx, int64_t planes, int row_bytes) {
     voc_ctx::LayerState L;
     L.ctx = ctx;
@@ -1923,6 +1951,8 @@ VOC_API voc_status voc_dbg_run_stage(voc_ctx* c, int stage, const float* in, int
   if ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15)
     return fail(c, VOC_INVALID_PARAMS, "buffers must be 16-byte aligned");
   if (!c->loaded) return fail(c, VOC_NOT_LOADED, "weights not loaded");
+  if (c->terms == 2)
+    return fail(c, VOC_INVALID_PARAMS, "the stage runner serves one-term decoders (operand_terms 0 or 1)");
   const int64_t t_out = T_in * si.ups;
   if (t_out > (int64_t(1) << 31) - 1) return fail(c, VOC_INVALID_PARAMS, "T too large");
   hipStream_t s = static_cast<hipStream_t>(stream);

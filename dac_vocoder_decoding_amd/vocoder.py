@@ -17,7 +17,7 @@ import numpy as np
 LIB_PATH = os.environ.get("VOC_LIBRARY") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libvocoder.so")
 
-VOC_ABI_VERSION = 3
+VOC_ABI_VERSION = 4
 VOC_MAX_BLOCKS = 8
 VOC_MAX_RES = 4
 
@@ -58,6 +58,7 @@ class voc_config(ctypes.Structure):
         ("enc_width", ctypes.c_int * (VOC_MAX_BLOCKS + 1)),
         ("af_snake", ctypes.c_int),
         ("out_channels", ctypes.c_int),
+        ("operand_terms", ctypes.c_int),
     ]
 
 
@@ -200,6 +201,7 @@ def config_from_dict(d: dict) -> voc_config:
         c.enc_width[i] = w
     c.af_snake = int(d.get("af_snake", 0))
     c.out_channels = int(d.get("out_channels", 1))
+    c.operand_terms = int(d.get("operand_terms", 0))
     return c
 
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define VOC_ABI_VERSION 3
+#define VOC_ABI_VERSION 4
 #define VOC_MAX_BLOCKS 8
 #define VOC_MAX_RES 4
 /* Bytes of the device array vocoder_decode_noalloc uses as its workspace
@@ -84,7 +84,8 @@ typedef enum voc_status {
 typedef enum voc_dtype {
   VOC_F32 = 0,  /* fp32 weights and matrix-core operands, fp32 accumulate   */
   VOC_BF16 = 1  /* bf16 weights (cast after the fold) and bf16 operands,    */
-                /* fp32 accumulate, fp32 residual stream and epilogues       */
+                /* fp32 accumulate and epilogues, fp16 residual stream       */
+                /* (operand_terms = 2: two bf16 terms per operand, below)    */
 } voc_dtype;
 
 typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
@@ -100,7 +101,9 @@ typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
  * causal is 0 or 1; an encoder (enc_width[0] > 0) needs every enc_width[b]
  * (b <= n_blocks) a positive multiple of 16 (F32) or 32 (BF16), at most
  * 8192, even strides and causal == 0; af_snake is 0 or 1, and 1 needs
- * causal == 0 and no encoder; out_channels is 1 or 2.
+ * causal == 0 and no encoder; out_channels is 1 or 2; operand_terms is 0, 1
+ * or 2, and 2 needs dtype == VOC_BF16, causal == 0, af_snake == 0,
+ * in_proj == 0 and no encoder.
  */
 typedef struct voc_config {
   int abi_version;
@@ -143,6 +146,14 @@ typedef struct voc_config {
   int out_channels;                /* conv_out output channels: 1 (mono rows)   */
                                    /* or 2 (one row decodes to stereo; the H3   */
                                    /* audio VAE, 32 channels -> stereo 32 kHz)  */
+  int operand_terms;               /* 0 or 1: each matrix-core activation       */
+                                   /* operand is one bf16 value; 2 (BF16): two  */
+                                   /* bf16 terms hi = bf16(x), lo = bf16(x-hi), */
+                                   /* both multiplied by the same bf16 weights  */
+                                   /* with fp32 accumulation: the operand holds */
+                                   /* x to ~2^-17 of its size, for twice the    */
+                                   /* matrix work and operand bytes (the bf16   */
+                                   /* weights and latent are unchanged)         */
 } voc_config;
 
 /* Fill *cfg with the full-width stereo window decoder: latent 64, widths

@@ -12,7 +12,7 @@
 namespace voc {
 // The fused residual-unit widths of the kernel file (fp32 16..128, bf16
 // 64..192), standing in for the kernels, which this build does not contain.
-int res_unit_tile(int op, int C, bool big) {
+int res_unit_tile(int op, int C, bool big, int /*terms*/) {
   const bool f = op == OP_F32 ? (C == 16 || C == 32 || C == 64 || C == 96 || C == 128)
                               : (C == 64 || C == 96 || C == 128 || C == 192);
   return f ? (big ? 256 : 128) : 0;
@@ -69,6 +69,9 @@ int main() {
       {"af 2", [](voc_config* x) { x->af_snake = 2; }},
       {"out 3", [](voc_config* x) { x->out_channels = 3; }},
       {"af causal", [](voc_config* x) { x->af_snake = 1; x->causal = 1; }},
+      {"terms 3", [](voc_config* x) { x->operand_terms = 3; }},
+      {"terms f32", [](voc_config* x) { x->operand_terms = 2; }},
+      {"terms causal", [](voc_config* x) { x->operand_terms = 2; x->dtype = VOC_BF16; x->causal = 1; }},
       {"abi", [](voc_config* x) { x->abi_version = VOC_ABI_VERSION + 1; }},
       {"hop", [](voc_config* x) { x->stride[0] = x->stride[1] = x->stride[2] = x->stride[3] = 64; }},
   };

@@ -1,0 +1,129 @@
+"""Two-term bf16 operands (voc_config.operand_terms = 2): every matrix-core
+activation operand is carried as hi = bf16(x) and lo = bf16(x - hi), both
+multiplied by the same bf16 weights with fp32 accumulation.  Held to the
+oracle that keeps the activations exact (bf16 weights and latent, fp64
+arithmetic) end to end, at a tolerance well inside the bf16 bound."""
+import numpy as np
+import pytest
+import torch
+
+from dac_vocoder_decoding_amd import inputs as I
+from dac_vocoder_decoding_amd import vocoder as V
+from oracle import oracle as O
+
+from gpu_util import TOL, rel_maxabs, rel_rms, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# Two terms hold each operand to ~2^-17 of its size: the oracle evaluated with
+# such operands lands within 1e-4 of RMS of the exact decode on these stacks,
+# and the GPU adds fp32 accumulation-order differences of the fp32 decodes'
+# order (1e-5).  1e-3 keeps a tenth of the margin and sits 20x inside the
+# bf16 bound (2e-2).
+TWO_TERM_TOL = 1e-3
+assert TWO_TERM_TOL < TOL["bf16"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    V.lib()
+
+
+def _decode(cfg, t, lat, **kw):
+    ctx = V.open_context(cfg, t, operand_terms=2, **kw)
+    try:
+        pcm = V.decode(ctx, to_dev(lat))
+        torch.cuda.synchronize()
+    finally:
+        V.vocoder_destroy(ctx)
+    return pcm.cpu().numpy()
+
+
+def _gate(got, ref, what):
+    e_max, e_rms = rel_maxabs(got, ref), rel_rms(got, ref)
+    print(f"two-term {what}: max-abs/RMS {e_max:.2e} rel-RMS {e_rms:.2e}")
+    assert e_max <= TWO_TERM_TOL, (what, e_max)
+
+
+@pytest.mark.parametrize("idx,frames,rows", [(2, 24, 2), (4, 12, 3)])
+def test_two_term_twin_decode_end_to_end(idx, frames, rows):
+    """Whole decodes of the batched-window and mono-codec stacks (full widths,
+    every fused and unfused width, a ragged tail) against the exact oracle."""
+    cfg = I.config(idx)
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg, batch=rows, frames=frames)
+    pcm = _decode(cfg, t, lat, tile_frames=0)
+    ref = O.Model(cfg, t).decode(lat)
+    assert pcm.shape == ref.shape
+    _gate(pcm, ref, f"cfg{idx} [{rows},{frames}]")
+
+
+@pytest.mark.parametrize("idx", [2, 4])
+def test_two_term_fullsize_sampled(idx):
+    """The full batched-window and mono-codec workloads: latent windows with
+    the exact halo at both clip ends and one interior window on sampled rows."""
+    cfg = I.config(idx)
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg)
+    pcm = _decode(cfg, t, lat)
+    B, T, hop = cfg["batch"], cfg["frames"], cfg["hop"]
+    m = O.Model(cfg, t)
+    halo = V.voc_config_halo(V.config_from_dict(cfg))
+    rng = np.random.default_rng(700 + idx)
+    w = 2
+    cases = [(0, 0, w), (B - 1, T - w, T)]
+    for r in sorted(rng.choice(B, size=4, replace=False)):
+        t0 = int(rng.integers(w, T - 2 * w))
+        cases.append((int(r), t0, t0 + w))
+    for r, t0, t1 in cases:
+        a, e = max(0, t0 - halo), min(T, t1 + halo)
+        ref = m.decode(lat[r:r + 1, :, a:e])[0, :, (t0 - a) * hop:(t1 - a) * hop]
+        _gate(pcm[r, :, t0 * hop:t1 * hop], ref, f"cfg{idx} row {r} frames [{t0},{t1})")
+
+
+def test_two_term_tiled_equals_untiled():
+    """Time-tiled decoding with exact halos reproduces the untiled two-term
+    decode bit for bit (same kernels, same per-element accumulation order)."""
+    cfg = I.config(2)
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg, batch=2, frames=300)
+    whole = _decode(cfg, t, lat, tile_frames=0)
+    tiled = _decode(cfg, t, lat, tile_frames=128)
+    assert np.array_equal(whole, tiled)
+
+
+def test_two_term_context_beside_one_term():
+    """A two-term and a one-term context of the same decoder on one device:
+    each decodes as it does alone, and the two-term decode is the closer to
+    the exact oracle."""
+    cfg = I.config(2)
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg, batch=2, frames=8)
+    c1 = V.open_context(cfg, t, tile_frames=0)
+    c2 = V.open_context(cfg, t, tile_frames=0, operand_terms=2)
+    try:
+        x = to_dev(lat)
+        p1a = V.decode(c1, x).cpu().numpy()
+        p2 = V.decode(c2, x).cpu().numpy()
+        p1b = V.decode(c1, x).cpu().numpy()
+    finally:
+        V.vocoder_destroy(c1)
+        V.vocoder_destroy(c2)
+    assert np.array_equal(p1a, p1b)
+    ref = O.Model(cfg, t).decode(lat)
+    assert rel_maxabs(p2, ref) * 10 < rel_maxabs(p1a, ref)
+
+
+def test_two_term_stage_runner_refuses():
+    """The per-stage runner serves one-term decoders; a two-term context
+    reports VOC_INVALID_PARAMS with a message."""
+    cfg = I.config(2)
+    t = I.make_weights(cfg)
+    ctx = V.open_context(cfg, t, operand_terms=2)
+    try:
+        lat = to_dev(I.make_latent(cfg, batch=1, frames=4))
+        with pytest.raises(V.VocError):
+            V.run_stage(ctx, 0, lat)
+    finally:
+        V.vocoder_destroy(ctx)
