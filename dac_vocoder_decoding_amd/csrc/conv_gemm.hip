@@ -50,12 +50,14 @@ namespace voc {
 // residual convs) so that profilers report them apart.  TAG 2 is the
 // strided conv: its input rows are read through phase streams (a runtime
 // stride; 1 elsewhere).
-// H32: the residual stream h (res, h_out) holds fp32 elements with bf16
-// operands (decoders with two-term operands); otherwise its element type
-// follows the operands (fp32, or fp16 with bf16).
-template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG, int NS, bool H32>
+// TT: an instance for decoders with two-term bf16 operands: the operand it
+// writes (s_out) holds both terms, and the residual stream h (res, h_out)
+// holds fp32 elements.  Otherwise one term, and h's element type follows the
+// operands (fp32, or fp16 with bf16).
+template <int OP, int TAPS, int WMB, int WNB, int WAVES_M, int WAVES_N, int TAG, int NS, bool TT>
 __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
-  constexpr int HO = H32 ? OP_F32 : OP;
+  constexpr int HO = TT ? OP_F32 : OP;
+  constexpr int ST = TT ? 2 : 1;  // terms of the written operand
   constexpr int CH = OpT<OP>::CH;
   constexpr int ES = OpT<OP>::ES;
   constexpr int BM = WAVES_M * WMB * 16;
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       }
       const int oc = o - lg * 4;                            // chunk's first channel
       const int cofs = (lg & 1) * 16 + (lg & 2) * 4;        // this lane's 8 channels
-      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout * (a.s_terms == 2 ? 2 : 1) + oc) * a.T_out + cofs;
+      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout * ST + oc) * a.T_out + cofs;
       const int64_t slo = static_cast<int64_t>(a.Cout) * a.T_out;  // low-term planes (two terms)
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
           sv[3] = snake_f32(v[3], sal[q][3], sinv[q][3]);
           pk[2 * q] = pack_bf16x2(sv[0], sv[1]);
           pk[2 * q + 1] = pack_bf16x2(sv[2], sv[3]);
-          if (a.s_terms == 2) {
+          if constexpr (TT) {
             const f4 lv = bf16_lo4(sv);
             pl[2 * q] = pack_bf16x2(lv[0], lv[1]);
             pl[2 * q + 1] = pack_bf16x2(lv[2], lv[3]);
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
           const u4v out = exchange(pk);
           if (ok)
             *reinterpret_cast<u4v*>(static_cast<uint16_t*>(a.s_out) + sbase + static_cast<int64_t>(tau) * CH) = out;
-          if (a.s_terms == 2) {
+          if constexpr (TT) {
             const u4v outl = exchange(pl);
             if (ok)
               *reinterpret_cast<u4v*>(static_cast<uint16_t*>(a.s_out) + sbase + slo +
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
         hsh = *reinterpret_cast<const f4*>(a.hs_h + o);
       }
       const int64_t hbase = (static_cast<int64_t>(row) * a.Cout + (o & ~15)) * a.T_out + (o & 15);
-      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout * (a.s_terms == 2 ? 2 : 1) + (o / CH) * CH) * a.T_out + (o % CH);
+      const int64_t sbase = (static_cast<int64_t>(row) * a.Cout * ST + (o / CH) * CH) * a.T_out + (o % CH);
       const int64_t slo = static_cast<int64_t>(a.Cout) * a.T_out;  // low-term planes (two terms)
   #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
           sv[2] = snake_f32(v[2], sal[2], sinv[2]);
           sv[3] = snake_f32(v[3], sal[3], sinv[3]);
           store_op4<OP>(a.s_out, sbase + static_cast<int64_t>(tau) * CH, sv);
-          if (a.s_terms == 2) store_op4<OP>(a.s_out, sbase + slo + static_cast<int64_t>(tau) * CH, bf16_lo4(sv));
+          if constexpr (TT) store_op4<OP>(a.s_out, sbase + slo + static_cast<int64_t>(tau) * CH, bf16_lo4(sv));
         }
       }
     }
@@ -471,7 +473,7 @@ template <int OP, int TAPS> struct Stages {
   static constexpr int v = (OP == OP_F32 ? f : b)[TAPS == 7 ? 0 : TAPS == 1 ? 2 : 1];  // 2 and 3 taps alike
 };
 
-template <int OP, int TAPS, int TAG, bool H32 = false>
+template <int OP, int TAPS, int TAG, bool TT = false>
 static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
   constexpr int NS = Stages<OP, TAPS>::v;
   const int total = a.n_tiles * a.m_tiles * a.rows;
@@ -479,7 +481,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
   switch (variant) {
 #define VOC_CASE(V, A, B, C, D)                                                            \
   case V:                                                                                  \
-    hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, H32>), grid, block, 0, s, a); \
+    hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, TT>), grid, block, 0, s, a); \
     break;
     VOC_CASE(CV_64x256, 4, 4, 1, 4)
     VOC_CASE(CV_96x256, 6, 4, 1, 4)
@@ -488,7 +490,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 #define VOC_CASE(V, A, B, C, D)                                                              \
   case V:                                                                                    \
     if constexpr (TAPS == 1 || TAPS == 2) {                                                  \
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, H32>), grid, block, 0, s, a); \
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, TT>), grid, block, 0, s, a); \
       break;                                                                                 \
     }                                                                                        \
     return hipErrorInvalidValue;
@@ -499,7 +501,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 #define VOC_CASE(V, A, B, C, D)                                                              \
   case V:                                                                                    \
     if constexpr (TAPS == 7 || (OP == OP_F32 && (TAPS == 1 || TAPS == 2))) {                 \
-      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, H32>), grid, block, 0, s, a); \
+      hipLaunchKernelGGL((conv_gemm_kernel<OP, TAPS, A, B, C, D, TAG, NS, TT>), grid, block, 0, s, a); \
       break;                                                                                 \
     }                                                                                        \
     return hipErrorInvalidValue;
@@ -516,7 +518,7 @@ static hipError_t launch_taps(int variant, const ConvArgs& a, hipStream_t s) {
 
 template <int OP>
 static hipError_t launch_op(int taps, int variant, int tag, const ConvArgs& a, hipStream_t s) {
-  if (a.h32) {  // bf16 operands with an fp32 residual stream: the decoder's convs only
+  if (a.two_term) {  // two-term operands, fp32 residual stream: the decoder's convs only
     if constexpr (OP == OP_BF16) {
       if (a.in_stride > 1 || (tag != 0 && tag != 1)) return hipErrorInvalidValue;
       switch (taps) {

@@ -69,10 +69,9 @@ struct ConvArgs {
   int lb;         // frames in [-lb, 0) of x are read from memory (a stream's context), else zero
   int in_stride;  // > 1: strided conv (2 taps); GEMM frame m of virtual chunk c reads input row
                   // m * s + c % s - s/2 of chunk c / s, s = in_stride (Cin counts real channels)
-  int s_terms;    // 2: s_out holds two-term bf16 operands, [row][2 * Cout / CH][T][CH] with
-                  // the low terms in channel planes Cout / CH.. (0 or 1: one term)
-  int h32;        // 1 (bf16 operands): res and h_out hold fp32 elements (decoders with
-                  // two-term operands keep an fp32 residual stream)
+  int two_term;   // 1 (bf16): a decoder with two-term operands: s_out holds both terms,
+                  // [row][2 * Cout / CH][T][CH] with the low terms in channel planes Cout / CH..,
+                  // and res / h_out hold fp32 elements (its residual stream is fp32)
 };
 
 // Tile shape families of the conv GEMM kernel.

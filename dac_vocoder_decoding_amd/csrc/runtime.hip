@@ -509,8 +509,7 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   a.h_out = io.h_out;
   a.res = io.res;
   a.s_out = io.s_out;
-  a.s_terms = io.s_out ? c->terms : 1;  // every operand a decoder writes feeds a two-term input
-  a.h32 = c->terms == 2 ? 1 : 0;
+  a.two_term = c->terms == 2 ? 1 : 0;  // every operand such a decoder writes feeds a two-term input
   a.s_alpha = io.snake_next ? io.snake_next->alpha : nullptr;
   a.s_invden = io.snake_next ? io.snake_next->invden : nullptr;
   a.hs_scale = io.h_snake ? io.h_snake->alpha : nullptr;
@@ -539,7 +538,7 @@ voc_status run_conv(voc_ctx* c, const ConvDev& L, const ConvIO& io, int rows, co
   double bytes = frames_in * L.cin * L.terms * es + wbytes;
   if (io.h_out) bytes += frames_out * L.cout * hsz(c);
   if (io.res) bytes += frames_out * L.cout * hsz(c);
-  if (io.s_out) bytes += frames_out * L.cout * es * a.s_terms;
+  if (io.s_out) bytes += frames_out * L.cout * es * c->terms;
   const int op = c->op;
   return launch(c, s, kind, flops, bytes, "conv launch",
                 [&] {
