@@ -82,7 +82,14 @@ void res_unit_kernel(const ResUnitArgs a) {
   constexpr bool kTwoWG8 = WAVES_M * WAVES_N == 8 && MINB > 2;
   constexpr bool kDB = VOC_RU_DB && WAVES_M * WAVES_N == 8 && !kTwoWG8;
   constexpr int NB = kDB ? 2 : 1;              // stage-1 LDS buffers
-  constexpr int S1 = NB * (XROWS + WROWS) * kRowBytes;
+  // Two terms with X staged from h: each channel chunk's X tile is staged
+  // once as a high-term and a low-term tile, and each weight group meets
+  // both (the loop runs over the NCH channel chunks); from an operand
+  // tensor the low terms are further chunks (KCH of them).
+  constexpr bool kPair = TERMS == 2 && XH;
+  constexpr int XT = kPair ? 2 * XROWS : XROWS;  // X rows per stage-1 buffer
+  constexpr int LCH = kPair ? NCH : KCH;         // stage-1 chunk steps
+  constexpr int S1 = NB * (XT + WROWS) * kRowBytes;
   constexpr int UB = KCH * BN * kRowBytes;     // U tile: [KCH][BN] rows
   constexpr int S2 = UB + C * kRowBytes;
   constexpr int LDS_T = S1 > S2 ? S1 : S2;
@@ -93,9 +100,9 @@ void res_unit_kernel(const ResUnitArgs a) {
   static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "four or eight waves");
   static_assert(C % CH == 0 && C % 16 == 0, "whole channel chunks");
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
-  // Stage-1 buffers: X tiles [NB][XROWS], then weight groups [NB][WROWS].
+  // Stage-1 buffers: X tiles [NB][XT], then weight groups [NB][WROWS].
   unsigned char* Xs = smem;
-  unsigned char* Ws = smem + NB * XROWS * kRowBytes;
+  unsigned char* Ws = smem + NB * XT * kRowBytes;
   unsigned char* Us = smem;          // stage 2 (after stage 1 is done)
   unsigned char* W2s = smem + UB;
 
@@ -260,6 +267,17 @@ void res_unit_kernel(const ResUnitArgs a) {
                          __float_as_uint(y[3]));
         }
         if (!in) v = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (kPair) {  // the low terms into the second half of the buffer
+#pragma unroll
+          for (int k = 0; k < 4 * HV; ++k) y[k] -= bf16_round(y[k]);
+          uint4 vl;
+          vl.x = pack_bf16x2(y[0], y[1]);
+          vl.y = pack_bf16x2(y[2], y[3]);
+          vl.z = pack_bf16x2(y[4], y[5]);
+          vl.w = pack_bf16x2(y[6], y[7]);
+          if (!in) vl = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(Xs + XROWS * kRowBytes + lds_off(r, unit_col(idx))) = vl;
+        }
       } else {
         v = xr[u];
       }
@@ -283,6 +301,10 @@ void res_unit_kernel(const ResUnitArgs a) {
     mma_steps<OP, WMB, WNB, TG, false>(
         acc, nt, [&](int jj, int mb) { return wt + (jj * C + mb * 16) * kRowBytes; },
         [&](int jj, int nb) { return xs + lds_off(xr0 + jj * d, lg) + nb * 1024; });
+    if constexpr (kPair)  // the same weights against the low-term tile
+      mma_steps<OP, WMB, WNB, TG, false>(
+          acc, nt, [&](int jj, int mb) { return wt + (jj * C + mb * 16) * kRowBytes; },
+          [&](int jj, int nb) { return xs + XROWS * kRowBytes + lds_off(xr0 + jj * d, lg) + nb * 1024; });
   };
   load_x(0);
   load_w(0, 0);
@@ -296,39 +318,39 @@ void res_unit_kernel(const ResUnitArgs a) {
     store_w(Ws);
     if (NG > 1) {
       load_w(0, 1);
-    } else if (KCH > 1) {
+    } else if (LCH > 1) {
       load_x(1);
       load_w(1, 0);
     }
     __syncthreads();
-    for (int c = 0; c < KCH; ++c) {
+    for (int c = 0; c < LCH; ++c) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const int p = c * NG + g;
         const int c1 = g + 1 < NG ? c : c + 1, g1 = g + 1 < NG ? g + 1 : 0;
         auto stage_next = [&]() {
-          if (c1 < KCH) {
-            if (g1 == 0) store_x(Xs + (c1 & 1) * XROWS * kRowBytes);
+          if (c1 < LCH) {
+            if (g1 == 0) store_x(Xs + (c1 & 1) * XT * kRowBytes);
             store_w(Ws + ((p + 1) & 1) * WROWS * kRowBytes);
             const int c2 = g1 + 1 < NG ? c1 : c1 + 1, g2 = g1 + 1 < NG ? g1 + 1 : 0;
-            if (c2 < KCH) {
+            if (c2 < LCH) {
               if (g2 == 0) load_x(c2);
               load_w(c2, g2);
             }
           }
         };
         if (VOC_RU_PINGPONG && wave >= WAVES_M * WAVES_N / 2) {
-          mma_group(g, Xs + (c & 1) * XROWS * kRowBytes, Ws + (p & 1) * WROWS * kRowBytes);
+          mma_group(g, Xs + (c & 1) * XT * kRowBytes, Ws + (p & 1) * WROWS * kRowBytes);
           stage_next();
         } else {
           stage_next();
-          mma_group(g, Xs + (c & 1) * XROWS * kRowBytes, Ws + (p & 1) * WROWS * kRowBytes);
+          mma_group(g, Xs + (c & 1) * XT * kRowBytes, Ws + (p & 1) * WROWS * kRowBytes);
         }
         __syncthreads();
       }
     }
   } else {
-    for (int c = 0; c < KCH; ++c) {
+    for (int c = 0; c < LCH; ++c) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if (g == 0) store_x(Xs);
@@ -336,7 +358,7 @@ void res_unit_kernel(const ResUnitArgs a) {
         __syncthreads();
         if (g + 1 < NG) {
           load_w(c, g + 1);
-        } else if (c + 1 < KCH) {
+        } else if (c + 1 < LCH) {
           load_x(c + 1);
           load_w(c + 1, 0);
         }
@@ -391,7 +413,9 @@ void res_unit_kernel(const ResUnitArgs a) {
   }
 
   // ------------------------------------------------------------ stage 2
-  for (int c = 0; c < KCH; ++c) {
+  // (Two terms: each conv2 weight chunk c meets U's high-term chunk c and its
+  // low-term chunk NCH + c.)
+  for (int c = 0; c < NCH; ++c) {
 #pragma unroll
     for (int u = 0; u < W2U; ++u) {
       const int idx = tid + u * NTH;
@@ -399,19 +423,22 @@ void res_unit_kernel(const ResUnitArgs a) {
       if (r < C) *reinterpret_cast<uint4*>(W2s + lds_off(r, unit_col(idx))) = w2r[u];
     }
     __syncthreads();
-    if (c + 1 < KCH) load_w2(c + 1);
+    if (c + 1 < NCH) load_w2(c + 1);
     uint4 A[WMB], B[WNB];
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb)
       A[mb] = *reinterpret_cast<const uint4*>(W2s + (wm * WMB * 16 + mb * 16) * kRowBytes + lane * 16);
 #pragma unroll
-    for (int nb = 0; nb < WNB; ++nb)
-      B[nb] = *reinterpret_cast<const uint4*>(
-          Us + (c * BN + wn * WNB * 16 + nb * 16) * kRowBytes + lane * 16);
+    for (int t = 0; t < TERMS; ++t) {
 #pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
+      for (int nb = 0; nb < WNB; ++nb)
+        B[nb] = *reinterpret_cast<const uint4*>(
+            Us + ((t * NCH + c) * BN + wn * WNB * 16 + nb * 16) * kRowBytes + lane * 16);
 #pragma unroll
-      for (int nb = 0; nb < WNB; ++nb) mfma_frag<OP>(A[mb], B[nb], acc[mb][nb]);
+      for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) mfma_frag<OP>(A[mb], B[nb], acc[mb][nb]);
+    }
     __syncthreads();
   }
 
@@ -617,6 +644,16 @@ static hipError_t launch_ru(const ResUnitArgs& a, bool big, hipStream_t s, int* 
     VOC_RU_T(A, B, WM, WN, TGV, MB, 1)                                                            \
     return hipGetLastError();                                                                     \
   }
+// A tile used with two-term operands only.
+#define VOC_RU2(CW, BIG, A, B, WM, WN, TGV, MB)                                                   \
+  if constexpr (OP == OP_BF16) {                                                                  \
+    if (a.C == CW && big == BIG && a.terms == 2) {                                                \
+      *bn = WN * B * 16;                                                                          \
+      if (a.n_tiles <= 0) return hipSuccess;                                                      \
+      VOC_RU_T(A, B, WM, WN, TGV, MB, 2)                                                          \
+      return hipGetLastError();                                                                   \
+    }                                                                                             \
+  }
 // A tile used with one-term operands only.
 #define VOC_RU1(CW, BIG, A, B, WM, WN, TGV, MB)                                                   \
   if (a.C == CW && big == BIG && a.terms != 2) {                                                  \
@@ -626,10 +663,15 @@ static hipError_t launch_ru(const ResUnitArgs& a, bool big, hipStream_t s, int* 
     return hipGetLastError();                                                                     \
   }
 #define VOC_RU1_(...) VOC_RU1(__VA_ARGS__)
+#define VOC_RU2_(...) VOC_RU2(__VA_ARGS__)
   if constexpr (OP == OP_BF16) {
     VOC_RU_(64, true, VOC_BF_RU64)
     VOC_RU(64, false, 4, 2, 1, 4, 7, 2)
     VOC_RU1_(96, true, VOC_BF_RU96)
+#ifndef VOC_BF_RU96_T2
+#define VOC_BF_RU96_T2 6, 2, 1, 4, 2, 2
+#endif
+    VOC_RU2_(96, false, VOC_BF_RU96_T2)
     VOC_RU(96, false, 6, 2, 1, 4, 7, 2)
     VOC_RU_(128, true, VOC_BF_RU128)
     VOC_RU(128, false, 4, 4, 2, 2, 4, 2)
@@ -649,6 +691,8 @@ static hipError_t launch_ru(const ResUnitArgs& a, bool big, hipStream_t s, int* 
 #undef VOC_RU_
 #undef VOC_RU1
 #undef VOC_RU1_
+#undef VOC_RU2
+#undef VOC_RU2_
 #undef VOC_RU_T
   return hipErrorInvalidValue;
 }
