@@ -70,7 +70,16 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
   static_assert(BM % 16 == 0 && XROWS % 16 == 0, "LDS tiles come in blocks of 16 rows");
   static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
   static_assert(NS == 1 || (NS - 2) * LW <= 63, "loads in flight must fit vmcnt");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE];
+  // Two-term instances with the register-staged single buffer stage each
+  // input chunk's high-term and low-term X tiles side by side against one
+  // weight tile (the input's low terms are chunk planes Cin/2 .. of x).
+  // Paired for the ConvTranspose1d (8-11 % faster than the doubled
+  // reduction); the 7-tap GEMM's doubled X staging costs a workgroup per CU
+  // and it runs 20 % slower paired, so it keeps the doubled reduction
+  // (conv_in, tag 1, reads the one-term latent operand).
+  constexpr bool kPair = TT && NS == 1 && TAG == 0 && TAPS == 2;
+  constexpr int XT = kPair ? 2 * XROWS : XROWS;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS == 1 ? (XT + WROWS) * kRowBytes : NS * STAGE];
 
   const int tid = threadIdx.x;
   const int total = a.n_tiles * a.m_tiles * a.rows;
@@ -186,7 +195,8 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
     constexpr int XU = (XROWS * 4 + 255) / 256;
     constexpr int WU = (WROWS * 4 + 255) / 256;
     const int xrows = BN + a.halo;
-    uint4 xr[XU], wr[WU];
+    uint4 xr[XU], xl[kPair ? XU : 1], wr[WU];
+    const int nsteps = kPair ? nchunks / 2 : nchunks;  // chunk steps (low terms paired)
     auto gload = [&](int c) {
       const unsigned char* xc = xrow + (c / S) * xplane;
       const int ph = c % S;
@@ -195,10 +205,15 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
         const int idx = tid + u * 256;
         const int r = unit_row(idx), col = unit_col(idx);
         const int t = (tfirst + r) * S + ph0 + ph;  // input row
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < xrows && t >= -a.lb && t < Lin)
+        uint4 v = make_uint4(0u, 0u, 0u, 0u), vl = v;
+        if (r < xrows && t >= -a.lb && t < Lin) {
           v = *reinterpret_cast<const uint4*>(xc + static_cast<int64_t>(t) * kChunkBytes + col * 16);
+          if constexpr (kPair)
+            vl = *reinterpret_cast<const uint4*>(xc + nsteps * xplane + static_cast<int64_t>(t) * kChunkBytes +
+                                                 col * 16);
+        }
         xr[u] = v;
+        if constexpr (kPair) xl[u] = vl;
       }
       const unsigned char* wc = wbase + c * wplane;
 #pragma unroll
@@ -214,14 +229,17 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
       }
     };
     unsigned char* Xs = smem;
-    unsigned char* Ws = smem + XROWS * kRowBytes;
+    unsigned char* Ws = smem + XT * kRowBytes;
     gload(0);
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = 0; c < nsteps; ++c) {
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
         const int idx = tid + u * 256;
         const int r = unit_row(idx);
-        if (r < xrows) *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = xr[u];
+        if (r < xrows) {
+          *reinterpret_cast<uint4*>(Xs + lds_off(r, unit_col(idx))) = xr[u];
+          if constexpr (kPair) *reinterpret_cast<uint4*>(Xs + XROWS * kRowBytes + lds_off(r, unit_col(idx))) = xl[u];
+        }
       }
 #pragma unroll
       for (int u = 0; u < WU; ++u) {
@@ -230,12 +248,16 @@ __global__ __launch_bounds__(256) void conv_gemm_kernel(const ConvArgs a) {
         if (r < WROWS) *reinterpret_cast<uint4*>(Ws + lds_off(r, unit_col(idx))) = wr[u];
       }
       __syncthreads();
-      if (c + 1 < nchunks) gload(c + 1);
+      if (c + 1 < nsteps) gload(c + 1);
       const unsigned char* wt = Ws + (wm * WMB * 16) * kRowBytes + lane * 16;
       const int xr0 = a.off0 - a.min_off + wn * WNB * 16 + lr;
       mma_steps<OP, WMB, WNB, TAPS, TAPS == 7>(
           acc, TAPS, [&](int j, int mb) { return wt + (j * BM + mb * 16) * kRowBytes; },
           [&](int j, int nb) { return Xs + lds_off(xr0 + j * a.offstep, lg) + nb * 1024; });
+      if constexpr (kPair)  // the same weights against the low-term tile
+        mma_steps<OP, WMB, WNB, TAPS, TAPS == 7>(
+            acc, TAPS, [&](int j, int mb) { return wt + (j * BM + mb * 16) * kRowBytes; },
+            [&](int j, int nb) { return Xs + XROWS * kRowBytes + lds_off(xr0 + j * a.offstep, lg) + nb * 1024; });
       __syncthreads();
     }
   } else {
