@@ -50,10 +50,8 @@ voc_status validate(const voc_config* c, std::string* why) {
   if (c->af_snake && c->enc_width[0] != 0) return bad("the alias-free Snake is built for the decoder only");
   if (c->out_channels != 1 && c->out_channels != 2) return bad("out_channels must be 1 or 2");
   if (c->operand_terms < 0 || c->operand_terms > 2) return bad("operand_terms must be 0, 1 or 2");
-  if (c->operand_terms == 2 &&
-      (c->dtype != VOC_BF16 || c->causal || c->af_snake || c->in_proj || c->enc_width[0] != 0))
-    return bad("operand_terms = 2 needs a bf16, non-causal decoder without the alias-free Snake, "
-               "dec_in_proj or an encoder");
+  if (c->operand_terms == 2 && (c->dtype != VOC_BF16 || c->af_snake || c->in_proj || c->enc_width[0] != 0))
+    return bad("operand_terms = 2 needs a bf16 decoder without the alias-free Snake, dec_in_proj or an encoder");
   for (int b = 0; b <= c->n_blocks; ++b)
     if (c->width[b] <= 0 || c->width[b] % q || c->width[b] > 8192)
       return bad("widths must be positive multiples of 16 (F32) / 32 (BF16), at most 8192");

@@ -1676,12 +1676,14 @@ std::vector<voc_ctx::LayerState> stream_layers(const voc_ctx* c) {
     L.row_bytes = row_bytes;
     v.push_back(L);
   };
+  // (Operand tensors of a two-term decoder hold twice the chunk planes; the
+  // latent operand conv_in reads has one term.)
   add(6, (g.in_proj > 0 ? g.in_proj : g.latent_channels) / op_rows, kChunkBytes);
   for (int b = 0; b < g.n_blocks; ++b) {
-    add(1, g.width[b] / op_rows, kChunkBytes);
+    add(1, c->terms * g.width[b] / op_rows, kChunkBytes);
     const int C = g.width[b + 1];
     for (int r = 0; r < g.n_res; ++r)
-      add(6 * g.dilation[r], unit_xh(c, C) ? C / 16 : C / op_rows, unit_xh(c, C) ? h_rows : kChunkBytes);
+      add(6 * g.dilation[r], unit_xh(c, C) ? C / 16 : c->terms * C / op_rows, unit_xh(c, C) ? h_rows : kChunkBytes);
   }
   // The head reads h (fp16, bf16 decoders) or Snake_out(h) in fp32.
   add(6, g.width[g.n_blocks] / 16, head_snake_at_load(c) ? h_rows : kChunkBytes);

@@ -102,8 +102,8 @@ typedef enum voc_act { VOC_SNAKE = 0, VOC_SNAKE_BETA = 1 } voc_act;
  * (b <= n_blocks) a positive multiple of 16 (F32) or 32 (BF16), at most
  * 8192, even strides and causal == 0; af_snake is 0 or 1, and 1 needs
  * causal == 0 and no encoder; out_channels is 1 or 2; operand_terms is 0, 1
- * or 2, and 2 needs dtype == VOC_BF16, causal == 0, af_snake == 0,
- * in_proj == 0 and no encoder.
+ * or 2, and 2 needs dtype == VOC_BF16, af_snake == 0, in_proj == 0 and no
+ * encoder.
  */
 typedef struct voc_config {
   int abi_version;

@@ -71,7 +71,7 @@ int main() {
       {"af causal", [](voc_config* x) { x->af_snake = 1; x->causal = 1; }},
       {"terms 3", [](voc_config* x) { x->operand_terms = 3; }},
       {"terms f32", [](voc_config* x) { x->operand_terms = 2; }},
-      {"terms causal", [](voc_config* x) { x->operand_terms = 2; x->dtype = VOC_BF16; x->causal = 1; }},
+      {"terms af", [](voc_config* x) { x->operand_terms = 2; x->dtype = VOC_BF16; x->af_snake = 1; }},
       {"abi", [](voc_config* x) { x->abi_version = VOC_ABI_VERSION + 1; }},
       {"hop", [](voc_config* x) { x->stride[0] = x->stride[1] = x->stride[2] = x->stride[3] = 64; }},
   };

@@ -86,7 +86,7 @@ def _bad(**kw):
     dict(convt_crop=2, causal=1), dict(convt_crop=-1),
     dict(af_snake=1, causal=1), dict(af_snake=1, enc_width=(0, 64)),
     dict(operand_terms=3), dict(operand_terms=-1), dict(operand_terms=2),  # the last: an fp32 config
-    dict(operand_terms=2, dtype=1, causal=1), dict(operand_terms=2, dtype=1, af_snake=1),
+    dict(operand_terms=2, dtype=1, af_snake=1),
     dict(operand_terms=2, dtype=1, in_proj=64), dict(operand_terms=2, dtype=1, enc_width=(0, 64)),
 ])
 def test_invalid_configs_rejected_before_any_device_call(kw):
@@ -102,7 +102,7 @@ def test_two_term_operands_validate_for_bf16_decoders():
     (plain, tiled, stereo windows), 0 and 1 mean one term."""
     for terms in (0, 1):
         assert V.voc_config_validate(_bad(operand_terms=terms)) == V.VOC_OK
-    for idx in (2, 4):
+    for idx in (2, 4, 7):
         d = dict(I.CONFIGS[idx])
         d["operand_terms"] = 2
         assert V.voc_config_validate(V.config_from_dict(d)) == V.VOC_OK

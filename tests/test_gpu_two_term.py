@@ -59,10 +59,12 @@ def test_two_term_twin_decode_end_to_end(idx, frames, rows):
     _gate(pcm, ref, f"cfg{idx} [{rows},{frames}]")
 
 
-@pytest.mark.parametrize("idx", [2, 4])
+@pytest.mark.parametrize("idx", [2, 4, 7])
 def test_two_term_fullsize_sampled(idx):
-    """The full batched-window and mono-codec workloads: latent windows with
-    the exact halo at both clip ends and one interior window on sampled rows."""
+    """The full batched-window, mono-codec and causal-codec workloads (the
+    last decoded offline): latent windows with the exact halo (left only for
+    the causal stack) at both clip ends and one interior window on sampled
+    rows."""
     cfg = I.config(idx)
     t = I.make_weights(cfg, twin=True)
     lat = I.make_latent(cfg)
@@ -70,6 +72,7 @@ def test_two_term_fullsize_sampled(idx):
     B, T, hop = cfg["batch"], cfg["frames"], cfg["hop"]
     m = O.Model(cfg, t)
     halo = V.voc_config_halo(V.config_from_dict(cfg))
+    halo_r = 0 if cfg.get("causal") else halo
     rng = np.random.default_rng(700 + idx)
     w = 2
     cases = [(0, 0, w), (B - 1, T - w, T)]
@@ -77,7 +80,7 @@ def test_two_term_fullsize_sampled(idx):
         t0 = int(rng.integers(w, T - 2 * w))
         cases.append((int(r), t0, t0 + w))
     for r, t0, t1 in cases:
-        a, e = max(0, t0 - halo), min(T, t1 + halo)
+        a, e = max(0, t0 - halo), min(T, t1 + halo_r)
         ref = m.decode(lat[r:r + 1, :, a:e])[0, :, (t0 - a) * hop:(t1 - a) * hop]
         _gate(pcm[r, :, t0 * hop:t1 * hop], ref, f"cfg{idx} row {r} frames [{t0},{t1})")
 
@@ -127,3 +130,36 @@ def test_two_term_stage_runner_refuses():
             V.run_stage(ctx, 0, lat)
     finally:
         V.vocoder_destroy(ctx)
+
+
+def _stream(ctx, lat, chunks):
+    """Feed lat [rows, C, T] through the stream in the given chunk sizes."""
+    rows, _, T = lat.shape
+    assert sum(chunks) == T
+    V.check(V.vocoder_stream_reset(ctx, rows), ctx)
+    out, t0 = [], 0
+    for t in chunks:
+        out.append(V.stream_decode(ctx, lat[:, :, t0:t0 + t].contiguous()))
+        t0 += t
+    torch.cuda.synchronize()
+    return torch.cat(out, dim=-1)
+
+
+def test_two_term_causal_decode_and_stream():
+    """The causal codec stack (strides 8/5/4/3, SnakeBeta) with two-term
+    operands: the offline decode against the exact oracle, and a stream fed
+    in uneven chunks reproducing the offline decode bit for bit (the carried
+    context of every operand layer holds both terms)."""
+    cfg = I.config(7)
+    t = I.make_weights(cfg, twin=True)
+    lat = I.make_latent(cfg, batch=2, frames=12)
+    ctx = V.open_context(cfg, t, operand_terms=2)
+    try:
+        x = to_dev(lat)
+        whole = V.decode(ctx, x)
+        torch.cuda.synchronize()
+        streamed = _stream(ctx, x, [1, 4, 2, 5])
+    finally:
+        V.vocoder_destroy(ctx)
+    assert torch.equal(whole, streamed)
+    _gate(whole.cpu().numpy(), O.Model(cfg, t).decode(lat), "cfg7 causal [2,12]")
