@@ -51,6 +51,10 @@ Readings of points the pages leave open (each listed in the design notes):
     also rounded to bf16, mirroring an implementation whose matrix-core
     operands are bf16 while accumulation and the residual stream stay wide;
     the output head (a contraction to one channel) keeps its input wide.
+    With ``operand_terms=2`` those operands are rounded to two bf16 terms
+    instead (hi = bf16(x), lo = bf16(x - hi), carried as hi + lo): the
+    reading of an implementation that multiplies both terms by the same
+    weights;
 
 Pins (tests/test_oracle_pins.py) hold every function here to closed forms,
 brute force, textbook/library routines and invariants the pages fix.
@@ -305,6 +309,17 @@ def round_bf16(x) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def round_bf16_two_term(x) -> np.ndarray:
+    """x as two bf16 terms: hi = bf16(x) and lo = bf16(x - hi), returned as
+    hi + lo in float64 (the value a two-term matrix-core operand carries:
+    both terms meet the same weights).  x is taken at float32, as the
+    operands are formed in float32."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32).astype(np.float64)
+    hi = round_bf16(x32)
+    lo = round_bf16((x32 - hi).astype(np.float32))
+    return hi + lo
+
+
 # --------------------------------------------------------------------------
 # The decoder.
 # --------------------------------------------------------------------------
@@ -313,11 +328,14 @@ class Model:
     """Folded weights of one decoder, held at the oracle's precision."""
 
     def __init__(self, cfg: dict, tensors: dict, prec: str = "f64",
-                 bf16: bool | None = None, round_operands: bool = False):
+                 bf16: bool | None = None, round_operands: bool = False, operand_terms: int = 1):
         self.cfg = cfg
         self.prec = prec
         self.bf16 = (cfg["dtype"] == "bf16") if bf16 is None else bf16
         self.round_operands = round_operands and self.bf16
+        # round_operands with two terms: each operand is rounded to the pair
+        # hi + lo of bf16 values instead of one bf16 value.
+        self._round_op = round_bf16_two_term if operand_terms == 2 else round_bf16
         self.beta = cfg["act"] == "snakebeta"
         self.causal = bool(cfg.get("causal", 0))
         self.af = bool(cfg.get("af_snake", 0))
@@ -375,7 +393,7 @@ class Model:
         matrix-core operand is rounded to bf16."""
         y = af_snake(x, a[0], a[1], self.prec) if self.af else snake(x, a[0], a[1], self.prec)
         if self.round_operands and operand:
-            y = _c(round_bf16(y), self.prec)
+            y = _c(self._round_op(y), self.prec)
         return y
 
     def _latent(self, latent):
@@ -387,7 +405,7 @@ class Model:
         if self.in_proj is not None:
             x = conv1d(x, self.in_proj[0], self.in_proj[1], 1, self.prec)
             if self.round_operands:  # conv_in's matrix-core operand
-                x = _c(round_bf16(x), self.prec)
+                x = _c(self._round_op(x), self.prec)
         w, b = self.conv_in
         return conv1d(x, w, b, 1, self.prec, self.causal)
 
