@@ -23,17 +23,19 @@ def _noalloc(ctx, x):
     return pcm
 
 
-@pytest.mark.parametrize("idx,shapes", [
-    (1, [(2, 689), (2, 100)]),     # full window: tiled into passes; then one pass
-    (0, [(2, 86), (1, 9)]),
-    (2, [(16, 689), (4, 40)]),     # bf16 batched windows
-    (3, [(2, 1200), (2, 300)]),    # SnakeBeta with 512-frame tiles
+@pytest.mark.parametrize("idx,shapes,terms", [
+    (1, [(2, 689), (2, 100)], 1),     # full window: tiled into passes; then one pass
+    (0, [(2, 86), (1, 9)], 1),
+    (2, [(16, 689), (4, 40)], 1),     # bf16 batched windows
+    (2, [(16, 689), (4, 40)], 2),     # the same with two-term operands (twice the operand planes)
+    (3, [(2, 1200), (2, 300)], 1),    # SnakeBeta with 512-frame tiles
 ])
-def test_noalloc_equals_decode_on_two_calls(idx, shapes, monkeypatch):
+def test_noalloc_equals_decode_on_two_calls(idx, shapes, terms, monkeypatch):
     cfg = I.config(idx)
     t = I.make_weights(cfg, twin=True)
     lats = [to_dev(I.make_latent(cfg, batch=b, frames=n)) for b, n in shapes]
-    ctx = V.open_context(cfg, t)
+    kw = {"operand_terms": 2} if terms == 2 else {}
+    ctx = V.open_context(cfg, t, **kw)
     try:
         refs = [V.decode(ctx, x) for x in lats]
         torch.cuda.synchronize()
@@ -42,7 +44,7 @@ def test_noalloc_equals_decode_on_two_calls(idx, shapes, monkeypatch):
     # A context whose workspace allocator is capped at one byte: any
     # allocation on the decode path would fail with VOC_OOM.
     monkeypatch.setenv("VOC_MAX_WORKSPACE_BYTES", "1")
-    ctx = V.open_context(cfg, t)
+    ctx = V.open_context(cfg, t, **kw)
     try:
         for x, ref in zip(lats, refs):
             got = _noalloc(ctx, x)
