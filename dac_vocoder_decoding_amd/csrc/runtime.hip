@@ -420,14 +420,17 @@ voc_status upload_rows(voc_ctx* c, const Plan& p, std::vector<int64_t>&& dst_in,
 // 3000 frames leaves the 64-row tiles short of workgroups; the 16-row tile
 // serves 16-channel units (23 us against 67 us for a 64-row tile three
 // quarters empty).  For 1 and 2 taps the narrow tiles measured level with
-// the 64-row ones and are taken when they fill the chip better.
+// the 64-row ones and are taken when they fill the chip better.  The bf16
+// 1-tap 64x128 tile runs 0.88-0.94 of the 128x128 one's rate on the wide
+// units, also where the 128x128 grid leaves its last round half empty
+// (512 channels x 5.5 k frames x 16 rows: 113 against 128 us).
 int pick_variant(int op, int taps, int M, int N, int rows) {
   //                                  128x256 64x256 96x256 128x128 64x128 192x128 16x128 32x128
   static const double f32[CV_COUNT]   = {0.60, 0.90, 0.85, 0.90, 1.00, 0.70, 0.50, 0.90};
   static const double f32_t7[CV_COUNT] = {0.00, 0.90, 0.85, 0.00, 1.00, 0.00, 0.00, 1.05};
   static const double bf_t2[CV_COUNT] = {0.90, 0.80, 0.85, 1.00, 0.75, 0.92, 0.00, 0.00};
   static const double bf_t7[CV_COUNT] = {0.00, 1.00, 1.00, 0.00, 0.88, 0.00, 0.00, 0.00};
-  static const double bf_t1[CV_COUNT] = {0.46, 0.94, 0.80, 1.00, 0.95, 0.68, 0.00, 0.00};
+  static const double bf_t1[CV_COUNT] = {0.46, 0.94, 0.80, 1.00, 0.88, 0.68, 0.00, 0.00};
   const double* speed = op == OP_F32 ? (taps == 7 ? f32_t7 : f32)
                                      : taps == 2 ? bf_t2 : taps == 7 ? bf_t7 : bf_t1;
   // The 16-row 7-tap tile exactly when M <= 16 (the other families would
