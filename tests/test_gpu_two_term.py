@@ -96,6 +96,23 @@ def test_two_term_tiled_equals_untiled():
     assert np.array_equal(whole, tiled)
 
 
+def test_two_term_windows_against_the_oracle():
+    """The windowed decode with stitching (three small stereo windows, the
+    last one ragged) of a two-term context against the exact oracle's
+    windowed decode."""
+    cfg = I.config(2)
+    t = I.make_weights(cfg, twin=True)
+    win = I.make_windows(cfg, windows=3, frames=12, last_frames=10)
+    ctx = V.open_context(cfg, t, operand_terms=2)
+    try:
+        pcm = V.decode_windows(ctx, to_dev(win), 2, 10, 3, 4).cpu().numpy()
+    finally:
+        V.vocoder_destroy(ctx)
+    ref = O.Model(cfg, t).decode_windows(win, 10, 3, 4)
+    assert pcm.shape == ref.shape == (2, 20 * cfg["hop"])
+    _gate(pcm, ref, "cfg2 windows")
+
+
 def test_two_term_context_beside_one_term():
     """A two-term and a one-term context of the same decoder on one device:
     each decodes as it does alone, and the two-term decode is the closer to
