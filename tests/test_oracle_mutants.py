@@ -189,3 +189,35 @@ def test_planted_python_mistake_is_caught(name, method, orig, bad, monkeypatch):
     monkeypatch.setattr(owner, meth, ns[meth])
     with pytest.raises(AssertionError):
         _py_pins(O)
+
+
+# Planted mistakes in the two-term operand rounding, against its own pins
+# (kept apart from the list above: the end-to-end pin decodes a full-width
+# stack, too slow to repeat for every mutant there).
+TT_MUTANTS = [
+    ("two_term_drops_low_term", "fn:round_bf16_two_term", "return hi + lo", "return hi"),
+    ("two_term_low_term_sign", "fn:round_bf16_two_term", "lo = round_bf16((x32 - hi).astype(np.float32))",
+     "lo = round_bf16((hi - x32).astype(np.float32))"),
+    ("two_term_low_term_unrounded", "fn:round_bf16_two_term", "lo = round_bf16((x32 - hi).astype(np.float32))",
+     "lo = (x32 - hi).astype(np.float32).astype(np.float64)"),
+    ("operand_terms_ignored", "__init__",
+     "self._round_op = round_bf16_two_term if operand_terms == 2 else round_bf16",
+     "self._round_op = round_bf16"),
+]
+
+
+def _tt_pins(orc):
+    P.test_two_term_bf16_rounding(orc)
+    P.test_two_term_operands_meet_the_bf16_bound_end_to_end(orc)
+
+
+@pytest.mark.parametrize("name,method,orig,bad", TT_MUTANTS, ids=[m[0] for m in TT_MUTANTS])
+def test_planted_two_term_mistake_is_caught(name, method, orig, bad, monkeypatch):
+    owner, meth = (O, method[3:]) if method.startswith("fn:") else (O.Model, method)
+    src = textwrap.dedent(inspect.getsource(getattr(owner, meth)))
+    assert src.count(orig) == 1, f"mutation site not unique: {name}"
+    ns = dict(vars(O))
+    exec(compile(src.replace(orig, bad), f"<mutant {name}>", "exec"), ns)
+    monkeypatch.setattr(owner, meth, ns[meth])
+    with pytest.raises(AssertionError):
+        _tt_pins(O)
